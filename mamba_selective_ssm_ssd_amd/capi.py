@@ -1,0 +1,96 @@
+"""ctypes binding of libm3ssm.so: the C ABI declared in include/m3_ssm.h.
+
+The functions here have the same names and arguments as the C entry points
+and only marshal arguments.  Loading fails loudly when the library has not
+been built; there is no other implementation behind these names.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libm3ssm.so")
+
+M3_DTYPE_F32 = 0
+M3_DTYPE_BF16 = 1
+
+M3_OK = 0
+M3_ERR_INVALID_ARGUMENT = 1
+M3_ERR_UNSUPPORTED = 2
+M3_ERR_WORKSPACE = 3
+M3_ERR_HIP = 4
+
+# Every symbol include/m3_ssm.h declares.
+EXPORTED = ("m3_ssm_prefill_workspace_bytes", "m3_ssm_prefill", "m3_ssm_decode_step",
+            "m3_status_string")
+
+
+class m3_shape_t(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64),
+                ("nheads", ctypes.c_int32), ("headdim", ctypes.c_int32),
+                ("dstate", ctypes.c_int32), ("rank", ctypes.c_int32),
+                ("chunk", ctypes.c_int32), ("io_dtype", ctypes.c_int32)]
+
+
+class m3_state_t(ctypes.Structure):
+    _fields_ = [("h", ctypes.c_void_p), ("phi", ctypes.c_void_p),
+                ("prev_B", ctypes.c_void_p), ("prev_x", ctypes.c_void_p)]
+
+
+class M3Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {m3_status_string(status)} ({status})")
+        self.status = status
+
+
+_lib = None
+
+
+def load():
+    """Load libm3ssm.so (raises if it is missing)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m mamba_selective_ssm_ssd_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, sp = ctypes.c_void_p, ctypes.POINTER(m3_shape_t)
+    stp = ctypes.POINTER(m3_state_t)
+    lib.m3_ssm_prefill_workspace_bytes.argtypes = [sp]
+    lib.m3_ssm_prefill_workspace_bytes.restype = ctypes.c_size_t
+    lib.m3_ssm_prefill.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, stp, stp, vp, vp,
+                                   ctypes.c_size_t, vp]
+    lib.m3_ssm_prefill.restype = ctypes.c_int
+    lib.m3_ssm_decode_step.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, stp, vp, vp]
+    lib.m3_ssm_decode_step.restype = ctypes.c_int
+    lib.m3_status_string.argtypes = [ctypes.c_int]
+    lib.m3_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def m3_status_string(status: int) -> str:
+    return load().m3_status_string(int(status)).decode()
+
+
+def m3_ssm_prefill_workspace_bytes(shape: m3_shape_t) -> int:
+    return int(load().m3_ssm_prefill_workspace_bytes(ctypes.byref(shape)))
+
+
+def m3_ssm_prefill(shape, x, dt, A, lam, theta, B, C, init, final_state, y, workspace,
+                   workspace_bytes, stream) -> int:
+    """Pointers are ints (device addresses) or None; init/final_state are
+    m3_state_t or None.  Returns the m3_status_t value."""
+    return int(load().m3_ssm_prefill(
+        ctypes.byref(shape), x, dt, A, lam, theta, B, C,
+        ctypes.byref(init) if init is not None else None,
+        ctypes.byref(final_state) if final_state is not None else None,
+        y, workspace, int(workspace_bytes), stream))
+
+
+def m3_ssm_decode_step(shape, x, dt, A, lam, theta, B, C, state, y, stream) -> int:
+    return int(load().m3_ssm_decode_step(
+        ctypes.byref(shape), x, dt, A, lam, theta, B, C,
+        ctypes.byref(state) if state is not None else None, y, stream))

@@ -1,0 +1,245 @@
+// m3_device.hpp -- device helpers shared by the gfx950 kernels of the mixer:
+// element types, vector loads, the 16x16x32 MFMA fragment abstraction and
+// wave-wide scans.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace m3 {
+
+constexpr int kQ = 64;        // tokens per chunk
+constexpr int kWave = 64;     // CDNA wavefront width
+constexpr int kThreads = 256; // threads per workgroup of the chunk kernels
+constexpr double kPi = 3.14159265358979323846;
+constexpr double kTwoPi = 6.28318530717958647692;
+
+// bf16 as stored in HBM: raw bits.
+struct bf16 {
+    uint16_t bits;
+};
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float floatx4;
+
+__device__ __forceinline__ float bits_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
+
+// fp32 -> bf16 bits, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint16_t f32_to_bits(float f) {
+    return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+__device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
+    return uint32_t(f32_to_bits(lo)) | (uint32_t(f32_to_bits(hi)) << 16);
+}
+
+// ---------------------------------------------------------------------------
+// I/O element access.  load8 reads 8 consecutive elements (16-byte aligned).
+// ---------------------------------------------------------------------------
+template <typename IO>
+struct io;
+
+template <>
+struct io<float> {
+    static __device__ __forceinline__ float get(const float *p) { return *p; }
+    static __device__ __forceinline__ void put(float *p, float v) { *p = v; }
+    static __device__ __forceinline__ void load8(const float *p, float v[8]) {
+        const float4 a = *reinterpret_cast<const float4 *>(p);
+        const float4 b = *reinterpret_cast<const float4 *>(p + 4);
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+    static __device__ __forceinline__ void load4(const float *p, float v[4]) {
+        const float4 a = *reinterpret_cast<const float4 *>(p);
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    }
+    static __device__ __forceinline__ void store4(float *p, const float v[4]) {
+        *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    }
+};
+
+template <>
+struct io<bf16> {
+    static __device__ __forceinline__ float get(const bf16 *p) { return bits_to_f32(p->bits); }
+    static __device__ __forceinline__ void put(bf16 *p, float v) { p->bits = f32_to_bits(v); }
+    static __device__ __forceinline__ void load8(const bf16 *p, float v[8]) {
+        const uint4 a = *reinterpret_cast<const uint4 *>(p);
+        const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = __uint_as_float(w[i] << 16);
+            v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+    }
+    static __device__ __forceinline__ void load4(const bf16 *p, float v[4]) {
+        const uint2 a = *reinterpret_cast<const uint2 *>(p);
+        v[0] = __uint_as_float(a.x << 16); v[1] = __uint_as_float(a.x & 0xffff0000u);
+        v[2] = __uint_as_float(a.y << 16); v[3] = __uint_as_float(a.y & 0xffff0000u);
+    }
+    static __device__ __forceinline__ void store4(bf16 *p, const float v[4]) {
+        *reinterpret_cast<uint2 *>(p) = make_uint2(pack2_bf16(v[0], v[1]), pack2_bf16(v[2], v[3]));
+    }
+};
+
+// ---------------------------------------------------------------------------
+// MFMA fragments for v_mfma_f32_16x16x32_bf16 (gfx950).
+// Operand A (16 x 32): lane l supplies row (l % 16) and eight k-slots
+// (group g = l / 16, j = 0..7).  Operand B (32 x 16): lane l supplies column
+// (l % 16) and the same eight k-slots.  The hardware pairs A and B by k-slot,
+// so a contraction only needs both operands to use one slot -> k mapping.
+// Result D (16 x 16 fp32): lane l holds D[4 g + v][l % 16], v = 0..3.
+//
+// Mma<false>: operands rounded to bf16, one MFMA per step.
+// Mma<true> : fp32 operands split a = hi + lo (both bf16); a*b is taken as
+//             hi*hi + hi*lo + lo*hi (three MFMAs), about 2^-16 relative.
+// ---------------------------------------------------------------------------
+template <bool F32>
+struct Mma;
+
+__device__ __forceinline__ bf16x8 bf16x8_from_words(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3) {
+    return __builtin_bit_cast(bf16x8, make_uint4(w0, w1, w2, w3));
+}
+
+template <>
+struct Mma<false> {
+    typedef uint16_t lds_t; // LDS element: bf16 bits
+    struct frag {
+        bf16x8 v;
+    };
+    static __device__ __forceinline__ frag zero() {
+        frag f;
+        f.v = bf16x8_from_words(0, 0, 0, 0);
+        return f;
+    }
+    static __device__ __forceinline__ frag pack(const float a[8]) {
+        frag f;
+        f.v = bf16x8_from_words(pack2_bf16(a[0], a[1]), pack2_bf16(a[2], a[3]),
+                                pack2_bf16(a[4], a[5]), pack2_bf16(a[6], a[7]));
+        return f;
+    }
+    static __device__ __forceinline__ floatx4 mma(floatx4 acc, const frag &a, const frag &b) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, acc, 0, 0, 0);
+    }
+    // 8 consecutive LDS elements (16-byte aligned).
+    static __device__ __forceinline__ frag lds8(const lds_t *p) {
+        frag f;
+        f.v = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(p));
+        return f;
+    }
+    // 4 consecutive elements from p0 then 4 from p1 (8-byte aligned each).
+    static __device__ __forceinline__ frag lds4x2(const lds_t *p0, const lds_t *p1) {
+        const uint2 a = *reinterpret_cast<const uint2 *>(p0);
+        const uint2 b = *reinterpret_cast<const uint2 *>(p1);
+        frag f;
+        f.v = bf16x8_from_words(a.x, a.y, b.x, b.y);
+        return f;
+    }
+    static __device__ __forceinline__ lds_t to_lds(float v) { return f32_to_bits(v); }
+    // Two adjacent LDS elements as one 32-bit store.
+    static __device__ __forceinline__ void st2(lds_t *p, float a, float b) {
+        *reinterpret_cast<uint32_t *>(p) = pack2_bf16(a, b);
+    }
+    // 8 consecutive LDS elements as one 16-byte store.
+    static __device__ __forceinline__ void st8(lds_t *p, const float a[8]) {
+        *reinterpret_cast<uint4 *>(p) = make_uint4(pack2_bf16(a[0], a[1]), pack2_bf16(a[2], a[3]),
+                                                   pack2_bf16(a[4], a[5]), pack2_bf16(a[6], a[7]));
+    }
+};
+
+template <>
+struct Mma<true> {
+    typedef float lds_t;
+    struct frag {
+        bf16x8 hi, lo;
+    };
+    static __device__ __forceinline__ frag zero() {
+        frag f;
+        f.hi = bf16x8_from_words(0, 0, 0, 0);
+        f.lo = f.hi;
+        return f;
+    }
+    static __device__ __forceinline__ frag pack(const float a[8]) {
+        uint32_t hw[4], lw[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint16_t h0 = f32_to_bits(a[2 * i]), h1 = f32_to_bits(a[2 * i + 1]);
+            const float r0 = a[2 * i] - bits_to_f32(h0), r1 = a[2 * i + 1] - bits_to_f32(h1);
+            hw[i] = uint32_t(h0) | (uint32_t(h1) << 16);
+            lw[i] = pack2_bf16(r0, r1);
+        }
+        frag f;
+        f.hi = bf16x8_from_words(hw[0], hw[1], hw[2], hw[3]);
+        f.lo = bf16x8_from_words(lw[0], lw[1], lw[2], lw[3]);
+        return f;
+    }
+    static __device__ __forceinline__ floatx4 mma(floatx4 acc, const frag &a, const frag &b) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.lo, b.hi, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.lo, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.hi, acc, 0, 0, 0);
+        return acc;
+    }
+    static __device__ __forceinline__ frag lds8(const lds_t *p) {
+        const float4 a = *reinterpret_cast<const float4 *>(p);
+        const float4 b = *reinterpret_cast<const float4 *>(p + 4);
+        const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        return pack(v);
+    }
+    static __device__ __forceinline__ frag lds4x2(const lds_t *p0, const lds_t *p1) {
+        const float4 a = *reinterpret_cast<const float4 *>(p0);
+        const float4 b = *reinterpret_cast<const float4 *>(p1);
+        const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        return pack(v);
+    }
+    static __device__ __forceinline__ lds_t to_lds(float v) { return v; }
+    static __device__ __forceinline__ void st2(lds_t *p, float a, float b) {
+        *reinterpret_cast<float2 *>(p) = make_float2(a, b);
+    }
+    static __device__ __forceinline__ void st8(lds_t *p, const float a[8]) {
+        *reinterpret_cast<float4 *>(p) = make_float4(a[0], a[1], a[2], a[3]);
+        *reinterpret_cast<float4 *>(p + 4) = make_float4(a[4], a[5], a[6], a[7]);
+    }
+};
+
+// Compute mode of an I/O type: bf16 I/O -> bf16 MFMA; fp32 I/O -> split fp32.
+template <typename IO>
+struct mode {
+    static constexpr bool f32 = false;
+};
+template <>
+struct mode<float> {
+    static constexpr bool f32 = true;
+};
+
+// ---------------------------------------------------------------------------
+// Wave-wide inclusive prefix sums (Kogge-Stone over the 64 lanes).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_inclusive_sum(float v, int lane) {
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const float u = __shfl_up(v, o, kWave);
+        if (lane >= o) v += u;
+    }
+    return v;
+}
+
+__device__ __forceinline__ double wave_inclusive_sum(double v, int lane) {
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const double u = __shfl_up(v, o, kWave);
+        if (lane >= o) v += u;
+    }
+    return v;
+}
+
+// Angle wrapped to [-pi, pi), fp64.
+__device__ __forceinline__ double wrap_angle(double a) {
+    return a - kTwoPi * floor((a + kPi) * (1.0 / kTwoPi));
+}
+
+// Rotation R(-phi) of a row pair: (u, v) -> (c u + s v, -s u + c v).
+__device__ __forceinline__ void rot_neg(float c, float s, float &u, float &v) {
+    const float a = u, b = v;
+    u = c * a + s * b;
+    v = c * b - s * a;
+}
+
+} // namespace m3

@@ -1,0 +1,123 @@
+"""torch-facing wrapper of the C ABI: prefill, decode_step and the carried State.
+
+torch is used only to hold device memory and to name the current stream;
+every step of the mixer runs in the HIP kernels of libm3ssm.so.  Tensors must
+be contiguous, on the current HIP device, in the layouts of include/m3_ssm.h:
+    x [b,T,H,R,P], B/C [b,T,H,R,N], dt/lam [b,T,H], theta [b,T,H,N/2] (I/O
+    dtype: float32 or bfloat16), A [H] float32.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import torch
+
+from . import capi
+
+_IO = {torch.float32: capi.M3_DTYPE_F32, torch.bfloat16: capi.M3_DTYPE_BF16}
+
+
+@dataclass
+class State:
+    """Carried state in the rotated frame (see include/m3_ssm.h)."""
+    h: torch.Tensor       # [b,H,N,P] float32
+    phi: torch.Tensor     # [b,H,N/2] float32
+    prev_B: torch.Tensor  # [b,H,R,N] float32
+    prev_x: torch.Tensor  # [b,H,R,P] I/O dtype
+
+    @staticmethod
+    def zeros(batch, H, N, P, R, io_dtype=torch.bfloat16, device="cuda") -> "State":
+        f = dict(device=device, dtype=torch.float32)
+        return State(torch.zeros(batch, H, N, P, **f), torch.zeros(batch, H, N // 2, **f),
+                     torch.zeros(batch, H, R, N, **f),
+                     torch.zeros(batch, H, R, P, device=device, dtype=io_dtype))
+
+    def c(self) -> capi.m3_state_t:
+        for t in (self.h, self.phi, self.prev_B, self.prev_x):
+            if not t.is_contiguous():
+                raise ValueError("state tensors must be contiguous")
+        return capi.m3_state_t(self.h.data_ptr(), self.phi.data_ptr(),
+                               self.prev_B.data_ptr(), self.prev_x.data_ptr())
+
+    def clone(self) -> "State":
+        return State(self.h.clone(), self.phi.clone(), self.prev_B.clone(), self.prev_x.clone())
+
+
+def _ptr(t: torch.Tensor, name: str, dtype) -> int:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def make_shape(batch, T, H, P, N, R, io_dtype, chunk=64) -> capi.m3_shape_t:
+    return capi.m3_shape_t(int(batch), int(T), int(H), int(P), int(N), int(R), int(chunk),
+                           int(_IO[io_dtype]))
+
+
+def workspace_bytes(batch, T, H, P, N, R, io_dtype=torch.bfloat16) -> int:
+    return capi.m3_ssm_prefill_workspace_bytes(make_shape(batch, T, H, P, N, R, io_dtype))
+
+
+def prefill(x, dt, A, lam, theta, B, C, state: State | None = None, final: State | None = None,
+            want_final: bool = True, y=None, workspace=None):
+    """Chunked prefill.  Returns (y, final_state or None).
+
+    ``state`` is the carried state to start from (None: fresh sequence).
+    The final state goes to ``final`` if given, else to ``state`` (in place)
+    when a state was given, else to a new State -- unless want_final=False.
+    """
+    b, T, H, R, P = x.shape
+    N = B.shape[-1]
+    io = x.dtype
+    shape = make_shape(b, T, H, P, N, R, io)
+    if y is None:
+        y = torch.empty_like(x)
+    if want_final and final is None:
+        final = state if state is not None else State(
+            torch.empty(b, H, N, P, device=x.device, dtype=torch.float32),
+            torch.empty(b, H, N // 2, device=x.device, dtype=torch.float32),
+            torch.empty(b, H, R, N, device=x.device, dtype=torch.float32),
+            torch.empty(b, H, R, P, device=x.device, dtype=io))
+    if not want_final:
+        final = None
+    need = capi.m3_ssm_prefill_workspace_bytes(shape)
+    if need == 0:
+        raise capi.M3Error(capi.M3_ERR_UNSUPPORTED if N % 2 == 0 else capi.M3_ERR_INVALID_ARGUMENT,
+                           "m3_ssm_prefill_workspace_bytes")
+    if workspace is None:
+        workspace = torch.empty(need, device=x.device, dtype=torch.uint8)
+    rc = capi.m3_ssm_prefill(
+        shape, _ptr(x, "x", io), _ptr(dt, "dt", io), _ptr(A, "A", torch.float32),
+        _ptr(lam, "lam", io), _ptr(theta, "theta", io), _ptr(B, "B", io), _ptr(C, "C", io),
+        state.c() if state is not None else None, final.c() if final is not None else None,
+        _ptr(y, "y", io), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+        _stream())
+    if rc != capi.M3_OK:
+        raise capi.M3Error(rc, "m3_ssm_prefill")
+    return y, final
+
+
+def decode_step(x, dt, A, lam, theta, B, C, state: State, y=None):
+    """One decode step (token axis dropped: x [b,H,R,P], ...).  Updates
+    ``state`` in place and returns y [b,H,R,P]."""
+    b, H, R, P = x.shape
+    N = B.shape[-1]
+    io = x.dtype
+    shape = make_shape(b, 1, H, P, N, R, io)
+    if y is None:
+        y = torch.empty_like(x)
+    rc = capi.m3_ssm_decode_step(
+        shape, _ptr(x, "x", io), _ptr(dt, "dt", io), _ptr(A, "A", torch.float32),
+        _ptr(lam, "lam", io), _ptr(theta, "theta", io), _ptr(B, "B", io), _ptr(C, "C", io),
+        state.c(), _ptr(y, "y", io), _stream())
+    if rc != capi.M3_OK:
+        raise capi.M3Error(rc, "m3_ssm_decode_step")
+    return y

@@ -1,0 +1,145 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/m3_ssm.h declares, and rejects bad arguments with the documented
+status codes.  Every call here fails validation before any HIP call, so no
+device is touched (the pointers are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from mamba_selective_ssm_ssd_amd import capi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "m3_ssm.h")
+
+FAKE = 0x10000          # aligned, never dereferenced
+FAKE_MISALIGNED = 0x10002
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(m3_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = capi.load()
+    names = _declared_functions()
+    assert set(names) == set(capi.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    assert capi.m3_status_string(capi.M3_OK) == "M3_OK"
+    assert capi.m3_status_string(capi.M3_ERR_WORKSPACE) == "M3_ERR_WORKSPACE"
+    assert capi.m3_status_string(99) == "M3_ERR_UNKNOWN"
+
+
+def _shape(**kw):
+    d = dict(batch=2, seqlen=100, nheads=3, headdim=64, dstate=64, rank=4, chunk=64,
+             io_dtype=capi.M3_DTYPE_BF16)
+    d.update(kw)
+    return capi.m3_shape_t(**d)
+
+
+def test_workspace_bytes():
+    ws = capi.m3_ssm_prefill_workspace_bytes(_shape())
+    bh, T, nC, N, P, K = 6, 100, 2, 64, 64, 32
+    at_least = 3 * bh * T * 4 + bh * nC * N * P * 4 + bh * nC * K * 16 + bh * N * P * 4 + bh * K * 8
+    assert at_least <= ws <= at_least + 8 * 256
+    # invalid or unsupported shapes report 0
+    assert capi.m3_ssm_prefill_workspace_bytes(_shape(dstate=63)) == 0
+    assert capi.m3_ssm_prefill_workspace_bytes(_shape(dstate=48)) == 0
+    assert capi.m3_ssm_prefill_workspace_bytes(_shape(headdim=128)) == 0
+    assert capi.m3_ssm_prefill_workspace_bytes(_shape(rank=5)) == 0
+    assert capi.m3_ssm_prefill_workspace_bytes(_shape(chunk=32)) == 0
+    assert capi.m3_ssm_prefill_workspace_bytes(_shape(seqlen=0)) == 0
+    # fp32 staging of a chunk at N=128, R>=3 does not fit in LDS
+    assert capi.m3_ssm_prefill_workspace_bytes(_shape(dstate=128, rank=3, io_dtype=capi.M3_DTYPE_F32)) == 0
+    assert capi.m3_ssm_prefill_workspace_bytes(_shape(dstate=128, rank=4)) > 0
+
+
+def _prefill(shape, **over):
+    args = dict(x=FAKE, dt=FAKE, A=FAKE, lam=FAKE, theta=FAKE, B=FAKE, C=FAKE, init=None,
+                final_state=None, y=FAKE, workspace=FAKE, workspace_bytes=0, stream=None)
+    args.update(over)
+    return capi.m3_ssm_prefill(shape, **args)
+
+
+@pytest.mark.parametrize("field,value,expect", [
+    ("dstate", 63, capi.M3_ERR_INVALID_ARGUMENT),
+    ("dstate", 48, capi.M3_ERR_UNSUPPORTED),
+    ("headdim", 0, capi.M3_ERR_INVALID_ARGUMENT),
+    ("headdim", 128, capi.M3_ERR_UNSUPPORTED),
+    ("rank", 0, capi.M3_ERR_INVALID_ARGUMENT),
+    ("rank", 5, capi.M3_ERR_UNSUPPORTED),
+    ("seqlen", 0, capi.M3_ERR_INVALID_ARGUMENT),
+    ("batch", 0, capi.M3_ERR_INVALID_ARGUMENT),
+    ("nheads", -1, capi.M3_ERR_INVALID_ARGUMENT),
+    ("chunk", 32, capi.M3_ERR_UNSUPPORTED),
+    ("chunk", 0, capi.M3_ERR_INVALID_ARGUMENT),
+    ("io_dtype", 7, capi.M3_ERR_INVALID_ARGUMENT),
+])
+def test_prefill_shape_errors(field, value, expect):
+    assert _prefill(_shape(**{field: value})) == expect
+
+
+@pytest.mark.parametrize("name", ["x", "dt", "A", "lam", "theta", "B", "C", "y"])
+def test_prefill_pointer_errors(name):
+    assert _prefill(_shape(), **{name: None}) == capi.M3_ERR_INVALID_ARGUMENT
+    assert _prefill(_shape(), **{name: FAKE_MISALIGNED}) == capi.M3_ERR_INVALID_ARGUMENT
+
+
+def test_prefill_state_errors():
+    bad = capi.m3_state_t(FAKE, None, FAKE, FAKE)
+    assert _prefill(_shape(), init=bad) == capi.M3_ERR_INVALID_ARGUMENT
+    assert _prefill(_shape(), final_state=bad) == capi.M3_ERR_INVALID_ARGUMENT
+    mis = capi.m3_state_t(FAKE, FAKE, FAKE_MISALIGNED, FAKE)
+    assert _prefill(_shape(), init=mis) == capi.M3_ERR_INVALID_ARGUMENT
+
+
+def test_prefill_workspace_errors():
+    need = capi.m3_ssm_prefill_workspace_bytes(_shape())
+    assert _prefill(_shape(), workspace=None, workspace_bytes=need) == capi.M3_ERR_WORKSPACE
+    assert _prefill(_shape(), workspace_bytes=need - 1) == capi.M3_ERR_WORKSPACE
+    assert _prefill(_shape(), workspace=FAKE_MISALIGNED, workspace_bytes=need) == capi.M3_ERR_WORKSPACE
+
+
+def test_decode_errors():
+    st = capi.m3_state_t(FAKE, FAKE, FAKE, FAKE)
+
+    def dec(shape, **over):
+        args = dict(x=FAKE, dt=FAKE, A=FAKE, lam=FAKE, theta=FAKE, B=FAKE, C=FAKE, state=st,
+                    y=FAKE, stream=None)
+        args.update(over)
+        return capi.m3_ssm_decode_step(shape, **args)
+
+    assert dec(_shape(), state=None) == capi.M3_ERR_INVALID_ARGUMENT
+    assert dec(_shape(), state=capi.m3_state_t(FAKE, FAKE, None, FAKE)) == capi.M3_ERR_INVALID_ARGUMENT
+    assert dec(_shape(), x=None) == capi.M3_ERR_INVALID_ARGUMENT
+    assert dec(_shape(dstate=7)) == capi.M3_ERR_INVALID_ARGUMENT
+    assert dec(_shape(rank=9)) == capi.M3_ERR_UNSUPPORTED
+    assert dec(_shape(io_dtype=3)) == capi.M3_ERR_INVALID_ARGUMENT
+
+
+def test_null_shape():
+    lib = capi.load()
+    assert lib.m3_ssm_prefill_workspace_bytes(None) == 0
+    st = capi.m3_state_t(FAKE, FAKE, FAKE, FAKE)
+    assert lib.m3_ssm_decode_step(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                  ctypes.byref(st), FAKE, None) == capi.M3_ERR_INVALID_ARGUMENT
+    assert lib.m3_ssm_prefill(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None,
+                              FAKE, FAKE, 1 << 30, None) == capi.M3_ERR_INVALID_ARGUMENT
+
+
+def test_product_path_does_not_import_the_oracle():
+    """The package never imports or loads the oracle."""
+    pkg = os.path.join(ROOT, "mamba_selective_ssm_ssd_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "from oracle" not in text, f
+                assert "m3_oracle" not in text and "libm3oracle" not in text, f

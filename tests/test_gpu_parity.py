@@ -1,0 +1,295 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the
+same seeded inputs, element by element, at sizes the oracle finishes in
+seconds that span several chunks and a ragged tail.  Plus the stress suites:
+slow decay (so the inter-chunk path dominates), split calls, extremes of the
+coefficients, tiny T, closed-form pins run on the GPU, determinism and
+out-of-bounds canaries.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from mamba_selective_ssm_ssd_amd import synth
+from _helpers import TOL, check_final_state, gpu_state, run_gpu_prefill, run_oracle, slice_err, to_dev
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(b, T, H, P, N, R, io, seed=0, cfg=50):
+    return synth.prefill_inputs(b, T, H, P, N, R, io=io, seed=seed, cfg=cfg)
+
+
+def _parity(d, io, init=None, init_np=None):
+    y, st = run_gpu_prefill(d, io, init=init)
+    yr, hT, phiT = run_oracle(d, init_np)
+    tol = TOL[io]
+    e_y = slice_err(y, yr, (0, 2))
+    assert e_y <= tol, f"y error {e_y:.3e} > {tol}"
+    e = check_final_state(st, d, hT, phiT, io, tol)
+    return e_y, e
+
+
+# --------------------------------------------------------------------------
+# Configuration 0 at full size, and the config shapes at oracle-sized T.
+# --------------------------------------------------------------------------
+def test_cfg0_tiny_siso_fp32():
+    d = synth.config_inputs(0)
+    e_y, _ = _parity(d, "f32")
+    print(f"cfg0 y err {e_y:.2e}")
+
+
+@pytest.mark.parametrize("N,P,R,io", [
+    (128, 64, 1, "bf16"),   # configuration 1 shape
+    (64, 64, 4, "bf16"),    # configurations 2-4 shape
+    (128, 64, 1, "f32"),
+    (64, 64, 4, "f32"),
+])
+def test_config_shapes_ragged(N, P, R, io):
+    d = _inputs(2, 300, 3, P, N, R, io, seed=1)      # 5 chunks, ragged tail of 44
+    _parity(d, io)
+
+
+@pytest.mark.parametrize("N,P", [(16, 16), (16, 64), (32, 32), (64, 16), (128, 32), (32, 64)])
+@pytest.mark.parametrize("R", [1, 2, 3, 4])
+def test_tile_set(N, P, R):
+    io = "bf16" if (N + P + R) % 2 == 0 else "f32"
+    d = _inputs(1, 150, 2, P, N, R, io, seed=N + P + R)
+    from mamba_selective_ssm_ssd_amd import capi, mixer
+    if mixer.workspace_bytes(1, 150, 2, P, N, R, torch.float32 if io == "f32" else torch.bfloat16) == 0:
+        with pytest.raises(capi.M3Error):
+            run_gpu_prefill(d, io)
+        return
+    _parity(d, io)
+
+
+# --------------------------------------------------------------------------
+# S1: slow decay -- the carried inter-chunk state dominates the output.
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("R", [1, 3, 4])
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_s1_slow_decay(R, io):
+    d = _inputs(2, 1000, 3, 32, 32, R, io, seed=7)
+    rng = np.random.default_rng(70)
+    d["A"] = (-np.exp(rng.uniform(math.log(1e-3), math.log(1e-1), size=3))).astype(np.float32)
+    _parity(d, io)
+
+
+def test_s1_inter_chunk_path_matters():
+    """The slow-decay case must depend on the carried state: zeroing the
+    chunk-to-chunk transfer in the oracle changes y far beyond tolerance."""
+    d = _inputs(1, 256, 2, 32, 32, 2, "f32", seed=8)
+    d["A"][:] = -1e-3
+    y_full, _, _ = run_oracle(d)
+    # run each chunk of 64 separately from a fresh state
+    parts = []
+    for c in range(4):
+        dc = {k: (v[:, 64 * c:64 * (c + 1)] if v.ndim >= 3 else v) for k, v in d.items()}
+        parts.append(run_oracle(dc)[0])
+    y_cut = np.concatenate(parts, axis=1)
+    assert slice_err(y_cut, y_full, (0, 2)) > 0.1
+    y, _ = run_gpu_prefill(d, "f32")
+    assert slice_err(y, y_full, (0, 2)) <= TOL["f32"]
+
+
+# --------------------------------------------------------------------------
+# S2: split calls and carried state.
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("T1", [1, 37, 64, 100])
+def test_s2_split_prefill(io, T1):
+    from mamba_selective_ssm_ssd_amd import mixer
+    d = _inputs(2, 230, 3, 32, 64, 3, io, seed=9)
+    d["A"] *= 0.01                                       # keep the carried state visible
+    yr, hT, phiT = run_oracle(d)
+    first = {k: (v[:, :T1] if v.ndim >= 3 else v) for k, v in d.items()}
+    second = {k: (v[:, T1:] if v.ndim >= 3 else v) for k, v in d.items()}
+    y1, st = run_gpu_prefill(first, io)
+    y2, st2 = run_gpu_prefill(second, io, init=st)       # final aliases init (in place)
+    assert st2 is st
+    y = np.concatenate([y1, y2], axis=1)
+    assert slice_err(y, yr, (0, 2)) <= TOL[io]
+    check_final_state(st2, d, hT, phiT, io, TOL[io])
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_s2_prefill_then_decode(io):
+    from mamba_selective_ssm_ssd_amd import mixer
+    b, T, H, P, N, R = 2, 150, 3, 64, 64, 4
+    d = _inputs(b, T, H, P, N, R, io, seed=10)
+    d["A"] *= 0.05
+    yr, hT, phiT = run_oracle(d)
+    T1 = 131
+    first = {k: (v[:, :T1] if v.ndim >= 3 else v) for k, v in d.items()}
+    y1, st = run_gpu_prefill(first, io)
+    t = to_dev(d, io)
+    ys = [y1]
+    for s in range(T1, T):
+        y = mixer.decode_step(t["x"][:, s].contiguous(), t["dt"][:, s].contiguous(), t["A"],
+                              t["lam"][:, s].contiguous(), t["theta"][:, s].contiguous(),
+                              t["B"][:, s].contiguous(), t["C"][:, s].contiguous(), st)
+        ys.append(y.double().cpu().numpy()[:, None])
+    yg = np.concatenate(ys, axis=1)
+    assert slice_err(yg, yr, (0, 2)) <= TOL[io]
+    check_final_state(st, d, hT, phiT, io, TOL[io])
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_carried_state_with_angle_and_previous_token(io):
+    """A random carried state (rotated frame, nonzero Phi and previous token)."""
+    from mamba_selective_ssm_ssd_amd import mixer
+    b, T, H, P, N, R = 2, 97, 2, 32, 32, 2
+    d = _inputs(b, T, H, P, N, R, io, seed=11)
+    rng = np.random.default_rng(111)
+    init_np = dict(h=rng.standard_normal((b, H, N, P)).astype(np.float32),
+                   phi=rng.uniform(-np.pi, np.pi, size=(b, H, N // 2)).astype(np.float32),
+                   prev_B=rng.standard_normal((b, H, R, N)).astype(np.float32),
+                   prev_x=synth.round_io(rng.standard_normal((b, H, R, P)), io))
+    init = mixer.State(*(torch.from_numpy(init_np[k]).cuda() for k in ("h", "phi", "prev_B")),
+                       torch.from_numpy(init_np["prev_x"]).to("cuda", torch.float32 if io == "f32" else torch.bfloat16))
+    init_keep = {k: v.astype(np.float64) for k, v in init_np.items()}
+    _parity(d, io, init=init, init_np=init_keep)
+
+
+# --------------------------------------------------------------------------
+# S3: extremes of the coefficients; S4: tiny T.
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("case", ["lam0", "lam1", "theta0", "dt_small", "dt_large", "A0"])
+def test_s3_extremes(case):
+    io = "f32"
+    d = _inputs(1, 200, 2, 32, 32, 2, io, seed=12)
+    if case == "lam0":
+        d["lam"][:] = 0.0
+    elif case == "lam1":
+        d["lam"][:] = 1.0
+    elif case == "theta0":
+        d["theta"][:] = 0.0
+    elif case == "dt_small":
+        d["dt"][:] = 1e-4
+    elif case == "dt_large":
+        d["dt"][:] = 10.0
+    elif case == "A0":
+        d["A"][:] = 0.0
+        d["dt"] *= 0.02                                  # bounded growth of the sum
+    _parity(d, io)
+
+
+@pytest.mark.parametrize("T", [1, 2, 63, 64, 65])
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_s4_short_sequences(T, io):
+    d = _inputs(2, T, 3, 64, 64, 4, io, seed=13)
+    _parity(d, io)
+
+
+# --------------------------------------------------------------------------
+# Closed-form pins on the GPU (parity by rotation, pure decay, impulse).
+# --------------------------------------------------------------------------
+def test_gpu_p6_parity():
+    b, T, H, P, N, R = 1, 500, 1, 16, 16, 1
+    d = _inputs(b, T, H, P, N, R, "f32", seed=14)
+    bits = np.random.default_rng(140).integers(0, 2, size=T)
+    d["A"][:] = 0.0
+    d["x"][:] = 0.0
+    d["theta"][:] = 0.0
+    d["theta"][0, :, 0, 0] = np.float32(np.pi) * bits
+    d["C"][:] = 0.0
+    d["C"][0, :, 0, 0, 0] = 1.0
+    from mamba_selective_ssm_ssd_amd import mixer
+    init = mixer.State.zeros(b, H, N, P, R, torch.float32)
+    init.h[0, 0, 0, 0] = 1.0
+    y, _ = run_gpu_prefill(d, "f32", init=init)
+    expect = (-1.0) ** np.cumsum(bits)
+    assert np.all(np.sign(y[0, :, 0, 0, 0]) == expect)
+    assert np.max(np.abs(np.abs(y[0, :, 0, 0, 0]) - 1.0)) < 1e-4
+
+
+def test_gpu_p7_pure_decay():
+    b, T, H, P, N, R = 2, 333, 2, 32, 64, 2
+    d = _inputs(b, T, H, P, N, R, "f32", seed=15)
+    d["x"][:] = 0.0
+    d["dt"] *= 0.01
+    from mamba_selective_ssm_ssd_amd import mixer
+    rng = np.random.default_rng(150)
+    h0 = rng.standard_normal((b, H, N, P)).astype(np.float32)
+    init = mixer.State.zeros(b, H, N, P, R, torch.float32)
+    init.h.copy_(torch.from_numpy(h0))
+    y, st = run_gpu_prefill(d, "f32", init=init)
+    z0 = h0[:, :, 0::2] + 1j * h0[:, :, 1::2]
+    tot = np.exp(np.sum(d["dt"].astype(np.float64) * d["A"], axis=1)[..., None]
+                 + 1j * np.sum(d["theta"].astype(np.float64), axis=1))        # [b,H,K]
+    zT = tot[..., None] * z0
+    hr = np.empty((b, H, N, P))
+    hr[:, :, 0::2], hr[:, :, 1::2] = zT.real, zT.imag
+    phiT = np.sum(d["theta"].astype(np.float64), axis=1)
+    g = gpu_state(st)
+    assert slice_err(oracle.state_to_true(g["h"], phiT), hr, (0, 1)) < 1e-4
+
+
+def test_gpu_p8_impulse():
+    b, T, H, P, N, R = 1, 128, 1, 16, 16, 2
+    d = _inputs(b, T, H, P, N, R, "f32", seed=16)
+    s = 40
+    d["x"][:] = 0.0
+    d["x"][0, s] = np.random.default_rng(160).standard_normal((H, R, P)).astype(np.float32)
+    d["theta"][:] = 0.0
+    d["dt"][:] = 0.25
+    d["lam"][:] = 0.75
+    d["A"][:] = -0.5
+    y, _ = run_gpu_prefill(d, "f32")
+    dt, lam, A = np.float64(np.float32(0.25)), 0.75, -0.5
+    alpha, gamma, delta = math.exp(dt * A), lam * dt, (1 - lam) * dt
+    v = np.einsum("hrn,hrp->hnp", d["B"][0, s].astype(np.float64), d["x"][0, s].astype(np.float64))
+    yr = np.zeros_like(y)
+    for t in range(s, T):
+        w = gamma if t == s else alpha ** (t - s) * (gamma + delta)
+        yr[0, t] = w * np.einsum("hin,hnp->hip", d["C"][0, t].astype(np.float64), v)
+    assert slice_err(y, yr, (0, 2)) < 1e-4
+
+
+# --------------------------------------------------------------------------
+# Structure: MIMO with one live channel equals SISO; determinism; canaries.
+# --------------------------------------------------------------------------
+def test_mimo_single_live_channel_equals_siso():
+    d4 = _inputs(1, 200, 2, 64, 64, 4, "f32", seed=17)
+    for k in ("x", "B", "C"):
+        d4[k][:, :, :, 1:] = 0.0
+    d1 = dict(d4)
+    for k in ("x", "B", "C"):
+        d1[k] = np.ascontiguousarray(d4[k][:, :, :, :1])
+    y4, _ = run_gpu_prefill(d4, "f32")
+    y1, _ = run_gpu_prefill(d1, "f32")
+    assert slice_err(y4[:, :, :, :1], y1, (0, 2)) < 1e-5
+    assert np.max(np.abs(y4[:, :, :, 1:])) == 0.0
+
+
+def test_determinism_bitwise():
+    from mamba_selective_ssm_ssd_amd import mixer
+    d = _inputs(2, 300, 4, 64, 64, 4, "bf16", seed=18)
+    t = to_dev(d, "bf16")
+    outs = []
+    for _ in range(2):
+        y, st = mixer.prefill(t["x"], t["dt"], t["A"], t["lam"], t["theta"], t["B"], t["C"])
+        outs.append((y.clone(), st.h.clone(), st.phi.clone(), st.prev_B.clone()))
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
+def test_output_canaries():
+    """Writes stay inside y and the state (ragged tail, odd sizes)."""
+    from mamba_selective_ssm_ssd_amd import mixer
+    b, T, H, P, N, R = 1, 77, 3, 32, 32, 3
+    d = _inputs(b, T, H, P, N, R, "bf16", seed=19)
+    t = to_dev(d, "bf16")
+    pad = 4096
+    ybuf = torch.full((b * T * H * R * P + pad,), 7.0, device="cuda", dtype=torch.bfloat16)
+    y = ybuf[:b * T * H * R * P].view(b, T, H, R, P)
+    hbuf = torch.full((b * H * N * P + pad,), 7.0, device="cuda")
+    st = mixer.State(hbuf[:b * H * N * P].view(b, H, N, P), torch.zeros(b, H, N // 2, device="cuda"),
+                     torch.zeros(b, H, R, N, device="cuda"),
+                     torch.zeros(b, H, R, P, device="cuda", dtype=torch.bfloat16))
+    mixer.prefill(t["x"], t["dt"], t["A"], t["lam"], t["theta"], t["B"], t["C"], final=st, y=y)
+    torch.cuda.synchronize()
+    assert torch.all(ybuf[b * T * H * R * P:] == 7.0)
+    assert torch.all(hbuf[b * H * N * P:] == 7.0)
