@@ -1,0 +1,347 @@
+"""Benchmark of the Mamba-3 SSM mixer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Prints ONE JSON line.  ``value`` is the prefill throughput (tokens/s) of the
+SISO prefill workload b4 T2048 H64 P64 N128 R1 (bf16 I/O, fp32 state, chunk
+64) with inputs resident in HBM; one step is one m3_ssm_prefill call (all four
+prefill kernels).  The same line carries the MIMO prefill workload
+(b4 T2048 H64 P64 N64 R4), the MIMO decode workload (b256 H64 P64 N64 R4,
+1000 consecutive steps, us/step), each kernel's average time measured with
+HIP events on the stream it runs on, the roofline of the dominant kernel, and
+the fp64 CPU oracle timed on a bounded sample of the prefill workload.
+Inputs are synthetic and seeded (see mamba_selective_ssm_ssd_amd/synth.py).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+METRIC = "Mamba-3 SSM prefill tokens/s + decode µs/step; % of MFMA / HBM peak"
+KERNELS = ("chunk_coef", "chunk_state", "state_scan", "chunk_output")
+KERNEL_SOURCES = {"chunk_output": ["k_chunk_output.hip", "m3_chunk.hpp", "m3_device.hpp", "m3_internal.hpp"],
+                  "decode_step": ["k_decode_step.hip", "m3_device.hpp", "m3_internal.hpp"]}
+
+
+# ---------------------------------------------------------------------------
+# Algorithmic bytes and flops (what each kernel must move / compute).
+# s = bytes of the I/O dtype.  "tok" = token-heads = b*T*H.
+# ---------------------------------------------------------------------------
+def kernel_bytes(kernel, b, T, H, P, N, R, s=2):
+    nC = math.ceil(T / 64)
+    K = N // 2
+    tok = b * T * H
+    ck = b * H * nC                      # chunk-heads
+    state = ck * N * P * 4               # one fp32 N x P state per chunk-head
+    if kernel == "chunk_coef":
+        return tok * 2 * s + tok * 3 * 4
+    if kernel == "chunk_state":
+        return tok * (R * P * s + R * N * s + K * s + 2 * 4) + state + ck * K * 16
+    if kernel == "state_scan":
+        return 2 * state + ck * (4 + K * 16)
+    if kernel == "chunk_output":
+        return tok * (R * P * s + 2 * R * N * s + K * s + 3 * 4 + R * P * s) + state
+    raise KeyError(kernel)
+
+
+def path_min_bytes(b, T, H, P, N, R, s=2):
+    """Inputs + outputs of the whole prefill (x, B, C, theta, dt, lam, y)."""
+    return b * T * H * (2 * R * P * s + 2 * R * N * s + (N // 2) * s + 2 * s)
+
+
+def output_useful_flops(b, T, H, P, N, R):
+    """Causal (s <= t) flops of the chunk-output kernel: C B^T and M x over
+    token pairs of a chunk, and the incoming-state product C H."""
+    total = 0
+    for c in range(math.ceil(T / 64)):
+        q = min(64, T - 64 * c)
+        pairs = q * (q + 1) // 2
+        total += pairs * R * R * 2 * (N + P) + q * R * 2 * N * P
+    return total * b * H
+
+
+def decode_bytes_per_step(b, H, P, N, R, s=2):
+    K = N // 2
+    per = (2 * N * P * 4 + 2 * R * N * 4 + 2 * R * P * s + 2 * K * 4
+           + R * P * s + 2 * R * N * s + K * s + 2 * s + R * P * s)
+    return b * H * per
+
+
+def sources_digest(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "mamba_selective_ssm_ssd_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def load_traffic(kernel, workload):
+    """HBM bytes per launch from rocprofv3 FETCH_SIZE/WRITE_SIZE counters,
+    recorded under profiles/ for the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("sources_sha256") != sources_digest(KERNEL_SOURCES[kernel]):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+def time_prefill(torch, mixer, inp, steps, warmup):
+    x, dt, A, lam, theta, B, C = (inp[k] for k in ("x", "dt", "A", "lam", "theta", "B", "C"))
+    b, T, H, R, P = x.shape
+    N = B.shape[-1]
+    y = torch.empty_like(x)
+    ws = torch.empty(mixer.workspace_bytes(b, T, H, P, N, R, x.dtype), device="cuda", dtype=torch.uint8)
+    st = mixer.State.zeros(b, H, N, P, R, x.dtype)
+    args = (x, dt, A, lam, theta, B, C)
+    for _ in range(warmup):
+        mixer.prefill(*args, final=st, y=y, workspace=ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        mixer.prefill(*args, final=st, y=y, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / steps
+    # each kernel alone, on the same stream, after a full prefill filled the workspace
+    per_kernel = {}
+    for name in KERNELS:
+        stage = mixer.capi.STAGES[name]
+        reps = max(steps, 10)
+        ks, ke = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        total = 0.0
+        for _ in range(reps):
+            if name == "state_scan":          # needs fresh chunk contributions each time
+                mixer.prefill_stage(mixer.capi.STAGES["chunk_state"], *args, None, st, y, ws)
+            ks.record()
+            mixer.prefill_stage(stage, *args, None, st, y, ws)
+            ke.record()
+            torch.cuda.synchronize()
+            total += ks.elapsed_time(ke)
+        per_kernel[name] = total / reps
+    mixer.prefill(*args, final=st, y=y, workspace=ws)   # leave a consistent state behind
+    torch.cuda.synchronize()
+    return ms, wall, per_kernel
+
+
+def time_decode(torch, mixer, synth, b, H, P, N, R, steps, warmup, seed=0):
+    # per-step inputs, step-major so that every step's slice is contiguous
+    inp = synth.torch_inputs(steps + warmup, b, H, P, N, R, io="bf16", seed=seed + 4)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed + 40)
+    st = mixer.State.zeros(b, H, N, P, R, torch.bfloat16)
+    st.h.copy_(torch.randn(st.h.shape, generator=g, device="cuda") * 0.1)
+    y = torch.empty(b, H, R, P, device="cuda", dtype=torch.bfloat16)
+    A = inp["A"]
+
+    def step(t):
+        mixer.decode_step(inp["x"][t], inp["dt"][t], A, inp["lam"][t], inp["theta"][t],
+                          inp["B"][t], inp["C"][t], st, y=y)
+
+    for t in range(warmup):
+        step(steps + t)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for t in range(steps):
+        step(t)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1000.0 / steps
+    del inp
+    return us
+
+
+def cpu_baseline(torch, inp, budget_s):
+    """The fp64 oracle on a sample of (b, h) instances of the prefill workload,
+    extrapolated to the whole batch.  Returns the cpu_baseline object."""
+    import numpy as np
+    import oracle
+
+    x = inp["x"]
+    b, T, H, R, P = x.shape
+    N = inp["B"].shape[-1]
+
+    def sample(heads):
+        sl = {}
+        for k in ("x", "dt", "lam", "theta", "B", "C"):
+            sl[k] = inp[k][0:1, :, heads].float().cpu().numpy().astype(np.float64)
+        sl["A"] = inp["A"][heads].cpu().numpy().astype(np.float64)
+        return sl
+
+    nthreads = oracle.default_threads()
+    one = sample(slice(0, 1))
+    t0 = time.perf_counter()
+    oracle.run(one["x"], one["dt"], one["A"], one["lam"], one["theta"], one["B"], one["C"], nthreads=1)
+    t1 = time.perf_counter() - t0
+    m = int(max(1, min(H, round(budget_s * nthreads / max(t1, 1e-6)))))
+    m = max(m, min(H, nthreads))
+    sl = sample(slice(0, m))
+    t0 = time.perf_counter()
+    _, _, used = oracle.run(sl["x"], sl["dt"], sl["A"], sl["lam"], sl["theta"], sl["B"], sl["C"],
+                            nthreads=nthreads)
+    dt_s = time.perf_counter() - t0
+    full_s = dt_s * (b * H) / m
+    return {"value": b * T / full_s, "unit": "tokens/s", "cores": int(used), "kind": "oracle",
+            "sample": f"{m} of {b * H} (batch, head) instances x {T} tokens of the prefill "
+                      f"workload, {dt_s:.1f} s on {used} threads, extrapolated to all instances",
+            "single_thread_s_per_instance": t1}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-mimo", action="store_true", help="skip the MIMO prefill workload")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode workload")
+    ap.add_argument("--long", action="store_true", help="also run the T=65536 MIMO prefill")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run one plain device copy of this size (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the mixer shards over (batch, head) with no communication; see DESIGN.md).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from mamba_selective_ssm_ssd_amd import mixer, synth
+    mixer.capi.load()  # fail loudly if the HIP library is missing
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    log = lambda *a: print(*a, file=sys.stderr, flush=True)
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(n, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log(f"copy calibration: {args.copy_calibration_mib} MiB read + written")
+
+    # --- SISO prefill workload (the headline value) ----------------------------
+    c1 = synth.CONFIGS[1]
+    b, T, H, P, N, R = (c1[k] for k in ("batch", "T", "H", "P", "N", "R"))
+    inp = synth.torch_inputs(b, T, H, P, N, R, io="bf16", seed=0)
+    ms, wall, pk = time_prefill(torch, mixer, inp, args.steps, args.warmup)
+    tok_s = b * T / (ms / 1000.0)
+    log(f"[siso prefill] {ms * 1000:.1f} us/call  {tok_s:.3e} tokens/s  per kernel (us): "
+        + ", ".join(f"{k} {v * 1000:.1f}" for k, v in pk.items()))
+    kern = {}
+    for k, v in pk.items():
+        nb = kernel_bytes(k, b, T, H, P, N, R)
+        kern[k] = {"avg_us": round(v * 1000, 2), "alg_bytes": nb,
+                   "gb_per_s": round(nb / (v / 1000) / 1e9, 1)}
+    dom = max(pk, key=pk.get)
+    dom_bytes = kernel_bytes(dom, b, T, H, P, N, R)
+    achieved = dom_bytes / (pk[dom] / 1000) / 1e9
+    traffic = load_traffic(dom, c1["name"]) if dom in KERNEL_SOURCES else None
+    flops = output_useful_flops(b, T, H, P, N, R)
+    roofline = {"kernel": f"k_{dom}", "bound": "hbm", "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic,
+                "mfma_useful_tflops": round(flops / (pk["chunk_output"] / 1000) / 1e12, 2)}
+    path_bytes = path_min_bytes(b, T, H, P, N, R)
+
+    result = {
+        "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": c1["name"], "batch": b, "seq_len": T, "heads": H, "headdim": P,
+                   "dstate": N, "rank": R, "chunk": 64, "state": "fp32"},
+        "roofline": roofline,
+        "path": {"min_bytes": path_bytes,
+                 "frac_of_hbm_peak_at_min_bytes": round(path_bytes / (ms / 1000) / 1e9 / HBM_PEAK_GBS, 4),
+                 "wall_s": round(wall, 3)},
+        "kernels": kern,
+    }
+
+    if not args.no_cpu:
+        log("[cpu baseline] timing the fp64 oracle on a sample ...")
+        result["cpu_baseline"] = cpu_baseline(torch, inp, args.cpu_budget)
+        log(f"[cpu baseline] {result['cpu_baseline']['value']:.3e} tokens/s on "
+            f"{result['cpu_baseline']['cores']} threads")
+    del inp
+    torch.cuda.empty_cache()
+
+    # --- MIMO prefill workload ------------------------------------------------
+    if not args.no_mimo:
+        c2 = synth.CONFIGS[2]
+        b2, T2, H2, P2, N2, R2 = (c2[k] for k in ("batch", "T", "H", "P", "N", "R"))
+        inp = synth.torch_inputs(b2, T2, H2, P2, N2, R2, io="bf16", seed=0)
+        ms2, _, pk2 = time_prefill(torch, mixer, inp, args.steps, args.warmup)
+        del inp
+        torch.cuda.empty_cache()
+        f2 = output_useful_flops(b2, T2, H2, P2, N2, R2)
+        result["mimo_prefill"] = {
+            "workload": c2["name"], "tokens_per_s": round(b2 * T2 / (ms2 / 1000), 1),
+            "ms_per_call": round(ms2, 4),
+            "kernels": {k: {"avg_us": round(v * 1000, 2),
+                            "gb_per_s": round(kernel_bytes(k, b2, T2, H2, P2, N2, R2) / (v / 1000) / 1e9, 1)}
+                        for k, v in pk2.items()},
+            "chunk_output_mfma_useful_tflops": round(f2 / (pk2["chunk_output"] / 1000) / 1e12, 2),
+            "chunk_output_mfma_frac_of_peak": round(f2 / (pk2["chunk_output"] / 1000) / 1e12
+                                                    / BF16_MFMA_PEAK_TFLOPS, 4),
+            "path_frac_of_hbm_peak_at_min_bytes": round(
+                path_min_bytes(b2, T2, H2, P2, N2, R2) / (ms2 / 1000) / 1e9 / HBM_PEAK_GBS, 4),
+        }
+        log(f"[mimo prefill] {ms2 * 1000:.1f} us/call  {b2 * T2 / (ms2 / 1000):.3e} tokens/s")
+
+    if args.long:
+        c3 = synth.CONFIGS[3]
+        b3, T3, H3, P3, N3, R3 = (c3[k] for k in ("batch", "T", "H", "P", "N", "R"))
+        inp = synth.torch_inputs(b3, T3, H3, P3, N3, R3, io="bf16", seed=0)
+        ms3, _, pk3 = time_prefill(torch, mixer, inp, max(3, args.steps // 4), 1)
+        del inp
+        torch.cuda.empty_cache()
+        result["long_mimo_prefill"] = {
+            "workload": c3["name"], "tokens_per_s": round(b3 * T3 / (ms3 / 1000), 1),
+            "ms_per_call": round(ms3, 4),
+            "kernels": {k: {"avg_us": round(v * 1000, 2)} for k, v in pk3.items()}}
+        log(f"[long mimo prefill] {ms3:.3f} ms/call")
+
+    # --- MIMO decode workload -------------------------------------------------
+    if not args.no_decode:
+        c4 = synth.CONFIGS[4]
+        b4, H4, P4, N4, R4 = (c4[k] for k in ("batch", "H", "P", "N", "R"))
+        us = time_decode(torch, mixer, synth, b4, H4, P4, N4, R4, args.decode_steps, 10)
+        db = decode_bytes_per_step(b4, H4, P4, N4, R4)
+        ach = db / (us * 1e-6) / 1e9
+        result["decode"] = {
+            "workload": c4["name"], "us_per_step": round(us, 2), "steps": args.decode_steps,
+            "roofline": {"kernel": "k_decode_step", "bound": "hbm", "achieved": round(ach, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                         "traffic": load_traffic("decode_step", c4["name"]),
+                         "alg_bytes_per_step": db}}
+        log(f"[mimo decode] {us:.1f} us/step  {ach:.0f} GB/s")
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

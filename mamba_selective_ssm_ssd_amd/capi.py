@@ -21,9 +21,16 @@ M3_ERR_UNSUPPORTED = 2
 M3_ERR_WORKSPACE = 3
 M3_ERR_HIP = 4
 
-# Every symbol include/m3_ssm.h declares.
+# Every function the headers under include/ declare.
 EXPORTED = ("m3_ssm_prefill_workspace_bytes", "m3_ssm_prefill", "m3_ssm_decode_step",
-            "m3_status_string")
+            "m3_status_string", "m3_ssm_prefill_stage")
+
+# Stages of the prefill (include/m3_ssm_stages.h).
+M3_STAGE_CHUNK_COEF = 0
+M3_STAGE_CHUNK_STATE = 1
+M3_STAGE_STATE_SCAN = 2
+M3_STAGE_CHUNK_OUTPUT = 3
+STAGES = {"chunk_coef": 0, "chunk_state": 1, "state_scan": 2, "chunk_output": 3}
 
 
 class m3_shape_t(ctypes.Structure):
@@ -65,6 +72,9 @@ def load():
     lib.m3_ssm_prefill.restype = ctypes.c_int
     lib.m3_ssm_decode_step.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, stp, vp, vp]
     lib.m3_ssm_decode_step.restype = ctypes.c_int
+    lib.m3_ssm_prefill_stage.argtypes = [ctypes.c_int32, sp, vp, vp, vp, vp, vp, vp, vp, stp, stp,
+                                         vp, vp, ctypes.c_size_t, vp]
+    lib.m3_ssm_prefill_stage.restype = ctypes.c_int
     lib.m3_status_string.argtypes = [ctypes.c_int]
     lib.m3_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -85,6 +95,15 @@ def m3_ssm_prefill(shape, x, dt, A, lam, theta, B, C, init, final_state, y, work
     m3_state_t or None.  Returns the m3_status_t value."""
     return int(load().m3_ssm_prefill(
         ctypes.byref(shape), x, dt, A, lam, theta, B, C,
+        ctypes.byref(init) if init is not None else None,
+        ctypes.byref(final_state) if final_state is not None else None,
+        y, workspace, int(workspace_bytes), stream))
+
+
+def m3_ssm_prefill_stage(stage, shape, x, dt, A, lam, theta, B, C, init, final_state, y,
+                         workspace, workspace_bytes, stream) -> int:
+    return int(load().m3_ssm_prefill_stage(
+        int(stage), ctypes.byref(shape), x, dt, A, lam, theta, B, C,
         ctypes.byref(init) if init is not None else None,
         ctypes.byref(final_state) if final_state is not None else None,
         y, workspace, int(workspace_bytes), stream))

@@ -7,8 +7,10 @@
 //   2. k_chunk_state   per-chunk state contribution U_c (MFMA), chunk angles
 //   3. k_state_scan    inter-chunk state passing; final carried state
 //   4. k_chunk_output  intra-chunk masked contraction + incoming state (MFMA)
-// Decode enqueues one k_decode_step.
+// Decode enqueues one k_decode_step.  m3_ssm_prefill_stage enqueues one of
+// the four prefill kernels alone (include/m3_ssm_stages.h).
 #include "../../include/m3_ssm.h"
+#include "../../include/m3_ssm_stages.h"
 #include "m3_internal.hpp"
 
 #include <limits>
@@ -96,10 +98,12 @@ size_t m3_ssm_prefill_workspace_bytes(const m3_shape_t *shape) {
     return layout(shape).total;
 }
 
-m3_status_t m3_ssm_prefill(const m3_shape_t *shape, const void *x, const void *dt, const float *A,
-                           const void *lam, const void *theta, const void *B, const void *C,
-                           const m3_state_t *init, m3_state_t *final_state, void *y,
-                           void *workspace, size_t workspace_bytes, hipStream_t stream) {
+// Validates a prefill call and resolves its parameters.
+static m3_status_t prepare_prefill(const m3_shape_t *shape, const void *x, const void *dt,
+                                   const float *A, const void *lam, const void *theta,
+                                   const void *B, const void *C, const m3_state_t *init,
+                                   m3_state_t *final_state, void *y, void *workspace,
+                                   size_t workspace_bytes, PrefillParams &p) {
     const m3_status_t sc = check_shape(shape, false);
     if (sc != M3_OK) return sc;
     const void *ptrs[] = {x, dt, A, lam, theta, B, C, y};
@@ -110,7 +114,7 @@ m3_status_t m3_ssm_prefill(const m3_shape_t *shape, const void *x, const void *d
     const WorkspaceLayout w = layout(shape);
     if (!workspace || !aligned16(workspace) || workspace_bytes < w.total) return M3_ERR_WORKSPACE;
 
-    PrefillParams p{};
+    p = PrefillParams{};
     p.batch = shape->batch;
     p.T = shape->seqlen;
     p.H = shape->nheads;
@@ -138,12 +142,44 @@ m3_status_t m3_ssm_prefill(const m3_shape_t *shape, const void *x, const void *d
     p.thetaCS = reinterpret_cast<float2 *>(ws + w.thetaCS);
     p.hinit = reinterpret_cast<float *>(ws + w.hinit);
     p.phi0ws = reinterpret_cast<double *>(ws + w.phi0);
+    return M3_OK;
+}
 
+static hipError_t launch_stage(int32_t stage, const PrefillParams &p, bool bf, hipStream_t stream) {
+    switch (stage) {
+    case M3_STAGE_CHUNK_COEF: return m3::launch_chunk_coef(p, bf, stream);
+    case M3_STAGE_CHUNK_STATE: return m3::launch_chunk_state(p, bf, stream);
+    case M3_STAGE_STATE_SCAN: return m3::launch_state_scan(p, bf, stream);
+    case M3_STAGE_CHUNK_OUTPUT: return m3::launch_chunk_output(p, bf, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+m3_status_t m3_ssm_prefill(const m3_shape_t *shape, const void *x, const void *dt, const float *A,
+                           const void *lam, const void *theta, const void *B, const void *C,
+                           const m3_state_t *init, m3_state_t *final_state, void *y,
+                           void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    PrefillParams p;
+    const m3_status_t sc = prepare_prefill(shape, x, dt, A, lam, theta, B, C, init, final_state, y,
+                                           workspace, workspace_bytes, p);
+    if (sc != M3_OK) return sc;
     const bool bf = shape->io_dtype == M3_DTYPE_BF16;
-    if (m3::launch_chunk_coef(p, bf, stream) != hipSuccess) return M3_ERR_HIP;
-    if (m3::launch_chunk_state(p, bf, stream) != hipSuccess) return M3_ERR_HIP;
-    if (m3::launch_state_scan(p, bf, stream) != hipSuccess) return M3_ERR_HIP;
-    if (m3::launch_chunk_output(p, bf, stream) != hipSuccess) return M3_ERR_HIP;
+    for (int32_t stage = M3_STAGE_CHUNK_COEF; stage <= M3_STAGE_CHUNK_OUTPUT; ++stage)
+        if (launch_stage(stage, p, bf, stream) != hipSuccess) return M3_ERR_HIP;
+    return M3_OK;
+}
+
+m3_status_t m3_ssm_prefill_stage(int32_t stage, const m3_shape_t *shape, const void *x,
+                                 const void *dt, const float *A, const void *lam,
+                                 const void *theta, const void *B, const void *C,
+                                 const m3_state_t *init, m3_state_t *final_state, void *y,
+                                 void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (stage < M3_STAGE_CHUNK_COEF || stage > M3_STAGE_CHUNK_OUTPUT) return M3_ERR_INVALID_ARGUMENT;
+    PrefillParams p;
+    const m3_status_t sc = prepare_prefill(shape, x, dt, A, lam, theta, B, C, init, final_state, y,
+                                           workspace, workspace_bytes, p);
+    if (sc != M3_OK) return sc;
+    if (launch_stage(stage, p, shape->io_dtype == M3_DTYPE_BF16, stream) != hipSuccess) return M3_ERR_HIP;
     return M3_OK;
 }
 

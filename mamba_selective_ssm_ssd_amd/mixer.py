@@ -105,6 +105,22 @@ def prefill(x, dt, A, lam, theta, B, C, state: State | None = None, final: State
     return y, final
 
 
+def prefill_stage(stage: int, x, dt, A, lam, theta, B, C, state, final, y, workspace):
+    """Enqueue one stage of the prefill (include/m3_ssm_stages.h) with the
+    arguments of a full prefill; used to time the kernels one at a time."""
+    b, T, H, R, P = x.shape
+    N = B.shape[-1]
+    io = x.dtype
+    rc = capi.m3_ssm_prefill_stage(
+        stage, make_shape(b, T, H, P, N, R, io), _ptr(x, "x", io), _ptr(dt, "dt", io),
+        _ptr(A, "A", torch.float32), _ptr(lam, "lam", io), _ptr(theta, "theta", io),
+        _ptr(B, "B", io), _ptr(C, "C", io), state.c() if state is not None else None,
+        final.c() if final is not None else None, _ptr(y, "y", io), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream())
+    if rc != capi.M3_OK:
+        raise capi.M3Error(rc, "m3_ssm_prefill_stage")
+
+
 def decode_step(x, dt, A, lam, theta, B, C, state: State, y=None):
     """One decode step (token axis dropped: x [b,H,R,P], ...).  Updates
     ``state`` in place and returns y [b,H,R,P]."""

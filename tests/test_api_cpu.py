@@ -11,16 +11,20 @@ import pytest
 from mamba_selective_ssm_ssd_amd import capi
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "m3_ssm.h")
+INCLUDE = os.path.join(ROOT, "include")
 
 FAKE = 0x10000          # aligned, never dereferenced
 FAKE_MISALIGNED = 0x10002
 
 
 def _declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(m3_\w+)\s*\(", text)))
+    names = set()
+    for f in os.listdir(INCLUDE):
+        if f.endswith(".h"):
+            text = open(os.path.join(INCLUDE, f)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"\b(m3_\w+)\s*\(", text))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_function():
@@ -105,6 +109,17 @@ def test_prefill_workspace_errors():
     assert _prefill(_shape(), workspace=None, workspace_bytes=need) == capi.M3_ERR_WORKSPACE
     assert _prefill(_shape(), workspace_bytes=need - 1) == capi.M3_ERR_WORKSPACE
     assert _prefill(_shape(), workspace=FAKE_MISALIGNED, workspace_bytes=need) == capi.M3_ERR_WORKSPACE
+
+
+def test_stage_errors():
+    need = capi.m3_ssm_prefill_workspace_bytes(_shape())
+    args = dict(x=FAKE, dt=FAKE, A=FAKE, lam=FAKE, theta=FAKE, B=FAKE, C=FAKE, init=None,
+                final_state=None, y=FAKE, workspace=FAKE, workspace_bytes=need, stream=None)
+    for bad in (-1, 4, 100):
+        assert capi.m3_ssm_prefill_stage(bad, _shape(), **args) == capi.M3_ERR_INVALID_ARGUMENT
+    args["workspace_bytes"] = need - 1
+    assert capi.m3_ssm_prefill_stage(0, _shape(), **args) == capi.M3_ERR_WORKSPACE
+    assert capi.m3_ssm_prefill_stage(3, _shape(dstate=5), **args) == capi.M3_ERR_INVALID_ARGUMENT
 
 
 def test_decode_errors():
