@@ -4,8 +4,8 @@
 
 Prints ONE JSON line.  ``value`` is the prefill throughput (tokens/s) of the
 SISO prefill workload b4 T2048 H64 P64 N128 R1 (bf16 I/O, fp32 state, chunk
-64) with inputs resident in HBM; one step is one m3_ssm_prefill call (all four
-prefill kernels).  The same line carries the MIMO prefill workload
+64) with inputs resident in HBM; one step is one m3_ssm_prefill call (the
+whole chunked prefill).  The same line carries the MIMO prefill workload
 (b4 T2048 H64 P64 N64 R4), the MIMO decode workload (b256 H64 P64 N64 R4,
 1000 consecutive steps, us/step), each kernel's average time measured with
 HIP events on the stream it runs on, the roofline of the dominant kernel, and
@@ -28,8 +28,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 METRIC = "Mamba-3 SSM prefill tokens/s + decode µs/step; % of MFMA / HBM peak"
-KERNELS = ("chunk_coef", "chunk_state", "state_scan", "chunk_output")
-KERNEL_SOURCES = {"chunk_output": ["k_chunk_output.hip", "m3_chunk.hpp", "m3_device.hpp", "m3_internal.hpp"],
+KERNELS = ("segment_state", "output")
+KERNEL_SOURCES = {"output": ["k_prefill.hpp", "m3_device.hpp", "m3_internal.hpp"],
                   "decode_step": ["k_decode_step.hip", "m3_device.hpp", "m3_internal.hpp"]}
 
 
@@ -37,20 +37,28 @@ KERNEL_SOURCES = {"chunk_output": ["k_chunk_output.hip", "m3_chunk.hpp", "m3_dev
 # Algorithmic bytes and flops (what each kernel must move / compute).
 # s = bytes of the I/O dtype.  "tok" = token-heads = b*T*H.
 # ---------------------------------------------------------------------------
-def kernel_bytes(kernel, b, T, H, P, N, R, s=2):
+def segments(b, H, T, slots=256):
+    """Segments per sequence chosen by the library for this shape."""
     nC = math.ceil(T / 64)
+    s = 1 if b * H >= slots else slots // (b * H)
+    s = max(1, min(s, nC))
+    cps = math.ceil(nC / s)
+    return math.ceil(nC / cps), cps
+
+
+def kernel_bytes(kernel, b, T, H, P, N, R, s=2):
+    """Bytes each prefill kernel must move: its inputs once, its outputs once."""
+    S, cps = segments(b, H, T)
     K = N // 2
-    tok = b * T * H
-    ck = b * H * nC                      # chunk-heads
-    state = ck * N * P * 4               # one fp32 N x P state per chunk-head
-    if kernel == "chunk_coef":
-        return tok * 2 * s + tok * 3 * 4
-    if kernel == "chunk_state":
-        return tok * (R * P * s + R * N * s + K * s + 2 * 4) + state + ck * K * 16
-    if kernel == "state_scan":
-        return 2 * state + ck * (4 + K * 16)
-    if kernel == "chunk_output":
-        return tok * (R * P * s + 2 * R * N * s + K * s + 3 * 4 + R * P * s) + state
+    state = b * H * N * P * 4
+    if kernel == "output":
+        # x, B, C, theta, dt, lam in, y out; aggregates of earlier segments in
+        return path_min_bytes(b, T, H, P, N, R, s) + state * S * (S - 1) // 2
+    if kernel == "segment_state":
+        if S == 1:
+            return 0
+        toks = b * H * min(T, (S - 1) * cps * 64)
+        return toks * (R * P * s + R * N * s + K * s + 2 * s) + state * (S - 1)
     raise KeyError(kernel)
 
 
@@ -60,13 +68,14 @@ def path_min_bytes(b, T, H, P, N, R, s=2):
 
 
 def output_useful_flops(b, T, H, P, N, R):
-    """Causal (s <= t) flops of the chunk-output kernel: C B^T and M x over
-    token pairs of a chunk, and the incoming-state product C H."""
+    """Useful (causal) MFMA flops of the output pass: C B^T and M x over token
+    pairs s <= t of a chunk, C H for the incoming state, and B^T x for the
+    state update."""
     total = 0
     for c in range(math.ceil(T / 64)):
         q = min(64, T - 64 * c)
         pairs = q * (q + 1) // 2
-        total += pairs * R * R * 2 * (N + P) + q * R * 2 * N * P
+        total += pairs * R * R * 2 * (N + P) + q * R * 2 * N * P * 2
     return total * b * H
 
 
@@ -127,8 +136,6 @@ def time_prefill(torch, mixer, inp, steps, warmup):
         ks, ke = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         total = 0.0
         for _ in range(reps):
-            if name == "state_scan":          # needs fresh chunk contributions each time
-                mixer.prefill_stage(mixer.capi.STAGES["chunk_state"], *args, None, st, y, ws)
             ks.record()
             mixer.prefill_stage(stage, *args, None, st, y, ws)
             ke.record()
@@ -255,7 +262,7 @@ def main():
     for k, v in pk.items():
         nb = kernel_bytes(k, b, T, H, P, N, R)
         kern[k] = {"avg_us": round(v * 1000, 2), "alg_bytes": nb,
-                   "gb_per_s": round(nb / (v / 1000) / 1e9, 1)}
+                   "gb_per_s": round(nb / (v / 1000) / 1e9, 1) if nb else None}
     dom = max(pk, key=pk.get)
     dom_bytes = kernel_bytes(dom, b, T, H, P, N, R)
     achieved = dom_bytes / (pk[dom] / 1000) / 1e9
@@ -264,7 +271,7 @@ def main():
     roofline = {"kernel": f"k_{dom}", "bound": "hbm", "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic,
-                "mfma_useful_tflops": round(flops / (pk["chunk_output"] / 1000) / 1e12, 2)}
+                "mfma_useful_tflops": round(flops / (pk["output"] / 1000) / 1e12, 2)}
     path_bytes = path_min_bytes(b, T, H, P, N, R)
 
     result = {
@@ -302,11 +309,12 @@ def main():
             "workload": c2["name"], "tokens_per_s": round(b2 * T2 / (ms2 / 1000), 1),
             "ms_per_call": round(ms2, 4),
             "kernels": {k: {"avg_us": round(v * 1000, 2),
-                            "gb_per_s": round(kernel_bytes(k, b2, T2, H2, P2, N2, R2) / (v / 1000) / 1e9, 1)}
+                            "gb_per_s": (round(kernel_bytes(k, b2, T2, H2, P2, N2, R2) / (v / 1000) / 1e9, 1)
+                                         if kernel_bytes(k, b2, T2, H2, P2, N2, R2) else None)}
                         for k, v in pk2.items()},
-            "chunk_output_mfma_useful_tflops": round(f2 / (pk2["chunk_output"] / 1000) / 1e12, 2),
-            "chunk_output_mfma_frac_of_peak": round(f2 / (pk2["chunk_output"] / 1000) / 1e12
-                                                    / BF16_MFMA_PEAK_TFLOPS, 4),
+            "output_mfma_useful_tflops": round(f2 / (pk2["output"] / 1000) / 1e12, 2),
+            "output_mfma_frac_of_peak": round(f2 / (pk2["output"] / 1000) / 1e12
+                                              / BF16_MFMA_PEAK_TFLOPS, 4),
             "path_frac_of_hbm_peak_at_min_bytes": round(
                 path_min_bytes(b2, T2, H2, P2, N2, R2) / (ms2 / 1000) / 1e9 / HBM_PEAK_GBS, 4),
         }

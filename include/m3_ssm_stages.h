@@ -2,26 +2,28 @@
  * m3_ssm_stages.h -- one stage of the chunked prefill at a time, for
  * measuring each kernel on its own (per-kernel time and bandwidth).
  *
- * m3_ssm_prefill (m3_ssm.h) enqueues four kernels in this order; together
- * they evaluate the chunkwise form of the SSD / masked-attention view of the
- * recurrence (Mamba-3 review, junhanzang.github.io, section 2.3 and section
- * 3.1.3, eq. (7); chunkwise algorithm on the "20.2 Mamba and S6" page,
- * sungeuns.github.io, section 2):
- *   M3_STAGE_CHUNK_COEF    per-chunk cumulative sum of log alpha = dt A, the
- *                          weights gamma_t and gamma_t + delta_{t+1}; folds the
- *                          carried state into the state entering chunk 0
- *   M3_STAGE_CHUNK_STATE   each chunk's own contribution to its end state and
- *                          its summed rotary angle (MFMA)
- *   M3_STAGE_STATE_SCAN    passes states from chunk to chunk; writes the
- *                          final carried state
- *   M3_STAGE_CHUNK_OUTPUT  intra-chunk masked contraction plus the incoming
- *                          state's contribution: y (MFMA)
- * Stage k reads what stages < k wrote into the workspace, so a full prefill is
- * the four stages in order with the same arguments.  Any single stage may be
- * enqueued again afterwards with the same arguments: CHUNK_COEF,
- * CHUNK_STATE and CHUNK_OUTPUT rewrite the same outputs; STATE_SCAN is not
- * repeatable on its own (it turns the chunk contributions into incoming
- * states in place) and must follow a CHUNK_STATE.
+ * m3_ssm_prefill (m3_ssm.h) evaluates the chunkwise form of the SSD /
+ * masked-attention view of the recurrence (Mamba-3 review,
+ * junhanzang.github.io, section 2.3 and section 3.1.3, eq. (7); chunkwise
+ * algorithm on the "20.2 Mamba and S6" page, sungeuns.github.io, section 2)
+ * with one persistent workgroup per (batch, head, segment of chunks) that
+ * passes the state from chunk to chunk on chip.  It enqueues, in order:
+ *   M3_STAGE_SEGMENT_STATE  when batch * heads is too small to fill the chip,
+ *                           every sequence is cut into segments and this
+ *                           pre-pass computes each segment's aggregate (its
+ *                           state from a zero start, summed log decay and
+ *                           rotary angle) and the carried state in its own
+ *                           frame; it enqueues nothing when there is one
+ *                           segment per sequence
+ *   M3_STAGE_OUTPUT         per segment: folds the aggregates before it into
+ *                           its starting state, then per chunk the decay and
+ *                           angle prefixes, the rotation of B and C, the
+ *                           intra-chunk masked contraction and the incoming-
+ *                           state term (MFMA), writing y; the last segment
+ *                           writes the final carried state
+ * The segmentation depends on the shape only.  Running the stages in order
+ * with the same arguments is a full prefill; either stage may be enqueued
+ * again afterwards with the same arguments and rewrites the same outputs.
  *
  * Arguments, ownership and errors are those of m3_ssm_prefill; an unknown
  * stage gives M3_ERR_INVALID_ARGUMENT.
@@ -36,10 +38,8 @@ extern "C" {
 #endif
 
 typedef enum {
-    M3_STAGE_CHUNK_COEF = 0,
-    M3_STAGE_CHUNK_STATE = 1,
-    M3_STAGE_STATE_SCAN = 2,
-    M3_STAGE_CHUNK_OUTPUT = 3
+    M3_STAGE_SEGMENT_STATE = 0,
+    M3_STAGE_OUTPUT = 1
 } m3_stage_t;
 
 m3_status_t m3_ssm_prefill_stage(int32_t stage, const m3_shape_t *shape, const void *x,

@@ -26,11 +26,9 @@ EXPORTED = ("m3_ssm_prefill_workspace_bytes", "m3_ssm_prefill", "m3_ssm_decode_s
             "m3_status_string", "m3_ssm_prefill_stage")
 
 # Stages of the prefill (include/m3_ssm_stages.h).
-M3_STAGE_CHUNK_COEF = 0
-M3_STAGE_CHUNK_STATE = 1
-M3_STAGE_STATE_SCAN = 2
-M3_STAGE_CHUNK_OUTPUT = 3
-STAGES = {"chunk_coef": 0, "chunk_state": 1, "state_scan": 2, "chunk_output": 3}
+M3_STAGE_SEGMENT_STATE = 0
+M3_STAGE_OUTPUT = 1
+STAGES = {"segment_state": 0, "output": 1}
 
 
 class m3_shape_t(ctypes.Structure):

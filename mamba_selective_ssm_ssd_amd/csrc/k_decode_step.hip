@@ -69,7 +69,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_step(const DecodeParams p) 
         const double ph = wrap_angle(double(p.phi[bh * K + tid]) +
                                      double(io<IO>::get(static_cast<const IO *>(p.theta) + bh * K + tid)));
         float sn, cs;
-        sincosf(float(ph), &sn, &cs);
+        sincos_wrapped(ph, &sn, &cs);
         cs_s[2 * tid] = cs;
         cs_s[2 * tid + 1] = sn;
         p.phi[bh * K + tid] = float(ph);

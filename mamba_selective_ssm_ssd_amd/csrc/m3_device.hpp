@@ -235,6 +235,43 @@ __device__ __forceinline__ double wrap_angle(double a) {
     return a - kTwoPi * floor((a + kPi) * (1.0 / kTwoPi));
 }
 
+// sin and cos of an angle already wrapped to [-pi, pi], fp64 arithmetic,
+// rounded to fp32.  Quadrant reduction x = q pi/2 + r (|r| <= pi/4, exact
+// enough in fp64 for |x| <= pi), then the Taylor series of sin r and cos r to
+// degree 17 and 18 (truncation below 1e-17 for |r| <= pi/4), and the
+// quadrant identities.  Small and branch-free, unlike a general-argument
+// library sincos.
+__device__ __forceinline__ void sincos_wrapped(double x, float *s_out, float *c_out) {
+    const double q = rint(x * (2.0 / kPi));
+    const double r = x - q * (kPi / 2.0);
+    const double r2 = r * r;
+    // sin r = r (1 - r2/3! (1 - r2/(4*5) (1 - r2/(6*7) (...))))
+    double sn = 1.0 - r2 * (1.0 / (16.0 * 17.0));
+    sn = 1.0 - r2 * (1.0 / (14.0 * 15.0)) * sn;
+    sn = 1.0 - r2 * (1.0 / (12.0 * 13.0)) * sn;
+    sn = 1.0 - r2 * (1.0 / (10.0 * 11.0)) * sn;
+    sn = 1.0 - r2 * (1.0 / (8.0 * 9.0)) * sn;
+    sn = 1.0 - r2 * (1.0 / (6.0 * 7.0)) * sn;
+    sn = 1.0 - r2 * (1.0 / (4.0 * 5.0)) * sn;
+    sn = 1.0 - r2 * (1.0 / (2.0 * 3.0)) * sn;
+    sn *= r;
+    // cos r = 1 - r2/2! (1 - r2/(3*4) (1 - r2/(5*6) (...)))
+    double cs = 1.0 - r2 * (1.0 / (17.0 * 18.0));
+    cs = 1.0 - r2 * (1.0 / (15.0 * 16.0)) * cs;
+    cs = 1.0 - r2 * (1.0 / (13.0 * 14.0)) * cs;
+    cs = 1.0 - r2 * (1.0 / (11.0 * 12.0)) * cs;
+    cs = 1.0 - r2 * (1.0 / (9.0 * 10.0)) * cs;
+    cs = 1.0 - r2 * (1.0 / (7.0 * 8.0)) * cs;
+    cs = 1.0 - r2 * (1.0 / (5.0 * 6.0)) * cs;
+    cs = 1.0 - r2 * (1.0 / (3.0 * 4.0)) * cs;
+    cs = 1.0 - r2 * 0.5 * cs;
+    const int qi = int(q) & 3;
+    const double s = qi == 0 ? sn : qi == 1 ? cs : qi == 2 ? -sn : -cs;
+    const double c = qi == 0 ? cs : qi == 1 ? -sn : qi == 2 ? -cs : sn;
+    *s_out = float(s);
+    *c_out = float(c);
+}
+
 // Rotation R(-phi) of a row pair: (u, v) -> (c u + s v, -s u + c v).
 __device__ __forceinline__ void rot_neg(float c, float s, float &u, float &v) {
     const float a = u, b = v;

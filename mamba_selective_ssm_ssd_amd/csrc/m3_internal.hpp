@@ -12,27 +12,26 @@ namespace m3 {
 struct PrefillParams {
     int64_t batch, T;
     int32_t H, P, N, R, K, nC; // K = N/2 rotation pairs, nC = ceil(T/64) chunks
+    int32_t S, cps;            // segments per sequence, chunks per segment
     // inputs (I/O dtype unless noted)
     const void *x, *dt, *lam, *theta, *B, *C;
     const float *A; // [H]
     void *y;
-    // initial carried state (read by the coefficient kernel only)
+    // initial carried state; read only by the first workgroup of a sequence
+    // (S == 1) or by the pre-pass (S > 1)
     int32_t has_init;
     const float *h0, *phi0, *prevB0;
     const void *prevx0;
-    // final carried state (written by the state-scan kernel only)
+    // final carried state; written only by the last segment's workgroup
     int32_t has_final;
     float *hT, *phiT, *prevBT;
     void *prevxT;
-    // workspace
-    float *ell;        // [b][H][T]   within-chunk inclusive cumsum of dt*A
-    float *gam;        // [b][H][T]   gamma_t = lam_t dt_t
-    float *wgt;        // [b][H][T]   gamma_t + delta_{t+1} (delta_T = 0)
-    float *ubuf;       // [b][H][nC][N][P]  chunk state, then incoming state
-    double *thetaC;    // [b][H][nC][K]     chunk angle totals
-    float2 *thetaCS;   // [b][H][nC][K]     (cos, sin) of the wrapped totals
-    float *hinit;      // [b][H][N][P]      incoming state of chunk 0
-    double *phi0ws;    // [b][H][K]         Phi_{-1}
+    // workspace (used when S > 1)
+    float *segU;    // [b][H][S][N][P]  segment aggregate: its state from a zero start
+    float *segG;    // [b][H][S]        summed log decay of the segment
+    double *segTh;  // [b][H][S][K]     summed rotary angle of the segment
+    float *hinit;   // [b][H][N][P]     carried state in its own frame at the sequence start
+    double *phi0ws; // [b][H][K]        Phi_{-1}
 };
 
 struct DecodeParams {
@@ -47,20 +46,24 @@ struct DecodeParams {
 
 // Workspace layout (byte offsets of each region, 256-byte aligned).
 struct WorkspaceLayout {
-    size_t ell, gam, wgt, ubuf, thetaC, thetaCS, hinit, phi0, total;
+    size_t segU, segG, segTh, hinit, phi0, total;
 };
 
-// Launchers: dispatch on (io dtype, N, P) and enqueue one kernel.
-// Return hipSuccess, or the launch error.  is_bf16 selects the I/O type.
-hipError_t launch_chunk_coef(const PrefillParams &p, bool is_bf16, hipStream_t s);
-hipError_t launch_chunk_state(const PrefillParams &p, bool is_bf16, hipStream_t s);
-hipError_t launch_state_scan(const PrefillParams &p, bool is_bf16, hipStream_t s);
-hipError_t launch_chunk_output(const PrefillParams &p, bool is_bf16, hipStream_t s);
+// Fused prefill launchers, one per (I/O type, N): out = false runs the
+// segment pre-pass (nothing to do when S == 1), out = true the output pass.
+hipError_t launch_prefill_bf16_n16(const PrefillParams &p, bool out, hipStream_t s);
+hipError_t launch_prefill_bf16_n32(const PrefillParams &p, bool out, hipStream_t s);
+hipError_t launch_prefill_bf16_n64(const PrefillParams &p, bool out, hipStream_t s);
+hipError_t launch_prefill_bf16_n128(const PrefillParams &p, bool out, hipStream_t s);
+hipError_t launch_prefill_f32_n16(const PrefillParams &p, bool out, hipStream_t s);
+hipError_t launch_prefill_f32_n32(const PrefillParams &p, bool out, hipStream_t s);
+hipError_t launch_prefill_f32_n64(const PrefillParams &p, bool out, hipStream_t s);
+hipError_t launch_prefill_f32_n128(const PrefillParams &p, bool out, hipStream_t s);
+
 hipError_t launch_decode_step(const DecodeParams &p, bool is_bf16, hipStream_t s);
 
-// Dynamic LDS bytes of the chunk kernels for a shape (0 if not compiled).
-size_t chunk_state_lds_bytes(bool is_bf16, int N, int P, int R);
-size_t chunk_output_lds_bytes(bool is_bf16, int N, int P, int R);
+// Dynamic LDS bytes of the fused prefill kernel for a shape (0: not compiled).
+size_t prefill_lds_bytes(bool is_bf16, int N, int P, int R);
 constexpr size_t kMaxLdsBytes = 160 * 1024; // LDS per workgroup on gfx950
 
 // Sizes handled by the compiled kernels.

@@ -1,16 +1,16 @@
 // m3_ssm.hip -- C ABI of the mixer: argument validation, workspace layout and
 // the launch sequence.  See include/m3_ssm.h for the contract.
 //
-// Prefill enqueues, on the caller's stream:
-//   1. k_chunk_coef    per-chunk cumsum of log alpha, gamma, trapezoid weights;
-//                      folds the carried state into the state entering chunk 0
-//   2. k_chunk_state   per-chunk state contribution U_c (MFMA), chunk angles
-//   3. k_state_scan    inter-chunk state passing; final carried state
-//   4. k_chunk_output  intra-chunk masked contraction + incoming state (MFMA)
-// Decode enqueues one k_decode_step.  m3_ssm_prefill_stage enqueues one of
-// the four prefill kernels alone (include/m3_ssm_stages.h).
+// Prefill enqueues, on the caller's stream, the fused chunked kernel
+// k_prefill (k_prefill.hpp): one persistent workgroup per (batch, head,
+// segment of chunks) that carries the state across its chunks on chip.  When
+// batch * heads is too small to fill the chip, each sequence is cut into S
+// segments and a pre-pass of the same kernel first computes every segment's
+// aggregate.  Decode enqueues one k_decode_step.  m3_ssm_prefill_stage
+// enqueues one of the two prefill kernels alone (include/m3_ssm_stages.h).
 #include "../../include/m3_ssm.h"
 #include "../../include/m3_ssm_stages.h"
+#include "k_prefill.hpp"
 #include "m3_internal.hpp"
 
 #include <limits>
@@ -44,29 +44,39 @@ m3_status_t check_shape(const m3_shape_t *s, bool decode) {
     const double elems = bh * T * double(s->rank) * double(s->dstate > s->headdim ? s->dstate : s->headdim);
     if (elems > 4.0e18) return M3_ERR_UNSUPPORTED;
     if (!decode) {
-        // the chunk kernels stage a whole chunk in LDS
-        const bool bf = s->io_dtype == M3_DTYPE_BF16;
-        const size_t a = m3::chunk_state_lds_bytes(bf, s->dstate, s->headdim, s->rank);
-        const size_t b = m3::chunk_output_lds_bytes(bf, s->dstate, s->headdim, s->rank);
-        if (a == 0 || b == 0 || a > m3::kMaxLdsBytes || b > m3::kMaxLdsBytes) return M3_ERR_UNSUPPORTED;
+        // the prefill kernel stages a whole chunk in LDS
+        const size_t lds = m3::prefill_lds_bytes(s->io_dtype == M3_DTYPE_BF16, s->dstate, s->headdim, s->rank);
+        if (lds == 0 || lds > m3::kMaxLdsBytes) return M3_ERR_UNSUPPORTED;
     }
     if (bh * ((T + 63.0) / 64.0) > double(std::numeric_limits<unsigned>::max()) / 2) return M3_ERR_UNSUPPORTED;
     return M3_OK;
 }
 
+// Workgroup slots the prefill aims to fill (MI355X has 256 compute units).
+constexpr int64_t kSlots = 256;
+
+// Segments per sequence: enough (batch, head, segment) workgroups to fill the
+// chip, never an empty segment.  Depends on the shape only.
+void segments(int64_t bh, int64_t T, int32_t &S, int32_t &cps) {
+    const int64_t nC = (T + 63) / 64;
+    int64_t s = bh >= kSlots ? 1 : kSlots / bh;
+    if (s > nC) s = nC;
+    if (s < 1) s = 1;
+    const int64_t c = (nC + s - 1) / s;
+    cps = int32_t(c);
+    S = int32_t((nC + c - 1) / c);
+}
+
 WorkspaceLayout layout(const m3_shape_t *s) {
     const size_t bh = size_t(s->batch) * size_t(s->nheads);
-    const size_t T = size_t(s->seqlen);
-    const size_t nC = (T + 63) / 64;
+    int32_t S, cps;
+    segments(int64_t(bh), s->seqlen, S, cps);
     const size_t N = size_t(s->dstate), P = size_t(s->headdim), K = N / 2;
     WorkspaceLayout w;
     size_t off = 0;
-    w.ell = off; off += round_up(bh * T * sizeof(float));
-    w.gam = off; off += round_up(bh * T * sizeof(float));
-    w.wgt = off; off += round_up(bh * T * sizeof(float));
-    w.ubuf = off; off += round_up(bh * nC * N * P * sizeof(float));
-    w.thetaC = off; off += round_up(bh * nC * K * sizeof(double));
-    w.thetaCS = off; off += round_up(bh * nC * K * sizeof(float) * 2);
+    w.segU = off; off += round_up(bh * S * N * P * sizeof(float));
+    w.segG = off; off += round_up(bh * S * sizeof(float));
+    w.segTh = off; off += round_up(bh * S * K * sizeof(double));
     w.hinit = off; off += round_up(bh * N * P * sizeof(float));
     w.phi0 = off; off += round_up(bh * K * sizeof(double));
     w.total = off;
@@ -79,6 +89,39 @@ bool state_ok(const m3_state_t *st) {
 }
 
 } // namespace
+
+namespace m3 {
+
+template <typename IO, int N>
+static size_t lds_np(int P, int R) {
+#define M3_LDS_R(PP)                                                                     \
+    switch (R) {                                                                         \
+    case 1: return Cfg<IO, N, PP, 1>::bytes;                                             \
+    case 2: return Cfg<IO, N, PP, 2>::bytes;                                             \
+    case 3: return Cfg<IO, N, PP, 3>::bytes;                                             \
+    case 4: return Cfg<IO, N, PP, 4>::bytes;                                             \
+    }                                                                                    \
+    return 0;
+    switch (P) {
+    case 16: M3_LDS_R(16)
+    case 32: M3_LDS_R(32)
+    case 64: M3_LDS_R(64)
+    }
+#undef M3_LDS_R
+    return 0;
+}
+
+size_t prefill_lds_bytes(bool is_bf16, int N, int P, int R) {
+    switch (N) {
+    case 16: return is_bf16 ? lds_np<bf16, 16>(P, R) : lds_np<float, 16>(P, R);
+    case 32: return is_bf16 ? lds_np<bf16, 32>(P, R) : lds_np<float, 32>(P, R);
+    case 64: return is_bf16 ? lds_np<bf16, 64>(P, R) : lds_np<float, 64>(P, R);
+    case 128: return is_bf16 ? lds_np<bf16, 128>(P, R) : lds_np<float, 128>(P, R);
+    }
+    return 0;
+}
+
+} // namespace m3
 
 extern "C" {
 
@@ -133,24 +176,24 @@ static m3_status_t prepare_prefill(const m3_shape_t *shape, const void *x, const
         p.hT = final_state->h; p.phiT = final_state->phi; p.prevBT = final_state->prev_B;
         p.prevxT = final_state->prev_x;
     }
+    segments(p.batch * p.H, p.T, p.S, p.cps);
     unsigned char *ws = static_cast<unsigned char *>(workspace);
-    p.ell = reinterpret_cast<float *>(ws + w.ell);
-    p.gam = reinterpret_cast<float *>(ws + w.gam);
-    p.wgt = reinterpret_cast<float *>(ws + w.wgt);
-    p.ubuf = reinterpret_cast<float *>(ws + w.ubuf);
-    p.thetaC = reinterpret_cast<double *>(ws + w.thetaC);
-    p.thetaCS = reinterpret_cast<float2 *>(ws + w.thetaCS);
+    p.segU = reinterpret_cast<float *>(ws + w.segU);
+    p.segG = reinterpret_cast<float *>(ws + w.segG);
+    p.segTh = reinterpret_cast<double *>(ws + w.segTh);
     p.hinit = reinterpret_cast<float *>(ws + w.hinit);
     p.phi0ws = reinterpret_cast<double *>(ws + w.phi0);
     return M3_OK;
 }
 
 static hipError_t launch_stage(int32_t stage, const PrefillParams &p, bool bf, hipStream_t stream) {
-    switch (stage) {
-    case M3_STAGE_CHUNK_COEF: return m3::launch_chunk_coef(p, bf, stream);
-    case M3_STAGE_CHUNK_STATE: return m3::launch_chunk_state(p, bf, stream);
-    case M3_STAGE_STATE_SCAN: return m3::launch_state_scan(p, bf, stream);
-    case M3_STAGE_CHUNK_OUTPUT: return m3::launch_chunk_output(p, bf, stream);
+    if (stage != M3_STAGE_SEGMENT_STATE && stage != M3_STAGE_OUTPUT) return hipErrorInvalidValue;
+    const bool out = stage == M3_STAGE_OUTPUT;
+    switch (p.N) {
+    case 16: return bf ? m3::launch_prefill_bf16_n16(p, out, stream) : m3::launch_prefill_f32_n16(p, out, stream);
+    case 32: return bf ? m3::launch_prefill_bf16_n32(p, out, stream) : m3::launch_prefill_f32_n32(p, out, stream);
+    case 64: return bf ? m3::launch_prefill_bf16_n64(p, out, stream) : m3::launch_prefill_f32_n64(p, out, stream);
+    case 128: return bf ? m3::launch_prefill_bf16_n128(p, out, stream) : m3::launch_prefill_f32_n128(p, out, stream);
     }
     return hipErrorInvalidValue;
 }
@@ -164,7 +207,7 @@ m3_status_t m3_ssm_prefill(const m3_shape_t *shape, const void *x, const void *d
                                            workspace, workspace_bytes, p);
     if (sc != M3_OK) return sc;
     const bool bf = shape->io_dtype == M3_DTYPE_BF16;
-    for (int32_t stage = M3_STAGE_CHUNK_COEF; stage <= M3_STAGE_CHUNK_OUTPUT; ++stage)
+    for (int32_t stage = M3_STAGE_SEGMENT_STATE; stage <= M3_STAGE_OUTPUT; ++stage)
         if (launch_stage(stage, p, bf, stream) != hipSuccess) return M3_ERR_HIP;
     return M3_OK;
 }
@@ -174,7 +217,7 @@ m3_status_t m3_ssm_prefill_stage(int32_t stage, const m3_shape_t *shape, const v
                                  const void *theta, const void *B, const void *C,
                                  const m3_state_t *init, m3_state_t *final_state, void *y,
                                  void *workspace, size_t workspace_bytes, hipStream_t stream) {
-    if (stage < M3_STAGE_CHUNK_COEF || stage > M3_STAGE_CHUNK_OUTPUT) return M3_ERR_INVALID_ARGUMENT;
+    if (stage != M3_STAGE_SEGMENT_STATE && stage != M3_STAGE_OUTPUT) return M3_ERR_INVALID_ARGUMENT;
     PrefillParams p;
     const m3_status_t sc = prepare_prefill(shape, x, dt, A, lam, theta, B, C, init, final_state, y,
                                            workspace, workspace_bytes, p);

@@ -50,9 +50,14 @@ def _shape(**kw):
 
 def test_workspace_bytes():
     ws = capi.m3_ssm_prefill_workspace_bytes(_shape())
-    bh, T, nC, N, P, K = 6, 100, 2, 64, 64, 32
-    at_least = 3 * bh * T * 4 + bh * nC * N * P * 4 + bh * nC * K * 16 + bh * N * P * 4 + bh * K * 8
-    assert at_least <= ws <= at_least + 8 * 256
+    # b2 T100 H3: 6 sequences of 2 chunks -> 2 segments of one chunk each
+    bh, S, N, P, K = 6, 2, 64, 64, 32
+    at_least = bh * S * N * P * 4 + bh * S * 4 + bh * S * K * 8 + bh * N * P * 4 + bh * K * 8
+    assert at_least <= ws <= at_least + 5 * 256
+    # one segment per sequence once batch * heads fills the chip
+    big = capi.m3_ssm_prefill_workspace_bytes(_shape(batch=4, nheads=64, seqlen=2048))
+    bh = 256
+    assert big <= bh * N * P * 4 * 2 + bh * (4 + K * 8 + K * 8) + 5 * 256
     # invalid or unsupported shapes report 0
     assert capi.m3_ssm_prefill_workspace_bytes(_shape(dstate=63)) == 0
     assert capi.m3_ssm_prefill_workspace_bytes(_shape(dstate=48)) == 0
@@ -60,9 +65,15 @@ def test_workspace_bytes():
     assert capi.m3_ssm_prefill_workspace_bytes(_shape(rank=5)) == 0
     assert capi.m3_ssm_prefill_workspace_bytes(_shape(chunk=32)) == 0
     assert capi.m3_ssm_prefill_workspace_bytes(_shape(seqlen=0)) == 0
-    # fp32 staging of a chunk at N=128, R>=3 does not fit in LDS
-    assert capi.m3_ssm_prefill_workspace_bytes(_shape(dstate=128, rank=3, io_dtype=capi.M3_DTYPE_F32)) == 0
-    assert capi.m3_ssm_prefill_workspace_bytes(_shape(dstate=128, rank=4)) > 0
+    # a whole fp32 chunk at N=128, R>=3 does not fit in LDS; every bf16 shape does
+    f32 = capi.M3_DTYPE_F32
+    assert capi.m3_ssm_prefill_workspace_bytes(_shape(dstate=128, rank=3, io_dtype=f32)) == 0
+    assert capi.m3_ssm_prefill_workspace_bytes(_shape(dstate=128, rank=2, io_dtype=f32)) > 0
+    assert capi.m3_ssm_prefill_workspace_bytes(_shape(io_dtype=f32)) > 0
+    for n in (16, 32, 64, 128):
+        for r in (1, 2, 3, 4):
+            for pd in (16, 32, 64):
+                assert capi.m3_ssm_prefill_workspace_bytes(_shape(dstate=n, rank=r, headdim=pd)) > 0
 
 
 def _prefill(shape, **over):
@@ -115,11 +126,11 @@ def test_stage_errors():
     need = capi.m3_ssm_prefill_workspace_bytes(_shape())
     args = dict(x=FAKE, dt=FAKE, A=FAKE, lam=FAKE, theta=FAKE, B=FAKE, C=FAKE, init=None,
                 final_state=None, y=FAKE, workspace=FAKE, workspace_bytes=need, stream=None)
-    for bad in (-1, 4, 100):
+    for bad in (-1, 2, 100):
         assert capi.m3_ssm_prefill_stage(bad, _shape(), **args) == capi.M3_ERR_INVALID_ARGUMENT
     args["workspace_bytes"] = need - 1
     assert capi.m3_ssm_prefill_stage(0, _shape(), **args) == capi.M3_ERR_WORKSPACE
-    assert capi.m3_ssm_prefill_stage(3, _shape(dstate=5), **args) == capi.M3_ERR_INVALID_ARGUMENT
+    assert capi.m3_ssm_prefill_stage(1, _shape(dstate=5), **args) == capi.M3_ERR_INVALID_ARGUMENT
 
 
 def test_decode_errors():

@@ -1,0 +1,85 @@
+"""Parity at the full workload sizes, in the launch configuration bench.py
+times (same shapes, bf16 I/O, fp32 state, chunk 64): the GPU runs the whole
+batch, the fp64 oracle recomputes a sample of (batch, head) instances one by
+one on the same inputs (drawn on the device with the seeded generator and
+copied to the host for the sample).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from mamba_selective_ssm_ssd_amd import synth
+from _helpers import TOL, slice_err
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+def _sample_inputs(inp, bi, hi):
+    d = {k: inp[k][bi:bi + 1, :, hi:hi + 1].float().cpu().numpy() for k in ("x", "dt", "lam", "theta", "B", "C")}
+    d["A"] = inp["A"][hi:hi + 1].cpu().numpy()
+    return d
+
+
+def _check_prefill(cfg, picks):
+    from mamba_selective_ssm_ssd_amd import mixer
+    c = synth.CONFIGS[cfg]
+    b, T, H, P, N, R = (c[k] for k in ("batch", "T", "H", "P", "N", "R"))
+    inp = synth.torch_inputs(b, T, H, P, N, R, io="bf16", seed=0)
+    y, st = mixer.prefill(*(inp[k] for k in ("x", "dt", "A", "lam", "theta", "B", "C")))
+    torch.cuda.synchronize()
+    for bi, hi in picks:
+        d = _sample_inputs(inp, bi, hi)
+        yr, hT, _ = oracle.run(d["x"], d["dt"], d["A"], d["lam"], d["theta"], d["B"], d["C"])
+        yg = y[bi:bi + 1, :, hi:hi + 1].double().cpu().numpy()
+        e = slice_err(yg, yr, (0, 2))
+        phiT = oracle.cumulative_angle(d["theta"])
+        hg = oracle.state_to_true(st.h[bi:bi + 1, hi:hi + 1].double().cpu().numpy(), phiT)
+        eh = slice_err(hg, hT, (0, 1))
+        print(f"cfg{cfg} (b={bi}, h={hi}): y err {e:.2e}, state err {eh:.2e}")
+        assert e <= TOL["bf16"] and eh <= TOL["bf16"]
+
+
+def test_siso_prefill_full_size():
+    _check_prefill(1, [(0, 0), (1, 17), (2, 40), (3, 63)])
+
+
+def test_mimo_prefill_full_size():
+    _check_prefill(2, [(0, 5), (1, 31), (3, 62)])
+
+
+def test_long_mimo_prefill_full_size():
+    _check_prefill(3, [(0, 0), (0, 37)])
+
+
+def test_mimo_decode_full_size():
+    """1000 consecutive decode steps of b256 H64 from an N(0, 0.1) state."""
+    from mamba_selective_ssm_ssd_amd import mixer
+    c = synth.CONFIGS[4]
+    b, steps, H, P, N, R = (c[k] for k in ("batch", "T", "H", "P", "N", "R"))
+    inp = synth.torch_inputs(steps, b, H, P, N, R, io="bf16", seed=4)   # step-major
+    st = mixer.State.zeros(b, H, N, P, R, torch.bfloat16)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(40)
+    st.h.copy_(torch.randn(st.h.shape, generator=g, device="cuda") * 0.1)
+    picks = [(0, 0), (77, 13), (255, 63)]
+    h0 = {pk: st.h[pk[0]:pk[0] + 1, pk[1]:pk[1] + 1].double().cpu().numpy() for pk in picks}
+    ys = {pk: [] for pk in picks}
+    for t in range(steps):
+        y = mixer.decode_step(inp["x"][t], inp["dt"][t], inp["A"], inp["lam"][t], inp["theta"][t],
+                              inp["B"][t], inp["C"][t], st)
+        for (bi, hi) in picks:
+            ys[(bi, hi)].append(y[bi, hi])
+    torch.cuda.synchronize()
+    for (bi, hi) in picks:
+        d = {k: inp[k][:, bi:bi + 1, hi:hi + 1].transpose(0, 1).float().cpu().numpy()
+             for k in ("x", "dt", "lam", "theta", "B", "C")}
+        d["A"] = inp["A"][hi:hi + 1].cpu().numpy()
+        yr, hT, _ = oracle.run(d["x"], d["dt"], d["A"], d["lam"], d["theta"], d["B"], d["C"], h0=h0[(bi, hi)])
+        yg = torch.stack(ys[(bi, hi)]).double().cpu().numpy()[None, :, None]
+        e = slice_err(yg, yr, (0, 2))
+        phiT = oracle.cumulative_angle(d["theta"])
+        hg = oracle.state_to_true(st.h[bi:bi + 1, hi:hi + 1].double().cpu().numpy(), phiT)
+        eh = slice_err(hg, hT, (0, 1))
+        print(f"decode (b={bi}, h={hi}): y err {e:.2e}, state err {eh:.2e}")
+        assert e <= TOL["bf16"] and eh <= TOL["bf16"]

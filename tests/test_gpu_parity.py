@@ -45,7 +45,7 @@ def test_cfg0_tiny_siso_fp32():
     (128, 64, 1, "bf16"),   # configuration 1 shape
     (64, 64, 4, "bf16"),    # configurations 2-4 shape
     (128, 64, 1, "f32"),
-    (64, 64, 4, "f32"),
+    (64, 64, 2, "f32"),
 ])
 def test_config_shapes_ragged(N, P, R, io):
     d = _inputs(2, 300, 3, P, N, R, io, seed=1)      # 5 chunks, ragged tail of 44
@@ -63,6 +63,23 @@ def test_tile_set(N, P, R):
             run_gpu_prefill(d, io)
         return
     _parity(d, io)
+
+
+@pytest.mark.parametrize("bh", [(8, 32), (5, 52)])
+def test_one_segment_per_sequence(bh):
+    """batch * heads >= 256: every sequence is one workgroup (no pre-pass);
+    (5, 52) = 260 workgroups is not a multiple of the 8 XCDs."""
+    b, H = bh
+    d = _inputs(b, 150, H, 32, 32, 2, "bf16", seed=3)
+    d["A"] *= 0.05
+    _parity(d, "bf16")
+
+
+def test_segmented_long_sequence():
+    """One sequence over many chunks and few heads: segments + pre-pass."""
+    d = _inputs(1, 1500, 2, 32, 64, 4, "bf16", seed=4)
+    d["A"] *= 0.01
+    _parity(d, "bf16")
 
 
 # --------------------------------------------------------------------------
