@@ -11,10 +11,10 @@
 // chunk ends (the "20.2 Mamba and S6" page, sungeuns.github.io, section 2).
 //
 // Per chunk c (tokens t0 .. t0+Tc-1, virtual rows v = s*R + r):
-//  a1  cumsum: ell_t = sum_{t0<=u<=t} dt_u A (one lane per token, wave scan),
+//  a1  cumsum: ell_t = sum_{t0<=u<=t} dt_u A (wave scan, lane = token),
 //      gam_t = lam_t dt_t, wgt_t = gam_t + delta_{t+1}, delta = (1-lam) dt,
 //      g_c = ell at the last token; angle prefix phi_t,k = sum theta (fp64
-//      wave scan, wrapped to [-pi, pi)) and the chunk total Theta_c,k.
+//      wave scans, wrapped to [-pi, pi)) and the chunk total Theta_c,k.
 //  a2  rotate: Bhat = R(-phi_t) B_t, Chat = R(-phi_t) C_t, i.e. the RoPE form
 //      relative to the chunk start.  The rotation accumulated before the chunk
 //      is carried by the state, which is kept in the frame of the chunk start.
@@ -32,11 +32,14 @@
 // from zero, summed log decay and angle) and each output workgroup folds the
 // aggregates of the segments before it into its starting state.
 //
-// Data layout: one workgroup of 512 threads (8 waves).  The next chunk's
-// inputs are loaded into registers while the current chunk computes.  LDS
-// holds the rotated B (row-major for S, transposed and scaled for the state
-// update), x transposed, the state H (bf16 or fp32, transposed) and the
-// angle table; the rotated C of a wave's 16-row blocks stays in registers.
+// Schedule: one workgroup of 512 threads (8 waves), two barriers per chunk.
+// While chunk c computes, the next chunk's B, x, C sit in registers (loaded
+// during c's staging) and the a1 prologue of chunk c+1 (wave-local DPP scans,
+// no barrier of its own) fills the second half of double-buffered prologue
+// tables.  LDS holds the rotated B (row-major for S, transposed and scaled
+// for the state update), x transposed, the state H (bf16 or fp32,
+// transposed) and the angle and coefficient tables; the rotated C of a wave's
+// 16-row blocks stays in registers.
 #pragma once
 
 #include "m3_device.hpp"
@@ -65,21 +68,21 @@ struct Cfg {
     static constexpr int NKS = N >= 32 ? N / 32 : 1;          // K-steps of 32 over N
     static constexpr int NT = N / 16, PT = P / 16, NTILE = NT * PT;
     static constexpr int TW = (NTILE + kPW - 1) / kPW;        // state tiles per wave
-    // 16-byte units of one chunk's inputs, and units per thread
-    static constexpr int URT = K * SZ / 16, UT = kQ * URT, UPT_T = (UT + kPT - 1) / kPT;
+    // 16-byte units of one chunk's B and x, and units per thread
     static constexpr int URB = N * SZ / 16, UB = V * URB, UPT_B = (UB + kPT - 1) / kPT;
     static constexpr int URX = P * SZ / 16, UX = V * URX, UPT_X = (UX + kPT - 1) / kPT;
     static constexpr int FU = 8 / EPU; // units per MFMA fragment (8 elements)
-    // blocked angle prefix: thread (k, blk), NB blocks of TPB tokens per pair
-    static constexpr int NB = kPT / K, TPB = kQ / NB;
-    static_assert(NB * TPB == kQ, "angle blocks");
-    // LDS layout, bytes
-    static constexpr size_t o_coef = 0;                       // ell, gam, wgt, scl [64] each
-    static constexpr size_t o_misc = o_coef + 4 * kQ * 4;     // g_c, delta_0
-    static constexpr size_t o_thc = o_misc + 64;              // float2 [K]: cos, sin Theta_c
-    static constexpr size_t o_ths = o_thc + size_t(K) * 8;    // double [K]: running angle
-    static constexpr size_t o_phi = o_ths + size_t(K) * 8;    // float [64][KP]
-    static constexpr size_t o_bs = align16(o_phi + size_t(kQ) * KP * 4);    // [V][NBP]
+    // prologue: the angle prefix is scanned per group of 8 pairs by one wave
+    // (lane = token); GU 16-byte units hold a group of one token
+    static constexpr int NG8 = K / 8, GU = 8 / EPU;
+    // LDS layout, bytes.  Prologue data is double-buffered: the prologue of
+    // chunk c+1 runs while chunk c computes.
+    static constexpr size_t o_coef = 0;                        // [2][4][64]: ell, gam, wgt, scl
+    static constexpr size_t o_misc = o_coef + 2 * 4 * kQ * 4;  // [2] g_c, [2] delta_0
+    static constexpr size_t o_thc = o_misc + 64;               // float2 [2][K]: cos, sin Theta_c
+    static constexpr size_t o_ths = o_thc + 2 * size_t(K) * 8; // double [K]: running angle
+    static constexpr size_t o_phi = o_ths + size_t(K) * 8;     // float [2][64][KP]
+    static constexpr size_t o_bs = align16(o_phi + 2 * size_t(kQ) * KP * 4); // [V][NBP]
     static constexpr size_t bst_bytes = size_t(N) * VP * sizeof(lds_t);     // [N][VP]
     static constexpr size_t rest_bytes = size_t(P) * VP * sizeof(lds_t) + size_t(P) * NBP * sizeof(lds_t);
     // The transposed, scaled copy of B (contiguous along v for the state
@@ -89,22 +92,24 @@ struct Cfg {
     static constexpr size_t o_bst = o_bs + size_t(V) * NBP * sizeof(lds_t);
     static constexpr size_t o_xt = o_bst + (BST ? bst_bytes : 0);            // [P][VP]
     static constexpr size_t o_ht = o_xt + size_t(P) * VP * sizeof(lds_t);   // [P][NBP]
-    // block sums of the angle prefix (double [NB][K]) live in the staging
-    // region of B and x, which is free between the end of a chunk's compute
-    // and its staging
-    static constexpr size_t o_blk = o_bs;
-    static constexpr size_t o_pro = o_blk + size_t(kPT) * 8;  // a [64], del [65] (prologue only)
-    static_assert(o_ht - o_bs >= size_t(kPT) * 8 + (2 * kQ + 4) * 4, "prologue data fits in the staging region");
     static constexpr size_t bytes = o_ht + size_t(P) * NBP * sizeof(lds_t);
-    static_assert(K * SZ % 16 == 0 && N % 16 == 0 && P % 16 == 0, "tile sizes");
+    static_assert(K * SZ % 16 == 0 && N % 16 == 0 && P % 16 == 0 && K % 8 == 0, "tile sizes");
+    static_assert(NG8 <= kPW, "angle groups per wave");
 };
 
-// Raw (undecoded) inputs of one chunk held in registers.
+// Raw (undecoded) B, x and C of one chunk held in registers.
 template <class C>
 struct RawChunk {
-    uint4 th[C::UPT_T], bb[C::UPT_B], xx[C::UPT_X];
+    uint4 bb[C::UPT_B], xx[C::UPT_X];
     uint4 cc[C::TBW][C::NKS][C::FU];
-    float dt, lam, deln;
+};
+
+// Raw prologue inputs of one chunk: a group of 8 rotation angles of this
+// lane's token (angle waves) or dt, lam of this lane's token (wave 0).
+template <class C>
+struct RawPro {
+    uint4 th[C::GU];
+    float dt, lam, dtn, lamn;
 };
 
 // Unpack one 16-byte unit into EPU floats.
@@ -130,9 +135,9 @@ __device__ __forceinline__ void st_unit(float *p, const float *v) {
     *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
 }
 __device__ __forceinline__ void st_one(uint16_t *p, float v) { *p = f32_to_bits(v); }
+__device__ __forceinline__ void st_one(float *p, float v) { *p = v; }
 __device__ __forceinline__ float lds_to_f32(uint16_t v) { return bits_to_f32(v); }
 __device__ __forceinline__ float lds_to_f32(float v) { return v; }
-__device__ __forceinline__ void st_one(float *p, float v) { *p = v; }
 // Four consecutive LDS elements.
 __device__ __forceinline__ void st_four(uint16_t *p, float a, float b, float c, float d) {
     *reinterpret_cast<uint2 *>(p) = make_uint2(pack2_bf16(a, b), pack2_bf16(c, d));
@@ -145,9 +150,9 @@ __device__ __forceinline__ void st_four(float *p, float a, float b, float c, flo
 // causal work of the two blocks balances across waves.
 __device__ __forceinline__ int wave_block(int i, int wave) { return i == 0 ? wave : 2 * kPW - 1 - wave; }
 
-// Loads chunk (b, h, t0 .. t0+Tc-1) into registers.  Addresses are a
-// uniform per-chunk base plus a 32-bit per-thread offset, so they stay in
-// scalar registers + one VGPR per load (saddr + voffset addressing).
+// Loads chunk (b, h, t0 .. t0+Tc-1)'s B, x and C into registers.  Addresses
+// are a uniform per-chunk base plus a 32-bit per-thread offset (saddr +
+// voffset addressing).
 template <class C, typename IO, bool OUT>
 __device__ __forceinline__ void load_chunk(const PrefillParams &p, int64_t b, int h, int64_t t0, int Tc,
                                            RawChunk<C> &r) {
@@ -156,19 +161,9 @@ __device__ __forceinline__ void load_chunk(const PrefillParams &p, int64_t b, in
     const uint4 z = make_uint4(0u, 0u, 0u, 0u);
     const int64_t tokbase = (b * p.T + t0) * p.H + h; // token-head index of t0
     const int H = p.H;
-    const IO *th = static_cast<const IO *>(p.theta) + tokbase * C::K;
     const IO *Bp = static_cast<const IO *>(p.B) + tokbase * (C::R * C::N);
     const IO *Xp = static_cast<const IO *>(p.x) + tokbase * (C::R * C::P);
     const IO *Cp = static_cast<const IO *>(p.C) + tokbase * (C::R * C::N);
-#pragma unroll
-    for (int j = 0; j < C::UPT_T; ++j) {
-        const int u = tid + j * kPT;
-        r.th[j] = z;
-        if (u < C::UT) {
-            const int tok = u / C::URT, q = u - tok * C::URT;
-            if (tok < Tc) r.th[j] = *reinterpret_cast<const uint4 *>(th + (tok * H * C::K + q * C::EPU));
-        }
-    }
 #pragma unroll
     for (int j = 0; j < C::UPT_B; ++j) {
         const int u = tid + j * kPT;
@@ -210,20 +205,84 @@ __device__ __forceinline__ void load_chunk(const PrefillParams &p, int64_t b, in
             }
         }
     }
+}
+
+// Loads the prologue inputs of chunk (b, h, t0 .. t0+Tc-1): wave w scans angle
+// group kPW-1-w (when there is one) and loads that group of its lane's token;
+// wave 0 loads dt and lam of its lane's token (and of token t0+64).
+template <class C, typename IO>
+__device__ __forceinline__ void load_pro(const PrefillParams &p, int64_t b, int h, int64_t t0, int Tc,
+                                         RawPro<C> &r) {
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int64_t tokbase = (b * p.T + t0) * p.H + h;
+    const int H = p.H;
+    const int grp = kPW - 1 - wave;
+    const IO *th = static_cast<const IO *>(p.theta) + tokbase * C::K;
+#pragma unroll
+    for (int f = 0; f < C::GU; ++f) {
+        r.th[f] = make_uint4(0u, 0u, 0u, 0u);
+        if (grp < C::NG8 && lane < Tc)
+            r.th[f] = *reinterpret_cast<const uint4 *>(th + (lane * H * C::K + 8 * grp + f * C::EPU));
+    }
+    r.dt = r.lam = r.dtn = r.lamn = 0.f;
     if (wave == 0) {
         const IO *dt = static_cast<const IO *>(p.dt) + tokbase;
         const IO *lam = static_cast<const IO *>(p.lam) + tokbase;
-        r.dt = 0.f;
-        r.lam = 0.f;
-        r.deln = 0.f;
         if (lane < Tc) {
             r.dt = io<IO>::get(dt + lane * H);
             r.lam = io<IO>::get(lam + lane * H);
         }
         if (lane == kWave - 1 && t0 + kQ < p.T) {
-            const float dn = io<IO>::get(dt + kQ * H);
-            const float ln = io<IO>::get(lam + kQ * H);
-            r.deln = (1.f - ln) * dn;
+            r.dtn = io<IO>::get(dt + kQ * H);
+            r.lamn = io<IO>::get(lam + kQ * H);
+        }
+    }
+}
+
+// a1 for one chunk from its raw prologue inputs, into one prologue buffer:
+// the angle table phi[t][k] (wrapped, fp32), the chunk rotation (cos, sin of
+// Theta_c) and the running fp64 angle; the coefficient table and g_c.  Every
+// scan is wave-local (DPP, lane = token), so no barrier is needed here.
+template <class C, typename IO>
+__device__ __forceinline__ void run_pro(const RawPro<C> &r, int Tc, int64_t t0, int64_t T, float A,
+                                        float *phi, float *coef, float *misc, float2 *thc, double *ths) {
+    constexpr int KP = C::KP, EPU = C::EPU;
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int grp = kPW - 1 - wave;
+    if (grp < C::NG8) {
+        float th[8];
+#pragma unroll
+        for (int f = 0; f < C::GU; ++f) unpack_unit(r.th[f], th + f * EPU, IO());
+        double v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = wave_scan_dpp(double(th[j]));
+#pragma unroll
+        for (int j = 0; j < 8; ++j) phi[lane * KP + 8 * grp + j] = float(wrap_angle(v[j]));
+        if (lane == kWave - 1) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                float sn, cs;
+                sincos_wrapped(wrap_angle(v[j]), &sn, &cs);
+                thc[8 * grp + j] = make_float2(cs, sn);
+                ths[8 * grp + j] += v[j];
+            }
+        }
+    }
+    if (wave == 0) {
+        const float ell = wave_scan_dpp(r.dt * A);
+        const float gam = r.lam * r.dt, del = (1.f - r.lam) * r.dt;
+        float dn = __shfl_down(del, 1, kWave);
+        if (lane == kWave - 1) dn = (1.f - r.lamn) * r.dtn;
+        if (t0 + lane + 1 >= T) dn = 0.f;
+        const float w = gam + dn;
+        const float gc = __shfl(ell, Tc - 1, kWave);
+        coef[lane] = ell;
+        coef[kQ + lane] = gam;
+        coef[2 * kQ + lane] = w;
+        coef[3 * kQ + lane] = lane < Tc ? __expf(gc - ell) * w : 0.f;
+        if (lane == 0) {
+            misc[0] = gc;
+            misc[2] = del;
         }
     }
 }
@@ -283,14 +342,11 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
     const int c_end = min(p.nC, c_begin + p.cps);
 
     extern __shared__ __align__(16) unsigned char smem[];
-    float *ell_s = reinterpret_cast<float *>(smem + C::o_coef);
-    float *gam_s = ell_s + kQ, *wgt_s = gam_s + kQ, *scl_s = wgt_s + kQ;
-    float *a_s = reinterpret_cast<float *>(smem + C::o_pro), *del_s = a_s + kQ;
-    double *blk_s = reinterpret_cast<double *>(smem + C::o_blk);
-    float *misc_s = reinterpret_cast<float *>(smem + C::o_misc);
-    float2 *thc_s = reinterpret_cast<float2 *>(smem + C::o_thc);
-    double *ths_s = reinterpret_cast<double *>(smem + C::o_ths);
-    float *phi_s = reinterpret_cast<float *>(smem + C::o_phi);
+    float *coef_s = reinterpret_cast<float *>(smem + C::o_coef);  // [2][4][64]
+    float *misc_s = reinterpret_cast<float *>(smem + C::o_misc);  // g_c [2], delta_0 [2]
+    float2 *thc_s = reinterpret_cast<float2 *>(smem + C::o_thc);  // [2][K]
+    double *ths_s = reinterpret_cast<double *>(smem + C::o_ths);  // [K]
+    float *phi_s = reinterpret_cast<float *>(smem + C::o_phi);    // [2][64][KP]
     lds_t *bs = reinterpret_cast<lds_t *>(smem + C::o_bs);
     lds_t *bst = reinterpret_cast<lds_t *>(smem + C::o_bst);
     lds_t *xt = reinterpret_cast<lds_t *>(smem + C::o_xt);
@@ -310,91 +366,27 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
     for (int j = 0; j < C::TW; ++j) st[j] = floatx4{0.f, 0.f, 0.f, 0.f};
     float gsum = 0.f;
     const float Ah = p.A[h];
+    auto tc_of = [&](int c) { return int(min<int64_t>(kQ, p.T - int64_t(c) * kQ)); };
 
+    // prologue of the first chunk, then its B, x, C and the next prologue inputs
+    RawPro<C> rp;
+    load_pro<C, IO>(p, b, h, int64_t(c_begin) * kQ, tc_of(c_begin), rp);
     RawChunk<C> raw;
-    {
-        const int64_t t0 = int64_t(c_begin) * kQ;
-        load_chunk<C, IO, OUT>(p, b, h, t0, int(min<int64_t>(kQ, p.T - t0)), raw);
-    }
+    load_chunk<C, IO, OUT>(p, b, h, int64_t(c_begin) * kQ, tc_of(c_begin), raw);
+    __syncthreads(); // ths_s initialised
+    run_pro<C, IO>(rp, tc_of(c_begin), int64_t(c_begin) * kQ, p.T, Ah, phi_s, coef_s, misc_s, thc_s, ths_s);
+    if (c_begin + 1 < c_end)
+        load_pro<C, IO>(p, b, h, int64_t(c_begin + 1) * kQ, tc_of(c_begin + 1), rp);
+    __syncthreads();
 
     for (int c = c_begin; c < c_end; ++c) {
         const int64_t t0 = int64_t(c) * kQ;
-        const int Tc = int(min<int64_t>(kQ, p.T - t0));
-
-        // ---- (1) theta to LDS; a1: decay and trapezoid coefficients (wave 0)
-#pragma unroll
-        for (int j = 0; j < C::UPT_T; ++j) {
-            const int u = tid + j * kPT;
-            if (u < C::UT) {
-                const int tok = u / C::URT, q = u - tok * C::URT;
-                float v[EPU];
-                unpack_unit(raw.th[j], v, IO());
-#pragma unroll
-                for (int e = 0; e < EPU; ++e) phi_s[tok * KP + q * EPU + e] = v[e];
-            }
-        }
-        if (wave == 0) {
-            const float d = raw.dt, l = raw.lam;
-            a_s[lane] = d * Ah;
-            gam_s[lane] = l * d;
-            const float del = (1.f - l) * d;
-            del_s[lane] = del;
-            if (lane == kWave - 1) del_s[kQ] = raw.deln; // first token of the next chunk
-        }
-        __syncthreads();
-
-        // ---- a1: within-chunk prefix sums.  Rotary angles in fp64, blocked:
-        // thread (k, blk) scans its TPB tokens serially, block totals go
-        // through LDS.  Log decay in fp32 by wave 0 (lane = token).
-        double loc[C::TPB];
-        const int ak = tid % K, ablk = tid / K;
-        {
-            double acc = 0.0;
-#pragma unroll
-            for (int i = 0; i < C::TPB; ++i) {
-                acc += double(phi_s[(ablk * C::TPB + i) * KP + ak]);
-                loc[i] = acc;
-            }
-            blk_s[ablk * K + ak] = acc;
-        }
-        if (wave == 0) {
-            float ell = 0.f;
-#pragma unroll
-            for (int m = 0; m < kQ / 4; ++m) {
-                const float4 a4 = *reinterpret_cast<const float4 *>(a_s + 4 * m);
-                ell += (4 * m + 0 <= lane ? a4.x : 0.f);
-                ell += (4 * m + 1 <= lane ? a4.y : 0.f);
-                ell += (4 * m + 2 <= lane ? a4.z : 0.f);
-                ell += (4 * m + 3 <= lane ? a4.w : 0.f);
-            }
-            const float gc = __shfl(ell, Tc - 1, kWave);
-            float dn = lane + 1 < kQ ? del_s[lane + 1] : del_s[kQ];
-            if (t0 + lane + 1 >= p.T) dn = 0.f;
-            const float w = gam_s[lane] + dn;
-            ell_s[lane] = ell;
-            wgt_s[lane] = w;
-            scl_s[lane] = lane < Tc ? __expf(gc - ell) * w : 0.f;
-            if (lane == 0) {
-                misc_s[0] = gc;
-                misc_s[1] = del_s[0];
-            }
-        }
-        __syncthreads();
-        {
-            double off = 0.0;
-            for (int b2 = 0; b2 < ablk; ++b2) off += blk_s[b2 * K + ak];
-#pragma unroll
-            for (int i = 0; i < C::TPB; ++i)
-                phi_s[(ablk * C::TPB + i) * KP + ak] = float(wrap_angle(off + loc[i]));
-            if (ablk == C::NB - 1) {
-                const double tot = off + loc[C::TPB - 1];
-                float sn, cs;
-                sincos_wrapped(wrap_angle(tot), &sn, &cs);
-                thc_s[ak] = make_float2(cs, sn);
-                ths_s[ak] += tot;
-            }
-        }
-        __syncthreads();
+        const int Tc = tc_of(c);
+        const int buf = (c - c_begin) & 1;
+        const float *phb = phi_s + buf * (kQ * KP);
+        const float *ell_s = coef_s + buf * (4 * kQ);
+        const float *gam_s = ell_s + kQ, *wgt_s = gam_s + kQ, *scl_s = wgt_s + kQ;
+        const float2 *thcb = thc_s + buf * K;
 
         // ---- a2: rotate B and C, stage B, x in LDS; C fragments to registers
 #pragma unroll
@@ -409,13 +401,13 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
 #pragma unroll
                     for (int pp = 0; pp < EPU / 2; ++pp) {
                         float sn, cs;
-                        __sincosf(phi_s[tok * KP + q * (EPU / 2) + pp], &sn, &cs);
+                        __sincosf(phb[tok * KP + q * (EPU / 2) + pp], &sn, &cs);
                         rot_neg(cs, sn, e[2 * pp], e[2 * pp + 1]);
                     }
                 }
                 st_unit(bs + v * NBP + q * EPU, e);
                 if (C::BST) {
-                    const float sc = tok < Tc ? scl_s[tok] : 0.f;
+                    const float sc = scl_s[tok];
 #pragma unroll
                     for (int ee = 0; ee < EPU; ++ee) st_one(bst + (q * EPU + ee) * VP + v, e[ee] * sc);
                 }
@@ -448,7 +440,7 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
 #pragma unroll
                         for (int pp = 0; pp < 4; ++pp) {
                             float sn, cs;
-                            __sincosf(phi_s[tok * KP + n0 / 2 + pp], &sn, &cs);
+                            __sincosf(phb[tok * KP + n0 / 2 + pp], &sn, &cs);
                             rot_neg(cs, sn, e[2 * pp], e[2 * pp + 1]);
                         }
                     }
@@ -459,7 +451,7 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
 
         // state at the start of this workgroup's first chunk
         if (c == c_begin) {
-            const float del0 = misc_s[1];
+            const float del0 = misc_s[2];
 #pragma unroll
             for (int j = 0; j < C::TW; ++j) {
                 const int tile = wave + kPW * j;
@@ -503,13 +495,10 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
         }
 
         // prefetch the next chunk while this one computes
-        if (c + 1 < c_end) {
-            const int64_t t1 = t0 + kQ;
-            load_chunk<C, IO, OUT>(p, b, h, t1, int(min<int64_t>(kQ, p.T - t1)), raw);
-        }
+        if (c + 1 < c_end) load_chunk<C, IO, OUT>(p, b, h, t0 + kQ, tc_of(c + 1), raw);
         __syncthreads();
 
-        const float gc = misc_s[0];
+        const float gc = misc_s[buf];
         if (OUT) {
             // ---- a3 + a5: y = M x + exp(ell) Chat H for this wave's row blocks
             IO *ybase = static_cast<IO *>(p.y) + ((b * p.T + t0) * p.H + h) * (R * P);
@@ -619,13 +608,21 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
                 }
 #pragma unroll
                 for (int q = 0; q < 2; ++q) {
-                    const float2 cs = thc_s[8 * nt + 2 * g + q];
+                    const float2 cs = thcb[8 * nt + 2 * g + q];
                     st[j][2 * q] = cs.x * acc[2 * q] - cs.y * acc[2 * q + 1];
                     st[j][2 * q + 1] = cs.y * acc[2 * q] + cs.x * acc[2 * q + 1];
                 }
             }
         }
         gsum += gc;
+
+        // ---- a1 of the next chunk into the other prologue buffer
+        if (c + 1 < c_end) {
+            const int nb = buf ^ 1;
+            run_pro<C, IO>(rp, tc_of(c + 1), t0 + kQ, p.T, Ah, phi_s + nb * (kQ * KP), coef_s + nb * (4 * kQ),
+                           misc_s + nb, thc_s + nb * K, ths_s);
+            if (c + 2 < c_end) load_pro<C, IO>(p, b, h, t0 + 2 * kQ, tc_of(c + 2), rp);
+        }
         __syncthreads();
 
         if (OUT) {

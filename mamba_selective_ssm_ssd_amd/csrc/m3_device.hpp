@@ -230,6 +230,37 @@ __device__ __forceinline__ double wave_inclusive_sum(double v, int lane) {
     return v;
 }
 
+// Wave-wide inclusive prefix sums with DPP lane moves (no LDS): Hillis-Steele
+// within each row of 16 lanes (row_shr 1, 2, 4, 8; lanes shifted in from
+// outside the row read 0), then row 0's total into row 1 and row 2's into
+// row 3 (row_bcast:15), then the total of rows 0-1 into rows 2-3
+// (row_bcast:31).
+template <int CTRL, int ROW_MASK, bool BOUND_ZERO>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), CTRL, ROW_MASK, 0xf, BOUND_ZERO));
+}
+template <int CTRL, int ROW_MASK, bool BOUND_ZERO>
+__device__ __forceinline__ float dpp_add(float v) {
+    return v + __uint_as_float(dpp_u32<CTRL, ROW_MASK, BOUND_ZERO>(__float_as_uint(v)));
+}
+template <int CTRL, int ROW_MASK, bool BOUND_ZERO>
+__device__ __forceinline__ double dpp_add(double v) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = dpp_u32<CTRL, ROW_MASK, BOUND_ZERO>(uint32_t(u));
+    const uint32_t hi = dpp_u32<CTRL, ROW_MASK, BOUND_ZERO>(uint32_t(u >> 32));
+    return v + __builtin_bit_cast(double, (uint64_t(hi) << 32) | lo);
+}
+template <typename T>
+__device__ __forceinline__ T wave_scan_dpp(T v) {
+    v = dpp_add<0x111, 0xf, true>(v);  // row_shr:1
+    v = dpp_add<0x112, 0xf, true>(v);  // row_shr:2
+    v = dpp_add<0x114, 0xf, true>(v);  // row_shr:4
+    v = dpp_add<0x118, 0xf, true>(v);  // row_shr:8
+    v = dpp_add<0x142, 0xa, false>(v); // row_bcast:15 -> rows 1, 3
+    v = dpp_add<0x143, 0xc, false>(v); // row_bcast:31 -> rows 2, 3
+    return v;
+}
+
 // Angle wrapped to [-pi, pi), fp64.
 __device__ __forceinline__ double wrap_angle(double a) {
     return a - kTwoPi * floor((a + kPi) * (1.0 / kTwoPi));

@@ -134,7 +134,8 @@ def test_s2_split_prefill(io, T1):
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 def test_s2_prefill_then_decode(io):
     from mamba_selective_ssm_ssd_amd import mixer
-    b, T, H, P, N, R = 2, 150, 3, 64, 64, 4
+    b, T, H, P, N = 2, 150, 3, 64, 64
+    R = 4 if io == "bf16" else 3          # fp32 staging of R = 4 at N = P = 64 exceeds LDS
     d = _inputs(b, T, H, P, N, R, io, seed=10)
     d["A"] *= 0.05
     yr, hT, phiT = run_oracle(d)
@@ -196,7 +197,7 @@ def test_s3_extremes(case):
 @pytest.mark.parametrize("T", [1, 2, 63, 64, 65])
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 def test_s4_short_sequences(T, io):
-    d = _inputs(2, T, 3, 64, 64, 4, io, seed=13)
+    d = _inputs(2, T, 3, 64, 64, 4 if io == "bf16" else 3, io, seed=13)
     _parity(d, io)
 
 
@@ -269,7 +270,7 @@ def test_gpu_p8_impulse():
 # Structure: MIMO with one live channel equals SISO; determinism; canaries.
 # --------------------------------------------------------------------------
 def test_mimo_single_live_channel_equals_siso():
-    d4 = _inputs(1, 200, 2, 64, 64, 4, "f32", seed=17)
+    d4 = _inputs(1, 200, 2, 64, 32, 4, "f32", seed=17)
     for k in ("x", "B", "C"):
         d4[k][:, :, :, 1:] = 0.0
     d1 = dict(d4)
