@@ -14,7 +14,8 @@
 //  a1  cumsum: ell_t = sum_{t0<=u<=t} dt_u A (wave scan, lane = token),
 //      gam_t = lam_t dt_t, wgt_t = gam_t + delta_{t+1}, delta = (1-lam) dt,
 //      g_c = ell at the last token; angle prefix phi_t,k = sum theta (fp64
-//      wave scans, wrapped to [-pi, pi)) and the chunk total Theta_c,k.
+//      wave scans, wrapped to [-pi, pi)) turned into a cos/sin table, and
+//      the chunk total Theta_c,k.
 //  a2  rotate: Bhat = R(-phi_t) B_t, Chat = R(-phi_t) C_t, i.e. the RoPE form
 //      relative to the chunk start.  The rotation accumulated before the chunk
 //      is carried by the state, which is kept in the frame of the chunk start.
@@ -35,11 +36,13 @@
 // Schedule: one workgroup of 512 threads (8 waves), two barriers per chunk.
 // While chunk c computes, the next chunk's B, x, C sit in registers (loaded
 // during c's staging) and the a1 prologue of chunk c+1 (wave-local DPP scans,
-// no barrier of its own) fills the second half of double-buffered prologue
-// tables.  LDS holds the rotated B (row-major for S, transposed and scaled
-// for the state update), x transposed, the state H (bf16 or fp32,
-// transposed) and the angle and coefficient tables; the rotated C of a wave's
-// 16-row blocks stays in registers.
+// no barrier of its own) fills the cos/sin table and the second half of the
+// double-buffered coefficient tables.  LDS holds the rotated B, x and the
+// scaled x row-major (16-byte stores, no transposed writes), the state H
+// (transposed), and the tables; operands whose contraction index is the LDS
+// row (x for M x, Bhat and scaled x for the state update) are read with the
+// transposing LDS load.  The rotated C of a wave's 16-row blocks stays in
+// registers.  bf16 I/O stages one bf16 plane per value, fp32 I/O two (hi, lo).
 #pragma once
 
 #include "m3_device.hpp"
@@ -54,15 +57,15 @@ constexpr size_t align16(size_t v) { return (v + 15) / 16 * 16; }
 
 template <typename IO, int N_, int P_, int R_>
 struct Cfg {
-    static constexpr int N = N_, P = P_, R = R_, K = N / 2, KP = K + 1, V = kQ * R;
-    typedef Mma<mode<IO>::f32> M;
-    typedef typename M::lds_t lds_t;
+    static constexpr int N = N_, P = P_, R = R_, K = N / 2, V = kQ * R;
+    static constexpr int PL = mode<IO>::f32 ? 2 : 1;          // bf16 planes per staged value
+    typedef Mma<PL> M;
     typedef typename M::frag frag;
     static constexpr int SZ = int(sizeof(IO));
     static constexpr int EPU = 16 / SZ;                       // I/O elements per 16-byte unit
-    static constexpr int PADE = 16 / int(sizeof(lds_t));      // 16 bytes of row padding
-    static constexpr int NBP = N + PADE;                      // row pitch of bs, ht
-    static constexpr int VP = V + PADE;                       // row pitch of bst, xt
+    static constexpr int NBP = N + 8;                         // row pitch of bs, ht (elements)
+    static constexpr int PP = P + 8;                          // row pitch of xr, xs (elements)
+    static constexpr int CSP = 2 * K + 4;                     // row pitch of the cos/sin table (floats)
     static constexpr int NTB = V / 16;                        // 16-row blocks of virtual rows
     static constexpr int TBW = NTB > kPW ? 2 : 1;             // blocks per wave
     static constexpr int NKS = N >= 32 ? N / 32 : 1;          // K-steps of 32 over N
@@ -75,26 +78,34 @@ struct Cfg {
     // prologue: the angle prefix is scanned per group of 8 pairs by one wave
     // (lane = token); GU 16-byte units hold a group of one token
     static constexpr int NG8 = K / 8, GU = 8 / EPU;
-    // LDS layout, bytes.  Prologue data is double-buffered: the prologue of
-    // chunk c+1 runs while chunk c computes.
-    static constexpr size_t o_coef = 0;                        // [2][4][64]: ell, gam, wgt, scl
-    static constexpr size_t o_misc = o_coef + 2 * 4 * kQ * 4;  // [2] g_c, [2] delta_0
-    static constexpr size_t o_thc = o_misc + 64;               // float2 [2][K]: cos, sin Theta_c
-    static constexpr size_t o_ths = o_thc + 2 * size_t(K) * 8; // double [K]: running angle
-    static constexpr size_t o_phi = o_ths + size_t(K) * 8;     // float [2][64][KP]
-    static constexpr size_t o_bs = align16(o_phi + 2 * size_t(kQ) * KP * 4); // [V][NBP]
-    static constexpr size_t bst_bytes = size_t(N) * VP * sizeof(lds_t);     // [N][VP]
-    static constexpr size_t rest_bytes = size_t(P) * VP * sizeof(lds_t) + size_t(P) * NBP * sizeof(lds_t);
-    // The transposed, scaled copy of B (contiguous along v for the state
-    // update) is kept when it fits; otherwise that operand is gathered from
-    // the row-major copy.
-    static constexpr bool BST = o_bs + size_t(V) * NBP * sizeof(lds_t) + bst_bytes + rest_bytes <= kMaxLdsBytes;
-    static constexpr size_t o_bst = o_bs + size_t(V) * NBP * sizeof(lds_t);
-    static constexpr size_t o_xt = o_bst + (BST ? bst_bytes : 0);            // [P][VP]
-    static constexpr size_t o_ht = o_xt + size_t(P) * VP * sizeof(lds_t);   // [P][NBP]
-    static constexpr size_t bytes = o_ht + size_t(P) * NBP * sizeof(lds_t);
+    // Angle groups go to the waves that own no intra-chunk row block when
+    // there are such waves (R = 1), GPW groups each; otherwise wave w takes
+    // group kPW - 1 - w.
+    static constexpr int FREEW = NTB < kPW ? kPW - NTB : 0;
+    static constexpr int GPW = FREEW ? (NG8 + FREEW - 1) / FREEW : 1;
+    // plane strides (elements) of the staged arrays
+    static constexpr int BS_PS = V * NBP, X_PS = V * PP, HT_PS = P * NBP;
+    // LDS layout, bytes.  The MFMA operands come first so that their offsets
+    // fit the LDS instructions' immediate field.  The cos/sin table is written
+    // by the prologue of chunk c+1 after chunk c's staging has read it; the
+    // coefficient and chunk-rotation tables are read while the next prologue
+    // runs, so they are double-buffered.
+    static constexpr size_t o_bs = 0;                                          // [PL][V][NBP]
+    static constexpr size_t o_xr = o_bs + size_t(PL) * BS_PS * 2;              // [PL][V][PP]
+    static constexpr size_t o_ht = o_xr + size_t(PL) * X_PS * 2;               // [PL][P][NBP]
+    static constexpr size_t o_cs = o_ht + size_t(PL) * HT_PS * 2;              // float [64][CSP]
+    static constexpr size_t o_coef = o_cs + size_t(kQ) * CSP * 4;              // [2][4][64]: ell, gam, wgt, scl
+    static constexpr size_t o_misc = o_coef + 2 * 4 * kQ * 4;                  // [2] g_c, [2] delta_0
+    static constexpr size_t o_thc = o_misc + 64;                               // float2 [2][K]: cos, sin Theta_c
+    static constexpr size_t o_ths = o_thc + 2 * size_t(K) * 8;                 // double [K]: running angle
+    static constexpr size_t o_xs = align16(o_ths + size_t(K) * 8);             // [PL][V][PP] scaled x
+    static constexpr size_t xs_bytes = size_t(PL) * X_PS * 2;
+    // The scaled copy of x (the state update's second operand) is kept when
+    // it fits; otherwise the scale is applied to that operand's fragments.
+    static constexpr bool XS = o_xs + xs_bytes <= kMaxLdsBytes;
+    static constexpr size_t bytes = o_xs + (XS ? xs_bytes : 0);
     static_assert(K * SZ % 16 == 0 && N % 16 == 0 && P % 16 == 0 && K % 8 == 0, "tile sizes");
-    static_assert(NG8 <= kPW, "angle groups per wave");
+    static_assert(FREEW ? NG8 <= FREEW * GPW : NG8 <= kPW, "angle groups per wave");
 };
 
 // Raw (undecoded) B, x and C of one chunk held in registers.
@@ -108,9 +119,18 @@ struct RawChunk {
 // lane's token (angle waves) or dt, lam of this lane's token (wave 0).
 template <class C>
 struct RawPro {
-    uint4 th[C::GU];
+    uint4 th[C::GPW][C::GU];
     float dt, lam, dtn, lamn;
 };
+
+// Angle group m (< GPW) scanned by a wave, or -1.
+template <class C>
+__device__ __forceinline__ int pro_group(int wave, int m) {
+    int grp;
+    if (C::FREEW) grp = wave >= C::NTB ? wave - C::NTB + m * C::FREEW : -1;
+    else grp = m == 0 ? kPW - 1 - wave : -1;
+    return grp >= 0 && grp < C::NG8 ? grp : -1;
+}
 
 // Unpack one 16-byte unit into EPU floats.
 __device__ __forceinline__ void unpack_unit(const uint4 &u, float *v, bf16) {
@@ -124,26 +144,6 @@ __device__ __forceinline__ void unpack_unit(const uint4 &u, float *v, bf16) {
 __device__ __forceinline__ void unpack_unit(const uint4 &u, float *v, float) {
     v[0] = __uint_as_float(u.x); v[1] = __uint_as_float(u.y);
     v[2] = __uint_as_float(u.z); v[3] = __uint_as_float(u.w);
-}
-
-// Store EPU floats as consecutive LDS elements (one 16-byte store).
-__device__ __forceinline__ void st_unit(uint16_t *p, const float *v) {
-    *reinterpret_cast<uint4 *>(p) = make_uint4(pack2_bf16(v[0], v[1]), pack2_bf16(v[2], v[3]),
-                                               pack2_bf16(v[4], v[5]), pack2_bf16(v[6], v[7]));
-}
-__device__ __forceinline__ void st_unit(float *p, const float *v) {
-    *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
-}
-__device__ __forceinline__ void st_one(uint16_t *p, float v) { *p = f32_to_bits(v); }
-__device__ __forceinline__ void st_one(float *p, float v) { *p = v; }
-__device__ __forceinline__ float lds_to_f32(uint16_t v) { return bits_to_f32(v); }
-__device__ __forceinline__ float lds_to_f32(float v) { return v; }
-// Four consecutive LDS elements.
-__device__ __forceinline__ void st_four(uint16_t *p, float a, float b, float c, float d) {
-    *reinterpret_cast<uint2 *>(p) = make_uint2(pack2_bf16(a, b), pack2_bf16(c, d));
-}
-__device__ __forceinline__ void st_four(float *p, float a, float b, float c, float d) {
-    *reinterpret_cast<float4 *>(p) = make_float4(a, b, c, d);
 }
 
 // Virtual-row block i (< TBW) of a wave: blocks w and 2*kPW-1-w, so that the
@@ -207,22 +207,25 @@ __device__ __forceinline__ void load_chunk(const PrefillParams &p, int64_t b, in
     }
 }
 
-// Loads the prologue inputs of chunk (b, h, t0 .. t0+Tc-1): wave w scans angle
-// group kPW-1-w (when there is one) and loads that group of its lane's token;
-// wave 0 loads dt and lam of its lane's token (and of token t0+64).
+// Loads the prologue inputs of chunk (b, h, t0 .. t0+Tc-1): the angle groups
+// of this wave for its lane's token; wave 0 loads dt and lam of its lane's
+// token (and of token t0+64).
 template <class C, typename IO>
 __device__ __forceinline__ void load_pro(const PrefillParams &p, int64_t b, int h, int64_t t0, int Tc,
                                          RawPro<C> &r) {
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const int64_t tokbase = (b * p.T + t0) * p.H + h;
     const int H = p.H;
-    const int grp = kPW - 1 - wave;
     const IO *th = static_cast<const IO *>(p.theta) + tokbase * C::K;
 #pragma unroll
-    for (int f = 0; f < C::GU; ++f) {
-        r.th[f] = make_uint4(0u, 0u, 0u, 0u);
-        if (grp < C::NG8 && lane < Tc)
-            r.th[f] = *reinterpret_cast<const uint4 *>(th + (lane * H * C::K + 8 * grp + f * C::EPU));
+    for (int m = 0; m < C::GPW; ++m) {
+        const int grp = pro_group<C>(wave, m);
+#pragma unroll
+        for (int f = 0; f < C::GU; ++f) {
+            r.th[m][f] = make_uint4(0u, 0u, 0u, 0u);
+            if (grp >= 0 && lane < Tc)
+                r.th[m][f] = *reinterpret_cast<const uint4 *>(th + (lane * H * C::K + 8 * grp + f * C::EPU));
+        }
     }
     r.dt = r.lam = r.dtn = r.lamn = 0.f;
     if (wave == 0) {
@@ -239,32 +242,43 @@ __device__ __forceinline__ void load_pro(const PrefillParams &p, int64_t b, int 
     }
 }
 
-// a1 for one chunk from its raw prologue inputs, into one prologue buffer:
-// the angle table phi[t][k] (wrapped, fp32), the chunk rotation (cos, sin of
-// Theta_c) and the running fp64 angle; the coefficient table and g_c.  Every
-// scan is wave-local (DPP, lane = token), so no barrier is needed here.
+// a1 for one chunk from its raw prologue inputs: the cos/sin table of the
+// within-chunk angle prefix (row = token, (cos, sin) per pair), the chunk
+// rotation (cos, sin of Theta_c, the table's row Tc-1) into one half of the
+// double-buffered table, the running fp64 angle; the coefficient table and
+// g_c.  The angle prefix is an exact integer scan of fixed-point turns (wraps
+// modulo one turn by itself); sin and cos take turns directly.  Every scan is
+// wave-local (DPP, lane = token), so no barrier is needed here.
 template <class C, typename IO>
 __device__ __forceinline__ void run_pro(const RawPro<C> &r, int Tc, int64_t t0, int64_t T, float A,
-                                        float *phi, float *coef, float *misc, float2 *thc, double *ths) {
-    constexpr int KP = C::KP, EPU = C::EPU;
+                                        float *cs, float *coef, float *misc, float2 *thc, double *ths) {
+    constexpr int EPU = C::EPU;
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-    const int grp = kPW - 1 - wave;
-    if (grp < C::NG8) {
+#pragma unroll
+    for (int m = 0; m < C::GPW; ++m) {
+        const int grp = pro_group<C>(wave, m);
+        if (grp < 0) continue;
         float th[8];
 #pragma unroll
-        for (int f = 0; f < C::GU; ++f) unpack_unit(r.th[f], th + f * EPU, IO());
-        double v[8];
+        for (int f = 0; f < C::GU; ++f) unpack_unit(r.th[m][f], th + f * EPU, IO());
+        uint32_t u[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = wave_scan_dpp(double(th[j]));
+        for (int j = 0; j < 8; ++j) u[j] = wave_scan_dpp(angle_to_turns32(th[j]));
+        float cn[8], sn[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) phi[lane * KP + 8 * grp + j] = float(wrap_angle(v[j]));
-        if (lane == kWave - 1) {
+        for (int j = 0; j < 8; ++j) {
+            const float tf = turns32_to_f32(u[j]);
+            sn[j] = __builtin_amdgcn_sinf(tf);
+            cn[j] = __builtin_amdgcn_cosf(tf);
+        }
+        float4 *row = reinterpret_cast<float4 *>(cs + lane * C::CSP + 16 * grp);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) row[j] = make_float4(cn[2 * j], sn[2 * j], cn[2 * j + 1], sn[2 * j + 1]);
+        if (lane == Tc - 1) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                float sn, cs;
-                sincos_wrapped(wrap_angle(v[j]), &sn, &cs);
-                thc[8 * grp + j] = make_float2(cs, sn);
-                ths[8 * grp + j] += v[j];
+                thc[8 * grp + j] = make_float2(cn[j], sn[j]);
+                ths[8 * grp + j] += turns32_to_rad(u[j]);
             }
         }
     }
@@ -322,9 +336,8 @@ template <typename IO, int N, int P, int R, bool OUT>
 __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
     typedef Cfg<IO, N, P, R> C;
     typedef typename C::M M;
-    typedef typename C::lds_t lds_t;
     typedef typename C::frag frag;
-    constexpr int K = C::K, KP = C::KP, V = C::V, NBP = C::NBP, VP = C::VP, EPU = C::EPU;
+    constexpr int PL = C::PL, K = C::K, V = C::V, NBP = C::NBP, PP = C::PP, EPU = C::EPU;
     constexpr int PT = C::PT, NKS = C::NKS;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const int g = lane >> 4, l16 = lane & 15;
@@ -342,15 +355,15 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
     const int c_end = min(p.nC, c_begin + p.cps);
 
     extern __shared__ __align__(16) unsigned char smem[];
-    float *coef_s = reinterpret_cast<float *>(smem + C::o_coef);  // [2][4][64]
-    float *misc_s = reinterpret_cast<float *>(smem + C::o_misc);  // g_c [2], delta_0 [2]
-    float2 *thc_s = reinterpret_cast<float2 *>(smem + C::o_thc);  // [2][K]
-    double *ths_s = reinterpret_cast<double *>(smem + C::o_ths);  // [K]
-    float *phi_s = reinterpret_cast<float *>(smem + C::o_phi);    // [2][64][KP]
-    lds_t *bs = reinterpret_cast<lds_t *>(smem + C::o_bs);
-    lds_t *bst = reinterpret_cast<lds_t *>(smem + C::o_bst);
-    lds_t *xt = reinterpret_cast<lds_t *>(smem + C::o_xt);
-    lds_t *ht = reinterpret_cast<lds_t *>(smem + C::o_ht);
+    uint16_t *bs = reinterpret_cast<uint16_t *>(smem + C::o_bs);   // rotated B, row-major
+    uint16_t *xr = reinterpret_cast<uint16_t *>(smem + C::o_xr);   // x, row-major
+    uint16_t *ht = reinterpret_cast<uint16_t *>(smem + C::o_ht);   // state, [p][n]
+    uint16_t *xs = reinterpret_cast<uint16_t *>(smem + C::o_xs);   // scaled x, row-major (XS)
+    float *cs_s = reinterpret_cast<float *>(smem + C::o_cs);       // [64][CSP]
+    float *coef_s = reinterpret_cast<float *>(smem + C::o_coef);   // [2][4][64]
+    float *misc_s = reinterpret_cast<float *>(smem + C::o_misc);   // g_c [2], delta_0 [2]
+    float2 *thc_s = reinterpret_cast<float2 *>(smem + C::o_thc);   // [2][K]
+    double *ths_s = reinterpret_cast<double *>(smem + C::o_ths);   // [K]
 
     // running angle: Phi_{-1} plus the segments before this one (output pass)
     for (int k = tid; k < K; k += kPT) {
@@ -374,7 +387,7 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
     RawChunk<C> raw;
     load_chunk<C, IO, OUT>(p, b, h, int64_t(c_begin) * kQ, tc_of(c_begin), raw);
     __syncthreads(); // ths_s initialised
-    run_pro<C, IO>(rp, tc_of(c_begin), int64_t(c_begin) * kQ, p.T, Ah, phi_s, coef_s, misc_s, thc_s, ths_s);
+    run_pro<C, IO>(rp, tc_of(c_begin), int64_t(c_begin) * kQ, p.T, Ah, cs_s, coef_s, misc_s, thc_s, ths_s);
     if (c_begin + 1 < c_end)
         load_pro<C, IO>(p, b, h, int64_t(c_begin + 1) * kQ, tc_of(c_begin + 1), rp);
     __syncthreads();
@@ -383,34 +396,26 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
         const int64_t t0 = int64_t(c) * kQ;
         const int Tc = tc_of(c);
         const int buf = (c - c_begin) & 1;
-        const float *phb = phi_s + buf * (kQ * KP);
         const float *ell_s = coef_s + buf * (4 * kQ);
         const float *gam_s = ell_s + kQ, *wgt_s = gam_s + kQ, *scl_s = wgt_s + kQ;
         const float2 *thcb = thc_s + buf * K;
 
-        // ---- a2: rotate B and C, stage B, x in LDS; C fragments to registers
+        // ---- a2: rotate B and C with the cos/sin table; stage B, x, scaled x
 #pragma unroll
         for (int j = 0; j < C::UPT_B; ++j) {
             const int u = tid + j * kPT;
             if (u < C::UB) {
                 const int v = u / C::URB, q = u - v * C::URB;
-                const int tok = v / R;
                 float e[EPU];
                 unpack_unit(raw.bb[j], e, IO());
-                if (tok < Tc) {
+                const float4 *cr = reinterpret_cast<const float4 *>(cs_s + (v / R) * C::CSP + q * EPU);
 #pragma unroll
-                    for (int pp = 0; pp < EPU / 2; ++pp) {
-                        float sn, cs;
-                        __sincosf(phb[tok * KP + q * (EPU / 2) + pp], &sn, &cs);
-                        rot_neg(cs, sn, e[2 * pp], e[2 * pp + 1]);
-                    }
+                for (int w4 = 0; w4 < EPU / 4; ++w4) {
+                    const float4 a = cr[w4];
+                    rot_neg(a.x, a.y, e[4 * w4], e[4 * w4 + 1]);
+                    rot_neg(a.z, a.w, e[4 * w4 + 2], e[4 * w4 + 3]);
                 }
-                st_unit(bs + v * NBP + q * EPU, e);
-                if (C::BST) {
-                    const float sc = scl_s[tok];
-#pragma unroll
-                    for (int ee = 0; ee < EPU; ++ee) st_one(bst + (q * EPU + ee) * VP + v, e[ee] * sc);
-                }
+                st_planes<PL, C::BS_PS, EPU>(bs + v * NBP + q * EPU, e);
             }
         }
 #pragma unroll
@@ -420,8 +425,16 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
                 const int v = u / C::URX, q = u - v * C::URX;
                 float e[EPU];
                 unpack_unit(raw.xx[j], e, IO());
+                if constexpr (PL == 1)
+                    *reinterpret_cast<uint4 *>(xr + v * PP + q * EPU) = raw.xx[j];
+                else
+                    st_planes<PL, C::X_PS, EPU>(xr + v * PP + q * EPU, e);
+                if constexpr (C::XS) {
+                    const float sc = scl_s[v / R];
 #pragma unroll
-                for (int ee = 0; ee < EPU; ++ee) st_one(xt + (q * EPU + ee) * VP + v, e[ee]);
+                    for (int ee = 0; ee < EPU; ++ee) e[ee] *= sc;
+                    st_planes<PL, C::X_PS, EPU>(xs + v * PP + q * EPU, e);
+                }
             }
         }
         frag cf[C::TBW][NKS];
@@ -436,12 +449,13 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
                     float e[8];
 #pragma unroll
                     for (int f = 0; f < C::FU; ++f) unpack_unit(raw.cc[i][ks][f], e + f * EPU, IO());
-                    if (tb < C::NTB && n0 < N && tok < Tc) {
+                    if (tb < C::NTB && n0 < N) {
+                        const float4 *cr = reinterpret_cast<const float4 *>(cs_s + tok * C::CSP + n0);
 #pragma unroll
-                        for (int pp = 0; pp < 4; ++pp) {
-                            float sn, cs;
-                            __sincosf(phb[tok * KP + n0 / 2 + pp], &sn, &cs);
-                            rot_neg(cs, sn, e[2 * pp], e[2 * pp + 1]);
+                        for (int w4 = 0; w4 < 2; ++w4) {
+                            const float4 a = cr[w4];
+                            rot_neg(a.x, a.y, e[4 * w4], e[4 * w4 + 1]);
+                            rot_neg(a.z, a.w, e[4 * w4 + 2], e[4 * w4 + 3]);
                         }
                     }
                     cf[i][ks] = M::pack(e);
@@ -482,7 +496,8 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
                             }
                         }
                     }
-                    st_four(ht + (16 * pt + l16) * NBP + 16 * nt + 4 * g, st[j][0], st[j][1], st[j][2], st[j][3]);
+                    const float sv[4] = {st[j][0], st[j][1], st[j][2], st[j][3]};
+                    st_planes<PL, C::HT_PS, 4>(ht + (16 * pt + l16) * NBP + 16 * nt + 4 * g, sv);
                 } else if (seg == 0 && p.has_init) {
                     const floatx4 hi4 = fold_init<C, IO>(p, bh, nt, pt, del0);
                     float *hi = p.hinit + bh * int64_t(N) * P;
@@ -516,7 +531,7 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
 #pragma unroll
                     for (int ks = 0; ks < NKS; ++ks) {
                         const int n0 = 32 * ks + 8 * g;
-                        const frag hb = n0 < N ? M::lds8(ht + (16 * pt + l16) * NBP + n0) : M::zero();
+                        const frag hb = n0 < N ? M::template lds8<C::HT_PS>(ht + (16 * pt + l16) * NBP + n0) : M::zero();
                         acc[pt] = M::mma(acc[pt], cf[i][ks], hb);
                     }
                 }
@@ -529,41 +544,70 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
                 }
                 const int tt = (t0v + l16) / R; // token of this lane's column t
                 const float ell_t = ell_s[tt], gam_t = gam_s[tt];
-                const bool live = tt < Tc;
-                for (int s0 = 0; s0 / R <= tok_last; s0 += 32) {
-                    floatx4 sb[2];
+                // mask weight of source token ts for this lane's column token
+                // tt (exp argument selected first, so masked entries cannot
+                // overflow)
+                auto mw = [&](int ts, float ell_ts, float wgt_ts) {
+                    const float e = __expf(ts < tt ? ell_t - ell_ts : 0.f) * wgt_ts;
+                    return ts < tt ? e : (ts == tt ? gam_t : 0.f);
+                };
+                // S^T for the 32 source rows s0 .. s0+31 (two 16-row blocks)
+                auto s_pair = [&](int s0, floatx4 *sb) {
 #pragma unroll
                     for (int q = 0; q < 2; ++q) {
                         sb[q] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                         for (int ks = 0; ks < NKS; ++ks) {
                             const int n0 = 32 * ks + 8 * g;
-                            const frag ab = n0 < N ? M::lds8(bs + (s0 + 16 * q + l16) * NBP + n0) : M::zero();
+                            const frag ab = n0 < N ? M::template lds8<C::BS_PS>(bs + (s0 + 16 * q + l16) * NBP + n0) : M::zero();
                             sb[q] = M::mma(sb[q], ab, cf[i][ks]);
                         }
                     }
+                };
+                // x operand of M x: slots 0-3 are rows s0 + 4g .. +3, slots
+                // 4-7 rows s0 + 16 + 4g .. +3 (the k order of the M fragment)
+                const uint16_t *xq = xr + (4 * g + (l16 >> 2)) * PP + 4 * (l16 & 3);
+                const int npairs = (R * (tok_last + 1) + 31) / 32;
+                floatx4 sn[2];
+                s_pair(0, sn);
+                for (int mp = 0; mp < npairs; ++mp) {
+                    const int s0 = 32 * mp;
+                    const floatx4 sb[2] = {sn[0], sn[1]};
+                    if (mp + 1 < npairs) s_pair(s0 + 32, sn); // next pair's S overlaps this mask
                     float m[8];
 #pragma unroll
                     for (int q = 0; q < 2; ++q) {
-                        int ts_prev = -1;
-                        float w = 0.f;
+                        const int r0 = s0 + 16 * q + 4 * g; // this lane's 4 source rows r0 .. r0+3
+                        float w[4];
+                        if constexpr (R == 1) {
+                            const float4 el = *reinterpret_cast<const float4 *>(ell_s + r0);
+                            const float4 wg = *reinterpret_cast<const float4 *>(wgt_s + r0);
+                            w[0] = mw(r0, el.x, wg.x);
+                            w[1] = mw(r0 + 1, el.y, wg.y);
+                            w[2] = mw(r0 + 2, el.z, wg.z);
+                            w[3] = mw(r0 + 3, el.w, wg.w);
+                        } else if constexpr (R == 2) {
+                            const float2 el = *reinterpret_cast<const float2 *>(ell_s + r0 / 2);
+                            const float2 wg = *reinterpret_cast<const float2 *>(wgt_s + r0 / 2);
+                            w[0] = w[1] = mw(r0 / 2, el.x, wg.x);
+                            w[2] = w[3] = mw(r0 / 2 + 1, el.y, wg.y);
+                        } else if constexpr (R == 4) {
+                            w[0] = w[1] = w[2] = w[3] = mw(r0 / 4, ell_s[r0 / 4], wgt_s[r0 / 4]);
+                        } else {
 #pragma unroll
-                        for (int v = 0; v < 4; ++v) {
-                            const int ts = (s0 + 16 * q + 4 * g + v) / R;
-                            if (ts != ts_prev) {
-                                w = 0.f;
-                                if (live && ts <= tt) w = ts == tt ? gam_t : __expf(ell_t - ell_s[ts]) * wgt_s[ts];
-                                ts_prev = ts;
+                            for (int v = 0; v < 4; ++v) {
+                                const int ts = (r0 + v) / R;
+                                w[v] = mw(ts, ell_s[ts], wgt_s[ts]);
                             }
-                            m[4 * q + v] = sb[q][v] * w;
                         }
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) m[4 * q + v] = sb[q][v] * w[v];
                     }
                     const frag mf = M::pack(m);
+                    const uint16_t *xs0 = xq + s0 * PP;
 #pragma unroll
-                    for (int pt = 0; pt < PT; ++pt) {
-                        const lds_t *xr = xt + (16 * pt + l16) * VP + s0 + 4 * g;
-                        acc[pt] = M::mma(acc[pt], mf, M::lds4x2(xr, xr + 16));
-                    }
+                    for (int pt = 0; pt < PT; ++pt)
+                        acc[pt] = M::mma(acc[pt], mf, M::template tr8<C::X_PS>(xs0 + 16 * pt, xs0 + 16 * PP + 16 * pt));
                 }
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
@@ -578,33 +622,31 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
             }
         }
 
-        // ---- a4: H <- R(Theta_c) (exp(g_c) H + sum_v (scaled Bhat)[v] x[v]^T)
+        // ---- a4: H <- R(Theta_c) (exp(g_c) H + sum_v Bhat[v] (scaled x)[v]^T)
         {
             const float eg = __expf(gc);
+            // slot j of both operands is virtual row 32 ks + 8 g + j
+            const int ra = 8 * g + (l16 >> 2), ca = 4 * (l16 & 3);
 #pragma unroll
             for (int j = 0; j < C::TW; ++j) {
                 const int tile = wave + kPW * j;
                 if (tile >= C::NTILE) continue;
                 const int nt = tile / PT, pt = tile - nt * PT;
                 floatx4 acc = st[j] * eg;
-                const lds_t *br = xt + (16 * pt + l16) * VP + 8 * g;
-                if (C::BST) {
-                    const lds_t *ar = bst + (16 * nt + l16) * VP + 8 * g;
+                const uint16_t *ap = bs + ra * NBP + 16 * nt + ca;
+                const uint16_t *bp = (C::XS ? xs : xr) + ra * PP + 16 * pt + ca;
 #pragma unroll 2
-                    for (int ks = 0; ks < V / 32; ++ks) acc = M::mma(acc, M::lds8(ar + 32 * ks), M::lds8(br + 32 * ks));
-                } else {
-                    // gather column n of the row-major copy and apply the scale here
-                    const lds_t *ac = bs + 16 * nt + l16;
-#pragma unroll 1
-                    for (int ks = 0; ks < V / 32; ++ks) {
-                        float a[8];
+                for (int ks = 0; ks < V / 32; ++ks) {
+                    const frag af = M::template tr8<C::BS_PS>(ap + 32 * ks * NBP, ap + (32 * ks + 4) * NBP);
+                    frag bf = M::template tr8<C::X_PS>(bp + 32 * ks * PP, bp + (32 * ks + 4) * PP);
+                    if constexpr (!C::XS) {
+                        float f[8];
+                        M::unpack(bf, f);
 #pragma unroll
-                        for (int jj = 0; jj < 8; ++jj) {
-                            const int v = 32 * ks + 8 * g + jj;
-                            a[jj] = lds_to_f32(ac[v * NBP]) * scl_s[v / R];
-                        }
-                        acc = M::mma(acc, M::pack(a), M::lds8(br + 32 * ks));
+                        for (int jj = 0; jj < 8; ++jj) f[jj] *= scl_s[(32 * ks + 8 * g + jj) / R];
+                        bf = M::pack(f);
                     }
+                    acc = M::mma(acc, af, bf);
                 }
 #pragma unroll
                 for (int q = 0; q < 2; ++q) {
@@ -616,11 +658,11 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
         }
         gsum += gc;
 
-        // ---- a1 of the next chunk into the other prologue buffer
+        // ---- a1 of the next chunk: cos/sin table, other coefficient buffer
         if (c + 1 < c_end) {
             const int nb = buf ^ 1;
-            run_pro<C, IO>(rp, tc_of(c + 1), t0 + kQ, p.T, Ah, phi_s + nb * (kQ * KP), coef_s + nb * (4 * kQ),
-                           misc_s + nb, thc_s + nb * K, ths_s);
+            run_pro<C, IO>(rp, tc_of(c + 1), t0 + kQ, p.T, Ah, cs_s, coef_s + nb * (4 * kQ), misc_s + nb,
+                           thc_s + nb * K, ths_s);
             if (c + 2 < c_end) load_pro<C, IO>(p, b, h, t0 + 2 * kQ, tc_of(c + 2), rp);
         }
         __syncthreads();
@@ -631,7 +673,8 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
                 const int tile = wave + kPW * j;
                 if (tile >= C::NTILE) continue;
                 const int nt = tile / PT, pt = tile - nt * PT;
-                st_four(ht + (16 * pt + l16) * NBP + 16 * nt + 4 * g, st[j][0], st[j][1], st[j][2], st[j][3]);
+                const float sv[4] = {st[j][0], st[j][1], st[j][2], st[j][3]};
+                st_planes<PL, C::HT_PS, 4>(ht + (16 * pt + l16) * NBP + 16 * nt + 4 * g, sv);
             }
         }
     }

@@ -28,8 +28,12 @@ __device__ __forceinline__ float bits_to_f32(uint32_t b16) { return __uint_as_fl
 __device__ __forceinline__ uint16_t f32_to_bits(float f) {
     return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
+// Two floats -> two bf16 in one word (lo in the low half), one instruction.
+typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+typedef float float2_v __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
-    return uint32_t(f32_to_bits(lo)) | (uint32_t(f32_to_bits(hi)) << 16);
+    const float2_v v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_v));
 }
 
 // ---------------------------------------------------------------------------
@@ -88,118 +92,119 @@ struct io<bf16> {
 // so a contraction only needs both operands to use one slot -> k mapping.
 // Result D (16 x 16 fp32): lane l holds D[4 g + v][l % 16], v = 0..3.
 //
-// Mma<false>: operands rounded to bf16, one MFMA per step.
-// Mma<true> : fp32 operands split a = hi + lo (both bf16); a*b is taken as
-//             hi*hi + hi*lo + lo*hi (three MFMAs), about 2^-16 relative.
+// Staged operands live in LDS as PL planes of bf16 bits, plane 1 a fixed
+// number of elements (PS) after plane 0:
+//   PL = 1 (bf16 I/O): the value rounded to bf16, one MFMA per step;
+//   PL = 2 (fp32 I/O): a = hi + lo, both bf16; a*b is taken as
+//          hi*hi + hi*lo + lo*hi (three MFMAs), about 2^-16 relative.
 // ---------------------------------------------------------------------------
-template <bool F32>
-struct Mma;
-
 __device__ __forceinline__ bf16x8 bf16x8_from_words(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3) {
     return __builtin_bit_cast(bf16x8, make_uint4(w0, w1, w2, w3));
 }
 
-template <>
-struct Mma<false> {
-    typedef uint16_t lds_t; // LDS element: bf16 bits
-    struct frag {
-        bf16x8 v;
-    };
-    static __device__ __forceinline__ frag zero() {
-        frag f;
-        f.v = bf16x8_from_words(0, 0, 0, 0);
-        return f;
-    }
-    static __device__ __forceinline__ frag pack(const float a[8]) {
-        frag f;
-        f.v = bf16x8_from_words(pack2_bf16(a[0], a[1]), pack2_bf16(a[2], a[3]),
-                                pack2_bf16(a[4], a[5]), pack2_bf16(a[6], a[7]));
-        return f;
-    }
-    static __device__ __forceinline__ floatx4 mma(floatx4 acc, const frag &a, const frag &b) {
-        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, acc, 0, 0, 0);
-    }
-    // 8 consecutive LDS elements (16-byte aligned).
-    static __device__ __forceinline__ frag lds8(const lds_t *p) {
-        frag f;
-        f.v = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(p));
-        return f;
-    }
-    // 4 consecutive elements from p0 then 4 from p1 (8-byte aligned each).
-    static __device__ __forceinline__ frag lds4x2(const lds_t *p0, const lds_t *p1) {
-        const uint2 a = *reinterpret_cast<const uint2 *>(p0);
-        const uint2 b = *reinterpret_cast<const uint2 *>(p1);
-        frag f;
-        f.v = bf16x8_from_words(a.x, a.y, b.x, b.y);
-        return f;
-    }
-    static __device__ __forceinline__ lds_t to_lds(float v) { return f32_to_bits(v); }
-    // Two adjacent LDS elements as one 32-bit store.
-    static __device__ __forceinline__ void st2(lds_t *p, float a, float b) {
-        *reinterpret_cast<uint32_t *>(p) = pack2_bf16(a, b);
-    }
-    // 8 consecutive LDS elements as one 16-byte store.
-    static __device__ __forceinline__ void st8(lds_t *p, const float a[8]) {
-        *reinterpret_cast<uint4 *>(p) = make_uint4(pack2_bf16(a[0], a[1]), pack2_bf16(a[2], a[3]),
-                                                   pack2_bf16(a[4], a[5]), pack2_bf16(a[6], a[7]));
-    }
-};
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
-template <>
-struct Mma<true> {
-    typedef float lds_t;
+// Transposing LDS load (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// lane i receives element (i % 4) of the 64-bit word addressed by lane
+// 4 s + i / 4 of its group, for s = 0..3.  So when lane j of a group
+// addresses row r0 + j / 4, elements c0 + 4 (j % 4) .. + 3 of a row-major
+// bf16 matrix, lane i receives column c0 + i of rows r0 .. r0 + 3.
+__device__ __forceinline__ uint2 lds_tr4(const uint16_t *p) {
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(p)));
+}
+
+template <int PL>
+struct Mma {
     struct frag {
-        bf16x8 hi, lo;
+        bf16x8 v[PL];
     };
     static __device__ __forceinline__ frag zero() {
         frag f;
-        f.hi = bf16x8_from_words(0, 0, 0, 0);
-        f.lo = f.hi;
+#pragma unroll
+        for (int k = 0; k < PL; ++k) f.v[k] = bf16x8_from_words(0, 0, 0, 0);
         return f;
     }
+    // Eight floats into the planes (hi = RNE bf16, lo = bf16 of the rest).
     static __device__ __forceinline__ frag pack(const float a[8]) {
         uint32_t hw[4], lw[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const uint16_t h0 = f32_to_bits(a[2 * i]), h1 = f32_to_bits(a[2 * i + 1]);
-            const float r0 = a[2 * i] - bits_to_f32(h0), r1 = a[2 * i + 1] - bits_to_f32(h1);
-            hw[i] = uint32_t(h0) | (uint32_t(h1) << 16);
-            lw[i] = pack2_bf16(r0, r1);
+            hw[i] = pack2_bf16(a[2 * i], a[2 * i + 1]);
+            if constexpr (PL == 2)
+                lw[i] = pack2_bf16(a[2 * i] - __uint_as_float(hw[i] << 16),
+                                   a[2 * i + 1] - __uint_as_float(hw[i] & 0xffff0000u));
         }
         frag f;
-        f.hi = bf16x8_from_words(hw[0], hw[1], hw[2], hw[3]);
-        f.lo = bf16x8_from_words(lw[0], lw[1], lw[2], lw[3]);
+        f.v[0] = bf16x8_from_words(hw[0], hw[1], hw[2], hw[3]);
+        if constexpr (PL == 2) f.v[1] = bf16x8_from_words(lw[0], lw[1], lw[2], lw[3]);
         return f;
     }
+    // The eight values a fragment stands for (sum of its planes).
+    static __device__ __forceinline__ void unpack(const frag &f, float a[8]) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) a[i] = 0.f;
+#pragma unroll
+        for (int k = 0; k < PL; ++k) {
+            const uint4 w = __builtin_bit_cast(uint4, f.v[k]);
+            const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                a[2 * i] += __uint_as_float(ws[i] << 16);
+                a[2 * i + 1] += __uint_as_float(ws[i] & 0xffff0000u);
+            }
+        }
+    }
     static __device__ __forceinline__ floatx4 mma(floatx4 acc, const frag &a, const frag &b) {
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.lo, b.hi, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.lo, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.hi, acc, 0, 0, 0);
-        return acc;
+        if constexpr (PL == 2) {
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v[1], b.v[0], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v[0], b.v[1], acc, 0, 0, 0);
+        }
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v[0], b.v[0], acc, 0, 0, 0);
     }
-    static __device__ __forceinline__ frag lds8(const lds_t *p) {
-        const float4 a = *reinterpret_cast<const float4 *>(p);
-        const float4 b = *reinterpret_cast<const float4 *>(p + 4);
-        const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-        return pack(v);
+    // Eight consecutive elements of each plane (16-byte aligned).
+    template <int PS>
+    static __device__ __forceinline__ frag lds8(const uint16_t *p) {
+        frag f;
+#pragma unroll
+        for (int k = 0; k < PL; ++k) f.v[k] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(p + k * PS));
+        return f;
     }
-    static __device__ __forceinline__ frag lds4x2(const lds_t *p0, const lds_t *p1) {
-        const float4 a = *reinterpret_cast<const float4 *>(p0);
-        const float4 b = *reinterpret_cast<const float4 *>(p1);
-        const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-        return pack(v);
-    }
-    static __device__ __forceinline__ lds_t to_lds(float v) { return v; }
-    static __device__ __forceinline__ void st2(lds_t *p, float a, float b) {
-        *reinterpret_cast<float2 *>(p) = make_float2(a, b);
-    }
-    static __device__ __forceinline__ void st8(lds_t *p, const float a[8]) {
-        *reinterpret_cast<float4 *>(p) = make_float4(a[0], a[1], a[2], a[3]);
-        *reinterpret_cast<float4 *>(p + 4) = make_float4(a[4], a[5], a[6], a[7]);
+    // Slots 0-3 from a transposing load at p0, slots 4-7 from one at p1.
+    template <int PS>
+    static __device__ __forceinline__ frag tr8(const uint16_t *p0, const uint16_t *p1) {
+        frag f;
+#pragma unroll
+        for (int k = 0; k < PL; ++k) {
+            const uint2 a = lds_tr4(p0 + k * PS), b = lds_tr4(p1 + k * PS);
+            f.v[k] = bf16x8_from_words(a.x, a.y, b.x, b.y);
+        }
+        return f;
     }
 };
 
-// Compute mode of an I/O type: bf16 I/O -> bf16 MFMA; fp32 I/O -> split fp32.
+// Store NV (4 or 8) floats as consecutive elements of each plane at p.
+template <int PL, int PS, int NV>
+__device__ __forceinline__ void st_planes(uint16_t *p, const float *v) {
+    uint32_t hw[NV / 2], lw[NV / 2];
+#pragma unroll
+    for (int i = 0; i < NV / 2; ++i) {
+        hw[i] = pack2_bf16(v[2 * i], v[2 * i + 1]);
+        if constexpr (PL == 2)
+            lw[i] = pack2_bf16(v[2 * i] - __uint_as_float(hw[i] << 16),
+                               v[2 * i + 1] - __uint_as_float(hw[i] & 0xffff0000u));
+    }
+    if constexpr (NV == 8) {
+        *reinterpret_cast<uint4 *>(p) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+        if constexpr (PL == 2) *reinterpret_cast<uint4 *>(p + PS) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+    } else {
+        static_assert(NV == 4, "4 or 8 values");
+        *reinterpret_cast<uint2 *>(p) = make_uint2(hw[0], hw[1]);
+        if constexpr (PL == 2) *reinterpret_cast<uint2 *>(p + PS) = make_uint2(lw[0], lw[1]);
+    }
+}
+
+// Compute mode of an I/O type: bf16 I/O -> one bf16 plane; fp32 I/O -> hi/lo planes.
 template <typename IO>
 struct mode {
     static constexpr bool f32 = false;
@@ -250,6 +255,10 @@ __device__ __forceinline__ double dpp_add(double v) {
     const uint32_t hi = dpp_u32<CTRL, ROW_MASK, BOUND_ZERO>(uint32_t(u >> 32));
     return v + __builtin_bit_cast(double, (uint64_t(hi) << 32) | lo);
 }
+template <int CTRL, int ROW_MASK, bool BOUND_ZERO>
+__device__ __forceinline__ uint32_t dpp_add(uint32_t v) {
+    return v + dpp_u32<CTRL, ROW_MASK, BOUND_ZERO>(v);
+}
 template <typename T>
 __device__ __forceinline__ T wave_scan_dpp(T v) {
     v = dpp_add<0x111, 0xf, true>(v);  // row_shr:1
@@ -260,6 +269,21 @@ __device__ __forceinline__ T wave_scan_dpp(T v) {
     v = dpp_add<0x143, 0xc, false>(v); // row_bcast:31 -> rows 2, 3
     return v;
 }
+
+// Angles as 32-bit fixed-point fractions of a turn (2^32 units per 2 pi):
+// integer sums of such values are exact modulo one turn, so an angle prefix
+// over many tokens needs no floating-point wrap.  Conversion rounds to the
+// nearest unit (1.46e-9 rad) in fp64.
+__device__ __forceinline__ uint32_t angle_to_turns32(float a) {
+    const double t = double(a) * (1.0 / kTwoPi);
+    double r = rint((t - rint(t)) * 4294967296.0); // [-2^31, 2^31]
+    if (r >= 2147483648.0) r -= 4294967296.0;
+    return uint32_t(int32_t(r));
+}
+// A fixed-point angle as fp32 turns in [-1/2, 1/2).
+__device__ __forceinline__ float turns32_to_f32(uint32_t u) { return float(int32_t(u)) * 0x1p-32f; }
+// ... and as fp64 radians in [-pi, pi).
+__device__ __forceinline__ double turns32_to_rad(uint32_t u) { return double(int32_t(u)) * (kTwoPi / 4294967296.0); }
 
 // Angle wrapped to [-pi, pi), fp64.
 __device__ __forceinline__ double wrap_angle(double a) {
