@@ -107,6 +107,48 @@ def load_traffic(kernel, workload):
     return rec.get("hbm_bytes_per_launch")
 
 
+def record_traffic(fetch_csv, write_csv, copy_mib):
+    """Per-launch HBM bytes of the output pass on the SISO prefill workload from
+    two rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE, in
+    KiB per dispatch) that also ran --copy-calibration-mib COPY_MIB: each
+    counter is scaled by what it reads for that plain device copy (COPY_MIB
+    read and COPY_MIB written).  Writes profiles/output_<workload>_traffic.json
+    tagged with the sha256 of the kernel sources."""
+    import csv
+    from mamba_selective_ssm_ssd_amd import synth
+    c1 = synth.CONFIGS[1]
+    tag = f"k_prefill<m3::bf16, {c1['N']}, {c1['P']}, {c1['R']}, true>"
+
+    def avg(path, counter):
+        kern, copy = [], []
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            v = float(r["Counter_Value"]) * 1024.0
+            if tag in r["Kernel_Name"]:
+                kern.append(v)
+            elif "copyBuffer" in r["Kernel_Name"] and v > 0.25 * copy_mib * (1 << 20):
+                copy.append(v)
+        if not kern or not copy:
+            raise SystemExit(f"{path}: no {counter} rows for {tag} or for the calibration copy")
+        return sum(kern) / len(kern), sum(copy) / len(copy)
+
+    fk, fc = avg(fetch_csv, "FETCH_SIZE")
+    wk, wc = avg(write_csv, "WRITE_SIZE")
+    nbytes = copy_mib * (1 << 20)
+    fs, ws = nbytes / fc, nbytes / wc
+    rec = {"kernel": tag, "workload": c1["name"],
+           "fetch_bytes_raw": fk, "write_bytes_raw": wk,
+           "calibration_copy_bytes": nbytes, "fetch_scale": fs, "write_scale": ws,
+           "hbm_read_bytes_per_launch": round(fk * fs), "hbm_write_bytes_per_launch": round(wk * ws),
+           "hbm_bytes_per_launch": round(fk * fs + wk * ws),
+           "sources_sha256": sources_digest(KERNEL_SOURCES["output"])}
+    out = os.path.join(ROOT, "profiles", f"output_{c1['name']}_traffic.json")
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+
+
 # ---------------------------------------------------------------------------
 def time_prefill(torch, mixer, inp, steps, warmup):
     x, dt, A, lam, theta, B, C = (inp[k] for k in ("x", "dt", "A", "lam", "theta", "B", "C"))
@@ -128,20 +170,21 @@ def time_prefill(torch, mixer, inp, steps, warmup):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = e0.elapsed_time(e1) / steps
-    # each kernel alone, on the same stream, after a full prefill filled the workspace
+    # each kernel alone, launched back to back on the same stream (after a full
+    # prefill filled the workspace): average launch duration
     per_kernel = {}
     for name in KERNELS:
         stage = mixer.capi.STAGES[name]
         reps = max(steps, 10)
         ks, ke = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        total = 0.0
+        mixer.prefill_stage(stage, *args, None, st, y, ws)
+        torch.cuda.synchronize()
+        ks.record()
         for _ in range(reps):
-            ks.record()
             mixer.prefill_stage(stage, *args, None, st, y, ws)
-            ke.record()
-            torch.cuda.synchronize()
-            total += ks.elapsed_time(ke)
-        per_kernel[name] = total / reps
+        ke.record()
+        torch.cuda.synchronize()
+        per_kernel[name] = ks.elapsed_time(ke) / reps
     mixer.prefill(*args, final=st, y=y, workspace=ws)   # leave a consistent state behind
     torch.cuda.synchronize()
     return ms, wall, per_kernel
@@ -224,7 +267,13 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device copy of this size (counter calibration)")
+    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the output pass's HBM traffic from two rocprofv3 counter "
+                         "runs (no GPU needed) and exit")
     args = ap.parse_args()
+    if args.record_traffic:
+        record_traffic(*args.record_traffic, copy_mib=args.copy_calibration_mib or 512)
+        return
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "

@@ -79,10 +79,13 @@ typedef enum {
     M3_ERR_HIP = 4               /* a kernel launch failed                              */
 } m3_status_t;
 
-/* Problem size.  Supported: chunk = 64; headdim P in {16, 32, 64, 128};
+/* Problem size.  Supported: chunk = 64; headdim P in {16, 32, 64};
  * dstate N in {16, 32, 64, 128}; rank R in 1..4; any batch >= 1, nheads >= 1
  * and seqlen >= 1 (a ragged last chunk is masked).  io_dtype is an
- * m3_dtype_t value. */
+ * m3_dtype_t value.  A prefill workgroup keeps one chunk's operands in the
+ * 160 KB of LDS of a gfx950 compute unit; (N, P, R) combinations that do not
+ * fit (with fp32 I/O: N = 128 with R >= 2, N = 64 with R = 4) are reported as
+ * M3_ERR_UNSUPPORTED by the prefill entry points (and a zero workspace size). */
 typedef struct {
     int64_t batch;
     int64_t seqlen;   /* T; ignored by m3_ssm_decode_step */
@@ -103,8 +106,10 @@ typedef struct {
 } m3_state_t;
 
 /* Bytes of device workspace m3_ssm_prefill needs for this shape (0 if the
- * shape is invalid).  The workspace holds per-token decay coefficients and
- * one N x P fp32 state per chunk. */
+ * shape is invalid or unsupported).  When batch * nheads is too small to fill
+ * the GPU, each sequence is cut into segments of whole chunks; the workspace
+ * holds each segment's aggregate (an N x P fp32 state, its summed log decay
+ * and rotation angle) and the carried state at the sequence start. */
 size_t m3_ssm_prefill_workspace_bytes(const m3_shape_t *shape);
 
 /*
