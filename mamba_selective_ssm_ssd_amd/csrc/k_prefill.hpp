@@ -98,7 +98,25 @@ struct Cfg {
     static constexpr size_t o_misc = o_coef + 2 * 4 * kQ * 4;                  // [2] g_c, [2] delta_0
     static constexpr size_t o_thc = o_misc + 64;                               // float2 [2][K]: cos, sin Theta_c
     static constexpr size_t o_ths = o_thc + 2 * size_t(K) * 8;                 // double [K]: running angle
-    static constexpr size_t o_xs = align16(o_ths + size_t(K) * 8);             // [PL][V][PP] scaled x
+    // The chunk's token mask L[t][s] (and e^{ell_t}) is tabulated once per
+    // chunk when it fits; otherwise each lane evaluates its mask entries.
+    static constexpr int LWP = kQ + 4;                                         // row pitch (floats)
+    static constexpr size_t o_lw = align16(o_ths + size_t(K) * 8);             // float [64][LWP]
+    static constexpr size_t lw_bytes = size_t(kQ) * LWP * 4 + kQ * 4;          // + e^{ell} [64]
+    static constexpr bool LWT = o_lw + lw_bytes <= kMaxLdsBytes;
+    // bf16 I/O: the within-chunk angle prefix is the matrix product of the
+    // lower-triangular ones matrix with the chunk's theta (MFMA, fp32
+    // accumulation), read from a row-major theta table; otherwise (fp32 I/O,
+    // or fewer than 16 pairs) exact fixed-point DPP scans.
+    static constexpr int THP = K + 8;                                          // theta table pitch (elements)
+    static constexpr int URT = K * SZ / 16, UT = kQ * URT, UPT_T = (UT + kPT - 1) / kPT;
+    static constexpr int NPB = K / 16, NTT = 4 * NPB;                          // 16x16 prefix tiles
+    static constexpr size_t o_th = align16(o_lw + (LWT ? lw_bytes : 0));       // bf16 [64][THP]
+    static constexpr size_t th_bytes = size_t(kQ) * THP * 2;
+    static constexpr bool MFP = PL == 1 && K % 16 == 0 && o_th + th_bytes <= kMaxLdsBytes;
+    static constexpr int MFW = FREEW ? FREEW : kPW;                            // waves sharing the prefix tiles
+    static constexpr int TPW = MFP ? (NTT + MFW - 1) / MFW : 0;
+    static constexpr size_t o_xs = align16(o_th + (MFP ? th_bytes : 0));       // [PL][V][PP] scaled x
     static constexpr size_t xs_bytes = size_t(PL) * X_PS * 2;
     // The scaled copy of x (the state update's second operand) is kept when
     // it fits; otherwise the scale is applied to that operand's fragments.
@@ -119,9 +137,19 @@ struct RawChunk {
 // lane's token (angle waves) or dt, lam of this lane's token (wave 0).
 template <class C>
 struct RawPro {
-    uint4 th[C::GPW][C::GU];
+    uint4 th[C::MFP ? 1 : C::GPW][C::GU];  // DPP scans: this wave's angle groups of its lane's token
+    uint4 thu[C::MFP ? C::UPT_T : 1];      // MFMA prefix: this thread's units of the theta rows
     float dt, lam, dtn, lamn;
 };
+
+// Prefix tile m (< TPW) computed by a wave, or -1.
+template <class C>
+__device__ __forceinline__ int mfp_tile(int wave, int m) {
+    int t;
+    if (C::FREEW) t = wave >= C::NTB ? wave - C::NTB + m * C::FREEW : -1;
+    else t = wave + m * kPW;
+    return t >= 0 && t < C::NTT ? t : -1;
+}
 
 // Angle group m (< GPW) scanned by a wave, or -1.
 template <class C>
@@ -217,14 +245,16 @@ __device__ __forceinline__ void load_pro(const PrefillParams &p, int64_t b, int 
     const int64_t tokbase = (b * p.T + t0) * p.H + h;
     const int H = p.H;
     const IO *th = static_cast<const IO *>(p.theta) + tokbase * C::K;
+    if constexpr (!C::MFP) {
 #pragma unroll
-    for (int m = 0; m < C::GPW; ++m) {
-        const int grp = pro_group<C>(wave, m);
+        for (int m = 0; m < C::GPW; ++m) {
+            const int grp = pro_group<C>(wave, m);
 #pragma unroll
-        for (int f = 0; f < C::GU; ++f) {
-            r.th[m][f] = make_uint4(0u, 0u, 0u, 0u);
-            if (grp >= 0 && lane < Tc)
-                r.th[m][f] = *reinterpret_cast<const uint4 *>(th + (lane * H * C::K + 8 * grp + f * C::EPU));
+            for (int f = 0; f < C::GU; ++f) {
+                r.th[m][f] = make_uint4(0u, 0u, 0u, 0u);
+                if (grp >= 0 && lane < Tc)
+                    r.th[m][f] = *reinterpret_cast<const uint4 *>(th + (lane * H * C::K + 8 * grp + f * C::EPU));
+            }
         }
     }
     r.dt = r.lam = r.dtn = r.lamn = 0.f;
@@ -242,6 +272,39 @@ __device__ __forceinline__ void load_pro(const PrefillParams &p, int64_t b, int 
     }
 }
 
+// Loads the theta rows of chunk (b, h, t0 .. t0+Tc-1), spread over all
+// threads (MFMA prefix only; issued a chunk ahead of their use).
+template <class C, typename IO>
+__device__ __forceinline__ void load_theta(const PrefillParams &p, int64_t b, int h, int64_t t0, int Tc,
+                                           RawPro<C> &r) {
+    if constexpr (C::MFP) {
+        const IO *th = static_cast<const IO *>(p.theta) + ((b * p.T + t0) * p.H + h) * C::K;
+        const int H = p.H;
+#pragma unroll
+        for (int j = 0; j < C::UPT_T; ++j) {
+            const int u = threadIdx.x + j * kPT;
+            const int tok = u / C::URT, q = u - tok * C::URT;
+            r.thu[j] = make_uint4(0u, 0u, 0u, 0u);
+            if (u < C::UT && tok < Tc)
+                r.thu[j] = *reinterpret_cast<const uint4 *>(th + (tok * H * C::K + q * C::EPU));
+        }
+    }
+}
+
+// Stores the raw theta rows of the next chunk as a row-major bf16 table
+// (MFMA prefix only).
+template <class C>
+__device__ __forceinline__ void write_theta(const RawPro<C> &r, uint16_t *tht) {
+    if constexpr (C::MFP) {
+#pragma unroll
+        for (int j = 0; j < C::UPT_T; ++j) {
+            const int u = threadIdx.x + j * kPT;
+            const int tok = u / C::URT, q = u - tok * C::URT;
+            if (u < C::UT) *reinterpret_cast<uint4 *>(tht + tok * C::THP + q * 8) = r.thu[j];
+        }
+    }
+}
+
 // a1 for one chunk from its raw prologue inputs: the cos/sin table of the
 // within-chunk angle prefix (row = token, (cos, sin) per pair), the chunk
 // rotation (cos, sin of Theta_c, the table's row Tc-1) into one half of the
@@ -251,11 +314,52 @@ __device__ __forceinline__ void load_pro(const PrefillParams &p, int64_t b, int 
 // wave-local (DPP, lane = token), so no barrier is needed here.
 template <class C, typename IO>
 __device__ __forceinline__ void run_pro(const RawPro<C> &r, int Tc, int64_t t0, int64_t T, float A,
-                                        float *cs, float *coef, float *misc, float2 *thc, double *ths) {
+                                        float *cs, float *coef, float *misc, float2 *thc, double *ths,
+                                        const uint16_t *tht) {
     constexpr int EPU = C::EPU;
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    if constexpr (C::MFP) {
+        // Phi[t][k] = sum_{s <= t} theta[s][k] as (lower-triangular ones) x theta,
+        // one 16x16 tile (16 tokens x 16 pairs) per step; the chunk total is
+        // the row of token Tc-1
+        typedef typename C::M M;
+        const int g = lane >> 4, l16 = lane & 15;
 #pragma unroll
-    for (int m = 0; m < C::GPW; ++m) {
+        for (int m = 0; m < C::TPW; ++m) {
+            const int tile = mfp_tile<C>(wave, m);
+            if (tile < 0) continue;
+            const int tb = tile & 3, pb = tile >> 2;
+            const int trow = 16 * tb + l16; // A row of this lane
+            floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+            for (int kb = 0; 32 * kb <= 16 * tb + 15; ++kb) {
+                uint32_t w[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int s0 = 32 * kb + 8 * g + 2 * i;
+                    w[i] = (s0 <= trow ? 0x3F80u : 0u) | (s0 + 1 <= trow ? 0x3F800000u : 0u);
+                }
+                typename M::frag a;
+                a.v[0] = bf16x8_from_words(w[0], w[1], w[2], w[3]);
+                const uint16_t *bp = tht + (32 * kb + 8 * g + (l16 >> 2)) * C::THP + 16 * pb + 4 * (l16 & 3);
+                acc = M::mma(acc, a, M::template tr8<0>(bp, bp + 4 * C::THP));
+            }
+            const int pair = 16 * pb + l16;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int t = 16 * tb + 4 * g + v;
+                float tf = acc[v] * float(1.0 / kTwoPi);
+                tf -= rintf(tf);
+                const float sn = __builtin_amdgcn_sinf(tf), cn = __builtin_amdgcn_cosf(tf);
+                *reinterpret_cast<float2 *>(cs + t * C::CSP + 2 * pair) = make_float2(cn, sn);
+                if (t == Tc - 1) {
+                    thc[pair] = make_float2(cn, sn);
+                    ths[pair] += double(acc[v]);
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < (C::MFP ? 0 : C::GPW); ++m) {
         const int grp = pro_group<C>(wave, m);
         if (grp < 0) continue;
         float th[8];
@@ -364,6 +468,8 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
     float *misc_s = reinterpret_cast<float *>(smem + C::o_misc);   // g_c [2], delta_0 [2]
     float2 *thc_s = reinterpret_cast<float2 *>(smem + C::o_thc);   // [2][K]
     double *ths_s = reinterpret_cast<double *>(smem + C::o_ths);   // [K]
+    float *lw_s = reinterpret_cast<float *>(smem + C::o_lw);       // [64][LWP] mask, then e^{ell} [64]
+    uint16_t *tht = reinterpret_cast<uint16_t *>(smem + C::o_th);  // theta rows of the next chunk
 
     // running angle: Phi_{-1} plus the segments before this one (output pass)
     for (int k = tid; k < K; k += kPT) {
@@ -384,12 +490,16 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
     // prologue of the first chunk, then its B, x, C and the next prologue inputs
     RawPro<C> rp;
     load_pro<C, IO>(p, b, h, int64_t(c_begin) * kQ, tc_of(c_begin), rp);
+    load_theta<C, IO>(p, b, h, int64_t(c_begin) * kQ, tc_of(c_begin), rp);
     RawChunk<C> raw;
     load_chunk<C, IO, OUT>(p, b, h, int64_t(c_begin) * kQ, tc_of(c_begin), raw);
-    __syncthreads(); // ths_s initialised
-    run_pro<C, IO>(rp, tc_of(c_begin), int64_t(c_begin) * kQ, p.T, Ah, cs_s, coef_s, misc_s, thc_s, ths_s);
-    if (c_begin + 1 < c_end)
+    write_theta<C>(rp, tht);
+    __syncthreads(); // ths_s, theta table
+    run_pro<C, IO>(rp, tc_of(c_begin), int64_t(c_begin) * kQ, p.T, Ah, cs_s, coef_s, misc_s, thc_s, ths_s, tht);
+    if (c_begin + 1 < c_end) {
         load_pro<C, IO>(p, b, h, int64_t(c_begin + 1) * kQ, tc_of(c_begin + 1), rp);
+        load_theta<C, IO>(p, b, h, int64_t(c_begin + 1) * kQ, tc_of(c_begin + 1), rp);
+    }
     __syncthreads();
 
     for (int c = c_begin; c < c_end; ++c) {
@@ -463,6 +573,37 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
             }
         }
 
+        // ---- a3 mask of this chunk: L[t][s] = exp(ell_t - ell_s) wgt_s (s < t),
+        // gam_t (s = t), 0 (s > t); row t, 8 consecutive s per thread
+        if constexpr (C::LWT) {
+            if (OUT) {
+                const int tt = tid >> 3, s0 = (tid & 7) * 8;
+                float w[8];
+                if (s0 <= tt) {
+                    const float et = ell_s[tt], gt = gam_s[tt];
+                    const float4 e0 = *reinterpret_cast<const float4 *>(ell_s + s0);
+                    const float4 e1 = *reinterpret_cast<const float4 *>(ell_s + s0 + 4);
+                    const float4 w0 = *reinterpret_cast<const float4 *>(wgt_s + s0);
+                    const float4 w1 = *reinterpret_cast<const float4 *>(wgt_s + s0 + 4);
+                    const float el[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
+                    const float wg[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const int ts = s0 + j;
+                        const float e = __expf(ts < tt ? et - el[j] : 0.f) * wg[j];
+                        w[j] = ts < tt ? e : (ts == tt ? gt : 0.f);
+                    }
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) w[j] = 0.f;
+                }
+                float4 *dst = reinterpret_cast<float4 *>(lw_s + tt * C::LWP + s0);
+                dst[0] = make_float4(w[0], w[1], w[2], w[3]);
+                dst[1] = make_float4(w[4], w[5], w[6], w[7]);
+                if (tid < kQ) lw_s[kQ * C::LWP + tid] = __expf(ell_s[tid]);
+            }
+        }
+
         // state at the start of this workgroup's first chunk
         if (c == c_begin) {
             const float del0 = misc_s[2];
@@ -509,8 +650,11 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
                 for (int k = tid; k < K; k += kPT) p.phi0ws[bh * K + k] = double(p.phi0[bh * K + k]);
         }
 
-        // prefetch the next chunk while this one computes
+        // theta rows of the next chunk for its prologue (after this barrier),
+        // then the prefetch of the next chunk and of the theta after it
+        if (c + 1 < c_end) write_theta<C>(rp, tht);
         if (c + 1 < c_end) load_chunk<C, IO, OUT>(p, b, h, t0 + kQ, tc_of(c + 1), raw);
+        if (c + 2 < c_end) load_theta<C, IO>(p, b, h, t0 + 2 * kQ, tc_of(c + 2), rp);
         __syncthreads();
 
         const float gc = misc_s[buf];
@@ -538,7 +682,10 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     const int tok = (t0v + 4 * g + v) / R;
-                    const float e = tok < Tc ? __expf(ell_s[tok]) : 0.f;
+                    float e;
+                    if constexpr (C::LWT) e = lw_s[kQ * C::LWP + tok];
+                    else e = __expf(ell_s[tok]);
+                    if (tok >= Tc) e = 0.f;
 #pragma unroll
                     for (int pt = 0; pt < PT; ++pt) acc[pt][v] *= e;
                 }
@@ -579,7 +726,20 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
                     for (int q = 0; q < 2; ++q) {
                         const int r0 = s0 + 16 * q + 4 * g; // this lane's 4 source rows r0 .. r0+3
                         float w[4];
-                        if constexpr (R == 1) {
+                        const float *lr = lw_s + tt * C::LWP; // mask row of this lane's column token
+                        if constexpr (C::LWT && R == 1) {
+                            const float4 a = *reinterpret_cast<const float4 *>(lr + r0);
+                            w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+                        } else if constexpr (C::LWT && R == 2) {
+                            const float2 a = *reinterpret_cast<const float2 *>(lr + r0 / 2);
+                            w[0] = w[1] = a.x;
+                            w[2] = w[3] = a.y;
+                        } else if constexpr (C::LWT && R == 4) {
+                            w[0] = w[1] = w[2] = w[3] = lr[r0 / 4];
+                        } else if constexpr (C::LWT) {
+#pragma unroll
+                            for (int v = 0; v < 4; ++v) w[v] = lr[(r0 + v) / R];
+                        } else if constexpr (R == 1) {
                             const float4 el = *reinterpret_cast<const float4 *>(ell_s + r0);
                             const float4 wg = *reinterpret_cast<const float4 *>(wgt_s + r0);
                             w[0] = mw(r0, el.x, wg.x);
@@ -662,7 +822,7 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
         if (c + 1 < c_end) {
             const int nb = buf ^ 1;
             run_pro<C, IO>(rp, tc_of(c + 1), t0 + kQ, p.T, Ah, cs_s, coef_s + nb * (4 * kQ), misc_s + nb,
-                           thc_s + nb * K, ths_s);
+                           thc_s + nb * K, ths_s, tht);
             if (c + 2 < c_end) load_pro<C, IO>(p, b, h, t0 + 2 * kQ, tc_of(c + 2), rp);
         }
         __syncthreads();

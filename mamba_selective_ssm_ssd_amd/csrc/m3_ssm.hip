@@ -8,8 +8,8 @@
 // segments and a pre-pass of the same kernel first computes every segment's
 // aggregate.  Decode enqueues one k_decode_step.  m3_ssm_prefill_stage
 // enqueues one of the two prefill kernels alone (include/m3_ssm_stages.h).
-#include "../../include/m3_ssm.h"
-#include "../../include/m3_ssm_stages.h"
+#include "m3_ssm.h"
+#include "m3_ssm_stages.h"
 #include "k_prefill.hpp"
 #include "m3_internal.hpp"
 
