@@ -83,6 +83,9 @@ struct Cfg {
     // group kPW - 1 - w.
     static constexpr int FREEW = NTB < kPW ? kPW - NTB : 0;
     static constexpr int GPW = FREEW ? (NG8 + FREEW - 1) / FREEW : 1;
+    // the wave that scans the decay coefficients (a wave without intra-chunk
+    // row blocks when there is one)
+    static constexpr int CW = FREEW ? kPW - 1 : 0;
     // plane strides (elements) of the staged arrays
     static constexpr int BS_PS = V * NBP, X_PS = V * PP, HT_PS = P * NBP;
     // LDS layout, bytes.  The MFMA operands come first so that their offsets
@@ -139,7 +142,7 @@ template <class C>
 struct RawPro {
     uint4 th[C::MFP ? 1 : C::GPW][C::GU];  // DPP scans: this wave's angle groups of its lane's token
     uint4 thu[C::MFP ? C::UPT_T : 1];      // MFMA prefix: this thread's units of the theta rows
-    float dt, lam, dtn, lamn;
+    uint32_t dt, lam, dtn, lamn;           // raw I/O bits of dt, lam (this lane's token, token t0+64)
 };
 
 // Prefix tile m (< TPW) computed by a wave, or -1.
@@ -181,7 +184,8 @@ __device__ __forceinline__ int wave_block(int i, int wave) { return i == 0 ? wav
 // Loads chunk (b, h, t0 .. t0+Tc-1)'s B, x and C into registers.  Addresses
 // are a uniform per-chunk base plus a 32-bit per-thread offset (saddr +
 // voffset addressing).
-template <class C, typename IO, bool OUT>
+// PARTS selects what is loaded: bit 0 B, bit 1 x, bit 2 C.
+template <class C, typename IO, bool OUT, int PARTS = 7>
 __device__ __forceinline__ void load_chunk(const PrefillParams &p, int64_t b, int h, int64_t t0, int Tc,
                                            RawChunk<C> &r) {
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
@@ -193,7 +197,7 @@ __device__ __forceinline__ void load_chunk(const PrefillParams &p, int64_t b, in
     const IO *Xp = static_cast<const IO *>(p.x) + tokbase * (C::R * C::P);
     const IO *Cp = static_cast<const IO *>(p.C) + tokbase * (C::R * C::N);
 #pragma unroll
-    for (int j = 0; j < C::UPT_B; ++j) {
+    for (int j = 0; j < ((PARTS & 1) ? C::UPT_B : 0); ++j) {
         const int u = tid + j * kPT;
         r.bb[j] = z;
         if (u < C::UB) {
@@ -204,7 +208,7 @@ __device__ __forceinline__ void load_chunk(const PrefillParams &p, int64_t b, in
         }
     }
 #pragma unroll
-    for (int j = 0; j < C::UPT_X; ++j) {
+    for (int j = 0; j < ((PARTS & 2) ? C::UPT_X : 0); ++j) {
         const int u = tid + j * kPT;
         r.xx[j] = z;
         if (u < C::UX) {
@@ -214,7 +218,7 @@ __device__ __forceinline__ void load_chunk(const PrefillParams &p, int64_t b, in
                 r.xx[j] = *reinterpret_cast<const uint4 *>(Xp + ((tok * H * C::R + ch) * C::P + q * C::EPU));
         }
     }
-    if (OUT) {
+    if (OUT && (PARTS & 4)) {
 #pragma unroll
         for (int i = 0; i < C::TBW; ++i) {
             const int tb = wave_block(i, wave);
@@ -257,17 +261,17 @@ __device__ __forceinline__ void load_pro(const PrefillParams &p, int64_t b, int 
             }
         }
     }
-    r.dt = r.lam = r.dtn = r.lamn = 0.f;
-    if (wave == 0) {
+    r.dt = r.lam = r.dtn = r.lamn = 0u;
+    if (wave == C::CW) {
         const IO *dt = static_cast<const IO *>(p.dt) + tokbase;
         const IO *lam = static_cast<const IO *>(p.lam) + tokbase;
         if (lane < Tc) {
-            r.dt = io<IO>::get(dt + lane * H);
-            r.lam = io<IO>::get(lam + lane * H);
+            r.dt = io<IO>::raw(dt + lane * H);
+            r.lam = io<IO>::raw(lam + lane * H);
         }
         if (lane == kWave - 1 && t0 + kQ < p.T) {
-            r.dtn = io<IO>::get(dt + kQ * H);
-            r.lamn = io<IO>::get(lam + kQ * H);
+            r.dtn = io<IO>::raw(dt + kQ * H);
+            r.lamn = io<IO>::raw(lam + kQ * H);
         }
     }
 }
@@ -305,17 +309,15 @@ __device__ __forceinline__ void write_theta(const RawPro<C> &r, uint16_t *tht) {
     }
 }
 
-// a1 for one chunk from its raw prologue inputs: the cos/sin table of the
-// within-chunk angle prefix (row = token, (cos, sin) per pair), the chunk
-// rotation (cos, sin of Theta_c, the table's row Tc-1) into one half of the
-// double-buffered table, the running fp64 angle; the coefficient table and
-// g_c.  The angle prefix is an exact integer scan of fixed-point turns (wraps
-// modulo one turn by itself); sin and cos take turns directly.  Every scan is
-// wave-local (DPP, lane = token), so no barrier is needed here.
+// a1 angles of one chunk: the cos/sin table of the within-chunk angle prefix
+// (row = token, (cos, sin) per pair), the chunk rotation (cos, sin of
+// Theta_c, the table's row Tc-1) into one half of the double-buffered table,
+// and the running fp64 angle.  bf16 I/O: MFMA prefix over the theta table;
+// otherwise exact integer scans of fixed-point turns (DPP, lane = token) of
+// this wave's angle groups held in registers.  Sin and cos take turns.
 template <class C, typename IO>
-__device__ __forceinline__ void run_pro(const RawPro<C> &r, int Tc, int64_t t0, int64_t T, float A,
-                                        float *cs, float *coef, float *misc, float2 *thc, double *ths,
-                                        const uint16_t *tht) {
+__device__ __forceinline__ void run_angles(const RawPro<C> &r, int Tc, float *cs, float2 *thc, double *ths,
+                                           const uint16_t *tht) {
     constexpr int EPU = C::EPU;
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     if constexpr (C::MFP) {
@@ -386,14 +388,26 @@ __device__ __forceinline__ void run_pro(const RawPro<C> &r, int Tc, int64_t t0, 
             }
         }
     }
-    if (wave == 0) {
-        const float ell = wave_scan_dpp(r.dt * A);
-        const float gam = r.lam * r.dt, del = (1.f - r.lam) * r.dt;
-        float dn = __shfl_down(del, 1, kWave);
-        if (lane == kWave - 1) dn = (1.f - r.lamn) * r.dtn;
+}
+
+// a1 coefficients of one chunk (the coefficient wave): the decay prefix ell,
+// gam, wgt = gam + delta of the next token, the chunk-end scale exp(g - ell) wgt,
+// g_c and delta of the first token, into one half of the double-buffered
+// tables.  Wave-local DPP scan; the next token's delta by a DPP wave shift.
+template <class C, typename IO>
+__device__ __forceinline__ void run_coef(const RawPro<C> &r, int Tc, int64_t t0, int64_t T, float A,
+                                         float *coef, float *misc) {
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    if (wave == C::CW) {
+        const float dtv = io<IO>::value(r.dt), lamv = io<IO>::value(r.lam);
+        const float ell = wave_scan_dpp(dtv * A);
+        const float gam = lamv * dtv, del = (1.f - lamv) * dtv;
+        // delta of the next token: DPP wave shift left by one lane
+        float dn = __uint_as_float(dpp_u32<0x130, 0xf, true>(__float_as_uint(del)));
+        if (lane == kWave - 1) dn = (1.f - io<IO>::value(r.lamn)) * io<IO>::value(r.dtn);
         if (t0 + lane + 1 >= T) dn = 0.f;
         const float w = gam + dn;
-        const float gc = __shfl(ell, Tc - 1, kWave);
+        const float gc = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(ell), Tc - 1));
         coef[lane] = ell;
         coef[kQ + lane] = gam;
         coef[2 * kQ + lane] = w;
@@ -494,13 +508,60 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
     RawChunk<C> raw;
     load_chunk<C, IO, OUT>(p, b, h, int64_t(c_begin) * kQ, tc_of(c_begin), raw);
     write_theta<C>(rp, tht);
+    run_coef<C, IO>(rp, tc_of(c_begin), int64_t(c_begin) * kQ, p.T, Ah, coef_s, misc_s);
     __syncthreads(); // ths_s, theta table
-    run_pro<C, IO>(rp, tc_of(c_begin), int64_t(c_begin) * kQ, p.T, Ah, cs_s, coef_s, misc_s, thc_s, ths_s, tht);
+    run_angles<C, IO>(rp, tc_of(c_begin), cs_s, thc_s, ths_s, tht);
     if (c_begin + 1 < c_end) {
         load_pro<C, IO>(p, b, h, int64_t(c_begin + 1) * kQ, tc_of(c_begin + 1), rp);
         load_theta<C, IO>(p, b, h, int64_t(c_begin + 1) * kQ, tc_of(c_begin + 1), rp);
     }
     __syncthreads();
+    // state at the start of this workgroup's first chunk (before the chunk loop,
+    // so that none of its loads is pending inside it)
+    {
+        const float del0 = misc_s[2];
+#pragma unroll
+        for (int j = 0; j < C::TW; ++j) {
+            const int tile = wave + kPW * j;
+            if (tile >= C::NTILE) continue;
+            const int nt = tile / PT, pt = tile - nt * PT;
+            if (OUT) {
+                if (p.S == 1) {
+                    if (p.has_init) st[j] = fold_init<C, IO>(p, bh, nt, pt, del0);
+                } else {
+                    const int pc = 16 * pt + l16;
+                    if (p.has_init) {
+                        const float *hi = p.hinit + bh * int64_t(N) * P;
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) st[j][v] = hi[(16 * nt + 4 * g + v) * P + pc];
+                    }
+                    for (int s2 = 0; s2 < seg; ++s2) {
+                        const int64_t so = bh * p.S + s2;
+                        const float eg = __expf(p.segG[so]);
+                        const float *U = p.segU + so * int64_t(N) * P;
+#pragma unroll
+                        for (int q = 0; q < 2; ++q) {
+                            const int k = 8 * nt + 2 * g + q;
+                            float sn, cs;
+                            sincos_wrapped(wrap_angle(p.segTh[so * K + k]), &sn, &cs);
+                            const float a0 = eg * st[j][2 * q], a1 = eg * st[j][2 * q + 1];
+                            st[j][2 * q] = cs * a0 - sn * a1 + U[(16 * nt + 4 * g + 2 * q) * P + pc];
+                            st[j][2 * q + 1] = sn * a0 + cs * a1 + U[(16 * nt + 4 * g + 2 * q + 1) * P + pc];
+                        }
+                    }
+                }
+                const float sv[4] = {st[j][0], st[j][1], st[j][2], st[j][3]};
+                st_planes<PL, C::HT_PS, 4>(ht + (16 * pt + l16) * NBP + 16 * nt + 4 * g, sv);
+            } else if (seg == 0 && p.has_init) {
+                const floatx4 hi4 = fold_init<C, IO>(p, bh, nt, pt, del0);
+                float *hi = p.hinit + bh * int64_t(N) * P;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) hi[(16 * nt + 4 * g + v) * P + 16 * pt + l16] = hi4[v];
+            }
+        }
+        if (!OUT && seg == 0 && p.has_init)
+            for (int k = tid; k < K; k += kPT) p.phi0ws[bh * K + k] = double(p.phi0[bh * K + k]);
+    }
 
     for (int c = c_begin; c < c_end; ++c) {
         const int64_t t0 = int64_t(c) * kQ;
@@ -572,6 +633,20 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
                 }
             }
         }
+        // Every load issued earlier has now been consumed (or, with bf16 I/O,
+        // is consumed right here: the next chunk's theta rows and
+        // coefficients); only then are the next loads issued, and none of
+        // them is touched before the next chunk, so no wait on a load is ever
+        // held up by a newer one.
+        if (C::MFP && c + 1 < c_end) {
+            write_theta<C>(rp, tht);
+            run_coef<C, IO>(rp, tc_of(c + 1), t0 + kQ, p.T, Ah, coef_s + (buf ^ 1) * (4 * kQ), misc_s + (buf ^ 1));
+        }
+        if (c + 1 < c_end) load_chunk<C, IO, OUT>(p, b, h, t0 + kQ, tc_of(c + 1), raw);
+        if (C::MFP && c + 2 < c_end) {
+            load_theta<C, IO>(p, b, h, t0 + 2 * kQ, tc_of(c + 2), rp);
+            load_pro<C, IO>(p, b, h, t0 + 2 * kQ, tc_of(c + 2), rp);
+        }
 
         // ---- a3 mask of this chunk: L[t][s] = exp(ell_t - ell_s) wgt_s (s < t),
         // gam_t (s = t), 0 (s > t); row t, 8 consecutive s per thread
@@ -604,57 +679,6 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
             }
         }
 
-        // state at the start of this workgroup's first chunk
-        if (c == c_begin) {
-            const float del0 = misc_s[2];
-#pragma unroll
-            for (int j = 0; j < C::TW; ++j) {
-                const int tile = wave + kPW * j;
-                if (tile >= C::NTILE) continue;
-                const int nt = tile / PT, pt = tile - nt * PT;
-                if (OUT) {
-                    if (p.S == 1) {
-                        if (p.has_init) st[j] = fold_init<C, IO>(p, bh, nt, pt, del0);
-                    } else {
-                        const int pc = 16 * pt + l16;
-                        if (p.has_init) {
-                            const float *hi = p.hinit + bh * int64_t(N) * P;
-#pragma unroll
-                            for (int v = 0; v < 4; ++v) st[j][v] = hi[(16 * nt + 4 * g + v) * P + pc];
-                        }
-                        for (int s2 = 0; s2 < seg; ++s2) {
-                            const int64_t so = bh * p.S + s2;
-                            const float eg = __expf(p.segG[so]);
-                            const float *U = p.segU + so * int64_t(N) * P;
-#pragma unroll
-                            for (int q = 0; q < 2; ++q) {
-                                const int k = 8 * nt + 2 * g + q;
-                                float sn, cs;
-                                sincos_wrapped(wrap_angle(p.segTh[so * K + k]), &sn, &cs);
-                                const float a0 = eg * st[j][2 * q], a1 = eg * st[j][2 * q + 1];
-                                st[j][2 * q] = cs * a0 - sn * a1 + U[(16 * nt + 4 * g + 2 * q) * P + pc];
-                                st[j][2 * q + 1] = sn * a0 + cs * a1 + U[(16 * nt + 4 * g + 2 * q + 1) * P + pc];
-                            }
-                        }
-                    }
-                    const float sv[4] = {st[j][0], st[j][1], st[j][2], st[j][3]};
-                    st_planes<PL, C::HT_PS, 4>(ht + (16 * pt + l16) * NBP + 16 * nt + 4 * g, sv);
-                } else if (seg == 0 && p.has_init) {
-                    const floatx4 hi4 = fold_init<C, IO>(p, bh, nt, pt, del0);
-                    float *hi = p.hinit + bh * int64_t(N) * P;
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) hi[(16 * nt + 4 * g + v) * P + 16 * pt + l16] = hi4[v];
-                }
-            }
-            if (!OUT && seg == 0 && p.has_init)
-                for (int k = tid; k < K; k += kPT) p.phi0ws[bh * K + k] = double(p.phi0[bh * K + k]);
-        }
-
-        // theta rows of the next chunk for its prologue (after this barrier),
-        // then the prefetch of the next chunk and of the theta after it
-        if (c + 1 < c_end) write_theta<C>(rp, tht);
-        if (c + 1 < c_end) load_chunk<C, IO, OUT>(p, b, h, t0 + kQ, tc_of(c + 1), raw);
-        if (c + 2 < c_end) load_theta<C, IO>(p, b, h, t0 + 2 * kQ, tc_of(c + 2), rp);
         __syncthreads();
 
         const float gc = misc_s[buf];
@@ -818,12 +842,13 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
         }
         gsum += gc;
 
-        // ---- a1 of the next chunk: cos/sin table, other coefficient buffer
+        // ---- a1 of the next chunk: angles (and, for fp32 I/O, coefficients)
         if (c + 1 < c_end) {
-            const int nb = buf ^ 1;
-            run_pro<C, IO>(rp, tc_of(c + 1), t0 + kQ, p.T, Ah, cs_s, coef_s + nb * (4 * kQ), misc_s + nb,
-                           thc_s + nb * K, ths_s, tht);
-            if (c + 2 < c_end) load_pro<C, IO>(p, b, h, t0 + 2 * kQ, tc_of(c + 2), rp);
+            run_angles<C, IO>(rp, tc_of(c + 1), cs_s, thc_s + (buf ^ 1) * K, ths_s, tht);
+            if constexpr (!C::MFP) {
+                run_coef<C, IO>(rp, tc_of(c + 1), t0 + kQ, p.T, Ah, coef_s + (buf ^ 1) * (4 * kQ), misc_s + (buf ^ 1));
+                if (c + 2 < c_end) load_pro<C, IO>(p, b, h, t0 + 2 * kQ, tc_of(c + 2), rp);
+            }
         }
         __syncthreads();
 

@@ -45,6 +45,10 @@ struct io;
 template <>
 struct io<float> {
     static __device__ __forceinline__ float get(const float *p) { return *p; }
+    // Raw bits of one element, and their value: a load kept as raw bits is not
+    // waited for until the value is used.
+    static __device__ __forceinline__ uint32_t raw(const float *p) { return __float_as_uint(*p); }
+    static __device__ __forceinline__ float value(uint32_t r) { return __uint_as_float(r); }
     static __device__ __forceinline__ void put(float *p, float v) { *p = v; }
     static __device__ __forceinline__ void load8(const float *p, float v[8]) {
         const float4 a = *reinterpret_cast<const float4 *>(p);
@@ -64,6 +68,8 @@ struct io<float> {
 template <>
 struct io<bf16> {
     static __device__ __forceinline__ float get(const bf16 *p) { return bits_to_f32(p->bits); }
+    static __device__ __forceinline__ uint32_t raw(const bf16 *p) { return p->bits; }
+    static __device__ __forceinline__ float value(uint32_t r) { return __uint_as_float(r << 16); }
     static __device__ __forceinline__ void put(bf16 *p, float v) { p->bits = f32_to_bits(v); }
     static __device__ __forceinline__ void load8(const bf16 *p, float v[8]) {
         const uint4 a = *reinterpret_cast<const uint4 *>(p);
