@@ -30,7 +30,7 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 METRIC = "Mamba-3 SSM prefill tokens/s + decode µs/step; % of MFMA / HBM peak"
 KERNELS = ("segment_state", "output")
 KERNEL_SOURCES = {"output": ["k_prefill.hpp", "m3_device.hpp", "m3_internal.hpp"],
-                  "decode_step": ["k_decode_step.hip", "m3_device.hpp", "m3_internal.hpp"]}
+                  "decode_step": ["k_decode.hpp", "k_decode_bf16.hip", "k_decode_f32.hip", "m3_device.hpp", "m3_internal.hpp"]}
 
 
 # ---------------------------------------------------------------------------

@@ -1,0 +1,325 @@
+// k_decode.hpp -- one fused decode step for every (batch, head).
+//
+// In the rotated (RoPE) frame of the Mamba-3 review, section 3.2.2,
+// Prop. 3.2.3, with the exponential-trapezoidal coefficients of section
+// 3.1.1, eq. (6), and the rank-R MIMO update of section 3.3:
+//   Phi   <- wrap(Phi + theta_t)                       (per rotation pair)
+//   B~    =  R(-Phi) B_t,   C~ = R(-Phi) C_t
+//   h~    <- alpha h~ + beta B~_prev x_prev^T + gamma B~ x_t^T
+//   y_t   =  C~^T h~
+//   B~_prev <- B~,  x_prev <- x_t
+// with alpha = exp(dt A), beta = (1 - lam) dt alpha, gamma = lam dt.
+//
+// Decode is bound by the read-modify-write of the fp32 state (N x P per
+// head).  Workgroups of 256 threads walk the (b, h) items grid-stride; each
+// thread owns float4 runs along P of the state, so every state access is a
+// coalesced 16-byte access, and the state of the workgroup's next item is
+// loaded while the current one is computed, so state loads are always in
+// flight.  The kernel is instantiated per (I/O type, N, P, R).  The small per-item vectors (B, C, x, x_prev, B~_prev) are read as
+// 16-byte units spread over the threads; a thread holding a unit of B or C
+// advances Phi for that unit's pairs (fp64 add and wrap, sin/cos of the angle
+// in turns) and rotates it.  Values read from the carried state are written
+// back only after the workgroup barrier, so no thread overwrites an input
+// another thread still reads.
+#pragma once
+#include "m3_device.hpp"
+#include "m3_internal.hpp"
+
+namespace m3 {
+
+constexpr int kDecodeCus = 256; // compute units of an MI355X
+// Resident decode workgroups per compute unit: each holds the state of two
+// items (current and prefetched) in registers.
+constexpr int decode_wg_per_cu(int N, int P) { return N * P > 4096 || (N > 64 && N * P >= 4096) ? 2 : 4; }
+
+template <int N, int P>
+struct DecodeLds {
+    static constexpr int K = N / 2, P4 = P / 4;
+    static constexpr int G = kThreads / P4; // row groups of the state
+    // floats: bt, bp, ct [4][N]; x, xp [4][P]; phi' [K]; a 16-byte sink for
+    // threads without a unit; red [G][4][P]
+    static constexpr int o_bt = 0, o_bp = o_bt + 4 * N, o_ct = o_bp + 4 * N;
+    static constexpr int o_x = o_ct + 4 * N, o_xp = o_x + 4 * P, o_ph = o_xp + 4 * P;
+    static constexpr int o_sink = o_ph + (K + 3) / 4 * 4, o_red = o_sink + 4;
+    static constexpr size_t floats = size_t(o_red) + size_t(G) * 4 * P;
+};
+
+// Rotation of one unit of B or C: EPU elements (EPU/2 pairs) by -Phi' with
+// Phi' = wrap(Phi + theta) (fp64 add and wrap; sin and cos of the angle in
+// turns).  Returns Phi' of the pairs in phn.
+template <int NP>
+__device__ __forceinline__ void rotate_unit(float *e, const float *ph, const float *th, float *phn) {
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+        const double a = wrap_angle(double(ph[j]) + double(th[j]));
+        float tf = float(a * (1.0 / kTwoPi));
+        tf -= rintf(tf);
+        const float sn = __builtin_amdgcn_sinf(tf), cs = __builtin_amdgcn_cosf(tf);
+        rot_neg(cs, sn, e[2 * j], e[2 * j + 1]);
+        phn[j] = float(a);
+    }
+}
+
+__device__ __forceinline__ void unpack16(const uint4 &u, float *v, bf16) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __uint_as_float(w[i] << 16);
+        v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+}
+__device__ __forceinline__ void unpack16(const uint4 &u, float *v, float) {
+    v[0] = __uint_as_float(u.x); v[1] = __uint_as_float(u.y);
+    v[2] = __uint_as_float(u.z); v[3] = __uint_as_float(u.w);
+}
+// theta of EPU/2 pairs held as 8 raw bytes
+__device__ __forceinline__ void unpack8(const uint2 &u, float *v, bf16) {
+    v[0] = __uint_as_float(u.x << 16); v[1] = __uint_as_float(u.x & 0xffff0000u);
+    v[2] = __uint_as_float(u.y << 16); v[3] = __uint_as_float(u.y & 0xffff0000u);
+}
+__device__ __forceinline__ void unpack8(const uint2 &u, float *v, float) {
+    v[0] = __uint_as_float(u.x); v[1] = __uint_as_float(u.y);
+}
+
+// The small per-item vectors are cut into 16-byte units, numbered
+// B (R*N/EPU units), C (same), x (R*P/EPU), x_prev (same), B~_prev (R*N/4,
+// fp32).  A thread owns units tid, tid + 256, ...; the unit's kind, its
+// source offset, item stride and LDS destination are fixed for the launch.
+enum : int { kUnitB = 0, kUnitC = 1, kUnitX = 2, kUnitXp = 3, kUnitBp = 4, kUnitNone = 5 };
+
+template <typename IO, int N, int P, int R>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode_wg_per_cu(N, P)))) void k_decode_step(const DecodeParams p) {
+    typedef DecodeLds<N, P> L;
+    constexpr int K = N / 2, P4 = L::P4, G = L::G;
+    constexpr int SZ = int(sizeof(IO)), EPU = 16 / SZ, NPU = EPU / 2;
+    constexpr int SLOTS = N * P4;                          // float4 runs in the state
+    constexpr int SPT = (SLOTS + kThreads - 1) / kThreads; // runs per thread
+    constexpr int URN = N * SZ / 16, URP = P * SZ / 16;    // 16-byte units per row of B/C and of x
+    constexpr int UB = R * URN, UX = R * URP, UPB = R * N / 4, UT = 2 * UB + 2 * UX + UPB;
+    constexpr int UPT = (UT + kThreads - 1) / kThreads;    // units per thread
+    constexpr int64_t sB = int64_t(R) * N * SZ, sX = int64_t(R) * P * SZ, sBp = int64_t(R) * N * 4; // item strides
+    __shared__ __align__(16) float sm[L::floats];
+    float *bt_s = sm + L::o_bt, *bp_s = sm + L::o_bp, *ct_s = sm + L::o_ct;
+    float *x_s = sm + L::o_x, *xp_s = sm + L::o_xp, *ph_s = sm + L::o_ph, *red = sm + L::o_red;
+
+    const int tid = threadIdx.x;
+    const int64_t BH = p.batch * p.H;
+    const int pg = tid % P4, rg = tid / P4;
+
+    // ---- per-thread unit table (launch constant)
+    int ukind[UPT], uw[UPT], udst[UPT], uk0[UPT];
+    const char *ubase[UPT];
+#pragma unroll
+    for (int j = 0; j < UPT; ++j) {
+        const int u = tid + j * kThreads;
+        int kind, w;
+        if (u < UB) kind = kUnitB, w = u;
+        else if (u < 2 * UB) kind = kUnitC, w = u - UB;
+        else if (u < 2 * UB + UX) kind = kUnitX, w = u - 2 * UB;
+        else if (u < 2 * UB + 2 * UX) kind = kUnitXp, w = u - 2 * UB - UX;
+        else if (u < UT) kind = kUnitBp, w = u - 2 * UB - 2 * UX;
+        else kind = kUnitNone, w = 0;
+        const void *b = kind == kUnitC ? p.C : kind == kUnitX ? p.x : kind == kUnitXp ? p.prevx : kind == kUnitBp ? static_cast<const void *>(p.prevB) : p.B;
+        ukind[j] = kind;
+        uw[j] = w;
+        ubase[j] = static_cast<const char *>(b) + int64_t(w) * 16;
+        udst[j] = kind == kUnitB ? L::o_bt + w * EPU : kind == kUnitC ? L::o_ct + w * EPU : kind == kUnitX ? L::o_x + w * EPU
+                : kind == kUnitXp ? L::o_xp + w * EPU : kind == kUnitBp ? L::o_bp + 4 * w : L::o_sink;
+        uk0[j] = kind <= kUnitC ? (w % URN) * NPU : 0;
+    }
+
+    // Every global load below is issued unconditionally (indices clamped) and
+    // its value is consumed on every path, so no load sinks into a branch and
+    // the compiler's wait counts are exact: waiting for an item's small
+    // vectors never waits for the state prefetch issued after them.
+    // The state of an item is SLOTS consecutive float4 runs; run tid + 256 j
+    // is row (tid + 256 j) / P4, columns 4 pg .. 4 pg + 3.
+    const int tslot = min(tid, SLOTS - 1);
+    auto load_state = [&](int64_t item, float4 *hv) {
+        const float4 *hs = reinterpret_cast<const float4 *>(p.h) + item * SLOTS;
+#pragma unroll
+        for (int j = 0; j < SPT; ++j) hv[j] = hs[j * kThreads + tslot];
+    };
+
+    auto step = [&](const int64_t item, const int h, const float4 *hc, float4 *hx) {
+        // ---- issue: small vectors of this item, then the next item's state
+        uint4 ud[UPT];
+        uint2 ut[UPT];
+        float ph[UPT][NPU];
+#pragma unroll
+        for (int j = 0; j < UPT; ++j) {
+            const int64_t st = ukind[j] == kUnitBp ? sBp : (ukind[j] == kUnitX || ukind[j] == kUnitXp) ? sX : sB;
+            ud[j] = *reinterpret_cast<const uint4 *>(ubase[j] + item * st);
+            ut[j] = *reinterpret_cast<const uint2 *>(static_cast<const IO *>(p.theta) + item * K + uk0[j]);
+            if constexpr (NPU == 4) {
+                const float4 a = *reinterpret_cast<const float4 *>(p.phi + item * K + uk0[j]);
+                ph[j][0] = a.x; ph[j][1] = a.y; ph[j][2] = a.z; ph[j][3] = a.w;
+            } else {
+                const float2 a = *reinterpret_cast<const float2 *>(p.phi + item * K + uk0[j]);
+                ph[j][0] = a.x; ph[j][1] = a.y;
+            }
+        }
+        const uint32_t dt_raw = io<IO>::raw(static_cast<const IO *>(p.dt) + item);
+        const uint32_t lam_raw = io<IO>::raw(static_cast<const IO *>(p.lam) + item);
+        const float Ah = p.A[h];
+        const int64_t nx = item + gridDim.x < BH ? item + gridDim.x : item;
+        load_state(nx, hx);
+
+        // ---- rotate B and C (every unit computes the rotation; only B and C
+        // units keep it), stage them and x, x_prev, B~_prev in LDS
+#pragma unroll
+        for (int j = 0; j < UPT; ++j) {
+            const int kind = ukind[j];
+            const bool rot = kind <= kUnitC;
+            float e[EPU], th[NPU], phn[NPU];
+            unpack16(ud[j], e, IO());
+            unpack8(ut[j], th, IO());
+            float o[EPU];
+#pragma unroll
+            for (int i = 0; i < EPU; ++i) o[i] = e[i];
+            rotate_unit<NPU>(o, ph[j], th, phn);
+#pragma unroll
+            for (int i = 0; i < EPU; ++i) o[i] = rot ? o[i] : e[i];
+            float4 v0 = make_float4(o[0], o[1], o[2], o[3]);
+            if (kind == kUnitBp) v0 = make_float4(__uint_as_float(ud[j].x), __uint_as_float(ud[j].y), __uint_as_float(ud[j].z), __uint_as_float(ud[j].w));
+            *reinterpret_cast<float4 *>(sm + udst[j]) = v0;
+            if constexpr (EPU == 8)
+                if (kind <= kUnitXp) *reinterpret_cast<float4 *>(sm + udst[j] + 4) = make_float4(o[4], o[5], o[6], o[7]);
+            if (kind == kUnitB && uw[j] < URN) {
+                float *pd = ph_s + uw[j] * NPU;
+                if constexpr (NPU == 4) *reinterpret_cast<float4 *>(pd) = make_float4(phn[0], phn[1], phn[2], phn[3]);
+                else *reinterpret_cast<float2 *>(pd) = make_float2(phn[0], phn[1]);
+            }
+            __builtin_amdgcn_sched_barrier(0); // one unit at a time: bounds register use
+        }
+        __syncthreads();
+
+        // ---- carried small state: B~_prev <- B~, x_prev <- x, Phi <- Phi'
+        for (int w = tid; w < UPB; w += kThreads)
+            *reinterpret_cast<float4 *>(p.prevB + item * R * N + 4 * w) = *reinterpret_cast<const float4 *>(bt_s + 4 * w);
+        for (int w = tid; w < UX; w += kThreads) {
+            const float *s = x_s + w * EPU;
+            IO *d = static_cast<IO *>(p.prevx) + item * R * P + w * EPU;
+#pragma unroll
+            for (int i = 0; i < EPU; i += 4) io<IO>::store4(d + i, s + i);
+        }
+        for (int k = tid; k < K; k += kThreads) p.phi[item * K + k] = ph_s[k];
+
+        // ---- state update and partial outputs
+        const float dtv = io<IO>::value(dt_raw), lamv = io<IO>::value(lam_raw);
+        const float alpha = __expf(dtv * Ah);
+        const float beta = (1.f - lamv) * dtv * alpha;
+        const float gamma = lamv * dtv;
+        float4 *hs = reinterpret_cast<float4 *>(p.h) + item * SLOTS;
+        float yp[R][4];
+#pragma unroll
+        for (int i = 0; i < R; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) yp[i][q] = 0.f;
+#pragma unroll
+        for (int j = 0; j < SPT; ++j) {
+            const int slot = tid + j * kThreads;
+            if (SLOTS % kThreads != 0 && slot >= SLOTS) continue;
+            const int n = slot / P4;
+            float u[4] = {alpha * hc[j].x, alpha * hc[j].y, alpha * hc[j].z, alpha * hc[j].w};
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const float cb = beta * bp_s[r * N + n], cg = gamma * bt_s[r * N + n];
+                const float4 xp4 = *reinterpret_cast<const float4 *>(xp_s + r * P + 4 * pg);
+                const float4 x4 = *reinterpret_cast<const float4 *>(x_s + r * P + 4 * pg);
+                u[0] += cb * xp4.x + cg * x4.x;
+                u[1] += cb * xp4.y + cg * x4.y;
+                u[2] += cb * xp4.z + cg * x4.z;
+                u[3] += cb * xp4.w + cg * x4.w;
+            }
+            hs[slot] = make_float4(u[0], u[1], u[2], u[3]);
+#pragma unroll
+            for (int i = 0; i < R; ++i) {
+                const float cc = ct_s[i * N + n];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) yp[i][q] += cc * u[q];
+            }
+            __builtin_amdgcn_sched_barrier(0); // one run at a time: bounds register use
+        }
+#pragma unroll
+        for (int i = 0; i < R; ++i)
+            *reinterpret_cast<float4 *>(red + (rg * 4 + i) * P + 4 * pg) = make_float4(yp[i][0], yp[i][1], yp[i][2], yp[i][3]);
+        __syncthreads();
+
+        // y: four consecutive outputs per thread, one 4-element store
+        IO *y = static_cast<IO *>(p.y) + item * R * P;
+        constexpr int GACT = G < N ? G : N; // row groups that own at least one row
+        for (int o = 4 * tid; o < R * P; o += 4 * kThreads) {
+            const int i = o / P, pc = o - i * P;
+            float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int r = 0; r < GACT; ++r) {
+                const float4 v = *reinterpret_cast<const float4 *>(red + (r * 4 + i) * P + pc);
+                s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+            }
+            const float sv[4] = {s.x, s.y, s.z, s.w};
+            io<IO>::store4(y + o, sv);
+        }
+    };
+
+    // Two items per trip, the state registers swapping roles, so the
+    // prefetched state is never copied (a copy would wait for it).
+    float4 ha[SPT], hb[SPT];
+    int64_t item = blockIdx.x; // the grid never exceeds the item count
+    int h = int(item % p.H);   // head of the item, advanced without a division
+    const int hstep = int(gridDim.x % unsigned(p.H));
+    auto advance = [&]() {
+        item += gridDim.x;
+        h += hstep;
+        if (h >= p.H) h -= p.H;
+    };
+    load_state(item, ha);
+    for (;;) {
+        step(item, h, ha, hb);
+        advance();
+        if (item >= BH) break;
+        step(item, h, hb, ha);
+        advance();
+        if (item >= BH) break;
+    }
+}
+
+template <typename IO, int N, int P, int R>
+hipError_t launch_decode_inst(const DecodeParams &p, hipStream_t s) {
+    const int64_t bh = p.batch * p.H;
+    const int64_t cap = int64_t(kDecodeCus) * decode_wg_per_cu(N, P);
+    const dim3 grid{static_cast<unsigned>(bh < cap ? bh : cap)}, block{kThreads};
+    hipLaunchKernelGGL((k_decode_step<IO, N, P, R>), grid, block, 0, s, p);
+    return hipGetLastError();
+}
+
+// Dispatch over (N, P, R) for one I/O type.
+template <typename IO>
+hipError_t launch_decode_io(const DecodeParams &p, hipStream_t s) {
+#define M3_DECODE_R(NN, PP)                                                   \
+    switch (p.R) {                                                            \
+    case 1: return launch_decode_inst<IO, NN, PP, 1>(p, s);                   \
+    case 2: return launch_decode_inst<IO, NN, PP, 2>(p, s);                   \
+    case 3: return launch_decode_inst<IO, NN, PP, 3>(p, s);                   \
+    case 4: return launch_decode_inst<IO, NN, PP, 4>(p, s);                   \
+    default: return hipErrorInvalidValue;                                     \
+    }
+#define M3_DECODE_P(NN)                                                       \
+    switch (p.P) {                                                            \
+    case 16: M3_DECODE_R(NN, 16)                                              \
+    case 32: M3_DECODE_R(NN, 32)                                              \
+    case 64: M3_DECODE_R(NN, 64)                                              \
+    default: return hipErrorInvalidValue;                                     \
+    }
+    switch (p.N) {
+    case 16: M3_DECODE_P(16)
+    case 32: M3_DECODE_P(32)
+    case 64: M3_DECODE_P(64)
+    case 128: M3_DECODE_P(128)
+    default: return hipErrorInvalidValue;
+    }
+#undef M3_DECODE_P
+#undef M3_DECODE_R
+}
+
+} // namespace m3

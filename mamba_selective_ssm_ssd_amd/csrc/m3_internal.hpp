@@ -60,7 +60,8 @@ hipError_t launch_prefill_f32_n32(const PrefillParams &p, bool out, hipStream_t 
 hipError_t launch_prefill_f32_n64(const PrefillParams &p, bool out, hipStream_t s);
 hipError_t launch_prefill_f32_n128(const PrefillParams &p, bool out, hipStream_t s);
 
-hipError_t launch_decode_step(const DecodeParams &p, bool is_bf16, hipStream_t s);
+hipError_t launch_decode_bf16(const DecodeParams &p, hipStream_t s);
+hipError_t launch_decode_f32(const DecodeParams &p, hipStream_t s);
 
 // Dynamic LDS bytes of the fused prefill kernel for a shape (0: not compiled).
 size_t prefill_lds_bytes(bool is_bf16, int N, int P, int R);

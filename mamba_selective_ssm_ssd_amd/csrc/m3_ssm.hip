@@ -244,7 +244,8 @@ m3_status_t m3_ssm_decode_step(const m3_shape_t *shape, const void *x, const voi
     p.K = p.N / 2;
     p.x = x; p.dt = dt; p.lam = lam; p.theta = theta; p.B = B; p.C = C; p.A = A; p.y = y;
     p.h = state->h; p.phi = state->phi; p.prevB = state->prev_B; p.prevx = state->prev_x;
-    if (m3::launch_decode_step(p, shape->io_dtype == M3_DTYPE_BF16, stream) != hipSuccess) return M3_ERR_HIP;
+    if ((shape->io_dtype == M3_DTYPE_BF16 ? m3::launch_decode_bf16(p, stream) : m3::launch_decode_f32(p, stream)) != hipSuccess)
+        return M3_ERR_HIP;
     return M3_OK;
 }
 
