@@ -323,17 +323,34 @@ __device__ __forceinline__ void run_angles(const RawPro<C> &r, int Tc, float *cs
     if constexpr (C::MFP) {
         // Phi[t][k] = sum_{s <= t} theta[s][k] as (lower-triangular ones) x theta,
         // one 16x16 tile (16 tokens x 16 pairs) per step; the chunk total is
-        // the row of token Tc-1
+        // the row of token Tc-1.  Every tile takes both 32-token k-steps (the
+        // ones matrix is zero beyond the tile's last token), so a wave issues
+        // all its operand reads, then all its products, then the sin/cos.
         typedef typename C::M M;
         const int g = lane >> 4, l16 = lane & 15;
+        if (mfp_tile<C>(wave, 0) < 0) return;
+        constexpr int KB = kQ / 32;
+        typename M::frag bf[C::TPW][KB];
+        int tbm[C::TPW], pbm[C::TPW];
 #pragma unroll
         for (int m = 0; m < C::TPW; ++m) {
             const int tile = mfp_tile<C>(wave, m);
-            if (tile < 0) continue;
-            const int tb = tile & 3, pb = tile >> 2;
-            const int trow = 16 * tb + l16; // A row of this lane
-            floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
-            for (int kb = 0; 32 * kb <= 16 * tb + 15; ++kb) {
+            const int tl = tile < 0 ? 0 : tile;
+            tbm[m] = tl & 3;
+            pbm[m] = tl >> 2;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                const uint16_t *bp = tht + (32 * kb + 8 * g + (l16 >> 2)) * C::THP + 16 * pbm[m] + 4 * (l16 & 3);
+                bf[m][kb] = M::template tr8<0>(bp, bp + 4 * C::THP);
+            }
+        }
+        floatx4 acc[C::TPW];
+#pragma unroll
+        for (int m = 0; m < C::TPW; ++m) {
+            const int trow = 16 * tbm[m] + l16; // A row of this lane
+            acc[m] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
                 uint32_t w[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -342,20 +359,23 @@ __device__ __forceinline__ void run_angles(const RawPro<C> &r, int Tc, float *cs
                 }
                 typename M::frag a;
                 a.v[0] = bf16x8_from_words(w[0], w[1], w[2], w[3]);
-                const uint16_t *bp = tht + (32 * kb + 8 * g + (l16 >> 2)) * C::THP + 16 * pb + 4 * (l16 & 3);
-                acc = M::mma(acc, a, M::template tr8<0>(bp, bp + 4 * C::THP));
+                acc[m] = M::mma(acc[m], a, bf[m][kb]);
             }
-            const int pair = 16 * pb + l16;
+        }
+#pragma unroll
+        for (int m = 0; m < C::TPW; ++m) {
+            if (mfp_tile<C>(wave, m) < 0) continue;
+            const int pair = 16 * pbm[m] + l16;
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                const int t = 16 * tb + 4 * g + v;
-                float tf = acc[v] * float(1.0 / kTwoPi);
+                const int t = 16 * tbm[m] + 4 * g + v;
+                float tf = acc[m][v] * float(1.0 / kTwoPi);
                 tf -= rintf(tf);
                 const float sn = __builtin_amdgcn_sinf(tf), cn = __builtin_amdgcn_cosf(tf);
                 *reinterpret_cast<float2 *>(cs + t * C::CSP + 2 * pair) = make_float2(cn, sn);
                 if (t == Tc - 1) {
                     thc[pair] = make_float2(cn, sn);
-                    ths[pair] += double(acc[v]);
+                    ths[pair] += double(acc[m][v]);
                 }
             }
         }
@@ -575,7 +595,7 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
 #pragma unroll
         for (int j = 0; j < C::UPT_B; ++j) {
             const int u = tid + j * kPT;
-            if (u < C::UB) {
+            if (C::UB % kPT == 0 || u < C::UB) {
                 const int v = u / C::URB, q = u - v * C::URB;
                 float e[EPU];
                 unpack_unit(raw.bb[j], e, IO());
@@ -592,7 +612,7 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
 #pragma unroll
         for (int j = 0; j < C::UPT_X; ++j) {
             const int u = tid + j * kPT;
-            if (u < C::UX) {
+            if (C::UX % kPT == 0 || u < C::UX) {
                 const int v = u / C::URX, q = u - v * C::URX;
                 float e[EPU];
                 unpack_unit(raw.xx[j], e, IO());
@@ -613,6 +633,7 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
 #pragma unroll
             for (int i = 0; i < C::TBW; ++i) {
                 const int tb = wave_block(i, wave);
+                if (tb >= C::NTB) continue; // uniform: waves without this row block
                 const int tok = (16 * tb + l16) / R;
 #pragma unroll
                 for (int ks = 0; ks < NKS; ++ks) {
@@ -620,7 +641,7 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
                     float e[8];
 #pragma unroll
                     for (int f = 0; f < C::FU; ++f) unpack_unit(raw.cc[i][ks][f], e + f * EPU, IO());
-                    if (tb < C::NTB && n0 < N) {
+                    if (N % 32 == 0 || n0 < N) {
                         const float4 *cr = reinterpret_cast<const float4 *>(cs_s + tok * C::CSP + n0);
 #pragma unroll
                         for (int w4 = 0; w4 < 2; ++w4) {
@@ -654,7 +675,8 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
             if (OUT) {
                 const int tt = tid >> 3, s0 = (tid & 7) * 8;
                 float w[8];
-                if (s0 <= tt) {
+                {
+                    // branch-free: every entry is evaluated, then selected
                     const float et = ell_s[tt], gt = gam_s[tt];
                     const float4 e0 = *reinterpret_cast<const float4 *>(ell_s + s0);
                     const float4 e1 = *reinterpret_cast<const float4 *>(ell_s + s0 + 4);
@@ -664,13 +686,13 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
                     const float wg[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
 #pragma unroll
                     for (int j = 0; j < 8; ++j) {
+                        // exp of a selected argument (0 where masked), then 0/1
+                        // weights: no select or branch around the exp
                         const int ts = s0 + j;
-                        const float e = __expf(ts < tt ? et - el[j] : 0.f) * wg[j];
-                        w[j] = ts < tt ? e : (ts == tt ? gt : 0.f);
+                        const float lt = ts < tt ? 1.f : 0.f, eq = ts == tt ? 1.f : 0.f;
+                        const float e = __expf(ts < tt ? et - el[j] : 0.f);
+                        w[j] = lt * (e * wg[j]) + eq * gt;
                     }
-                } else {
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) w[j] = 0.f;
                 }
                 float4 *dst = reinterpret_cast<float4 *>(lw_s + tt * C::LWP + s0);
                 dst[0] = make_float4(w[0], w[1], w[2], w[3]);
