@@ -124,7 +124,13 @@ struct Cfg {
     // The scaled copy of x (the state update's second operand) is kept when
     // it fits; otherwise the scale is applied to that operand's fragments.
     static constexpr bool XS = o_xs + xs_bytes <= kMaxLdsBytes;
-    static constexpr size_t bytes = o_xs + (XS ? xs_bytes : 0);
+    // When some waves own no intra-chunk row block, the rotated C is staged in
+    // LDS by all waves (as B is) instead of by the row-block waves into their
+    // registers, when it fits; the row-block waves then read their fragments.
+    static constexpr size_t o_cl = align16(o_xs + (XS ? xs_bytes : 0));       // [PL][V][NBP] rotated C
+    static constexpr size_t cl_bytes = size_t(PL) * BS_PS * 2;
+    static constexpr bool CL = FREEW > 0 && o_cl + cl_bytes <= kMaxLdsBytes;
+    static constexpr size_t bytes = o_cl + (CL ? cl_bytes : 0);
     static_assert(K * SZ % 16 == 0 && N % 16 == 0 && P % 16 == 0 && K % 8 == 0, "tile sizes");
     static_assert(FREEW ? NG8 <= FREEW * GPW : NG8 <= kPW, "angle groups per wave");
 };
@@ -133,7 +139,8 @@ struct Cfg {
 template <class C>
 struct RawChunk {
     uint4 bb[C::UPT_B], xx[C::UPT_X];
-    uint4 cc[C::TBW][C::NKS][C::FU];
+    uint4 cc[C::CL ? 1 : C::TBW][C::CL ? 1 : C::NKS][C::CL ? 1 : C::FU]; // C of this wave's row blocks
+    uint4 cu[C::CL ? C::UPT_B : 1];                                       // C units, spread as B's (CL)
 };
 
 // Raw prologue inputs of one chunk: a group of 8 rotation angles of this
@@ -183,14 +190,17 @@ __device__ __forceinline__ int wave_block(int i, int wave) { return i == 0 ? wav
 
 // Loads chunk (b, h, t0 .. t0+Tc-1)'s B, x and C into registers.  Addresses
 // are a uniform per-chunk base plus a 32-bit per-thread offset (saddr +
-// voffset addressing).
+// voffset addressing).  Every load is issued (indices clamped to the last
+// unit and the last token): a token past Tc repeats token Tc-1, whose finite
+// values meet only zero mask entries, zero state-update scales and outputs
+// that are not stored.  With no load under a condition the compiler's wait
+// counts stay exact.
 // PARTS selects what is loaded: bit 0 B, bit 1 x, bit 2 C.
 template <class C, typename IO, bool OUT, int PARTS = 7>
 __device__ __forceinline__ void load_chunk(const PrefillParams &p, int64_t b, int h, int64_t t0, int Tc,
                                            RawChunk<C> &r) {
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const int g = lane >> 4, l16 = lane & 15;
-    const uint4 z = make_uint4(0u, 0u, 0u, 0u);
     const int64_t tokbase = (b * p.T + t0) * p.H + h; // token-head index of t0
     const int H = p.H;
     const IO *Bp = static_cast<const IO *>(p.B) + tokbase * (C::R * C::N);
@@ -198,42 +208,39 @@ __device__ __forceinline__ void load_chunk(const PrefillParams &p, int64_t b, in
     const IO *Cp = static_cast<const IO *>(p.C) + tokbase * (C::R * C::N);
 #pragma unroll
     for (int j = 0; j < ((PARTS & 1) ? C::UPT_B : 0); ++j) {
-        const int u = tid + j * kPT;
-        r.bb[j] = z;
-        if (u < C::UB) {
-            const int v = u / C::URB, q = u - v * C::URB;
-            const int tok = v / C::R, ch = v - tok * C::R;
-            if (tok < Tc)
-                r.bb[j] = *reinterpret_cast<const uint4 *>(Bp + ((tok * H * C::R + ch) * C::N + q * C::EPU));
-        }
+        const int u = min(tid + j * kPT, C::UB - 1);
+        const int v = u / C::URB, q = u - v * C::URB;
+        const int tok = min(v / C::R, Tc - 1), ch = v % C::R;
+        r.bb[j] = ld16(Bp + ((tok * H * C::R + ch) * C::N + q * C::EPU));
     }
 #pragma unroll
     for (int j = 0; j < ((PARTS & 2) ? C::UPT_X : 0); ++j) {
-        const int u = tid + j * kPT;
-        r.xx[j] = z;
-        if (u < C::UX) {
-            const int v = u / C::URX, q = u - v * C::URX;
-            const int tok = v / C::R, ch = v - tok * C::R;
-            if (tok < Tc)
-                r.xx[j] = *reinterpret_cast<const uint4 *>(Xp + ((tok * H * C::R + ch) * C::P + q * C::EPU));
-        }
+        const int u = min(tid + j * kPT, C::UX - 1);
+        const int v = u / C::URX, q = u - v * C::URX;
+        const int tok = min(v / C::R, Tc - 1), ch = v % C::R;
+        r.xx[j] = ld16(Xp + ((tok * H * C::R + ch) * C::P + q * C::EPU));
     }
-    if (OUT && (PARTS & 4)) {
+    if constexpr (OUT && (PARTS & 4) && C::CL) {
+#pragma unroll
+        for (int j = 0; j < C::UPT_B; ++j) {
+            const int u = min(tid + j * kPT, C::UB - 1);
+            const int v = u / C::URB, q = u - v * C::URB;
+            const int tok = min(v / C::R, Tc - 1), ch = v % C::R;
+            r.cu[j] = ld16(Cp + ((tok * H * C::R + ch) * C::N + q * C::EPU));
+        }
+    } else if (OUT && (PARTS & 4)) {
 #pragma unroll
         for (int i = 0; i < C::TBW; ++i) {
-            const int tb = wave_block(i, wave);
+            // a wave without this row block loads the last block's rows (unused)
+            const int tb = min(wave_block(i, wave), C::NTB - 1);
             const int v = 16 * tb + l16;
-            const int tok = v / C::R, ch = v - tok * C::R;
+            const int tok = min(v / C::R, Tc - 1), ch = v % C::R;
 #pragma unroll
             for (int ks = 0; ks < C::NKS; ++ks) {
-                const int n0 = 32 * ks + 8 * g;
+                const int n0 = min(32 * ks + 8 * g, C::N - 8);
 #pragma unroll
-                for (int f = 0; f < C::FU; ++f) {
-                    r.cc[i][ks][f] = z;
-                    if (tb < C::NTB && n0 < C::N && tok < Tc)
-                        r.cc[i][ks][f] = *reinterpret_cast<const uint4 *>(
-                            Cp + ((tok * H * C::R + ch) * C::N + n0 + f * C::EPU));
-                }
+                for (int f = 0; f < C::FU; ++f)
+                    r.cc[i][ks][f] = ld16(Cp + ((tok * H * C::R + ch) * C::N + n0 + f * C::EPU));
             }
         }
     }
@@ -257,22 +264,22 @@ __device__ __forceinline__ void load_pro(const PrefillParams &p, int64_t b, int 
             for (int f = 0; f < C::GU; ++f) {
                 r.th[m][f] = make_uint4(0u, 0u, 0u, 0u);
                 if (grp >= 0 && lane < Tc)
-                    r.th[m][f] = *reinterpret_cast<const uint4 *>(th + (lane * H * C::K + 8 * grp + f * C::EPU));
+                    r.th[m][f] = ld16(th + (lane * H * C::K + 8 * grp + f * C::EPU));
             }
         }
     }
     r.dt = r.lam = r.dtn = r.lamn = 0u;
     if (wave == C::CW) {
+        // token past Tc: repeats token Tc-1; next chunk's first token: clamped
+        // to the last token (its delta is not used when t0 + 64 >= T)
         const IO *dt = static_cast<const IO *>(p.dt) + tokbase;
         const IO *lam = static_cast<const IO *>(p.lam) + tokbase;
-        if (lane < Tc) {
-            r.dt = io<IO>::raw(dt + lane * H);
-            r.lam = io<IO>::raw(lam + lane * H);
-        }
-        if (lane == kWave - 1 && t0 + kQ < p.T) {
-            r.dtn = io<IO>::raw(dt + kQ * H);
-            r.lamn = io<IO>::raw(lam + kQ * H);
-        }
+        const int lt = min(lane, Tc - 1);
+        const int64_t tn = min<int64_t>(kQ, p.T - 1 - t0);
+        r.dt = io<IO>::raw(dt + lt * H);
+        r.lam = io<IO>::raw(lam + lt * H);
+        r.dtn = io<IO>::raw(dt + tn * H);
+        r.lamn = io<IO>::raw(lam + tn * H);
     }
 }
 
@@ -287,10 +294,10 @@ __device__ __forceinline__ void load_theta(const PrefillParams &p, int64_t b, in
 #pragma unroll
         for (int j = 0; j < C::UPT_T; ++j) {
             const int u = threadIdx.x + j * kPT;
-            const int tok = u / C::URT, q = u - tok * C::URT;
-            r.thu[j] = make_uint4(0u, 0u, 0u, 0u);
-            if (u < C::UT && tok < Tc)
-                r.thu[j] = *reinterpret_cast<const uint4 *>(th + (tok * H * C::K + q * C::EPU));
+            const int uc = u < C::UT ? u : C::UT - 1;
+            const int tr = uc / C::URT, q = uc - tr * C::URT;
+            const int tok = tr < Tc ? tr : Tc - 1; // a row past Tc repeats row Tc-1
+            r.thu[j] = ld16(th + (tok * H * C::K + q * C::EPU));
         }
     }
 }
@@ -479,6 +486,9 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
     constexpr int PT = C::PT, NKS = C::NKS;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const int g = lane >> 4, l16 = lane & 15;
+    // bf16 I/O with a wave free of intra-chunk rows: that wave scans the next
+    // chunk's coefficients in the second phase instead of the first
+    constexpr bool CP2 = C::MFP && C::FREEW > 0;
 
     // workgroup -> (b, h, segment); consecutive heads land on the same XCD
     const int nseg = OUT ? p.S : p.S - 1;
@@ -497,6 +507,7 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
     uint16_t *xr = reinterpret_cast<uint16_t *>(smem + C::o_xr);   // x, row-major
     uint16_t *ht = reinterpret_cast<uint16_t *>(smem + C::o_ht);   // state, [p][n]
     uint16_t *xs = reinterpret_cast<uint16_t *>(smem + C::o_xs);   // scaled x, row-major (XS)
+    uint16_t *cl = reinterpret_cast<uint16_t *>(smem + C::o_cl);   // rotated C, row-major (CL)
     float *cs_s = reinterpret_cast<float *>(smem + C::o_cs);       // [64][CSP]
     float *coef_s = reinterpret_cast<float *>(smem + C::o_coef);   // [2][4][64]
     float *misc_s = reinterpret_cast<float *>(smem + C::o_misc);   // g_c [2], delta_0 [2]
@@ -600,13 +611,20 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
                 float e[EPU];
                 unpack_unit(raw.bb[j], e, IO());
                 const float4 *cr = reinterpret_cast<const float4 *>(cs_s + (v / R) * C::CSP + q * EPU);
+                float ec[EPU];
+                if constexpr (OUT && C::CL) unpack_unit(raw.cu[j], ec, IO());
 #pragma unroll
                 for (int w4 = 0; w4 < EPU / 4; ++w4) {
                     const float4 a = cr[w4];
                     rot_neg(a.x, a.y, e[4 * w4], e[4 * w4 + 1]);
                     rot_neg(a.z, a.w, e[4 * w4 + 2], e[4 * w4 + 3]);
+                    if constexpr (OUT && C::CL) {
+                        rot_neg(a.x, a.y, ec[4 * w4], ec[4 * w4 + 1]);
+                        rot_neg(a.z, a.w, ec[4 * w4 + 2], ec[4 * w4 + 3]);
+                    }
                 }
                 st_planes<PL, C::BS_PS, EPU>(bs + v * NBP + q * EPU, e);
+                if constexpr (OUT && C::CL) st_planes<PL, C::BS_PS, EPU>(cl + v * NBP + q * EPU, ec);
             }
         }
 #pragma unroll
@@ -629,7 +647,7 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
             }
         }
         frag cf[C::TBW][NKS];
-        if (OUT) {
+        if (OUT && !C::CL) {
 #pragma unroll
             for (int i = 0; i < C::TBW; ++i) {
                 const int tb = wave_block(i, wave);
@@ -655,18 +673,19 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
             }
         }
         // Every load issued earlier has now been consumed (or, with bf16 I/O,
-        // is consumed right here: the next chunk's theta rows and
-        // coefficients); only then are the next loads issued, and none of
-        // them is touched before the next chunk, so no wait on a load is ever
-        // held up by a newer one.
+        // is consumed right here: the next chunk's theta rows and, without a
+        // free coefficient wave, coefficients); only then are the next loads
+        // issued, and none of them is touched before the next chunk, so no
+        // wait on a load is ever held up by a newer one.
         if (C::MFP && c + 1 < c_end) {
             write_theta<C>(rp, tht);
-            run_coef<C, IO>(rp, tc_of(c + 1), t0 + kQ, p.T, Ah, coef_s + (buf ^ 1) * (4 * kQ), misc_s + (buf ^ 1));
+            if constexpr (!CP2)
+                run_coef<C, IO>(rp, tc_of(c + 1), t0 + kQ, p.T, Ah, coef_s + (buf ^ 1) * (4 * kQ), misc_s + (buf ^ 1));
         }
         if (c + 1 < c_end) load_chunk<C, IO, OUT>(p, b, h, t0 + kQ, tc_of(c + 1), raw);
         if (C::MFP && c + 2 < c_end) {
             load_theta<C, IO>(p, b, h, t0 + 2 * kQ, tc_of(c + 2), rp);
-            load_pro<C, IO>(p, b, h, t0 + 2 * kQ, tc_of(c + 2), rp);
+            if constexpr (!CP2) load_pro<C, IO>(p, b, h, t0 + 2 * kQ, tc_of(c + 2), rp);
         }
 
         // ---- a3 mask of this chunk: L[t][s] = exp(ell_t - ell_s) wgt_s (s < t),
@@ -704,8 +723,17 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
         __syncthreads();
 
         const float gc = misc_s[buf];
+        // a1 coefficients of the next chunk on the free coefficient wave, first
+        // thing after the barrier: its dt, lam were loaded a chunk earlier and
+        // only unconditional loads were issued since
+        if (CP2 && c + 1 < c_end) {
+            run_coef<C, IO>(rp, tc_of(c + 1), t0 + kQ, p.T, Ah, coef_s + (buf ^ 1) * (4 * kQ), misc_s + (buf ^ 1));
+            if (c + 2 < c_end) load_pro<C, IO>(p, b, h, t0 + 2 * kQ, tc_of(c + 2), rp);
+        }
         if (OUT) {
-            // ---- a3 + a5: y = M x + exp(ell) Chat H for this wave's row blocks
+            // ---- a3 + a5: y = M x + exp(ell) Chat H for this wave's row blocks,
+            // evaluated transposed (y^T = x^T M^T + H^T Chat^T exp(ell)) so that
+            // each lane holds consecutive outputs along P
             IO *ybase = static_cast<IO *>(p.y) + ((b * p.T + t0) * p.H + h) * (R * P);
 #pragma unroll
             for (int i = 0; i < C::TBW; ++i) {
@@ -714,26 +742,47 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
                 const int t0v = 16 * tb;
                 if (t0v / R >= Tc) continue;
                 const int tok_last = min((t0v + 15) / R, Tc - 1);
-                floatx4 acc[PT];
-#pragma unroll
-                for (int pt = 0; pt < PT; ++pt) {
-                    acc[pt] = floatx4{0.f, 0.f, 0.f, 0.f};
+                if constexpr (C::CL) {
 #pragma unroll
                     for (int ks = 0; ks < NKS; ++ks) {
                         const int n0 = 32 * ks + 8 * g;
-                        const frag hb = n0 < N ? M::template lds8<C::HT_PS>(ht + (16 * pt + l16) * NBP + n0) : M::zero();
-                        acc[pt] = M::mma(acc[pt], cf[i][ks], hb);
+                        cf[i][ks] = (N % 32 == 0 || n0 < N) ? M::template lds8<C::BS_PS>(cl + (t0v + l16) * NBP + n0) : M::zero();
                     }
                 }
+                floatx4 acc[PT];
 #pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int tok = (t0v + 4 * g + v) / R;
+                for (int pt = 0; pt < PT; ++pt) acc[pt] = floatx4{0.f, 0.f, 0.f, 0.f};
+                {
+                    // C~ H, the state fragments read DEPTH products ahead
+                    constexpr int NI = PT * NKS, DEPTH = NI < 4 ? NI : 4;
+                    // step it: k-step it / PT, column tile it % PT (consecutive
+                    // products go to different accumulators)
+                    auto hfrag = [&](int it) {
+                        const int pt = it % PT, n0 = 32 * (it / PT) + 8 * g;
+                        return (N % 32 == 0 || n0 < N) ? M::template lds8<C::HT_PS>(ht + (16 * pt + l16) * NBP + n0) : M::zero();
+                    };
+                    __builtin_amdgcn_sched_barrier(0);
+                    frag hq[DEPTH];
+#pragma unroll
+                    for (int d = 0; d < DEPTH; ++d) hq[d] = hfrag(d);
+#pragma unroll
+                    for (int it = 0; it < NI; ++it) {
+                        acc[it % PT] = M::mma(acc[it % PT], hq[it % DEPTH], cf[i][it / PT]);
+                        if (it + DEPTH < NI) hq[it % DEPTH] = hfrag(it + DEPTH);
+                    }
+                    if constexpr (N % 32 == 0) sched_pipeline<NI, DEPTH, PL, M::kMfma>();
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                {
+                    // the products are transposed (rows p, column = this lane's
+                    // virtual row t0v + l16), so one decay factor per lane
+                    const int tok = (t0v + l16) / R;
                     float e;
                     if constexpr (C::LWT) e = lw_s[kQ * C::LWP + tok];
                     else e = __expf(ell_s[tok]);
                     if (tok >= Tc) e = 0.f;
 #pragma unroll
-                    for (int pt = 0; pt < PT; ++pt) acc[pt][v] *= e;
+                    for (int pt = 0; pt < PT; ++pt) acc[pt] *= e;
                 }
                 const int tt = (t0v + l16) / R; // token of this lane's column t
                 const float ell_t = ell_s[tt], gam_t = gam_s[tt];
@@ -746,83 +795,118 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
                 };
                 // S^T for the 32 source rows s0 .. s0+31 (two 16-row blocks)
                 auto s_pair = [&](int s0, floatx4 *sb) {
+                    // step it: k-step it / 2, block it % 2, the B~ fragments
+                    // read D2 products ahead
+                    constexpr int NI2 = 2 * NKS, D2 = NI2 < 4 ? NI2 : 4;
+                    auto bfrag = [&](int it) {
+                        const int n0 = 32 * (it / 2) + 8 * g;
+                        return (N % 32 == 0 || n0 < N) ? M::template lds8<C::BS_PS>(bs + (s0 + 16 * (it % 2) + l16) * NBP + n0) : M::zero();
+                    };
+                    sb[0] = sb[1] = floatx4{0.f, 0.f, 0.f, 0.f};
+                    frag bq[D2];
 #pragma unroll
-                    for (int q = 0; q < 2; ++q) {
-                        sb[q] = floatx4{0.f, 0.f, 0.f, 0.f};
+                    for (int d = 0; d < D2; ++d) bq[d] = bfrag(d);
 #pragma unroll
-                        for (int ks = 0; ks < NKS; ++ks) {
-                            const int n0 = 32 * ks + 8 * g;
-                            const frag ab = n0 < N ? M::template lds8<C::BS_PS>(bs + (s0 + 16 * q + l16) * NBP + n0) : M::zero();
-                            sb[q] = M::mma(sb[q], ab, cf[i][ks]);
-                        }
+                    for (int it = 0; it < NI2; ++it) {
+                        sb[it % 2] = M::mma(sb[it % 2], bq[it % D2], cf[i][it / 2]);
+                        if (it + D2 < NI2) bq[it % D2] = bfrag(it + D2);
                     }
+                    if constexpr (N % 32 == 0) sched_pipeline<NI2, D2, PL, M::kMfma>();
                 };
                 // x operand of M x: slots 0-3 are rows s0 + 4g .. +3, slots
                 // 4-7 rows s0 + 16 + 4g .. +3 (the k order of the M fragment)
                 const uint16_t *xq = xr + (4 * g + (l16 >> 2)) * PP + 4 * (l16 & 3);
                 const int npairs = (R * (tok_last + 1) + 31) / 32;
+                // mask weights of this lane's 4 source rows r0 .. r0+3 of block q
+                // of the pair at s0, for its column token tt
+                auto mask4 = [&](int s0, int q, float *w) {
+                    const int r0 = s0 + 16 * q + 4 * g;
+                    const float *lr = lw_s + tt * C::LWP; // mask row of this lane's column token
+                    if constexpr (C::LWT && R == 1) {
+                        const float4 a = *reinterpret_cast<const float4 *>(lr + r0);
+                        w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+                    } else if constexpr (C::LWT && R == 2) {
+                        const float2 a = *reinterpret_cast<const float2 *>(lr + r0 / 2);
+                        w[0] = w[1] = a.x;
+                        w[2] = w[3] = a.y;
+                    } else if constexpr (C::LWT && R == 4) {
+                        w[0] = w[1] = w[2] = w[3] = lr[r0 / 4];
+                    } else if constexpr (C::LWT) {
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) w[v] = lr[(r0 + v) / R];
+                    } else if constexpr (R == 1) {
+                        const float4 el = *reinterpret_cast<const float4 *>(ell_s + r0);
+                        const float4 wg = *reinterpret_cast<const float4 *>(wgt_s + r0);
+                        w[0] = mw(r0, el.x, wg.x);
+                        w[1] = mw(r0 + 1, el.y, wg.y);
+                        w[2] = mw(r0 + 2, el.z, wg.z);
+                        w[3] = mw(r0 + 3, el.w, wg.w);
+                    } else if constexpr (R == 2) {
+                        const float2 el = *reinterpret_cast<const float2 *>(ell_s + r0 / 2);
+                        const float2 wg = *reinterpret_cast<const float2 *>(wgt_s + r0 / 2);
+                        w[0] = w[1] = mw(r0 / 2, el.x, wg.x);
+                        w[2] = w[3] = mw(r0 / 2 + 1, el.y, wg.y);
+                    } else if constexpr (R == 4) {
+                        w[0] = w[1] = w[2] = w[3] = mw(r0 / 4, ell_s[r0 / 4], wgt_s[r0 / 4]);
+                    } else {
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) {
+                            const int ts = (r0 + v) / R;
+                            w[v] = mw(ts, ell_s[ts], wgt_s[ts]);
+                        }
+                    }
+                };
+                // the next pair's S and (tabulated) mask weights are fetched
+                // while this pair's M x issues
                 floatx4 sn[2];
+                float wn[2][4];
                 s_pair(0, sn);
+                if constexpr (C::LWT) {
+                    mask4(0, 0, wn[0]);
+                    mask4(0, 1, wn[1]);
+                }
                 for (int mp = 0; mp < npairs; ++mp) {
                     const int s0 = 32 * mp;
                     const floatx4 sb[2] = {sn[0], sn[1]};
-                    if (mp + 1 < npairs) s_pair(s0 + 32, sn); // next pair's S overlaps this mask
+                    float wb[2][4];
+#pragma unroll
+                    for (int q = 0; q < 2; ++q)
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) wb[q][v] = wn[q][v];
+                    if (mp + 1 < npairs) {
+                        s_pair(s0 + 32, sn);
+                        if constexpr (C::LWT) {
+                            mask4(s0 + 32, 0, wn[0]);
+                            mask4(s0 + 32, 1, wn[1]);
+                        }
+                    }
+                    if constexpr (!C::LWT) {
+                        mask4(s0, 0, wb[0]);
+                        mask4(s0, 1, wb[1]);
+                    }
                     float m[8];
 #pragma unroll
-                    for (int q = 0; q < 2; ++q) {
-                        const int r0 = s0 + 16 * q + 4 * g; // this lane's 4 source rows r0 .. r0+3
-                        float w[4];
-                        const float *lr = lw_s + tt * C::LWP; // mask row of this lane's column token
-                        if constexpr (C::LWT && R == 1) {
-                            const float4 a = *reinterpret_cast<const float4 *>(lr + r0);
-                            w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
-                        } else if constexpr (C::LWT && R == 2) {
-                            const float2 a = *reinterpret_cast<const float2 *>(lr + r0 / 2);
-                            w[0] = w[1] = a.x;
-                            w[2] = w[3] = a.y;
-                        } else if constexpr (C::LWT && R == 4) {
-                            w[0] = w[1] = w[2] = w[3] = lr[r0 / 4];
-                        } else if constexpr (C::LWT) {
+                    for (int q = 0; q < 2; ++q)
 #pragma unroll
-                            for (int v = 0; v < 4; ++v) w[v] = lr[(r0 + v) / R];
-                        } else if constexpr (R == 1) {
-                            const float4 el = *reinterpret_cast<const float4 *>(ell_s + r0);
-                            const float4 wg = *reinterpret_cast<const float4 *>(wgt_s + r0);
-                            w[0] = mw(r0, el.x, wg.x);
-                            w[1] = mw(r0 + 1, el.y, wg.y);
-                            w[2] = mw(r0 + 2, el.z, wg.z);
-                            w[3] = mw(r0 + 3, el.w, wg.w);
-                        } else if constexpr (R == 2) {
-                            const float2 el = *reinterpret_cast<const float2 *>(ell_s + r0 / 2);
-                            const float2 wg = *reinterpret_cast<const float2 *>(wgt_s + r0 / 2);
-                            w[0] = w[1] = mw(r0 / 2, el.x, wg.x);
-                            w[2] = w[3] = mw(r0 / 2 + 1, el.y, wg.y);
-                        } else if constexpr (R == 4) {
-                            w[0] = w[1] = w[2] = w[3] = mw(r0 / 4, ell_s[r0 / 4], wgt_s[r0 / 4]);
-                        } else {
-#pragma unroll
-                            for (int v = 0; v < 4; ++v) {
-                                const int ts = (r0 + v) / R;
-                                w[v] = mw(ts, ell_s[ts], wgt_s[ts]);
-                            }
-                        }
-#pragma unroll
-                        for (int v = 0; v < 4; ++v) m[4 * q + v] = sb[q][v] * w[v];
-                    }
+                        for (int v = 0; v < 4; ++v) m[4 * q + v] = sb[q][v] * wb[q][v];
                     const frag mf = M::pack(m);
                     const uint16_t *xs0 = xq + s0 * PP;
 #pragma unroll
                     for (int pt = 0; pt < PT; ++pt)
-                        acc[pt] = M::mma(acc[pt], mf, M::template tr8<C::X_PS>(xs0 + 16 * pt, xs0 + 16 * PP + 16 * pt));
+                        acc[pt] = M::mma(acc[pt], M::template tr8<C::X_PS>(xs0 + 16 * pt, xs0 + 16 * PP + 16 * pt), mf);
                 }
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int vr = t0v + 4 * g + v;
+                {
+                    // y^T tile: this lane holds outputs p = 16 pt + 4 g .. +3 of
+                    // virtual row t0v + l16, four consecutive elements per store
+                    const int vr = t0v + l16;
                     const int tok = vr / R, ch = vr - tok * R;
                     if (tok < Tc) {
-                        IO *dst = ybase + ((tok * p.H * R + ch) * P + l16);
+                        IO *dst = ybase + ((tok * p.H * R + ch) * P + 4 * g);
 #pragma unroll
-                        for (int pt = 0; pt < PT; ++pt) io<IO>::put(dst + 16 * pt, acc[pt][v]);
+                        for (int pt = 0; pt < PT; ++pt) {
+                            const float o4[4] = {acc[pt][0], acc[pt][1], acc[pt][2], acc[pt][3]};
+                            io<IO>::store4(dst + 16 * pt, o4);
+                        }
                     }
                 }
             }

@@ -31,6 +31,14 @@ __device__ __forceinline__ uint16_t f32_to_bits(float f) {
 // Two floats -> two bf16 in one word (lo in the low half), one instruction.
 typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
 typedef float float2_v __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4_v __attribute__((ext_vector_type(4)));
+
+// One 16-byte global load as a plain vector value (not an aggregate copy,
+// which can leave its destination in private memory).
+__device__ __forceinline__ uint4 ld16(const void *p) {
+    const u32x4_v v = *static_cast<const u32x4_v *>(p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
 __device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
     const float2_v v = {lo, hi};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_v));
@@ -120,8 +128,25 @@ __device__ __forceinline__ uint2 lds_tr4(const uint16_t *p) {
     return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(p)));
 }
 
+// Scheduling order of a pipelined loop of NI products whose operands are LDS
+// reads (RD reads each, MF MFMAs each) issued DEPTH products ahead: DEPTH
+// operand reads, then (product, next operand) pairs, then the last DEPTH
+// products.  A hint to the scheduler only; it keeps the LDS reads in flight
+// instead of waiting for each one in turn.
+template <int NI, int DEPTH, int RD, int MF>
+__device__ __forceinline__ void sched_pipeline() {
+    __builtin_amdgcn_sched_group_barrier(0x100, DEPTH * RD, 0);
+#pragma unroll
+    for (int i = 0; i < NI - DEPTH; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, MF, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, DEPTH * MF, 0);
+}
+
 template <int PL>
 struct Mma {
+    static constexpr int kMfma = PL == 2 ? 3 : 1; // MFMA instructions per product
     struct frag {
         bf16x8 v[PL];
     };
