@@ -83,9 +83,10 @@ struct Cfg {
     // group kPW - 1 - w.
     static constexpr int FREEW = NTB < kPW ? kPW - NTB : 0;
     static constexpr int GPW = FREEW ? (NG8 + FREEW - 1) / FREEW : 1;
-    // the wave that scans the decay coefficients (a wave without intra-chunk
-    // row blocks when there is one)
-    static constexpr int CW = FREEW ? kPW - 1 : 0;
+    // the wave that scans the decay coefficients: the first wave without
+    // intra-chunk row blocks when there is one (waves w and w + 4 share a
+    // SIMD, and wave w's row block w is the lightest for w = 0)
+    static constexpr int CW = FREEW ? NTB : 0;
     // plane strides (elements) of the staged arrays
     static constexpr int BS_PS = V * NBP, X_PS = V * PP, HT_PS = P * NBP;
     // LDS layout, bytes.  The MFMA operands come first so that their offsets
@@ -152,11 +153,13 @@ struct RawPro {
     uint32_t dt, lam, dtn, lamn;           // raw I/O bits of dt, lam (this lane's token, token t0+64)
 };
 
-// Prefix tile m (< TPW) computed by a wave, or -1.
+// Prefix tile m (< TPW) computed by a wave, or -1.  With free waves each
+// takes TPW consecutive tiles (token blocks m of one pair block when TPW = 4:
+// one operand read serves all four, and every wave gets one chunk-end row).
 template <class C>
 __device__ __forceinline__ int mfp_tile(int wave, int m) {
     int t;
-    if (C::FREEW) t = wave >= C::NTB ? wave - C::NTB + m * C::FREEW : -1;
+    if (C::FREEW) t = wave >= C::NTB ? (wave - C::NTB) * C::TPW + m : -1;
     else t = wave + m * kPW;
     return t >= 0 && t < C::NTT ? t : -1;
 }
@@ -917,32 +920,44 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
             const float eg = __expf(gc);
             // slot j of both operands is virtual row 32 ks + 8 g + j
             const int ra = 8 * g + (l16 >> 2), ca = 4 * (l16 & 3);
+            // tile j of this wave: wave + 8 j, i.e. row block nt_j = (wave + 8 j) / PT
+            // and the same column block pt = wave % PT for every j (8 is a
+            // multiple of PT), so each k-step reads the x operand once
+            static_assert(kPW % PT == 0, "state tiles share their column block");
+            const int pt = wave % PT;
+            floatx4 acc[C::TW];
+#pragma unroll
+            for (int j = 0; j < C::TW; ++j) acc[j] = st[j] * eg;
+            const uint16_t *bp = (C::XS ? xs : xr) + ra * PP + 16 * pt + ca;
+#pragma unroll 2
+            for (int ks = 0; ks < V / 32; ++ks) {
+                frag bf = M::template tr8<C::X_PS>(bp + 32 * ks * PP, bp + (32 * ks + 4) * PP);
+                if constexpr (!C::XS) {
+                    float f[8];
+                    M::unpack(bf, f);
+#pragma unroll
+                    for (int jj = 0; jj < 8; ++jj) f[jj] *= scl_s[(32 * ks + 8 * g + jj) / R];
+                    bf = M::pack(f);
+                }
+#pragma unroll
+                for (int j = 0; j < C::TW; ++j) {
+                    const int tile = wave + kPW * j;
+                    if (tile >= C::NTILE) continue;
+                    const uint16_t *ap = bs + ra * NBP + 16 * (tile / PT) + ca;
+                    const frag af = M::template tr8<C::BS_PS>(ap + 32 * ks * NBP, ap + (32 * ks + 4) * NBP);
+                    acc[j] = M::mma(acc[j], af, bf);
+                }
+            }
 #pragma unroll
             for (int j = 0; j < C::TW; ++j) {
                 const int tile = wave + kPW * j;
                 if (tile >= C::NTILE) continue;
-                const int nt = tile / PT, pt = tile - nt * PT;
-                floatx4 acc = st[j] * eg;
-                const uint16_t *ap = bs + ra * NBP + 16 * nt + ca;
-                const uint16_t *bp = (C::XS ? xs : xr) + ra * PP + 16 * pt + ca;
-#pragma unroll 2
-                for (int ks = 0; ks < V / 32; ++ks) {
-                    const frag af = M::template tr8<C::BS_PS>(ap + 32 * ks * NBP, ap + (32 * ks + 4) * NBP);
-                    frag bf = M::template tr8<C::X_PS>(bp + 32 * ks * PP, bp + (32 * ks + 4) * PP);
-                    if constexpr (!C::XS) {
-                        float f[8];
-                        M::unpack(bf, f);
-#pragma unroll
-                        for (int jj = 0; jj < 8; ++jj) f[jj] *= scl_s[(32 * ks + 8 * g + jj) / R];
-                        bf = M::pack(f);
-                    }
-                    acc = M::mma(acc, af, bf);
-                }
+                const int nt = tile / PT;
 #pragma unroll
                 for (int q = 0; q < 2; ++q) {
                     const float2 cs = thcb[8 * nt + 2 * g + q];
-                    st[j][2 * q] = cs.x * acc[2 * q] - cs.y * acc[2 * q + 1];
-                    st[j][2 * q + 1] = cs.y * acc[2 * q] + cs.x * acc[2 * q + 1];
+                    st[j][2 * q] = cs.x * acc[j][2 * q] - cs.y * acc[j][2 * q + 1];
+                    st[j][2 * q + 1] = cs.y * acc[j][2 * q] + cs.x * acc[j][2 * q + 1];
                 }
             }
         }
