@@ -45,6 +45,8 @@
 // registers.  bf16 I/O stages one bf16 plane per value, fp32 I/O two (hi, lo).
 #pragma once
 
+#include <type_traits>
+
 #include "m3_device.hpp"
 #include "m3_internal.hpp"
 
@@ -55,16 +57,22 @@ constexpr int kPW = kPT / kWave; // waves per prefill workgroup
 
 constexpr size_t align16(size_t v) { return (v + 15) / 16 * 16; }
 
-template <typename IO, int N_, int P_, int R_>
-struct Cfg {
+// Row pitch (bf16 elements) of an LDS table with n columns: padded to an odd
+// multiple of 16 elements (row pitch = 8 mod 16 banks), where the row-operand,
+// transposing and mask reads of this kernel are free of bank conflicts, or
+// (narrow layout) by 8 elements only.
+constexpr int lds_pitch(int n, bool wide) { return wide ? (n + 31) / 32 * 32 + 16 : n + 8; }
+
+template <typename IO, int N_, int P_, int R_, bool WIDE>
+struct CfgW {
     static constexpr int N = N_, P = P_, R = R_, K = N / 2, V = kQ * R;
     static constexpr int PL = mode<IO>::f32 ? 2 : 1;          // bf16 planes per staged value
     typedef Mma<PL> M;
     typedef typename M::frag frag;
     static constexpr int SZ = int(sizeof(IO));
     static constexpr int EPU = 16 / SZ;                       // I/O elements per 16-byte unit
-    static constexpr int NBP = N + 8;                         // row pitch of bs, ht (elements)
-    static constexpr int PP = P + 8;                          // row pitch of xr, xs (elements)
+    static constexpr int NBP = lds_pitch(N, WIDE);            // row pitch of bs, ht, cl (elements)
+    static constexpr int PP = lds_pitch(P, WIDE);             // row pitch of xr, xs (elements)
     static constexpr int CSP = 2 * K + 4;                     // row pitch of the cos/sin table (floats)
     static constexpr int NTB = V / 16;                        // 16-row blocks of virtual rows
     static constexpr int TBW = NTB > kPW ? 2 : 1;             // blocks per wave
@@ -104,7 +112,7 @@ struct Cfg {
     static constexpr size_t o_ths = o_thc + 2 * size_t(K) * 8;                 // double [K]: running angle
     // The chunk's token mask L[t][s] (and e^{ell_t}) is tabulated once per
     // chunk when it fits; otherwise each lane evaluates its mask entries.
-    static constexpr int LWP = kQ + 4;                                         // row pitch (floats)
+    static constexpr int LWP = WIDE ? kQ + 8 : kQ + 4;                         // row pitch (floats)
     static constexpr size_t o_lw = align16(o_ths + size_t(K) * 8);             // float [64][LWP]
     static constexpr size_t lw_bytes = size_t(kQ) * LWP * 4 + kQ * 4;          // + e^{ell} [64]
     static constexpr bool LWT = o_lw + lw_bytes <= kMaxLdsBytes;
@@ -112,7 +120,7 @@ struct Cfg {
     // lower-triangular ones matrix with the chunk's theta (MFMA, fp32
     // accumulation), read from a row-major theta table; otherwise (fp32 I/O,
     // or fewer than 16 pairs) exact fixed-point DPP scans.
-    static constexpr int THP = K + 8;                                          // theta table pitch (elements)
+    static constexpr int THP = lds_pitch(K, WIDE);                             // theta table pitch (elements)
     static constexpr int URT = K * SZ / 16, UT = kQ * URT, UPT_T = (UT + kPT - 1) / kPT;
     static constexpr int NPB = K / 16, NTT = 4 * NPB;                          // 16x16 prefix tiles
     static constexpr size_t o_th = align16(o_lw + (LWT ? lw_bytes : 0));       // bf16 [64][THP]
@@ -135,6 +143,19 @@ struct Cfg {
     static_assert(K * SZ % 16 == 0 && N % 16 == 0 && P % 16 == 0 && K % 8 == 0, "tile sizes");
     static_assert(FREEW ? NG8 <= FREEW * GPW : NG8 <= kPW, "angle groups per wave");
 };
+
+// The wide (conflict-free) layout when it fits with every optional table the
+// narrow one has, else the narrow layout.
+template <typename IO, int N, int P, int R>
+struct CfgPick {
+    typedef CfgW<IO, N, P, R, true> Wd;
+    typedef CfgW<IO, N, P, R, false> Nw;
+    static constexpr bool wide = Wd::bytes <= kMaxLdsBytes && Wd::LWT == Nw::LWT && Wd::MFP == Nw::MFP &&
+                                 Wd::XS == Nw::XS && Wd::CL == Nw::CL;
+    typedef typename std::conditional<wide, Wd, Nw>::type type;
+};
+template <typename IO, int N, int P, int R>
+using Cfg = typename CfgPick<IO, N, P, R>::type;
 
 // Raw (undecoded) B, x and C of one chunk held in registers.
 template <class C>
@@ -350,8 +371,9 @@ __device__ __forceinline__ void run_angles(const RawPro<C> &r, int Tc, float *cs
             pbm[m] = tl >> 2;
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
-                const uint16_t *bp = tht + (32 * kb + 8 * g + (l16 >> 2)) * C::THP + 16 * pbm[m] + 4 * (l16 & 3);
-                bf[m][kb] = M::template tr8<0>(bp, bp + 4 * C::THP);
+                // slots 0-3: tokens 32 kb + 4 g .. +3, slots 4-7: 16 tokens further
+                const uint16_t *bp = tht + (32 * kb + 4 * g + (l16 >> 2)) * C::THP + 16 * pbm[m] + 4 * (l16 & 3);
+                bf[m][kb] = M::template tr8<0>(bp, bp + 16 * C::THP);
             }
         }
         floatx4 acc[C::TPW];
@@ -364,7 +386,7 @@ __device__ __forceinline__ void run_angles(const RawPro<C> &r, int Tc, float *cs
                 uint32_t w[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int s0 = 32 * kb + 8 * g + 2 * i;
+                    const int s0 = 32 * kb + (i < 2 ? 4 * g + 2 * i : 16 + 4 * g + 2 * (i - 2)); // token of slot 2 i
                     w[i] = (s0 <= trow ? 0x3F80u : 0u) | (s0 + 1 <= trow ? 0x3F800000u : 0u);
                 }
                 typename M::frag a;
@@ -918,8 +940,9 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
         // ---- a4: H <- R(Theta_c) (exp(g_c) H + sum_v Bhat[v] (scaled x)[v]^T)
         {
             const float eg = __expf(gc);
-            // slot j of both operands is virtual row 32 ks + 8 g + j
-            const int ra = 8 * g + (l16 >> 2), ca = 4 * (l16 & 3);
+            // slot j of both operands is virtual row 32 ks + 4 g + j (j < 4) or
+            // 32 ks + 16 + 4 g + j - 4 (j >= 4)
+            const int ra = 4 * g + (l16 >> 2), ca = 4 * (l16 & 3);
             // tile j of this wave: wave + 8 j, i.e. row block nt_j = (wave + 8 j) / PT
             // and the same column block pt = wave % PT for every j (8 is a
             // multiple of PT), so each k-step reads the x operand once
@@ -931,12 +954,12 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
             const uint16_t *bp = (C::XS ? xs : xr) + ra * PP + 16 * pt + ca;
 #pragma unroll 2
             for (int ks = 0; ks < V / 32; ++ks) {
-                frag bf = M::template tr8<C::X_PS>(bp + 32 * ks * PP, bp + (32 * ks + 4) * PP);
+                frag bf = M::template tr8<C::X_PS>(bp + 32 * ks * PP, bp + (32 * ks + 16) * PP);
                 if constexpr (!C::XS) {
                     float f[8];
                     M::unpack(bf, f);
 #pragma unroll
-                    for (int jj = 0; jj < 8; ++jj) f[jj] *= scl_s[(32 * ks + 8 * g + jj) / R];
+                    for (int jj = 0; jj < 8; ++jj) f[jj] *= scl_s[(32 * ks + (jj < 4 ? 4 * g + jj : 12 + 4 * g + jj)) / R];
                     bf = M::pack(f);
                 }
 #pragma unroll
@@ -944,7 +967,7 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
                     const int tile = wave + kPW * j;
                     if (tile >= C::NTILE) continue;
                     const uint16_t *ap = bs + ra * NBP + 16 * (tile / PT) + ca;
-                    const frag af = M::template tr8<C::BS_PS>(ap + 32 * ks * NBP, ap + (32 * ks + 4) * NBP);
+                    const frag af = M::template tr8<C::BS_PS>(ap + 32 * ks * NBP, ap + (32 * ks + 16) * NBP);
                     acc[j] = M::mma(acc[j], af, bf);
                 }
             }
