@@ -170,21 +170,22 @@ def time_prefill(torch, mixer, inp, steps, warmup):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = e0.elapsed_time(e1) / steps
-    # each kernel alone, launched back to back on the same stream (after a full
-    # prefill filled the workspace): average launch duration
+    # each kernel alone on the same stream (after a full prefill filled the
+    # workspace), every launch bracketed by its own event pair: average launch
+    # duration, gaps between launches excluded
     per_kernel = {}
     for name in KERNELS:
         stage = mixer.capi.STAGES[name]
         reps = max(steps, 10)
-        ks, ke = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
         mixer.prefill_stage(stage, *args, None, st, y, ws)
         torch.cuda.synchronize()
-        ks.record()
-        for _ in range(reps):
+        for ks, ke in ev:
+            ks.record()
             mixer.prefill_stage(stage, *args, None, st, y, ws)
-        ke.record()
+            ke.record()
         torch.cuda.synchronize()
-        per_kernel[name] = ks.elapsed_time(ke) / reps
+        per_kernel[name] = sum(ks.elapsed_time(ke) for ks, ke in ev) / reps
     mixer.prefill(*args, final=st, y=y, workspace=ws)   # leave a consistent state behind
     torch.cuda.synchronize()
     return ms, wall, per_kernel
