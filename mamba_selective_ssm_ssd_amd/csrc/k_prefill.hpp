@@ -212,6 +212,15 @@ __device__ __forceinline__ void unpack_unit(const uint4 &u, float *v, float) {
 // causal work of the two blocks balances across waves.
 __device__ __forceinline__ int wave_block(int i, int wave) { return i == 0 ? wave : 2 * kPW - 1 - wave; }
 
+// f(integral_constant<J>) for J = J0 .. NJ-1, unrolled at compile time.
+template <int J0, int NJ, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+    if constexpr (J0 < NJ) {
+        f(std::integral_constant<int, J0>{});
+        static_for<J0 + 1, NJ>(f);
+    }
+}
+
 // Loads chunk (b, h, t0 .. t0+Tc-1)'s B, x and C into registers.  Addresses
 // are a uniform per-chunk base plus a 32-bit per-thread offset (saddr +
 // voffset addressing).  Every load is issued (indices clamped to the last
@@ -219,8 +228,9 @@ __device__ __forceinline__ int wave_block(int i, int wave) { return i == 0 ? wav
 // values meet only zero mask entries, zero state-update scales and outputs
 // that are not stored.  With no load under a condition the compiler's wait
 // counts stay exact.
-// PARTS selects what is loaded: bit 0 B, bit 1 x, bit 2 C.
-template <class C, typename IO, bool OUT, int PARTS = 7>
+// PARTS selects what is loaded: bit 0 B, bit 1 x, bit 2 C; J >= 0 loads only
+// unit J of B, x and the spread C units.
+template <class C, typename IO, bool OUT, int PARTS = 7, int J = -1>
 __device__ __forceinline__ void load_chunk(const PrefillParams &p, int64_t b, int h, int64_t t0, int Tc,
                                            RawChunk<C> &r) {
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
@@ -232,6 +242,7 @@ __device__ __forceinline__ void load_chunk(const PrefillParams &p, int64_t b, in
     const IO *Cp = static_cast<const IO *>(p.C) + tokbase * (C::R * C::N);
 #pragma unroll
     for (int j = 0; j < ((PARTS & 1) ? C::UPT_B : 0); ++j) {
+        if (J >= 0 && j != J) continue;
         const int u = min(tid + j * kPT, C::UB - 1);
         const int v = u / C::URB, q = u - v * C::URB;
         const int tok = min(v / C::R, Tc - 1), ch = v % C::R;
@@ -239,6 +250,7 @@ __device__ __forceinline__ void load_chunk(const PrefillParams &p, int64_t b, in
     }
 #pragma unroll
     for (int j = 0; j < ((PARTS & 2) ? C::UPT_X : 0); ++j) {
+        if (J >= 0 && j != J) continue;
         const int u = min(tid + j * kPT, C::UX - 1);
         const int v = u / C::URX, q = u - v * C::URX;
         const int tok = min(v / C::R, Tc - 1), ch = v % C::R;
@@ -247,6 +259,7 @@ __device__ __forceinline__ void load_chunk(const PrefillParams &p, int64_t b, in
     if constexpr (OUT && (PARTS & 4) && C::CL) {
 #pragma unroll
         for (int j = 0; j < C::UPT_B; ++j) {
+            if (J >= 0 && j != J) continue;
             const int u = min(tid + j * kPT, C::UB - 1);
             const int v = u / C::URB, q = u - v * C::URB;
             const int tok = min(v / C::R, Tc - 1), ch = v % C::R;
@@ -627,9 +640,15 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
         const float *gam_s = ell_s + kQ, *wgt_s = gam_s + kQ, *scl_s = wgt_s + kQ;
         const float2 *thcb = thc_s + buf * K;
 
-        // ---- a2: rotate B and C with the cos/sin table; stage B, x, scaled x
-#pragma unroll
-        for (int j = 0; j < C::UPT_B; ++j) {
+        // ---- a2: rotate B and C with the cos/sin table; stage B, x, scaled x.
+        // Each unit's register is refilled with the next chunk's unit as soon
+        // as it is consumed, so the load issue overlaps the staging work.
+        const bool more = c + 1 < c_end;
+        const int64_t tn0 = t0 + kQ;
+        const int Tn = more ? tc_of(c + 1) : 1;
+        constexpr int CPART = (OUT && C::CL) ? 4 : 0;
+        static_for<0, C::UPT_B>([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
             const int u = tid + j * kPT;
             if (C::UB % kPT == 0 || u < C::UB) {
                 const int v = u / C::URB, q = u - v * C::URB;
@@ -638,6 +657,7 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
                 const float4 *cr = reinterpret_cast<const float4 *>(cs_s + (v / R) * C::CSP + q * EPU);
                 float ec[EPU];
                 if constexpr (OUT && C::CL) unpack_unit(raw.cu[j], ec, IO());
+                if (more) load_chunk<C, IO, OUT, 1 | CPART, j>(p, b, h, tn0, Tn, raw);
 #pragma unroll
                 for (int w4 = 0; w4 < EPU / 4; ++w4) {
                     const float4 a = cr[w4];
@@ -650,10 +670,12 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
                 }
                 st_planes<PL, C::BS_PS, EPU>(bs + v * NBP + q * EPU, e);
                 if constexpr (OUT && C::CL) st_planes<PL, C::BS_PS, EPU>(cl + v * NBP + q * EPU, ec);
+            } else if (more) {
+                load_chunk<C, IO, OUT, 1 | CPART, j>(p, b, h, tn0, Tn, raw);
             }
-        }
-#pragma unroll
-        for (int j = 0; j < C::UPT_X; ++j) {
+        });
+        static_for<0, C::UPT_X>([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
             const int u = tid + j * kPT;
             if (C::UX % kPT == 0 || u < C::UX) {
                 const int v = u / C::URX, q = u - v * C::URX;
@@ -663,14 +685,17 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
                     *reinterpret_cast<uint4 *>(xr + v * PP + q * EPU) = raw.xx[j];
                 else
                     st_planes<PL, C::X_PS, EPU>(xr + v * PP + q * EPU, e);
+                if (more) load_chunk<C, IO, OUT, 2, j>(p, b, h, tn0, Tn, raw);
                 if constexpr (C::XS) {
                     const float sc = scl_s[v / R];
 #pragma unroll
                     for (int ee = 0; ee < EPU; ++ee) e[ee] *= sc;
                     st_planes<PL, C::X_PS, EPU>(xs + v * PP + q * EPU, e);
                 }
+            } else if (more) {
+                load_chunk<C, IO, OUT, 2, j>(p, b, h, tn0, Tn, raw);
             }
-        }
+        });
         frag cf[C::TBW][NKS];
         if (OUT && !C::CL) {
 #pragma unroll
@@ -707,7 +732,7 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
             if constexpr (!CP2)
                 run_coef<C, IO>(rp, tc_of(c + 1), t0 + kQ, p.T, Ah, coef_s + (buf ^ 1) * (4 * kQ), misc_s + (buf ^ 1));
         }
-        if (c + 1 < c_end) load_chunk<C, IO, OUT>(p, b, h, t0 + kQ, tc_of(c + 1), raw);
+        if (OUT && !C::CL && more) load_chunk<C, IO, OUT, 4>(p, b, h, tn0, Tn, raw);
         if (C::MFP && c + 2 < c_end) {
             load_theta<C, IO>(p, b, h, t0 + 2 * kQ, tc_of(c + 2), rp);
             if constexpr (!CP2) load_pro<C, IO>(p, b, h, t0 + 2 * kQ, tc_of(c + 2), rp);
