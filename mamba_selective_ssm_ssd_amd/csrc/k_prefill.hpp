@@ -908,10 +908,11 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
                 };
                 // the next pair's S and (tabulated) mask weights are fetched
                 // while this pair's M x issues
+                constexpr bool MPF = C::LWT && R == 1; // mask weights fetched a pair ahead (measured: helps R = 1 only)
                 floatx4 sn[2];
                 float wn[2][4];
                 s_pair(0, sn);
-                if constexpr (C::LWT) {
+                if constexpr (MPF) {
                     mask4(0, 0, wn[0]);
                     mask4(0, 1, wn[1]);
                 }
@@ -925,12 +926,12 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
                         for (int v = 0; v < 4; ++v) wb[q][v] = wn[q][v];
                     if (mp + 1 < npairs) {
                         s_pair(s0 + 32, sn);
-                        if constexpr (C::LWT) {
+                        if constexpr (MPF) {
                             mask4(s0 + 32, 0, wn[0]);
                             mask4(s0 + 32, 1, wn[1]);
                         }
                     }
-                    if constexpr (!C::LWT) {
+                    if constexpr (!MPF) {
                         mask4(s0, 0, wb[0]);
                         mask4(s0, 1, wb[1]);
                     }
