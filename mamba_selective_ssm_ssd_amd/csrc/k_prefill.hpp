@@ -643,24 +643,36 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
         // ---- a2: rotate B and C with the cos/sin table; stage B, x, scaled x.
         // Each unit's register is refilled with the next chunk's unit as soon
         // as it is consumed, so the load issue overlaps the staging work.
+        // The next chunk's loads are unconditional: past the last chunk they
+        // reload the last one (unused).  A load under a condition would keep
+        // the old register value alive beside the new one and cost register
+        // copies, and a wait for every load, at the end of each chunk.
         const bool more = c + 1 < c_end;
-        const int64_t tn0 = t0 + kQ;
-        const int Tn = more ? tc_of(c + 1) : 1;
+        const int cn = more ? c + 1 : c, cn2 = min(c + 2, c_end - 1);
+        const int64_t tn0 = int64_t(cn) * kQ;
+        const int Tn = tc_of(cn);
         constexpr int CPART = (OUT && C::CL) ? 4 : 0;
         static_for<0, C::UPT_B>([&](auto jc) {
             constexpr int j = decltype(jc)::value;
             const int u = tid + j * kPT;
             if (C::UB % kPT == 0 || u < C::UB) {
                 const int v = u / C::URB, q = u - v * C::URB;
+                const float4 *cr = reinterpret_cast<const float4 *>(cs_s + (v / R) * C::CSP + q * EPU);
+                float4 csr[EPU / 4];
+#pragma unroll
+                for (int w4 = 0; w4 < EPU / 4; ++w4) csr[w4] = cr[w4];
                 float e[EPU];
                 unpack_unit(raw.bb[j], e, IO());
-                const float4 *cr = reinterpret_cast<const float4 *>(cs_s + (v / R) * C::CSP + q * EPU);
                 float ec[EPU];
                 if constexpr (OUT && C::CL) unpack_unit(raw.cu[j], ec, IO());
-                if (more) load_chunk<C, IO, OUT, 1 | CPART, j>(p, b, h, tn0, Tn, raw);
+                // the unit's registers are free from here: the next chunk's unit
+                // is loaded into them (kept after the unpack, so the loop needs
+                // no register copies)
+                __builtin_amdgcn_sched_barrier(0);
+                load_chunk<C, IO, OUT, 1 | CPART, j>(p, b, h, tn0, Tn, raw);
 #pragma unroll
                 for (int w4 = 0; w4 < EPU / 4; ++w4) {
-                    const float4 a = cr[w4];
+                    const float4 a = csr[w4];
                     rot_neg(a.x, a.y, e[4 * w4], e[4 * w4 + 1]);
                     rot_neg(a.z, a.w, e[4 * w4 + 2], e[4 * w4 + 3]);
                     if constexpr (OUT && C::CL) {
@@ -670,7 +682,7 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
                 }
                 st_planes<PL, C::BS_PS, EPU>(bs + v * NBP + q * EPU, e);
                 if constexpr (OUT && C::CL) st_planes<PL, C::BS_PS, EPU>(cl + v * NBP + q * EPU, ec);
-            } else if (more) {
+            } else {
                 load_chunk<C, IO, OUT, 1 | CPART, j>(p, b, h, tn0, Tn, raw);
             }
         });
@@ -685,14 +697,15 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
                     *reinterpret_cast<uint4 *>(xr + v * PP + q * EPU) = raw.xx[j];
                 else
                     st_planes<PL, C::X_PS, EPU>(xr + v * PP + q * EPU, e);
-                if (more) load_chunk<C, IO, OUT, 2, j>(p, b, h, tn0, Tn, raw);
+                __builtin_amdgcn_sched_barrier(0);
+                load_chunk<C, IO, OUT, 2, j>(p, b, h, tn0, Tn, raw);
                 if constexpr (C::XS) {
                     const float sc = scl_s[v / R];
 #pragma unroll
                     for (int ee = 0; ee < EPU; ++ee) e[ee] *= sc;
                     st_planes<PL, C::X_PS, EPU>(xs + v * PP + q * EPU, e);
                 }
-            } else if (more) {
+            } else {
                 load_chunk<C, IO, OUT, 2, j>(p, b, h, tn0, Tn, raw);
             }
         });
@@ -701,7 +714,7 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
 #pragma unroll
             for (int i = 0; i < C::TBW; ++i) {
                 const int tb = wave_block(i, wave);
-                if (tb >= C::NTB) continue; // uniform: waves without this row block
+                if (C::NTB < C::TBW * kPW && tb >= C::NTB) continue; // uniform: waves without this row block
                 const int tok = (16 * tb + l16) / R;
 #pragma unroll
                 for (int ks = 0; ks < NKS; ++ks) {
@@ -732,10 +745,13 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
             if constexpr (!CP2)
                 run_coef<C, IO>(rp, tc_of(c + 1), t0 + kQ, p.T, Ah, coef_s + (buf ^ 1) * (4 * kQ), misc_s + (buf ^ 1));
         }
-        if (OUT && !C::CL && more) load_chunk<C, IO, OUT, 4>(p, b, h, tn0, Tn, raw);
-        if (C::MFP && c + 2 < c_end) {
-            load_theta<C, IO>(p, b, h, t0 + 2 * kQ, tc_of(c + 2), rp);
-            if constexpr (!CP2) load_pro<C, IO>(p, b, h, t0 + 2 * kQ, tc_of(c + 2), rp);
+        if (OUT && !C::CL) {
+            __builtin_amdgcn_sched_barrier(0); // after the C fragments are unpacked
+            load_chunk<C, IO, OUT, 4>(p, b, h, tn0, Tn, raw);
+        }
+        if constexpr (C::MFP) {
+            load_theta<C, IO>(p, b, h, int64_t(cn2) * kQ, tc_of(cn2), rp);
+            if constexpr (!CP2) load_pro<C, IO>(p, b, h, int64_t(cn2) * kQ, tc_of(cn2), rp);
         }
 
         // ---- a3 mask of this chunk: L[t][s] = exp(ell_t - ell_s) wgt_s (s < t),
@@ -776,9 +792,10 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
         // a1 coefficients of the next chunk on the free coefficient wave, first
         // thing after the barrier: its dt, lam were loaded a chunk earlier and
         // only unconditional loads were issued since
-        if (CP2 && c + 1 < c_end) {
-            run_coef<C, IO>(rp, tc_of(c + 1), t0 + kQ, p.T, Ah, coef_s + (buf ^ 1) * (4 * kQ), misc_s + (buf ^ 1));
-            if (c + 2 < c_end) load_pro<C, IO>(p, b, h, t0 + 2 * kQ, tc_of(c + 2), rp);
+        if constexpr (CP2) {
+            if (c + 1 < c_end)
+                run_coef<C, IO>(rp, tc_of(c + 1), t0 + kQ, p.T, Ah, coef_s + (buf ^ 1) * (4 * kQ), misc_s + (buf ^ 1));
+            load_pro<C, IO>(p, b, h, int64_t(cn2) * kQ, tc_of(cn2), rp);
         }
         if (OUT) {
             // ---- a3 + a5: y = M x + exp(ell) Chat H for this wave's row blocks,
@@ -1017,7 +1034,7 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
             run_angles<C, IO>(rp, tc_of(c + 1), cs_s, thc_s + (buf ^ 1) * K, ths_s, tht);
             if constexpr (!C::MFP) {
                 run_coef<C, IO>(rp, tc_of(c + 1), t0 + kQ, p.T, Ah, coef_s + (buf ^ 1) * (4 * kQ), misc_s + (buf ^ 1));
-                if (c + 2 < c_end) load_pro<C, IO>(p, b, h, t0 + 2 * kQ, tc_of(c + 2), rp);
+                load_pro<C, IO>(p, b, h, int64_t(cn2) * kQ, tc_of(cn2), rp);
             }
         }
         __syncthreads();
