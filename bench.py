@@ -171,21 +171,23 @@ def time_prefill(torch, mixer, inp, steps, warmup):
     wall = time.perf_counter() - t0
     ms = e0.elapsed_time(e1) / steps
     # each kernel alone on the same stream (after a full prefill filled the
-    # workspace), every launch bracketed by its own event pair: average launch
-    # duration, gaps between launches excluded
+    # workspace): `steps` launches back to back between one event pair (an
+    # event pair costs a few microseconds; per-launch pairs would add that to
+    # every launch), right after the timed calls, so at the same clocks
     per_kernel = {}
     for name in KERNELS:
         stage = mixer.capi.STAGES[name]
         reps = max(steps, 10)
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-        mixer.prefill_stage(stage, *args, None, st, y, ws)
-        torch.cuda.synchronize()
-        for ks, ke in ev:
-            ks.record()
+        for _ in range(3):
             mixer.prefill_stage(stage, *args, None, st, y, ws)
-            ke.record()
         torch.cuda.synchronize()
-        per_kernel[name] = sum(ks.elapsed_time(ke) for ks, ke in ev) / reps
+        ks, ke = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ks.record()
+        for _ in range(reps):
+            mixer.prefill_stage(stage, *args, None, st, y, ws)
+        ke.record()
+        torch.cuda.synchronize()
+        per_kernel[name] = ks.elapsed_time(ke) / reps
     mixer.prefill(*args, final=st, y=y, workspace=ws)   # leave a consistent state behind
     torch.cuda.synchronize()
     return ms, wall, per_kernel
@@ -206,7 +208,7 @@ def time_decode(torch, mixer, synth, b, H, P, N, R, steps, warmup, seed=0):
                           inp["B"][t], inp["C"][t], st, y=y)
 
     for t in range(warmup):
-        step(steps + t)
+        step(steps + t)                  # (clocks up: the prefill ran just before)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
@@ -256,8 +258,11 @@ def cpu_baseline(torch, inp, budget_s):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    # The GPU raises its clocks only after some milliseconds of sustained
+    # work: a short run measures the ramp (about 15% slower per call), so the
+    # defaults time 200 calls after 50 untimed ones (tens of milliseconds).
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-mimo", action="store_true", help="skip the MIMO prefill workload")
