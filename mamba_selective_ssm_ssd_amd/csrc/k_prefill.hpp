@@ -418,10 +418,21 @@ __device__ __forceinline__ void run_angles(const RawPro<C> &r, int Tc, float *cs
                 tf -= rintf(tf);
                 const float sn = __builtin_amdgcn_sinf(tf), cn = __builtin_amdgcn_cosf(tf);
                 *reinterpret_cast<float2 *>(cs + t * C::CSP + 2 * pair) = make_float2(cn, sn);
-                if (t == Tc - 1) {
-                    thc[pair] = make_float2(cn, sn);
-                    ths[pair] += double(acc[m][v]);
-                }
+            }
+        }
+        // the chunk total: row Tc-1, held by lane group ge of the tile of
+        // token block te (element ve of the lane's four rows)
+        const int te = (Tc - 1) >> 4, ge = ((Tc - 1) & 15) >> 2, ve = (Tc - 1) & 3;
+#pragma unroll
+        for (int m = 0; m < C::TPW; ++m) {
+            if (mfp_tile<C>(wave, m) < 0 || tbm[m] != te) continue; // uniform
+            if (g == ge) {
+                const float a = ve == 0 ? acc[m][0] : ve == 1 ? acc[m][1] : ve == 2 ? acc[m][2] : acc[m][3];
+                float tf = a * float(1.0 / kTwoPi);
+                tf -= rintf(tf);
+                const int pair = 16 * pbm[m] + l16;
+                thc[pair] = make_float2(__builtin_amdgcn_cosf(tf), __builtin_amdgcn_sinf(tf));
+                ths[pair] += double(a);
             }
         }
     }
@@ -755,10 +766,15 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
         }
 
         // ---- a3 mask of this chunk: L[t][s] = exp(ell_t - ell_s) wgt_s (s < t),
-        // gam_t (s = t), 0 (s > t); row t, 8 consecutive s per thread
+        // gam_t (s = t), 0 (s > t); row t, 8 consecutive s per thread.  With
+        // R = 1 the rows t < 32 are read for s < 32 only (their source pair),
+        // so 384 groups are evaluated, by the first six waves.
         if constexpr (C::LWT) {
-            if (OUT) {
-                const int tt = tid >> 3, s0 = (tid & 7) * 8;
+            constexpr bool HALF = R == 1 && kQ == 64 && kPT == 512;
+            const int gi = HALF && tid >= 128 ? tid + 128 : tid; // skip rows < 32 x s >= 32
+            const int tt = HALF ? (tid < 128 ? tid >> 2 : gi >> 3) : tid >> 3;
+            const int s0 = HALF ? (tid < 128 ? (tid & 3) * 8 : (gi & 7) * 8) : (tid & 7) * 8;
+            if (OUT && (!HALF || tid < 384)) {
                 float w[8];
                 {
                     // branch-free: every entry is evaluated, then selected
@@ -782,8 +798,8 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
                 float4 *dst = reinterpret_cast<float4 *>(lw_s + tt * C::LWP + s0);
                 dst[0] = make_float4(w[0], w[1], w[2], w[3]);
                 dst[1] = make_float4(w[4], w[5], w[6], w[7]);
-                if (tid < kQ) lw_s[kQ * C::LWP + tid] = __expf(ell_s[tid]);
             }
+            if (OUT && tid < kQ) lw_s[kQ * C::LWP + tid] = __expf(ell_s[tid]);
         }
 
         __syncthreads();
