@@ -160,3 +160,56 @@ def wrap_angle(phi):
     """Map angles to [-pi, pi) in fp64."""
     phi = np.asarray(phi, dtype=np.float64)
     return phi - 2.0 * np.pi * np.floor((phi + np.pi) / (2.0 * np.pi))
+
+
+# ---------------------------------------------------------------------------
+# Block prologue and epilogue around the mixer (fp64, plain numpy).
+#
+# Mamba-3 review, section 3.4 (Mamba-3 architecture; "BC/QK normalisation" and
+# "B, C biases"): after the B and C projections each is RMS-normalised, then a
+# learnable per-head, per-channel bias is added; the mixer output then passes
+# the block's output gate.  The pages give no formulas; the readings taken:
+#   - the RMS is over the N state channels of each (token, head, rank) row,
+#     with eps inside the square root, followed by an optional per-(head, rank,
+#     channel) weight (the usual RMS-norm scale) and the bias;
+#   - the gate is y * silu(z) = y * z / (1 + exp(-z)), z shaped like y.
+# ---------------------------------------------------------------------------
+
+def bc_norm(V, weight=None, bias=None, eps=1e-6, norm=True):
+    """Prologue on B or C: V [b,T,H,R,N] (or [b,H,R,N] for one decode step).
+
+    Returns V / sqrt(mean_n V^2 + eps) * weight[h,r,n] + bias[h,r,n] (fp64);
+    ``norm=False`` skips the division, ``None`` weight/bias mean 1 and 0.
+    """
+    V = np.asarray(V, dtype=np.float64)
+    if norm:
+        V = V / np.sqrt(np.mean(V * V, axis=-1, keepdims=True) + float(eps))
+    if weight is not None:
+        V = V * np.asarray(weight, dtype=np.float64)
+    if bias is not None:
+        V = V + np.asarray(bias, dtype=np.float64)
+    return V
+
+
+def gate(y, z):
+    """Epilogue: y * silu(z) = y * z / (1 + exp(-z)) (fp64)."""
+    z = np.asarray(z, dtype=np.float64)
+    return np.asarray(y, dtype=np.float64) * z / (1.0 + np.exp(-z))
+
+
+def run_block(x, dt, A, lam, theta, B, C, block=None, h0=None, prevB0=None,
+              prevx0=None, nthreads: int = 0):
+    """``run`` with the block prologue applied to B and C and the gate to y.
+
+    ``block``: dict with optional keys bc_norm (bool), eps, B_weight, B_bias,
+    C_weight, C_bias ([H,R,N]) and z (shaped like y).  The carried previous B
+    (prevB0) is taken as already prologued (it is the previous token's B).
+    """
+    block = block or {}
+    nrm, eps = bool(block.get("bc_norm", False)), block.get("eps", 1e-6)
+    Bp = bc_norm(B, block.get("B_weight"), block.get("B_bias"), eps, nrm)
+    Cp = bc_norm(C, block.get("C_weight"), block.get("C_bias"), eps, nrm)
+    y, hT, used = run(x, dt, A, lam, theta, Bp, Cp, h0, prevB0, prevx0, nthreads)
+    if block.get("z") is not None:
+        y = gate(y, block["z"])
+    return y, hT, used
