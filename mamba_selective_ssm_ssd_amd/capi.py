@@ -1,4 +1,4 @@
-"""ctypes binding of libm3ssm.so: the C ABI declared in include/m3_ssm.h.
+"""ctypes binding of libm3ssm.so: the C ABI declared in include/m3_ssm*.h.
 
 The functions here have the same names and arguments as the C entry points
 and only marshal arguments.  Loading fails loudly when the library has not
@@ -23,7 +23,8 @@ M3_ERR_HIP = 4
 
 # Every function the headers under include/ declare.
 EXPORTED = ("m3_ssm_prefill_workspace_bytes", "m3_ssm_prefill", "m3_ssm_decode_step",
-            "m3_status_string", "m3_ssm_prefill_stage")
+            "m3_status_string", "m3_ssm_prefill_stage", "m3_ssm_prefill_block",
+            "m3_ssm_decode_step_block")
 
 # Stages of the prefill (include/m3_ssm_stages.h).
 M3_STAGE_SEGMENT_STATE = 0
@@ -41,6 +42,14 @@ class m3_shape_t(ctypes.Structure):
 class m3_state_t(ctypes.Structure):
     _fields_ = [("h", ctypes.c_void_p), ("phi", ctypes.c_void_p),
                 ("prev_B", ctypes.c_void_p), ("prev_x", ctypes.c_void_p)]
+
+
+class m3_block_t(ctypes.Structure):
+    """Block prologue/epilogue (include/m3_ssm_block.h)."""
+    _fields_ = [("bc_norm", ctypes.c_int32), ("norm_eps", ctypes.c_float),
+                ("B_weight", ctypes.c_void_p), ("B_bias", ctypes.c_void_p),
+                ("C_weight", ctypes.c_void_p), ("C_bias", ctypes.c_void_p),
+                ("z", ctypes.c_void_p)]
 
 
 class M3Error(RuntimeError):
@@ -73,6 +82,12 @@ def load():
     lib.m3_ssm_prefill_stage.argtypes = [ctypes.c_int32, sp, vp, vp, vp, vp, vp, vp, vp, stp, stp,
                                          vp, vp, ctypes.c_size_t, vp]
     lib.m3_ssm_prefill_stage.restype = ctypes.c_int
+    bkp = ctypes.POINTER(m3_block_t)
+    lib.m3_ssm_prefill_block.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, bkp, stp, stp, vp, vp,
+                                         ctypes.c_size_t, vp]
+    lib.m3_ssm_prefill_block.restype = ctypes.c_int
+    lib.m3_ssm_decode_step_block.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, bkp, stp, vp, vp]
+    lib.m3_ssm_decode_step_block.restype = ctypes.c_int
     lib.m3_status_string.argtypes = [ctypes.c_int]
     lib.m3_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -110,4 +125,23 @@ def m3_ssm_prefill_stage(stage, shape, x, dt, A, lam, theta, B, C, init, final_s
 def m3_ssm_decode_step(shape, x, dt, A, lam, theta, B, C, state, y, stream) -> int:
     return int(load().m3_ssm_decode_step(
         ctypes.byref(shape), x, dt, A, lam, theta, B, C,
+        ctypes.byref(state) if state is not None else None, y, stream))
+
+
+def m3_ssm_prefill_block(shape, x, dt, A, lam, theta, B, C, block, init, final_state, y,
+                         workspace, workspace_bytes, stream) -> int:
+    """m3_ssm_prefill with ``block`` (an m3_block_t or None)."""
+    return int(load().m3_ssm_prefill_block(
+        ctypes.byref(shape), x, dt, A, lam, theta, B, C,
+        ctypes.byref(block) if block is not None else None,
+        ctypes.byref(init) if init is not None else None,
+        ctypes.byref(final_state) if final_state is not None else None,
+        y, workspace, int(workspace_bytes), stream))
+
+
+def m3_ssm_decode_step_block(shape, x, dt, A, lam, theta, B, C, block, state, y, stream) -> int:
+    """m3_ssm_decode_step with ``block`` (an m3_block_t or None)."""
+    return int(load().m3_ssm_decode_step_block(
+        ctypes.byref(shape), x, dt, A, lam, theta, B, C,
+        ctypes.byref(block) if block is not None else None,
         ctypes.byref(state) if state is not None else None, y, stream))

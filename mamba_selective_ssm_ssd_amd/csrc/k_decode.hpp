@@ -21,6 +21,13 @@
 // in turns) and rotates it.  Values read from the carried state are written
 // back only after the workgroup barrier, so no thread overwrites an input
 // another thread still reads.
+//
+// With BLK the Mamba-3 block's prologue and epilogue (review, section 3.4:
+// BC normalisation, B/C biases, output gate) run inside the step: a B or C
+// unit is scaled by its row's 1 / sqrt(mean_n v^2 + eps) (the row's units sit
+// in aligned groups of consecutive lanes, summed by lane shuffles), times the
+// per-head weight plus bias, before its rotation; each output is multiplied
+// by silu(z) at its store.
 #pragma once
 #include "m3_device.hpp"
 #include "m3_internal.hpp"
@@ -87,7 +94,7 @@ __device__ __forceinline__ void unpack8(const uint2 &u, float *v, float) {
 // source offset, item stride and LDS destination are fixed for the launch.
 enum : int { kUnitB = 0, kUnitC = 1, kUnitX = 2, kUnitXp = 3, kUnitBp = 4, kUnitNone = 5 };
 
-template <typename IO, int N, int P, int R>
+template <typename IO, int N, int P, int R, bool BLK>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode_wg_per_cu(N, P)))) void k_decode_step(const DecodeParams p) {
     typedef DecodeLds<N, P> L;
     constexpr int K = N / 2, P4 = L::P4, G = L::G;
@@ -98,6 +105,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode
     constexpr int UB = R * URN, UX = R * URP, UPB = R * N / 4, UT = 2 * UB + 2 * UX + UPB;
     constexpr int UPT = (UT + kThreads - 1) / kThreads;    // units per thread
     constexpr int64_t sB = int64_t(R) * N * SZ, sX = int64_t(R) * P * SZ, sBp = int64_t(R) * N * 4; // item strides
+    static_assert(!BLK || R * P <= 4 * kThreads, "one gated output quad per thread");
     __shared__ __align__(16) float sm[L::floats];
     float *bt_s = sm + L::o_bt, *bp_s = sm + L::o_bp, *ct_s = sm + L::o_ct;
     float *x_s = sm + L::o_x, *xp_s = sm + L::o_xp, *ph_s = sm + L::o_ph, *red = sm + L::o_red;
@@ -162,6 +170,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode
         const uint32_t dt_raw = io<IO>::raw(static_cast<const IO *>(p.dt) + item);
         const uint32_t lam_raw = io<IO>::raw(static_cast<const IO *>(p.lam) + item);
         const float Ah = p.A[h];
+        // (BLK) weight and bias of each unit's channels and the gate input of
+        // this thread's outputs; a missing piece is read from a valid stand-in
+        // (the item's state, x) and replaced by its neutral value below
+        float4 wq[BLK ? UPT : 1][EPU / 4], bq[BLK ? UPT : 1][EPU / 4];
+        typename io4<IO>::raw zr;
+        if constexpr (BLK) {
+            const float *hs0 = p.h + item * (N * P);
+#pragma unroll
+            for (int j = 0; j < UPT; ++j) {
+                const bool isc = ukind[j] == kUnitC;
+                const int off = ukind[j] <= kUnitC ? h * (R * N) + uw[j] * EPU : 0;
+                const float *ws = isc ? p.blk.cw : p.blk.bw, *bs = isc ? p.blk.cb : p.blk.bb;
+                const float4 *wa = reinterpret_cast<const float4 *>(ws ? ws + off : hs0);
+                const float4 *ba = reinterpret_cast<const float4 *>(bs ? bs + off : hs0);
+#pragma unroll
+                for (int i = 0; i < EPU / 4; ++i) wq[j][i] = wa[i], bq[j][i] = ba[i];
+            }
+            const IO *zs = static_cast<const IO *>(p.blk.z ? p.blk.z : p.x) + item * (R * P) + min(4 * tid, R * P - 4);
+            zr = io4<IO>::load(zs);
+        }
         const int64_t nx = item + gridDim.x < BH ? item + gridDim.x : item;
         load_state(nx, hx);
 
@@ -177,6 +205,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode
             float o[EPU];
 #pragma unroll
             for (int i = 0; i < EPU; ++i) o[i] = e[i];
+            if constexpr (BLK) {
+                // block prologue of a B or C unit (its row's lanes all take part)
+                float inv = 1.f;
+                if (p.blk.norm) {
+                    float ss = 0.f;
+#pragma unroll
+                    for (int i = 0; i < EPU; ++i) ss += e[i] * e[i];
+                    inv = rsqrtf(row_sum<URN>(ss) * (1.f / N) + p.blk.eps);
+                }
+                const bool hw = (ukind[j] == kUnitC ? p.blk.cw : p.blk.bw) != nullptr;
+                const bool hb = (ukind[j] == kUnitC ? p.blk.cb : p.blk.bb) != nullptr;
+#pragma unroll
+                for (int i = 0; i < EPU; ++i) {
+                    const float4 a = wq[j][i / 4], c = bq[j][i / 4];
+                    const float wv = (&a.x)[i % 4], bv = (&c.x)[i % 4];
+                    o[i] = o[i] * inv * (hw ? wv : 1.f) + (hb ? bv : 0.f);
+                }
+            }
             rotate_unit<NPU>(o, ph[j], th, phn);
 #pragma unroll
             for (int i = 0; i < EPU; ++i) o[i] = rot ? o[i] : e[i];
@@ -257,7 +303,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode
                 const float4 v = *reinterpret_cast<const float4 *>(red + (r * 4 + i) * P + pc);
                 s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
             }
-            const float sv[4] = {s.x, s.y, s.z, s.w};
+            float sv[4] = {s.x, s.y, s.z, s.w};
+            if constexpr (BLK) {
+                if (p.blk.z) { // output gate y * silu(z)
+                    float zv[4];
+                    io4<IO>::unpack(zr, zv);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) sv[q] *= zv[q] / (1.f + __expf(-zv[q]));
+                }
+            }
             io<IO>::store4(y + o, sv);
         }
     };
@@ -284,24 +338,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode
     }
 }
 
-template <typename IO, int N, int P, int R>
+template <typename IO, int N, int P, int R, bool BLK>
 hipError_t launch_decode_inst(const DecodeParams &p, hipStream_t s) {
     const int64_t bh = p.batch * p.H;
     const int64_t cap = int64_t(kDecodeCus) * decode_wg_per_cu(N, P);
     const dim3 grid{static_cast<unsigned>(bh < cap ? bh : cap)}, block{kThreads};
-    hipLaunchKernelGGL((k_decode_step<IO, N, P, R>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((k_decode_step<IO, N, P, R, BLK>), grid, block, 0, s, p);
     return hipGetLastError();
 }
 
-// Dispatch over (N, P, R) for one I/O type.
-template <typename IO>
+// Dispatch over (N, P, R) for one I/O type, with or without the block ops.
+template <typename IO, bool BLK>
 hipError_t launch_decode_io(const DecodeParams &p, hipStream_t s) {
 #define M3_DECODE_R(NN, PP)                                                   \
     switch (p.R) {                                                            \
-    case 1: return launch_decode_inst<IO, NN, PP, 1>(p, s);                   \
-    case 2: return launch_decode_inst<IO, NN, PP, 2>(p, s);                   \
-    case 3: return launch_decode_inst<IO, NN, PP, 3>(p, s);                   \
-    case 4: return launch_decode_inst<IO, NN, PP, 4>(p, s);                   \
+    case 1: return launch_decode_inst<IO, NN, PP, 1, BLK>(p, s);              \
+    case 2: return launch_decode_inst<IO, NN, PP, 2, BLK>(p, s);              \
+    case 3: return launch_decode_inst<IO, NN, PP, 3, BLK>(p, s);              \
+    case 4: return launch_decode_inst<IO, NN, PP, 4, BLK>(p, s);              \
     default: return hipErrorInvalidValue;                                     \
     }
 #define M3_DECODE_P(NN)                                                       \

@@ -3,6 +3,9 @@
 
 namespace m3 {
 
-hipError_t launch_decode_bf16(const DecodeParams &p, hipStream_t s) { return launch_decode_io<bf16>(p, s); }
+hipError_t launch_decode_bf16(const DecodeParams &p, hipStream_t s) {
+    if (p.blk.on) return launch_decode_bf16_blk(p, s);
+    return launch_decode_io<bf16, false>(p, s);
+}
 
 } // namespace m3

@@ -63,7 +63,7 @@ constexpr size_t align16(size_t v) { return (v + 15) / 16 * 16; }
 // (narrow layout) by 8 elements only.
 constexpr int lds_pitch(int n, bool wide) { return wide ? (n + 31) / 32 * 32 + 16 : n + 8; }
 
-template <typename IO, int N_, int P_, int R_, bool WIDE>
+template <typename IO, int N_, int P_, int R_, bool WIDE, bool BLK>
 struct CfgW {
     static constexpr int N = N_, P = P_, R = R_, K = N / 2, V = kQ * R;
     static constexpr int PL = mode<IO>::f32 ? 2 : 1;          // bf16 planes per staged value
@@ -113,7 +113,10 @@ struct CfgW {
     // The chunk's token mask L[t][s] (and e^{ell_t}) is tabulated once per
     // chunk when it fits; otherwise each lane evaluates its mask entries.
     static constexpr int LWP = WIDE ? kQ + 8 : kQ + 4;                         // row pitch (floats)
-    static constexpr size_t o_lw = align16(o_ths + size_t(K) * 8);             // float [64][LWP]
+    // block prologue tables (BLK): B weight, B bias, C weight, C bias [R][N]
+    static constexpr size_t o_blk = align16(o_ths + size_t(K) * 8);
+    static constexpr size_t blk_bytes = BLK ? 16 * size_t(R) * N : 0;
+    static constexpr size_t o_lw = align16(o_blk + blk_bytes);                 // float [64][LWP]
     static constexpr size_t lw_bytes = size_t(kQ) * LWP * 4 + kQ * 4;          // + e^{ell} [64]
     static constexpr bool LWT = o_lw + lw_bytes <= kMaxLdsBytes;
     // bf16 I/O: the within-chunk angle prefix is the matrix product of the
@@ -146,16 +149,16 @@ struct CfgW {
 
 // The wide (conflict-free) layout when it fits with every optional table the
 // narrow one has, else the narrow layout.
-template <typename IO, int N, int P, int R>
+template <typename IO, int N, int P, int R, bool BLK>
 struct CfgPick {
-    typedef CfgW<IO, N, P, R, true> Wd;
-    typedef CfgW<IO, N, P, R, false> Nw;
+    typedef CfgW<IO, N, P, R, true, BLK> Wd;
+    typedef CfgW<IO, N, P, R, false, BLK> Nw;
     static constexpr bool wide = Wd::bytes <= kMaxLdsBytes && Wd::LWT == Nw::LWT && Wd::MFP == Nw::MFP &&
                                  Wd::XS == Nw::XS && Wd::CL == Nw::CL;
     typedef typename std::conditional<wide, Wd, Nw>::type type;
 };
-template <typename IO, int N, int P, int R>
-using Cfg = typename CfgPick<IO, N, P, R>::type;
+template <typename IO, int N, int P, int R, bool BLK = false>
+using Cfg = typename CfgPick<IO, N, P, R, BLK>::type;
 
 // Raw (undecoded) B, x and C of one chunk held in registers.
 template <class C>
@@ -495,6 +498,23 @@ __device__ __forceinline__ void run_coef(const RawPro<C> &r, int Tc, int64_t t0,
     }
 }
 
+// Block prologue (Mamba-3 review, section 3.4: BC normalisation, B/C biases)
+// on NV consecutive channels of one B or C row: e <- e * inv * w + bias, with
+// w, bias the row's [N] weight and bias at those channels (LDS) and inv the
+// row's 1 / sqrt(mean_n e^2 + eps) (1 without the normalisation).
+template <int NV>
+__device__ __forceinline__ void block_unit(float *e, float inv, const float *w, const float *bias) {
+#pragma unroll
+    for (int i = 0; i < NV; i += 4) {
+        const float4 a = *reinterpret_cast<const float4 *>(w + i);
+        const float4 c = *reinterpret_cast<const float4 *>(bias + i);
+        e[i] = e[i] * inv * a.x + c.x;
+        e[i + 1] = e[i + 1] * inv * a.y + c.y;
+        e[i + 2] = e[i + 2] * inv * a.z + c.z;
+        e[i + 3] = e[i + 3] * inv * a.w + c.w;
+    }
+}
+
 // State entering the sequence, as one 16x16 tile of this lane (rows
 // n = 16 nt + 4 g + v, column 16 pt + l16), in the state's own frame at the
 // sequence start: R(Phi_{-1}) (h~ + delta_0 B~_prev x_prev^T).
@@ -526,9 +546,9 @@ __device__ __forceinline__ floatx4 fold_init(const PrefillParams &p, int64_t bh,
     return o;
 }
 
-template <typename IO, int N, int P, int R, bool OUT>
+template <typename IO, int N, int P, int R, bool OUT, bool BLK>
 __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
-    typedef Cfg<IO, N, P, R> C;
+    typedef Cfg<IO, N, P, R, BLK> C;
     typedef typename C::M M;
     typedef typename C::frag frag;
     constexpr int PL = C::PL, K = C::K, V = C::V, NBP = C::NBP, PP = C::PP, EPU = C::EPU;
@@ -564,6 +584,7 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
     double *ths_s = reinterpret_cast<double *>(smem + C::o_ths);   // [K]
     float *lw_s = reinterpret_cast<float *>(smem + C::o_lw);       // [64][LWP] mask, then e^{ell} [64]
     uint16_t *tht = reinterpret_cast<uint16_t *>(smem + C::o_th);  // theta rows of the next chunk
+    float *blk_s = reinterpret_cast<float *>(smem + C::o_blk);     // (BLK) [4][R][N] B w, B b, C w, C b
 
     // running angle: Phi_{-1} plus the segments before this one (output pass)
     for (int k = tid; k < K; k += kPT) {
@@ -589,7 +610,17 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
     load_chunk<C, IO, OUT>(p, b, h, int64_t(c_begin) * kQ, tc_of(c_begin), raw);
     write_theta<C>(rp, tht);
     run_coef<C, IO>(rp, tc_of(c_begin), int64_t(c_begin) * kQ, p.T, Ah, coef_s, misc_s);
-    __syncthreads(); // ths_s, theta table
+    if constexpr (BLK) {
+        // this head's block prologue weights and biases (1 and 0 when absent)
+        const int64_t hb0 = int64_t(h) * R * N;
+        for (int i = tid; i < R * N; i += kPT) {
+            blk_s[i] = p.blk.bw ? p.blk.bw[hb0 + i] : 1.f;
+            blk_s[R * N + i] = p.blk.bb ? p.blk.bb[hb0 + i] : 0.f;
+            blk_s[2 * R * N + i] = p.blk.cw ? p.blk.cw[hb0 + i] : 1.f;
+            blk_s[3 * R * N + i] = p.blk.cb ? p.blk.cb[hb0 + i] : 0.f;
+        }
+    }
+    __syncthreads(); // ths_s, theta table, block tables
     run_angles<C, IO>(rp, tc_of(c_begin), cs_s, thc_s, ths_s, tht);
     if (c_begin + 1 < c_end) {
         load_pro<C, IO>(p, b, h, int64_t(c_begin + 1) * kQ, tc_of(c_begin + 1), rp);
@@ -681,6 +712,30 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
                 // no register copies)
                 __builtin_amdgcn_sched_barrier(0);
                 load_chunk<C, IO, OUT, 1 | CPART, j>(p, b, h, tn0, Tn, raw);
+                if constexpr (BLK) {
+                    // block prologue of the row's channels q*EPU..: the row is
+                    // held by URB consecutive lanes
+                    const int r = v % R;
+                    float inv = 1.f, invc = 1.f;
+                    if (p.blk.norm) {
+                        float ss = 0.f, sc = 0.f;
+#pragma unroll
+                        for (int i = 0; i < EPU; ++i) ss += e[i] * e[i];
+                        if constexpr (OUT && C::CL) {
+#pragma unroll
+                            for (int i = 0; i < EPU; ++i) sc += ec[i] * ec[i];
+                        }
+                        ss = row_sum<C::URB>(ss);
+                        inv = rsqrtf(ss * (1.f / N) + p.blk.eps);
+                        if constexpr (OUT && C::CL) {
+                            sc = row_sum<C::URB>(sc);
+                            invc = rsqrtf(sc * (1.f / N) + p.blk.eps);
+                        }
+                    }
+                    const float *wr = blk_s + r * N + q * EPU;
+                    block_unit<EPU>(e, inv, wr, wr + R * N);
+                    if constexpr (OUT && C::CL) block_unit<EPU>(ec, invc, wr + 2 * R * N, wr + 3 * R * N);
+                }
 #pragma unroll
                 for (int w4 = 0; w4 < EPU / 4; ++w4) {
                     const float4 a = csr[w4];
@@ -727,12 +782,36 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
                 const int tb = wave_block(i, wave);
                 if (C::NTB < C::TBW * kPW && tb >= C::NTB) continue; // uniform: waves without this row block
                 const int tok = (16 * tb + l16) / R;
+                // (BLK) block prologue of this lane's channels of its row; the
+                // row's channels are spread over lanes l16, l16 + 16, +32, +48
+                float inv = 1.f;
+                if constexpr (BLK) {
+                    if (p.blk.norm) {
+                        float ss = 0.f;
+#pragma unroll
+                        for (int ks = 0; ks < NKS; ++ks) {
+                            float e[8], sk = 0.f;
+#pragma unroll
+                            for (int f = 0; f < C::FU; ++f) unpack_unit(raw.cc[i][ks][f], e + f * EPU, IO());
+#pragma unroll
+                            for (int jj = 0; jj < 8; ++jj) sk += e[jj] * e[jj];
+                            ss += (N % 32 == 0 || 32 * ks + 8 * g < N) ? sk : 0.f;
+                        }
+                        ss += __shfl_xor(ss, 16);
+                        ss += __shfl_xor(ss, 32);
+                        inv = rsqrtf(ss * (1.f / N) + p.blk.eps);
+                    }
+                }
 #pragma unroll
                 for (int ks = 0; ks < NKS; ++ks) {
                     const int n0 = 32 * ks + 8 * g;
                     float e[8];
 #pragma unroll
                     for (int f = 0; f < C::FU; ++f) unpack_unit(raw.cc[i][ks][f], e + f * EPU, IO());
+                    if constexpr (BLK) {
+                        const float *wr = blk_s + 2 * R * N + ((16 * tb + l16) % R) * N + min(n0, N - 8);
+                        block_unit<8>(e, inv, wr, wr + R * N);
+                    }
                     if (N % 32 == 0 || n0 < N) {
                         const float4 *cr = reinterpret_cast<const float4 *>(cs_s + tok * C::CSP + n0);
 #pragma unroll
@@ -825,6 +904,17 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
                 const int t0v = 16 * tb;
                 if (t0v / R >= Tc) continue;
                 const int tok_last = min((t0v + 15) / R, Tc - 1);
+                // (BLK) gate inputs of this lane's outputs, issued here and used
+                // at the store; without a gate they are read from x (unused)
+                typename io4<IO>::raw zr[BLK ? PT : 1];
+                if constexpr (BLK) {
+                    const int vr = t0v + l16;
+                    const int tz = min(vr / R, Tc - 1), cz = vr % R;
+                    const IO *zb = static_cast<const IO *>(p.blk.z ? p.blk.z : p.x) +
+                                   ((b * p.T + t0 + tz) * p.H + h) * (R * P) + cz * P + 4 * g;
+#pragma unroll
+                    for (int pt = 0; pt < PT; ++pt) zr[pt] = io4<IO>::load(zb + 16 * pt);
+                }
                 if constexpr (C::CL) {
 #pragma unroll
                     for (int ks = 0; ks < NKS; ++ks) {
@@ -988,7 +1078,16 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
                         IO *dst = ybase + ((tok * p.H * R + ch) * P + 4 * g);
 #pragma unroll
                         for (int pt = 0; pt < PT; ++pt) {
-                            const float o4[4] = {acc[pt][0], acc[pt][1], acc[pt][2], acc[pt][3]};
+                            float o4[4] = {acc[pt][0], acc[pt][1], acc[pt][2], acc[pt][3]};
+                            if constexpr (BLK) {
+                                if (p.blk.z) {
+                                    // output gate: y * silu(z)
+                                    float zv[4];
+                                    io4<IO>::unpack(zr[pt], zv);
+#pragma unroll
+                                    for (int q = 0; q < 4; ++q) o4[q] *= zv[q] / (1.f + __expf(-zv[q]));
+                                }
+                            }
                             io<IO>::store4(dst + 16 * pt, o4);
                         }
                     }
@@ -1110,6 +1209,23 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
         sincos_wrapped(wrap_angle(ths_s[k]), &sn, &cs);
         const IO *Bl = static_cast<const IO *>(p.B) + (tl * R + r) * N + 2 * k;
         float u = io<IO>::get(Bl), v = io<IO>::get(Bl + 1);
+        if constexpr (BLK) {
+            // block prologue of the last token's B row r (its RMS over N
+            // summed here by this thread)
+            float inv = 1.f;
+            if (p.blk.norm) {
+                const IO *row = Bl - 2 * k;
+                float ss = 0.f;
+                for (int n = 0; n < N; ++n) {
+                    const float t = io<IO>::get(row + n);
+                    ss += t * t;
+                }
+                inv = rsqrtf(ss * (1.f / N) + p.blk.eps);
+            }
+            const float *wr = blk_s + r * N + 2 * k;
+            u = u * inv * wr[0] + wr[R * N];
+            v = v * inv * wr[1] + wr[R * N + 1];
+        }
         rot_neg(cs, sn, u, v);
         p.prevBT[(bh * R + r) * N + 2 * k] = u;
         p.prevBT[(bh * R + r) * N + 2 * k + 1] = v;
@@ -1119,19 +1235,20 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
     for (int i = tid; i < R * P; i += kPT) px[i] = xl[i];
 }
 
-// Host-side launch of one instantiation (pre-pass when OUT is false).
-template <typename IO, int N, int P, int R, bool OUT>
+// Host-side launch of one instantiation (pre-pass when OUT is false; the
+// block prologue/epilogue kernels when BLK).
+template <typename IO, int N, int P, int R, bool OUT, bool BLK>
 hipError_t launch_prefill_inst(const PrefillParams &p, hipStream_t s) {
-    typedef Cfg<IO, N, P, R> C;
+    typedef Cfg<IO, N, P, R, BLK> C;
     const int nseg = OUT ? p.S : p.S - 1;
     if (nseg <= 0) return hipSuccess;
     if (C::bytes > 65536) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_prefill<IO, N, P, R, OUT>),
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_prefill<IO, N, P, R, OUT, BLK>),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, int(C::bytes));
         if (e != hipSuccess) return e;
     }
     const dim3 grid(unsigned(p.batch * p.H * nseg)), block(kPT);
-    hipLaunchKernelGGL((k_prefill<IO, N, P, R, OUT>), grid, block, C::bytes, s, p);
+    hipLaunchKernelGGL((k_prefill<IO, N, P, R, OUT, BLK>), grid, block, C::bytes, s, p);
     return hipGetLastError();
 }
 

@@ -1,4 +1,4 @@
-// k_prefill_f32_n128.hip -- instantiations of the fused prefill kernel for fp32 I/O, N = 128.
+// k_prefill_f32_n128.hip -- instantiations of the fused prefill kernel for f32 I/O, N = 128.
 #include "k_prefill.hpp"
 
 namespace m3 {
@@ -6,15 +6,16 @@ namespace m3 {
 template <int P>
 static hipError_t by_rank(const PrefillParams &p, bool out, hipStream_t s) {
     switch (p.R) {
-    case 1: return out ? launch_prefill_inst<float, 128, P, 1, true>(p, s) : launch_prefill_inst<float, 128, P, 1, false>(p, s);
-    case 2: return out ? launch_prefill_inst<float, 128, P, 2, true>(p, s) : launch_prefill_inst<float, 128, P, 2, false>(p, s);
-    case 3: return out ? launch_prefill_inst<float, 128, P, 3, true>(p, s) : launch_prefill_inst<float, 128, P, 3, false>(p, s);
-    case 4: return out ? launch_prefill_inst<float, 128, P, 4, true>(p, s) : launch_prefill_inst<float, 128, P, 4, false>(p, s);
+    case 1: return out ? launch_prefill_inst<float, 128, P, 1, true, false>(p, s) : launch_prefill_inst<float, 128, P, 1, false, false>(p, s);
+    case 2: return out ? launch_prefill_inst<float, 128, P, 2, true, false>(p, s) : launch_prefill_inst<float, 128, P, 2, false, false>(p, s);
+    case 3: return out ? launch_prefill_inst<float, 128, P, 3, true, false>(p, s) : launch_prefill_inst<float, 128, P, 3, false, false>(p, s);
+    case 4: return out ? launch_prefill_inst<float, 128, P, 4, true, false>(p, s) : launch_prefill_inst<float, 128, P, 4, false, false>(p, s);
     }
     return hipErrorInvalidValue;
 }
 
 hipError_t launch_prefill_f32_n128(const PrefillParams &p, bool out, hipStream_t s) {
+    if (p.blk.on) return launch_prefill_f32_n128_blk(p, out, s);
     switch (p.P) {
     case 16: return by_rank<16>(p, out, s);
     case 32: return by_rank<32>(p, out, s);

@@ -98,6 +98,29 @@ struct io<bf16> {
     }
 };
 
+// Four consecutive I/O elements kept as raw bits (8 bytes for bf16, 16 for
+// fp32): loaded early, decoded when used.
+template <typename IO>
+struct io4;
+template <>
+struct io4<bf16> {
+    typedef uint2 raw;
+    static __device__ __forceinline__ raw load(const bf16 *p) { return *reinterpret_cast<const uint2 *>(p); }
+    static __device__ __forceinline__ void unpack(const raw &r, float v[4]) {
+        v[0] = __uint_as_float(r.x << 16); v[1] = __uint_as_float(r.x & 0xffff0000u);
+        v[2] = __uint_as_float(r.y << 16); v[3] = __uint_as_float(r.y & 0xffff0000u);
+    }
+};
+template <>
+struct io4<float> {
+    typedef uint4 raw;
+    static __device__ __forceinline__ raw load(const float *p) { return *reinterpret_cast<const uint4 *>(p); }
+    static __device__ __forceinline__ void unpack(const raw &r, float v[4]) {
+        v[0] = __uint_as_float(r.x); v[1] = __uint_as_float(r.y);
+        v[2] = __uint_as_float(r.z); v[3] = __uint_as_float(r.w);
+    }
+};
+
 // ---------------------------------------------------------------------------
 // MFMA fragments for v_mfma_f32_16x16x32_bf16 (gfx950).
 // Operand A (16 x 32): lane l supplies row (l % 16) and eight k-slots
@@ -356,6 +379,15 @@ __device__ __forceinline__ void sincos_wrapped(double x, float *s_out, float *c_
     const double c = qi == 0 ? cs : qi == 1 ? -sn : qi == 2 ? -cs : sn;
     *s_out = float(s);
     *c_out = float(c);
+}
+
+// Sum of v over the W consecutive lanes that hold one row (W a power of two
+// dividing 64, every lane of the row active).
+template <int W>
+__device__ __forceinline__ float row_sum(float v) {
+#pragma unroll
+    for (int m = 1; m < W; m <<= 1) v += __shfl_xor(v, m);
+    return v;
 }
 
 // Rotation R(-phi) of a row pair: (u, v) -> (c u + s v, -s u + c v).

@@ -8,6 +8,17 @@
 
 namespace m3 {
 
+// Block prologue and epilogue around the mixer (Mamba-3 review, section 3.4):
+// B and C rows RMS-normalised over N, then weight and bias per (head, rank,
+// channel); y gated by silu(z).  Absent pieces are null / zero.
+struct BlockParams {
+    int32_t on;                     // any piece present: the block kernels run
+    int32_t norm;                   // RMS-normalise the B and C rows
+    float eps;                      // inside the square root
+    const float *bw, *bb, *cw, *cb; // [H][R][N] fp32: B weight, B bias, C weight, C bias
+    const void *z;                  // gate, shaped like y (I/O dtype)
+};
+
 // Everything one prefill call needs, resolved to device pointers.
 struct PrefillParams {
     int64_t batch, T;
@@ -32,6 +43,7 @@ struct PrefillParams {
     double *segTh;  // [b][H][S][K]     summed rotary angle of the segment
     float *hinit;   // [b][H][N][P]     carried state in its own frame at the sequence start
     double *phi0ws; // [b][H][K]        Phi_{-1}
+    BlockParams blk;
 };
 
 struct DecodeParams {
@@ -42,6 +54,7 @@ struct DecodeParams {
     void *y;
     float *h, *phi, *prevB;
     void *prevx;
+    BlockParams blk;
 };
 
 // Workspace layout (byte offsets of each region, 256-byte aligned).
@@ -59,12 +72,24 @@ hipError_t launch_prefill_f32_n16(const PrefillParams &p, bool out, hipStream_t 
 hipError_t launch_prefill_f32_n32(const PrefillParams &p, bool out, hipStream_t s);
 hipError_t launch_prefill_f32_n64(const PrefillParams &p, bool out, hipStream_t s);
 hipError_t launch_prefill_f32_n128(const PrefillParams &p, bool out, hipStream_t s);
+// the same with the block prologue/epilogue (p.blk.on)
+hipError_t launch_prefill_bf16_n16_blk(const PrefillParams &p, bool out, hipStream_t s);
+hipError_t launch_prefill_bf16_n32_blk(const PrefillParams &p, bool out, hipStream_t s);
+hipError_t launch_prefill_bf16_n64_blk(const PrefillParams &p, bool out, hipStream_t s);
+hipError_t launch_prefill_bf16_n128_blk(const PrefillParams &p, bool out, hipStream_t s);
+hipError_t launch_prefill_f32_n16_blk(const PrefillParams &p, bool out, hipStream_t s);
+hipError_t launch_prefill_f32_n32_blk(const PrefillParams &p, bool out, hipStream_t s);
+hipError_t launch_prefill_f32_n64_blk(const PrefillParams &p, bool out, hipStream_t s);
+hipError_t launch_prefill_f32_n128_blk(const PrefillParams &p, bool out, hipStream_t s);
 
 hipError_t launch_decode_bf16(const DecodeParams &p, hipStream_t s);
 hipError_t launch_decode_f32(const DecodeParams &p, hipStream_t s);
+// the same with the block prologue/epilogue (p.blk.on)
+hipError_t launch_decode_bf16_blk(const DecodeParams &p, hipStream_t s);
+hipError_t launch_decode_f32_blk(const DecodeParams &p, hipStream_t s);
 
 // Dynamic LDS bytes of the fused prefill kernel for a shape (0: not compiled).
-size_t prefill_lds_bytes(bool is_bf16, int N, int P, int R);
+size_t prefill_lds_bytes(bool is_bf16, int N, int P, int R, bool blk = false);
 constexpr size_t kMaxLdsBytes = 160 * 1024; // LDS per workgroup on gfx950
 
 // Sizes handled by the compiled kernels.

@@ -9,6 +9,7 @@
 // aggregate.  Decode enqueues one k_decode_step.  m3_ssm_prefill_stage
 // enqueues one of the two prefill kernels alone (include/m3_ssm_stages.h).
 #include "m3_ssm.h"
+#include "m3_ssm_block.h"
 #include "m3_ssm_stages.h"
 #include "k_prefill.hpp"
 #include "m3_internal.hpp"
@@ -92,14 +93,14 @@ bool state_ok(const m3_state_t *st) {
 
 namespace m3 {
 
-template <typename IO, int N>
+template <typename IO, int N, bool BLK>
 static size_t lds_np(int P, int R) {
 #define M3_LDS_R(PP)                                                                     \
     switch (R) {                                                                         \
-    case 1: return Cfg<IO, N, PP, 1>::bytes;                                             \
-    case 2: return Cfg<IO, N, PP, 2>::bytes;                                             \
-    case 3: return Cfg<IO, N, PP, 3>::bytes;                                             \
-    case 4: return Cfg<IO, N, PP, 4>::bytes;                                             \
+    case 1: return Cfg<IO, N, PP, 1, BLK>::bytes;                                        \
+    case 2: return Cfg<IO, N, PP, 2, BLK>::bytes;                                        \
+    case 3: return Cfg<IO, N, PP, 3, BLK>::bytes;                                        \
+    case 4: return Cfg<IO, N, PP, 4, BLK>::bytes;                                        \
     }                                                                                    \
     return 0;
     switch (P) {
@@ -111,14 +112,19 @@ static size_t lds_np(int P, int R) {
     return 0;
 }
 
-size_t prefill_lds_bytes(bool is_bf16, int N, int P, int R) {
+template <bool BLK>
+static size_t lds_n(bool is_bf16, int N, int P, int R) {
     switch (N) {
-    case 16: return is_bf16 ? lds_np<bf16, 16>(P, R) : lds_np<float, 16>(P, R);
-    case 32: return is_bf16 ? lds_np<bf16, 32>(P, R) : lds_np<float, 32>(P, R);
-    case 64: return is_bf16 ? lds_np<bf16, 64>(P, R) : lds_np<float, 64>(P, R);
-    case 128: return is_bf16 ? lds_np<bf16, 128>(P, R) : lds_np<float, 128>(P, R);
+    case 16: return is_bf16 ? lds_np<bf16, 16, BLK>(P, R) : lds_np<float, 16, BLK>(P, R);
+    case 32: return is_bf16 ? lds_np<bf16, 32, BLK>(P, R) : lds_np<float, 32, BLK>(P, R);
+    case 64: return is_bf16 ? lds_np<bf16, 64, BLK>(P, R) : lds_np<float, 64, BLK>(P, R);
+    case 128: return is_bf16 ? lds_np<bf16, 128, BLK>(P, R) : lds_np<float, 128, BLK>(P, R);
     }
     return 0;
+}
+
+size_t prefill_lds_bytes(bool is_bf16, int N, int P, int R, bool blk) {
+    return blk ? lds_n<true>(is_bf16, N, P, R) : lds_n<false>(is_bf16, N, P, R);
 }
 
 } // namespace m3
@@ -141,14 +147,40 @@ size_t m3_ssm_prefill_workspace_bytes(const m3_shape_t *shape) {
     return layout(shape).total;
 }
 
+// Validates the optional block prologue/epilogue and resolves it.
+static m3_status_t resolve_block(const m3_block_t *blk, m3::BlockParams &b) {
+    b = m3::BlockParams{};
+    if (!blk) return M3_OK;
+    const void *ptrs[] = {blk->B_weight, blk->B_bias, blk->C_weight, blk->C_bias, blk->z};
+    for (const void *q : ptrs)
+        if (q && !aligned16(q)) return M3_ERR_INVALID_ARGUMENT;
+    if (blk->bc_norm && !(blk->norm_eps >= 0.f && blk->norm_eps <= 3.0e38f)) return M3_ERR_INVALID_ARGUMENT;
+    b.norm = blk->bc_norm != 0;
+    b.eps = blk->norm_eps;
+    b.bw = blk->B_weight; b.bb = blk->B_bias; b.cw = blk->C_weight; b.cb = blk->C_bias;
+    b.z = blk->z;
+    b.on = b.norm || b.bw || b.bb || b.cw || b.cb || b.z;
+    return M3_OK;
+}
+
 // Validates a prefill call and resolves its parameters.
 static m3_status_t prepare_prefill(const m3_shape_t *shape, const void *x, const void *dt,
                                    const float *A, const void *lam, const void *theta,
                                    const void *B, const void *C, const m3_state_t *init,
                                    m3_state_t *final_state, void *y, void *workspace,
-                                   size_t workspace_bytes, PrefillParams &p) {
+                                   size_t workspace_bytes, PrefillParams &p,
+                                   const m3_block_t *block = nullptr) {
     const m3_status_t sc = check_shape(shape, false);
     if (sc != M3_OK) return sc;
+    m3::BlockParams bp;
+    const m3_status_t sb = resolve_block(block, bp);
+    if (sb != M3_OK) return sb;
+    if (bp.on) {
+        // the block kernels also keep this head's weights and biases in LDS
+        const size_t lds = m3::prefill_lds_bytes(shape->io_dtype == M3_DTYPE_BF16, shape->dstate,
+                                                 shape->headdim, shape->rank, true);
+        if (lds == 0 || lds > m3::kMaxLdsBytes) return M3_ERR_UNSUPPORTED;
+    }
     const void *ptrs[] = {x, dt, A, lam, theta, B, C, y};
     for (const void *q : ptrs)
         if (!q || !aligned16(q)) return M3_ERR_INVALID_ARGUMENT;
@@ -183,6 +215,7 @@ static m3_status_t prepare_prefill(const m3_shape_t *shape, const void *x, const
     p.segTh = reinterpret_cast<double *>(ws + w.segTh);
     p.hinit = reinterpret_cast<float *>(ws + w.hinit);
     p.phi0ws = reinterpret_cast<double *>(ws + w.phi0);
+    p.blk = bp;
     return M3_OK;
 }
 
@@ -202,9 +235,18 @@ m3_status_t m3_ssm_prefill(const m3_shape_t *shape, const void *x, const void *d
                            const void *lam, const void *theta, const void *B, const void *C,
                            const m3_state_t *init, m3_state_t *final_state, void *y,
                            void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    return m3_ssm_prefill_block(shape, x, dt, A, lam, theta, B, C, nullptr, init, final_state, y,
+                                workspace, workspace_bytes, stream);
+}
+
+m3_status_t m3_ssm_prefill_block(const m3_shape_t *shape, const void *x, const void *dt,
+                                 const float *A, const void *lam, const void *theta,
+                                 const void *B, const void *C, const m3_block_t *block,
+                                 const m3_state_t *init, m3_state_t *final_state, void *y,
+                                 void *workspace, size_t workspace_bytes, hipStream_t stream) {
     PrefillParams p;
     const m3_status_t sc = prepare_prefill(shape, x, dt, A, lam, theta, B, C, init, final_state, y,
-                                           workspace, workspace_bytes, p);
+                                           workspace, workspace_bytes, p, block);
     if (sc != M3_OK) return sc;
     const bool bf = shape->io_dtype == M3_DTYPE_BF16;
     for (int32_t stage = M3_STAGE_SEGMENT_STATE; stage <= M3_STAGE_OUTPUT; ++stage)
@@ -229,8 +271,18 @@ m3_status_t m3_ssm_prefill_stage(int32_t stage, const m3_shape_t *shape, const v
 m3_status_t m3_ssm_decode_step(const m3_shape_t *shape, const void *x, const void *dt, const float *A,
                                const void *lam, const void *theta, const void *B, const void *C,
                                m3_state_t *state, void *y, hipStream_t stream) {
+    return m3_ssm_decode_step_block(shape, x, dt, A, lam, theta, B, C, nullptr, state, y, stream);
+}
+
+m3_status_t m3_ssm_decode_step_block(const m3_shape_t *shape, const void *x, const void *dt,
+                                     const float *A, const void *lam, const void *theta,
+                                     const void *B, const void *C, const m3_block_t *block,
+                                     m3_state_t *state, void *y, hipStream_t stream) {
     const m3_status_t sc = check_shape(shape, true);
     if (sc != M3_OK) return sc;
+    m3::BlockParams bp;
+    const m3_status_t sb = resolve_block(block, bp);
+    if (sb != M3_OK) return sb;
     const void *ptrs[] = {x, dt, A, lam, theta, B, C, y};
     for (const void *q : ptrs)
         if (!q || !aligned16(q)) return M3_ERR_INVALID_ARGUMENT;
@@ -244,6 +296,7 @@ m3_status_t m3_ssm_decode_step(const m3_shape_t *shape, const void *x, const voi
     p.K = p.N / 2;
     p.x = x; p.dt = dt; p.lam = lam; p.theta = theta; p.B = B; p.C = C; p.A = A; p.y = y;
     p.h = state->h; p.phi = state->phi; p.prevB = state->prev_B; p.prevx = state->prev_x;
+    p.blk = bp;
     if ((shape->io_dtype == M3_DTYPE_BF16 ? m3::launch_decode_bf16(p, stream) : m3::launch_decode_f32(p, stream)) != hipSuccess)
         return M3_ERR_HIP;
     return M3_OK;

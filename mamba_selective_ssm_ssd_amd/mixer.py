@@ -5,6 +5,9 @@ every step of the mixer runs in the HIP kernels of libm3ssm.so.  Tensors must
 be contiguous, on the current HIP device, in the layouts of include/m3_ssm.h:
     x [b,T,H,R,P], B/C [b,T,H,R,N], dt/lam [b,T,H], theta [b,T,H,N/2] (I/O
     dtype: float32 or bfloat16), A [H] float32.
+With a ``Block`` (and/or a gate input ``z`` shaped like y) the Mamba-3
+block's B/C normalisation, B/C weight and bias and output gate run inside the
+same kernels (include/m3_ssm_block.h).
 """
 from __future__ import annotations
 
@@ -43,6 +46,35 @@ class State:
         return State(self.h.clone(), self.phi.clone(), self.prev_B.clone(), self.prev_x.clone())
 
 
+@dataclass
+class Block:
+    """Per-layer parameters of the block prologue: RMS normalisation of the
+    B and C rows over N (``bc_norm``, ``eps``), then per-head, per-channel
+    weight and bias, each [H,R,N] float32 or None (1 / 0)."""
+    bc_norm: bool = True
+    eps: float = 1e-6
+    B_weight: torch.Tensor | None = None
+    B_bias: torch.Tensor | None = None
+    C_weight: torch.Tensor | None = None
+    C_bias: torch.Tensor | None = None
+
+
+def _block_c(block: Block | None, z, io, H, R, N) -> capi.m3_block_t | None:
+    if block is None and z is None:
+        return None
+    blk = block if block is not None else Block(bc_norm=False)
+    c = capi.m3_block_t(int(bool(blk.bc_norm)), float(blk.eps))
+    for name in ("B_weight", "B_bias", "C_weight", "C_bias"):
+        t = getattr(blk, name)
+        if t is not None:
+            if tuple(t.shape) != (H, R, N):
+                raise ValueError(f"{name} must be [H,R,N] = {(H, R, N)}, got {tuple(t.shape)}")
+            setattr(c, name, _ptr(t, name, torch.float32))
+    if z is not None:
+        c.z = _ptr(z, "z", io)
+    return c
+
+
 def _ptr(t: torch.Tensor, name: str, dtype) -> int:
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
@@ -67,8 +99,10 @@ def workspace_bytes(batch, T, H, P, N, R, io_dtype=torch.bfloat16) -> int:
 
 
 def prefill(x, dt, A, lam, theta, B, C, state: State | None = None, final: State | None = None,
-            want_final: bool = True, y=None, workspace=None):
+            want_final: bool = True, y=None, workspace=None, block: Block | None = None, z=None):
     """Chunked prefill.  Returns (y, final_state or None).
+
+    ``block`` / ``z`` (shaped like x) add the block prologue and output gate.
 
     ``state`` is the carried state to start from (None: fresh sequence).
     The final state goes to ``final`` if given, else to ``state`` (in place)
@@ -94,14 +128,20 @@ def prefill(x, dt, A, lam, theta, B, C, state: State | None = None, final: State
                            "m3_ssm_prefill_workspace_bytes")
     if workspace is None:
         workspace = torch.empty(need, device=x.device, dtype=torch.uint8)
-    rc = capi.m3_ssm_prefill(
-        shape, _ptr(x, "x", io), _ptr(dt, "dt", io), _ptr(A, "A", torch.float32),
-        _ptr(lam, "lam", io), _ptr(theta, "theta", io), _ptr(B, "B", io), _ptr(C, "C", io),
-        state.c() if state is not None else None, final.c() if final is not None else None,
-        _ptr(y, "y", io), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-        _stream())
+    if z is not None and tuple(z.shape) != tuple(x.shape):
+        raise ValueError("z must be shaped like x")
+    args = [shape, _ptr(x, "x", io), _ptr(dt, "dt", io), _ptr(A, "A", torch.float32),
+            _ptr(lam, "lam", io), _ptr(theta, "theta", io), _ptr(B, "B", io), _ptr(C, "C", io)]
+    tail = [state.c() if state is not None else None, final.c() if final is not None else None,
+            _ptr(y, "y", io), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+            _stream()]
+    blk = _block_c(block, z, io, H, R, N)
+    if blk is None:
+        rc, fn = capi.m3_ssm_prefill(*args, *tail), "m3_ssm_prefill"
+    else:
+        rc, fn = capi.m3_ssm_prefill_block(*args, blk, *tail), "m3_ssm_prefill_block"
     if rc != capi.M3_OK:
-        raise capi.M3Error(rc, "m3_ssm_prefill")
+        raise capi.M3Error(rc, fn)
     return y, final
 
 
@@ -121,19 +161,27 @@ def prefill_stage(stage: int, x, dt, A, lam, theta, B, C, state, final, y, works
         raise capi.M3Error(rc, "m3_ssm_prefill_stage")
 
 
-def decode_step(x, dt, A, lam, theta, B, C, state: State, y=None):
+def decode_step(x, dt, A, lam, theta, B, C, state: State, y=None, block: Block | None = None,
+                z=None):
     """One decode step (token axis dropped: x [b,H,R,P], ...).  Updates
-    ``state`` in place and returns y [b,H,R,P]."""
+    ``state`` in place and returns y [b,H,R,P].  ``block`` / ``z`` (shaped
+    like x) add the block prologue and output gate."""
     b, H, R, P = x.shape
     N = B.shape[-1]
     io = x.dtype
     shape = make_shape(b, 1, H, P, N, R, io)
     if y is None:
         y = torch.empty_like(x)
-    rc = capi.m3_ssm_decode_step(
-        shape, _ptr(x, "x", io), _ptr(dt, "dt", io), _ptr(A, "A", torch.float32),
-        _ptr(lam, "lam", io), _ptr(theta, "theta", io), _ptr(B, "B", io), _ptr(C, "C", io),
-        state.c(), _ptr(y, "y", io), _stream())
+    if z is not None and tuple(z.shape) != tuple(x.shape):
+        raise ValueError("z must be shaped like x")
+    args = [shape, _ptr(x, "x", io), _ptr(dt, "dt", io), _ptr(A, "A", torch.float32),
+            _ptr(lam, "lam", io), _ptr(theta, "theta", io), _ptr(B, "B", io), _ptr(C, "C", io)]
+    blk = _block_c(block, z, io, H, R, N)
+    if blk is None:
+        rc, fn = capi.m3_ssm_decode_step(*args, state.c(), _ptr(y, "y", io), _stream()), "m3_ssm_decode_step"
+    else:
+        rc, fn = (capi.m3_ssm_decode_step_block(*args, blk, state.c(), _ptr(y, "y", io), _stream()),
+                  "m3_ssm_decode_step_block")
     if rc != capi.M3_OK:
-        raise capi.M3Error(rc, "m3_ssm_decode_step")
+        raise capi.M3Error(rc, fn)
     return y

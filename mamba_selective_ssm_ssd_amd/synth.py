@@ -11,6 +11,9 @@ workloads of the Mamba-3 review's experiments (section 4; appendix D):
     lam     = sigmoid(N(0, 1))
     theta   ~ U(0, pi)                  per (b, t, h, pair)
     A       = -exp(U(0, ln 16))         per head, kept in fp32
+and for the block prologue/epilogue (``block_inputs``):
+    B/C weight = 1 + 0.25 N(0, 1),  B/C bias = 0.5 N(0, 1)   per (h, r, n), fp32
+    z       ~ N(0, 1)                   shaped like x
 Every tensor has its own stream: ``numpy.random.default_rng([seed, cfg, id])``
 (with the decode step appended for per-step decode inputs).  bf16 values are
 obtained from the fp32 draw by round-to-nearest-even; dt and lam are computed
@@ -42,7 +45,8 @@ CONFIGS = {
             batch=256, T=1000, H=64, P=64, N=64, R=4, io="bf16"),
 }
 
-TENSOR_IDS = dict(x=1, dt=2, A=3, lam=4, theta=5, B=6, C=7, h0=8)
+TENSOR_IDS = dict(x=1, dt=2, A=3, lam=4, theta=5, B=6, C=7, h0=8, B_weight=9, B_bias=10,
+                  C_weight=11, C_bias=12, z=13)
 
 
 def to_bf16_bits(a) -> np.ndarray:
@@ -106,6 +110,22 @@ def prefill_inputs(batch, T, H, P, N, R, io="bf16", seed=0, cfg=0, step=None):
     out = dict(x=x, dt=dt, lam=lam, theta=theta, B=B, C=C)
     out = {k: round_io(v, io) for k, v in out.items()}
     out["A"] = head_decay(H, seed, cfg)
+    return out
+
+
+def block_inputs(batch, T, H, P, N, R, io="bf16", seed=0, cfg=0, step=None):
+    """Draw the block prologue/epilogue parameters with numpy: B_weight,
+    B_bias, C_weight, C_bias [H,R,N] fp32 (per layer, so no ``step``) and the
+    gate input z [b,T,H,R,P] rounded to the I/O dtype (T=None drops the token
+    axis, as for one decode step)."""
+    f32 = np.float32
+    out = {}
+    for name, (mean, std) in (("B_weight", (1.0, 0.25)), ("B_bias", (0.0, 0.5)),
+                              ("C_weight", (1.0, 0.25)), ("C_bias", (0.0, 0.5))):
+        v = _rng(seed, cfg, name).standard_normal((H, R, N), dtype=f32)
+        out[name] = (f32(mean) + f32(std) * v).astype(f32)
+    zshape = (batch, H, R, P) if T is None else (batch, T, H, R, P)
+    out["z"] = round_io(_rng(seed, cfg, "z", step).standard_normal(zshape, dtype=f32), io)
     return out
 
 

@@ -170,3 +170,41 @@ def test_product_path_does_not_import_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text, f
                 assert "m3_oracle" not in text and "libm3oracle" not in text, f
+
+
+def _prefill_block(shape, block, **over):
+    args = dict(x=FAKE, dt=FAKE, A=FAKE, lam=FAKE, theta=FAKE, B=FAKE, C=FAKE, block=block,
+                init=None, final_state=None, y=FAKE, workspace=FAKE, workspace_bytes=0,
+                stream=None)
+    args.update(over)
+    return capi.m3_ssm_prefill_block(shape, **args)
+
+
+def test_block_errors():
+    """Validation of the block prologue/epilogue (include/m3_ssm_block.h).
+    Valid blocks reach the workspace check, which fails (0 bytes given)."""
+    W = capi.M3_ERR_WORKSPACE
+    assert _prefill_block(_shape(), None) == W
+    assert _prefill_block(_shape(), capi.m3_block_t(1, 1e-6, FAKE, FAKE, FAKE, FAKE, FAKE)) == W
+    assert _prefill_block(_shape(), capi.m3_block_t(0, -1.0)) == W          # eps unused
+    for eps in (-1e-6, float("nan"), float("inf")):
+        assert _prefill_block(_shape(), capi.m3_block_t(1, eps)) == capi.M3_ERR_INVALID_ARGUMENT
+    for i in range(5):
+        ptrs = [None] * 5
+        ptrs[i] = FAKE_MISALIGNED
+        assert _prefill_block(_shape(), capi.m3_block_t(0, 0.0, *ptrs)) == capi.M3_ERR_INVALID_ARGUMENT
+    # bf16, N = 128, P = 64, R = 4: the weight table no longer fits in LDS
+    big = _shape(dstate=128, rank=4)
+    assert _prefill_block(big, None) == W
+    assert _prefill_block(big, capi.m3_block_t(1, 1e-6)) == capi.M3_ERR_UNSUPPORTED
+    st = capi.m3_state_t(FAKE, FAKE, FAKE, FAKE)
+
+    def dec(block, **over):
+        args = dict(x=FAKE, dt=FAKE, A=FAKE, lam=FAKE, theta=FAKE, B=FAKE, C=FAKE, block=block,
+                    state=st, y=FAKE, stream=None)
+        args.update(over)
+        return capi.m3_ssm_decode_step_block(_shape(), **args)
+
+    assert dec(capi.m3_block_t(1, -2.0)) == capi.M3_ERR_INVALID_ARGUMENT
+    assert dec(capi.m3_block_t(0, 0.0, None, None, None, None, FAKE_MISALIGNED)) == capi.M3_ERR_INVALID_ARGUMENT
+    assert dec(capi.m3_block_t(1, 1e-6), x=None) == capi.M3_ERR_INVALID_ARGUMENT
