@@ -150,7 +150,9 @@ def record_traffic(fetch_csv, write_csv, copy_mib):
 
 
 # ---------------------------------------------------------------------------
-def time_prefill(torch, mixer, inp, steps, warmup):
+def time_prefill(torch, mixer, inp, steps, warmup, block=None, z=None):
+    """Whole prefill calls back to back; then each kernel alone (plain path).
+    With ``block``/``z`` only the whole calls are timed."""
     x, dt, A, lam, theta, B, C = (inp[k] for k in ("x", "dt", "A", "lam", "theta", "B", "C"))
     b, T, H, R, P = x.shape
     N = B.shape[-1]
@@ -158,18 +160,21 @@ def time_prefill(torch, mixer, inp, steps, warmup):
     ws = torch.empty(mixer.workspace_bytes(b, T, H, P, N, R, x.dtype), device="cuda", dtype=torch.uint8)
     st = mixer.State.zeros(b, H, N, P, R, x.dtype)
     args = (x, dt, A, lam, theta, B, C)
+    kw = dict(final=st, y=y, workspace=ws, block=block, z=z)
     for _ in range(warmup):
-        mixer.prefill(*args, final=st, y=y, workspace=ws)
+        mixer.prefill(*args, **kw)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     e0.record()
     for _ in range(steps):
-        mixer.prefill(*args, final=st, y=y, workspace=ws)
+        mixer.prefill(*args, **kw)
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = e0.elapsed_time(e1) / steps
+    if block is not None or z is not None:
+        return ms, wall, {}
     # each kernel alone on the same stream (after a full prefill filled the
     # workspace): `steps` launches back to back between one event pair (an
     # event pair costs a few microseconds; per-launch pairs would add that to
@@ -193,7 +198,19 @@ def time_prefill(torch, mixer, inp, steps, warmup):
     return ms, wall, per_kernel
 
 
-def time_decode(torch, mixer, synth, b, H, P, N, R, steps, warmup, seed=0):
+def block_params(torch, H, R, N, shape, seed=5):
+    """Block prologue/epilogue parameters of the synthetic distributions
+    (weight 1 + 0.25 N(0,1), bias 0.5 N(0,1), z ~ N(0,1) shaped like x)."""
+    from mamba_selective_ssm_ssd_amd import mixer
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    bw, cw = (1.0 + 0.25 * torch.randn(H, R, N, generator=g, device="cuda") for _ in range(2))
+    bb, cb = (0.5 * torch.randn(H, R, N, generator=g, device="cuda") for _ in range(2))
+    z = torch.randn(shape, generator=g, device="cuda").to(torch.bfloat16)
+    return mixer.Block(bc_norm=True, eps=1e-6, B_weight=bw, B_bias=bb, C_weight=cw, C_bias=cb), z
+
+
+def time_decode(torch, mixer, synth, b, H, P, N, R, steps, warmup, seed=0, with_block=False):
     # per-step inputs, step-major so that every step's slice is contiguous
     inp = synth.torch_inputs(steps + warmup, b, H, P, N, R, io="bf16", seed=seed + 4)
     g = torch.Generator(device="cuda")
@@ -202,10 +219,12 @@ def time_decode(torch, mixer, synth, b, H, P, N, R, steps, warmup, seed=0):
     st.h.copy_(torch.randn(st.h.shape, generator=g, device="cuda") * 0.1)
     y = torch.empty(b, H, R, P, device="cuda", dtype=torch.bfloat16)
     A = inp["A"]
+    block, z = block_params(torch, H, R, N, (steps + warmup, b, H, R, P)) if with_block else (None, None)
 
     def step(t):
         mixer.decode_step(inp["x"][t], inp["dt"][t], A, inp["lam"][t], inp["theta"][t],
-                          inp["B"][t], inp["C"][t], st, y=y)
+                          inp["B"][t], inp["C"][t], st, y=y, block=block,
+                          z=z[t] if z is not None else None)
 
     for t in range(warmup):
         step(steps + t)                  # (clocks up: the prefill ran just before)
@@ -267,6 +286,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-mimo", action="store_true", help="skip the MIMO prefill workload")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode workload")
+    ap.add_argument("--no-block", action="store_true",
+                    help="skip the workloads with the block prologue/epilogue")
     ap.add_argument("--long", action="store_true", help="also run the T=65536 MIMO prefill")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="CPU-seconds of oracle work")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -341,6 +362,19 @@ def main():
         "kernels": kern,
     }
 
+    if not args.no_block:
+        # the same SISO workload with BC norm, B/C weight and bias and the gate
+        blk, z = block_params(torch, H, R, N, inp["x"].shape)
+        msb, _, _ = time_prefill(torch, mixer, inp, args.steps, args.warmup, block=blk, z=z)
+        zb = b * T * H * R * P * 2
+        result["block_siso_prefill"] = {
+            "workload": c1["name"] + "+bcnorm_bias_gate", "tokens_per_s": round(b * T / (msb / 1000), 1),
+            "ms_per_call": round(msb, 4), "vs_plain": round(ms / msb, 4),
+            "path_min_bytes": path_bytes + zb,
+            "frac_of_hbm_peak_at_min_bytes": round((path_bytes + zb) / (msb / 1000) / 1e9 / HBM_PEAK_GBS, 4)}
+        log(f"[siso prefill + block] {msb * 1000:.1f} us/call")
+        del blk, z
+
     if not args.no_cpu:
         log("[cpu baseline] timing the fp64 oracle on a sample ...")
         result["cpu_baseline"] = cpu_baseline(torch, inp, args.cpu_budget)
@@ -355,6 +389,11 @@ def main():
         b2, T2, H2, P2, N2, R2 = (c2[k] for k in ("batch", "T", "H", "P", "N", "R"))
         inp = synth.torch_inputs(b2, T2, H2, P2, N2, R2, io="bf16", seed=0)
         ms2, _, pk2 = time_prefill(torch, mixer, inp, args.steps, args.warmup)
+        ms2b = None
+        if not args.no_block:
+            blk, z = block_params(torch, H2, R2, N2, inp["x"].shape)
+            ms2b, _, _ = time_prefill(torch, mixer, inp, args.steps, args.warmup, block=blk, z=z)
+            del blk, z
         del inp
         torch.cuda.empty_cache()
         f2 = output_useful_flops(b2, T2, H2, P2, N2, R2)
@@ -372,6 +411,12 @@ def main():
                 path_min_bytes(b2, T2, H2, P2, N2, R2) / (ms2 / 1000) / 1e9 / HBM_PEAK_GBS, 4),
         }
         log(f"[mimo prefill] {ms2 * 1000:.1f} us/call  {b2 * T2 / (ms2 / 1000):.3e} tokens/s")
+        if ms2b is not None:
+            result["block_mimo_prefill"] = {
+                "workload": c2["name"] + "+bcnorm_bias_gate",
+                "tokens_per_s": round(b2 * T2 / (ms2b / 1000), 1), "ms_per_call": round(ms2b, 4),
+                "vs_plain": round(ms2 / ms2b, 4)}
+            log(f"[mimo prefill + block] {ms2b * 1000:.1f} us/call")
 
     if args.long:
         c3 = synth.CONFIGS[3]
@@ -400,6 +445,15 @@ def main():
                          "traffic": load_traffic("decode_step", c4["name"]),
                          "alg_bytes_per_step": db}}
         log(f"[mimo decode] {us:.1f} us/step  {ach:.0f} GB/s")
+        if not args.no_block:
+            usb = time_decode(torch, mixer, synth, b4, H4, P4, N4, R4, args.decode_steps, 10,
+                              with_block=True)
+            dbb = db + b4 * H4 * R4 * P4 * 2         # + the gate input z
+            result["block_decode"] = {
+                "workload": c4["name"] + "+bcnorm_bias_gate", "us_per_step": round(usb, 2),
+                "vs_plain": round(us / usb, 4), "alg_bytes_per_step": dbb,
+                "frac_of_hbm_peak": round(dbb / (usb * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+            log(f"[mimo decode + block] {usb:.1f} us/step")
 
     print(json.dumps(result), flush=True)
 

@@ -309,7 +309,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode
                     float zv[4];
                     io4<IO>::unpack(zr, zv);
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) sv[q] *= zv[q] / (1.f + __expf(-zv[q]));
+                    for (int q = 0; q < 4; ++q) sv[q] *= silu(zv[q]);
                 }
             }
             io<IO>::store4(y + o, sv);

@@ -63,9 +63,14 @@ constexpr size_t align16(size_t v) { return (v + 15) / 16 * 16; }
 // (narrow layout) by 8 elements only.
 constexpr int lds_pitch(int n, bool wide) { return wide ? (n + 31) / 32 * 32 + 16 : n + 8; }
 
-template <typename IO, int N_, int P_, int R_, bool WIDE, bool BLK>
+template <typename IO, int N_, int P_, int R_, bool WIDE, bool BLK, bool BPAD = false>
 struct CfgW {
     static constexpr int N = N_, P = P_, R = R_, K = N / 2, V = kQ * R;
+    static constexpr bool kWide = WIDE;
+    // (BLK) the block prologue's weight/bias table [4][R][N] floats sits in
+    // its own region, or (BPAD) one float4 per staged-B row in that row's
+    // padding columns (never read or written by the staging and the products)
+    static constexpr bool kBpad = BPAD;
     static constexpr int PL = mode<IO>::f32 ? 2 : 1;          // bf16 planes per staged value
     typedef Mma<PL> M;
     typedef typename M::frag frag;
@@ -115,7 +120,7 @@ struct CfgW {
     static constexpr int LWP = WIDE ? kQ + 8 : kQ + 4;                         // row pitch (floats)
     // block prologue tables (BLK): B weight, B bias, C weight, C bias [R][N]
     static constexpr size_t o_blk = align16(o_ths + size_t(K) * 8);
-    static constexpr size_t blk_bytes = BLK ? 16 * size_t(R) * N : 0;
+    static constexpr size_t blk_bytes = BLK && !BPAD ? 16 * size_t(R) * N : 0;
     static constexpr size_t o_lw = align16(o_blk + blk_bytes);                 // float [64][LWP]
     static constexpr size_t lw_bytes = size_t(kQ) * LWP * 4 + kQ * 4;          // + e^{ell} [64]
     static constexpr bool LWT = o_lw + lw_bytes <= kMaxLdsBytes;
@@ -145,6 +150,7 @@ struct CfgW {
     static constexpr size_t bytes = o_cl + (CL ? cl_bytes : 0);
     static_assert(K * SZ % 16 == 0 && N % 16 == 0 && P % 16 == 0 && K % 8 == 0, "tile sizes");
     static_assert(FREEW ? NG8 <= FREEW * GPW : NG8 <= kPW, "angle groups per wave");
+    static_assert(!BPAD || (BLK && V >= R * N && (NBP - N) * 2 >= 16), "block table in the B row padding");
 };
 
 // The wide (conflict-free) layout when it fits with every optional table the
@@ -157,8 +163,32 @@ struct CfgPick {
                                  Wd::XS == Nw::XS && Wd::CL == Nw::CL;
     typedef typename std::conditional<wide, Wd, Nw>::type type;
 };
+// With the block prologue the layout is the plain one whenever the table fits
+// in the staged-B row padding (N <= 64: one 16-byte slot per row), so the
+// block variant keeps every optional table of the plain kernel.
+template <typename IO, int N, int P, int R, bool BLK>
+struct CfgSel {
+    typedef typename CfgPick<IO, N, P, R, false>::type Plain;
+    static constexpr bool pad = BLK && N <= kQ;
+    typedef typename std::conditional<pad, CfgW<IO, N, P, R, Plain::kWide, true, true>,
+                                      typename CfgPick<IO, N, P, R, BLK>::type>::type type;
+};
 template <typename IO, int N, int P, int R, bool BLK = false>
-using Cfg = typename CfgPick<IO, N, P, R, BLK>::type;
+using Cfg = typename CfgSel<IO, N, P, R, BLK>::type;
+
+// (BLK) entries of the block table at float offset o (a multiple of 4 for
+// the float4 read)
+template <class C>
+__device__ __forceinline__ const float *blk_row(const unsigned char *smem, int o) {
+    if constexpr (C::kBpad)
+        return reinterpret_cast<const float *>(smem + C::o_bs + size_t(o >> 2) * (C::NBP * 2) + C::N * 2) + (o & 3);
+    else
+        return reinterpret_cast<const float *>(smem + C::o_blk) + o;
+}
+template <class C>
+__device__ __forceinline__ float4 blk_tbl4(const unsigned char *smem, int o) {
+    return *reinterpret_cast<const float4 *>(blk_row<C>(smem, o));
+}
 
 // Raw (undecoded) B, x and C of one chunk held in registers.
 template <class C>
@@ -209,6 +239,24 @@ __device__ __forceinline__ void unpack_unit(const uint4 &u, float *v, bf16) {
 __device__ __forceinline__ void unpack_unit(const uint4 &u, float *v, float) {
     v[0] = __uint_as_float(u.x); v[1] = __uint_as_float(u.y);
     v[2] = __uint_as_float(u.z); v[3] = __uint_as_float(u.w);
+}
+// Sum of squares of a 16-byte unit's elements, read from the raw bits (bf16:
+// one v_dot2 per pair, so no unpacked copy of the unit is kept for it).
+__device__ __forceinline__ float unit_sumsq(const uint4 &u, bf16) {
+    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+    float s = 0.f;
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const bf2 v = __builtin_bit_cast(bf2, w[i]);
+        s = __builtin_amdgcn_fdot2_f32_bf16(v, v, s, false);
+    }
+    return s;
+}
+__device__ __forceinline__ float unit_sumsq(const uint4 &u, float) {
+    const float a = __uint_as_float(u.x), b = __uint_as_float(u.y);
+    const float c = __uint_as_float(u.z), d = __uint_as_float(u.w);
+    return a * a + b * b + c * c + d * d;
 }
 
 // Virtual-row block i (< TBW) of a wave: blocks w and 2*kPW-1-w, so that the
@@ -500,14 +548,15 @@ __device__ __forceinline__ void run_coef(const RawPro<C> &r, int Tc, int64_t t0,
 
 // Block prologue (Mamba-3 review, section 3.4: BC normalisation, B/C biases)
 // on NV consecutive channels of one B or C row: e <- e * inv * w + bias, with
-// w, bias the row's [N] weight and bias at those channels (LDS) and inv the
-// row's 1 / sqrt(mean_n e^2 + eps) (1 without the normalisation).
-template <int NV>
-__device__ __forceinline__ void block_unit(float *e, float inv, const float *w, const float *bias) {
+// w, bias the row's [N] weight and bias at those channels (block table
+// offsets ow, ob) and inv the row's 1 / sqrt(mean_n e^2 + eps) (1 without
+// the normalisation).
+template <class C, int NV>
+__device__ __forceinline__ void block_unit(float *e, float inv, const unsigned char *smem, int ow, int ob) {
 #pragma unroll
     for (int i = 0; i < NV; i += 4) {
-        const float4 a = *reinterpret_cast<const float4 *>(w + i);
-        const float4 c = *reinterpret_cast<const float4 *>(bias + i);
+        const float4 a = blk_tbl4<C>(smem, ow + i);
+        const float4 c = blk_tbl4<C>(smem, ob + i);
         e[i] = e[i] * inv * a.x + c.x;
         e[i + 1] = e[i + 1] * inv * a.y + c.y;
         e[i + 2] = e[i + 2] * inv * a.z + c.z;
@@ -584,7 +633,6 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
     double *ths_s = reinterpret_cast<double *>(smem + C::o_ths);   // [K]
     float *lw_s = reinterpret_cast<float *>(smem + C::o_lw);       // [64][LWP] mask, then e^{ell} [64]
     uint16_t *tht = reinterpret_cast<uint16_t *>(smem + C::o_th);  // theta rows of the next chunk
-    float *blk_s = reinterpret_cast<float *>(smem + C::o_blk);     // (BLK) [4][R][N] B w, B b, C w, C b
 
     // running angle: Phi_{-1} plus the segments before this one (output pass)
     for (int k = tid; k < K; k += kPT) {
@@ -613,11 +661,13 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
     if constexpr (BLK) {
         // this head's block prologue weights and biases (1 and 0 when absent)
         const int64_t hb0 = int64_t(h) * R * N;
-        for (int i = tid; i < R * N; i += kPT) {
-            blk_s[i] = p.blk.bw ? p.blk.bw[hb0 + i] : 1.f;
-            blk_s[R * N + i] = p.blk.bb ? p.blk.bb[hb0 + i] : 0.f;
-            blk_s[2 * R * N + i] = p.blk.cw ? p.blk.cw[hb0 + i] : 1.f;
-            blk_s[3 * R * N + i] = p.blk.cb ? p.blk.cb[hb0 + i] : 0.f;
+        constexpr int F4 = R * N / 4; // float4 entries per array
+        for (int f = tid; f < 4 * F4; f += kPT) {
+            const int a = f / F4, i = 4 * (f - a * F4);
+            const float *src = a == 0 ? p.blk.bw : a == 1 ? p.blk.bb : a == 2 ? p.blk.cw : p.blk.cb;
+            const float dflt = (a & 1) ? 0.f : 1.f;
+            const float4 v = src ? *reinterpret_cast<const float4 *>(src + hb0 + i) : make_float4(dflt, dflt, dflt, dflt);
+            *reinterpret_cast<float4 *>(const_cast<float *>(blk_row<C>(smem, 4 * f))) = v;
         }
     }
     __syncthreads(); // ths_s, theta table, block tables
@@ -732,9 +782,9 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
                             invc = rsqrtf(sc * (1.f / N) + p.blk.eps);
                         }
                     }
-                    const float *wr = blk_s + r * N + q * EPU;
-                    block_unit<EPU>(e, inv, wr, wr + R * N);
-                    if constexpr (OUT && C::CL) block_unit<EPU>(ec, invc, wr + 2 * R * N, wr + 3 * R * N);
+                    const int wo = r * N + q * EPU;
+                    block_unit<C, EPU>(e, inv, smem, wo, wo + R * N);
+                    if constexpr (OUT && C::CL) block_unit<C, EPU>(ec, invc, smem, wo + 2 * R * N, wo + 3 * R * N);
                 }
 #pragma unroll
                 for (int w4 = 0; w4 < EPU / 4; ++w4) {
@@ -790,11 +840,9 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
                         float ss = 0.f;
 #pragma unroll
                         for (int ks = 0; ks < NKS; ++ks) {
-                            float e[8], sk = 0.f;
+                            float sk = 0.f;
 #pragma unroll
-                            for (int f = 0; f < C::FU; ++f) unpack_unit(raw.cc[i][ks][f], e + f * EPU, IO());
-#pragma unroll
-                            for (int jj = 0; jj < 8; ++jj) sk += e[jj] * e[jj];
+                            for (int f = 0; f < C::FU; ++f) sk += unit_sumsq(raw.cc[i][ks][f], IO());
                             ss += (N % 32 == 0 || 32 * ks + 8 * g < N) ? sk : 0.f;
                         }
                         ss += __shfl_xor(ss, 16);
@@ -809,8 +857,8 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
 #pragma unroll
                     for (int f = 0; f < C::FU; ++f) unpack_unit(raw.cc[i][ks][f], e + f * EPU, IO());
                     if constexpr (BLK) {
-                        const float *wr = blk_s + 2 * R * N + ((16 * tb + l16) % R) * N + min(n0, N - 8);
-                        block_unit<8>(e, inv, wr, wr + R * N);
+                        const int wo = 2 * R * N + ((16 * tb + l16) % R) * N + min(n0, N - 8);
+                        block_unit<C, 8>(e, inv, smem, wo, wo + R * N);
                     }
                     if (N % 32 == 0 || n0 < N) {
                         const float4 *cr = reinterpret_cast<const float4 *>(cs_s + tok * C::CSP + n0);
@@ -821,7 +869,18 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
                             rot_neg(a.z, a.w, e[4 * w4 + 2], e[4 * w4 + 3]);
                         }
                     }
-                    cf[i][ks] = M::pack(e);
+                    frag cv = M::pack(e);
+                    // (BLK) one fragment at a time, computed here (not next to
+                    // its first use): bounds the table reads in flight
+                    if constexpr (BLK) {
+#pragma unroll
+                        for (int k = 0; k < PL; ++k) {
+                            u32x4_v t = __builtin_bit_cast(u32x4_v, cv.v[k]);
+                            __asm__ volatile("" : "+v"(t));
+                            cv.v[k] = __builtin_bit_cast(bf16x8, t);
+                        }
+                    }
+                    cf[i][ks] = cv;
                 }
             }
         }
@@ -1085,7 +1144,7 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
                                     float zv[4];
                                     io4<IO>::unpack(zr[pt], zv);
 #pragma unroll
-                                    for (int q = 0; q < 4; ++q) o4[q] *= zv[q] / (1.f + __expf(-zv[q]));
+                                    for (int q = 0; q < 4; ++q) o4[q] *= silu(zv[q]);
                                 }
                             }
                             io<IO>::store4(dst + 16 * pt, o4);
@@ -1222,9 +1281,9 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
                 }
                 inv = rsqrtf(ss * (1.f / N) + p.blk.eps);
             }
-            const float *wr = blk_s + r * N + 2 * k;
-            u = u * inv * wr[0] + wr[R * N];
-            v = v * inv * wr[1] + wr[R * N + 1];
+            const float *wr = blk_row<C>(smem, r * N + 2 * k), *br = blk_row<C>(smem, R * N + r * N + 2 * k);
+            u = u * inv * wr[0] + br[0];
+            v = v * inv * wr[1] + br[1];
         }
         rot_neg(cs, sn, u, v);
         p.prevBT[(bh * R + r) * N + 2 * k] = u;

@@ -382,13 +382,27 @@ __device__ __forceinline__ void sincos_wrapped(double x, float *s_out, float *c_
 }
 
 // Sum of v over the W consecutive lanes that hold one row (W a power of two
-// dividing 64, every lane of the row active).
+// dividing 64, every lane of the row active).  Within a 16-lane DPP row the
+// partial sums are exchanged with DPP moves (quad permutations, then the
+// half-row and row mirrors), across rows with lane shuffles.
+template <int C>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), C, 0xf, 0xf, false));
+}
 template <int W>
 __device__ __forceinline__ float row_sum(float v) {
+    if constexpr (W >= 2) v += dpp_f32<0xb1>(v);  // quad_perm [1, 0, 3, 2]
+    if constexpr (W >= 4) v += dpp_f32<0x4e>(v);  // quad_perm [2, 3, 0, 1]
+    if constexpr (W >= 8) v += dpp_f32<0x141>(v); // row_half_mirror
+    if constexpr (W >= 16) v += dpp_f32<0x140>(v); // row_mirror
 #pragma unroll
-    for (int m = 1; m < W; m <<= 1) v += __shfl_xor(v, m);
+    for (int m = 16; m < W; m <<= 1) v += __shfl_xor(v, m);
     return v;
 }
+
+// Output gate factor silu(z) = z / (1 + e^{-z}) (hardware reciprocal; for
+// z -> -inf the exponential overflows to inf and the factor to -0).
+__device__ __forceinline__ float silu(float z) { return z * __builtin_amdgcn_rcpf(1.f + __expf(-z)); }
 
 // Rotation R(-phi) of a row pair: (u, v) -> (c u + s v, -s u + c v).
 __device__ __forceinline__ void rot_neg(float c, float s, float &u, float &v) {
