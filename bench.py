@@ -117,7 +117,7 @@ def record_traffic(fetch_csv, write_csv, copy_mib):
     import csv
     from mamba_selective_ssm_ssd_amd import synth
     c1 = synth.CONFIGS[1]
-    tag = f"k_prefill<m3::bf16, {c1['N']}, {c1['P']}, {c1['R']}, true>"
+    tag = f"k_prefill<m3::bf16, {c1['N']}, {c1['P']}, {c1['R']}, true, false>"
 
     def avg(path, counter):
         kern, copy = [], []
