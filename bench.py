@@ -181,6 +181,9 @@ def time_prefill(torch, mixer, inp, steps, warmup, block=None, z=None):
     # every launch), right after the timed calls, so at the same clocks
     per_kernel = {}
     for name in KERNELS:
+        if name == "segment_state" and segments(b, H, T)[0] == 1:
+            per_kernel[name] = 0.0       # one segment per sequence: no pre-pass launch
+            continue
         stage = mixer.capi.STAGES[name]
         reps = max(steps, 10)
         for _ in range(3):
