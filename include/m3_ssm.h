@@ -27,10 +27,14 @@
  * aligned.  Sizes: b = batch, T = seqlen, H = nheads, P = headdim,
  * N = dstate (even), R = rank, K = N / 2 rotation pairs.
  *     x, y          [b][T][H][R][P]    I/O dtype
- *     B, C          [b][T][H][R][N]    I/O dtype   (B[..][r][n] is B_t[n, r])
+ *     B, C          [b][T][G][R][N]    I/O dtype   (B[..][r][n] is B_t[n, r])
  *     dt, lam       [b][T][H]          I/O dtype
  *     theta         [b][T][H][K]       I/O dtype   (angle of pair k, radians)
  *     A             [H]                float32     (one decay rate per head)
+ * G = ngroups divides H (0 means G = H): head h reads the B and C of group
+ * h / (H / G), as the shared B, C projection of the MIMO instantiation in the
+ * Mamba-3 review (section 3.3) suggests; every head keeps its own dt, lam,
+ * theta, A, x and state, so a group's B and C still rotate per head.
  * The per-step rotation angle is theta_t itself; a caller that wants
  * dt_t * theta_t passes the product.  Decode calls drop the T axis.
  *
@@ -85,7 +89,8 @@ typedef enum {
  * m3_dtype_t value.  A prefill workgroup keeps one chunk's operands in the
  * 160 KB of LDS of a gfx950 compute unit; (N, P, R) combinations that do not
  * fit (with fp32 I/O: N = 128 with R >= 2, N = 64 with R = 4) are reported as
- * M3_ERR_UNSUPPORTED by the prefill entry points (and a zero workspace size). */
+ * M3_ERR_UNSUPPORTED by the prefill entry points (and a zero workspace size).
+ * ngroups < 0 or not dividing nheads is M3_ERR_INVALID_ARGUMENT. */
 typedef struct {
     int64_t batch;
     int64_t seqlen;   /* T; ignored by m3_ssm_decode_step */
@@ -95,6 +100,7 @@ typedef struct {
     int32_t rank;     /* R, 1 = SISO */
     int32_t chunk;    /* Q, must be 64 */
     int32_t io_dtype; /* m3_dtype_t */
+    int32_t ngroups;  /* G: B and C shared by groups of H/G consecutive heads; 0 = H */
 } m3_shape_t;
 
 /* Carried state of one batch of sequences (caller-owned device buffers). */
@@ -132,7 +138,7 @@ m3_status_t m3_ssm_prefill(const m3_shape_t *shape, const void *x, const void *d
 /*
  * One decode step: consumes token t for every (batch, head), updating the
  * carried state in place, and writes y_t.  Inputs drop the T axis:
- * x [b][H][R][P], dt/lam [b][H], theta [b][H][K], B/C [b][H][R][N].
+ * x [b][H][R][P], dt/lam [b][H], theta [b][H][K], B/C [b][G][R][N].
  * Equivalent to m3_ssm_prefill with seqlen = 1, init = final_state = state.
  * shape->seqlen is ignored; state must not be NULL.
  */

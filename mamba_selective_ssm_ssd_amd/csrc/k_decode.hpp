@@ -149,7 +149,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode
         for (int j = 0; j < SPT; ++j) hv[j] = hs[j * kThreads + tslot];
     };
 
-    auto step = [&](const int64_t item, const int h, const float4 *hc, float4 *hx) {
+    // item = (batch, head); gitem = (batch, B/C group of the head)
+    auto step = [&](const int64_t item, const int64_t gitem, const int h, const float4 *hc, float4 *hx) {
         // ---- issue: small vectors of this item, then the next item's state
         uint4 ud[UPT];
         uint2 ut[UPT];
@@ -157,7 +158,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode
 #pragma unroll
         for (int j = 0; j < UPT; ++j) {
             const int64_t st = ukind[j] == kUnitBp ? sBp : (ukind[j] == kUnitX || ukind[j] == kUnitXp) ? sX : sB;
-            ud[j] = *reinterpret_cast<const uint4 *>(ubase[j] + item * st);
+            // B, C units (and threads without a unit, which read B's first
+            // unit) are rows of the item's B/C group
+            const bool grp = ukind[j] <= kUnitC || ukind[j] == kUnitNone;
+            ud[j] = *reinterpret_cast<const uint4 *>(ubase[j] + (grp ? gitem : item) * st);
             ut[j] = *reinterpret_cast<const uint2 *>(static_cast<const IO *>(p.theta) + item * K + uk0[j]);
             if constexpr (NPU == 4) {
                 const float4 a = *reinterpret_cast<const float4 *>(p.phi + item * K + uk0[j]);
@@ -319,20 +323,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode
     // Two items per trip, the state registers swapping roles, so the
     // prefetched state is never copied (a copy would wait for it).
     float4 ha[SPT], hb[SPT];
-    int64_t item = blockIdx.x; // the grid never exceeds the item count
-    int h = int(item % p.H);   // head of the item, advanced without a division
+    int64_t item = blockIdx.x;       // the grid never exceeds the item count
+    int h = int(item % p.H);         // head and batch of the item, advanced
+    int64_t bi = item / p.H;         // without a division
     const int hstep = int(gridDim.x % unsigned(p.H));
+    const int64_t bstep = gridDim.x / unsigned(p.H);
     auto advance = [&]() {
         item += gridDim.x;
         h += hstep;
-        if (h >= p.H) h -= p.H;
+        bi += bstep;
+        if (h >= p.H) h -= p.H, ++bi;
     };
+    auto gitem = [&]() { return bi * p.G + h / p.hpg; };
     load_state(item, ha);
     for (;;) {
-        step(item, h, ha, hb);
+        step(item, gitem(), h, ha, hb);
         advance();
         if (item >= BH) break;
-        step(item, h, hb, ha);
+        step(item, gitem(), h, hb, ha);
         advance();
         if (item >= BH) break;
     }

@@ -282,22 +282,23 @@ __device__ __forceinline__ void static_for(F &&f) {
 // PARTS selects what is loaded: bit 0 B, bit 1 x, bit 2 C; J >= 0 loads only
 // unit J of B, x and the spread C units.
 template <class C, typename IO, bool OUT, int PARTS = 7, int J = -1>
-__device__ __forceinline__ void load_chunk(const PrefillParams &p, int64_t b, int h, int64_t t0, int Tc,
+__device__ __forceinline__ void load_chunk(const PrefillParams &p, int64_t b, int h, int hg, int64_t t0, int Tc,
                                            RawChunk<C> &r) {
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const int g = lane >> 4, l16 = lane & 15;
-    const int64_t tokbase = (b * p.T + t0) * p.H + h; // token-head index of t0
-    const int H = p.H;
-    const IO *Bp = static_cast<const IO *>(p.B) + tokbase * (C::R * C::N);
+    const int64_t tokbase = (b * p.T + t0) * p.H + h;  // token-head index of t0
+    const int64_t tokgrp = (b * p.T + t0) * p.G + hg;  // token-group index of t0 (B, C)
+    const int H = p.H, G = p.G;
+    const IO *Bp = static_cast<const IO *>(p.B) + tokgrp * (C::R * C::N);
     const IO *Xp = static_cast<const IO *>(p.x) + tokbase * (C::R * C::P);
-    const IO *Cp = static_cast<const IO *>(p.C) + tokbase * (C::R * C::N);
+    const IO *Cp = static_cast<const IO *>(p.C) + tokgrp * (C::R * C::N);
 #pragma unroll
     for (int j = 0; j < ((PARTS & 1) ? C::UPT_B : 0); ++j) {
         if (J >= 0 && j != J) continue;
         const int u = min(tid + j * kPT, C::UB - 1);
         const int v = u / C::URB, q = u - v * C::URB;
         const int tok = min(v / C::R, Tc - 1), ch = v % C::R;
-        r.bb[j] = ld16(Bp + ((tok * H * C::R + ch) * C::N + q * C::EPU));
+        r.bb[j] = ld16(Bp + ((tok * G * C::R + ch) * C::N + q * C::EPU));
     }
 #pragma unroll
     for (int j = 0; j < ((PARTS & 2) ? C::UPT_X : 0); ++j) {
@@ -314,7 +315,7 @@ __device__ __forceinline__ void load_chunk(const PrefillParams &p, int64_t b, in
             const int u = min(tid + j * kPT, C::UB - 1);
             const int v = u / C::URB, q = u - v * C::URB;
             const int tok = min(v / C::R, Tc - 1), ch = v % C::R;
-            r.cu[j] = ld16(Cp + ((tok * H * C::R + ch) * C::N + q * C::EPU));
+            r.cu[j] = ld16(Cp + ((tok * G * C::R + ch) * C::N + q * C::EPU));
         }
     } else if (OUT && (PARTS & 4)) {
 #pragma unroll
@@ -328,7 +329,7 @@ __device__ __forceinline__ void load_chunk(const PrefillParams &p, int64_t b, in
                 const int n0 = min(32 * ks + 8 * g, C::N - 8);
 #pragma unroll
                 for (int f = 0; f < C::FU; ++f)
-                    r.cc[i][ks][f] = ld16(Cp + ((tok * H * C::R + ch) * C::N + n0 + f * C::EPU));
+                    r.cc[i][ks][f] = ld16(Cp + ((tok * G * C::R + ch) * C::N + n0 + f * C::EPU));
             }
         }
     }
@@ -616,6 +617,7 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
     const int seg = int(li % nseg);
     const int64_t bh = li / nseg;
     const int h = int(bh % p.H);
+    const int hg = h / p.hpg; // B/C group of the head
     const int64_t b = bh / p.H;
     const int c_begin = seg * p.cps;
     const int c_end = min(p.nC, c_begin + p.cps);
@@ -655,7 +657,7 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
     load_pro<C, IO>(p, b, h, int64_t(c_begin) * kQ, tc_of(c_begin), rp);
     load_theta<C, IO>(p, b, h, int64_t(c_begin) * kQ, tc_of(c_begin), rp);
     RawChunk<C> raw;
-    load_chunk<C, IO, OUT>(p, b, h, int64_t(c_begin) * kQ, tc_of(c_begin), raw);
+    load_chunk<C, IO, OUT>(p, b, h, hg, int64_t(c_begin) * kQ, tc_of(c_begin), raw);
     write_theta<C>(rp, tht);
     run_coef<C, IO>(rp, tc_of(c_begin), int64_t(c_begin) * kQ, p.T, Ah, coef_s, misc_s);
     if constexpr (BLK) {
@@ -761,7 +763,7 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
                 // is loaded into them (kept after the unpack, so the loop needs
                 // no register copies)
                 __builtin_amdgcn_sched_barrier(0);
-                load_chunk<C, IO, OUT, 1 | CPART, j>(p, b, h, tn0, Tn, raw);
+                load_chunk<C, IO, OUT, 1 | CPART, j>(p, b, h, hg, tn0, Tn, raw);
                 if constexpr (BLK) {
                     // block prologue of the row's channels q*EPU..: the row is
                     // held by URB consecutive lanes
@@ -799,7 +801,7 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
                 st_planes<PL, C::BS_PS, EPU>(bs + v * NBP + q * EPU, e);
                 if constexpr (OUT && C::CL) st_planes<PL, C::BS_PS, EPU>(cl + v * NBP + q * EPU, ec);
             } else {
-                load_chunk<C, IO, OUT, 1 | CPART, j>(p, b, h, tn0, Tn, raw);
+                load_chunk<C, IO, OUT, 1 | CPART, j>(p, b, h, hg, tn0, Tn, raw);
             }
         });
         static_for<0, C::UPT_X>([&](auto jc) {
@@ -814,7 +816,7 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
                 else
                     st_planes<PL, C::X_PS, EPU>(xr + v * PP + q * EPU, e);
                 __builtin_amdgcn_sched_barrier(0);
-                load_chunk<C, IO, OUT, 2, j>(p, b, h, tn0, Tn, raw);
+                load_chunk<C, IO, OUT, 2, j>(p, b, h, hg, tn0, Tn, raw);
                 if constexpr (C::XS) {
                     const float sc = scl_s[v / R];
 #pragma unroll
@@ -822,7 +824,7 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
                     st_planes<PL, C::X_PS, EPU>(xs + v * PP + q * EPU, e);
                 }
             } else {
-                load_chunk<C, IO, OUT, 2, j>(p, b, h, tn0, Tn, raw);
+                load_chunk<C, IO, OUT, 2, j>(p, b, h, hg, tn0, Tn, raw);
             }
         });
         frag cf[C::TBW][NKS];
@@ -896,7 +898,7 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
         }
         if (OUT && !C::CL) {
             __builtin_amdgcn_sched_barrier(0); // after the C fragments are unpacked
-            load_chunk<C, IO, OUT, 4>(p, b, h, tn0, Tn, raw);
+            load_chunk<C, IO, OUT, 4>(p, b, h, hg, tn0, Tn, raw);
         }
         if constexpr (C::MFP) {
             load_theta<C, IO>(p, b, h, int64_t(cn2) * kQ, tc_of(cn2), rp);
@@ -1260,13 +1262,14 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
             hT[(16 * nt + 4 * g + 2 * q + 1) * P + 16 * pt + l16] = v;
         }
     }
-    const int64_t tl = (b * p.T + p.T - 1) * p.H + h; // token-head index of T-1
+    const int64_t tl = (b * p.T + p.T - 1) * p.H + h;   // token-head index of T-1 (x)
+    const int64_t tlg = (b * p.T + p.T - 1) * p.G + hg; // token-group index of T-1 (B)
     for (int k = tid; k < K; k += kPT) p.phiT[bh * K + k] = float(wrap_angle(ths_s[k]));
     for (int i = tid; i < R * K; i += kPT) {
         const int r = i / K, k = i - r * K;
         float sn, cs;
         sincos_wrapped(wrap_angle(ths_s[k]), &sn, &cs);
-        const IO *Bl = static_cast<const IO *>(p.B) + (tl * R + r) * N + 2 * k;
+        const IO *Bl = static_cast<const IO *>(p.B) + (tlg * R + r) * N + 2 * k;
         float u = io<IO>::get(Bl), v = io<IO>::get(Bl + 1);
         if constexpr (BLK) {
             // block prologue of the last token's B row r (its RMS over N

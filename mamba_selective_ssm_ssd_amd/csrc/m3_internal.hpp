@@ -23,6 +23,7 @@ struct BlockParams {
 struct PrefillParams {
     int64_t batch, T;
     int32_t H, P, N, R, K, nC; // K = N/2 rotation pairs, nC = ceil(T/64) chunks
+    int32_t G, hpg;            // B/C groups, heads per group (head h reads group h / hpg)
     int32_t S, cps;            // segments per sequence, chunks per segment
     // inputs (I/O dtype unless noted)
     const void *x, *dt, *lam, *theta, *B, *C;
@@ -49,6 +50,7 @@ struct PrefillParams {
 struct DecodeParams {
     int64_t batch;
     int32_t H, P, N, R, K;
+    int32_t G, hpg; // B/C groups, heads per group
     const void *x, *dt, *lam, *theta, *B, *C;
     const float *A;
     void *y;

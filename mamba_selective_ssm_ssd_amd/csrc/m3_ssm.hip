@@ -36,6 +36,7 @@ m3_status_t check_shape(const m3_shape_t *s, bool decode) {
     if (!decode && s->seqlen < 1) return M3_ERR_INVALID_ARGUMENT;
     if (s->dstate % 2 != 0) return M3_ERR_INVALID_ARGUMENT;
     if (s->chunk < 1) return M3_ERR_INVALID_ARGUMENT;
+    if (s->ngroups < 0 || (s->ngroups > 0 && s->nheads % s->ngroups != 0)) return M3_ERR_INVALID_ARGUMENT;
     if (s->chunk != 64) return M3_ERR_UNSUPPORTED;
     if (!m3::supported_N(s->dstate) || !m3::supported_P(s->headdim) || s->rank > 4)
         return M3_ERR_UNSUPPORTED;
@@ -197,6 +198,8 @@ static m3_status_t prepare_prefill(const m3_shape_t *shape, const void *x, const
     p.N = shape->dstate;
     p.R = shape->rank;
     p.K = p.N / 2;
+    p.G = shape->ngroups ? shape->ngroups : shape->nheads;
+    p.hpg = p.H / p.G;
     p.nC = int32_t((p.T + 63) / 64);
     p.x = x; p.dt = dt; p.lam = lam; p.theta = theta; p.B = B; p.C = C; p.A = A; p.y = y;
     p.has_init = init != nullptr;
@@ -294,6 +297,8 @@ m3_status_t m3_ssm_decode_step_block(const m3_shape_t *shape, const void *x, con
     p.N = shape->dstate;
     p.R = shape->rank;
     p.K = p.N / 2;
+    p.G = shape->ngroups ? shape->ngroups : shape->nheads;
+    p.hpg = p.H / p.G;
     p.x = x; p.dt = dt; p.lam = lam; p.theta = theta; p.B = B; p.C = C; p.A = A; p.y = y;
     p.h = state->h; p.phi = state->phi; p.prevB = state->prev_B; p.prevx = state->prev_x;
     p.blk = bp;

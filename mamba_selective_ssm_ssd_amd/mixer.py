@@ -3,8 +3,8 @@
 torch is used only to hold device memory and to name the current stream;
 every step of the mixer runs in the HIP kernels of libm3ssm.so.  Tensors must
 be contiguous, on the current HIP device, in the layouts of include/m3_ssm.h:
-    x [b,T,H,R,P], B/C [b,T,H,R,N], dt/lam [b,T,H], theta [b,T,H,N/2] (I/O
-    dtype: float32 or bfloat16), A [H] float32.
+    x [b,T,H,R,P], B/C [b,T,G,R,N] (G divides H; G = H: per head), dt/lam
+    [b,T,H], theta [b,T,H,N/2] (I/O dtype: float32 or bfloat16), A [H] float32.
 With a ``Block`` (and/or a gate input ``z`` shaped like y) the Mamba-3
 block's B/C normalisation, B/C weight and bias and output gate run inside the
 same kernels (include/m3_ssm_block.h).
@@ -85,13 +85,21 @@ def _ptr(t: torch.Tensor, name: str, dtype) -> int:
     return t.data_ptr()
 
 
+def _check_bc(B, C, lead, R, N):
+    """B and C: lead + (G, R, N), the same shape (G checked by the library)."""
+    if tuple(B.shape) != tuple(C.shape) or tuple(B.shape[:len(lead)]) != tuple(lead) \
+            or tuple(B.shape[len(lead) + 1:]) != (R, N):
+        raise ValueError(f"B/C must be {tuple(lead)} + (G, {R}, {N}), got {tuple(B.shape)}, {tuple(C.shape)}")
+
+
 def _stream() -> int:
     return torch.cuda.current_stream().cuda_stream
 
 
-def make_shape(batch, T, H, P, N, R, io_dtype, chunk=64) -> capi.m3_shape_t:
+def make_shape(batch, T, H, P, N, R, io_dtype, chunk=64, G=0) -> capi.m3_shape_t:
+    """G: B/C head groups (0 or H: per head)."""
     return capi.m3_shape_t(int(batch), int(T), int(H), int(P), int(N), int(R), int(chunk),
-                           int(_IO[io_dtype]))
+                           int(_IO[io_dtype]), int(G))
 
 
 def workspace_bytes(batch, T, H, P, N, R, io_dtype=torch.bfloat16) -> int:
@@ -111,7 +119,8 @@ def prefill(x, dt, A, lam, theta, B, C, state: State | None = None, final: State
     b, T, H, R, P = x.shape
     N = B.shape[-1]
     io = x.dtype
-    shape = make_shape(b, T, H, P, N, R, io)
+    _check_bc(B, C, (b, T), R, N)
+    shape = make_shape(b, T, H, P, N, R, io, G=B.shape[2])
     if y is None:
         y = torch.empty_like(x)
     if want_final and final is None:
@@ -151,8 +160,9 @@ def prefill_stage(stage: int, x, dt, A, lam, theta, B, C, state, final, y, works
     b, T, H, R, P = x.shape
     N = B.shape[-1]
     io = x.dtype
+    _check_bc(B, C, (b, T), R, N)
     rc = capi.m3_ssm_prefill_stage(
-        stage, make_shape(b, T, H, P, N, R, io), _ptr(x, "x", io), _ptr(dt, "dt", io),
+        stage, make_shape(b, T, H, P, N, R, io, G=B.shape[2]), _ptr(x, "x", io), _ptr(dt, "dt", io),
         _ptr(A, "A", torch.float32), _ptr(lam, "lam", io), _ptr(theta, "theta", io),
         _ptr(B, "B", io), _ptr(C, "C", io), state.c() if state is not None else None,
         final.c() if final is not None else None, _ptr(y, "y", io), workspace.data_ptr(),
@@ -169,7 +179,8 @@ def decode_step(x, dt, A, lam, theta, B, C, state: State, y=None, block: Block |
     b, H, R, P = x.shape
     N = B.shape[-1]
     io = x.dtype
-    shape = make_shape(b, 1, H, P, N, R, io)
+    _check_bc(B, C, (b,), R, N)
+    shape = make_shape(b, 1, H, P, N, R, io, G=B.shape[1])
     if y is None:
         y = torch.empty_like(x)
     if z is not None and tuple(z.shape) != tuple(x.shape):

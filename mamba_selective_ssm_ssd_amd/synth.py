@@ -91,19 +91,21 @@ def head_decay(H: int, seed: int = 0, cfg: int = 0) -> np.ndarray:
     return (-np.exp(u)).astype(np.float32)
 
 
-def prefill_inputs(batch, T, H, P, N, R, io="bf16", seed=0, cfg=0, step=None):
+def prefill_inputs(batch, T, H, P, N, R, io="bf16", seed=0, cfg=0, step=None, G=None):
     """Draw one batch of mixer inputs with numpy.
 
     Returns a dict of fp32 arrays holding exactly the values the I/O dtype
     stores: x [b,T,H,R,P], dt [b,T,H], lam [b,T,H], theta [b,T,H,N/2],
-    B [b,T,H,R,N], C [b,T,H,R,N]; and A [H] (always fp32).
+    B [b,T,G,R,N], C [b,T,G,R,N] (G = H unless given: B/C head groups); and
+    A [H] (always fp32).
     """
     if N % 2:
         raise ValueError("N must be even")
+    G = H if G is None else G
     f32 = np.float32
     x = _rng(seed, cfg, "x", step).standard_normal((batch, T, H, R, P), dtype=f32)
-    B = _rng(seed, cfg, "B", step).standard_normal((batch, T, H, R, N), dtype=f32)
-    C = _rng(seed, cfg, "C", step).standard_normal((batch, T, H, R, N), dtype=f32)
+    B = _rng(seed, cfg, "B", step).standard_normal((batch, T, G, R, N), dtype=f32)
+    C = _rng(seed, cfg, "C", step).standard_normal((batch, T, G, R, N), dtype=f32)
     dt = _softplus(_rng(seed, cfg, "dt", step).standard_normal((batch, T, H), dtype=f32) - f32(1.0))
     lam = _sigmoid(_rng(seed, cfg, "lam", step).standard_normal((batch, T, H), dtype=f32))
     theta = _rng(seed, cfg, "theta", step).uniform(0.0, math.pi, size=(batch, T, H, N // 2)).astype(f32)
@@ -143,11 +145,13 @@ def config_inputs(cfg: int, seed: int = 0, **override):
                           io=c["io"], seed=seed, cfg=cfg)
 
 
-def torch_inputs(batch, T, H, P, N, R, io="bf16", seed=0, device="cuda"):
+def torch_inputs(batch, T, H, P, N, R, io="bf16", seed=0, device="cuda", G=None):
     """Same distributions drawn on a device with torch (large benchmark buffers).
 
-    Returns device tensors in the I/O dtype (A in fp32).
+    Returns device tensors in the I/O dtype (A in fp32); B/C have G head
+    groups (G = H unless given).
     """
+    G = H if G is None else G
     import torch
 
     g = torch.Generator(device=device)
@@ -159,8 +163,8 @@ def torch_inputs(batch, T, H, P, N, R, io="bf16", seed=0, device="cuda"):
         return torch.randn(shape, generator=g, device=device, dtype=f32)
 
     x = normal((batch, T, H, R, P)).to(dtype)
-    B = normal((batch, T, H, R, N)).to(dtype)
-    C = normal((batch, T, H, R, N)).to(dtype)
+    B = normal((batch, T, G, R, N)).to(dtype)
+    C = normal((batch, T, G, R, N)).to(dtype)
     dt = torch.nn.functional.softplus(normal((batch, T, H)) - 1.0).to(dtype)
     lam = torch.sigmoid(normal((batch, T, H))).to(dtype)
     theta = (torch.rand((batch, T, H, N // 2), generator=g, device=device, dtype=f32)

@@ -73,16 +73,34 @@ def default_threads() -> int:
     return int(_load().m3o_default_threads())
 
 
+def heads_from_groups(V, H: int, axis: int = 2):
+    """B or C shared by head groups -> one copy per head.
+
+    V has G groups on ``axis`` (G divides H); head h reads group h // (H // G),
+    i.e. consecutive heads share a group.  This is the shared B, C projection
+    of the MIMO instantiation (Mamba-3 review, section 3.3) written out: with
+    G = H it returns V unchanged.
+    """
+    V = np.asarray(V)
+    G = V.shape[axis]
+    if H % G:
+        raise ValueError(f"{G} groups do not divide {H} heads")
+    return V if G == H else np.repeat(V, H // G, axis=axis)
+
+
 def run(x, dt, A, lam, theta, B, C, h0=None, prevB0=None, prevx0=None,
         nthreads: int = 0):
     """Run the fp64 recurrence.
 
     Shapes (any float dtype; converted to fp64): x [b,T,H,R,P], dt/lam [b,T,H],
-    A [H], theta [b,T,H,N/2], B/C [b,T,H,R,N]; optional carried state in the
-    state's own frame: h0 [b,H,N,P], prevB0 [b,H,R,N], prevx0 [b,H,R,P].
+    A [H], theta [b,T,H,N/2], B/C [b,T,H,R,N] or [b,T,G,R,N] (shared by head
+    groups, see ``heads_from_groups``); optional carried state in the state's
+    own frame: h0 [b,H,N,P], prevB0 [b,H,R,N], prevx0 [b,H,R,P].
 
     Returns (y [b,T,H,R,P], hT [b,H,N,P] true frame, threads used).
     """
+    H = np.shape(x)[2]
+    B, C = heads_from_groups(B, H), heads_from_groups(C, H)
     x, dt, A, lam, theta, B, C = map(_f64, (x, dt, A, lam, theta, B, C))
     h0, prevB0, prevx0 = map(_f64, (h0, prevB0, prevx0))
     b, T, H, R, P = x.shape
@@ -206,6 +224,8 @@ def run_block(x, dt, A, lam, theta, B, C, block=None, h0=None, prevB0=None,
     (prevB0) is taken as already prologued (it is the previous token's B).
     """
     block = block or {}
+    H = np.shape(x)[2]
+    B, C = heads_from_groups(B, H), heads_from_groups(C, H)
     nrm, eps = bool(block.get("bc_norm", False)), block.get("eps", 1e-6)
     Bp = bc_norm(B, block.get("B_weight"), block.get("B_bias"), eps, nrm)
     Cp = bc_norm(C, block.get("C_weight"), block.get("C_bias"), eps, nrm)

@@ -86,7 +86,7 @@ def check_final_state(st, d, hT_ref, phiT_ref, io, tol):
     e_h = slice_err(h_true, hT_ref, (0, 1))
     dphi = oracle.wrap_angle(g["phi"] - phiT_ref)
     e_phi = float(np.max(np.abs(dphi)))
-    B_last = d["B"][:, -1].astype(np.float64)               # [b,H,R,N]
+    B_last = oracle.heads_from_groups(d["B"][:, -1], d["x"].shape[2], axis=1).astype(np.float64)  # [b,H,R,N]
     e_B = slice_err(oracle.prevB_to_true(g["prev_B"], phiT_ref), B_last, (0, 1))
     x_last = d["x"][:, -1].astype(np.float64)
     assert np.array_equal(g["prev_x"], x_last), "prev_x must be the last token's x, bit for bit"

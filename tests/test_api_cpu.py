@@ -208,3 +208,21 @@ def test_block_errors():
     assert dec(capi.m3_block_t(1, -2.0)) == capi.M3_ERR_INVALID_ARGUMENT
     assert dec(capi.m3_block_t(0, 0.0, None, None, None, None, FAKE_MISALIGNED)) == capi.M3_ERR_INVALID_ARGUMENT
     assert dec(capi.m3_block_t(1, 1e-6), x=None) == capi.M3_ERR_INVALID_ARGUMENT
+
+
+def test_group_errors():
+    """ngroups (B/C shared by head groups) must divide nheads; 0 means per head."""
+    W = capi.M3_ERR_WORKSPACE
+    assert _prefill(_shape(nheads=6, ngroups=0)) == W
+    assert _prefill(_shape(nheads=6, ngroups=3)) == W
+    assert _prefill(_shape(nheads=6, ngroups=1)) == W
+    assert _prefill(_shape(nheads=6, ngroups=6)) == W
+    for g in (-1, 4, 7):
+        assert _prefill(_shape(nheads=6, ngroups=g)) == capi.M3_ERR_INVALID_ARGUMENT
+        assert capi.m3_ssm_prefill_workspace_bytes(_shape(nheads=6, ngroups=g)) == 0
+    st = capi.m3_state_t(FAKE, FAKE, FAKE, FAKE)
+    assert capi.m3_ssm_decode_step(_shape(nheads=6, ngroups=4), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                   FAKE, st, FAKE, None) == capi.M3_ERR_INVALID_ARGUMENT
+    # group count does not change the workspace
+    assert (capi.m3_ssm_prefill_workspace_bytes(_shape(nheads=6, ngroups=2))
+            == capi.m3_ssm_prefill_workspace_bytes(_shape(nheads=6)))

@@ -47,8 +47,8 @@ def _check_state(st, d, bp, blk, hT, phiT, io):
     g = gpu_state(st)
     e_h = slice_err(oracle.state_to_true(g["h"], phiT), hT, (0, 1))
     e_phi = float(np.max(np.abs(oracle.wrap_angle(g["phi"] - phiT))))
-    B_last = oracle.bc_norm(d["B"][:, -1], blk.get("B_weight"), blk.get("B_bias"), EPS,
-                            blk["bc_norm"])
+    B_last = oracle.bc_norm(oracle.heads_from_groups(d["B"][:, -1], d["x"].shape[2], axis=1),
+                            blk.get("B_weight"), blk.get("B_bias"), EPS, blk["bc_norm"])
     e_B = slice_err(oracle.prevB_to_true(g["prev_B"], phiT), B_last, (0, 1))
     assert np.array_equal(g["prev_x"], d["x"][:, -1].astype(np.float64))
     assert e_h <= TOL[io], f"final state error {e_h:.3e}"
