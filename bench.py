@@ -79,9 +79,9 @@ def output_useful_flops(b, T, H, P, N, R):
     return total * b * H
 
 
-def decode_bytes_per_step(b, H, P, N, R, s=2):
+def decode_bytes_per_step(b, H, P, N, R, s=2, state_bytes=4):
     K = N // 2
-    per = (2 * N * P * 4 + 2 * R * N * 4 + 2 * R * P * s + 2 * K * 4
+    per = (2 * N * P * state_bytes + 2 * R * N * 4 + 2 * R * P * s + 2 * K * 4
            + R * P * s + 2 * R * N * s + K * s + 2 * s + R * P * s)
     return b * H * per
 
@@ -213,12 +213,13 @@ def block_params(torch, H, R, N, shape, seed=5):
     return mixer.Block(bc_norm=True, eps=1e-6, B_weight=bw, B_bias=bb, C_weight=cw, C_bias=cb), z
 
 
-def time_decode(torch, mixer, synth, b, H, P, N, R, steps, warmup, seed=0, with_block=False):
+def time_decode(torch, mixer, synth, b, H, P, N, R, steps, warmup, seed=0, with_block=False,
+                state_dtype=None):
     # per-step inputs, step-major so that every step's slice is contiguous
     inp = synth.torch_inputs(steps + warmup, b, H, P, N, R, io="bf16", seed=seed + 4)
     g = torch.Generator(device="cuda")
     g.manual_seed(seed + 40)
-    st = mixer.State.zeros(b, H, N, P, R, torch.bfloat16)
+    st = mixer.State.zeros(b, H, N, P, R, torch.bfloat16, state_dtype=state_dtype or torch.float32)
     st.h.copy_(torch.randn(st.h.shape, generator=g, device="cuda") * 0.1)
     y = torch.empty(b, H, R, P, device="cuda", dtype=torch.bfloat16)
     A = inp["A"]
@@ -280,17 +281,21 @@ def cpu_baseline(torch, inp, budget_s):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    # The GPU raises its clocks only after some milliseconds of sustained
-    # work: a short run measures the ramp (about 15% slower per call), so the
-    # defaults time 200 calls after 50 untimed ones (tens of milliseconds).
+    # The GPU raises its clocks only after about 100 ms of sustained work: a
+    # short run measures the ramp (5-15% slower per call), so the defaults
+    # time 200 calls after 800 untimed ones (about 0.1 s of SISO prefill).
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=800)
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-mimo", action="store_true", help="skip the MIMO prefill workload")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode workload")
     ap.add_argument("--no-block", action="store_true",
                     help="skip the workloads with the block prologue/epilogue")
+    ap.add_argument("--no-bf16-state", action="store_true",
+                    help="skip the decode workload with a bf16 carried state")
+    ap.add_argument("--no-groups", action="store_true",
+                    help="skip the SISO workload with B/C shared by all heads")
     ap.add_argument("--long", action="store_true", help="also run the T=65536 MIMO prefill")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="CPU-seconds of oracle work")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -378,6 +383,23 @@ def main():
         log(f"[siso prefill + block] {msb * 1000:.1f} us/call")
         del blk, z
 
+    if not args.no_groups:
+        # the same SISO workload with one B/C group shared by all heads
+        del inp
+        torch.cuda.empty_cache()
+        inp = synth.torch_inputs(b, T, H, P, N, R, io="bf16", seed=0, G=1)
+        msg, _, _ = time_prefill(torch, mixer, inp, args.steps, args.warmup)
+        gb = path_min_bytes(b, T, H, P, N, R) - b * T * (H - 1) * 2 * R * N * 2
+        result["groups_siso_prefill"] = {
+            "workload": c1["name"] + "_G1", "ngroups": 1,
+            "tokens_per_s": round(b * T / (msg / 1000), 1), "ms_per_call": round(msg / 1, 4),
+            "vs_per_head_bc": round(ms / msg, 4), "path_min_bytes": gb,
+            "frac_of_hbm_peak_at_min_bytes": round(gb / (msg / 1000) / 1e9 / HBM_PEAK_GBS, 4)}
+        log(f"[siso prefill, one B/C group] {msg * 1000:.1f} us/call")
+        del inp
+        torch.cuda.empty_cache()
+        inp = synth.torch_inputs(b, T, H, P, N, R, io="bf16", seed=0)
+
     if not args.no_cpu:
         log("[cpu baseline] timing the fp64 oracle on a sample ...")
         result["cpu_baseline"] = cpu_baseline(torch, inp, args.cpu_budget)
@@ -457,6 +479,15 @@ def main():
                 "vs_plain": round(us / usb, 4), "alg_bytes_per_step": dbb,
                 "frac_of_hbm_peak": round(dbb / (usb * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
             log(f"[mimo decode + block] {usb:.1f} us/step")
+        if not args.no_bf16_state:
+            uss = time_decode(torch, mixer, synth, b4, H4, P4, N4, R4, args.decode_steps, 10,
+                              state_dtype=torch.bfloat16)
+            dbs = decode_bytes_per_step(b4, H4, P4, N4, R4, state_bytes=2)
+            result["bf16_state_decode"] = {
+                "workload": c4["name"] + "_bf16_state", "us_per_step": round(uss, 2),
+                "vs_fp32_state": round(us / uss, 4), "alg_bytes_per_step": dbs,
+                "frac_of_hbm_peak": round(dbs / (uss * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+            log(f"[mimo decode, bf16 state] {uss:.1f} us/step")
 
     print(json.dumps(result), flush=True)
 

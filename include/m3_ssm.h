@@ -90,7 +90,11 @@ typedef enum {
  * 160 KB of LDS of a gfx950 compute unit; (N, P, R) combinations that do not
  * fit (with fp32 I/O: N = 128 with R >= 2, N = 64 with R = 4) are reported as
  * M3_ERR_UNSUPPORTED by the prefill entry points (and a zero workspace size).
- * ngroups < 0 or not dividing nheads is M3_ERR_INVALID_ARGUMENT. */
+ * ngroups < 0 or not dividing nheads is M3_ERR_INVALID_ARGUMENT.
+ * state_dtype BF16 keeps h~ in bf16 (round to nearest even at every store;
+ * all arithmetic stays fp32): half the state traffic of a decode step, at a
+ * rounding error of about 2^-9 of the state per store.  Phi and prev_B stay
+ * fp32.  Another value is M3_ERR_INVALID_ARGUMENT. */
 typedef struct {
     int64_t batch;
     int64_t seqlen;   /* T; ignored by m3_ssm_decode_step */
@@ -101,11 +105,12 @@ typedef struct {
     int32_t chunk;    /* Q, must be 64 */
     int32_t io_dtype; /* m3_dtype_t */
     int32_t ngroups;  /* G: B and C shared by groups of H/G consecutive heads; 0 = H */
+    int32_t state_dtype; /* m3_dtype_t of the carried state h~: F32 (0, default) or BF16 */
 } m3_shape_t;
 
 /* Carried state of one batch of sequences (caller-owned device buffers). */
 typedef struct {
-    float *h;       /* [b][H][N][P]  rotated-frame state h~ = R(-Phi) h               */
+    void  *h;       /* [b][H][N][P]  rotated-frame state h~ = R(-Phi) h, state_dtype  */
     float *phi;     /* [b][H][K]     cumulative angle Phi, wrapped to [-pi, pi)       */
     float *prev_B;  /* [b][H][R][N]  rotated B~ = R(-Phi) B of the last consumed token */
     void  *prev_x;  /* [b][H][R][P]  x of the last consumed token (I/O dtype)          */

@@ -37,7 +37,7 @@ class m3_shape_t(ctypes.Structure):
                 ("nheads", ctypes.c_int32), ("headdim", ctypes.c_int32),
                 ("dstate", ctypes.c_int32), ("rank", ctypes.c_int32),
                 ("chunk", ctypes.c_int32), ("io_dtype", ctypes.c_int32),
-                ("ngroups", ctypes.c_int32)]
+                ("ngroups", ctypes.c_int32), ("state_dtype", ctypes.c_int32)]
 
 
 class m3_state_t(ctypes.Structure):

@@ -94,8 +94,33 @@ __device__ __forceinline__ void unpack8(const uint2 &u, float *v, float) {
 // source offset, item stride and LDS destination are fixed for the launch.
 enum : int { kUnitB = 0, kUnitC = 1, kUnitX = 2, kUnitXp = 3, kUnitBp = 4, kUnitNone = 5 };
 
-template <typename IO, int N, int P, int R, bool BLK>
+// One run of four consecutive state values (along P) as stored: fp32 (16
+// bytes) or, with a bf16 state (SB), four bf16 (8 bytes, rounded to nearest
+// even when stored).  Registers hold the stored form until the run is used.
+template <bool SB>
+struct StateRun;
+template <>
+struct StateRun<false> {
+    typedef float4 raw;
+    static constexpr int bytes = 16;
+    static __device__ __forceinline__ float4 unpack(const raw &r) { return r; }
+    static __device__ __forceinline__ raw pack(const float u[4]) { return make_float4(u[0], u[1], u[2], u[3]); }
+};
+template <>
+struct StateRun<true> {
+    typedef uint2 raw;
+    static constexpr int bytes = 8;
+    static __device__ __forceinline__ float4 unpack(const raw &r) {
+        return make_float4(__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xffff0000u),
+                           __uint_as_float(r.y << 16), __uint_as_float(r.y & 0xffff0000u));
+    }
+    static __device__ __forceinline__ raw pack(const float u[4]) { return make_uint2(pack2_bf16(u[0], u[1]), pack2_bf16(u[2], u[3])); }
+};
+
+template <typename IO, int N, int P, int R, bool BLK, bool SB>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode_wg_per_cu(N, P)))) void k_decode_step(const DecodeParams p) {
+    typedef StateRun<SB> SR;
+    typedef typename SR::raw HV;
     typedef DecodeLds<N, P> L;
     constexpr int K = N / 2, P4 = L::P4, G = L::G;
     constexpr int SZ = int(sizeof(IO)), EPU = 16 / SZ, NPU = EPU / 2;
@@ -143,14 +168,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode
     // The state of an item is SLOTS consecutive float4 runs; run tid + 256 j
     // is row (tid + 256 j) / P4, columns 4 pg .. 4 pg + 3.
     const int tslot = min(tid, SLOTS - 1);
-    auto load_state = [&](int64_t item, float4 *hv) {
-        const float4 *hs = reinterpret_cast<const float4 *>(p.h) + item * SLOTS;
+    auto load_state = [&](int64_t item, HV *hv) {
+        const HV *hs = static_cast<const HV *>(p.h) + item * SLOTS;
 #pragma unroll
         for (int j = 0; j < SPT; ++j) hv[j] = hs[j * kThreads + tslot];
     };
 
     // item = (batch, head); gitem = (batch, B/C group of the head)
-    auto step = [&](const int64_t item, const int64_t gitem, const int h, const float4 *hc, float4 *hx) {
+    auto step = [&](const int64_t item, const int64_t gitem, const int h, const HV *hc, HV *hx) {
         // ---- issue: small vectors of this item, then the next item's state
         uint4 ud[UPT];
         uint2 ut[UPT];
@@ -180,7 +205,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode
         float4 wq[BLK ? UPT : 1][EPU / 4], bq[BLK ? UPT : 1][EPU / 4];
         typename io4<IO>::raw zr;
         if constexpr (BLK) {
-            const float *hs0 = p.h + item * (N * P);
+            const float *hs0 = reinterpret_cast<const float *>(static_cast<const char *>(p.h) + item * (N * P / 4 * SR::bytes));
 #pragma unroll
             for (int j = 0; j < UPT; ++j) {
                 const bool isc = ukind[j] == kUnitC;
@@ -260,7 +285,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode
         const float alpha = __expf(dtv * Ah);
         const float beta = (1.f - lamv) * dtv * alpha;
         const float gamma = lamv * dtv;
-        float4 *hs = reinterpret_cast<float4 *>(p.h) + item * SLOTS;
+        HV *hs = static_cast<HV *>(p.h) + item * SLOTS;
         float yp[R][4];
 #pragma unroll
         for (int i = 0; i < R; ++i)
@@ -271,7 +296,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode
             const int slot = tid + j * kThreads;
             if (SLOTS % kThreads != 0 && slot >= SLOTS) continue;
             const int n = slot / P4;
-            float u[4] = {alpha * hc[j].x, alpha * hc[j].y, alpha * hc[j].z, alpha * hc[j].w};
+            const float4 hv = SR::unpack(hc[j]);
+            float u[4] = {alpha * hv.x, alpha * hv.y, alpha * hv.z, alpha * hv.w};
 #pragma unroll
             for (int r = 0; r < R; ++r) {
                 const float cb = beta * bp_s[r * N + n], cg = gamma * bt_s[r * N + n];
@@ -282,7 +308,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode
                 u[2] += cb * xp4.z + cg * x4.z;
                 u[3] += cb * xp4.w + cg * x4.w;
             }
-            hs[slot] = make_float4(u[0], u[1], u[2], u[3]);
+            hs[slot] = SR::pack(u);
 #pragma unroll
             for (int i = 0; i < R; ++i) {
                 const float cc = ct_s[i * N + n];
@@ -322,7 +348,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode
 
     // Two items per trip, the state registers swapping roles, so the
     // prefetched state is never copied (a copy would wait for it).
-    float4 ha[SPT], hb[SPT];
+    HV ha[SPT], hb[SPT];
     int64_t item = blockIdx.x;       // the grid never exceeds the item count
     int h = int(item % p.H);         // head and batch of the item, advanced
     int64_t bi = item / p.H;         // without a division
@@ -346,24 +372,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode
     }
 }
 
-template <typename IO, int N, int P, int R, bool BLK>
+template <typename IO, int N, int P, int R, bool BLK, bool SB>
 hipError_t launch_decode_inst(const DecodeParams &p, hipStream_t s) {
     const int64_t bh = p.batch * p.H;
     const int64_t cap = int64_t(kDecodeCus) * decode_wg_per_cu(N, P);
     const dim3 grid{static_cast<unsigned>(bh < cap ? bh : cap)}, block{kThreads};
-    hipLaunchKernelGGL((k_decode_step<IO, N, P, R, BLK>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((k_decode_step<IO, N, P, R, BLK, SB>), grid, block, 0, s, p);
     return hipGetLastError();
 }
 
-// Dispatch over (N, P, R) for one I/O type, with or without the block ops.
-template <typename IO, bool BLK>
+// Dispatch over (N, P, R) for one I/O type, with or without the block ops,
+// fp32 or bf16 state.
+template <typename IO, bool BLK, bool SB>
 hipError_t launch_decode_io(const DecodeParams &p, hipStream_t s) {
 #define M3_DECODE_R(NN, PP)                                                   \
     switch (p.R) {                                                            \
-    case 1: return launch_decode_inst<IO, NN, PP, 1, BLK>(p, s);              \
-    case 2: return launch_decode_inst<IO, NN, PP, 2, BLK>(p, s);              \
-    case 3: return launch_decode_inst<IO, NN, PP, 3, BLK>(p, s);              \
-    case 4: return launch_decode_inst<IO, NN, PP, 4, BLK>(p, s);              \
+    case 1: return launch_decode_inst<IO, NN, PP, 1, BLK, SB>(p, s);          \
+    case 2: return launch_decode_inst<IO, NN, PP, 2, BLK, SB>(p, s);          \
+    case 3: return launch_decode_inst<IO, NN, PP, 3, BLK, SB>(p, s);          \
+    case 4: return launch_decode_inst<IO, NN, PP, 4, BLK, SB>(p, s);          \
     default: return hipErrorInvalidValue;                                     \
     }
 #define M3_DECODE_P(NN)                                                       \

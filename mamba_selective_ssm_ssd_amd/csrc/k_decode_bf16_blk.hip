@@ -3,6 +3,6 @@
 
 namespace m3 {
 
-hipError_t launch_decode_bf16_blk(const DecodeParams &p, hipStream_t s) { return launch_decode_io<bf16, true>(p, s); }
+hipError_t launch_decode_bf16_blk(const DecodeParams &p, hipStream_t s) { return launch_decode_io<bf16, true, false>(p, s); }
 
 } // namespace m3

@@ -1,0 +1,8 @@
+// k_decode_bf16_sb.hip -- instantiations of the fused decode step for bf16 I/O with a bf16 carried state.
+#include "k_decode.hpp"
+
+namespace m3 {
+
+hipError_t launch_decode_bf16_sb(const DecodeParams &p, hipStream_t s) { return launch_decode_io<bf16, false, true>(p, s); }
+
+} // namespace m3

@@ -3,6 +3,6 @@
 
 namespace m3 {
 
-hipError_t launch_decode_f32_blk(const DecodeParams &p, hipStream_t s) { return launch_decode_io<float, true>(p, s); }
+hipError_t launch_decode_f32_blk(const DecodeParams &p, hipStream_t s) { return launch_decode_io<float, true, false>(p, s); }
 
 } // namespace m3

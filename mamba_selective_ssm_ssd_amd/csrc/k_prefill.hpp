@@ -572,14 +572,15 @@ template <class C, typename IO>
 __device__ __forceinline__ floatx4 fold_init(const PrefillParams &p, int64_t bh, int nt, int pt, float del0) {
     const int lane = threadIdx.x & (kWave - 1), g = lane >> 4, l16 = lane & 15;
     const int pc = 16 * pt + l16;
-    const float *h0 = p.h0 + bh * int64_t(C::N) * C::P;
+    const int64_t h0b = bh * int64_t(C::N) * C::P;
     const float *pb = p.prevB0 + bh * int64_t(C::R) * C::N;
     const IO *px = static_cast<const IO *>(p.prevx0) + bh * int64_t(C::R) * C::P;
     float a[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
         const int n = 16 * nt + 4 * g + v;
-        float s = h0[n * C::P + pc];
+        float s = p.sbf16 ? bits_to_f32(static_cast<const uint16_t *>(p.h0)[h0b + n * C::P + pc])
+                          : static_cast<const float *>(p.h0)[h0b + n * C::P + pc];
 #pragma unroll
         for (int r = 0; r < C::R; ++r) s += del0 * pb[r * C::N + n] * io<IO>::get(px + r * C::P + pc);
         a[v] = s;
@@ -1245,7 +1246,11 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
     if (seg != p.S - 1 || !p.has_final) return;
 
     // final carried state in the rotated frame: h~ = R(-Phi_{T-1}) H
-    float *hT = p.hT + bh * int64_t(N) * P;
+    const int64_t hTb = bh * int64_t(N) * P;
+    auto put_h = [&](int64_t i, float v) { // final state in its storage type
+        if (p.sbf16) static_cast<uint16_t *>(p.hT)[hTb + i] = f32_to_bits(v);
+        else static_cast<float *>(p.hT)[hTb + i] = v;
+    };
 #pragma unroll
     for (int j = 0; j < C::TW; ++j) {
         const int tile = wave + kPW * j;
@@ -1258,8 +1263,8 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
             sincos_wrapped(wrap_angle(ths_s[k]), &sn, &cs);
             float u = st[j][2 * q], v = st[j][2 * q + 1];
             rot_neg(cs, sn, u, v);
-            hT[(16 * nt + 4 * g + 2 * q) * P + 16 * pt + l16] = u;
-            hT[(16 * nt + 4 * g + 2 * q + 1) * P + 16 * pt + l16] = v;
+            put_h((16 * nt + 4 * g + 2 * q) * P + 16 * pt + l16, u);
+            put_h((16 * nt + 4 * g + 2 * q + 1) * P + 16 * pt + l16, v);
         }
     }
     const int64_t tl = (b * p.T + p.T - 1) * p.H + h;   // token-head index of T-1 (x)

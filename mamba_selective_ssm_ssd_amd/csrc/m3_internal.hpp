@@ -24,6 +24,7 @@ struct PrefillParams {
     int64_t batch, T;
     int32_t H, P, N, R, K, nC; // K = N/2 rotation pairs, nC = ceil(T/64) chunks
     int32_t G, hpg;            // B/C groups, heads per group (head h reads group h / hpg)
+    int32_t sbf16;             // carried state h~ stored in bf16
     int32_t S, cps;            // segments per sequence, chunks per segment
     // inputs (I/O dtype unless noted)
     const void *x, *dt, *lam, *theta, *B, *C;
@@ -32,11 +33,13 @@ struct PrefillParams {
     // initial carried state; read only by the first workgroup of a sequence
     // (S == 1) or by the pre-pass (S > 1)
     int32_t has_init;
-    const float *h0, *phi0, *prevB0;
+    const void *h0; // state_dtype (sbf16: bf16, else fp32)
+    const float *phi0, *prevB0;
     const void *prevx0;
     // final carried state; written only by the last segment's workgroup
     int32_t has_final;
-    float *hT, *phiT, *prevBT;
+    void *hT; // state_dtype
+    float *phiT, *prevBT;
     void *prevxT;
     // workspace (used when S > 1)
     float *segU;    // [b][H][S][N][P]  segment aggregate: its state from a zero start
@@ -51,10 +54,12 @@ struct DecodeParams {
     int64_t batch;
     int32_t H, P, N, R, K;
     int32_t G, hpg; // B/C groups, heads per group
+    int32_t sbf16;  // state h~ stored in bf16
     const void *x, *dt, *lam, *theta, *B, *C;
     const float *A;
     void *y;
-    float *h, *phi, *prevB;
+    void *h; // state_dtype
+    float *phi, *prevB;
     void *prevx;
     BlockParams blk;
 };
@@ -89,6 +94,11 @@ hipError_t launch_decode_f32(const DecodeParams &p, hipStream_t s);
 // the same with the block prologue/epilogue (p.blk.on)
 hipError_t launch_decode_bf16_blk(const DecodeParams &p, hipStream_t s);
 hipError_t launch_decode_f32_blk(const DecodeParams &p, hipStream_t s);
+// the same with a bf16 carried state (p.sbf16), plain and with the block ops
+hipError_t launch_decode_bf16_sb(const DecodeParams &p, hipStream_t s);
+hipError_t launch_decode_f32_sb(const DecodeParams &p, hipStream_t s);
+hipError_t launch_decode_bf16_blk_sb(const DecodeParams &p, hipStream_t s);
+hipError_t launch_decode_f32_blk_sb(const DecodeParams &p, hipStream_t s);
 
 // Dynamic LDS bytes of the fused prefill kernel for a shape (0: not compiled).
 size_t prefill_lds_bytes(bool is_bf16, int N, int P, int R, bool blk = false);

@@ -37,6 +37,7 @@ m3_status_t check_shape(const m3_shape_t *s, bool decode) {
     if (s->dstate % 2 != 0) return M3_ERR_INVALID_ARGUMENT;
     if (s->chunk < 1) return M3_ERR_INVALID_ARGUMENT;
     if (s->ngroups < 0 || (s->ngroups > 0 && s->nheads % s->ngroups != 0)) return M3_ERR_INVALID_ARGUMENT;
+    if (s->state_dtype != M3_DTYPE_F32 && s->state_dtype != M3_DTYPE_BF16) return M3_ERR_INVALID_ARGUMENT;
     if (s->chunk != 64) return M3_ERR_UNSUPPORTED;
     if (!m3::supported_N(s->dstate) || !m3::supported_P(s->headdim) || s->rank > 4)
         return M3_ERR_UNSUPPORTED;
@@ -200,6 +201,7 @@ static m3_status_t prepare_prefill(const m3_shape_t *shape, const void *x, const
     p.K = p.N / 2;
     p.G = shape->ngroups ? shape->ngroups : shape->nheads;
     p.hpg = p.H / p.G;
+    p.sbf16 = shape->state_dtype == M3_DTYPE_BF16;
     p.nC = int32_t((p.T + 63) / 64);
     p.x = x; p.dt = dt; p.lam = lam; p.theta = theta; p.B = B; p.C = C; p.A = A; p.y = y;
     p.has_init = init != nullptr;
@@ -299,6 +301,7 @@ m3_status_t m3_ssm_decode_step_block(const m3_shape_t *shape, const void *x, con
     p.K = p.N / 2;
     p.G = shape->ngroups ? shape->ngroups : shape->nheads;
     p.hpg = p.H / p.G;
+    p.sbf16 = shape->state_dtype == M3_DTYPE_BF16;
     p.x = x; p.dt = dt; p.lam = lam; p.theta = theta; p.B = B; p.C = C; p.A = A; p.y = y;
     p.h = state->h; p.phi = state->phi; p.prevB = state->prev_B; p.prevx = state->prev_x;
     p.blk = bp;

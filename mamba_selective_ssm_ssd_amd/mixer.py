@@ -23,15 +23,17 @@ _IO = {torch.float32: capi.M3_DTYPE_F32, torch.bfloat16: capi.M3_DTYPE_BF16}
 @dataclass
 class State:
     """Carried state in the rotated frame (see include/m3_ssm.h)."""
-    h: torch.Tensor       # [b,H,N,P] float32
+    h: torch.Tensor       # [b,H,N,P] float32 or bfloat16 (state_dtype)
     phi: torch.Tensor     # [b,H,N/2] float32
     prev_B: torch.Tensor  # [b,H,R,N] float32
     prev_x: torch.Tensor  # [b,H,R,P] I/O dtype
 
     @staticmethod
-    def zeros(batch, H, N, P, R, io_dtype=torch.bfloat16, device="cuda") -> "State":
+    def zeros(batch, H, N, P, R, io_dtype=torch.bfloat16, device="cuda",
+              state_dtype=torch.float32) -> "State":
         f = dict(device=device, dtype=torch.float32)
-        return State(torch.zeros(batch, H, N, P, **f), torch.zeros(batch, H, N // 2, **f),
+        return State(torch.zeros(batch, H, N, P, device=device, dtype=state_dtype),
+                     torch.zeros(batch, H, N // 2, **f),
                      torch.zeros(batch, H, R, N, **f),
                      torch.zeros(batch, H, R, P, device=device, dtype=io_dtype))
 
@@ -96,10 +98,11 @@ def _stream() -> int:
     return torch.cuda.current_stream().cuda_stream
 
 
-def make_shape(batch, T, H, P, N, R, io_dtype, chunk=64, G=0) -> capi.m3_shape_t:
-    """G: B/C head groups (0 or H: per head)."""
+def make_shape(batch, T, H, P, N, R, io_dtype, chunk=64, G=0,
+               state_dtype=torch.float32) -> capi.m3_shape_t:
+    """G: B/C head groups (0 or H: per head); state_dtype: storage of h~."""
     return capi.m3_shape_t(int(batch), int(T), int(H), int(P), int(N), int(R), int(chunk),
-                           int(_IO[io_dtype]), int(G))
+                           int(_IO[io_dtype]), int(G), int(_IO[state_dtype]))
 
 
 def workspace_bytes(batch, T, H, P, N, R, io_dtype=torch.bfloat16) -> int:
@@ -107,8 +110,12 @@ def workspace_bytes(batch, T, H, P, N, R, io_dtype=torch.bfloat16) -> int:
 
 
 def prefill(x, dt, A, lam, theta, B, C, state: State | None = None, final: State | None = None,
-            want_final: bool = True, y=None, workspace=None, block: Block | None = None, z=None):
+            want_final: bool = True, y=None, workspace=None, block: Block | None = None, z=None,
+            state_dtype=None):
     """Chunked prefill.  Returns (y, final_state or None).
+
+    The carried state's h~ is float32 or bfloat16: the dtype of the given
+    state(s), else ``state_dtype`` (default float32) for a new final state.
 
     ``block`` / ``z`` (shaped like x) add the block prologue and output gate.
 
@@ -120,12 +127,16 @@ def prefill(x, dt, A, lam, theta, B, C, state: State | None = None, final: State
     N = B.shape[-1]
     io = x.dtype
     _check_bc(B, C, (b, T), R, N)
-    shape = make_shape(b, T, H, P, N, R, io, G=B.shape[2])
+    given = [s.h.dtype for s in (state, final) if s is not None]
+    sd = given[0] if given else (state_dtype or torch.float32)
+    if any(d != sd for d in given) or (state_dtype is not None and state_dtype != sd):
+        raise ValueError("initial and final states must share one state dtype")
+    shape = make_shape(b, T, H, P, N, R, io, G=B.shape[2], state_dtype=sd)
     if y is None:
         y = torch.empty_like(x)
     if want_final and final is None:
         final = state if state is not None else State(
-            torch.empty(b, H, N, P, device=x.device, dtype=torch.float32),
+            torch.empty(b, H, N, P, device=x.device, dtype=sd),
             torch.empty(b, H, N // 2, device=x.device, dtype=torch.float32),
             torch.empty(b, H, R, N, device=x.device, dtype=torch.float32),
             torch.empty(b, H, R, P, device=x.device, dtype=io))
@@ -162,7 +173,9 @@ def prefill_stage(stage: int, x, dt, A, lam, theta, B, C, state, final, y, works
     io = x.dtype
     _check_bc(B, C, (b, T), R, N)
     rc = capi.m3_ssm_prefill_stage(
-        stage, make_shape(b, T, H, P, N, R, io, G=B.shape[2]), _ptr(x, "x", io), _ptr(dt, "dt", io),
+        stage, make_shape(b, T, H, P, N, R, io, G=B.shape[2],
+                          state_dtype=next((q.h.dtype for q in (state, final) if q is not None), torch.float32)),
+        _ptr(x, "x", io), _ptr(dt, "dt", io),
         _ptr(A, "A", torch.float32), _ptr(lam, "lam", io), _ptr(theta, "theta", io),
         _ptr(B, "B", io), _ptr(C, "C", io), state.c() if state is not None else None,
         final.c() if final is not None else None, _ptr(y, "y", io), workspace.data_ptr(),
@@ -180,7 +193,7 @@ def decode_step(x, dt, A, lam, theta, B, C, state: State, y=None, block: Block |
     N = B.shape[-1]
     io = x.dtype
     _check_bc(B, C, (b,), R, N)
-    shape = make_shape(b, 1, H, P, N, R, io, G=B.shape[1])
+    shape = make_shape(b, 1, H, P, N, R, io, G=B.shape[1], state_dtype=state.h.dtype)
     if y is None:
         y = torch.empty_like(x)
     if z is not None and tuple(z.shape) != tuple(x.shape):

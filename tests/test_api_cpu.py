@@ -226,3 +226,14 @@ def test_group_errors():
     # group count does not change the workspace
     assert (capi.m3_ssm_prefill_workspace_bytes(_shape(nheads=6, ngroups=2))
             == capi.m3_ssm_prefill_workspace_bytes(_shape(nheads=6)))
+
+
+def test_state_dtype_errors():
+    W = capi.M3_ERR_WORKSPACE
+    assert _prefill(_shape(state_dtype=capi.M3_DTYPE_F32)) == W
+    assert _prefill(_shape(state_dtype=capi.M3_DTYPE_BF16)) == W
+    for sd in (-1, 2, 9):
+        assert _prefill(_shape(state_dtype=sd)) == capi.M3_ERR_INVALID_ARGUMENT
+    st = capi.m3_state_t(FAKE, FAKE, FAKE, FAKE)
+    assert capi.m3_ssm_decode_step(_shape(state_dtype=5), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                   FAKE, st, FAKE, None) == capi.M3_ERR_INVALID_ARGUMENT

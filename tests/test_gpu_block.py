@@ -171,8 +171,8 @@ def _decode_run(d, bp, pieces, io, st, t0, t1):
     block, z = _gpu_block(bp, pieces, io)
     ys = []
     for s in range(t0, t1):
-        zs = z[:, s].contiguous() if z is not None else None
-        y = mixer.decode_step(*(t[k][:, s].contiguous() if k != "A" else t[k]
+        zs = z[:, s].clone() if z is not None else None
+        y = mixer.decode_step(*(t[k][:, s].clone() if k != "A" else t[k]
                                 for k in ("x", "dt", "A", "lam", "theta", "B", "C")),
                               st, block=block, z=zs)
         ys.append(y.double().cpu().numpy()[:, None])

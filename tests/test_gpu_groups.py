@@ -60,7 +60,7 @@ def test_groups_split_prefill_then_decode(io):
     t = to_dev(d, io)
     ys = [y1, y2]
     for s in range(T2, T):
-        y = mixer.decode_step(*(t[k][:, s].contiguous() if k != "A" else t[k]
+        y = mixer.decode_step(*(t[k][:, s].clone() if k != "A" else t[k]
                                 for k in ("x", "dt", "A", "lam", "theta", "B", "C")), st)
         ys.append(y.double().cpu().numpy()[:, None])
     assert slice_err(np.concatenate(ys, axis=1), yr, (0, 2)) <= TOL[io]
@@ -79,7 +79,7 @@ def test_groups_decode(N, P, R, io, H, G):
     st = mixer.State.zeros(b, H, N, P, R, torch_io(io))
     ys = []
     for s in range(T):
-        y = mixer.decode_step(*(t[k][:, s].contiguous() if k != "A" else t[k]
+        y = mixer.decode_step(*(t[k][:, s].clone() if k != "A" else t[k]
                                 for k in ("x", "dt", "A", "lam", "theta", "B", "C")), st)
         ys.append(y.double().cpu().numpy()[:, None])
     yr, hT, phiT = run_oracle(d)

@@ -145,9 +145,9 @@ def test_s2_prefill_then_decode(io):
     t = to_dev(d, io)
     ys = [y1]
     for s in range(T1, T):
-        y = mixer.decode_step(t["x"][:, s].contiguous(), t["dt"][:, s].contiguous(), t["A"],
-                              t["lam"][:, s].contiguous(), t["theta"][:, s].contiguous(),
-                              t["B"][:, s].contiguous(), t["C"][:, s].contiguous(), st)
+        y = mixer.decode_step(t["x"][:, s].clone(), t["dt"][:, s].clone(), t["A"],
+                              t["lam"][:, s].clone(), t["theta"][:, s].clone(),
+                              t["B"][:, s].clone(), t["C"][:, s].clone(), st)
         ys.append(y.double().cpu().numpy()[:, None])
     yg = np.concatenate(ys, axis=1)
     assert slice_err(yg, yr, (0, 2)) <= TOL[io]
