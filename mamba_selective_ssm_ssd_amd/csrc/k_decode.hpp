@@ -36,8 +36,12 @@ namespace m3 {
 
 constexpr int kDecodeCus = 256; // compute units of an MI355X
 // Resident decode workgroups per compute unit: each holds the state of two
-// items (current and prefetched) in registers.
-constexpr int decode_wg_per_cu(int N, int P) { return N * P > 4096 || (N > 64 && N * P >= 4096) ? 2 : 4; }
+// items (current and prefetched) in registers; a bf16 state takes half the
+// registers, so one more workgroup fits (measured: 75.0 vs 77.4 us per step
+// of the b256 H64 P64 N64 R4 decode).
+constexpr int decode_wg_per_cu(int N, int P, bool SB = false) {
+    return N * P > 4096 || (N > 64 && N * P >= 4096) ? 2 : (SB ? 5 : 4);
+}
 
 template <int N, int P>
 struct DecodeLds {
@@ -118,7 +122,7 @@ struct StateRun<true> {
 };
 
 template <typename IO, int N, int P, int R, bool BLK, bool SB>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode_wg_per_cu(N, P)))) void k_decode_step(const DecodeParams p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode_wg_per_cu(N, P, SB)))) void k_decode_step(const DecodeParams p) {
     typedef StateRun<SB> SR;
     typedef typename SR::raw HV;
     typedef DecodeLds<N, P> L;
@@ -375,7 +379,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode
 template <typename IO, int N, int P, int R, bool BLK, bool SB>
 hipError_t launch_decode_inst(const DecodeParams &p, hipStream_t s) {
     const int64_t bh = p.batch * p.H;
-    const int64_t cap = int64_t(kDecodeCus) * decode_wg_per_cu(N, P);
+    const int64_t cap = int64_t(kDecodeCus) * decode_wg_per_cu(N, P, SB);
     const dim3 grid{static_cast<unsigned>(bh < cap ? bh : cap)}, block{kThreads};
     hipLaunchKernelGGL((k_decode_step<IO, N, P, R, BLK, SB>), grid, block, 0, s, p);
     return hipGetLastError();
