@@ -24,7 +24,8 @@ M3_ERR_HIP = 4
 # Every function the headers under include/ declare.
 EXPORTED = ("m3_ssm_prefill_workspace_bytes", "m3_ssm_prefill", "m3_ssm_decode_step",
             "m3_status_string", "m3_ssm_prefill_stage", "m3_ssm_prefill_block",
-            "m3_ssm_decode_step_block")
+            "m3_ssm_decode_step_block", "m3_ssm_prefill_backward_workspace_bytes",
+            "m3_ssm_prefill_backward")
 
 # Stages of the prefill (include/m3_ssm_stages.h).
 M3_STAGE_SEGMENT_STATE = 0
@@ -51,6 +52,12 @@ class m3_block_t(ctypes.Structure):
                 ("B_weight", ctypes.c_void_p), ("B_bias", ctypes.c_void_p),
                 ("C_weight", ctypes.c_void_p), ("C_bias", ctypes.c_void_p),
                 ("z", ctypes.c_void_p)]
+
+
+class m3_grads_t(ctypes.Structure):
+    """Gradient outputs of the backward pass (include/m3_ssm_backward.h)."""
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("x", "dt", "A", "lam", "theta", "B", "C", "h", "phi", "prev_B", "prev_x")]
 
 
 class M3Error(RuntimeError):
@@ -89,6 +96,12 @@ def load():
     lib.m3_ssm_prefill_block.restype = ctypes.c_int
     lib.m3_ssm_decode_step_block.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, bkp, stp, vp, vp]
     lib.m3_ssm_decode_step_block.restype = ctypes.c_int
+    gp = ctypes.POINTER(m3_grads_t)
+    lib.m3_ssm_prefill_backward_workspace_bytes.argtypes = [sp]
+    lib.m3_ssm_prefill_backward_workspace_bytes.restype = ctypes.c_size_t
+    lib.m3_ssm_prefill_backward.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, stp, vp, gp, vp,
+                                            ctypes.c_size_t, vp]
+    lib.m3_ssm_prefill_backward.restype = ctypes.c_int
     lib.m3_status_string.argtypes = [ctypes.c_int]
     lib.m3_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -146,3 +159,17 @@ def m3_ssm_decode_step_block(shape, x, dt, A, lam, theta, B, C, block, state, y,
         ctypes.byref(shape), x, dt, A, lam, theta, B, C,
         ctypes.byref(block) if block is not None else None,
         ctypes.byref(state) if state is not None else None, y, stream))
+
+
+def m3_ssm_prefill_backward_workspace_bytes(shape: m3_shape_t) -> int:
+    return int(load().m3_ssm_prefill_backward_workspace_bytes(ctypes.byref(shape)))
+
+
+def m3_ssm_prefill_backward(shape, x, dt, A, lam, theta, B, C, init, gy, grads, workspace,
+                            workspace_bytes, stream) -> int:
+    """grads: an m3_grads_t of device addresses."""
+    return int(load().m3_ssm_prefill_backward(
+        ctypes.byref(shape), x, dt, A, lam, theta, B, C,
+        ctypes.byref(init) if init is not None else None, gy,
+        ctypes.byref(grads) if grads is not None else None,
+        workspace, int(workspace_bytes), stream))

@@ -64,6 +64,25 @@ struct DecodeParams {
     BlockParams blk;
 };
 
+// Backward pass (one workgroup per (batch, head), sequential in time).
+struct BwdParams {
+    int64_t batch, T;
+    int32_t H, P, N, R, K, nC;
+    const void *x, *dt, *lam, *theta, *B, *C, *gy; // I/O dtype
+    const float *A;
+    int32_t has_init;
+    const float *h0, *phi0, *prevB0; // rotated frame, fp32
+    const void *prevx0;             // I/O dtype
+    // outputs (fp32); the carried-state ones may be null
+    float *gx, *gdt, *glam, *gtheta, *gB, *gC, *gA;
+    float *gh0, *gphi0, *gprevB0, *gprevx0;
+    // workspace
+    float *ck_h;    // [b][H][nC][N][P]  state before each chunk
+    double *ck_phi; // [b][H][nC][K]     angle before each chunk
+    float *slab;    // [b][H][65][N][P]  one chunk's states, h~_{t0-1} .. h~_{t0+63}
+    float *gA_part; // [b][H]
+};
+
 // Workspace layout (byte offsets of each region, 256-byte aligned).
 struct WorkspaceLayout {
     size_t segU, segG, segTh, hinit, phi0, total;
@@ -99,6 +118,9 @@ hipError_t launch_decode_bf16_sb(const DecodeParams &p, hipStream_t s);
 hipError_t launch_decode_f32_sb(const DecodeParams &p, hipStream_t s);
 hipError_t launch_decode_bf16_blk_sb(const DecodeParams &p, hipStream_t s);
 hipError_t launch_decode_f32_blk_sb(const DecodeParams &p, hipStream_t s);
+
+hipError_t launch_backward_bf16(const BwdParams &p, hipStream_t s);
+hipError_t launch_backward_f32(const BwdParams &p, hipStream_t s);
 
 // Dynamic LDS bytes of the fused prefill kernel for a shape (0: not compiled).
 size_t prefill_lds_bytes(bool is_bf16, int N, int P, int R, bool blk = false);

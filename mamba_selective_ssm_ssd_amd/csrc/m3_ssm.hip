@@ -10,6 +10,7 @@
 // enqueues one of the two prefill kernels alone (include/m3_ssm_stages.h).
 #include "m3_ssm.h"
 #include "m3_ssm_block.h"
+#include "m3_ssm_backward.h"
 #include "m3_ssm_stages.h"
 #include "k_prefill.hpp"
 #include "m3_internal.hpp"
@@ -84,6 +85,34 @@ WorkspaceLayout layout(const m3_shape_t *s) {
     w.phi0 = off; off += round_up(bh * K * sizeof(double));
     w.total = off;
     return w;
+}
+
+// Backward workspace: chunk-start states and angles, one chunk's states per
+// sequence, the per-sequence partials of dA.
+struct BwdLayout {
+    size_t ck_h, ck_phi, slab, gA, total;
+};
+BwdLayout bwd_layout(const m3_shape_t *s) {
+    const size_t bh = size_t(s->batch) * size_t(s->nheads);
+    const size_t nC = size_t((s->seqlen + 63) / 64);
+    const size_t N = size_t(s->dstate), P = size_t(s->headdim), K = N / 2;
+    BwdLayout w;
+    size_t off = 0;
+    w.ck_h = off; off += round_up(bh * nC * N * P * sizeof(float));
+    w.ck_phi = off; off += round_up(bh * nC * K * sizeof(double));
+    w.slab = off; off += round_up(bh * 65 * N * P * sizeof(float));
+    w.gA = off; off += round_up(bh * sizeof(float));
+    w.total = off;
+    return w;
+}
+
+m3_status_t check_backward_shape(const m3_shape_t *s) {
+    const m3_status_t sc = check_shape(s, false);
+    if (sc != M3_OK) return sc;
+    if (s->ngroups != 0 && s->ngroups != s->nheads) return M3_ERR_UNSUPPORTED;
+    if (s->state_dtype != M3_DTYPE_F32) return M3_ERR_UNSUPPORTED;
+    if (double(s->batch) * double(s->nheads) > 2.0e9) return M3_ERR_UNSUPPORTED;
+    return M3_OK;
 }
 
 bool state_ok(const m3_state_t *st) {
@@ -308,6 +337,59 @@ m3_status_t m3_ssm_decode_step_block(const m3_shape_t *shape, const void *x, con
     if ((shape->io_dtype == M3_DTYPE_BF16 ? m3::launch_decode_bf16(p, stream) : m3::launch_decode_f32(p, stream)) != hipSuccess)
         return M3_ERR_HIP;
     return M3_OK;
+}
+
+size_t m3_ssm_prefill_backward_workspace_bytes(const m3_shape_t *shape) {
+    if (check_backward_shape(shape) != M3_OK) return 0;
+    return bwd_layout(shape).total;
+}
+
+m3_status_t m3_ssm_prefill_backward(const m3_shape_t *shape, const void *x, const void *dt,
+                                    const float *A, const void *lam, const void *theta,
+                                    const void *B, const void *C, const m3_state_t *init,
+                                    const void *gy, const m3_grads_t *grads, void *workspace,
+                                    size_t workspace_bytes, hipStream_t stream) {
+    const m3_status_t sc = check_backward_shape(shape);
+    if (sc != M3_OK) return sc;
+    const void *ptrs[] = {x, dt, A, lam, theta, B, C, gy};
+    for (const void *q : ptrs)
+        if (!q || !aligned16(q)) return M3_ERR_INVALID_ARGUMENT;
+    if (!grads) return M3_ERR_INVALID_ARGUMENT;
+    const void *outs[] = {grads->x, grads->dt, grads->A, grads->lam, grads->theta, grads->B, grads->C};
+    for (const void *q : outs)
+        if (!q || !aligned16(q)) return M3_ERR_INVALID_ARGUMENT;
+    const void *opt[] = {grads->h, grads->phi, grads->prev_B, grads->prev_x};
+    for (const void *q : opt)
+        if (q && !aligned16(q)) return M3_ERR_INVALID_ARGUMENT;
+    if (init && !state_ok(init)) return M3_ERR_INVALID_ARGUMENT;
+    const BwdLayout w = bwd_layout(shape);
+    if (!workspace || !aligned16(workspace) || workspace_bytes < w.total) return M3_ERR_WORKSPACE;
+    m3::BwdParams p{};
+    p.batch = shape->batch;
+    p.T = shape->seqlen;
+    p.H = shape->nheads;
+    p.P = shape->headdim;
+    p.N = shape->dstate;
+    p.R = shape->rank;
+    p.K = p.N / 2;
+    p.nC = int32_t((p.T + 63) / 64);
+    p.x = x; p.dt = dt; p.lam = lam; p.theta = theta; p.B = B; p.C = C; p.gy = gy; p.A = A;
+    p.has_init = init != nullptr;
+    if (init) {
+        p.h0 = static_cast<const float *>(init->h); p.phi0 = init->phi; p.prevB0 = init->prev_B;
+        p.prevx0 = init->prev_x;
+        p.gh0 = grads->h; p.gphi0 = grads->phi; p.gprevB0 = grads->prev_B; p.gprevx0 = grads->prev_x;
+    }
+    p.gx = grads->x; p.gdt = grads->dt; p.glam = grads->lam; p.gtheta = grads->theta;
+    p.gB = grads->B; p.gC = grads->C; p.gA = grads->A;
+    unsigned char *ws = static_cast<unsigned char *>(workspace);
+    p.ck_h = reinterpret_cast<float *>(ws + w.ck_h);
+    p.ck_phi = reinterpret_cast<double *>(ws + w.ck_phi);
+    p.slab = reinterpret_cast<float *>(ws + w.slab);
+    p.gA_part = reinterpret_cast<float *>(ws + w.gA);
+    const hipError_t e = shape->io_dtype == M3_DTYPE_BF16 ? m3::launch_backward_bf16(p, stream)
+                                                          : m3::launch_backward_f32(p, stream);
+    return e == hipSuccess ? M3_OK : M3_ERR_HIP;
 }
 
 } // extern "C"

@@ -209,3 +209,39 @@ def decode_step(x, dt, A, lam, theta, B, C, state: State, y=None, block: Block |
     if rc != capi.M3_OK:
         raise capi.M3Error(rc, fn)
     return y
+
+
+def backward(x, dt, A, lam, theta, B, C, gy, state: State | None = None, workspace=None):
+    """Gradients of sum(gy * y) for y = prefill(x, ..., state=state).
+
+    Returns a dict of fp32 tensors: x, dt, A, lam, theta, B, C and, when a
+    carried state is given, h, phi, prev_B, prev_x (its gradients).
+    """
+    b, T, H, R, P = x.shape
+    N = B.shape[-1]
+    io = x.dtype
+    _check_bc(B, C, (b, T), R, N)
+    if tuple(gy.shape) != tuple(x.shape):
+        raise ValueError("gy must be shaped like x")
+    shape = make_shape(b, T, H, P, N, R, io, G=B.shape[2],
+                       state_dtype=state.h.dtype if state is not None else torch.float32)
+    need = capi.m3_ssm_prefill_backward_workspace_bytes(shape)
+    if need == 0:
+        raise capi.M3Error(capi.M3_ERR_UNSUPPORTED, "m3_ssm_prefill_backward_workspace_bytes")
+    if workspace is None:
+        workspace = torch.empty(need, device=x.device, dtype=torch.uint8)
+    f = dict(device=x.device, dtype=torch.float32)
+    g = {k: torch.empty(v.shape, **f) for k, v in dict(x=x, dt=dt, A=A, lam=lam, theta=theta, B=B, C=C).items()}
+    if state is not None:
+        g.update(h=torch.empty(state.h.shape, **f), phi=torch.empty(state.phi.shape, **f),
+                 prev_B=torch.empty(state.prev_B.shape, **f), prev_x=torch.empty(state.prev_x.shape, **f))
+    gs = capi.m3_grads_t(*(g[k].data_ptr() if k in g else None for k in
+                           ("x", "dt", "A", "lam", "theta", "B", "C", "h", "phi", "prev_B", "prev_x")))
+    rc = capi.m3_ssm_prefill_backward(
+        shape, _ptr(x, "x", io), _ptr(dt, "dt", io), _ptr(A, "A", torch.float32),
+        _ptr(lam, "lam", io), _ptr(theta, "theta", io), _ptr(B, "B", io), _ptr(C, "C", io),
+        state.c() if state is not None else None, _ptr(gy, "gy", io), gs,
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream())
+    if rc != capi.M3_OK:
+        raise capi.M3Error(rc, "m3_ssm_prefill_backward")
+    return g

@@ -237,3 +237,30 @@ def test_state_dtype_errors():
     st = capi.m3_state_t(FAKE, FAKE, FAKE, FAKE)
     assert capi.m3_ssm_decode_step(_shape(state_dtype=5), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                                    FAKE, st, FAKE, None) == capi.M3_ERR_INVALID_ARGUMENT
+
+
+def test_backward_errors():
+    """Validation of the backward entry (include/m3_ssm_backward.h)."""
+    W = capi.M3_ERR_WORKSPACE
+    g = capi.m3_grads_t(*([FAKE] * 7 + [None] * 4))
+
+    def bwd(shape, **over):
+        args = dict(x=FAKE, dt=FAKE, A=FAKE, lam=FAKE, theta=FAKE, B=FAKE, C=FAKE, init=None, gy=FAKE,
+                    grads=g, workspace=FAKE, workspace_bytes=0, stream=None)
+        args.update(over)
+        return capi.m3_ssm_prefill_backward(shape, **args)
+
+    assert bwd(_shape()) == W
+    assert capi.m3_ssm_prefill_backward_workspace_bytes(_shape()) > 0
+    assert bwd(_shape(nheads=6, ngroups=2)) == capi.M3_ERR_UNSUPPORTED
+    assert bwd(_shape(state_dtype=capi.M3_DTYPE_BF16)) == capi.M3_ERR_UNSUPPORTED
+    assert capi.m3_ssm_prefill_backward_workspace_bytes(_shape(nheads=6, ngroups=3)) == 0
+    assert bwd(_shape(), gy=None) == capi.M3_ERR_INVALID_ARGUMENT
+    assert bwd(_shape(), grads=None) == capi.M3_ERR_INVALID_ARGUMENT
+    for i in range(7):
+        ptrs = [FAKE] * 7 + [None] * 4
+        ptrs[i] = None
+        assert bwd(_shape(), grads=capi.m3_grads_t(*ptrs)) == capi.M3_ERR_INVALID_ARGUMENT
+    assert bwd(_shape(), grads=capi.m3_grads_t(*([FAKE] * 7 + [FAKE_MISALIGNED, None, None, None]))) \
+        == capi.M3_ERR_INVALID_ARGUMENT
+    assert bwd(_shape(dstate=5)) == capi.M3_ERR_INVALID_ARGUMENT
