@@ -79,6 +79,30 @@ def output_useful_flops(b, T, H, P, N, R):
     return total * b * H
 
 
+def backward_bytes(b, T, H, P, N, R, s=2):
+    """Inputs (x, gy, B, C, theta, dt, lam) read once, fp32 gradients written once."""
+    K = N // 2
+    rd = 2 * R * P * s + 2 * R * N * s + K * s + 2 * s
+    wr = 4 * (R * P + 2 * R * N + K + 2)
+    return b * T * H * (rd + wr)
+
+
+def time_backward(torch, mixer, inp, reps=3):
+    args = [inp[k] for k in ("x", "dt", "A", "lam", "theta", "B", "C")]
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    gy = torch.randn(inp["x"].shape, generator=g, device="cuda").to(inp["x"].dtype)
+    mixer.backward(*args, gy)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        mixer.backward(*args, gy)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
 def decode_bytes_per_step(b, H, P, N, R, s=2, state_bytes=4):
     K = N // 2
     per = (2 * N * P * state_bytes + 2 * R * N * 4 + 2 * R * P * s + 2 * K * 4
@@ -294,6 +318,7 @@ def main():
                     help="skip the workloads with the block prologue/epilogue")
     ap.add_argument("--no-bf16-state", action="store_true",
                     help="skip the decode workload with a bf16 carried state")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward pass")
     ap.add_argument("--no-groups", action="store_true",
                     help="skip the SISO workload with B/C shared by all heads")
     ap.add_argument("--long", action="store_true", help="also run the T=65536 MIMO prefill")
@@ -400,6 +425,16 @@ def main():
         torch.cuda.empty_cache()
         inp = synth.torch_inputs(b, T, H, P, N, R, io="bf16", seed=0)
 
+    if not args.no_backward:
+        msb = time_backward(torch, mixer, inp)
+        bb = backward_bytes(b, T, H, P, N, R)
+        result["backward_siso_prefill"] = {
+            "workload": c1["name"], "ms_per_call": round(msb, 3),
+            "tokens_per_s": round(b * T / (msb / 1000), 1), "alg_bytes": bb,
+            "frac_of_hbm_peak_at_alg_bytes": round(bb / (msb / 1000) / 1e9 / HBM_PEAK_GBS, 4),
+            "note": "sequential adjoint per (batch, head); bound by the per-token dependency chain"}
+        log(f"[siso backward] {msb:.3f} ms/call")
+
     if not args.no_cpu:
         log("[cpu baseline] timing the fp64 oracle on a sample ...")
         result["cpu_baseline"] = cpu_baseline(torch, inp, args.cpu_budget)
@@ -415,6 +450,13 @@ def main():
         inp = synth.torch_inputs(b2, T2, H2, P2, N2, R2, io="bf16", seed=0)
         ms2, _, pk2 = time_prefill(torch, mixer, inp, args.steps, args.warmup)
         ms2b = None
+        if not args.no_backward:
+            msw = time_backward(torch, mixer, inp)
+            result["backward_mimo_prefill"] = {
+                "workload": c2["name"], "ms_per_call": round(msw, 3),
+                "tokens_per_s": round(b2 * T2 / (msw / 1000), 1),
+                "alg_bytes": backward_bytes(b2, T2, H2, P2, N2, R2)}
+            log(f"[mimo backward] {msw:.3f} ms/call")
         if not args.no_block:
             blk, z = block_params(torch, H2, R2, N2, inp["x"].shape)
             ms2b, _, _ = time_prefill(torch, mixer, inp, args.steps, args.warmup, block=blk, z=z)
