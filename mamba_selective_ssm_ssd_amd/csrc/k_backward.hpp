@@ -33,6 +33,8 @@
 
 namespace m3 {
 
+constexpr int kQB = kBwdQ; // tokens per recomputed stretch
+
 // Threads per workgroup: 512 for the larger MIMO states (measured on the
 // b4 T2048 H64 P64 N64 R4 workload: 14.7 vs 17.8 ms), else 256 (SISO N128:
 // 11.1 vs 12.1 ms).
@@ -49,9 +51,9 @@ struct BwdCfg {
     static constexpr int t_dt = t_th + K, t_lam = t_dt + 1, TB = (t_lam + 1 + 3) / 4 * 4;
     static constexpr int SV = t_lam + 1;                 // staged values per token
     static constexpr int SVPT = (SV + kBT - 1) / kBT;
-    // LDS (floats): two token buffers, cos/sin table [65][K] float2, dx
+    // LDS (floats): two token buffers, cos/sin table [kQB + 1][K] float2, dx
     // partials [RG][R][P], dB~ and dC~ [R][N], scalar partials
-    static constexpr int o_tok = 0, o_cs = 2 * TB, o_red = o_cs + 2 * 65 * K;
+    static constexpr int o_tok = 0, o_cs = 2 * TB, o_red = o_cs + 2 * (kQB + 1) * K;
     static constexpr int o_gb = o_red + RG * R * P, o_gc = o_gb + R * N, o_sc = o_gc + R * N;
     static constexpr int floats = o_sc + 4 * (kBT / kWave);
     static constexpr size_t bytes = size_t(floats) * 4;
@@ -210,7 +212,7 @@ __global__ __launch_bounds__(bwd_threads(N, P, R)) void k_backward(const BwdPara
     const int nC = p.nC;
     float *ckh = p.ck_h + bh * nC * int64_t(N) * P;
     double *ckp = p.ck_phi + bh * nC * int64_t(K);
-    float *slab = p.slab + bh * 65 * int64_t(N) * P;
+    float *slab = p.slab + bh * (kQB + 1) * int64_t(N) * P;
     if (p.has_init) ld_state(p.h0 + bh * int64_t(N) * P, hv);
     else
 #pragma unroll
@@ -220,7 +222,7 @@ __global__ __launch_bounds__(bwd_threads(N, P, R)) void k_backward(const BwdPara
     for (int c = 0; c < nC; ++c) {
         st_state(ckh + c * int64_t(N) * P, hv);
         if (tid < K) ckp[c * K + tid] = phi;
-        forward(int64_t(c) * kQ, min<int64_t>(T, int64_t(c + 1) * kQ), nullptr);
+        forward(int64_t(c) * kQB, min<int64_t>(T, int64_t(c + 1) * kQB), nullptr);
     }
 
     // ---- backward, chunk by chunk
@@ -231,7 +233,7 @@ __global__ __launch_bounds__(bwd_threads(N, P, R)) void k_backward(const BwdPara
     double acc = 0.0;         // running sum of dPhi (owners of a pair)
     float gA = 0.f;
     for (int c = nC - 1; c >= 0; --c) {
-        const int64_t t0 = int64_t(c) * kQ, t1 = min<int64_t>(T, t0 + kQ);
+        const int64_t t0 = int64_t(c) * kQB, t1 = min<int64_t>(T, t0 + kQB);
         const int Tc = int(t1 - t0);
         // recompute the chunk's states from its checkpoint
         __syncthreads();

@@ -94,13 +94,13 @@ struct BwdLayout {
 };
 BwdLayout bwd_layout(const m3_shape_t *s) {
     const size_t bh = size_t(s->batch) * size_t(s->nheads);
-    const size_t nC = size_t((s->seqlen + 63) / 64);
+    const size_t nC = size_t((s->seqlen + m3::kBwdQ - 1) / m3::kBwdQ);
     const size_t N = size_t(s->dstate), P = size_t(s->headdim), K = N / 2;
     BwdLayout w;
     size_t off = 0;
     w.ck_h = off; off += round_up(bh * nC * N * P * sizeof(float));
     w.ck_phi = off; off += round_up(bh * nC * K * sizeof(double));
-    w.slab = off; off += round_up(bh * 65 * N * P * sizeof(float));
+    w.slab = off; off += round_up(bh * (m3::kBwdQ + 1) * N * P * sizeof(float));
     w.gA = off; off += round_up(bh * sizeof(float));
     w.total = off;
     return w;
@@ -372,7 +372,7 @@ m3_status_t m3_ssm_prefill_backward(const m3_shape_t *shape, const void *x, cons
     p.N = shape->dstate;
     p.R = shape->rank;
     p.K = p.N / 2;
-    p.nC = int32_t((p.T + 63) / 64);
+    p.nC = int32_t((p.T + m3::kBwdQ - 1) / m3::kBwdQ);
     p.x = x; p.dt = dt; p.lam = lam; p.theta = theta; p.B = B; p.C = C; p.gy = gy; p.A = A;
     p.has_init = init != nullptr;
     if (init) {
