@@ -178,31 +178,48 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode
         for (int j = 0; j < SPT; ++j) hv[j] = hs[j * kThreads + tslot];
     };
 
-    // item = (batch, head); gitem = (batch, B/C group of the head)
-    auto step = [&](const int64_t item, const int64_t gitem, const int h, const HV *hc, HV *hx) {
-        // ---- issue: small vectors of this item, then the next item's state
+    // The small vectors of an item, as loaded (raw bits).  They are loaded one
+    // item ahead, with that item's state, so an item's step never waits for
+    // a load issued in the same step.
+    struct Small {
         uint4 ud[UPT];
         uint2 ut[UPT];
         float ph[UPT][NPU];
+        uint32_t dt_raw, lam_raw;
+        float Ah;
+    };
+    // item = (batch, head); gitem = (batch, B/C group of the head)
+    auto load_small = [&](const int64_t item, const int64_t gitem, const int h, Small &sv) {
 #pragma unroll
         for (int j = 0; j < UPT; ++j) {
             const int64_t st = ukind[j] == kUnitBp ? sBp : (ukind[j] == kUnitX || ukind[j] == kUnitXp) ? sX : sB;
             // B, C units (and threads without a unit, which read B's first
             // unit) are rows of the item's B/C group
             const bool grp = ukind[j] <= kUnitC || ukind[j] == kUnitNone;
-            ud[j] = *reinterpret_cast<const uint4 *>(ubase[j] + (grp ? gitem : item) * st);
-            ut[j] = *reinterpret_cast<const uint2 *>(static_cast<const IO *>(p.theta) + item * K + uk0[j]);
+            sv.ud[j] = *reinterpret_cast<const uint4 *>(ubase[j] + (grp ? gitem : item) * st);
+            sv.ut[j] = *reinterpret_cast<const uint2 *>(static_cast<const IO *>(p.theta) + item * K + uk0[j]);
             if constexpr (NPU == 4) {
                 const float4 a = *reinterpret_cast<const float4 *>(p.phi + item * K + uk0[j]);
-                ph[j][0] = a.x; ph[j][1] = a.y; ph[j][2] = a.z; ph[j][3] = a.w;
+                sv.ph[j][0] = a.x; sv.ph[j][1] = a.y; sv.ph[j][2] = a.z; sv.ph[j][3] = a.w;
             } else {
                 const float2 a = *reinterpret_cast<const float2 *>(p.phi + item * K + uk0[j]);
-                ph[j][0] = a.x; ph[j][1] = a.y;
+                sv.ph[j][0] = a.x; sv.ph[j][1] = a.y;
             }
         }
-        const uint32_t dt_raw = io<IO>::raw(static_cast<const IO *>(p.dt) + item);
-        const uint32_t lam_raw = io<IO>::raw(static_cast<const IO *>(p.lam) + item);
-        const float Ah = p.A[h];
+        sv.dt_raw = io<IO>::raw(static_cast<const IO *>(p.dt) + item);
+        sv.lam_raw = io<IO>::raw(static_cast<const IO *>(p.lam) + item);
+        sv.Ah = p.A[h];
+    };
+
+    // one item: cur holds its small vectors and hc its state; the next item's
+    // (ni, ngi, nh) small vectors go to nxt and its state to hx
+    auto step = [&](const int64_t item, const int h, const Small &cur, Small &nxt, const int64_t ni,
+                    const int64_t ngi, const int nh, const HV *hc, HV *hx) {
+        const uint4 *ud = cur.ud;
+        const uint2 *ut = cur.ut;
+        const auto &ph = cur.ph;
+        const uint32_t dt_raw = cur.dt_raw, lam_raw = cur.lam_raw;
+        const float Ah = cur.Ah;
         // (BLK) weight and bias of each unit's channels and the gate input of
         // this thread's outputs; a missing piece is read from a valid stand-in
         // (the item's state, x) and replaced by its neutral value below
@@ -223,8 +240,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode
             const IO *zs = static_cast<const IO *>(p.blk.z ? p.blk.z : p.x) + item * (R * P) + min(4 * tid, R * P - 4);
             zr = io4<IO>::load(zs);
         }
-        const int64_t nx = item + gridDim.x < BH ? item + gridDim.x : item;
-        load_state(nx, hx);
+        // ---- issue the next item's small vectors and state
+        load_small(ni, ngi, nh, nxt);
+        load_state(ni, hx);
 
         // ---- rotate B and C (every unit computes the rotation; only B and C
         // units keep it), stage them and x, x_prev, B~_prev in LDS
@@ -365,12 +383,28 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode
         if (h >= p.H) h -= p.H, ++bi;
     };
     auto gitem = [&]() { return bi * p.G + h / p.hpg; };
+    // the item after this one (this one again past the last)
+    int64_t ni, ngi;
+    int nh;
+    auto peek = [&]() {
+        ni = item + gridDim.x;
+        int hh = h + hstep;
+        int64_t bb = bi + bstep;
+        if (hh >= p.H) hh -= p.H, ++bb;
+        if (ni >= BH) ni = item, hh = h, bb = bi;
+        nh = hh;
+        ngi = bb * p.G + hh / p.hpg;
+    };
+    Small sa, sb;
+    load_small(item, gitem(), h, sa);
     load_state(item, ha);
     for (;;) {
-        step(item, gitem(), h, ha, hb);
+        peek();
+        step(item, h, sa, sb, ni, ngi, nh, ha, hb);
         advance();
         if (item >= BH) break;
-        step(item, gitem(), h, hb, ha);
+        peek();
+        step(item, h, sb, sa, ni, ngi, nh, hb, ha);
         advance();
         if (item >= BH) break;
     }
