@@ -30,7 +30,7 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 METRIC = "Mamba-3 SSM prefill tokens/s + decode µs/step; % of MFMA / HBM peak"
 KERNELS = ("segment_state", "output")
 KERNEL_SOURCES = {"output": ["k_prefill.hpp", "m3_device.hpp", "m3_internal.hpp"],
-                  "decode_step": ["k_decode.hpp", "k_decode_bf16.hip", "k_decode_f32.hip", "m3_device.hpp", "m3_internal.hpp"]}
+                  "decode_step": ["k_decode.hpp", "k_decode_bf16.hip", "m3_device.hpp", "m3_internal.hpp"]}
 
 
 # ---------------------------------------------------------------------------
@@ -132,18 +132,22 @@ def load_traffic(kernel, workload):
 
 
 def record_traffic(fetch_csv, write_csv, copy_mib):
-    """Per-launch HBM bytes of the output pass on the SISO prefill workload from
-    two rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE, in
-    KiB per dispatch) that also ran --copy-calibration-mib COPY_MIB: each
-    counter is scaled by what it reads for that plain device copy (COPY_MIB
-    read and COPY_MIB written).  Writes profiles/output_<workload>_traffic.json
-    tagged with the sha256 of the kernel sources."""
+    """Per-launch HBM bytes of the prefill output pass (SISO workload) and of
+    the decode step (MIMO decode workload) from two rocprofv3 --pmc runs of
+    this script (FETCH_SIZE, then WRITE_SIZE, in KiB per dispatch) that also
+    ran --copy-calibration-mib COPY_MIB: each counter is scaled by what it
+    reads for that plain device copy (COPY_MIB read and COPY_MIB written).
+    Writes profiles/<kernel>_<workload>_traffic.json for each kernel the runs
+    hold, tagged with the sha256 of the kernel sources."""
     import csv
     from mamba_selective_ssm_ssd_amd import synth
-    c1 = synth.CONFIGS[1]
-    tag = f"k_prefill<m3::bf16, {c1['N']}, {c1['P']}, {c1['R']}, true, false>"
+    c1, c4 = synth.CONFIGS[1], synth.CONFIGS[4]
+    kernels = {
+        "output": (f"k_prefill<m3::bf16, {c1['N']}, {c1['P']}, {c1['R']}, true, false>", c1["name"]),
+        "decode_step": (f"k_decode_step<m3::bf16, {c4['N']}, {c4['P']}, {c4['R']}, false, false>", c4["name"]),
+    }
 
-    def avg(path, counter):
+    def avg(path, counter, tag):
         kern, copy = [], []
         for r in csv.DictReader(open(path)):
             if r["Counter_Name"] != counter:
@@ -151,26 +155,31 @@ def record_traffic(fetch_csv, write_csv, copy_mib):
             v = float(r["Counter_Value"]) * 1024.0
             if tag in r["Kernel_Name"]:
                 kern.append(v)
-            elif "copyBuffer" in r["Kernel_Name"] and v > 0.25 * copy_mib * (1 << 20):
+            elif "copyBuffer" in r["Kernel_Name"]:
                 copy.append(v)
-        if not kern or not copy:
-            raise SystemExit(f"{path}: no {counter} rows for {tag} or for the calibration copy")
-        return sum(kern) / len(kern), sum(copy) / len(copy)
+        if not copy:
+            raise SystemExit(f"{path}: no {counter} rows for the calibration copy")
+        # the calibration copy is the largest copy of the run (others, such as
+        # filling the decode state, are smaller)
+        return (sum(kern) / len(kern) if kern else None), max(copy)
 
-    fk, fc = avg(fetch_csv, "FETCH_SIZE")
-    wk, wc = avg(write_csv, "WRITE_SIZE")
     nbytes = copy_mib * (1 << 20)
-    fs, ws = nbytes / fc, nbytes / wc
-    rec = {"kernel": tag, "workload": c1["name"],
-           "fetch_bytes_raw": fk, "write_bytes_raw": wk,
-           "calibration_copy_bytes": nbytes, "fetch_scale": fs, "write_scale": ws,
-           "hbm_read_bytes_per_launch": round(fk * fs), "hbm_write_bytes_per_launch": round(wk * ws),
-           "hbm_bytes_per_launch": round(fk * fs + wk * ws),
-           "sources_sha256": sources_digest(KERNEL_SOURCES["output"])}
-    out = os.path.join(ROOT, "profiles", f"output_{c1['name']}_traffic.json")
-    with open(out, "w") as f:
-        json.dump(rec, f, indent=1)
-    print(json.dumps(rec))
+    for key, (tag, workload) in kernels.items():
+        fk, fc = avg(fetch_csv, "FETCH_SIZE", tag)
+        wk, wc = avg(write_csv, "WRITE_SIZE", tag)
+        if fk is None or wk is None:
+            continue
+        fs, ws = nbytes / fc, nbytes / wc
+        rec = {"kernel": tag, "workload": workload,
+               "fetch_bytes_raw": fk, "write_bytes_raw": wk,
+               "calibration_copy_bytes": nbytes, "fetch_scale": fs, "write_scale": ws,
+               "hbm_read_bytes_per_launch": round(fk * fs), "hbm_write_bytes_per_launch": round(wk * ws),
+               "hbm_bytes_per_launch": round(fk * fs + wk * ws),
+               "sources_sha256": sources_digest(KERNEL_SOURCES[key])}
+        out = os.path.join(ROOT, "profiles", f"{key}_{workload}_traffic.json")
+        with open(out, "w") as f:
+            json.dump(rec, f, indent=1)
+        print(json.dumps(rec))
 
 
 # ---------------------------------------------------------------------------
