@@ -1,434 +1,707 @@
-// k_backward.hpp -- gradients of the mixer: one workgroup per (batch, head),
-// sequential in time (the adjoint recurrence), fp32 arithmetic, fp64 angles.
+// k_backward.hpp -- gradients of the mixer in chunked form: one workgroup per
+// (batch, head), chunks of Q tokens processed last to first, every product
+// of a chunk on fp32 MFMA (v_mfma_f32_16x16x4_f32), angles in fp64.
 //
-// The forward map is the rotated-frame form of the Mamba-3 review, section
-// 3.2.2, Prop. 3.2.3, with the coefficients of section 3.1.1, eq. (6), and
-// the rank-R products of section 3.3:
+// Forward map: the rotated-frame form of the Mamba-3 review, section 3.2.2,
+// Prop. 3.2.3, with the coefficients of section 3.1.1, eq. (6), and the
+// rank-R products of section 3.3:
 //   h~_t = a_t h~_{t-1} + b_t B~_{t-1} x_{t-1}^T + g_t B~_t x_t^T,  y_t = C~_t^T h~_t,
-//   B~_t = R(-Phi_t) B_t, C~_t = R(-Phi_t) C_t, Phi_t = Phi_{t-1} + theta_t,
-//   a_t = exp(dt_t A), b_t = (1 - lam_t) dt_t a_t, g_t = lam_t dt_t.
-// For L = sum <gy_t, y_t> the adjoint of h~_t is
-//   G_t = C~_t gy_t + a_{t+1} G_{t+1}                      (G_T = 0)
-// and, with M_t = g_t G_t + b_{t+1} G_{t+1},
-//   d a_t = <G_t, h~_{t-1}>,  d b_t = <G_t, B~_{t-1} x_{t-1}^T>,  d g_t = <G_t, B~_t x_t^T>,
-//   dB~_t = M_t x_t^T,  dx_t = B~_t^T M_t,  dC~_t = h~_t gy_t^T,
-//   dB_t = R(Phi_t) dB~_t (same for C), and per row pair k
-//   dPhi_t = sum_r (dB~[2k] B~[2k+1] - dB~[2k+1] B~[2k]) + (the same for C),
-//   dtheta_t = sum_{s >= t} dPhi_s,
-//   d dt = d a A a + d b (1 - lam)(a + dt A a) + d g lam,
-//   d lam = -d b dt a + d g dt,  dA = sum_t (d a dt a + d b (1 - lam) dt^2 a);
-// the carried state gets dh~_{-1} = a_0 G_0, dB~_{-1} = b_0 G_0 x_{-1}^T,
-// dx_{-1} = b_0 B~_{-1}^T G_0 and dPhi_{-1} = sum_t dPhi_t.
+//   B~_t = R(-Phi_t) B_t (same for C), Phi_t = Phi_{t-1} + theta_t,
+//   a_t = e^{l_t}, l_t = dt_t A, b_t = d_t a_t, d_t = (1 - lam_t) dt_t, g_t = lam_t dt_t.
+// Since b_{s+1} e^{-cum_{s+1}} = d_{s+1} e^{-cum_s}, token s enters h~_t
+// (t >= s) with weight e^{cum_t - cum_s} (g_s + [t > s] d_{s+1}): the two taps
+// of the trapezoid fold into one decay mask (the review, section 3.1.3,
+// eq. (7)), and the chunked SSD form of its section 2.3 applies.
 //
-// The states the adjoint needs are rebuilt chunk by chunk: a forward sweep
-// stores the state and angle at every chunk start (workspace), then for each
-// chunk, last to first, the chunk's states are recomputed into a per-sequence
-// slab (workspace) with their angles' cos/sin in LDS, and the chunk's tokens
-// are processed backwards.  Each thread owns float4 runs of the N x P state
-// (along P); the small per-token vectors are staged in LDS, the next token's
-// ones loaded into registers one step ahead.
+// A chunk holds V = Q R rows (token i, rank r -> row i R + r; rows past the
+// chunk's tokens are zero).  With ec_i the sum of l over the chunk's tokens
+// up to i, dn_j = d of token j + 1, and
+//   W(i,j) = [i >= j] e^{ec_i - ec_j} (g_j + [i > j] dn_j),
+//   U_j = e^{ec_end - ec_j} (g_j + dn_j),  E_i = e^{ec_i},
+//   H_c = h~_{t0-1} + d_{t0} B~_{t0-1} x_{t0-1}^T  (the state entering the chunk),
+// the forward is y_v = sum_v' W S(v,v') x_v' + E_i C~_v^T H_c with S = C~ B~^T,
+// and H_{c+1} = e^{ec_end} H_c + sum_v' U_j B~_v' x_v'^T.  Given G, the
+// gradient of H_{c+1} (zero after the last chunk), and D = gy x^T:
+//   dx  = (W.S)^T gy + diag(U) B~ G,     dC~ = (W.D) B~ + diag(E) gy H_c^T,
+//   dB~ = (W.D)^T C~ + diag(U) x G^T,    dH_c = e^{ec_end} G + C~^T diag(E) gy,
+//   dW(i,j) = sum over the R x R block of S.D,  dU_j = <G, B~_j x_j^T>,
+//   dE_i = <C~_i, H_c gy_i>,  d e^{ec_end} = <G, H_c>,
+// and the chain rule through W, U and E gives the gradient of each ec_k,
+// whose suffix sums over the chunk are the gradients of l.  The rotations give
+// dB = R(Phi) dB~ (same for C) and dPhi_t[k] = sum_r (dB~_2k B~_2k+1 -
+// dB~_2k+1 B~_2k) + (the same for C); dtheta_t = sum_{s >= t} dPhi_s.  The
+// carried state gets dh~_{-1} = dH_0, dB~_{-1} = d_0 dH_0 x_{-1},
+// dx_{-1} = d_0 B~_{-1}^T dH_0, dPhi_{-1} = sum_t dPhi_t, and d_0 receives
+// <dH_0, B~_{-1} x_{-1}^T>.
+//
+// Two sweeps per workgroup: forward over the chunks storing H_c and the
+// angle at each chunk start (workspace), then backward over the chunks.
+// MFMA operand convention: in step (kb, e) of a product, k-slot g of lane l
+// stands for contraction index 16 kb + 4 g + e.  An operand in LDS is stored
+// with the contraction index as its row ("k-major", pitch = 4 mod 16: no
+// bank conflicts), and a 16 x 16 accumulator tile (lane l holds rows
+// 4 (l / 16) + e of column l % 16) is the B operand of step (kb, e) as it
+// stands, which keeps the carried gradient G (in both orientations) and H_c
+// in registers.
 #pragma once
 #include "m3_device.hpp"
 #include "m3_internal.hpp"
 
 namespace m3 {
 
-constexpr int kQB = kBwdQ; // tokens per recomputed stretch
+constexpr int kBwdThreads = 256; // 4 waves, one per SIMD
 
-// Threads per workgroup: 512 for the larger MIMO states (measured on the
-// b4 T2048 H64 P64 N64 R4 workload: 14.7 vs 17.8 ms), else 256 (SISO N128:
-// 11.1 vs 12.1 ms).
-constexpr int bwd_threads(int N, int P, int R) { return R >= 2 && N * P >= 4096 ? 512 : 256; }
+// v_mfma_f32_16x16x4_f32: lane l supplies A[l % 16][slot l / 16] and
+// B[slot l / 16][l % 16]; element e of the result is D[4 (l / 16) + e][l % 16].
+__device__ __forceinline__ floatx4 mfma4(float a, float b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// acc[vb] += A B for NV row blocks of A (vb = 0 .. NV-1), contraction length
+// KD: A[i][k] = a[k * PA + 16 vb + i], B[k][j] = bm[k * PBM + j].
+template <int KD, int PA, int PBM, int NV>
+__device__ __forceinline__ void mm_lds(floatx4 (&acc)[NV], const float *a, const float *bm, int i, int g) {
+#pragma unroll
+    for (int kb = 0; kb < KD / 16; ++kb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int k = kb * 16 + 4 * g + e;
+            const float bv = bm[k * PBM + i];
+#pragma unroll
+            for (int vb = 0; vb < NV; ++vb) acc[vb] = mfma4(a[k * PA + 16 * vb + i], bv, acc[vb]);
+        }
+}
+
+__device__ __forceinline__ floatx4 zero4() { return floatx4{0.f, 0.f, 0.f, 0.f}; }
 
 template <int N, int P, int R>
 struct BwdCfg {
-    static constexpr int N_ = N, P_ = P, R_ = R;
-    static constexpr int kBT = bwd_threads(N, P, R);
-    static constexpr int K = N / 2, P4 = P / 4, RG = kBT / P4;
-    static constexpr int SLOTS = N * P / 4, SPT = (SLOTS + kBT - 1) / kBT;
-    // token buffer (floats): B~ [R][N], C~ [R][N], x [R][P], gy [R][P], theta [K], dt, lam
-    static constexpr int t_b = 0, t_c = R * N, t_x = 2 * R * N, t_gy = t_x + R * P, t_th = t_gy + R * P;
-    static constexpr int t_dt = t_th + K, t_lam = t_dt + 1, TB = (t_lam + 1 + 3) / 4 * 4;
-    static constexpr int SV = t_lam + 1;                 // staged values per token
-    static constexpr int SVPT = (SV + kBT - 1) / kBT;
-    // LDS (floats): two token buffers, cos/sin table [kQB + 1][K] float2, dx
-    // partials [RG][R][P], dB~ and dC~ [R][N], scalar partials
-    static constexpr int o_tok = 0, o_cs = 2 * TB, o_red = o_cs + 2 * (kQB + 1) * K;
-    static constexpr int o_gb = o_red + RG * R * P, o_gc = o_gb + R * N, o_sc = o_gc + R * N;
-    static constexpr int floats = o_sc + 4 * (kBT / kWave);
+    static constexpr int V = kBwdV, Q = V / R, VQ = Q * R, QP = Q + 1;
+    static constexpr int K = N / 2, NB = N / 16, PB = P / 16, VB = V / 16, NBW = (NB + 3) / 4;
+    static constexpr int pV = V + 4, pN = N + 4, pP = P + 4, pQ = QP + 1, SQ = 36;
+    static constexpr int TPS = (Q + 7) / 8; // tokens per segment of the angle prefix
+    // token scalar tables, SQ floats each
+    static constexpr int s_ec = 0, s_E = 1, s_EU = 2, s_U = 3, s_g = 4, s_dn = 5, s_dt = 6, s_lam = 7, s_misc = 8;
+    // LDS (floats)
+    static constexpr int o_bt = 0;              // B~ [N][pV]
+    static constexpr int o_ct = o_bt + N * pV;  // C~ [N][pV]
+    static constexpr int o_bn = o_ct + N * pV;  // B~ [V][pN]
+    static constexpr int o_cn = o_bn + V * pN;  // C~ [V][pN]
+    static constexpr int o_xt = o_cn + V * pN;  // x  [P][pV]
+    static constexpr int o_gt = o_xt + P * pV;  // gy [P][pV]
+    static constexpr int o_gn = o_gt + P * pV;  // gy [V][pP]  (forward sweep: x)
+    static constexpr int o_ms = o_gn + V * pP;  // W.S [V][pV]  (row v, column v')
+    static constexpr int o_mn = o_ms + V * pV;  // W.D [V][pV]
+    static constexpr int o_mt = o_mn + V * pV;  // W.D [V][pV]  (row v', column v)
+    static constexpr int o_sd = o_mt + V * pV;  // S.D [V][pV]
+    static constexpr int o_ph = o_sd + V * pV;  // dPhi terms [V][K]
+    static constexpr int o_tf = o_ph + V * K;   // Phi in turns [Q][K]
+    static constexpr int o_et = o_tf + Q * K;   // e^{ec_i - ec_j} [QP][pQ]
+    static constexpr int o_dw = o_et + QP * pQ; // dW [Q][pQ]
+    static constexpr int o_sc = o_dw + Q * pQ;  // token scalars [9][SQ]
+    static constexpr int o_pu = o_sc + 9 * SQ;  // dU partials [4][V]
+    static constexpr int o_pe = o_pu + 4 * V;   // dE partials [4][V]
+    static constexpr int o_pz = o_pe + 4 * V;   // per-wave scalars [4][4]
+    static constexpr int o_phe = (o_pz + 16 + 1) / 2 * 2; // Phi at the chunk end, fp64 [K]
+    static constexpr int floats = o_phe + 2 * K;
     static constexpr size_t bytes = size_t(floats) * 4;
+    static_assert(bytes <= kMaxLdsBytes, "backward LDS layout exceeds the workgroup's LDS");
+    // 4-element groups of B / C and of x / gy per chunk, per thread
+    static constexpr int NBL = (V * N / 4 + kBwdThreads - 1) / kBwdThreads;
+    static constexpr int NXL = (V * P / 4 + kBwdThreads - 1) / kBwdThreads;
 };
 
-// Raw bits of one staged value of token t (t = -1: the carried previous
-// token; values absent there read as zero).  The index is clamped, so every
-// thread issues its loads.
-template <class Cf, typename IO>
-__device__ __forceinline__ uint32_t bwd_raw(const BwdParams &p, int64_t b, int h, int64_t t, int e) {
-    constexpr int R = Cf::R_, N = Cf::N_, P = Cf::P_, K = Cf::K;
-    const int i = min(e, Cf::SV - 1);
-    if (t < 0) {
-        const int64_t bh = b * p.H + h;
-        if (!p.has_init || (i >= Cf::t_c && i < Cf::t_x) || i >= Cf::t_gy) return 0u;
-        if (i < Cf::t_c) return __float_as_uint(p.prevB0[bh * R * N + i]);
-        return io<IO>::raw(static_cast<const IO *>(p.prevx0) + bh * R * P + (i - Cf::t_x));
-    }
-    const int64_t tok = (b * p.T + t) * p.H + h;
-    if (i < Cf::t_c) return io<IO>::raw(static_cast<const IO *>(p.B) + tok * R * N + i);
-    if (i < Cf::t_x) return io<IO>::raw(static_cast<const IO *>(p.C) + tok * R * N + (i - Cf::t_c));
-    if (i < Cf::t_gy) return io<IO>::raw(static_cast<const IO *>(p.x) + tok * R * P + (i - Cf::t_x));
-    if (i < Cf::t_th) return io<IO>::raw(static_cast<const IO *>(p.gy) + tok * R * P + (i - Cf::t_gy));
-    if (i < Cf::t_dt) return io<IO>::raw(static_cast<const IO *>(p.theta) + tok * K + (i - Cf::t_th));
-    if (i == Cf::t_dt) return io<IO>::raw(static_cast<const IO *>(p.dt) + tok);
-    return io<IO>::raw(static_cast<const IO *>(p.lam) + tok);
-}
-
 template <typename IO, int N, int P, int R>
-__global__ __launch_bounds__(bwd_threads(N, P, R)) void k_backward(const BwdParams p) {
+__global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
     typedef BwdCfg<N, P, R> Cf;
-    constexpr int kBT = Cf::kBT;
-    constexpr int K = Cf::K, P4 = Cf::P4, RG = Cf::RG, SLOTS = Cf::SLOTS, SPT = Cf::SPT, SVPT = Cf::SVPT;
-    constexpr int TB = Cf::TB;
+    constexpr int V = Cf::V, Q = Cf::Q, VQ = Cf::VQ, QP = Cf::QP, K = Cf::K;
+    constexpr int NB = Cf::NB, PB = Cf::PB, VB = Cf::VB, NBW = Cf::NBW, TPS = Cf::TPS;
+    constexpr int pV = Cf::pV, pN = Cf::pN, pP = Cf::pP, pQ = Cf::pQ, SQ = Cf::SQ;
+    constexpr int NBL = Cf::NBL, NXL = Cf::NXL;
     extern __shared__ __align__(16) float sm[];
-    float2 *cs = reinterpret_cast<float2 *>(sm + Cf::o_cs);
-    float *red = sm + Cf::o_red, *gbs = sm + Cf::o_gb, *gcs = sm + Cf::o_gc, *scs = sm + Cf::o_sc;
+    float *BT = sm + Cf::o_bt, *CT = sm + Cf::o_ct, *BN = sm + Cf::o_bn, *CN = sm + Cf::o_cn;
+    float *XT = sm + Cf::o_xt, *GT = sm + Cf::o_gt, *GN = sm + Cf::o_gn;
+    float *MS = sm + Cf::o_ms, *MN = sm + Cf::o_mn, *MT = sm + Cf::o_mt, *SD = sm + Cf::o_sd;
+    float *PH = sm + Cf::o_ph, *TF = sm + Cf::o_tf, *ET = sm + Cf::o_et, *DW = sm + Cf::o_dw;
+    float *SC = sm + Cf::o_sc, *PU = sm + Cf::o_pu, *PE = sm + Cf::o_pe, *PZ = sm + Cf::o_pz;
+    double *PHE = reinterpret_cast<double *>(sm + Cf::o_phe);
+    auto sc = [&](int s, int i) -> float & { return SC[s * SQ + i]; };
 
-    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    // lane ids, re-derived through an opaque copy at the top of every chunk so
+    // that the per-lane addresses built from them are not hoisted out of the
+    // chunk loops (kept live across them, they exceed the register file)
+    int tid = threadIdx.x, lane = 0, w = 0, li = 0, lg = 0;
+    auto lane_ids = [&]() {
+        asm volatile("" : "+v"(tid));
+        lane = tid & (kWave - 1);
+        w = __builtin_amdgcn_readfirstlane(tid) / kWave;
+        li = lane & 15;
+        lg = lane >> 4;
+    };
+    lane_ids();
     const int64_t bh = blockIdx.x;
     const int h = int(bh % p.H);
     const int64_t b = bh / p.H;
-    const float Ah = p.A[h];
-    const int pg = tid % P4, rg = tid / P4;
-    const int tslot = min(tid, SLOTS - 1);
-    const bool own = tid < SLOTS || SLOTS % kBT == 0;
-
-    // ---- small-vector staging: raw bits of one token into registers, then
-    // into a token buffer as floats (B and C rotated in place by the owner of
-    // each row pair, unless the token is the carried one, already rotated)
-    auto tok_of = [&](int64_t t) -> float * { return sm + Cf::o_tok + (int(t & 1)) * TB; };
-    uint32_t rv[SVPT];
-    auto load_raw = [&](int64_t t) {
-#pragma unroll
-        for (int j = 0; j < SVPT; ++j) rv[j] = bwd_raw<Cf, IO>(p, b, h, t, tid + j * kBT);
-    };
-    auto store_raw = [&](int64_t t) {
-        float *tb = tok_of(t);
-#pragma unroll
-        for (int j = 0; j < SVPT; ++j) {
-            const int e = tid + j * kBT;
-            if (e >= Cf::SV) continue;
-            const bool fp = t < 0 && e < Cf::t_c; // carried B~ is fp32
-            tb[e] = fp ? __uint_as_float(rv[j]) : io<IO>::value(rv[j]);
-        }
-    };
-    // rotate token t's B and C by -Phi (cos/sin entry c)
-    auto rotate_tok = [&](int64_t t, float2 c) {
-        float *tb = tok_of(t);
-        const int k = tid;
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            rot_neg(c.x, c.y, tb[Cf::t_b + r * N + 2 * k], tb[Cf::t_b + r * N + 2 * k + 1]);
-            rot_neg(c.x, c.y, tb[Cf::t_c + r * N + 2 * k], tb[Cf::t_c + r * N + 2 * k + 1]);
-        }
-    };
-    auto cs_of = [](double a) {
-        float tf = float(a * (1.0 / kTwoPi));
-        tf -= rintf(tf);
-        return make_float2(__builtin_amdgcn_cosf(tf), __builtin_amdgcn_sinf(tf));
-    };
-    // coefficients of token t from its buffer
-    auto coef = [&](const float *tb, float &a, float &bt, float &g) {
-        const float d = tb[Cf::t_dt], l = tb[Cf::t_lam];
-        a = __expf(d * Ah);
-        bt = (1.f - l) * d * a;
-        g = l * d;
-    };
-
-    float4 hv[SPT];                 // running state (forward sweeps)
-    double phi = 0.0;               // Phi of the last processed token (owners of a pair)
-
-    // state of slot j into/out of a buffer of N x P floats
-    auto ld_state = [&](const float *src, float4 *dst) {
-#pragma unroll
-        for (int j = 0; j < SPT; ++j) dst[j] = reinterpret_cast<const float4 *>(src)[j * kBT + tslot];
-    };
-    auto st_state = [&](float *dstp, const float4 *src) {
-#pragma unroll
-        for (int j = 0; j < SPT; ++j)
-            if (own || j * kBT + tid < SLOTS) reinterpret_cast<float4 *>(dstp)[j * kBT + tid] = src[j];
-    };
-
-    // forward over tokens t0 .. t1-1 from hv, phi (token t0-1 staged and
-    // rotated in its buffer); writes cos/sin of Phi_t to cs[t - t0 + 1] and,
-    // with slab, the states after each token to slab[t - t0 + 1]
-    auto forward = [&](int64_t t0, int64_t t1, float *slab) {
-        load_raw(t0);
-        for (int64_t t = t0; t < t1; ++t) {
-            __syncthreads(); // buffer of token t is free (token t-2 consumed)
-            store_raw(t);
-            if (t + 1 < t1) load_raw(t + 1);
-            __syncthreads();
-            float *tb = tok_of(t);
-            if (tid < K) {
-                phi = wrap_angle(phi + double(tb[Cf::t_th + tid]));
-                const float2 c = cs_of(phi);
-                cs[int(t - t0 + 1) * K + tid] = c;
-                rotate_tok(t, c);
-            }
-            __syncthreads();
-            const float *tp = tok_of(t - 1);
-            float a, bb, g;
-            coef(tb, a, bb, g);
-#pragma unroll
-            for (int j = 0; j < SPT; ++j) {
-                const int slot = j * kBT + tslot;
-                const int n = slot / P4;
-                float u[4] = {a * hv[j].x, a * hv[j].y, a * hv[j].z, a * hv[j].w};
-#pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    const float cb = bb * tp[Cf::t_b + r * N + n], cg = g * tb[Cf::t_b + r * N + n];
-                    const float4 xp = *reinterpret_cast<const float4 *>(tp + Cf::t_x + r * P + 4 * pg);
-                    const float4 xc = *reinterpret_cast<const float4 *>(tb + Cf::t_x + r * P + 4 * pg);
-                    u[0] += cb * xp.x + cg * xc.x;
-                    u[1] += cb * xp.y + cg * xc.y;
-                    u[2] += cb * xp.z + cg * xc.z;
-                    u[3] += cb * xp.w + cg * xc.w;
-                }
-                hv[j] = make_float4(u[0], u[1], u[2], u[3]);
-            }
-            if (slab) st_state(slab + (t - t0 + 1) * int64_t(N) * P, hv);
-        }
-    };
-    // stage token t (t >= -1) synchronously, rotated with cos/sin entry c
-    auto stage_sync = [&](int64_t t, float2 c) {
-        load_raw(t);
-        __syncthreads();
-        store_raw(t);
-        __syncthreads();
-        if (tid < K && t >= 0) rotate_tok(t, c);
-    };
-
-    // ---- forward sweep: chunk-start checkpoints
     const int64_t T = p.T;
     const int nC = p.nC;
-    float *ckh = p.ck_h + bh * nC * int64_t(N) * P;
-    double *ckp = p.ck_phi + bh * nC * int64_t(K);
-    float *slab = p.slab + bh * (kQB + 1) * int64_t(N) * P;
-    if (p.has_init) ld_state(p.h0 + bh * int64_t(N) * P, hv);
-    else
-#pragma unroll
-        for (int j = 0; j < SPT; ++j) hv[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (tid < K) phi = p.has_init ? double(p.phi0[bh * K + tid]) : 0.0;
-    stage_sync(-1, make_float2(1.f, 0.f));
-    for (int c = 0; c < nC; ++c) {
-        st_state(ckh + c * int64_t(N) * P, hv);
-        if (tid < K) ckp[c * K + tid] = phi;
-        forward(int64_t(c) * kQB, min<int64_t>(T, int64_t(c + 1) * kQB), nullptr);
-    }
+    const float Ah = p.A[h];
+    const IO *xg = static_cast<const IO *>(p.x), *Bg = static_cast<const IO *>(p.B);
+    const IO *Cg = static_cast<const IO *>(p.C), *gyg = static_cast<const IO *>(p.gy);
+    const IO *thg = static_cast<const IO *>(p.theta), *dtg = static_cast<const IO *>(p.dt);
+    const IO *lmg = static_cast<const IO *>(p.lam);
+    auto tok = [&](int64_t t) { return (b * T + t) * p.H + h; };
+    float *ckh = p.ck_h + bh * int64_t(nC) * N * P;
+    double *ckp = p.ck_phi + bh * int64_t(nC) * K;
+    // this lane's slot in a chunk's stored state: tile (nb, pb), lane-major
+    auto ck_at = [&](int c, int nb, int pb) { return ckh + ((int64_t(c) * NB + nb) * PB + pb) * 256 + lane * 4; };
+    auto row_tok = [&](int v) { return min(v / R, Q); }; // token slot of a row (Q: padding)
 
-    // ---- backward, chunk by chunk
-    float4 Gn[SPT];
-#pragma unroll
-    for (int j = 0; j < SPT; ++j) Gn[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-    float a1 = 0.f, b1 = 0.f; // a_{t+1}, b_{t+1}
-    double acc = 0.0;         // running sum of dPhi (owners of a pair)
-    float gA = 0.f;
-    for (int c = nC - 1; c >= 0; --c) {
-        const int64_t t0 = int64_t(c) * kQB, t1 = min<int64_t>(T, t0 + kQB);
-        const int Tc = int(t1 - t0);
-        // recompute the chunk's states from its checkpoint
-        __syncthreads();
-        ld_state(ckh + c * int64_t(N) * P, hv);
-        if (tid < K) {
-            phi = ckp[c * K + tid];
-            cs[tid] = cs_of(phi);
+    // ---- staging: token scalars (wave 0, lane = token; lane Q carries the
+    // next chunk's first token for its d)
+    auto stage_scalars = [&](int64_t t0, int Tc) {
+        if (w == 0) {
+            const int i = lane;
+            const bool real = i < Tc, nxt = i == Q && t0 + Q < T;
+            float d = 0.f, l = 0.f;
+            if (real || nxt) {
+                d = io<IO>::get(dtg + tok(t0 + i));
+                l = io<IO>::get(lmg + tok(t0 + i));
+            }
+            const float ell = real ? d * Ah : 0.f;
+            const float gam = real ? l * d : 0.f;
+            const float dlt = real || nxt ? (1.f - l) * d : 0.f;
+            float dn = __shfl_down(dlt, 1);
+            if (i >= Q) dn = 0.f;
+            const float ec = wave_inclusive_sum(ell, lane);
+            const float ecE = __shfl(ec, Q - 1);
+            const float E = __expf(ec), EU = __expf(ecE - ec);
+            const float U = EU * (gam + dn);
+            if (i <= Q) {
+                sc(Cf::s_ec, i) = ec; sc(Cf::s_E, i) = E; sc(Cf::s_EU, i) = EU; sc(Cf::s_U, i) = U;
+                sc(Cf::s_g, i) = gam; sc(Cf::s_dn, i) = dn; sc(Cf::s_dt, i) = real ? d : 0.f;
+                sc(Cf::s_lam, i) = real ? l : 0.f;
+            }
+            if (i == 0) sc(Cf::s_misc, 0) = __expf(ecE);
         }
-        st_state(slab, hv);
-        __syncthreads();
-        stage_sync(t0 - 1, t0 >= 1 ? cs[tid < K ? tid : 0] : make_float2(1.f, 0.f));
-        forward(t0, t1, slab);
-        __syncthreads(); // slab and cos/sin table complete
-        // stage tokens t1-1 and t1-2 (rotated), the first two the loop reads
-        float4 hc[SPT], hp[SPT];
-        ld_state(slab + Tc * int64_t(N) * P, hc);
-        ld_state(slab + (Tc - 1) * int64_t(N) * P, hp);
-        stage_sync(t1 - 1, cs[Tc * K + (tid < K ? tid : 0)]);
-        stage_sync(t1 - 2, cs[(Tc - 1) * K + (tid < K ? tid : 0)]);
-        __syncthreads();
-        if (t1 - 3 >= t0 - 1) load_raw(t1 - 3);
-        for (int64_t t = t1 - 1; t >= t0; --t) {
-            const int i = int(t - t0);
-            const float *tb = tok_of(t), *tp = tok_of(t - 1);
-            float a, bb, g;
-            coef(tb, a, bb, g);
-            float4 hn[SPT];
-            if (i >= 1) ld_state(slab + (i - 1) * int64_t(N) * P, hn); // h~_{t-2}, next step's h~_{t-1}
-            float sa = 0.f, sb = 0.f, sg = 0.f;
-            float gxp[R][4];
+    };
+    // Phi_t = Phi_start + the sum of theta over the chunk's tokens up to t,
+    // fp64: lane = 8 segments x 8 pairs, a segment's prefix in registers, the
+    // segment totals scanned over lanes 8 apart.  Writes TF (turns, wrapped)
+    // and PHE (the wrapped angle of the chunk's last token).
+    auto stage_angles = [&](int64_t t0, int Tc, bool fwd, int c) {
 #pragma unroll
-            for (int r = 0; r < R; ++r)
+        for (int kp = 0; kp < K; kp += 32) {
+            const int k = kp + 8 * w + (lane & 7), seg = lane >> 3;
+            const bool kv = k < K;
+            const int kc = kv ? k : 0;
+            const double ph0 = fwd ? PHE[kc] : ckp[int64_t(c) * K + kc];
+            double lp[TPS];
+            double run = 0.0;
 #pragma unroll
-                for (int q = 0; q < 4; ++q) gxp[r][q] = 0.f;
+            for (int u = 0; u < TPS; ++u) {
+                const int i = seg * TPS + u;
+                const bool ok = kv && i < Tc;
+                const float th = io<IO>::get(thg + tok(t0 + (ok ? i : 0)) * K + kc);
+                run += ok ? double(th) : 0.0;
+                lp[u] = run;
+            }
+            double x = run;
 #pragma unroll
-            for (int j = 0; j < SPT; ++j) {
-                const int slot = j * kBT + tslot;
-                const int n = slot / P4;
-                float G[4] = {a1 * Gn[j].x, a1 * Gn[j].y, a1 * Gn[j].z, a1 * Gn[j].w};
-                float bx[4] = {0.f, 0.f, 0.f, 0.f}, bxp[4] = {0.f, 0.f, 0.f, 0.f};
-                float4 xr[R], gyr[R];
+            for (int o = 8; o < kWave; o <<= 1) {
+                const double y = __shfl_up(x, o, kWave);
+                if (lane >= o) x += y;
+            }
+            const double ex = x - run;
+            if (fwd && kv && seg == 0) ckp[int64_t(c) * K + k] = ph0;
 #pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    xr[r] = *reinterpret_cast<const float4 *>(tb + Cf::t_x + r * P + 4 * pg);
-                    gyr[r] = *reinterpret_cast<const float4 *>(tb + Cf::t_gy + r * P + 4 * pg);
-                    const float4 xq = *reinterpret_cast<const float4 *>(tp + Cf::t_x + r * P + 4 * pg);
-                    const float cc = tb[Cf::t_c + r * N + n], bc = tb[Cf::t_b + r * N + n], bq = tp[Cf::t_b + r * N + n];
-                    G[0] += cc * gyr[r].x; G[1] += cc * gyr[r].y; G[2] += cc * gyr[r].z; G[3] += cc * gyr[r].w;
-                    bx[0] += bc * xr[r].x; bx[1] += bc * xr[r].y; bx[2] += bc * xr[r].z; bx[3] += bc * xr[r].w;
-                    bxp[0] += bq * xq.x; bxp[1] += bq * xq.y; bxp[2] += bq * xq.z; bxp[3] += bq * xq.w;
+            for (int u = 0; u < TPS; ++u) {
+                const int i = seg * TPS + u;
+                if (kv && i < Q) {
+                    const double ph = ph0 + ex + lp[u];
+                    double tr = ph * (1.0 / kTwoPi);
+                    tr -= rint(tr);
+                    TF[i * K + k] = float(tr);
+                    if (i == Tc - 1) PHE[k] = wrap_angle(ph);
                 }
-                const float hq[4] = {hp[j].x, hp[j].y, hp[j].z, hp[j].w};
-                const float gn[4] = {Gn[j].x, Gn[j].y, Gn[j].z, Gn[j].w};
-                const float hcv[4] = {hc[j].x, hc[j].y, hc[j].z, hc[j].w};
-                float M[4];
-                const bool live = own || slot == j * kBT + tid;
+            }
+        }
+    };
+    // B (and C) of the chunk into registers, four elements per group, row
+    // v = group % V fastest (rows past the chunk's tokens read as zero)
+    float rb[NBL][4], rc[NBL][4];
+    auto load_bc = [&](int64_t t0, int Tc, bool withC) {
+#pragma unroll
+        for (int j = 0; j < NBL; ++j) {
+            const int gi = tid + j * kBwdThreads;
+            const int v = gi % V, n = 4 * (gi / V), i = v / R;
+            const bool ok = gi < V * N / 4 && v < VQ && i < Tc;
+            const int64_t off = ok ? tok(t0 + i) * (R * N) + (v - i * R) * N + n : 0;
+            float vb[4], vc[4];
+            io<IO>::load4(Bg + off, vb);
+            if (withC) io<IO>::load4(Cg + off, vc);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                rb[j][q] = ok ? vb[q] : 0.f;
+                rc[j][q] = ok && withC ? vc[q] : 0.f;
+            }
+        }
+    };
+    // rotate by -Phi (TF) and store k-major (dT, [n][v]) and row-major (dN, [v][n])
+    auto rot_store = [&](float (&rv)[NBL][4], float *dT, float *dN) {
+#pragma unroll
+        for (int j = 0; j < NBL; ++j) {
+            const int gi = tid + j * kBwdThreads;
+            if (gi >= V * N / 4) continue;
+            const int v = gi % V, n = 4 * (gi / V), i = min(v / R, Q - 1);
+            const float f0 = TF[i * K + n / 2], f1 = TF[i * K + n / 2 + 1];
+            float o[4] = {rv[j][0], rv[j][1], rv[j][2], rv[j][3]};
+            rot_neg(__builtin_amdgcn_cosf(f0), __builtin_amdgcn_sinf(f0), o[0], o[1]);
+            rot_neg(__builtin_amdgcn_cosf(f1), __builtin_amdgcn_sinf(f1), o[2], o[3]);
+            if (dN) *reinterpret_cast<float4 *>(dN + v * pN + n) = make_float4(o[0], o[1], o[2], o[3]);
+            if (dT)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) dT[(n + q) * pV + v] = o[q];
+        }
+    };
+    // x (and gy) of the chunk into LDS: the forward sweep keeps x row-major
+    // in GN; the backward sweep keeps x k-major (XT) and gy both ways (GT, GN)
+    auto stage_xg = [&](int64_t t0, int Tc, bool fwd) {
+#pragma unroll
+        for (int j = 0; j < NXL; ++j) {
+            const int gi = tid + j * kBwdThreads;
+            if (gi >= V * P / 4) continue;
+            const int v = gi % V, pc = 4 * (gi / V), i = v / R;
+            const bool ok = v < VQ && i < Tc;
+            const int64_t off = ok ? tok(t0 + i) * (R * P) + (v - i * R) * P + pc : 0;
+            float xv[4], gv[4];
+            io<IO>::load4(xg + off, xv);
+            if (!fwd) io<IO>::load4(gyg + off, gv);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                xv[q] = ok ? xv[q] : 0.f;
+                gv[q] = ok && !fwd ? gv[q] : 0.f;
+            }
+            if (fwd) {
+                *reinterpret_cast<float4 *>(GN + v * pP + pc) = make_float4(xv[0], xv[1], xv[2], xv[3]);
+            } else {
+                *reinterpret_cast<float4 *>(GN + v * pP + pc) = make_float4(gv[0], gv[1], gv[2], gv[3]);
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    sa += live ? G[q] * hq[q] : 0.f;
-                    sb += live ? G[q] * bxp[q] : 0.f;
-                    sg += live ? G[q] * bx[q] : 0.f;
-                    M[q] = g * G[q] + b1 * gn[q];
+                    XT[(pc + q) * pV + v] = xv[q];
+                    GT[(pc + q) * pV + v] = gv[q];
                 }
-#pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    float vb = M[0] * xr[r].x + M[1] * xr[r].y + M[2] * xr[r].z + M[3] * xr[r].w;
-                    float vc = hcv[0] * gyr[r].x + hcv[1] * gyr[r].y + hcv[2] * gyr[r].z + hcv[3] * gyr[r].w;
-                    vb = row_sum<P4>(vb);
-                    vc = row_sum<P4>(vc);
-                    if (pg == 0 && live) {
-                        gbs[r * N + n] = vb;
-                        gcs[r * N + n] = vc;
-                    }
-                    const float bc = tb[Cf::t_b + r * N + n];
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) gxp[r][q] += live ? bc * M[q] : 0.f;
-                }
-                Gn[j] = make_float4(G[0], G[1], G[2], G[3]);
             }
-#pragma unroll
-            for (int r = 0; r < R; ++r)
-                *reinterpret_cast<float4 *>(red + (rg * R + r) * P + 4 * pg) = make_float4(gxp[r][0], gxp[r][1], gxp[r][2], gxp[r][3]);
-            // scalar partials: wave sums, then one value per wave in LDS
-            sa = row_sum<16>(sa); sb = row_sum<16>(sb); sg = row_sum<16>(sg);
-            sa += __shfl_xor(sa, 16); sb += __shfl_xor(sb, 16); sg += __shfl_xor(sg, 16);
-            sa += __shfl_xor(sa, 32); sb += __shfl_xor(sb, 32); sg += __shfl_xor(sg, 32);
-            if (lane == 0) {
-                scs[wave * 4 + 0] = sa;
-                scs[wave * 4 + 1] = sb;
-                scs[wave * 4 + 2] = sg;
-            }
-            __syncthreads();
-            const int64_t tok = (b * T + t) * p.H + h;
-            if (tid == 0) {
-                float da = 0.f, db = 0.f, dg = 0.f;
-#pragma unroll
-                for (int w = 0; w < kBT / kWave; ++w) da += scs[w * 4], db += scs[w * 4 + 1], dg += scs[w * 4 + 2];
-                const float d = tb[Cf::t_dt], l = tb[Cf::t_lam];
-                p.gdt[tok] = da * Ah * a + db * (1.f - l) * (a + d * Ah * a) + dg * l;
-                p.glam[tok] = -db * d * a + dg * d;
-                gA += da * d * a + db * (1.f - l) * d * d * a;
-            }
-            for (int o = tid; o < R * P; o += kBT) {
-                float s = 0.f;
-                for (int q = 0; q < RG && q * P4 < N * P4; ++q) s += red[q * R * P + o];
-                p.gx[tok * R * P + o] = s;
-            }
-            if (tid < K) {
-                const int k = tid;
-                const float2 c = cs[(i + 1) * K + k];
-                float dphi = 0.f;
-#pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    const float gb0 = gbs[r * N + 2 * k], gb1 = gbs[r * N + 2 * k + 1];
-                    const float gc0 = gcs[r * N + 2 * k], gc1 = gcs[r * N + 2 * k + 1];
-                    const float b0 = tb[Cf::t_b + r * N + 2 * k], b1v = tb[Cf::t_b + r * N + 2 * k + 1];
-                    const float c0 = tb[Cf::t_c + r * N + 2 * k], c1 = tb[Cf::t_c + r * N + 2 * k + 1];
-                    dphi += gb0 * b1v - gb1 * b0 + gc0 * c1 - gc1 * c0;
-                    // dB = R(Phi) dB~
-                    p.gB[(tok * R + r) * N + 2 * k] = c.x * gb0 - c.y * gb1;
-                    p.gB[(tok * R + r) * N + 2 * k + 1] = c.y * gb0 + c.x * gb1;
-                    p.gC[(tok * R + r) * N + 2 * k] = c.x * gc0 - c.y * gc1;
-                    p.gC[(tok * R + r) * N + 2 * k + 1] = c.y * gc0 + c.x * gc1;
-                }
-                acc += double(dphi);
-                p.gtheta[tok * K + k] = float(acc);
-            }
-            a1 = a;
-            b1 = bb;
-#pragma unroll
-            for (int j = 0; j < SPT; ++j) {
-                hc[j] = hp[j];
-                if (i >= 1) hp[j] = hn[j];
-            }
-            __syncthreads(); // token t's buffer, gbs, gcs, red consumed
-            if (t - 2 >= t0 - 1) {
-                store_raw(t - 2);
-                if (t - 3 >= t0 - 1) load_raw(t - 3);
-                __syncthreads();
-                if (tid < K && t - 2 >= 0) rotate_tok(t - 2, cs[(i - 1) * K + tid]);
-            }
-            __syncthreads();
         }
-    }
-    if (tid == 0) p.gA_part[bh] = gA;
+    };
 
-    // ---- the carried state: G_0 is in Gn, a_0 = a1, b_0 = b1, token -1 in its buffer
-    if (p.gh0) {
+    // ===================== forward sweep: H_c and Phi at each chunk start
+    // Hf: transposed tiles (pb, nb = w + 4 q) of H_c; element e of lane
+    // (li, lg) is H[nb*16 + li][pb*16 + 4 lg + e].  G1 below has this layout.
+    floatx4 Hf[NBW][PB];
+    {
+        const float d0 = io<IO>::get(dtg + tok(0)), l0 = io<IO>::get(lmg + tok(0));
+        const float dl0 = (1.f - l0) * d0;
 #pragma unroll
-        for (int j = 0; j < SPT; ++j) {
-            const float4 v = make_float4(a1 * Gn[j].x, a1 * Gn[j].y, a1 * Gn[j].z, a1 * Gn[j].w);
-            if (own || j * kBT + tid < SLOTS) reinterpret_cast<float4 *>(p.gh0 + bh * int64_t(N) * P)[j * kBT + tid] = v;
-        }
+        for (int q = 0; q < NBW; ++q)
+#pragma unroll
+            for (int pb = 0; pb < PB; ++pb) {
+                Hf[q][pb] = zero4();
+                const int nb = w + 4 * q;
+                if (nb >= NB || !p.has_init) continue;
+                const int n = nb * 16 + li, pc = pb * 16 + 4 * lg;
+                const float4 hv = *reinterpret_cast<const float4 *>(p.h0 + (bh * N + n) * int64_t(P) + pc);
+                float hh[4] = {hv.x, hv.y, hv.z, hv.w};
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const float bb = dl0 * p.prevB0[(bh * R + r) * N + n];
+                    float xv[4];
+                    io<IO>::load4(static_cast<const IO *>(p.prevx0) + (bh * R + r) * P + pc, xv);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) hh[e] += bb * xv[e];
+                }
+                Hf[q][pb] = floatx4{hh[0], hh[1], hh[2], hh[3]};
+            }
+        if (tid < K) PHE[tid] = p.has_init ? double(p.phi0[bh * K + tid]) : 0.0;
     }
-    if (p.gphi0 && tid < K) p.gphi0[bh * K + tid] = float(acc);
-    if (p.gprevB0 || p.gprevx0) {
-        const float *tp = tok_of(-1);
-        float gxp[R][4];
+    __syncthreads();
+    for (int c = 0; c < nC; ++c) {
+        lane_ids();
+        const int64_t t0 = int64_t(c) * Q;
+        const int Tc = int(min<int64_t>(T - t0, Q));
 #pragma unroll
-        for (int r = 0; r < R; ++r)
+        for (int q = 0; q < NBW; ++q)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) gxp[r][q] = 0.f;
+            for (int pb = 0; pb < PB; ++pb)
+                if (w + 4 * q < NB) *reinterpret_cast<floatx4 *>(ck_at(c, w + 4 * q, pb)) = Hf[q][pb];
+        stage_scalars(t0, Tc);
+        stage_angles(t0, Tc, true, c);
+        load_bc(t0, Tc, false);
+        stage_xg(t0, Tc, true);
+        __syncthreads();
+        rot_store(rb, nullptr, BN);
+        __syncthreads();
+        // H^T[p][n] <- e^{ec_end} H^T + sum_v x[v][p] U_v B~[v][n]
+        {
+            const float eE = sc(Cf::s_misc, 0);
+            float uv[VB][4];
 #pragma unroll
-        for (int j = 0; j < SPT; ++j) {
-            const int slot = j * kBT + tslot;
-            const int n = slot / P4;
-            const bool live = own || slot == j * kBT + tid;
-            const float M[4] = {b1 * Gn[j].x, b1 * Gn[j].y, b1 * Gn[j].z, b1 * Gn[j].w};
+            for (int kb = 0; kb < VB; ++kb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) uv[kb][e] = sc(Cf::s_U, row_tok(kb * 16 + 4 * lg + e));
+#pragma unroll
+            for (int q = 0; q < NBW; ++q) {
+                const int nb = w + 4 * q;
+                if (nb >= NB) continue;
+#pragma unroll
+                for (int pb = 0; pb < PB; ++pb) {
+                    floatx4 acc = Hf[q][pb] * eE;
+#pragma unroll
+                    for (int kb = 0; kb < VB; ++kb)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int v = kb * 16 + 4 * lg + e;
+                            acc = mfma4(GN[v * pP + pb * 16 + li] * uv[kb][e], BN[v * pN + nb * 16 + li], acc);
+                        }
+                    Hf[q][pb] = acc;
+                }
+            }
+        }
+        __syncthreads();
+    }
+
+    // ===================== backward sweep
+    // G1: the gradient G of H_{c+1} in Hf's layout; G2: G in tiles (nb, pb = w),
+    // element e of lane (li, lg) = G[nb*16 + 4 lg + e][w*16 + li].
+    floatx4 G1[NBW][PB], G2[NB];
+#pragma unroll
+    for (int q = 0; q < NBW; ++q)
+#pragma unroll
+        for (int pb = 0; pb < PB; ++pb) G1[q][pb] = zero4();
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) G2[nb] = zero4();
+    double acc_th = 0.0; // wave 1, lane k: running sum of dPhi
+    float gA = 0.f;      // wave 0: this lane's share of dA
+    bool pend = false;   // wave 0, lane 0: the later chunk's first token awaits its d(delta)
+    float pd_g = 0.f, pd_l = 0.f, pd_dt = 0.f, pd_lam = 0.f;
+    int64_t pd_tok = 0;
+    for (int c = nC - 1; c >= 0; --c) {
+        lane_ids();
+        const int64_t t0 = int64_t(c) * Q;
+        const int Tc = int(min<int64_t>(T - t0, Q));
+        stage_scalars(t0, Tc);
+        stage_angles(t0, Tc, false, c);
+        load_bc(t0, Tc, true);
+        stage_xg(t0, Tc, false);
+        __syncthreads();
+        // ---- rotate; the table of e^{ec_i - ec_j}
+        for (int idx = tid; idx < QP * QP; idx += kBwdThreads) {
+            const int i = idx / QP, j = idx - i * QP;
+            ET[i * pQ + j] = i >= j ? __expf(sc(Cf::s_ec, i) - sc(Cf::s_ec, j)) : 0.f;
+        }
+        rot_store(rb, BT, BN);
+        rot_store(rc, CT, CN);
+        __syncthreads();
+        // ---- S = C~ B~^T and D = gy x^T, one 16 x 16 tile per wave; masks
+        {
+            const int vb = w >> 1, vb2 = w & 1;
+            floatx4 S[1] = {zero4()}, D[1] = {zero4()};
+            mm_lds<N, pV, pV, 1>(S, CT + vb * 16, BT + vb2 * 16, li, lg);
+            mm_lds<P, pV, pV, 1>(D, GT + vb * 16, XT + vb2 * 16, li, lg);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int v = vb * 16 + 4 * lg + e, v2 = vb2 * 16 + li;
+                const int ti = row_tok(v), tj = row_tok(v2);
+                const float wgt =
+                    ti >= tj ? ET[ti * pQ + tj] * (sc(Cf::s_g, tj) + (ti > tj ? sc(Cf::s_dn, tj) : 0.f)) : 0.f;
+                MS[v * pV + v2] = wgt * S[0][e];
+                MN[v * pV + v2] = wgt * D[0][e];
+                MT[v2 * pV + v] = wgt * D[0][e];
+                SD[v * pV + v2] = S[0][e] * D[0][e];
+            }
+        }
+        __syncthreads();
+        // ---- dW; the six products; the gradient of H_c
+        for (int idx = tid; idx < Q * Q; idx += kBwdThreads) {
+            const int i = idx / Q, j = idx - i * Q;
+            float s = 0.f;
+            if (i >= j)
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+#pragma unroll
+                    for (int r2 = 0; r2 < R; ++r2) s += SD[(i * R + r) * pV + j * R + r2];
+            DW[i * pQ + j] = s;
+        }
+        const float eE = sc(Cf::s_misc, 0);
+        float ev[VB][4];
+#pragma unroll
+        for (int kb = 0; kb < VB; ++kb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ev[kb][e] = sc(Cf::s_E, row_tok(kb * 16 + 4 * lg + e));
+        // dx = (W.S)^T gy + diag(U) B~ G   (tiles (vb, pb = w))
+        if (w < PB) {
+            const int pb = w;
+            floatx4 acc[VB];
+#pragma unroll
+            for (int vb = 0; vb < VB; ++vb) acc[vb] = zero4();
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int k = nb * 16 + 4 * lg + e;
+#pragma unroll
+                    for (int vb = 0; vb < VB; ++vb) acc[vb] = mfma4(BT[k * pV + vb * 16 + li], G2[nb][e], acc[vb]);
+                }
+#pragma unroll
+            for (int vb = 0; vb < VB; ++vb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[vb][e] *= sc(Cf::s_U, row_tok(vb * 16 + 4 * lg + e));
+            mm_lds<V, pV, pP, VB>(acc, MS, GN + pb * 16, li, lg);
+#pragma unroll
+            for (int vb = 0; vb < VB; ++vb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int v = vb * 16 + 4 * lg + e, i = v / R;
+                    if (v < VQ && i < Tc) p.gx[(tok(t0 + i) * R + (v - i * R)) * P + pb * 16 + li] = acc[vb][e];
+                }
+            // G <- e^{ec_end} G + C~^T diag(E) gy  (this orientation)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                floatx4 a = G2[nb] * eE;
+#pragma unroll
+                for (int kb = 0; kb < VB; ++kb)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int v = kb * 16 + 4 * lg + e;
+                        a = mfma4(CN[v * pN + nb * 16 + li] * ev[kb][e], GN[v * pP + pb * 16 + li], a);
+                    }
+                G2[nb] = a;
+            }
+        }
+        // dC~ and dB~ (tiles (vb, nb = w + 4 q)), rotated back; dPhi terms
+        float pe[VB][4], pu[VB][4];
+#pragma unroll
+        for (int vb = 0; vb < VB; ++vb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) pe[vb][e] = pu[vb][e] = 0.f;
+        float pz = 0.f;
+#pragma unroll
+        for (int q = 0; q < NBW; ++q) {
+            const int nb = w + 4 * q;
+            if (nb >= NB) continue;
+            floatx4 dc[VB], db[VB], hq[PB];
+#pragma unroll
+            for (int pb = 0; pb < PB; ++pb) hq[pb] = *reinterpret_cast<const floatx4 *>(ck_at(c, nb, pb));
+#pragma unroll
+            for (int vb = 0; vb < VB; ++vb) dc[vb] = db[vb] = zero4();
+#pragma unroll
+            for (int pb = 0; pb < PB; ++pb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int k = pb * 16 + 4 * lg + e;
+#pragma unroll
+                    for (int vb = 0; vb < VB; ++vb) {
+                        dc[vb] = mfma4(GT[k * pV + vb * 16 + li], hq[pb][e], dc[vb]);
+                        db[vb] = mfma4(XT[k * pV + vb * 16 + li], G1[q][pb][e], db[vb]);
+                    }
+                }
+#pragma unroll
+            for (int vb = 0; vb < VB; ++vb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int v = vb * 16 + 4 * lg + e, n = nb * 16 + li, ti = row_tok(v);
+                    pe[vb][e] += dc[vb][e] * CN[v * pN + n];
+                    pu[vb][e] += db[vb][e] * BN[v * pN + n];
+                    dc[vb][e] *= sc(Cf::s_E, ti);
+                    db[vb][e] *= sc(Cf::s_U, ti);
+                }
+            mm_lds<V, pV, pN, VB>(dc, MT, BN + nb * 16, li, lg);
+            mm_lds<V, pV, pN, VB>(db, MN, CN + nb * 16, li, lg);
+#pragma unroll
+            for (int vb = 0; vb < VB; ++vb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int v = vb * 16 + 4 * lg + e, n = nb * 16 + li, i = v / R;
+                    const bool odd = n & 1;
+                    const float f = TF[min(i, Q - 1) * K + (n >> 1)];
+                    const float cs = __builtin_amdgcn_cosf(f), sn = __builtin_amdgcn_sinf(f);
+                    const float ob = __shfl_xor(db[vb][e], 1), oc = __shfl_xor(dc[vb][e], 1);
+                    const float b0 = odd ? ob : db[vb][e], b1 = odd ? db[vb][e] : ob;
+                    const float c0 = odd ? oc : dc[vb][e], c1 = odd ? dc[vb][e] : oc;
+                    if (v < VQ && i < Tc) {
+                        const int64_t o = (tok(t0 + i) * R + (v - i * R)) * N + n;
+                        p.gB[o] = odd ? sn * b0 + cs * b1 : cs * b0 - sn * b1;
+                        p.gC[o] = odd ? sn * c0 + cs * c1 : cs * c0 - sn * c1;
+                    }
+                    if (!odd) {
+                        const float2 bt = *reinterpret_cast<const float2 *>(BN + v * pN + n);
+                        const float2 ct = *reinterpret_cast<const float2 *>(CN + v * pN + n);
+                        PH[v * K + (n >> 1)] = b0 * bt.y - b1 * bt.x + c0 * ct.y - c1 * ct.x;
+                    }
+                }
+            // d e^{ec_end} = <G, H_c>; then G <- e^{ec_end} G + C~^T diag(E) gy (this orientation)
+#pragma unroll
+            for (int pb = 0; pb < PB; ++pb) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) pz += G1[q][pb][e] * hq[pb][e];
+                floatx4 a = G1[q][pb] * eE;
+#pragma unroll
+                for (int kb = 0; kb < VB; ++kb)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int v = kb * 16 + 4 * lg + e;
+                        a = mfma4(GN[v * pP + pb * 16 + li] * ev[kb][e], CN[v * pN + nb * 16 + li], a);
+                    }
+                G1[q][pb] = a;
+            }
+        }
+        // per-row partial sums of dE and dU over this wave's columns
+#pragma unroll
+        for (int vb = 0; vb < VB; ++vb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float se = row_sum<16>(pe[vb][e]), su = row_sum<16>(pu[vb][e]);
+                if (li == 0) {
+                    PE[w * V + vb * 16 + 4 * lg + e] = se;
+                    PU[w * V + vb * 16 + 4 * lg + e] = su;
+                }
+            }
+        pz = row_sum<16>(pz);
+        pz += __shfl_xor(pz, 16);
+        pz += __shfl_xor(pz, 32);
+        if (lane == 0) PZ[w * 4] = pz;
+        __syncthreads();
+        // ---- the scalars (wave 0, lane = token) and dtheta (wave 1, lane = pair)
+        if (w == 0) {
+            const int j = lane;
+            const bool tj = j < Q;
+            float colE = 0.f, rowW = 0.f;
+#pragma unroll 4
+            for (int i = 0; i < Q; ++i) {
+                if (tj && i > j) colE += DW[i * pQ + j] * ET[i * pQ + j];
+                if (tj && i < j) rowW += DW[j * pQ + i] * ET[j * pQ + i] * (sc(Cf::s_g, i) + sc(Cf::s_dn, i));
+            }
+            float dEj = 0.f, dUj = 0.f;
+            if (tj)
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+#pragma unroll
+                    for (int ww = 0; ww < 4; ++ww) {
+                        dEj += PE[ww * V + j * R + r];
+                        dUj += PU[ww * V + j * R + r];
+                    }
+            const int js = tj ? j : Q;
+            const float Ej = sc(Cf::s_E, js), EUj = sc(Cf::s_EU, js), Uj = sc(Cf::s_U, js);
+            const float gd = sc(Cf::s_g, js) + sc(Cf::s_dn, js);
+            const float dgam = (tj ? DW[j * pQ + j] : 0.f) + colE + dUj * EUj;
+            const float ddn = colE + dUj * EUj;
+            float dec = rowW - colE * gd + dEj * Ej - dUj * Uj;
+            float uu = dUj * Uj;
+#pragma unroll
+            for (int o = 1; o < kWave; o <<= 1) uu += __shfl_xor(uu, o);
+            if (j == Tc - 1) dec += uu + (PZ[0] + PZ[4] + PZ[8] + PZ[12]) * sc(Cf::s_misc, 0);
+            const float incl = wave_inclusive_sum(dec, lane);
+            const float dl = __shfl(incl, kWave - 1) - incl + dec;
+            const float dd = __shfl_up(ddn, 1);
+            const float ddLast = __shfl(ddn, Q - 1);
+            const float dtj = sc(Cf::s_dt, js), lmj = sc(Cf::s_lam, js);
+            if (j >= 1 && j < Tc) {
+                const int64_t o = tok(t0 + j);
+                p.gdt[o] = dgam * lmj + dd * (1.f - lmj) + dl * Ah;
+                p.glam[o] = (dgam - dd) * dtj;
+            }
+            if (j < Tc) gA += dl * dtj;
+            if (j == 0) {
+                if (pend) {
+                    p.gdt[pd_tok] = pd_g * pd_lam + ddLast * (1.f - pd_lam) + pd_l * Ah;
+                    p.glam[pd_tok] = (pd_g - ddLast) * pd_dt;
+                }
+                pend = true;
+                pd_g = dgam; pd_l = dl; pd_dt = dtj; pd_lam = lmj; pd_tok = tok(t0);
+            }
+        } else if (w == 1 && lane < K) {
+            const int k = lane;
+#pragma unroll 4
+            for (int i = Q - 1; i >= 0; --i) {
+                if (i < Tc) {
+                    float s = 0.f;
+#pragma unroll
+                    for (int r = 0; r < R; ++r) s += PH[(i * R + r) * K + k];
+                    acc_th += double(s);
+                    p.gtheta[tok(t0 + i) * K + k] = float(acc_th);
+                }
+            }
+        }
+        __syncthreads();
+    }
+
+    // ===================== the carried state (G is now the gradient of H_0)
+    lane_ids();
+    float dd0 = 0.f;
+    if (p.has_init) {
+        const float d0 = io<IO>::get(dtg + tok(0)), l0 = io<IO>::get(lmg + tok(0));
+        const float dl0 = (1.f - l0) * d0;
+        // from G2 (columns p = w*16 + li): dx_{-1} and the gradient of d_0
+        float part = 0.f;
+        if (w < PB) {
+            const int pc = w * 16 + li;
 #pragma unroll
             for (int r = 0; r < R; ++r) {
-                const float4 xq = *reinterpret_cast<const float4 *>(tp + Cf::t_x + r * P + 4 * pg);
-                float vb = M[0] * xq.x + M[1] * xq.y + M[2] * xq.z + M[3] * xq.w;
-                vb = row_sum<P4>(vb);
-                if (pg == 0 && live && p.gprevB0) p.gprevB0[(bh * R + r) * N + n] = vb;
-                const float bq = tp[Cf::t_b + r * N + n];
+                const float xr = io<IO>::get(static_cast<const IO *>(p.prevx0) + (bh * R + r) * P + pc);
+                float s = 0.f;
 #pragma unroll
-                for (int q = 0; q < 4; ++q) gxp[r][q] += live ? bq * M[q] : 0.f;
+                for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) s += p.prevB0[(bh * R + r) * N + nb * 16 + 4 * lg + e] * G2[nb][e];
+                s += __shfl_xor(s, 16);
+                s += __shfl_xor(s, 32);
+                if (lg == 0 && p.gprevx0) p.gprevx0[(bh * R + r) * P + pc] = dl0 * s;
+                part += lg == 0 ? s * xr : 0.f;
             }
         }
+        part = row_sum<16>(part);
+        part += __shfl_xor(part, 16);
+        part += __shfl_xor(part, 32);
+        if (lane == 0) PZ[w * 4 + 1] = part;
+        // from G1 (rows n = nb*16 + li): dh~_{-1} and dB~_{-1}
 #pragma unroll
-        for (int r = 0; r < R; ++r)
-            *reinterpret_cast<float4 *>(red + (rg * R + r) * P + 4 * pg) = make_float4(gxp[r][0], gxp[r][1], gxp[r][2], gxp[r][3]);
-        __syncthreads();
-        if (p.gprevx0)
-            for (int o = tid; o < R * P; o += kBT) {
+        for (int q = 0; q < NBW; ++q) {
+            const int nb = w + 4 * q;
+            if (nb >= NB) continue;
+            const int n = nb * 16 + li;
+#pragma unroll
+            for (int pb = 0; pb < PB; ++pb)
+                if (p.gh0)
+                    *reinterpret_cast<float4 *>(p.gh0 + (bh * N + n) * int64_t(P) + pb * 16 + 4 * lg) =
+                        make_float4(G1[q][pb][0], G1[q][pb][1], G1[q][pb][2], G1[q][pb][3]);
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
                 float s = 0.f;
-                for (int q = 0; q < RG && q * P4 < N * P4; ++q) s += red[q * R * P + o];
-                p.gprevx0[bh * R * P + o] = s;
+#pragma unroll
+                for (int pb = 0; pb < PB; ++pb) {
+                    float xv[4];
+                    io<IO>::load4(static_cast<const IO *>(p.prevx0) + (bh * R + r) * P + pb * 16 + 4 * lg, xv);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) s += G1[q][pb][e] * xv[e];
+                }
+                s += __shfl_xor(s, 16);
+                s += __shfl_xor(s, 32);
+                if (lg == 0 && p.gprevB0) p.gprevB0[(bh * R + r) * N + n] = dl0 * s;
             }
+        }
+        if (p.gphi0 && w == 1 && lane < K) p.gphi0[bh * K + lane] = float(acc_th);
+        __syncthreads();
+        dd0 = PZ[1] + PZ[5] + PZ[9] + PZ[13];
+    }
+    if (w == 0) {
+        if (lane == 0 && pend) {
+            p.gdt[pd_tok] = pd_g * pd_lam + dd0 * (1.f - pd_lam) + pd_l * Ah;
+            p.glam[pd_tok] = (pd_g - dd0) * pd_dt;
+        }
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) gA += __shfl_xor(gA, o);
+        if (lane == 0) p.gA_part[bh] = gA;
     }
 }
-
-} // namespace m3
-
-namespace m3 {
 
 // Sum of the per-(batch, head) partials of dA over the batch.
 static __global__ void k_backward_gA(const BwdParams p) {
@@ -447,7 +720,7 @@ hipError_t launch_backward_inst(const BwdParams &p, hipStream_t s) {
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, int(Cf::bytes));
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((k_backward<IO, N, P, R>), dim3(unsigned(p.batch * p.H)), dim3(Cf::kBT), Cf::bytes, s, p);
+    hipLaunchKernelGGL((k_backward<IO, N, P, R>), dim3(unsigned(p.batch * p.H)), dim3(kBwdThreads), Cf::bytes, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_backward_gA, dim3(unsigned((p.H + 255) / 256)), dim3(256), 0, s, p);

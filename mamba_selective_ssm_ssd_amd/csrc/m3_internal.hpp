@@ -64,12 +64,9 @@ struct DecodeParams {
     BlockParams blk;
 };
 
-// Backward pass (one workgroup per (batch, head), sequential in time).
-// Tokens per stretch of the backward's recomputation: the forward sweep
-// stores the state before each stretch; a stretch's states are recomputed
-// into a slab of kBwdQ + 1 states before its tokens are processed backwards
-// (16 and 32 measured no faster on the b4 T2048 H64 workloads).
-constexpr int kBwdQ = 64;
+// Backward pass (one workgroup per (batch, head), chunks of kBwdV / R
+// tokens processed last to first): kBwdV rows (token, rank) per chunk.
+constexpr int kBwdV = 32;
 
 struct BwdParams {
     int64_t batch, T;
@@ -83,9 +80,8 @@ struct BwdParams {
     float *gx, *gdt, *glam, *gtheta, *gB, *gC, *gA;
     float *gh0, *gphi0, *gprevB0, *gprevx0;
     // workspace
-    float *ck_h;    // [b][H][nC][N][P]  state before each stretch of QB tokens
-    double *ck_phi; // [b][H][nC][K]     angle before each stretch
-    float *slab;    // [b][H][QB+1][N][P] one stretch's states, h~_{t0-1} .. h~_{t0+QB-1}
+    float *ck_h;    // [b][H][nC][N x P] state entering each chunk (tile-major)
+    double *ck_phi; // [b][H][nC][K]     angle before each chunk
     float *gA_part; // [b][H]
 };
 

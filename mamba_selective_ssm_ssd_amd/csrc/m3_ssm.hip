@@ -87,20 +87,20 @@ WorkspaceLayout layout(const m3_shape_t *s) {
     return w;
 }
 
-// Backward workspace: chunk-start states and angles, one chunk's states per
-// sequence, the per-sequence partials of dA.
+// Backward workspace: the state and angle entering each chunk, the
+// per-sequence partials of dA.
 struct BwdLayout {
-    size_t ck_h, ck_phi, slab, gA, total;
+    size_t ck_h, ck_phi, gA, total;
 };
 BwdLayout bwd_layout(const m3_shape_t *s) {
     const size_t bh = size_t(s->batch) * size_t(s->nheads);
-    const size_t nC = size_t((s->seqlen + m3::kBwdQ - 1) / m3::kBwdQ);
+    const size_t Q = size_t(m3::kBwdV / s->rank);
+    const size_t nC = (size_t(s->seqlen) + Q - 1) / Q;
     const size_t N = size_t(s->dstate), P = size_t(s->headdim), K = N / 2;
     BwdLayout w;
     size_t off = 0;
     w.ck_h = off; off += round_up(bh * nC * N * P * sizeof(float));
     w.ck_phi = off; off += round_up(bh * nC * K * sizeof(double));
-    w.slab = off; off += round_up(bh * (m3::kBwdQ + 1) * N * P * sizeof(float));
     w.gA = off; off += round_up(bh * sizeof(float));
     w.total = off;
     return w;
@@ -372,7 +372,7 @@ m3_status_t m3_ssm_prefill_backward(const m3_shape_t *shape, const void *x, cons
     p.N = shape->dstate;
     p.R = shape->rank;
     p.K = p.N / 2;
-    p.nC = int32_t((p.T + m3::kBwdQ - 1) / m3::kBwdQ);
+    p.nC = int32_t((p.T + m3::kBwdV / p.R - 1) / (m3::kBwdV / p.R));
     p.x = x; p.dt = dt; p.lam = lam; p.theta = theta; p.B = B; p.C = C; p.gy = gy; p.A = A;
     p.has_init = init != nullptr;
     if (init) {
@@ -385,7 +385,6 @@ m3_status_t m3_ssm_prefill_backward(const m3_shape_t *shape, const void *x, cons
     unsigned char *ws = static_cast<unsigned char *>(workspace);
     p.ck_h = reinterpret_cast<float *>(ws + w.ck_h);
     p.ck_phi = reinterpret_cast<double *>(ws + w.ck_phi);
-    p.slab = reinterpret_cast<float *>(ws + w.slab);
     p.gA_part = reinterpret_cast<float *>(ws + w.gA);
     const hipError_t e = shape->io_dtype == M3_DTYPE_BF16 ? m3::launch_backward_bf16(p, stream)
                                                           : m3::launch_backward_f32(p, stream);
