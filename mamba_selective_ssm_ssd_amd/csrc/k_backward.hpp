@@ -38,8 +38,9 @@
 // angle at each chunk start (workspace), then backward over the chunks.
 // MFMA operand convention: in step (kb, e) of a product, k-slot g of lane l
 // stands for contraction index 16 kb + 4 g + e.  An operand in LDS is stored
-// with the contraction index as its row ("k-major", pitch = 4 mod 16: no
-// bank conflicts), and a 16 x 16 accumulator tile (lane l holds rows
+// with the contraction index contiguous (row pitch 4 x odd, so that 16-byte
+// reads of 16 rows hit distinct banks): one 16-byte read gives a lane its
+// operand for four steps.  A 16 x 16 accumulator tile (lane l holds rows
 // 4 (l / 16) + e of column l % 16) is the B operand of step (kb, e) as it
 // stands, which keeps the carried gradient G (in both orientations) and H_c
 // in registers.
@@ -57,48 +58,74 @@ __device__ __forceinline__ floatx4 mfma4(float a, float b, floatx4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// acc[vb] += A B for NV row blocks of A (vb = 0 .. NV-1), contraction length
-// KD: A[i][k] = a[k * PA + 16 vb + i], B[k][j] = bm[k * PBM + j].
+__device__ __forceinline__ floatx4 zero4() { return floatx4{0.f, 0.f, 0.f, 0.f}; }
+__device__ __forceinline__ floatx4 lds4(const float *q) { return *reinterpret_cast<const floatx4 *>(q); }
+
+// acc[vb] += A B over k = 0 .. KD-1 for NV row blocks of A: A[i][k] =
+// a[(16 vb + i) * PA + k], B[k][j] = bm[j * PBM + k] (both k-contiguous).
+// Lane (i, g) reads four consecutive k (16 kb + 4 g ..) of its row and
+// column with one 16-byte read each: steps (kb, 0..3).
+// The reads of group kb + 1 are issued before the products of group kb
+// (the schedule is pinned: one wave per SIMD leaves no other wave to cover
+// the LDS latency).
 template <int KD, int PA, int PBM, int NV>
 __device__ __forceinline__ void mm_lds(floatx4 (&acc)[NV], const float *a, const float *bm, int i, int g) {
+    constexpr int NK = KD / 16;
+    floatx4 bv[2], av[2][NV];
+    __builtin_amdgcn_sched_barrier(0);
+    bv[0] = lds4(bm + i * PBM + 4 * g);
 #pragma unroll
-    for (int kb = 0; kb < KD / 16; ++kb)
+    for (int vb = 0; vb < NV; ++vb) av[0][vb] = lds4(a + (16 * vb + i) * PA + 4 * g);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int k = kb * 16 + 4 * g + e;
-            const float bv = bm[k * PBM + i];
+    for (int kb = 0; kb < NK; ++kb) {
+        const int cu = kb & 1, nx = cu ^ 1;
+        if (kb + 1 < NK) {
+            bv[nx] = lds4(bm + i * PBM + 16 * (kb + 1) + 4 * g);
 #pragma unroll
-            for (int vb = 0; vb < NV; ++vb) acc[vb] = mfma4(a[k * PA + 16 * vb + i], bv, acc[vb]);
+            for (int vb = 0; vb < NV; ++vb) av[nx][vb] = lds4(a + (16 * vb + i) * PA + 16 * (kb + 1) + 4 * g);
         }
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int vb = 0; vb < NV; ++vb) acc[vb] = mfma4(av[cu][vb][e], bv[cu][e], acc[vb]);
+    }
+    // reads of group 0, then per group: the next group's reads, its MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, 1 + NV, 0);
+#pragma unroll
+    for (int kb = 0; kb < NK; ++kb) {
+        if (kb + 1 < NK) __builtin_amdgcn_sched_group_barrier(0x100, 1 + NV, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 4 * NV, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
 }
-
-__device__ __forceinline__ floatx4 zero4() { return floatx4{0.f, 0.f, 0.f, 0.f}; }
 
 template <int N, int P, int R>
 struct BwdCfg {
     static constexpr int V = kBwdV, Q = V / R, VQ = Q * R, QP = Q + 1;
     static constexpr int K = N / 2, NB = N / 16, PB = P / 16, VB = V / 16, NBW = (NB + 3) / 4;
-    static constexpr int pV = V + 4, pN = N + 4, pP = P + 4, pQ = QP + 1, SQ = 36;
-    static constexpr int TPS = (Q + 7) / 8; // tokens per segment of the angle prefix
+    // row pitches 4 x odd: 16-byte reads of 16 rows hit distinct banks
+    static constexpr int pV = V + 4, pN = N + 4, pP = P + 4, pK = K + 4, pC = K + 1, pQ = QP + 1, SQ = 36;
+    static constexpr int TPS = (Q + 7) / 8; // tokens per segment of the angle scans
+    static constexpr int KP = (K + 31) / 32; // passes of the angle scans (32 pairs each)
     // token scalar tables, SQ floats each
     static constexpr int s_ec = 0, s_E = 1, s_EU = 2, s_U = 3, s_g = 4, s_dn = 5, s_dt = 6, s_lam = 7, s_misc = 8;
     // LDS (floats)
-    static constexpr int o_bt = 0;              // B~ [N][pV]
-    static constexpr int o_ct = o_bt + N * pV;  // C~ [N][pV]
+    static constexpr int o_bt = 0;              // B~^T [N][pV]
+    static constexpr int o_ct = o_bt + N * pV;  // C~^T [N][pV]
     static constexpr int o_bn = o_ct + N * pV;  // B~ [V][pN]
     static constexpr int o_cn = o_bn + V * pN;  // C~ [V][pN]
-    static constexpr int o_xt = o_cn + V * pN;  // x  [P][pV]
-    static constexpr int o_gt = o_xt + P * pV;  // gy [P][pV]
-    static constexpr int o_gn = o_gt + P * pV;  // gy [V][pP]  (forward sweep: x)
-    static constexpr int o_ms = o_gn + V * pP;  // W.S [V][pV]  (row v, column v')
-    static constexpr int o_mn = o_ms + V * pV;  // W.D [V][pV]
-    static constexpr int o_mt = o_mn + V * pV;  // W.D [V][pV]  (row v', column v)
+    static constexpr int o_t2 = o_cn + V * pN;  // gy^T [P][pV]  (forward sweep: x^T)
+    static constexpr int o_xn = o_t2 + P * pV;  // x [V][pP]
+    static constexpr int o_gn = o_xn + V * pP;  // gy [V][pP]
+    static constexpr int o_ms = o_gn + V * pP;  // (W.S)^T [V][pV]  (row v', column v)
+    static constexpr int o_mn = o_ms + V * pV;  // W.D [V][pV]      (row v, column v')
+    static constexpr int o_mt = o_mn + V * pV;  // (W.D)^T [V][pV]
     static constexpr int o_sd = o_mt + V * pV;  // S.D [V][pV]
-    static constexpr int o_ph = o_sd + V * pV;  // dPhi terms [V][K]
-    static constexpr int o_tf = o_ph + V * K;   // Phi in turns [Q][K]
-    static constexpr int o_et = o_tf + Q * K;   // e^{ec_i - ec_j} [QP][pQ]
-    static constexpr int o_dw = o_et + QP * pQ; // dW [Q][pQ]
-    static constexpr int o_sc = o_dw + Q * pQ;  // token scalars [9][SQ]
+    static constexpr int o_ph = o_sd + V * pV;  // dPhi terms [V][pK]
+    static constexpr int o_cs = (o_ph + V * pK + 1) / 2 * 2; // cos, sin of Phi [Q][pC] float2
+    static constexpr int o_et = o_cs + 2 * Q * pC; // e^{ec_i - ec_j} [QP][pQ]
+    static constexpr int o_dw = o_et + QP * pQ; // per token: row sums, column sums, diagonal [3][pQ]
+    static constexpr int o_sc = o_dw + 3 * pQ;  // token scalars [9][SQ]
     static constexpr int o_pu = o_sc + 9 * SQ;  // dU partials [4][V]
     static constexpr int o_pe = o_pu + 4 * V;   // dE partials [4][V]
     static constexpr int o_pz = o_pe + 4 * V;   // per-wave scalars [4][4]
@@ -106,6 +133,7 @@ struct BwdCfg {
     static constexpr int floats = o_phe + 2 * K;
     static constexpr size_t bytes = size_t(floats) * 4;
     static_assert(bytes <= kMaxLdsBytes, "backward LDS layout exceeds the workgroup's LDS");
+    static_assert(Q * 8 <= kBwdThreads, "one group of 8 threads per token");
     // 4-element groups of B / C and of x / gy per chunk, per thread
     static constexpr int NBL = (V * N / 4 + kBwdThreads - 1) / kBwdThreads;
     static constexpr int NXL = (V * P / 4 + kBwdThreads - 1) / kBwdThreads;
@@ -115,14 +143,15 @@ template <typename IO, int N, int P, int R>
 __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
     typedef BwdCfg<N, P, R> Cf;
     constexpr int V = Cf::V, Q = Cf::Q, VQ = Cf::VQ, QP = Cf::QP, K = Cf::K;
-    constexpr int NB = Cf::NB, PB = Cf::PB, VB = Cf::VB, NBW = Cf::NBW, TPS = Cf::TPS;
-    constexpr int pV = Cf::pV, pN = Cf::pN, pP = Cf::pP, pQ = Cf::pQ, SQ = Cf::SQ;
+    constexpr int NB = Cf::NB, PB = Cf::PB, VB = Cf::VB, NBW = Cf::NBW, TPS = Cf::TPS, KP = Cf::KP;
+    constexpr int pV = Cf::pV, pN = Cf::pN, pP = Cf::pP, pK = Cf::pK, pC = Cf::pC, pQ = Cf::pQ, SQ = Cf::SQ;
     constexpr int NBL = Cf::NBL, NXL = Cf::NXL;
     extern __shared__ __align__(16) float sm[];
     float *BT = sm + Cf::o_bt, *CT = sm + Cf::o_ct, *BN = sm + Cf::o_bn, *CN = sm + Cf::o_cn;
-    float *XT = sm + Cf::o_xt, *GT = sm + Cf::o_gt, *GN = sm + Cf::o_gn;
+    float *T2 = sm + Cf::o_t2, *XN = sm + Cf::o_xn, *GN = sm + Cf::o_gn;
     float *MS = sm + Cf::o_ms, *MN = sm + Cf::o_mn, *MT = sm + Cf::o_mt, *SD = sm + Cf::o_sd;
-    float *PH = sm + Cf::o_ph, *TF = sm + Cf::o_tf, *ET = sm + Cf::o_et, *DW = sm + Cf::o_dw;
+    float *PH = sm + Cf::o_ph, *ET = sm + Cf::o_et, *DW = sm + Cf::o_dw;
+    float2 *CS = reinterpret_cast<float2 *>(sm + Cf::o_cs);
     float *SC = sm + Cf::o_sc, *PU = sm + Cf::o_pu, *PE = sm + Cf::o_pe, *PZ = sm + Cf::o_pz;
     double *PHE = reinterpret_cast<double *>(sm + Cf::o_phe);
     auto sc = [&](int s, int i) -> float & { return SC[s * SQ + i]; };
@@ -156,6 +185,50 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
     auto ck_at = [&](int c, int nb, int pb) { return ckh + ((int64_t(c) * NB + nb) * PB + pb) * 256 + lane * 4; };
     auto row_tok = [&](int v) { return min(v / R, Q); }; // token slot of a row (Q: padding)
 
+    // ---- a chunk's inputs are loaded into registers (raw bits) one chunk
+    // ahead, during the previous chunk's products, and staged from there.
+    // Loads past the chunk's tokens read a valid element and are zeroed when
+    // staged.
+    typedef typename io4<IO>::raw raw4;
+    raw4 qb[NBL], qc[NBL], qx[NXL], qg[NXL];
+    uint32_t qth[KP][TPS], qdt = 0, qlm = 0;
+    auto issue = [&](int64_t t0, int Tc, bool bwd) {
+#pragma unroll
+        for (int j = 0; j < NBL; ++j) {
+            const int gi = tid + j * kBwdThreads;
+            const int v = gi % V, n = 4 * (gi / V), i = v / R;
+            const bool ok = gi < V * N / 4 && v < VQ && i < Tc;
+            const int64_t off = ok ? tok(t0 + i) * (R * N) + (v - i * R) * N + n : 0;
+            qb[j] = io4<IO>::load(Bg + off);
+            if (bwd) qc[j] = io4<IO>::load(Cg + off);
+        }
+#pragma unroll
+        for (int j = 0; j < NXL; ++j) {
+            const int gi = tid + j * kBwdThreads;
+            const int v = gi % V, pc = 4 * (gi / V), i = v / R;
+            const bool ok = gi < V * P / 4 && v < VQ && i < Tc;
+            const int64_t off = ok ? tok(t0 + i) * (R * P) + (v - i * R) * P + pc : 0;
+            qx[j] = io4<IO>::load(xg + off);
+            if (bwd) qg[j] = io4<IO>::load(gyg + off);
+        }
+#pragma unroll
+        for (int kp = 0; kp < KP; ++kp) {
+            const int k = 32 * kp + 8 * w + (lane & 7), seg = lane >> 3;
+            const int kc = k < K ? k : 0;
+#pragma unroll
+            for (int u = 0; u < TPS; ++u) {
+                const int i = seg * TPS + u;
+                qth[kp][u] = io<IO>::raw(thg + tok(t0 + (i < Tc ? i : 0)) * K + kc);
+            }
+        }
+        if (w == 0) {
+            const int i = lane;
+            const bool ld = i < Tc || (i == Q && t0 + Q < T);
+            qdt = io<IO>::raw(dtg + tok(t0 + (ld ? i : 0)));
+            qlm = io<IO>::raw(lmg + tok(t0 + (ld ? i : 0)));
+        }
+    };
+
     // ---- staging: token scalars (wave 0, lane = token; lane Q carries the
     // next chunk's first token for its d)
     auto stage_scalars = [&](int64_t t0, int Tc) {
@@ -164,15 +237,15 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
             const bool real = i < Tc, nxt = i == Q && t0 + Q < T;
             float d = 0.f, l = 0.f;
             if (real || nxt) {
-                d = io<IO>::get(dtg + tok(t0 + i));
-                l = io<IO>::get(lmg + tok(t0 + i));
+                d = io<IO>::value(qdt);
+                l = io<IO>::value(qlm);
             }
             const float ell = real ? d * Ah : 0.f;
             const float gam = real ? l * d : 0.f;
             const float dlt = real || nxt ? (1.f - l) * d : 0.f;
             float dn = __shfl_down(dlt, 1);
             if (i >= Q) dn = 0.f;
-            const float ec = wave_inclusive_sum(ell, lane);
+            const float ec = wave_scan_dpp(ell);
             const float ecE = __shfl(ec, Q - 1);
             const float E = __expf(ec), EU = __expf(ecE - ec);
             const float U = EU * (gam + dn);
@@ -186,12 +259,12 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
     };
     // Phi_t = Phi_start + the sum of theta over the chunk's tokens up to t,
     // fp64: lane = 8 segments x 8 pairs, a segment's prefix in registers, the
-    // segment totals scanned over lanes 8 apart.  Writes TF (turns, wrapped)
-    // and PHE (the wrapped angle of the chunk's last token).
+    // segment totals scanned over lanes 8 apart.  Writes CS (cos and sin of
+    // Phi_t) and PHE (the wrapped angle of the chunk's last token).
     auto stage_angles = [&](int64_t t0, int Tc, bool fwd, int c) {
 #pragma unroll
-        for (int kp = 0; kp < K; kp += 32) {
-            const int k = kp + 8 * w + (lane & 7), seg = lane >> 3;
+        for (int kp = 0; kp < KP; ++kp) {
+            const int k = 32 * kp + 8 * w + (lane & 7), seg = lane >> 3;
             const bool kv = k < K;
             const int kc = kv ? k : 0;
             const double ph0 = fwd ? PHE[kc] : ckp[int64_t(c) * K + kc];
@@ -201,7 +274,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
             for (int u = 0; u < TPS; ++u) {
                 const int i = seg * TPS + u;
                 const bool ok = kv && i < Tc;
-                const float th = io<IO>::get(thg + tok(t0 + (ok ? i : 0)) * K + kc);
+                const float th = io<IO>::value(qth[kp][u]);
                 run += ok ? double(th) : 0.0;
                 lp[u] = run;
             }
@@ -220,78 +293,69 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
                     const double ph = ph0 + ex + lp[u];
                     double tr = ph * (1.0 / kTwoPi);
                     tr -= rint(tr);
-                    TF[i * K + k] = float(tr);
+                    const float tf = float(tr);
+                    CS[i * pC + k] = make_float2(__builtin_amdgcn_cosf(tf), __builtin_amdgcn_sinf(tf));
                     if (i == Tc - 1) PHE[k] = wrap_angle(ph);
                 }
             }
         }
     };
-    // B (and C) of the chunk into registers, four elements per group, row
-    // v = group % V fastest (rows past the chunk's tokens read as zero)
-    float rb[NBL][4], rc[NBL][4];
-    auto load_bc = [&](int64_t t0, int Tc, bool withC) {
-#pragma unroll
-        for (int j = 0; j < NBL; ++j) {
-            const int gi = tid + j * kBwdThreads;
-            const int v = gi % V, n = 4 * (gi / V), i = v / R;
-            const bool ok = gi < V * N / 4 && v < VQ && i < Tc;
-            const int64_t off = ok ? tok(t0 + i) * (R * N) + (v - i * R) * N + n : 0;
-            float vb[4], vc[4];
-            io<IO>::load4(Bg + off, vb);
-            if (withC) io<IO>::load4(Cg + off, vc);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                rb[j][q] = ok ? vb[q] : 0.f;
-                rc[j][q] = ok && withC ? vc[q] : 0.f;
-            }
-        }
-    };
-    // rotate by -Phi (TF) and store k-major (dT, [n][v]) and row-major (dN, [v][n])
-    auto rot_store = [&](float (&rv)[NBL][4], float *dT, float *dN) {
+    // rotate by -Phi (CS) and store transposed (dT, [n][v]) and row-major (dN, [v][n])
+    // (B or C of the chunk, row v = group % V fastest)
+    auto rot_store = [&](const raw4 (&qv)[NBL], int Tc, float *dT, float *dN) {
 #pragma unroll
         for (int j = 0; j < NBL; ++j) {
             const int gi = tid + j * kBwdThreads;
             if (gi >= V * N / 4) continue;
             const int v = gi % V, n = 4 * (gi / V), i = min(v / R, Q - 1);
-            const float f0 = TF[i * K + n / 2], f1 = TF[i * K + n / 2 + 1];
-            float o[4] = {rv[j][0], rv[j][1], rv[j][2], rv[j][3]};
-            rot_neg(__builtin_amdgcn_cosf(f0), __builtin_amdgcn_sinf(f0), o[0], o[1]);
-            rot_neg(__builtin_amdgcn_cosf(f1), __builtin_amdgcn_sinf(f1), o[2], o[3]);
+            const bool ok = v < VQ && v / R < Tc;
+            const float2 c0 = CS[i * pC + n / 2], c1 = CS[i * pC + n / 2 + 1];
+            float o[4];
+            io4<IO>::unpack(qv[j], o);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) o[q] = ok ? o[q] : 0.f;
+            rot_neg(c0.x, c0.y, o[0], o[1]);
+            rot_neg(c1.x, c1.y, o[2], o[3]);
             if (dN) *reinterpret_cast<float4 *>(dN + v * pN + n) = make_float4(o[0], o[1], o[2], o[3]);
             if (dT)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) dT[(n + q) * pV + v] = o[q];
         }
     };
-    // x (and gy) of the chunk into LDS: the forward sweep keeps x row-major
-    // in GN; the backward sweep keeps x k-major (XT) and gy both ways (GT, GN)
-    auto stage_xg = [&](int64_t t0, int Tc, bool fwd) {
+    // x (and gy) of the chunk into LDS: the forward sweep keeps x transposed
+    // (T2); the backward sweep keeps x row-major (XN) and gy both ways (GN, T2)
+    auto stage_xg = [&](int Tc, bool fwd) {
 #pragma unroll
         for (int j = 0; j < NXL; ++j) {
             const int gi = tid + j * kBwdThreads;
             if (gi >= V * P / 4) continue;
             const int v = gi % V, pc = 4 * (gi / V), i = v / R;
             const bool ok = v < VQ && i < Tc;
-            const int64_t off = ok ? tok(t0 + i) * (R * P) + (v - i * R) * P + pc : 0;
             float xv[4], gv[4];
-            io<IO>::load4(xg + off, xv);
-            if (!fwd) io<IO>::load4(gyg + off, gv);
+            io4<IO>::unpack(qx[j], xv);
+            if (!fwd) io4<IO>::unpack(qg[j], gv);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 xv[q] = ok ? xv[q] : 0.f;
                 gv[q] = ok && !fwd ? gv[q] : 0.f;
             }
             if (fwd) {
-                *reinterpret_cast<float4 *>(GN + v * pP + pc) = make_float4(xv[0], xv[1], xv[2], xv[3]);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) T2[(pc + q) * pV + v] = xv[q];
             } else {
+                *reinterpret_cast<float4 *>(XN + v * pP + pc) = make_float4(xv[0], xv[1], xv[2], xv[3]);
                 *reinterpret_cast<float4 *>(GN + v * pP + pc) = make_float4(gv[0], gv[1], gv[2], gv[3]);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    XT[(pc + q) * pV + v] = xv[q];
-                    GT[(pc + q) * pV + v] = gv[q];
-                }
+                for (int q = 0; q < 4; ++q) T2[(pc + q) * pV + v] = gv[q];
             }
         }
+    };
+    // the factor of row 16 kb + 4 lg + e of this lane's k-slots, per step
+    auto row_factor = [&](int s, float (&f)[VB][4]) {
+#pragma unroll
+        for (int kb = 0; kb < VB; ++kb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) f[kb][e] = sc(s, row_tok(kb * 16 + 4 * lg + e));
     };
 
     // ===================== forward sweep: H_c and Phi at each chunk start
@@ -323,6 +387,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
             }
         if (tid < K) PHE[tid] = p.has_init ? double(p.phi0[bh * K + tid]) : 0.0;
     }
+    issue(0, int(min<int64_t>(T, Q)), false);
     __syncthreads();
     for (int c = 0; c < nC; ++c) {
         lane_ids();
@@ -335,35 +400,37 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
                 if (w + 4 * q < NB) *reinterpret_cast<floatx4 *>(ck_at(c, w + 4 * q, pb)) = Hf[q][pb];
         stage_scalars(t0, Tc);
         stage_angles(t0, Tc, true, c);
-        load_bc(t0, Tc, false);
-        stage_xg(t0, Tc, true);
+        stage_xg(Tc, true);
         __syncthreads();
-        rot_store(rb, nullptr, BN);
+        rot_store(qb, Tc, BT, nullptr);
         __syncthreads();
+        if (c + 1 < nC) issue(t0 + Q, int(min<int64_t>(T - t0 - Q, Q)), false);
         // H^T[p][n] <- e^{ec_end} H^T + sum_v x[v][p] U_v B~[v][n]
         {
             const float eE = sc(Cf::s_misc, 0);
             float uv[VB][4];
+            row_factor(Cf::s_U, uv);
 #pragma unroll
-            for (int kb = 0; kb < VB; ++kb)
+            for (int q = 0; q < NBW; ++q)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) uv[kb][e] = sc(Cf::s_U, row_tok(kb * 16 + 4 * lg + e));
+                for (int pb = 0; pb < PB; ++pb) Hf[q][pb] *= eE;
 #pragma unroll
-            for (int q = 0; q < NBW; ++q) {
-                const int nb = w + 4 * q;
-                if (nb >= NB) continue;
+            for (int kb = 0; kb < VB; ++kb) {
+                floatx4 bv[NBW], av[PB];
 #pragma unroll
-                for (int pb = 0; pb < PB; ++pb) {
-                    floatx4 acc = Hf[q][pb] * eE;
+                for (int q = 0; q < NBW; ++q)
+                    if (w + 4 * q < NB) bv[q] = lds4(BT + ((w + 4 * q) * 16 + li) * pV + 16 * kb + 4 * lg);
 #pragma unroll
-                    for (int kb = 0; kb < VB; ++kb)
+                for (int pb = 0; pb < PB; ++pb) av[pb] = lds4(T2 + (pb * 16 + li) * pV + 16 * kb + 4 * lg);
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const int v = kb * 16 + 4 * lg + e;
-                            acc = mfma4(GN[v * pP + pb * 16 + li] * uv[kb][e], BN[v * pN + nb * 16 + li], acc);
-                        }
-                    Hf[q][pb] = acc;
-                }
+                for (int e = 0; e < 4; ++e)
+#pragma unroll
+                    for (int q = 0; q < NBW; ++q) {
+                        if (w + 4 * q >= NB) continue;
+                        const float bq = bv[q][e] * uv[kb][e];
+#pragma unroll
+                        for (int pb = 0; pb < PB; ++pb) Hf[q][pb] = mfma4(av[pb][e], bq, Hf[q][pb]);
+                    }
             }
         }
         __syncthreads();
@@ -379,102 +446,153 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
         for (int pb = 0; pb < PB; ++pb) G1[q][pb] = zero4();
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) G2[nb] = zero4();
-    double acc_th = 0.0; // wave 1, lane k: running sum of dPhi
+    double carry[KP];    // lanes (pair, segment): sum of dPhi over the later chunks
+#pragma unroll
+    for (int kp = 0; kp < KP; ++kp) carry[kp] = 0.0;
     float gA = 0.f;      // wave 0: this lane's share of dA
     bool pend = false;   // wave 0, lane 0: the later chunk's first token awaits its d(delta)
     float pd_g = 0.f, pd_l = 0.f, pd_dt = 0.f, pd_lam = 0.f;
     int64_t pd_tok = 0;
+    issue(int64_t(nC - 1) * Q, int(T - int64_t(nC - 1) * Q), true);
     for (int c = nC - 1; c >= 0; --c) {
         lane_ids();
         const int64_t t0 = int64_t(c) * Q;
         const int Tc = int(min<int64_t>(T - t0, Q));
         stage_scalars(t0, Tc);
         stage_angles(t0, Tc, false, c);
-        load_bc(t0, Tc, true);
-        stage_xg(t0, Tc, false);
+        stage_xg(Tc, false);
         __syncthreads();
         // ---- rotate; the table of e^{ec_i - ec_j}
         for (int idx = tid; idx < QP * QP; idx += kBwdThreads) {
             const int i = idx / QP, j = idx - i * QP;
             ET[i * pQ + j] = i >= j ? __expf(sc(Cf::s_ec, i) - sc(Cf::s_ec, j)) : 0.f;
         }
-        rot_store(rb, BT, BN);
-        rot_store(rc, CT, CN);
+        rot_store(qb, Tc, BT, BN);
+        rot_store(qc, Tc, CT, CN);
         __syncthreads();
         // ---- S = C~ B~^T and D = gy x^T, one 16 x 16 tile per wave; masks
         {
             const int vb = w >> 1, vb2 = w & 1;
             floatx4 S[1] = {zero4()}, D[1] = {zero4()};
-            mm_lds<N, pV, pV, 1>(S, CT + vb * 16, BT + vb2 * 16, li, lg);
-            mm_lds<P, pV, pV, 1>(D, GT + vb * 16, XT + vb2 * 16, li, lg);
+            mm_lds<N, pN, pN, 1>(S, CN + vb * 16 * pN, BN + vb2 * 16 * pN, li, lg);
+            mm_lds<P, pP, pP, 1>(D, GN + vb * 16 * pP, XN + vb2 * 16 * pP, li, lg);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int v = vb * 16 + 4 * lg + e, v2 = vb2 * 16 + li;
                 const int ti = row_tok(v), tj = row_tok(v2);
                 const float wgt =
                     ti >= tj ? ET[ti * pQ + tj] * (sc(Cf::s_g, tj) + (ti > tj ? sc(Cf::s_dn, tj) : 0.f)) : 0.f;
-                MS[v * pV + v2] = wgt * S[0][e];
+                MS[v2 * pV + v] = wgt * S[0][e];
                 MN[v * pV + v2] = wgt * D[0][e];
                 MT[v2 * pV + v] = wgt * D[0][e];
                 SD[v * pV + v2] = S[0][e] * D[0][e];
             }
         }
         __syncthreads();
-        // ---- dW; the six products; the gradient of H_c
-        for (int idx = tid; idx < Q * Q; idx += kBwdThreads) {
-            const int i = idx / Q, j = idx - i * Q;
-            float s = 0.f;
-            if (i >= j)
+        // H_c (this wave's tiles) and the previous chunk's inputs, in flight
+        // during the products
+        floatx4 hq[NBW][PB];
+#pragma unroll
+        for (int q = 0; q < NBW; ++q)
+#pragma unroll
+            for (int pb = 0; pb < PB; ++pb)
+                hq[q][pb] = w + 4 * q < NB ? *reinterpret_cast<const floatx4 *>(ck_at(c, w + 4 * q, pb)) : zero4();
+        if (c > 0) issue(t0 - Q, Q, true);
+        // ---- per token j (8 threads each): row sums of dW.W and column sums
+        // of dW.e^{ec_i - ec_j} off the diagonal, and dW(j, j); dW(i, j) is
+        // the sum of S.D over the R x R block of the token pair
+        {
+            constexpr int QC = (Q + 7) / 8;
+            const int r0 = tid >> 3, ch = tid & 7;
+            auto dWf = [&](int i, int j) {
+                float s = 0.f;
 #pragma unroll
                 for (int r = 0; r < R; ++r)
 #pragma unroll
                     for (int r2 = 0; r2 < R; ++r2) s += SD[(i * R + r) * pV + j * R + r2];
-            DW[i * pQ + j] = s;
+                return s;
+            };
+            float rw = 0.f, ce = 0.f, dg = 0.f;
+            if (r0 < Q)
+#pragma unroll
+                for (int u = 0; u < QC; ++u) {
+                    const int j = ch * QC + u;
+                    if (j >= Q) continue;
+                    if (j < r0) rw += dWf(r0, j) * ET[r0 * pQ + j] * (sc(Cf::s_g, j) + sc(Cf::s_dn, j));
+                    if (j > r0) ce += dWf(j, r0) * ET[j * pQ + r0];
+                    if (j == r0) dg = dWf(r0, r0);
+                }
+            rw = row_sum<8>(rw);
+            ce = row_sum<8>(ce);
+            dg = row_sum<8>(dg);
+            if (ch == 0 && r0 < Q) {
+                DW[r0] = rw;
+                DW[pQ + r0] = ce;
+                DW[2 * pQ + r0] = dg;
+            }
         }
+        // ---- the six products; the gradient of H_c.  Outputs of token
+        // t0 + i, rank r are addressed as the chunk's base + a 32-bit offset.
+        const int64_t tb0 = tok(t0);
+        const int HR = p.H * R;
+        float *gxb = p.gx + tb0 * (R * P), *gBb = p.gB + tb0 * (R * N), *gCb = p.gC + tb0 * (R * N);
         const float eE = sc(Cf::s_misc, 0);
         float ev[VB][4];
-#pragma unroll
-        for (int kb = 0; kb < VB; ++kb)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) ev[kb][e] = sc(Cf::s_E, row_tok(kb * 16 + 4 * lg + e));
+        row_factor(Cf::s_E, ev);
         // dx = (W.S)^T gy + diag(U) B~ G   (tiles (vb, pb = w))
         if (w < PB) {
             const int pb = w;
             floatx4 acc[VB];
 #pragma unroll
             for (int vb = 0; vb < VB; ++vb) acc[vb] = zero4();
+            {
+                floatx4 av[2][VB];
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
+                for (int vb = 0; vb < VB; ++vb) av[0][vb] = lds4(BN + (vb * 16 + li) * pN + 4 * lg);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int k = nb * 16 + 4 * lg + e;
+                for (int nb = 0; nb < NB; ++nb) {
+                    const int cu = nb & 1, nx = cu ^ 1;
+                    if (nb + 1 < NB)
 #pragma unroll
-                    for (int vb = 0; vb < VB; ++vb) acc[vb] = mfma4(BT[k * pV + vb * 16 + li], G2[nb][e], acc[vb]);
+                        for (int vb = 0; vb < VB; ++vb) av[nx][vb] = lds4(BN + (vb * 16 + li) * pN + (nb + 1) * 16 + 4 * lg);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+#pragma unroll
+                        for (int vb = 0; vb < VB; ++vb) acc[vb] = mfma4(av[cu][vb][e], G2[nb][e], acc[vb]);
                 }
+                __builtin_amdgcn_sched_group_barrier(0x100, VB, 0);
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    if (nb + 1 < NB) __builtin_amdgcn_sched_group_barrier(0x100, VB, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x008, 4 * VB, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
 #pragma unroll
             for (int vb = 0; vb < VB; ++vb)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) acc[vb][e] *= sc(Cf::s_U, row_tok(vb * 16 + 4 * lg + e));
-            mm_lds<V, pV, pP, VB>(acc, MS, GN + pb * 16, li, lg);
+            mm_lds<V, pV, pV, VB>(acc, MS, T2 + pb * 16 * pV, li, lg);
 #pragma unroll
             for (int vb = 0; vb < VB; ++vb)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int v = vb * 16 + 4 * lg + e, i = v / R;
-                    if (v < VQ && i < Tc) p.gx[(tok(t0 + i) * R + (v - i * R)) * P + pb * 16 + li] = acc[vb][e];
+                    if (v < VQ && i < Tc) gxb[(i * HR + v - i * R) * P + pb * 16 + li] = acc[vb][e];
                 }
             // G <- e^{ec_end} G + C~^T diag(E) gy  (this orientation)
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                floatx4 a = G2[nb] * eE;
+            for (int nb = 0; nb < NB; ++nb) G2[nb] *= eE;
 #pragma unroll
-                for (int kb = 0; kb < VB; ++kb)
+            for (int kb = 0; kb < VB; ++kb) {
+                const floatx4 bq = lds4(T2 + (pb * 16 + li) * pV + 16 * kb + 4 * lg);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int v = kb * 16 + 4 * lg + e;
-                        a = mfma4(CN[v * pN + nb * 16 + li] * ev[kb][e], GN[v * pP + pb * 16 + li], a);
-                    }
-                G2[nb] = a;
+                for (int nb = 0; nb < NB; ++nb) {
+                    const floatx4 aq = lds4(CT + (nb * 16 + li) * pV + 16 * kb + 4 * lg);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) G2[nb] = mfma4(aq[e], bq[e] * ev[kb][e], G2[nb]);
+                }
             }
         }
         // dC~ and dB~ (tiles (vb, nb = w + 4 q)), rotated back; dPhi terms
@@ -488,22 +606,42 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
         for (int q = 0; q < NBW; ++q) {
             const int nb = w + 4 * q;
             if (nb >= NB) continue;
-            floatx4 dc[VB], db[VB], hq[PB];
-#pragma unroll
-            for (int pb = 0; pb < PB; ++pb) hq[pb] = *reinterpret_cast<const floatx4 *>(ck_at(c, nb, pb));
+            floatx4 dc[VB], db[VB];
 #pragma unroll
             for (int vb = 0; vb < VB; ++vb) dc[vb] = db[vb] = zero4();
+            {
+                floatx4 ag[2][VB], ax[2][VB];
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int pb = 0; pb < PB; ++pb)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int k = pb * 16 + 4 * lg + e;
-#pragma unroll
-                    for (int vb = 0; vb < VB; ++vb) {
-                        dc[vb] = mfma4(GT[k * pV + vb * 16 + li], hq[pb][e], dc[vb]);
-                        db[vb] = mfma4(XT[k * pV + vb * 16 + li], G1[q][pb][e], db[vb]);
-                    }
+                for (int vb = 0; vb < VB; ++vb) {
+                    ag[0][vb] = lds4(GN + (vb * 16 + li) * pP + 4 * lg);
+                    ax[0][vb] = lds4(XN + (vb * 16 + li) * pP + 4 * lg);
                 }
+#pragma unroll
+                for (int pb = 0; pb < PB; ++pb) {
+                    const int cu = pb & 1, nx = cu ^ 1;
+                    if (pb + 1 < PB)
+#pragma unroll
+                        for (int vb = 0; vb < VB; ++vb) {
+                            ag[nx][vb] = lds4(GN + (vb * 16 + li) * pP + (pb + 1) * 16 + 4 * lg);
+                            ax[nx][vb] = lds4(XN + (vb * 16 + li) * pP + (pb + 1) * 16 + 4 * lg);
+                        }
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+#pragma unroll
+                        for (int vb = 0; vb < VB; ++vb) {
+                            dc[vb] = mfma4(ag[cu][vb][e], hq[q][pb][e], dc[vb]);
+                            db[vb] = mfma4(ax[cu][vb][e], G1[q][pb][e], db[vb]);
+                        }
+                }
+                __builtin_amdgcn_sched_group_barrier(0x100, 2 * VB, 0);
+#pragma unroll
+                for (int pb = 0; pb < PB; ++pb) {
+                    if (pb + 1 < PB) __builtin_amdgcn_sched_group_barrier(0x100, 2 * VB, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x008, 8 * VB, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
 #pragma unroll
             for (int vb = 0; vb < VB; ++vb)
 #pragma unroll
@@ -514,45 +652,58 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
                     dc[vb][e] *= sc(Cf::s_E, ti);
                     db[vb][e] *= sc(Cf::s_U, ti);
                 }
-            mm_lds<V, pV, pN, VB>(dc, MT, BN + nb * 16, li, lg);
-            mm_lds<V, pV, pN, VB>(db, MN, CN + nb * 16, li, lg);
+            mm_lds<V, pV, pV, VB>(dc, MN, BT + nb * 16 * pV, li, lg);
+            mm_lds<V, pV, pV, VB>(db, MT, CT + nb * 16 * pV, li, lg);
 #pragma unroll
             for (int vb = 0; vb < VB; ++vb)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int v = vb * 16 + 4 * lg + e, n = nb * 16 + li, i = v / R;
                     const bool odd = n & 1;
-                    const float f = TF[min(i, Q - 1) * K + (n >> 1)];
-                    const float cs = __builtin_amdgcn_cosf(f), sn = __builtin_amdgcn_sinf(f);
+                    const float2 cz = CS[min(i, Q - 1) * pC + (n >> 1)];
+                    const float cs = cz.x, sn = cz.y;
                     const float ob = __shfl_xor(db[vb][e], 1), oc = __shfl_xor(dc[vb][e], 1);
                     const float b0 = odd ? ob : db[vb][e], b1 = odd ? db[vb][e] : ob;
                     const float c0 = odd ? oc : dc[vb][e], c1 = odd ? dc[vb][e] : oc;
                     if (v < VQ && i < Tc) {
-                        const int64_t o = (tok(t0 + i) * R + (v - i * R)) * N + n;
-                        p.gB[o] = odd ? sn * b0 + cs * b1 : cs * b0 - sn * b1;
-                        p.gC[o] = odd ? sn * c0 + cs * c1 : cs * c0 - sn * c1;
+                        const int o = (i * HR + v - i * R) * N + n;
+                        gBb[o] = odd ? sn * b0 + cs * b1 : cs * b0 - sn * b1;
+                        gCb[o] = odd ? sn * c0 + cs * c1 : cs * c0 - sn * c1;
                     }
                     if (!odd) {
                         const float2 bt = *reinterpret_cast<const float2 *>(BN + v * pN + n);
                         const float2 ct = *reinterpret_cast<const float2 *>(CN + v * pN + n);
-                        PH[v * K + (n >> 1)] = b0 * bt.y - b1 * bt.x + c0 * ct.y - c1 * ct.x;
+                        PH[v * pK + (n >> 1)] = b0 * bt.y - b1 * bt.x + c0 * ct.y - c1 * ct.x;
                     }
                 }
-            // d e^{ec_end} = <G, H_c>; then G <- e^{ec_end} G + C~^T diag(E) gy (this orientation)
+            // d e^{ec_end} = <G, H_c>
 #pragma unroll
-            for (int pb = 0; pb < PB; ++pb) {
+            for (int pb = 0; pb < PB; ++pb)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) pz += G1[q][pb][e] * hq[pb][e];
-                floatx4 a = G1[q][pb] * eE;
+                for (int e = 0; e < 4; ++e) pz += G1[q][pb][e] * hq[q][pb][e];
+        }
+        // G <- e^{ec_end} G + C~^T diag(E) gy  (the transposed orientation)
 #pragma unroll
-                for (int kb = 0; kb < VB; ++kb)
+        for (int q = 0; q < NBW; ++q)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int v = kb * 16 + 4 * lg + e;
-                        a = mfma4(GN[v * pP + pb * 16 + li] * ev[kb][e], CN[v * pN + nb * 16 + li], a);
-                    }
-                G1[q][pb] = a;
-            }
+            for (int pb = 0; pb < PB; ++pb) G1[q][pb] *= eE;
+#pragma unroll
+        for (int kb = 0; kb < VB; ++kb) {
+            floatx4 bc[NBW], ag[PB];
+#pragma unroll
+            for (int q = 0; q < NBW; ++q)
+                if (w + 4 * q < NB) bc[q] = lds4(CT + ((w + 4 * q) * 16 + li) * pV + 16 * kb + 4 * lg);
+#pragma unroll
+            for (int pb = 0; pb < PB; ++pb) ag[pb] = lds4(T2 + (pb * 16 + li) * pV + 16 * kb + 4 * lg);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int q = 0; q < NBW; ++q) {
+                    if (w + 4 * q >= NB) continue;
+                    const float bq = bc[q][e] * ev[kb][e];
+#pragma unroll
+                    for (int pb = 0; pb < PB; ++pb) G1[q][pb] = mfma4(ag[pb][e], bq, G1[q][pb]);
+                }
         }
         // per-row partial sums of dE and dU over this wave's columns
 #pragma unroll
@@ -570,16 +721,11 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
         pz += __shfl_xor(pz, 32);
         if (lane == 0) PZ[w * 4] = pz;
         __syncthreads();
-        // ---- the scalars (wave 0, lane = token) and dtheta (wave 1, lane = pair)
+        // ---- the scalars (wave 0, lane = token)
         if (w == 0) {
             const int j = lane;
             const bool tj = j < Q;
-            float colE = 0.f, rowW = 0.f;
-#pragma unroll 4
-            for (int i = 0; i < Q; ++i) {
-                if (tj && i > j) colE += DW[i * pQ + j] * ET[i * pQ + j];
-                if (tj && i < j) rowW += DW[j * pQ + i] * ET[j * pQ + i] * (sc(Cf::s_g, i) + sc(Cf::s_dn, i));
-            }
+            const int js = tj ? j : Q;
             float dEj = 0.f, dUj = 0.f;
             if (tj)
 #pragma unroll
@@ -589,18 +735,17 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
                         dEj += PE[ww * V + j * R + r];
                         dUj += PU[ww * V + j * R + r];
                     }
-            const int js = tj ? j : Q;
+            const float rowW = tj ? DW[j] : 0.f, colE = tj ? DW[pQ + j] : 0.f, dgj = tj ? DW[2 * pQ + j] : 0.f;
             const float Ej = sc(Cf::s_E, js), EUj = sc(Cf::s_EU, js), Uj = sc(Cf::s_U, js);
             const float gd = sc(Cf::s_g, js) + sc(Cf::s_dn, js);
-            const float dgam = (tj ? DW[j * pQ + j] : 0.f) + colE + dUj * EUj;
+            const float dgam = dgj + colE + dUj * EUj;
             const float ddn = colE + dUj * EUj;
             float dec = rowW - colE * gd + dEj * Ej - dUj * Uj;
-            float uu = dUj * Uj;
-#pragma unroll
-            for (int o = 1; o < kWave; o <<= 1) uu += __shfl_xor(uu, o);
+            auto last = [](float x) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), kWave - 1)); };
+            const float uu = last(wave_scan_dpp(dUj * Uj));
             if (j == Tc - 1) dec += uu + (PZ[0] + PZ[4] + PZ[8] + PZ[12]) * sc(Cf::s_misc, 0);
-            const float incl = wave_inclusive_sum(dec, lane);
-            const float dl = __shfl(incl, kWave - 1) - incl + dec;
+            const float incl = wave_scan_dpp(dec);
+            const float dl = last(incl) - incl + dec;
             const float dd = __shfl_up(ddn, 1);
             const float ddLast = __shfl(ddn, Q - 1);
             const float dtj = sc(Cf::s_dt, js), lmj = sc(Cf::s_lam, js);
@@ -618,18 +763,40 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
                 pend = true;
                 pd_g = dgam; pd_l = dl; pd_dt = dtj; pd_lam = lmj; pd_tok = tok(t0);
             }
-        } else if (w == 1 && lane < K) {
-            const int k = lane;
-#pragma unroll 4
-            for (int i = Q - 1; i >= 0; --i) {
-                if (i < Tc) {
-                    float s = 0.f;
+        }
+        // ---- dtheta_t = carry + the suffix sum of dPhi over the chunk (every
+        // wave: lane = 8 segments x 8 pairs, segment totals scanned over lanes
+        // 8 apart, fp64)
 #pragma unroll
-                    for (int r = 0; r < R; ++r) s += PH[(i * R + r) * K + k];
-                    acc_th += double(s);
-                    p.gtheta[tok(t0 + i) * K + k] = float(acc_th);
-                }
+        for (int kp = 0; kp < KP; ++kp) {
+            const int k = 32 * kp + 8 * w + (lane & 7), seg = lane >> 3;
+            const bool kv = k < K;
+            const int kc = kv ? k : 0;
+            double ls[TPS];
+            double run = 0.0;
+#pragma unroll
+            for (int u = TPS - 1; u >= 0; --u) {
+                const int i = seg * TPS + u;
+                float s = 0.f;
+                if (i < Tc)
+#pragma unroll
+                    for (int r = 0; r < R; ++r) s += PH[(i * R + r) * pK + kc];
+                run += double(s);
+                ls[u] = run;
             }
+            double x = run;
+#pragma unroll
+            for (int o = 8; o < kWave; o <<= 1) {
+                const double y = __shfl_down(x, o, kWave);
+                if (lane + o < kWave) x += y;
+            }
+            const double ex = x - run;
+#pragma unroll
+            for (int u = 0; u < TPS; ++u) {
+                const int i = seg * TPS + u;
+                if (kv && i < Tc) p.gtheta[tb0 * K + (i * p.H * K + k)] = float(carry[kp] + ex + ls[u]);
+            }
+            carry[kp] += __shfl(x, lane & 7, kWave);
         }
         __syncthreads();
     }
@@ -688,7 +855,12 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
                 if (lg == 0 && p.gprevB0) p.gprevB0[(bh * R + r) * N + n] = dl0 * s;
             }
         }
-        if (p.gphi0 && w == 1 && lane < K) p.gphi0[bh * K + lane] = float(acc_th);
+        if (p.gphi0)
+#pragma unroll
+            for (int kp = 0; kp < KP; ++kp) {
+                const int k = 32 * kp + 8 * w + lane;
+                if (lane < 8 && k < K) p.gphi0[bh * K + k] = float(carry[kp]);
+            }
         __syncthreads();
         dd0 = PZ[1] + PZ[5] + PZ[9] + PZ[13];
     }
