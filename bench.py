@@ -87,12 +87,31 @@ def backward_bytes(b, T, H, P, N, R, s=2):
     return b * T * H * (rd + wr)
 
 
-def time_backward(torch, mixer, inp, reps=3):
+FP32_MFMA_PEAK_TFLOPS = 157.3
+
+
+def backward_flops(b, T, H, P, N, R, rows=32):
+    """Algorithmic flops of the chunked backward's products, chunks of
+    rows // R tokens: per chunk, the five masked products over token pairs
+    i >= j (S = C~ B~^T, D = gy x^T, (W.S)^T gy, (W.D) B~, (W.D)^T C~) and the
+    five state-sized ones (B~ G, gy H^T, x G^T, the update of G, and the
+    forward sweep's update of H), each counted once."""
+    Q = rows // R
+    total = 0
+    for c in range(math.ceil(T / Q)):
+        q = min(Q, T - Q * c)
+        pairs = q * (q + 1) // 2
+        total += pairs * R * R * 2 * (3 * N + 2 * P) + 5 * q * R * N * P * 2
+    return total * b * H
+
+
+def time_backward(torch, mixer, inp, reps=10, warmup=10):
     args = [inp[k] for k in ("x", "dt", "A", "lam", "theta", "B", "C")]
     g = torch.Generator(device="cuda")
     g.manual_seed(7)
     gy = torch.randn(inp["x"].shape, generator=g, device="cuda").to(inp["x"].dtype)
-    mixer.backward(*args, gy)
+    for _ in range(warmup):
+        mixer.backward(*args, gy)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
@@ -437,11 +456,14 @@ def main():
     if not args.no_backward:
         msb = time_backward(torch, mixer, inp)
         bb = backward_bytes(b, T, H, P, N, R)
+        bf = backward_flops(b, T, H, P, N, R)
         result["backward_siso_prefill"] = {
             "workload": c1["name"], "ms_per_call": round(msb, 3),
             "tokens_per_s": round(b * T / (msb / 1000), 1), "alg_bytes": bb,
             "frac_of_hbm_peak_at_alg_bytes": round(bb / (msb / 1000) / 1e9 / HBM_PEAK_GBS, 4),
-            "note": "sequential adjoint per (batch, head); bound by the per-token dependency chain"}
+            "alg_flops": bf, "tflops_at_alg_flops": round(bf / (msb / 1000) / 1e12, 2),
+            "frac_of_fp32_mfma_peak": round(bf / (msb / 1000) / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4),
+            "note": "chunked, 32 (token, rank) rows per chunk, products on fp32 MFMA"}
         log(f"[siso backward] {msb:.3f} ms/call")
 
     if not args.no_cpu:
@@ -461,10 +483,14 @@ def main():
         ms2b = None
         if not args.no_backward:
             msw = time_backward(torch, mixer, inp)
+            bf2 = backward_flops(b2, T2, H2, P2, N2, R2)
+            bb2 = backward_bytes(b2, T2, H2, P2, N2, R2)
             result["backward_mimo_prefill"] = {
                 "workload": c2["name"], "ms_per_call": round(msw, 3),
-                "tokens_per_s": round(b2 * T2 / (msw / 1000), 1),
-                "alg_bytes": backward_bytes(b2, T2, H2, P2, N2, R2)}
+                "tokens_per_s": round(b2 * T2 / (msw / 1000), 1), "alg_bytes": bb2,
+                "frac_of_hbm_peak_at_alg_bytes": round(bb2 / (msw / 1000) / 1e9 / HBM_PEAK_GBS, 4),
+                "alg_flops": bf2, "tflops_at_alg_flops": round(bf2 / (msw / 1000) / 1e12, 2),
+                "frac_of_fp32_mfma_peak": round(bf2 / (msw / 1000) / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4)}
             log(f"[mimo backward] {msw:.3f} ms/call")
         if not args.no_block:
             blk, z = block_params(torch, H2, R2, N2, inp["x"].shape)
