@@ -192,25 +192,31 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
     typedef typename io4<IO>::raw raw4;
     raw4 qb[NBL], qc[NBL], qx[NXL], qg[NXL];
     uint32_t qth[KP][TPS], qdt = 0, qlm = 0;
+    // (addresses: the chunk's first token + a 32-bit offset; token i of the
+    // chunk is i * H rows further)
     auto issue = [&](int64_t t0, int Tc, bool bwd) {
+        const int64_t tb = tok(t0);
+        const int HR = p.H * R;
+        const IO *bb = Bg + tb * (R * N), *cb = Cg + tb * (R * N), *xb = xg + tb * (R * P), *gb = gyg + tb * (R * P);
 #pragma unroll
         for (int j = 0; j < NBL; ++j) {
             const int gi = tid + j * kBwdThreads;
             const int v = gi % V, n = 4 * (gi / V), i = v / R;
             const bool ok = gi < V * N / 4 && v < VQ && i < Tc;
-            const int64_t off = ok ? tok(t0 + i) * (R * N) + (v - i * R) * N + n : 0;
-            qb[j] = io4<IO>::load(Bg + off);
-            if (bwd) qc[j] = io4<IO>::load(Cg + off);
+            const int off = ok ? (i * HR + v - i * R) * N + n : 0;
+            qb[j] = io4<IO>::load(bb + off);
+            if (bwd) qc[j] = io4<IO>::load(cb + off);
         }
 #pragma unroll
         for (int j = 0; j < NXL; ++j) {
             const int gi = tid + j * kBwdThreads;
             const int v = gi % V, pc = 4 * (gi / V), i = v / R;
             const bool ok = gi < V * P / 4 && v < VQ && i < Tc;
-            const int64_t off = ok ? tok(t0 + i) * (R * P) + (v - i * R) * P + pc : 0;
-            qx[j] = io4<IO>::load(xg + off);
-            if (bwd) qg[j] = io4<IO>::load(gyg + off);
+            const int off = ok ? (i * HR + v - i * R) * P + pc : 0;
+            qx[j] = io4<IO>::load(xb + off);
+            if (bwd) qg[j] = io4<IO>::load(gb + off);
         }
+        const IO *tbp = thg + tb * K;
 #pragma unroll
         for (int kp = 0; kp < KP; ++kp) {
             const int k = 32 * kp + 8 * w + (lane & 7), seg = lane >> 3;
@@ -218,14 +224,14 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
 #pragma unroll
             for (int u = 0; u < TPS; ++u) {
                 const int i = seg * TPS + u;
-                qth[kp][u] = io<IO>::raw(thg + tok(t0 + (i < Tc ? i : 0)) * K + kc);
+                qth[kp][u] = io<IO>::raw(tbp + ((i < Tc ? i : 0) * p.H * K + kc));
             }
         }
         if (w == 0) {
             const int i = lane;
             const bool ld = i < Tc || (i == Q && t0 + Q < T);
-            qdt = io<IO>::raw(dtg + tok(t0 + (ld ? i : 0)));
-            qlm = io<IO>::raw(lmg + tok(t0 + (ld ? i : 0)));
+            qdt = io<IO>::raw(dtg + tb + (ld ? i : 0) * p.H);
+            qlm = io<IO>::raw(lmg + tb + (ld ? i : 0) * p.H);
         }
     };
 
@@ -662,7 +668,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
                     const bool odd = n & 1;
                     const float2 cz = CS[min(i, Q - 1) * pC + (n >> 1)];
                     const float cs = cz.x, sn = cz.y;
-                    const float ob = __shfl_xor(db[vb][e], 1), oc = __shfl_xor(dc[vb][e], 1);
+                    const float ob = dpp_f32<0xb1>(db[vb][e]), oc = dpp_f32<0xb1>(dc[vb][e]); // lane ^ 1
                     const float b0 = odd ? ob : db[vb][e], b1 = odd ? db[vb][e] : ob;
                     const float c0 = odd ? oc : dc[vb][e], c1 = odd ? dc[vb][e] : oc;
                     if (v < VQ && i < Tc) {

@@ -83,3 +83,37 @@ def test_mimo_decode_full_size():
         eh = slice_err(hg, hT, (0, 1))
         print(f"decode (b={bi}, h={hi}): y err {e:.2e}, state err {eh:.2e}")
         assert e <= TOL["bf16"] and eh <= TOL["bf16"]
+
+
+def _check_backward(cfg, picks):
+    """The backward at the full workload size: every per-token gradient of
+    sampled (batch, head) sequences against the oracle's fp64 autograd
+    gradients of that sequence alone (sequences are independent).  dA sums
+    over the batch and is checked at the small sizes of test_gpu_backward."""
+    from oracle import backward as ob
+    from mamba_selective_ssm_ssd_amd import mixer
+    c = synth.CONFIGS[cfg]
+    b, T, H, P, N, R = (c[k] for k in ("batch", "T", "H", "P", "N", "R"))
+    inp = synth.torch_inputs(b, T, H, P, N, R, io="bf16", seed=0)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    gy = torch.randn(inp["x"].shape, generator=g, device="cuda").to(torch.bfloat16)
+    grads = mixer.backward(*(inp[k] for k in ("x", "dt", "A", "lam", "theta", "B", "C")), gy)
+    torch.cuda.synchronize()
+    axes = dict(x=(0, 2), dt=(0, 2), lam=(0, 2), theta=(0, 2), B=(0, 2), C=(0, 2))
+    for bi, hi in picks:
+        d = {k: v.astype(np.float64) for k, v in _sample_inputs(inp, bi, hi).items()}
+        gys = gy[bi:bi + 1, :, hi:hi + 1].double().cpu().numpy()
+        _, r = ob.grad(d, gys)
+        errs = {k: slice_err(grads[k][bi:bi + 1, :, hi:hi + 1].double().cpu().numpy(), r[k], axes[k]) for k in axes}
+        print(f"cfg{cfg} backward (b={bi}, h={hi}): " + " ".join(f"{k} {v:.1e}" for k, v in errs.items()))
+        for k, v in errs.items():
+            assert v <= 1e-4, f"gradient of {k}: {v:.3e}"
+
+
+def test_siso_backward_full_size():
+    _check_backward(1, [(0, 3), (3, 60)])
+
+
+def test_mimo_backward_full_size():
+    _check_backward(2, [(1, 9), (2, 50)])
