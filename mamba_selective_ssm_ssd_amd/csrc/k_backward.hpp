@@ -50,7 +50,11 @@
 
 namespace m3 {
 
-constexpr int kBwdThreads = 256; // 4 waves, one per SIMD
+// 8 waves, two per SIMD, in two groups of four: waves 0-3 carry G in one
+// orientation (dx and its update), waves 4-7 in the other (dC~, dB~ and its
+// update), so that one wave's vector work overlaps the other's MFMAs.
+constexpr int kBwdThreads = 512;
+constexpr int kBwdWaves = kBwdThreads / 64;
 
 // v_mfma_f32_16x16x4_f32: lane l supplies A[l % 16][slot l / 16] and
 // B[slot l / 16][l % 16]; element e of the result is D[4 (l / 16) + e][l % 16].
@@ -106,7 +110,9 @@ struct BwdCfg {
     // row pitches 4 x odd: 16-byte reads of 16 rows hit distinct banks
     static constexpr int pV = V + 4, pN = N + 4, pP = P + 4, pK = K + 4, pC = K + 1, pQ = QP + 1, SQ = 36;
     static constexpr int TPS = (Q + 7) / 8; // tokens per segment of the angle scans
-    static constexpr int KP = (K + 31) / 32; // passes of the angle scans (32 pairs each)
+    static constexpr int KS = 8 * kBwdWaves, KP = (K + KS - 1) / KS; // pairs per pass, passes of the angle scans
+    static constexpr int NBH = (NB + kBwdWaves - 1) / kBwdWaves; // forward sweep: column blocks per wave
+    static constexpr int GSN = NB > NBW * PB ? NB : NBW * PB;   // registers of G (either orientation)
     // token scalar tables, SQ floats each
     static constexpr int s_ec = 0, s_E = 1, s_EU = 2, s_U = 3, s_g = 4, s_dn = 5, s_dt = 6, s_lam = 7, s_misc = 8;
     // LDS (floats)
@@ -134,6 +140,7 @@ struct BwdCfg {
     static constexpr size_t bytes = size_t(floats) * 4;
     static_assert(bytes <= kMaxLdsBytes, "backward LDS layout exceeds the workgroup's LDS");
     static_assert(Q * 8 <= kBwdThreads, "one group of 8 threads per token");
+    static_assert(PB <= 4, "one column block of dx per wave of the first group");
     // 4-element groups of B / C and of x / gy per chunk, per thread
     static constexpr int NBL = (V * N / 4 + kBwdThreads - 1) / kBwdThreads;
     static constexpr int NXL = (V * P / 4 + kBwdThreads - 1) / kBwdThreads;
@@ -143,7 +150,8 @@ template <typename IO, int N, int P, int R>
 __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
     typedef BwdCfg<N, P, R> Cf;
     constexpr int V = Cf::V, Q = Cf::Q, VQ = Cf::VQ, QP = Cf::QP, K = Cf::K;
-    constexpr int NB = Cf::NB, PB = Cf::PB, VB = Cf::VB, NBW = Cf::NBW, TPS = Cf::TPS, KP = Cf::KP;
+    constexpr int NB = Cf::NB, PB = Cf::PB, VB = Cf::VB, NBW = Cf::NBW, TPS = Cf::TPS, KP = Cf::KP, KS = Cf::KS;
+    constexpr int NBH = Cf::NBH, GSN = Cf::GSN;
     constexpr int pV = Cf::pV, pN = Cf::pN, pP = Cf::pP, pK = Cf::pK, pC = Cf::pC, pQ = Cf::pQ, SQ = Cf::SQ;
     constexpr int NBL = Cf::NBL, NXL = Cf::NXL;
     extern __shared__ __align__(16) float sm[];
@@ -219,7 +227,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
         const IO *tbp = thg + tb * K;
 #pragma unroll
         for (int kp = 0; kp < KP; ++kp) {
-            const int k = 32 * kp + 8 * w + (lane & 7), seg = lane >> 3;
+            const int k = KS * kp + 8 * w + (lane & 7), seg = lane >> 3;
             const int kc = k < K ? k : 0;
 #pragma unroll
             for (int u = 0; u < TPS; ++u) {
@@ -270,7 +278,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
     auto stage_angles = [&](int64_t t0, int Tc, bool fwd, int c) {
 #pragma unroll
         for (int kp = 0; kp < KP; ++kp) {
-            const int k = 32 * kp + 8 * w + (lane & 7), seg = lane >> 3;
+            const int k = KS * kp + 8 * w + (lane & 7), seg = lane >> 3;
             const bool kv = k < K;
             const int kc = kv ? k : 0;
             const double ph0 = fwd ? PHE[kc] : ckp[int64_t(c) * K + kc];
@@ -365,18 +373,19 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
     };
 
     // ===================== forward sweep: H_c and Phi at each chunk start
-    // Hf: transposed tiles (pb, nb = w + 4 q) of H_c; element e of lane
-    // (li, lg) is H[nb*16 + li][pb*16 + 4 lg + e].  G1 below has this layout.
-    floatx4 Hf[NBW][PB];
+    // Hf: transposed tiles (pb, nb = w + 8 q) of H_c; element e of lane
+    // (li, lg) is H[nb*16 + li][pb*16 + 4 lg + e] (the layout of G in the
+    // second wave group below).
+    floatx4 Hf[NBH][PB];
     {
         const float d0 = io<IO>::get(dtg + tok(0)), l0 = io<IO>::get(lmg + tok(0));
         const float dl0 = (1.f - l0) * d0;
 #pragma unroll
-        for (int q = 0; q < NBW; ++q)
+        for (int q = 0; q < NBH; ++q)
 #pragma unroll
             for (int pb = 0; pb < PB; ++pb) {
                 Hf[q][pb] = zero4();
-                const int nb = w + 4 * q;
+                const int nb = w + kBwdWaves * q;
                 if (nb >= NB || !p.has_init) continue;
                 const int n = nb * 16 + li, pc = pb * 16 + 4 * lg;
                 const float4 hv = *reinterpret_cast<const float4 *>(p.h0 + (bh * N + n) * int64_t(P) + pc);
@@ -400,10 +409,10 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
         const int64_t t0 = int64_t(c) * Q;
         const int Tc = int(min<int64_t>(T - t0, Q));
 #pragma unroll
-        for (int q = 0; q < NBW; ++q)
+        for (int q = 0; q < NBH; ++q)
 #pragma unroll
             for (int pb = 0; pb < PB; ++pb)
-                if (w + 4 * q < NB) *reinterpret_cast<floatx4 *>(ck_at(c, w + 4 * q, pb)) = Hf[q][pb];
+                if (w + kBwdWaves * q < NB) *reinterpret_cast<floatx4 *>(ck_at(c, w + kBwdWaves * q, pb)) = Hf[q][pb];
         stage_scalars(t0, Tc);
         stage_angles(t0, Tc, true, c);
         stage_xg(Tc, true);
@@ -417,22 +426,22 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
             float uv[VB][4];
             row_factor(Cf::s_U, uv);
 #pragma unroll
-            for (int q = 0; q < NBW; ++q)
+            for (int q = 0; q < NBH; ++q)
 #pragma unroll
                 for (int pb = 0; pb < PB; ++pb) Hf[q][pb] *= eE;
 #pragma unroll
             for (int kb = 0; kb < VB; ++kb) {
-                floatx4 bv[NBW], av[PB];
+                floatx4 bv[NBH], av[PB];
 #pragma unroll
-                for (int q = 0; q < NBW; ++q)
-                    if (w + 4 * q < NB) bv[q] = lds4(BT + ((w + 4 * q) * 16 + li) * pV + 16 * kb + 4 * lg);
+                for (int q = 0; q < NBH; ++q)
+                    if (w + kBwdWaves * q < NB) bv[q] = lds4(BT + ((w + kBwdWaves * q) * 16 + li) * pV + 16 * kb + 4 * lg);
 #pragma unroll
                 for (int pb = 0; pb < PB; ++pb) av[pb] = lds4(T2 + (pb * 16 + li) * pV + 16 * kb + 4 * lg);
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
 #pragma unroll
-                    for (int q = 0; q < NBW; ++q) {
-                        if (w + 4 * q >= NB) continue;
+                    for (int q = 0; q < NBH; ++q) {
+                        if (w + kBwdWaves * q >= NB) continue;
                         const float bq = bv[q][e] * uv[kb][e];
 #pragma unroll
                         for (int pb = 0; pb < PB; ++pb) Hf[q][pb] = mfma4(av[pb][e], bq, Hf[q][pb]);
@@ -443,15 +452,15 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
     }
 
     // ===================== backward sweep
-    // G1: the gradient G of H_{c+1} in Hf's layout; G2: G in tiles (nb, pb = w),
-    // element e of lane (li, lg) = G[nb*16 + 4 lg + e][w*16 + li].
-    floatx4 G1[NBW][PB], G2[NB];
+    // G, the gradient of H_{c+1}, in registers GS: waves 0-3 hold G in tiles
+    // (nb, pb = w), element e of lane (li, lg) = G[nb*16 + 4 lg + e][w*16 + li]
+    // (G2 below); waves 4-7 hold it in Hf's transposed layout, tiles
+    // (pb, nb = w - 4 + 4 q) (G1 below).
+    floatx4 GS[GSN];
 #pragma unroll
-    for (int q = 0; q < NBW; ++q)
-#pragma unroll
-        for (int pb = 0; pb < PB; ++pb) G1[q][pb] = zero4();
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) G2[nb] = zero4();
+    for (int i = 0; i < GSN; ++i) GS[i] = zero4();
+#define G2(nb) GS[nb]
+#define G1(q, pb) GS[(q) * PB + (pb)]
     double carry[KP];    // lanes (pair, segment): sum of dPhi over the later chunks
 #pragma unroll
     for (int kp = 0; kp < KP; ++kp) carry[kp] = 0.0;
@@ -476,8 +485,9 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
         rot_store(qb, Tc, BT, BN);
         rot_store(qc, Tc, CT, CN);
         __syncthreads();
-        // ---- S = C~ B~^T and D = gy x^T, one 16 x 16 tile per wave; masks
-        {
+        // ---- S = C~ B~^T and D = gy x^T, one 16 x 16 tile per wave of the
+        // first group; masks
+        if (w < 4) {
             const int vb = w >> 1, vb2 = w & 1;
             floatx4 S[1] = {zero4()}, D[1] = {zero4()};
             mm_lds<N, pN, pN, 1>(S, CN + vb * 16 * pN, BN + vb2 * 16 * pN, li, lg);
@@ -497,13 +507,16 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
         __syncthreads();
         // H_c (this wave's tiles) and the previous chunk's inputs, in flight
         // during the products
+        const int wb = w - 4; // wave index in the second group
         floatx4 hq[NBW][PB];
 #pragma unroll
         for (int q = 0; q < NBW; ++q)
 #pragma unroll
             for (int pb = 0; pb < PB; ++pb)
-                hq[q][pb] = w + 4 * q < NB ? *reinterpret_cast<const floatx4 *>(ck_at(c, w + 4 * q, pb)) : zero4();
-        if (c > 0) issue(t0 - Q, Q, true);
+                hq[q][pb] = w >= 4 && wb + 4 * q < NB ? *reinterpret_cast<const floatx4 *>(ck_at(c, wb + 4 * q, pb)) : zero4();
+        // (the first group, whose products are fewer, prefetches now, the
+        // second after its products)
+        if (c > 0 && w < 4) issue(t0 - Q, Q, true);
         // ---- per token j (8 threads each): row sums of dW.W and column sums
         // of dW.e^{ec_i - ec_j} off the diagonal, and dW(j, j); dW(i, j) is
         // the sum of S.D over the R x R block of the token pair
@@ -565,7 +578,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
 #pragma unroll
-                        for (int vb = 0; vb < VB; ++vb) acc[vb] = mfma4(av[cu][vb][e], G2[nb][e], acc[vb]);
+                        for (int vb = 0; vb < VB; ++vb) acc[vb] = mfma4(av[cu][vb][e], G2(nb)[e], acc[vb]);
                 }
                 __builtin_amdgcn_sched_group_barrier(0x100, VB, 0);
 #pragma unroll
@@ -589,7 +602,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
                 }
             // G <- e^{ec_end} G + C~^T diag(E) gy  (this orientation)
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) G2[nb] *= eE;
+            for (int nb = 0; nb < NB; ++nb) G2(nb) *= eE;
 #pragma unroll
             for (int kb = 0; kb < VB; ++kb) {
                 const floatx4 bq = lds4(T2 + (pb * 16 + li) * pV + 16 * kb + 4 * lg);
@@ -597,7 +610,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
                 for (int nb = 0; nb < NB; ++nb) {
                     const floatx4 aq = lds4(CT + (nb * 16 + li) * pV + 16 * kb + 4 * lg);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) G2[nb] = mfma4(aq[e], bq[e] * ev[kb][e], G2[nb]);
+                    for (int e = 0; e < 4; ++e) G2(nb) = mfma4(aq[e], bq[e] * ev[kb][e], G2(nb));
                 }
             }
         }
@@ -610,8 +623,8 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
         float pz = 0.f;
 #pragma unroll
         for (int q = 0; q < NBW; ++q) {
-            const int nb = w + 4 * q;
-            if (nb >= NB) continue;
+            const int nb = wb + 4 * q;
+            if (w < 4 || nb >= NB) continue;
             floatx4 dc[VB], db[VB];
 #pragma unroll
             for (int vb = 0; vb < VB; ++vb) dc[vb] = db[vb] = zero4();
@@ -637,7 +650,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
 #pragma unroll
                         for (int vb = 0; vb < VB; ++vb) {
                             dc[vb] = mfma4(ag[cu][vb][e], hq[q][pb][e], dc[vb]);
-                            db[vb] = mfma4(ax[cu][vb][e], G1[q][pb][e], db[vb]);
+                            db[vb] = mfma4(ax[cu][vb][e], G1(q, pb)[e], db[vb]);
                         }
                 }
                 __builtin_amdgcn_sched_group_barrier(0x100, 2 * VB, 0);
@@ -686,29 +699,30 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
 #pragma unroll
             for (int pb = 0; pb < PB; ++pb)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) pz += G1[q][pb][e] * hq[q][pb][e];
+                for (int e = 0; e < 4; ++e) pz += G1(q, pb)[e] * hq[q][pb][e];
         }
         // G <- e^{ec_end} G + C~^T diag(E) gy  (the transposed orientation)
+        if (w >= 4) {
 #pragma unroll
         for (int q = 0; q < NBW; ++q)
 #pragma unroll
-            for (int pb = 0; pb < PB; ++pb) G1[q][pb] *= eE;
+            for (int pb = 0; pb < PB; ++pb) G1(q, pb) *= eE;
 #pragma unroll
         for (int kb = 0; kb < VB; ++kb) {
             floatx4 bc[NBW], ag[PB];
 #pragma unroll
             for (int q = 0; q < NBW; ++q)
-                if (w + 4 * q < NB) bc[q] = lds4(CT + ((w + 4 * q) * 16 + li) * pV + 16 * kb + 4 * lg);
+                if (wb + 4 * q < NB) bc[q] = lds4(CT + ((wb + 4 * q) * 16 + li) * pV + 16 * kb + 4 * lg);
 #pragma unroll
             for (int pb = 0; pb < PB; ++pb) ag[pb] = lds4(T2 + (pb * 16 + li) * pV + 16 * kb + 4 * lg);
 #pragma unroll
             for (int e = 0; e < 4; ++e)
 #pragma unroll
                 for (int q = 0; q < NBW; ++q) {
-                    if (w + 4 * q >= NB) continue;
+                    if (wb + 4 * q >= NB) continue;
                     const float bq = bc[q][e] * ev[kb][e];
 #pragma unroll
-                    for (int pb = 0; pb < PB; ++pb) G1[q][pb] = mfma4(ag[pb][e], bq, G1[q][pb]);
+                    for (int pb = 0; pb < PB; ++pb) G1(q, pb) = mfma4(ag[pb][e], bq, G1(q, pb));
                 }
         }
         // per-row partial sums of dE and dU over this wave's columns
@@ -718,14 +732,16 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
             for (int e = 0; e < 4; ++e) {
                 const float se = row_sum<16>(pe[vb][e]), su = row_sum<16>(pu[vb][e]);
                 if (li == 0) {
-                    PE[w * V + vb * 16 + 4 * lg + e] = se;
-                    PU[w * V + vb * 16 + 4 * lg + e] = su;
+                    PE[wb * V + vb * 16 + 4 * lg + e] = se;
+                    PU[wb * V + vb * 16 + 4 * lg + e] = su;
                 }
             }
         pz = row_sum<16>(pz);
         pz += __shfl_xor(pz, 16);
         pz += __shfl_xor(pz, 32);
-        if (lane == 0) PZ[w * 4] = pz;
+        if (lane == 0) PZ[wb * 4] = pz;
+        if (c > 0) issue(t0 - Q, Q, true);
+        }
         __syncthreads();
         // ---- the scalars (wave 0, lane = token)
         if (w == 0) {
@@ -775,7 +791,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
         // 8 apart, fp64)
 #pragma unroll
         for (int kp = 0; kp < KP; ++kp) {
-            const int k = 32 * kp + 8 * w + (lane & 7), seg = lane >> 3;
+            const int k = KS * kp + 8 * w + (lane & 7), seg = lane >> 3;
             const bool kv = k < K;
             const int kc = kv ? k : 0;
             double ls[TPS];
@@ -824,7 +840,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) s += p.prevB0[(bh * R + r) * N + nb * 16 + 4 * lg + e] * G2[nb][e];
+                    for (int e = 0; e < 4; ++e) s += p.prevB0[(bh * R + r) * N + nb * 16 + 4 * lg + e] * G2(nb)[e];
                 s += __shfl_xor(s, 16);
                 s += __shfl_xor(s, 32);
                 if (lg == 0 && p.gprevx0) p.gprevx0[(bh * R + r) * P + pc] = dl0 * s;
@@ -834,18 +850,19 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
         part = row_sum<16>(part);
         part += __shfl_xor(part, 16);
         part += __shfl_xor(part, 32);
-        if (lane == 0) PZ[w * 4 + 1] = part;
+        if (lane == 0 && w < 4) PZ[w * 4 + 1] = part;
         // from G1 (rows n = nb*16 + li): dh~_{-1} and dB~_{-1}
+        const int wb = w - 4;
 #pragma unroll
         for (int q = 0; q < NBW; ++q) {
-            const int nb = w + 4 * q;
-            if (nb >= NB) continue;
+            const int nb = wb + 4 * q;
+            if (w < 4 || nb >= NB) continue;
             const int n = nb * 16 + li;
 #pragma unroll
             for (int pb = 0; pb < PB; ++pb)
                 if (p.gh0)
                     *reinterpret_cast<float4 *>(p.gh0 + (bh * N + n) * int64_t(P) + pb * 16 + 4 * lg) =
-                        make_float4(G1[q][pb][0], G1[q][pb][1], G1[q][pb][2], G1[q][pb][3]);
+                        make_float4(G1(q, pb)[0], G1(q, pb)[1], G1(q, pb)[2], G1(q, pb)[3]);
 #pragma unroll
             for (int r = 0; r < R; ++r) {
                 float s = 0.f;
@@ -854,7 +871,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
                     float xv[4];
                     io<IO>::load4(static_cast<const IO *>(p.prevx0) + (bh * R + r) * P + pb * 16 + 4 * lg, xv);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) s += G1[q][pb][e] * xv[e];
+                    for (int e = 0; e < 4; ++e) s += G1(q, pb)[e] * xv[e];
                 }
                 s += __shfl_xor(s, 16);
                 s += __shfl_xor(s, 32);
@@ -864,7 +881,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
         if (p.gphi0)
 #pragma unroll
             for (int kp = 0; kp < KP; ++kp) {
-                const int k = 32 * kp + 8 * w + lane;
+                const int k = KS * kp + 8 * w + lane;
                 if (lane < 8 && k < K) p.gphi0[bh * K + k] = float(carry[kp]);
             }
         __syncthreads();
@@ -879,6 +896,8 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
         for (int o = 1; o < kWave; o <<= 1) gA += __shfl_xor(gA, o);
         if (lane == 0) p.gA_part[bh] = gA;
     }
+#undef G1
+#undef G2
 }
 
 // Sum of the per-(batch, head) partials of dA over the batch.
