@@ -476,6 +476,14 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
         stage_scalars(t0, Tc);
         stage_angles(t0, Tc, false, c);
         stage_xg(Tc, false);
+        // H_c (the second group's tiles), in flight during the staging
+        const int wb = w - 4; // wave index in the second group
+        floatx4 hq[NBW][PB];
+#pragma unroll
+        for (int q = 0; q < NBW; ++q)
+#pragma unroll
+            for (int pb = 0; pb < PB; ++pb)
+                hq[q][pb] = w >= 4 && wb + 4 * q < NB ? *reinterpret_cast<const floatx4 *>(ck_at(c, wb + 4 * q, pb)) : zero4();
         __syncthreads();
         // ---- rotate; the table of e^{ec_i - ec_j}
         for (int idx = tid; idx < QP * QP; idx += kBwdThreads) {
@@ -486,7 +494,73 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
         rot_store(qc, Tc, CT, CN);
         __syncthreads();
         // ---- S = C~ B~^T and D = gy x^T, one 16 x 16 tile per wave of the
-        // first group; masks
+        // first group; masks.  The second group meanwhile starts dC~ and dB~
+        // with gy H_c^T and x G^T (nothing of this phase needed), their row
+        // dots with C~ and B~ (the partial sums of dE and dU) and <G, H_c>.
+        floatx4 dcq[NBW][VB], dbq[NBW][VB];
+        float pe[VB][4], pu[VB][4];
+#pragma unroll
+        for (int vb = 0; vb < VB; ++vb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) pe[vb][e] = pu[vb][e] = 0.f;
+        float pz = 0.f;
+        if (w >= 4) {
+#pragma unroll
+            for (int q = 0; q < NBW; ++q) {
+                const int nb = wb + 4 * q;
+                if (nb >= NB) continue;
+                floatx4 (&dc)[VB] = dcq[q], (&db)[VB] = dbq[q];
+#pragma unroll
+                for (int vb = 0; vb < VB; ++vb) dc[vb] = db[vb] = zero4();
+                {
+                    floatx4 ag[2][VB], ax[2][VB];
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int vb = 0; vb < VB; ++vb) {
+                        ag[0][vb] = lds4(GN + (vb * 16 + li) * pP + 4 * lg);
+                        ax[0][vb] = lds4(XN + (vb * 16 + li) * pP + 4 * lg);
+                    }
+#pragma unroll
+                    for (int pb = 0; pb < PB; ++pb) {
+                        const int cu = pb & 1, nx = cu ^ 1;
+                        if (pb + 1 < PB)
+#pragma unroll
+                            for (int vb = 0; vb < VB; ++vb) {
+                                ag[nx][vb] = lds4(GN + (vb * 16 + li) * pP + (pb + 1) * 16 + 4 * lg);
+                                ax[nx][vb] = lds4(XN + (vb * 16 + li) * pP + (pb + 1) * 16 + 4 * lg);
+                            }
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+#pragma unroll
+                            for (int vb = 0; vb < VB; ++vb) {
+                                dc[vb] = mfma4(ag[cu][vb][e], hq[q][pb][e], dc[vb]);
+                                db[vb] = mfma4(ax[cu][vb][e], G1(q, pb)[e], db[vb]);
+                            }
+                    }
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2 * VB, 0);
+#pragma unroll
+                    for (int pb = 0; pb < PB; ++pb) {
+                        if (pb + 1 < PB) __builtin_amdgcn_sched_group_barrier(0x100, 2 * VB, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x008, 8 * VB, 0);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+#pragma unroll
+                for (int vb = 0; vb < VB; ++vb)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int v = vb * 16 + 4 * lg + e, n = nb * 16 + li, ti = row_tok(v);
+                        pe[vb][e] += dc[vb][e] * CN[v * pN + n];
+                        pu[vb][e] += db[vb][e] * BN[v * pN + n];
+                        dc[vb][e] *= sc(Cf::s_E, ti);
+                        db[vb][e] *= sc(Cf::s_U, ti);
+                    }
+#pragma unroll
+                for (int pb = 0; pb < PB; ++pb)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) pz += G1(q, pb)[e] * hq[q][pb][e];
+            }
+        }
         if (w < 4) {
             const int vb = w >> 1, vb2 = w & 1;
             floatx4 S[1] = {zero4()}, D[1] = {zero4()};
@@ -505,17 +579,9 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
             }
         }
         __syncthreads();
-        // H_c (this wave's tiles) and the previous chunk's inputs, in flight
-        // during the products
-        const int wb = w - 4; // wave index in the second group
-        floatx4 hq[NBW][PB];
-#pragma unroll
-        for (int q = 0; q < NBW; ++q)
-#pragma unroll
-            for (int pb = 0; pb < PB; ++pb)
-                hq[q][pb] = w >= 4 && wb + 4 * q < NB ? *reinterpret_cast<const floatx4 *>(ck_at(c, wb + 4 * q, pb)) : zero4();
-        // (the first group, whose products are fewer, prefetches now, the
-        // second after its products)
+        // the previous chunk's inputs, in flight during the products (the first
+        // group, whose products are fewer, prefetches now, the second after its
+        // products)
         if (c > 0 && w < 4) issue(t0 - Q, Q, true);
         // ---- per token j (8 threads each): row sums of dW.W and column sums
         // of dW.e^{ec_i - ec_j} off the diagonal, and dW(j, j); dW(i, j) is
@@ -614,63 +680,12 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
                 }
             }
         }
-        // dC~ and dB~ (tiles (vb, nb = w + 4 q)), rotated back; dPhi terms
-        float pe[VB][4], pu[VB][4];
-#pragma unroll
-        for (int vb = 0; vb < VB; ++vb)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) pe[vb][e] = pu[vb][e] = 0.f;
-        float pz = 0.f;
+        // dC~ and dB~ (tiles (vb, nb = w + 4 q)) completed, rotated back; dPhi terms
 #pragma unroll
         for (int q = 0; q < NBW; ++q) {
             const int nb = wb + 4 * q;
             if (w < 4 || nb >= NB) continue;
-            floatx4 dc[VB], db[VB];
-#pragma unroll
-            for (int vb = 0; vb < VB; ++vb) dc[vb] = db[vb] = zero4();
-            {
-                floatx4 ag[2][VB], ax[2][VB];
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int vb = 0; vb < VB; ++vb) {
-                    ag[0][vb] = lds4(GN + (vb * 16 + li) * pP + 4 * lg);
-                    ax[0][vb] = lds4(XN + (vb * 16 + li) * pP + 4 * lg);
-                }
-#pragma unroll
-                for (int pb = 0; pb < PB; ++pb) {
-                    const int cu = pb & 1, nx = cu ^ 1;
-                    if (pb + 1 < PB)
-#pragma unroll
-                        for (int vb = 0; vb < VB; ++vb) {
-                            ag[nx][vb] = lds4(GN + (vb * 16 + li) * pP + (pb + 1) * 16 + 4 * lg);
-                            ax[nx][vb] = lds4(XN + (vb * 16 + li) * pP + (pb + 1) * 16 + 4 * lg);
-                        }
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-#pragma unroll
-                        for (int vb = 0; vb < VB; ++vb) {
-                            dc[vb] = mfma4(ag[cu][vb][e], hq[q][pb][e], dc[vb]);
-                            db[vb] = mfma4(ax[cu][vb][e], G1(q, pb)[e], db[vb]);
-                        }
-                }
-                __builtin_amdgcn_sched_group_barrier(0x100, 2 * VB, 0);
-#pragma unroll
-                for (int pb = 0; pb < PB; ++pb) {
-                    if (pb + 1 < PB) __builtin_amdgcn_sched_group_barrier(0x100, 2 * VB, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x008, 8 * VB, 0);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-            }
-#pragma unroll
-            for (int vb = 0; vb < VB; ++vb)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int v = vb * 16 + 4 * lg + e, n = nb * 16 + li, ti = row_tok(v);
-                    pe[vb][e] += dc[vb][e] * CN[v * pN + n];
-                    pu[vb][e] += db[vb][e] * BN[v * pN + n];
-                    dc[vb][e] *= sc(Cf::s_E, ti);
-                    db[vb][e] *= sc(Cf::s_U, ti);
-                }
+            floatx4 (&dc)[VB] = dcq[q], (&db)[VB] = dbq[q];
             mm_lds<V, pV, pV, VB>(dc, MN, BT + nb * 16 * pV, li, lg);
             mm_lds<V, pV, pV, VB>(db, MT, CT + nb * 16 * pV, li, lg);
 #pragma unroll
@@ -695,11 +710,6 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
                         PH[v * pK + (n >> 1)] = b0 * bt.y - b1 * bt.x + c0 * ct.y - c1 * ct.x;
                     }
                 }
-            // d e^{ec_end} = <G, H_c>
-#pragma unroll
-            for (int pb = 0; pb < PB; ++pb)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) pz += G1(q, pb)[e] * hq[q][pb][e];
         }
         // G <- e^{ec_end} G + C~^T diag(E) gy  (the transposed orientation)
         if (w >= 4) {
