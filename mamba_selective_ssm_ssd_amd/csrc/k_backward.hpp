@@ -69,9 +69,9 @@ __device__ __forceinline__ floatx4 lds4(const float *q) { return *reinterpret_ca
 // a[(16 vb + i) * PA + k], B[k][j] = bm[j * PBM + k] (both k-contiguous).
 // Lane (i, g) reads four consecutive k (16 kb + 4 g ..) of its row and
 // column with one 16-byte read each: steps (kb, 0..3).
-// The reads of group kb + 1 are issued before the products of group kb
-// (the schedule is pinned: one wave per SIMD leaves no other wave to cover
-// the LDS latency).
+// The reads of group kb + 1 are issued before the products of group kb (the
+// schedule is pinned, so that each group of MFMAs has the next group's
+// operands in flight).
 template <int KD, int PA, int PBM, int NV>
 __device__ __forceinline__ void mm_lds(floatx4 (&acc)[NV], const float *a, const float *bm, int i, int g) {
     constexpr int NK = KD / 16;
