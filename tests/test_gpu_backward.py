@@ -73,3 +73,26 @@ def test_backward_short_and_ragged(T):
     errs = _run(1, T, 3, 16, 32, 2, "f32", seed=T, with_init=True)
     for k, v in errs.items():
         assert v <= BAR, f"T={T}: gradient of {k}: error {v:.3e}"
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_backward_random_case(seed):
+    """Seeded random configurations: N, P, R, I/O type, batch, heads, T
+    (several chunks with a ragged tail, or fewer tokens than one chunk) and a
+    carried state or none."""
+    rng = np.random.default_rng(3000 + seed)
+    N = int(rng.choice([16, 32, 64, 128]))
+    P = int(rng.choice([16, 32, 64]))
+    R = int(rng.integers(1, 5))
+    io = str(rng.choice(["f32", "bf16"]))
+    b, H = int(rng.integers(1, 3)), int(rng.integers(1, 4))
+    T = int(rng.integers(1, 320))
+    with_init = bool(rng.random() < 0.5)
+    from mamba_selective_ssm_ssd_amd import capi, mixer
+    if capi.m3_ssm_prefill_backward_workspace_bytes(mixer.make_shape(b, T, H, P, N, R, torch_io(io))) == 0:
+        pytest.skip(f"shape outside the compiled set (the shapes m3_ssm_prefill supports): N{N} P{P} R{R} {io}")
+    errs = _run(b, T, H, P, N, R, io, seed=4000 + seed, with_init=with_init)
+    print(f"case {seed}: N{N} P{P} R{R} {io} b{b} H{H} T{T} init={with_init}: "
+          + " ".join(f"{k} {v:.1e}" for k, v in errs.items()))
+    for k, v in errs.items():
+        assert v <= BAR, f"case {seed}: gradient of {k}: error {v:.3e}"
