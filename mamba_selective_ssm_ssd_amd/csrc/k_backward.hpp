@@ -693,18 +693,17 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int v = vb * 16 + 4 * lg + e, n = nb * 16 + li, i = v / R;
-                    const bool odd = n & 1;
-                    const float2 cz = CS[min(i, Q - 1) * pC + (n >> 1)];
-                    const float cs = cz.x, sn = cz.y;
-                    const float ob = dpp_f32<0xb1>(db[vb][e]), oc = dpp_f32<0xb1>(dc[vb][e]); // lane ^ 1
-                    const float b0 = odd ? ob : db[vb][e], b1 = odd ? db[vb][e] : ob;
-                    const float c0 = odd ? oc : dc[vb][e], c1 = odd ? dc[vb][e] : oc;
-                    if (v < VQ && i < Tc) {
-                        const int o = (i * HR + v - i * R) * N + n;
-                        gBb[o] = odd ? sn * b0 + cs * b1 : cs * b0 - sn * b1;
-                        gCb[o] = odd ? sn * c0 + cs * c1 : cs * c0 - sn * c1;
-                    }
-                    if (!odd) {
+                    // the even lane of each row pair takes its partner's
+                    // values and writes both rotated outputs (8 bytes)
+                    const float b1 = dpp_f32<0xb1>(db[vb][e]), c1 = dpp_f32<0xb1>(dc[vb][e]); // lane ^ 1
+                    if (!(n & 1)) {
+                        const float b0 = db[vb][e], c0 = dc[vb][e];
+                        const float2 cz = CS[min(i, Q - 1) * pC + (n >> 1)];
+                        if (v < VQ && i < Tc) {
+                            const int o = (i * HR + v - i * R) * N + n;
+                            *reinterpret_cast<float2 *>(gBb + o) = make_float2(cz.x * b0 - cz.y * b1, cz.y * b0 + cz.x * b1);
+                            *reinterpret_cast<float2 *>(gCb + o) = make_float2(cz.x * c0 - cz.y * c1, cz.y * c0 + cz.x * c1);
+                        }
                         const float2 bt = *reinterpret_cast<const float2 *>(BN + v * pN + n);
                         const float2 ct = *reinterpret_cast<const float2 *>(CN + v * pN + n);
                         PH[v * pK + (n >> 1)] = b0 * bt.y - b1 * bt.x + c0 * ct.y - c1 * ct.x;
