@@ -275,7 +275,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
     // fp64: lane = 8 segments x 8 pairs, a segment's prefix in registers, the
     // segment totals scanned over lanes 8 apart.  Writes CS (cos and sin of
     // Phi_t) and PHE (the wrapped angle of the chunk's last token).
-    auto stage_angles = [&](int64_t t0, int Tc, bool fwd, int c) {
+    auto stage_angles = [&](int Tc, bool fwd, int c) {
 #pragma unroll
         for (int kp = 0; kp < KP; ++kp) {
             const int k = KS * kp + 8 * w + (lane & 7), seg = lane >> 3;
@@ -414,7 +414,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
             for (int pb = 0; pb < PB; ++pb)
                 if (w + kBwdWaves * q < NB) *reinterpret_cast<floatx4 *>(ck_at(c, w + kBwdWaves * q, pb)) = Hf[q][pb];
         stage_scalars(t0, Tc);
-        stage_angles(t0, Tc, true, c);
+        stage_angles(Tc, true, c);
         stage_xg(Tc, true);
         __syncthreads();
         rot_store(qb, Tc, BT, nullptr);
@@ -474,7 +474,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
         const int64_t t0 = int64_t(c) * Q;
         const int Tc = int(min<int64_t>(T - t0, Q));
         stage_scalars(t0, Tc);
-        stage_angles(t0, Tc, false, c);
+        stage_angles(Tc, false, c);
         stage_xg(Tc, false);
         // H_c (the second group's tiles), in flight during the staging
         const int wb = w - 4; // wave index in the second group
