@@ -72,33 +72,32 @@ __device__ __forceinline__ floatx4 lds4(const float *q) { return *reinterpret_ca
 // The reads of group kb + 1 are issued before the products of group kb (the
 // schedule is pinned, so that each group of MFMAs has the next group's
 // operands in flight).
-template <int KD, int PA, int PBM, int NV>
+// ZV >= 0: the block of A in row block ZV and k block ZK is known to be zero
+// (a masked triangle) and its products are skipped.
+template <int KD, int PA, int PBM, int NV, int ZV = -1, int ZK = -1>
 __device__ __forceinline__ void mm_lds(floatx4 (&acc)[NV], const float *a, const float *bm, int i, int g) {
     constexpr int NK = KD / 16;
+    auto live = [](int vb, int kb) { return !(vb == ZV && kb == ZK); };
     floatx4 bv[2], av[2][NV];
     __builtin_amdgcn_sched_barrier(0);
     bv[0] = lds4(bm + i * PBM + 4 * g);
 #pragma unroll
-    for (int vb = 0; vb < NV; ++vb) av[0][vb] = lds4(a + (16 * vb + i) * PA + 4 * g);
+    for (int vb = 0; vb < NV; ++vb)
+        if (live(vb, 0)) av[0][vb] = lds4(a + (16 * vb + i) * PA + 4 * g);
 #pragma unroll
     for (int kb = 0; kb < NK; ++kb) {
         const int cu = kb & 1, nx = cu ^ 1;
         if (kb + 1 < NK) {
             bv[nx] = lds4(bm + i * PBM + 16 * (kb + 1) + 4 * g);
 #pragma unroll
-            for (int vb = 0; vb < NV; ++vb) av[nx][vb] = lds4(a + (16 * vb + i) * PA + 16 * (kb + 1) + 4 * g);
+            for (int vb = 0; vb < NV; ++vb)
+                if (live(vb, kb + 1)) av[nx][vb] = lds4(a + (16 * vb + i) * PA + 16 * (kb + 1) + 4 * g);
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e)
 #pragma unroll
-            for (int vb = 0; vb < NV; ++vb) acc[vb] = mfma4(av[cu][vb][e], bv[cu][e], acc[vb]);
-    }
-    // reads of group 0, then per group: the next group's reads, its MFMAs
-    __builtin_amdgcn_sched_group_barrier(0x100, 1 + NV, 0);
-#pragma unroll
-    for (int kb = 0; kb < NK; ++kb) {
-        if (kb + 1 < NK) __builtin_amdgcn_sched_group_barrier(0x100, 1 + NV, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 4 * NV, 0);
+            for (int vb = 0; vb < NV; ++vb)
+                if (live(vb, kb)) acc[vb] = mfma4(av[cu][vb][e], bv[cu][e], acc[vb]);
     }
     __builtin_amdgcn_sched_barrier(0);
 }
@@ -141,6 +140,10 @@ struct BwdCfg {
     static_assert(bytes <= kMaxLdsBytes, "backward LDS layout exceeds the workgroup's LDS");
     static_assert(Q * 8 <= kBwdThreads, "one group of 8 threads per token");
     static_assert(PB <= 4, "one column block of dx per wave of the first group");
+    // with R dividing 16 no token's rows straddle the two 16-row blocks, so
+    // the masks vanish on the block of later rows x earlier columns' transpose
+    static constexpr bool TRI = 16 % R == 0 && V == 32;
+    static constexpr int ZLO = TRI ? 1 : -1, ZHI = TRI ? 0 : -1; // row block with a zero k block
     // 4-element groups of B / C and of x / gy per chunk, per thread
     static constexpr int NBL = (V * N / 4 + kBwdThreads - 1) / kBwdThreads;
     static constexpr int NXL = (V * P / 4 + kBwdThreads - 1) / kBwdThreads;
@@ -151,7 +154,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
     typedef BwdCfg<N, P, R> Cf;
     constexpr int V = Cf::V, Q = Cf::Q, VQ = Cf::VQ, QP = Cf::QP, K = Cf::K;
     constexpr int NB = Cf::NB, PB = Cf::PB, VB = Cf::VB, NBW = Cf::NBW, TPS = Cf::TPS, KP = Cf::KP, KS = Cf::KS;
-    constexpr int NBH = Cf::NBH, GSN = Cf::GSN;
+    constexpr int NBH = Cf::NBH, GSN = Cf::GSN, ZLO = Cf::ZLO, ZHI = Cf::ZHI;
     constexpr int pV = Cf::pV, pN = Cf::pN, pP = Cf::pP, pK = Cf::pK, pC = Cf::pC, pQ = Cf::pQ, SQ = Cf::SQ;
     constexpr int NBL = Cf::NBL, NXL = Cf::NXL;
     extern __shared__ __align__(16) float sm[];
@@ -564,8 +567,10 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
         if (w < 4) {
             const int vb = w >> 1, vb2 = w & 1;
             floatx4 S[1] = {zero4()}, D[1] = {zero4()};
-            mm_lds<N, pN, pN, 1>(S, CN + vb * 16 * pN, BN + vb2 * 16 * pN, li, lg);
-            mm_lds<P, pP, pP, 1>(D, GN + vb * 16 * pP, XN + vb2 * 16 * pP, li, lg);
+            if (!(Cf::TRI && vb == 0 && vb2 == 1)) { // that tile is masked out entirely
+                mm_lds<N, pN, pN, 1>(S, CN + vb * 16 * pN, BN + vb2 * 16 * pN, li, lg);
+                mm_lds<P, pP, pP, 1>(D, GN + vb * 16 * pP, XN + vb2 * 16 * pP, li, lg);
+            }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int v = vb * 16 + 4 * lg + e, v2 = vb2 * 16 + li;
@@ -658,7 +663,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
             for (int vb = 0; vb < VB; ++vb)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) acc[vb][e] *= sc(Cf::s_U, row_tok(vb * 16 + 4 * lg + e));
-            mm_lds<V, pV, pV, VB>(acc, MS, T2 + pb * 16 * pV, li, lg);
+            mm_lds<V, pV, pV, VB, ZLO, 0>(acc, MS, T2 + pb * 16 * pV, li, lg);
 #pragma unroll
             for (int vb = 0; vb < VB; ++vb)
 #pragma unroll
@@ -686,8 +691,8 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
             const int nb = wb + 4 * q;
             if (w < 4 || nb >= NB) continue;
             floatx4 (&dc)[VB] = dcq[q], (&db)[VB] = dbq[q];
-            mm_lds<V, pV, pV, VB>(dc, MN, BT + nb * 16 * pV, li, lg);
-            mm_lds<V, pV, pV, VB>(db, MT, CT + nb * 16 * pV, li, lg);
+            mm_lds<V, pV, pV, VB, ZHI, 1>(dc, MN, BT + nb * 16 * pV, li, lg);
+            mm_lds<V, pV, pV, VB, ZLO, 0>(db, MT, CT + nb * 16 * pV, li, lg);
 #pragma unroll
             for (int vb = 0; vb < VB; ++vb)
 #pragma unroll
