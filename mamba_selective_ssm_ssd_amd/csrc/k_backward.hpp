@@ -108,6 +108,7 @@ struct BwdCfg {
     static constexpr int K = N / 2, NB = N / 16, PB = P / 16, VB = V / 16, NBW = (NB + 3) / 4;
     // row pitches 4 x odd: 16-byte reads of 16 rows hit distinct banks
     static constexpr int pV = V + 4, pN = N + 4, pP = P + 4, pK = K + 4, pC = K + 1, pQ = QP + 1, SQ = 36;
+    static_assert(P <= 2 * V, "the forward sweep's second x^T buffer is the mask area");
     static constexpr int TPS = (Q + 7) / 8; // tokens per segment of the angle scans
     static constexpr int KS = 8 * kBwdWaves, KP = (K + KS - 1) / KS; // pairs per pass, passes of the angle scans
     static constexpr int NBH = (NB + kBwdWaves - 1) / kBwdWaves; // forward sweep: column blocks per wave
@@ -341,7 +342,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
     };
     // x (and gy) of the chunk into LDS: the forward sweep keeps x transposed
     // (T2); the backward sweep keeps x row-major (XN) and gy both ways (GN, T2)
-    auto stage_xg = [&](int Tc, bool fwd) {
+    auto stage_xg = [&](int Tc, bool fwd, float *xT) {
 #pragma unroll
         for (int j = 0; j < NXL; ++j) {
             const int gi = tid + j * kBwdThreads;
@@ -358,7 +359,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
             }
             if (fwd) {
 #pragma unroll
-                for (int q = 0; q < 4; ++q) T2[(pc + q) * pV + v] = xv[q];
+                for (int q = 0; q < 4; ++q) xT[(pc + q) * pV + v] = xv[q];
             } else {
                 *reinterpret_cast<float4 *>(XN + v * pP + pc) = make_float4(xv[0], xv[1], xv[2], xv[3]);
                 *reinterpret_cast<float4 *>(GN + v * pP + pc) = make_float4(gv[0], gv[1], gv[2], gv[3]);
@@ -418,16 +419,21 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
                 if (w + kBwdWaves * q < NB) *reinterpret_cast<floatx4 *>(ck_at(c, w + kBwdWaves * q, pb)) = Hf[q][pb];
         stage_scalars(t0, Tc);
         stage_angles(Tc, true, c);
-        stage_xg(Tc, true);
+        // x^T alternates between two buffers (T2 and the mask area, unused in
+        // this sweep), so the next chunk's staging needs no barrier after
+        // this chunk's update; the token factors are read before the second
+        // barrier for the same reason
+        float *xT = (c & 1) ? MS : T2;
+        stage_xg(Tc, true, xT);
         __syncthreads();
         rot_store(qb, Tc, BT, nullptr);
+        const float eE = sc(Cf::s_misc, 0);
+        float uv[VB][4];
+        row_factor(Cf::s_U, uv);
         __syncthreads();
         if (c + 1 < nC) issue(t0 + Q, int(min<int64_t>(T - t0 - Q, Q)), false);
         // H^T[p][n] <- e^{ec_end} H^T + sum_v x[v][p] U_v B~[v][n]
         {
-            const float eE = sc(Cf::s_misc, 0);
-            float uv[VB][4];
-            row_factor(Cf::s_U, uv);
 #pragma unroll
             for (int q = 0; q < NBH; ++q)
 #pragma unroll
@@ -439,7 +445,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
                 for (int q = 0; q < NBH; ++q)
                     if (w + kBwdWaves * q < NB) bv[q] = lds4(BT + ((w + kBwdWaves * q) * 16 + li) * pV + 16 * kb + 4 * lg);
 #pragma unroll
-                for (int pb = 0; pb < PB; ++pb) av[pb] = lds4(T2 + (pb * 16 + li) * pV + 16 * kb + 4 * lg);
+                for (int pb = 0; pb < PB; ++pb) av[pb] = lds4(xT + (pb * 16 + li) * pV + 16 * kb + 4 * lg);
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
 #pragma unroll
@@ -451,8 +457,8 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
                     }
             }
         }
-        __syncthreads();
     }
+    __syncthreads(); // the backward sweep's staging reuses the LDS
 
     // ===================== backward sweep
     // G, the gradient of H_{c+1}, in registers GS: waves 0-3 hold G in tiles
@@ -478,7 +484,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
         const int Tc = int(min<int64_t>(T - t0, Q));
         stage_scalars(t0, Tc);
         stage_angles(Tc, false, c);
-        stage_xg(Tc, false);
+        stage_xg(Tc, false, nullptr);
         // H_c (the second group's tiles), in flight during the staging
         const int wb = w - 4; // wave index in the second group
         floatx4 hq[NBW][PB];
