@@ -42,7 +42,12 @@ typedef struct {
     float *prev_x; /* [b][H][R][P]  of its previous x                         */
 } m3_grads_t;
 
-/* Bytes of device workspace m3_ssm_prefill_backward needs (0: unsupported). */
+/* Bytes of device workspace m3_ssm_prefill_backward needs (0: unsupported).
+ * The pass stores the state entering every chunk of 32 / R tokens in fp32
+ * and the angle there in fp64, so the size grows with the sequence:
+ * batch * H * ceil(T / (32 / R)) * (N * P * 4 + N / 2 * 8) bytes, plus
+ * alignment and 4 bytes per (batch, head).  The workspace is caller-owned
+ * and needs no initialisation. */
 size_t m3_ssm_prefill_backward_workspace_bytes(const m3_shape_t *shape);
 
 /*

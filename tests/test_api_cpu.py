@@ -264,3 +264,16 @@ def test_backward_errors():
     assert bwd(_shape(), grads=capi.m3_grads_t(*([FAKE] * 7 + [FAKE_MISALIGNED, None, None, None]))) \
         == capi.M3_ERR_INVALID_ARGUMENT
     assert bwd(_shape(dstate=5)) == capi.M3_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("b,T,H,P,N,R", [(4, 2048, 64, 64, 128, 1), (4, 2048, 64, 64, 64, 4),
+                                        (1, 150, 2, 32, 64, 3), (2, 1, 3, 16, 16, 2)])
+def test_backward_workspace_size_as_documented(b, T, H, P, N, R):
+    """include/m3_ssm_backward.h: per (batch, head), one fp32 state and one
+    fp64 angle vector per chunk of 32 / R tokens, plus alignment and 4 bytes."""
+    import math
+    torch = pytest.importorskip("torch")
+    from mamba_selective_ssm_ssd_amd import capi, mixer
+    got = capi.m3_ssm_prefill_backward_workspace_bytes(mixer.make_shape(b, T, H, P, N, R, torch.bfloat16))
+    est = b * H * math.ceil(T / (32 // R)) * (N * P * 4 + N // 2 * 8) + 4 * b * H
+    assert est <= got <= est + 3 * 256
