@@ -83,13 +83,21 @@ typedef enum {
     M3_ERR_HIP = 4               /* a kernel launch failed                              */
 } m3_status_t;
 
-/* Problem size.  Supported: chunk = 64; headdim P in {16, 32, 64};
- * dstate N in {16, 32, 64, 128}; rank R in 1..4; any batch >= 1, nheads >= 1
- * and seqlen >= 1 (a ragged last chunk is masked).  io_dtype is an
- * m3_dtype_t value.  A prefill workgroup keeps one chunk's operands in the
- * 160 KB of LDS of a gfx950 compute unit; (N, P, R) combinations that do not
- * fit (with fp32 I/O: N = 128 with R >= 2, N = 64 with R = 4) are reported as
- * M3_ERR_UNSUPPORTED by the prefill entry points (and a zero workspace size).
+/* Problem size.  Supported: headdim P in {16, 32, 64}; dstate N in
+ * {16, 32, 64, 128}; rank R in 1..4, in both I/O types; any batch >= 1,
+ * nheads >= 1 and seqlen >= 1 (a ragged last chunk is masked).  io_dtype is
+ * an m3_dtype_t value.
+ * chunk is the chunk length Q in tokens of the chunked (SSD) form, 64 or the
+ * rank's small chunk qs(R) = 64 / R tokens (R = 3: 32), i.e. 64 virtual
+ * (token, rank) rows, the chunk that the Mamba-3 review's FLOP count for MIMO
+ * (section 3.3, R times the SISO cost) describes.  A prefill workgroup keeps
+ * one chunk's operands in the 160 KB of LDS of a gfx950 compute unit; with
+ * chunk = 64, shapes whose 64-token chunk does not fit (with fp32 I/O: N = 64
+ * with R = 4, N = 128 with R >= 2) take chunks of qs(R) tokens.  qs(R)
+ * divides 64, so either chunking gives the same result up to rounding.
+ * Another chunk value is M3_ERR_UNSUPPORTED.
+ * Element offsets within one token are 32-bit: 64 * nheads * R * max(N, P)
+ * (and 64 * ngroups * R * N) must stay below 2^31, else M3_ERR_UNSUPPORTED.
  * ngroups < 0 or not dividing nheads is M3_ERR_INVALID_ARGUMENT.
  * state_dtype BF16 keeps h~ in bf16 (round to nearest even at every store;
  * all arithmetic stays fp32): half the state traffic of a decode step, at a
@@ -102,7 +110,7 @@ typedef struct {
     int32_t headdim;  /* P */
     int32_t dstate;   /* N, even */
     int32_t rank;     /* R, 1 = SISO */
-    int32_t chunk;    /* Q, must be 64 */
+    int32_t chunk;    /* Q: 64, or qs(R) = 64 / R tokens (R = 3: 32) */
     int32_t io_dtype; /* m3_dtype_t */
     int32_t ngroups;  /* G: B and C shared by groups of H/G consecutive heads; 0 = H */
     int32_t state_dtype; /* m3_dtype_t of the carried state h~: F32 (0, default) or BF16 */
@@ -118,9 +126,12 @@ typedef struct {
 
 /* Bytes of device workspace m3_ssm_prefill needs for this shape (0 if the
  * shape is invalid or unsupported).  When batch * nheads is too small to fill
- * the GPU, each sequence is cut into segments of whole chunks; the workspace
- * holds each segment's aggregate (an N x P fp32 state, its summed log decay
- * and rotation angle) and the carried state at the sequence start. */
+ * the GPU (below 256), each sequence is cut into S segments of whole chunks;
+ * the workspace holds each segment's aggregate (an N x P fp32 state, its
+ * summed log decay and rotation angle) and the carried state at the sequence
+ * start.  It is sized for the largest S any chunk length of the shape can
+ * give, so it serves m3_ssm_prefill_block too; batch * nheads * S <= 256, so
+ * it never exceeds about 17 MB.  With S = 1 it is 256 bytes, unused. */
 size_t m3_ssm_prefill_workspace_bytes(const m3_shape_t *shape);
 
 /*

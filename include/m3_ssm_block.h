@@ -27,9 +27,12 @@
  * must stay valid until the stream reaches the call.  A NULL block pointer,
  * or a block with no piece present, gives exactly m3_ssm_prefill /
  * m3_ssm_decode_step.  M3_ERR_INVALID_ARGUMENT: a misaligned block pointer,
- * or eps < 0 or not finite with bc_norm set.  M3_ERR_UNSUPPORTED: a prefill
- * shape whose kernel has no LDS left for the head's weight/bias table
- * (bf16 I/O with N = 128, P = 64, R = 4); decode takes every shape.
+ * or eps < 0 or not finite with bc_norm set.  The block kernels also keep
+ * the head's weight/bias table in LDS: with chunk = 64, a shape whose
+ * 64-token chunk then no longer fits (bf16 I/O with N = 128, P = 64, R = 4,
+ * and the fp32 shapes m3_ssm.h lists) takes chunks of qs(R) tokens, as
+ * m3_ssm_prefill does; the workspace m3_ssm_prefill_workspace_bytes reports
+ * serves both.  Every shape of m3_ssm.h is supported.
  */
 #ifndef M3_SSM_BLOCK_H
 #define M3_SSM_BLOCK_H

@@ -63,9 +63,10 @@ constexpr size_t align16(size_t v) { return (v + 15) / 16 * 16; }
 // (narrow layout) by 8 elements only.
 constexpr int lds_pitch(int n, bool wide) { return wide ? (n + 31) / 32 * 32 + 16 : n + 8; }
 
-template <typename IO, int N_, int P_, int R_, bool WIDE, bool BLK, bool BPAD = false>
+template <typename IO, int N_, int P_, int R_, int Q_, bool WIDE, bool BLK, bool BPAD = false>
 struct CfgW {
-    static constexpr int N = N_, P = P_, R = R_, K = N / 2, V = kQ * R;
+    // Q tokens per chunk, V = Q R virtual rows (token, rank) per chunk
+    static constexpr int N = N_, P = P_, R = R_, Q = Q_, K = N / 2, V = Q * R;
     static constexpr bool kWide = WIDE;
     // (BLK) the block prologue's weight/bias table [4][R][N] floats sits in
     // its own region, or (BPAD) one float4 per staged-B row in that row's
@@ -110,29 +111,34 @@ struct CfgW {
     static constexpr size_t o_bs = 0;                                          // [PL][V][NBP]
     static constexpr size_t o_xr = o_bs + size_t(PL) * BS_PS * 2;              // [PL][V][PP]
     static constexpr size_t o_ht = o_xr + size_t(PL) * X_PS * 2;               // [PL][P][NBP]
-    static constexpr size_t o_cs = o_ht + size_t(PL) * HT_PS * 2;              // float [64][CSP]
-    static constexpr size_t o_coef = o_cs + size_t(kQ) * CSP * 4;              // [2][4][64]: ell, gam, wgt, scl
-    static constexpr size_t o_misc = o_coef + 2 * 4 * kQ * 4;                  // [2] g_c, [2] delta_0
+    static constexpr size_t o_cs = o_ht + size_t(PL) * HT_PS * 2;              // float [Q][CSP]
+    static constexpr size_t o_coef = o_cs + size_t(Q) * CSP * 4;               // [2][4][64]: ell, gam, wgt, scl (lane = token)
+    static constexpr size_t o_misc = o_coef + 2 * 4 * kWave * 4;                  // [2] g_c, [2] delta_0
     static constexpr size_t o_thc = o_misc + 64;                               // float2 [2][K]: cos, sin Theta_c
     static constexpr size_t o_ths = o_thc + 2 * size_t(K) * 8;                 // double [K]: running angle
     // The chunk's token mask L[t][s] (and e^{ell_t}) is tabulated once per
     // chunk when it fits; otherwise each lane evaluates its mask entries.
-    static constexpr int LWP = WIDE ? kQ + 8 : kQ + 4;                         // row pitch (floats)
+    static constexpr int LWP = WIDE ? Q + 8 : Q + 4;                           // row pitch (floats)
     // block prologue tables (BLK): B weight, B bias, C weight, C bias [R][N]
     static constexpr size_t o_blk = align16(o_ths + size_t(K) * 8);
     static constexpr size_t blk_bytes = BLK && !BPAD ? 16 * size_t(R) * N : 0;
-    static constexpr size_t o_lw = align16(o_blk + blk_bytes);                 // float [64][LWP]
-    static constexpr size_t lw_bytes = size_t(kQ) * LWP * 4 + kQ * 4;          // + e^{ell} [64]
+    static constexpr size_t o_lw = align16(o_blk + blk_bytes);                 // float [Q][LWP]
+    static constexpr size_t lw_bytes = size_t(Q) * LWP * 4 + Q * 4;            // + e^{ell} [Q]
     static constexpr bool LWT = o_lw + lw_bytes <= kMaxLdsBytes;
     // bf16 I/O: the within-chunk angle prefix is the matrix product of the
     // lower-triangular ones matrix with the chunk's theta (MFMA, fp32
     // accumulation), read from a row-major theta table; otherwise (fp32 I/O,
     // or fewer than 16 pairs) exact fixed-point DPP scans.
+    // The table has at least 32 rows (one k-step of the product); rows past
+    // the chunk's last token repeat that token (finite values that meet zero
+    // entries of the ones matrix).
     static constexpr int THP = lds_pitch(K, WIDE);                             // theta table pitch (elements)
-    static constexpr int URT = K * SZ / 16, UT = kQ * URT, UPT_T = (UT + kPT - 1) / kPT;
-    static constexpr int NPB = K / 16, NTT = 4 * NPB;                          // 16x16 prefix tiles
-    static constexpr size_t o_th = align16(o_lw + (LWT ? lw_bytes : 0));       // bf16 [64][THP]
-    static constexpr size_t th_bytes = size_t(kQ) * THP * 2;
+    static constexpr int QTH = Q < 32 ? 32 : Q;                                // theta table rows
+    static constexpr int URT = K * SZ / 16, UT = QTH * URT, UPT_T = (UT + kPT - 1) / kPT;
+    static constexpr int TB = Q / 16;                                          // 16-token blocks per chunk
+    static constexpr int NPB = K / 16, NTT = TB * NPB;                         // 16x16 prefix tiles
+    static constexpr size_t o_th = align16(o_lw + (LWT ? lw_bytes : 0));       // bf16 [QTH][THP]
+    static constexpr size_t th_bytes = size_t(QTH) * THP * 2;
     static constexpr bool MFP = PL == 1 && K % 16 == 0 && o_th + th_bytes <= kMaxLdsBytes;
     static constexpr int MFW = FREEW ? FREEW : kPW;                            // waves sharing the prefix tiles
     static constexpr int TPW = MFP ? (NTT + MFW - 1) / MFW : 0;
@@ -149,16 +155,17 @@ struct CfgW {
     static constexpr bool CL = FREEW > 0 && o_cl + cl_bytes <= kMaxLdsBytes;
     static constexpr size_t bytes = o_cl + (CL ? cl_bytes : 0);
     static_assert(K * SZ % 16 == 0 && N % 16 == 0 && P % 16 == 0 && K % 8 == 0, "tile sizes");
+    static_assert(Q % 16 == 0 && Q <= kQ && V % 32 == 0 && V <= 2 * 16 * kPW, "chunk rows");
     static_assert(FREEW ? NG8 <= FREEW * GPW : NG8 <= kPW, "angle groups per wave");
     static_assert(!BPAD || (BLK && V >= R * N && (NBP - N) * 2 >= 16), "block table in the B row padding");
 };
 
 // The wide (conflict-free) layout when it fits with every optional table the
 // narrow one has, else the narrow layout.
-template <typename IO, int N, int P, int R, bool BLK>
+template <typename IO, int N, int P, int R, int Q, bool BLK>
 struct CfgPick {
-    typedef CfgW<IO, N, P, R, true, BLK> Wd;
-    typedef CfgW<IO, N, P, R, false, BLK> Nw;
+    typedef CfgW<IO, N, P, R, Q, true, BLK> Wd;
+    typedef CfgW<IO, N, P, R, Q, false, BLK> Nw;
     static constexpr bool wide = Wd::bytes <= kMaxLdsBytes && Wd::LWT == Nw::LWT && Wd::MFP == Nw::MFP &&
                                  Wd::XS == Nw::XS && Wd::CL == Nw::CL;
     typedef typename std::conditional<wide, Wd, Nw>::type type;
@@ -166,15 +173,15 @@ struct CfgPick {
 // With the block prologue the layout is the plain one whenever the table fits
 // in the staged-B row padding (N <= 64: one 16-byte slot per row), so the
 // block variant keeps every optional table of the plain kernel.
-template <typename IO, int N, int P, int R, bool BLK>
+template <typename IO, int N, int P, int R, int Q, bool BLK>
 struct CfgSel {
-    typedef typename CfgPick<IO, N, P, R, false>::type Plain;
-    static constexpr bool pad = BLK && N <= kQ;
-    typedef typename std::conditional<pad, CfgW<IO, N, P, R, Plain::kWide, true, true>,
-                                      typename CfgPick<IO, N, P, R, BLK>::type>::type type;
+    typedef typename CfgPick<IO, N, P, R, Q, false>::type Plain;
+    static constexpr bool pad = BLK && N <= Q;
+    typedef typename std::conditional<pad, CfgW<IO, N, P, R, Q, Plain::kWide, true, true>,
+                                      typename CfgPick<IO, N, P, R, Q, BLK>::type>::type type;
 };
-template <typename IO, int N, int P, int R, bool BLK = false>
-using Cfg = typename CfgSel<IO, N, P, R, BLK>::type;
+template <typename IO, int N, int P, int R, int Q, bool BLK = false>
+using Cfg = typename CfgSel<IO, N, P, R, Q, BLK>::type;
 
 // (BLK) entries of the block table at float offset o (a multiple of 4 for
 // the float4 read)
@@ -204,12 +211,13 @@ template <class C>
 struct RawPro {
     uint4 th[C::MFP ? 1 : C::GPW][C::GU];  // DPP scans: this wave's angle groups of its lane's token
     uint4 thu[C::MFP ? C::UPT_T : 1];      // MFMA prefix: this thread's units of the theta rows
-    uint32_t dt, lam, dtn, lamn;           // raw I/O bits of dt, lam (this lane's token, token t0+64)
+    uint32_t dt, lam, dtn, lamn;           // raw I/O bits of dt, lam (this lane's token, token t0+Q)
 };
 
-// Prefix tile m (< TPW) computed by a wave, or -1.  With free waves each
-// takes TPW consecutive tiles (token blocks m of one pair block when TPW = 4:
-// one operand read serves all four, and every wave gets one chunk-end row).
+// Prefix tile m (< TPW) computed by a wave, or -1.  Tile t covers token block
+// t % TB and pair block t / TB.  With free waves each takes TPW consecutive
+// tiles (the token blocks of one pair block when TPW = TB = 4: one operand
+// read serves all four, and every wave gets one chunk-end row).
 template <class C>
 __device__ __forceinline__ int mfp_tile(int wave, int m) {
     int t;
@@ -364,7 +372,7 @@ __device__ __forceinline__ void load_pro(const PrefillParams &p, int64_t b, int 
         const IO *dt = static_cast<const IO *>(p.dt) + tokbase;
         const IO *lam = static_cast<const IO *>(p.lam) + tokbase;
         const int lt = min(lane, Tc - 1);
-        const int64_t tn = min<int64_t>(kQ, p.T - 1 - t0);
+        const int64_t tn = min<int64_t>(C::Q, p.T - 1 - t0);
         r.dt = io<IO>::raw(dt + lt * H);
         r.lam = io<IO>::raw(lam + lt * H);
         r.dtn = io<IO>::raw(dt + tn * H);
@@ -425,15 +433,15 @@ __device__ __forceinline__ void run_angles(const RawPro<C> &r, int Tc, float *cs
         typedef typename C::M M;
         const int g = lane >> 4, l16 = lane & 15;
         if (mfp_tile<C>(wave, 0) < 0) return;
-        constexpr int KB = kQ / 32;
+        constexpr int KB = C::QTH / 32;
         typename M::frag bf[C::TPW][KB];
         int tbm[C::TPW], pbm[C::TPW];
 #pragma unroll
         for (int m = 0; m < C::TPW; ++m) {
             const int tile = mfp_tile<C>(wave, m);
             const int tl = tile < 0 ? 0 : tile;
-            tbm[m] = tl & 3;
-            pbm[m] = tl >> 2;
+            tbm[m] = tl % C::TB;
+            pbm[m] = tl / C::TB;
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
                 // slots 0-3: tokens 32 kb + 4 g .. +3, slots 4-7: 16 tokens further
@@ -506,8 +514,10 @@ __device__ __forceinline__ void run_angles(const RawPro<C> &r, int Tc, float *cs
             cn[j] = __builtin_amdgcn_cosf(tf);
         }
         float4 *row = reinterpret_cast<float4 *>(cs + lane * C::CSP + 16 * grp);
+        if (C::Q == kWave || lane < C::Q) { // the table has a row per token of the chunk
 #pragma unroll
-        for (int j = 0; j < 4; ++j) row[j] = make_float4(cn[2 * j], sn[2 * j], cn[2 * j + 1], sn[2 * j + 1]);
+            for (int j = 0; j < 4; ++j) row[j] = make_float4(cn[2 * j], sn[2 * j], cn[2 * j + 1], sn[2 * j + 1]);
+        }
         if (lane == Tc - 1) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
@@ -532,14 +542,14 @@ __device__ __forceinline__ void run_coef(const RawPro<C> &r, int Tc, int64_t t0,
         const float gam = lamv * dtv, del = (1.f - lamv) * dtv;
         // delta of the next token: DPP wave shift left by one lane
         float dn = __uint_as_float(dpp_u32<0x130, 0xf, true>(__float_as_uint(del)));
-        if (lane == kWave - 1) dn = (1.f - io<IO>::value(r.lamn)) * io<IO>::value(r.dtn);
+        if (lane == C::Q - 1) dn = (1.f - io<IO>::value(r.lamn)) * io<IO>::value(r.dtn);
         if (t0 + lane + 1 >= T) dn = 0.f;
         const float w = gam + dn;
         const float gc = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(ell), Tc - 1));
         coef[lane] = ell;
-        coef[kQ + lane] = gam;
-        coef[2 * kQ + lane] = w;
-        coef[3 * kQ + lane] = lane < Tc ? __expf(gc - ell) * w : 0.f;
+        coef[kWave + lane] = gam;
+        coef[2 * kWave + lane] = w;
+        coef[3 * kWave + lane] = lane < Tc ? __expf(gc - ell) * w : 0.f;
         if (lane == 0) {
             misc[0] = gc;
             misc[2] = del;
@@ -597,9 +607,9 @@ __device__ __forceinline__ floatx4 fold_init(const PrefillParams &p, int64_t bh,
     return o;
 }
 
-template <typename IO, int N, int P, int R, bool OUT, bool BLK>
+template <typename IO, int N, int P, int R, int QC, bool OUT, bool BLK>
 __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
-    typedef Cfg<IO, N, P, R, BLK> C;
+    typedef Cfg<IO, N, P, R, QC, BLK> C;
     typedef typename C::M M;
     typedef typename C::frag frag;
     constexpr int PL = C::PL, K = C::K, V = C::V, NBP = C::NBP, PP = C::PP, EPU = C::EPU;
@@ -651,16 +661,17 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
     for (int j = 0; j < C::TW; ++j) st[j] = floatx4{0.f, 0.f, 0.f, 0.f};
     float gsum = 0.f;
     const float Ah = p.A[h];
-    auto tc_of = [&](int c) { return int(min<int64_t>(kQ, p.T - int64_t(c) * kQ)); };
+    constexpr int Q = C::Q;
+    auto tc_of = [&](int c) { return int(min<int64_t>(Q, p.T - int64_t(c) * Q)); };
 
     // prologue of the first chunk, then its B, x, C and the next prologue inputs
     RawPro<C> rp;
-    load_pro<C, IO>(p, b, h, int64_t(c_begin) * kQ, tc_of(c_begin), rp);
-    load_theta<C, IO>(p, b, h, int64_t(c_begin) * kQ, tc_of(c_begin), rp);
+    load_pro<C, IO>(p, b, h, int64_t(c_begin) * Q, tc_of(c_begin), rp);
+    load_theta<C, IO>(p, b, h, int64_t(c_begin) * Q, tc_of(c_begin), rp);
     RawChunk<C> raw;
-    load_chunk<C, IO, OUT>(p, b, h, hg, int64_t(c_begin) * kQ, tc_of(c_begin), raw);
+    load_chunk<C, IO, OUT>(p, b, h, hg, int64_t(c_begin) * Q, tc_of(c_begin), raw);
     write_theta<C>(rp, tht);
-    run_coef<C, IO>(rp, tc_of(c_begin), int64_t(c_begin) * kQ, p.T, Ah, coef_s, misc_s);
+    run_coef<C, IO>(rp, tc_of(c_begin), int64_t(c_begin) * Q, p.T, Ah, coef_s, misc_s);
     if constexpr (BLK) {
         // this head's block prologue weights and biases (1 and 0 when absent)
         const int64_t hb0 = int64_t(h) * R * N;
@@ -676,8 +687,8 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
     __syncthreads(); // ths_s, theta table, block tables
     run_angles<C, IO>(rp, tc_of(c_begin), cs_s, thc_s, ths_s, tht);
     if (c_begin + 1 < c_end) {
-        load_pro<C, IO>(p, b, h, int64_t(c_begin + 1) * kQ, tc_of(c_begin + 1), rp);
-        load_theta<C, IO>(p, b, h, int64_t(c_begin + 1) * kQ, tc_of(c_begin + 1), rp);
+        load_pro<C, IO>(p, b, h, int64_t(c_begin + 1) * Q, tc_of(c_begin + 1), rp);
+        load_theta<C, IO>(p, b, h, int64_t(c_begin + 1) * Q, tc_of(c_begin + 1), rp);
     }
     __syncthreads();
     // state at the start of this workgroup's first chunk (before the chunk loop,
@@ -728,11 +739,11 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
     }
 
     for (int c = c_begin; c < c_end; ++c) {
-        const int64_t t0 = int64_t(c) * kQ;
+        const int64_t t0 = int64_t(c) * Q;
         const int Tc = tc_of(c);
         const int buf = (c - c_begin) & 1;
-        const float *ell_s = coef_s + buf * (4 * kQ);
-        const float *gam_s = ell_s + kQ, *wgt_s = gam_s + kQ, *scl_s = wgt_s + kQ;
+        const float *ell_s = coef_s + buf * (4 * kWave);
+        const float *gam_s = ell_s + kWave, *wgt_s = gam_s + kWave, *scl_s = wgt_s + kWave;
         const float2 *thcb = thc_s + buf * K;
 
         // ---- a2: rotate B and C with the cos/sin table; stage B, x, scaled x.
@@ -744,7 +755,7 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
         // copies, and a wait for every load, at the end of each chunk.
         const bool more = c + 1 < c_end;
         const int cn = more ? c + 1 : c, cn2 = min(c + 2, c_end - 1);
-        const int64_t tn0 = int64_t(cn) * kQ;
+        const int64_t tn0 = int64_t(cn) * Q;
         const int Tn = tc_of(cn);
         constexpr int CPART = (OUT && C::CL) ? 4 : 0;
         static_for<0, C::UPT_B>([&](auto jc) {
@@ -895,27 +906,29 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
         if (C::MFP && c + 1 < c_end) {
             write_theta<C>(rp, tht);
             if constexpr (!CP2)
-                run_coef<C, IO>(rp, tc_of(c + 1), t0 + kQ, p.T, Ah, coef_s + (buf ^ 1) * (4 * kQ), misc_s + (buf ^ 1));
+                run_coef<C, IO>(rp, tc_of(c + 1), t0 + Q, p.T, Ah, coef_s + (buf ^ 1) * (4 * kWave), misc_s + (buf ^ 1));
         }
         if (OUT && !C::CL) {
             __builtin_amdgcn_sched_barrier(0); // after the C fragments are unpacked
             load_chunk<C, IO, OUT, 4>(p, b, h, hg, tn0, Tn, raw);
         }
         if constexpr (C::MFP) {
-            load_theta<C, IO>(p, b, h, int64_t(cn2) * kQ, tc_of(cn2), rp);
-            if constexpr (!CP2) load_pro<C, IO>(p, b, h, int64_t(cn2) * kQ, tc_of(cn2), rp);
+            load_theta<C, IO>(p, b, h, int64_t(cn2) * Q, tc_of(cn2), rp);
+            if constexpr (!CP2) load_pro<C, IO>(p, b, h, int64_t(cn2) * Q, tc_of(cn2), rp);
         }
 
         // ---- a3 mask of this chunk: L[t][s] = exp(ell_t - ell_s) wgt_s (s < t),
-        // gam_t (s = t), 0 (s > t); row t, 8 consecutive s per thread.  With
-        // R = 1 the rows t < 32 are read for s < 32 only (their source pair),
-        // so 384 groups are evaluated, by the first six waves.
+        // gam_t (s = t), 0 (s > t); row t, 8 consecutive s per thread (Q / 8
+        // threads per row).  With R = 1 and 64-token chunks the rows t < 32 are
+        // read for s < 32 only (their source pair), so 384 groups are
+        // evaluated, by the first six waves.
         if constexpr (C::LWT) {
-            constexpr bool HALF = R == 1 && kQ == 64 && kPT == 512;
+            constexpr bool HALF = R == 1 && Q == 64 && kPT == 512;
+            constexpr int G8 = Q / 8; // threads per mask row
             const int gi = HALF && tid >= 128 ? tid + 128 : tid; // skip rows < 32 x s >= 32
-            const int tt = HALF ? (tid < 128 ? tid >> 2 : gi >> 3) : tid >> 3;
-            const int s0 = HALF ? (tid < 128 ? (tid & 3) * 8 : (gi & 7) * 8) : (tid & 7) * 8;
-            if (OUT && (!HALF || tid < 384)) {
+            const int tt = HALF ? (tid < 128 ? tid >> 2 : gi >> 3) : tid / G8;
+            const int s0 = HALF ? (tid < 128 ? (tid & 3) * 8 : (gi & 7) * 8) : (tid % G8) * 8;
+            if (OUT && (HALF ? tid < 384 : tid < Q * G8)) {
                 float w[8];
                 {
                     // branch-free: every entry is evaluated, then selected
@@ -940,7 +953,7 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
                 dst[0] = make_float4(w[0], w[1], w[2], w[3]);
                 dst[1] = make_float4(w[4], w[5], w[6], w[7]);
             }
-            if (OUT && tid < kQ) lw_s[kQ * C::LWP + tid] = __expf(ell_s[tid]);
+            if (OUT && tid < Q) lw_s[Q * C::LWP + tid] = __expf(ell_s[tid]);
         }
 
         __syncthreads();
@@ -951,8 +964,8 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
         // only unconditional loads were issued since
         if constexpr (CP2) {
             if (c + 1 < c_end)
-                run_coef<C, IO>(rp, tc_of(c + 1), t0 + kQ, p.T, Ah, coef_s + (buf ^ 1) * (4 * kQ), misc_s + (buf ^ 1));
-            load_pro<C, IO>(p, b, h, int64_t(cn2) * kQ, tc_of(cn2), rp);
+                run_coef<C, IO>(rp, tc_of(c + 1), t0 + Q, p.T, Ah, coef_s + (buf ^ 1) * (4 * kWave), misc_s + (buf ^ 1));
+            load_pro<C, IO>(p, b, h, int64_t(cn2) * Q, tc_of(cn2), rp);
         }
         if (OUT) {
             // ---- a3 + a5: y = M x + exp(ell) Chat H for this wave's row blocks,
@@ -1013,7 +1026,7 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
                     // virtual row t0v + l16), so one decay factor per lane
                     const int tok = (t0v + l16) / R;
                     float e;
-                    if constexpr (C::LWT) e = lw_s[kQ * C::LWP + tok];
+                    if constexpr (C::LWT) e = lw_s[Q * C::LWP + tok];
                     else e = __expf(ell_s[tok]);
                     if (tok >= Tc) e = 0.f;
 #pragma unroll
@@ -1210,8 +1223,8 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
         if (c + 1 < c_end) {
             run_angles<C, IO>(rp, tc_of(c + 1), cs_s, thc_s + (buf ^ 1) * K, ths_s, tht);
             if constexpr (!C::MFP) {
-                run_coef<C, IO>(rp, tc_of(c + 1), t0 + kQ, p.T, Ah, coef_s + (buf ^ 1) * (4 * kQ), misc_s + (buf ^ 1));
-                load_pro<C, IO>(p, b, h, int64_t(cn2) * kQ, tc_of(cn2), rp);
+                run_coef<C, IO>(rp, tc_of(c + 1), t0 + Q, p.T, Ah, coef_s + (buf ^ 1) * (4 * kWave), misc_s + (buf ^ 1));
+                load_pro<C, IO>(p, b, h, int64_t(cn2) * Q, tc_of(cn2), rp);
             }
         }
         __syncthreads();
@@ -1304,19 +1317,55 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
 
 // Host-side launch of one instantiation (pre-pass when OUT is false; the
 // block prologue/epilogue kernels when BLK).
-template <typename IO, int N, int P, int R, bool OUT, bool BLK>
+template <typename IO, int N, int P, int R, int QC, bool OUT, bool BLK>
 hipError_t launch_prefill_inst(const PrefillParams &p, hipStream_t s) {
-    typedef Cfg<IO, N, P, R, BLK> C;
+    typedef Cfg<IO, N, P, R, QC, BLK> C;
     const int nseg = OUT ? p.S : p.S - 1;
     if (nseg <= 0) return hipSuccess;
     if (C::bytes > 65536) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_prefill<IO, N, P, R, OUT, BLK>),
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_prefill<IO, N, P, R, QC, OUT, BLK>),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, int(C::bytes));
         if (e != hipSuccess) return e;
     }
     const dim3 grid(unsigned(p.batch * p.H * nseg)), block(kPT);
-    hipLaunchKernelGGL((k_prefill<IO, N, P, R, OUT, BLK>), grid, block, C::bytes, s, p);
+    hipLaunchKernelGGL((k_prefill<IO, N, P, R, QC, OUT, BLK>), grid, block, C::bytes, s, p);
     return hipGetLastError();
+}
+
+// The instantiation for rank R with chunks of 64 tokens (SMALL false) or of
+// small_chunk(R) tokens (SMALL true); combinations whose tiles do not fit in
+// the LDS of a CU are not compiled and report hipErrorInvalidValue, as does a
+// call whose chunk length p.Q is not this one's.
+template <typename IO, int N, int P, int R, bool BLK, bool SMALL>
+hipError_t launch_prefill_r(const PrefillParams &p, bool out, hipStream_t s) {
+    constexpr int QC = SMALL ? small_chunk(R) : kQ;
+    if constexpr ((SMALL && QC == kQ) || Cfg<IO, N, P, R, QC, BLK>::bytes > kMaxLdsBytes) {
+        return hipErrorInvalidValue;
+    } else {
+        if (p.Q != QC) return hipErrorInvalidValue;
+        return out ? launch_prefill_inst<IO, N, P, R, QC, true, BLK>(p, s)
+                   : launch_prefill_inst<IO, N, P, R, QC, false, BLK>(p, s);
+    }
+}
+template <typename IO, int N, int P, bool BLK, bool SMALL>
+hipError_t launch_prefill_pr(const PrefillParams &p, bool out, hipStream_t s) {
+    switch (p.R) {
+    case 1: return launch_prefill_r<IO, N, P, 1, BLK, SMALL>(p, out, s);
+    case 2: return launch_prefill_r<IO, N, P, 2, BLK, SMALL>(p, out, s);
+    case 3: return launch_prefill_r<IO, N, P, 3, BLK, SMALL>(p, out, s);
+    case 4: return launch_prefill_r<IO, N, P, 4, BLK, SMALL>(p, out, s);
+    }
+    return hipErrorInvalidValue;
+}
+// Every (P, R) of one (I/O type, N, block variant, chunk kind).
+template <typename IO, int N, bool BLK, bool SMALL>
+hipError_t launch_prefill_np(const PrefillParams &p, bool out, hipStream_t s) {
+    switch (p.P) {
+    case 16: return launch_prefill_pr<IO, N, 16, BLK, SMALL>(p, out, s);
+    case 32: return launch_prefill_pr<IO, N, 32, BLK, SMALL>(p, out, s);
+    case 64: return launch_prefill_pr<IO, N, 64, BLK, SMALL>(p, out, s);
+    }
+    return hipErrorInvalidValue;
 }
 
 } // namespace m3

@@ -1,27 +1,11 @@
-// k_prefill_f32_n32.hip -- instantiations of the fused prefill kernel for f32 I/O, N = 32.
+// k_prefill_f32_n32.hip -- instantiations of the fused prefill kernel for
+// fp32 I/O, N = 32, 64-token chunks.
 #include "k_prefill.hpp"
 
 namespace m3 {
 
-template <int P>
-static hipError_t by_rank(const PrefillParams &p, bool out, hipStream_t s) {
-    switch (p.R) {
-    case 1: return out ? launch_prefill_inst<float, 32, P, 1, true, false>(p, s) : launch_prefill_inst<float, 32, P, 1, false, false>(p, s);
-    case 2: return out ? launch_prefill_inst<float, 32, P, 2, true, false>(p, s) : launch_prefill_inst<float, 32, P, 2, false, false>(p, s);
-    case 3: return out ? launch_prefill_inst<float, 32, P, 3, true, false>(p, s) : launch_prefill_inst<float, 32, P, 3, false, false>(p, s);
-    case 4: return out ? launch_prefill_inst<float, 32, P, 4, true, false>(p, s) : launch_prefill_inst<float, 32, P, 4, false, false>(p, s);
-    }
-    return hipErrorInvalidValue;
-}
-
 hipError_t launch_prefill_f32_n32(const PrefillParams &p, bool out, hipStream_t s) {
-    if (p.blk.on) return launch_prefill_f32_n32_blk(p, out, s);
-    switch (p.P) {
-    case 16: return by_rank<16>(p, out, s);
-    case 32: return by_rank<32>(p, out, s);
-    case 64: return by_rank<64>(p, out, s);
-    }
-    return hipErrorInvalidValue;
+    return launch_prefill_np<float, 32, false, false>(p, out, s);
 }
 
 } // namespace m3

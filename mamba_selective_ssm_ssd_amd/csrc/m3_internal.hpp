@@ -22,10 +22,13 @@ struct BlockParams {
 // Everything one prefill call needs, resolved to device pointers.
 struct PrefillParams {
     int64_t batch, T;
-    int32_t H, P, N, R, K, nC; // K = N/2 rotation pairs, nC = ceil(T/64) chunks
+    int32_t H, P, N, R, K;     // K = N/2 rotation pairs
+    int32_t Q, nC;             // tokens per chunk of the launched pass (64 or small_chunk(R)), ceil(T/Q) chunks
     int32_t G, hpg;            // B/C groups, heads per group (head h reads group h / hpg)
     int32_t sbf16;             // carried state h~ stored in bf16
-    int32_t S, cps;            // segments per sequence, chunks per segment
+    int32_t S, cps;            // segments per sequence, chunks of the launched pass per segment
+    int32_t Qpre, Qout;        // tokens per chunk of the pre-pass and of the output pass (host)
+    int64_t seglen;            // tokens per segment, a multiple of both (host)
     // inputs (I/O dtype unless noted)
     const void *x, *dt, *lam, *theta, *B, *C;
     const float *A; // [H]
@@ -90,25 +93,48 @@ struct WorkspaceLayout {
     size_t segU, segG, segTh, hinit, phi0, total;
 };
 
-// Fused prefill launchers, one per (I/O type, N): out = false runs the
-// segment pre-pass (nothing to do when S == 1), out = true the output pass.
+// Tokens per chunk of the small MIMO chunk: 64/R tokens, i.e. 64 virtual
+// (token, rank) rows (R = 3: 32 tokens, 96 rows, since the products take
+// rows 32 at a time); 64 for R = 1.
+constexpr int small_chunk(int R) { return R == 4 ? 16 : R >= 2 ? 32 : 64; }
+
+// Fused prefill launchers, one per (I/O type, N, block variant, chunk kind):
+// out = false runs the segment pre-pass (nothing to do when S == 1), out =
+// true the output pass.  "_blk": the block prologue/epilogue kernels
+// (p.blk.on); "_qs": chunks of small_chunk(R) tokens instead of 64.
+typedef hipError_t (*prefill_launcher_t)(const PrefillParams &p, bool out, hipStream_t s);
 hipError_t launch_prefill_bf16_n16(const PrefillParams &p, bool out, hipStream_t s);
-hipError_t launch_prefill_bf16_n32(const PrefillParams &p, bool out, hipStream_t s);
-hipError_t launch_prefill_bf16_n64(const PrefillParams &p, bool out, hipStream_t s);
-hipError_t launch_prefill_bf16_n128(const PrefillParams &p, bool out, hipStream_t s);
-hipError_t launch_prefill_f32_n16(const PrefillParams &p, bool out, hipStream_t s);
-hipError_t launch_prefill_f32_n32(const PrefillParams &p, bool out, hipStream_t s);
-hipError_t launch_prefill_f32_n64(const PrefillParams &p, bool out, hipStream_t s);
-hipError_t launch_prefill_f32_n128(const PrefillParams &p, bool out, hipStream_t s);
-// the same with the block prologue/epilogue (p.blk.on)
 hipError_t launch_prefill_bf16_n16_blk(const PrefillParams &p, bool out, hipStream_t s);
+hipError_t launch_prefill_bf16_n16_qs(const PrefillParams &p, bool out, hipStream_t s);
+hipError_t launch_prefill_bf16_n16_blk_qs(const PrefillParams &p, bool out, hipStream_t s);
+hipError_t launch_prefill_bf16_n32(const PrefillParams &p, bool out, hipStream_t s);
 hipError_t launch_prefill_bf16_n32_blk(const PrefillParams &p, bool out, hipStream_t s);
+hipError_t launch_prefill_bf16_n32_qs(const PrefillParams &p, bool out, hipStream_t s);
+hipError_t launch_prefill_bf16_n32_blk_qs(const PrefillParams &p, bool out, hipStream_t s);
+hipError_t launch_prefill_bf16_n64(const PrefillParams &p, bool out, hipStream_t s);
 hipError_t launch_prefill_bf16_n64_blk(const PrefillParams &p, bool out, hipStream_t s);
+hipError_t launch_prefill_bf16_n64_qs(const PrefillParams &p, bool out, hipStream_t s);
+hipError_t launch_prefill_bf16_n64_blk_qs(const PrefillParams &p, bool out, hipStream_t s);
+hipError_t launch_prefill_bf16_n128(const PrefillParams &p, bool out, hipStream_t s);
 hipError_t launch_prefill_bf16_n128_blk(const PrefillParams &p, bool out, hipStream_t s);
+hipError_t launch_prefill_bf16_n128_qs(const PrefillParams &p, bool out, hipStream_t s);
+hipError_t launch_prefill_bf16_n128_blk_qs(const PrefillParams &p, bool out, hipStream_t s);
+hipError_t launch_prefill_f32_n16(const PrefillParams &p, bool out, hipStream_t s);
 hipError_t launch_prefill_f32_n16_blk(const PrefillParams &p, bool out, hipStream_t s);
+hipError_t launch_prefill_f32_n16_qs(const PrefillParams &p, bool out, hipStream_t s);
+hipError_t launch_prefill_f32_n16_blk_qs(const PrefillParams &p, bool out, hipStream_t s);
+hipError_t launch_prefill_f32_n32(const PrefillParams &p, bool out, hipStream_t s);
 hipError_t launch_prefill_f32_n32_blk(const PrefillParams &p, bool out, hipStream_t s);
+hipError_t launch_prefill_f32_n32_qs(const PrefillParams &p, bool out, hipStream_t s);
+hipError_t launch_prefill_f32_n32_blk_qs(const PrefillParams &p, bool out, hipStream_t s);
+hipError_t launch_prefill_f32_n64(const PrefillParams &p, bool out, hipStream_t s);
 hipError_t launch_prefill_f32_n64_blk(const PrefillParams &p, bool out, hipStream_t s);
+hipError_t launch_prefill_f32_n64_qs(const PrefillParams &p, bool out, hipStream_t s);
+hipError_t launch_prefill_f32_n64_blk_qs(const PrefillParams &p, bool out, hipStream_t s);
+hipError_t launch_prefill_f32_n128(const PrefillParams &p, bool out, hipStream_t s);
 hipError_t launch_prefill_f32_n128_blk(const PrefillParams &p, bool out, hipStream_t s);
+hipError_t launch_prefill_f32_n128_qs(const PrefillParams &p, bool out, hipStream_t s);
+hipError_t launch_prefill_f32_n128_blk_qs(const PrefillParams &p, bool out, hipStream_t s);
 
 hipError_t launch_decode_bf16(const DecodeParams &p, hipStream_t s);
 hipError_t launch_decode_f32(const DecodeParams &p, hipStream_t s);
@@ -124,8 +150,9 @@ hipError_t launch_decode_f32_blk_sb(const DecodeParams &p, hipStream_t s);
 hipError_t launch_backward_bf16(const BwdParams &p, hipStream_t s);
 hipError_t launch_backward_f32(const BwdParams &p, hipStream_t s);
 
-// Dynamic LDS bytes of the fused prefill kernel for a shape (0: not compiled).
-size_t prefill_lds_bytes(bool is_bf16, int N, int P, int R, bool blk = false);
+// Dynamic LDS bytes of the fused prefill kernel for a shape and chunk length
+// Q (64 or small_chunk(R)); 0: not compiled.
+size_t prefill_lds_bytes(bool is_bf16, int N, int P, int R, bool blk, int Q);
 constexpr size_t kMaxLdsBytes = 160 * 1024; // LDS per workgroup on gfx950
 
 // Sizes handled by the compiled kernels.

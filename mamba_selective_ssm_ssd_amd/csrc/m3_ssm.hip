@@ -28,8 +28,38 @@ size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Checks the shape.  Returns M3_OK or the error to report.
-m3_status_t check_shape(const m3_shape_t *s, bool decode) {
+// Tokens per chunk the prefill kernels use for a shape (0: no compiled
+// kernel), for the segment pre-pass (out = false) or the output pass.
+// chunk = small_chunk(R) takes chunks of that many tokens in both passes.
+// chunk = 64 takes 64-token chunks when their tiles fit in the LDS of a CU,
+// else small ones; where both fit, the output pass of bf16 MIMO shapes
+// takes the small chunk, which measured faster (a quarter of the quadratic
+// intra-chunk work per token), and the pre-pass the 64-token chunk (it has
+// no intra-chunk product, only per-chunk overheads).  small_chunk(R)
+// divides 64, so segments of whole 64-token chunks are whole small chunks
+// too, and every choice gives the same result up to rounding.
+int chunk_tokens(const m3_shape_t *s, bool blk, bool out) {
+    const bool bf = s->io_dtype == M3_DTYPE_BF16;
+    const int qs = m3::small_chunk(s->rank);
+    auto fits = [&](int q) {
+        const size_t lds = m3::prefill_lds_bytes(bf, s->dstate, s->headdim, s->rank, blk, q);
+        return lds > 0 && lds <= m3::kMaxLdsBytes;
+    };
+    if (s->chunk == qs) return fits(qs) ? qs : 0;
+    if (s->chunk != 64) return 0;
+    if (!fits(64)) return fits(qs) ? qs : 0;
+    if (out && bf && s->rank == 4 && fits(qs)) return qs;
+    return 64;
+}
+
+// Which entry point a shape is checked for.
+enum class Use { prefill, decode, backward };
+
+// Checks the shape.  Returns M3_OK or the error to report.  Only the
+// prefill's kernels stage chunks in LDS; the backward's LDS layout fits for
+// every (N, P, R) of the tile set by construction (checked at compile time).
+m3_status_t check_shape(const m3_shape_t *s, Use use) {
+    const bool decode = use == Use::decode;
     if (!s) return M3_ERR_INVALID_ARGUMENT;
     if (s->io_dtype != M3_DTYPE_F32 && s->io_dtype != M3_DTYPE_BF16) return M3_ERR_INVALID_ARGUMENT;
     if (s->batch < 1 || s->nheads < 1 || s->headdim < 1 || s->dstate < 2 || s->rank < 1)
@@ -39,20 +69,22 @@ m3_status_t check_shape(const m3_shape_t *s, bool decode) {
     if (s->chunk < 1) return M3_ERR_INVALID_ARGUMENT;
     if (s->ngroups < 0 || (s->ngroups > 0 && s->nheads % s->ngroups != 0)) return M3_ERR_INVALID_ARGUMENT;
     if (s->state_dtype != M3_DTYPE_F32 && s->state_dtype != M3_DTYPE_BF16) return M3_ERR_INVALID_ARGUMENT;
-    if (s->chunk != 64) return M3_ERR_UNSUPPORTED;
     if (!m3::supported_N(s->dstate) || !m3::supported_P(s->headdim) || s->rank > 4)
         return M3_ERR_UNSUPPORTED;
-    // every grid dimension and element offset must stay in range
+    if (s->chunk != 64 && s->chunk != m3::small_chunk(s->rank)) return M3_ERR_UNSUPPORTED;
+    // every grid dimension and element offset must stay in range: offsets
+    // across tokens and sequences are 64-bit, the kernels' offsets within a
+    // chunk (up to 64 tokens of the x, y, B, C, theta rows) 32-bit
     const double bh = double(s->batch) * double(s->nheads);
     const double T = decode ? 1.0 : double(s->seqlen);
-    const double elems = bh * T * double(s->rank) * double(s->dstate > s->headdim ? s->dstate : s->headdim);
+    const double wide = double(s->dstate > s->headdim ? s->dstate : s->headdim);
+    const double elems = bh * T * double(s->rank) * wide;
     if (elems > 4.0e18) return M3_ERR_UNSUPPORTED;
-    if (!decode) {
-        // the prefill kernel stages a whole chunk in LDS
-        const size_t lds = m3::prefill_lds_bytes(s->io_dtype == M3_DTYPE_BF16, s->dstate, s->headdim, s->rank);
-        if (lds == 0 || lds > m3::kMaxLdsBytes) return M3_ERR_UNSUPPORTED;
-    }
-    if (bh * ((T + 63.0) / 64.0) > double(std::numeric_limits<unsigned>::max()) / 2) return M3_ERR_UNSUPPORTED;
+    if (64.0 * double(s->nheads) * double(s->rank) * wide >= 2147483648.0) return M3_ERR_UNSUPPORTED;
+    // the prefill kernel stages a whole chunk in LDS
+    if (use == Use::prefill && (chunk_tokens(s, false, false) == 0 || chunk_tokens(s, false, true) == 0))
+        return M3_ERR_UNSUPPORTED;
+    if (bh * ((T + 15.0) / 16.0) > double(std::numeric_limits<unsigned>::max()) / 2) return M3_ERR_UNSUPPORTED;
     return M3_OK;
 }
 
@@ -60,9 +92,10 @@ m3_status_t check_shape(const m3_shape_t *s, bool decode) {
 constexpr int64_t kSlots = 256;
 
 // Segments per sequence: enough (batch, head, segment) workgroups to fill the
-// chip, never an empty segment.  Depends on the shape only.
-void segments(int64_t bh, int64_t T, int32_t &S, int32_t &cps) {
-    const int64_t nC = (T + 63) / 64;
+// chip, never an empty segment.  Depends on the shape and the chunk length Q
+// only.
+void segments(int64_t bh, int64_t T, int Q, int32_t &S, int32_t &cps) {
+    const int64_t nC = (T + Q - 1) / Q;
     int64_t s = bh >= kSlots ? 1 : kSlots / bh;
     if (s > nC) s = nC;
     if (s < 1) s = 1;
@@ -71,19 +104,24 @@ void segments(int64_t bh, int64_t T, int32_t &S, int32_t &cps) {
     S = int32_t((nC + c - 1) / c);
 }
 
+// Sized for the largest segment count any chunk length of the shape can
+// give (the smallest chunk has the most chunks), so one workspace serves the
+// plain and the block kernels.  Only a sequence cut into S > 1 segments uses
+// it; with S = 1 for every chunk length it is one aligned block, unused.
 WorkspaceLayout layout(const m3_shape_t *s) {
     const size_t bh = size_t(s->batch) * size_t(s->nheads);
     int32_t S, cps;
-    segments(int64_t(bh), s->seqlen, S, cps);
+    segments(int64_t(bh), s->seqlen, m3::small_chunk(s->rank), S, cps);
     const size_t N = size_t(s->dstate), P = size_t(s->headdim), K = N / 2;
+    const size_t used = S > 1 ? 1 : 0;
     WorkspaceLayout w;
     size_t off = 0;
-    w.segU = off; off += round_up(bh * S * N * P * sizeof(float));
-    w.segG = off; off += round_up(bh * S * sizeof(float));
-    w.segTh = off; off += round_up(bh * S * K * sizeof(double));
-    w.hinit = off; off += round_up(bh * N * P * sizeof(float));
-    w.phi0 = off; off += round_up(bh * K * sizeof(double));
-    w.total = off;
+    w.segU = off; off += round_up(used * bh * S * N * P * sizeof(float));
+    w.segG = off; off += round_up(used * bh * S * sizeof(float));
+    w.segTh = off; off += round_up(used * bh * S * K * sizeof(double));
+    w.hinit = off; off += round_up(used * bh * N * P * sizeof(float));
+    w.phi0 = off; off += round_up(used * bh * K * sizeof(double));
+    w.total = off > kAlign ? off : kAlign;
     return w;
 }
 
@@ -107,7 +145,7 @@ BwdLayout bwd_layout(const m3_shape_t *s) {
 }
 
 m3_status_t check_backward_shape(const m3_shape_t *s) {
-    const m3_status_t sc = check_shape(s, false);
+    const m3_status_t sc = check_shape(s, Use::backward);
     if (sc != M3_OK) return sc;
     if (s->ngroups != 0 && s->ngroups != s->nheads) return M3_ERR_UNSUPPORTED;
     if (s->state_dtype != M3_DTYPE_F32) return M3_ERR_UNSUPPORTED;
@@ -124,14 +162,22 @@ bool state_ok(const m3_state_t *st) {
 
 namespace m3 {
 
+template <typename IO, int N, int P, int R, bool BLK>
+static size_t lds_q(int Q) {
+    constexpr int QS = small_chunk(R);
+    if (Q == 64) return Cfg<IO, N, P, R, 64, BLK>::bytes;
+    if (Q == QS) return Cfg<IO, N, P, R, QS, BLK>::bytes;
+    return 0;
+}
+
 template <typename IO, int N, bool BLK>
-static size_t lds_np(int P, int R) {
+static size_t lds_np(int P, int R, int Q) {
 #define M3_LDS_R(PP)                                                                     \
     switch (R) {                                                                         \
-    case 1: return Cfg<IO, N, PP, 1, BLK>::bytes;                                        \
-    case 2: return Cfg<IO, N, PP, 2, BLK>::bytes;                                        \
-    case 3: return Cfg<IO, N, PP, 3, BLK>::bytes;                                        \
-    case 4: return Cfg<IO, N, PP, 4, BLK>::bytes;                                        \
+    case 1: return lds_q<IO, N, PP, 1, BLK>(Q);                                          \
+    case 2: return lds_q<IO, N, PP, 2, BLK>(Q);                                          \
+    case 3: return lds_q<IO, N, PP, 3, BLK>(Q);                                          \
+    case 4: return lds_q<IO, N, PP, 4, BLK>(Q);                                          \
     }                                                                                    \
     return 0;
     switch (P) {
@@ -144,18 +190,18 @@ static size_t lds_np(int P, int R) {
 }
 
 template <bool BLK>
-static size_t lds_n(bool is_bf16, int N, int P, int R) {
+static size_t lds_n(bool is_bf16, int N, int P, int R, int Q) {
     switch (N) {
-    case 16: return is_bf16 ? lds_np<bf16, 16, BLK>(P, R) : lds_np<float, 16, BLK>(P, R);
-    case 32: return is_bf16 ? lds_np<bf16, 32, BLK>(P, R) : lds_np<float, 32, BLK>(P, R);
-    case 64: return is_bf16 ? lds_np<bf16, 64, BLK>(P, R) : lds_np<float, 64, BLK>(P, R);
-    case 128: return is_bf16 ? lds_np<bf16, 128, BLK>(P, R) : lds_np<float, 128, BLK>(P, R);
+    case 16: return is_bf16 ? lds_np<bf16, 16, BLK>(P, R, Q) : lds_np<float, 16, BLK>(P, R, Q);
+    case 32: return is_bf16 ? lds_np<bf16, 32, BLK>(P, R, Q) : lds_np<float, 32, BLK>(P, R, Q);
+    case 64: return is_bf16 ? lds_np<bf16, 64, BLK>(P, R, Q) : lds_np<float, 64, BLK>(P, R, Q);
+    case 128: return is_bf16 ? lds_np<bf16, 128, BLK>(P, R, Q) : lds_np<float, 128, BLK>(P, R, Q);
     }
     return 0;
 }
 
-size_t prefill_lds_bytes(bool is_bf16, int N, int P, int R, bool blk) {
-    return blk ? lds_n<true>(is_bf16, N, P, R) : lds_n<false>(is_bf16, N, P, R);
+size_t prefill_lds_bytes(bool is_bf16, int N, int P, int R, bool blk, int Q) {
+    return blk ? lds_n<true>(is_bf16, N, P, R, Q) : lds_n<false>(is_bf16, N, P, R, Q);
 }
 
 } // namespace m3
@@ -174,7 +220,7 @@ const char *m3_status_string(m3_status_t status) {
 }
 
 size_t m3_ssm_prefill_workspace_bytes(const m3_shape_t *shape) {
-    if (check_shape(shape, false) != M3_OK) return 0;
+    if (check_shape(shape, Use::prefill) != M3_OK) return 0;
     return layout(shape).total;
 }
 
@@ -201,17 +247,14 @@ static m3_status_t prepare_prefill(const m3_shape_t *shape, const void *x, const
                                    m3_state_t *final_state, void *y, void *workspace,
                                    size_t workspace_bytes, PrefillParams &p,
                                    const m3_block_t *block = nullptr) {
-    const m3_status_t sc = check_shape(shape, false);
+    const m3_status_t sc = check_shape(shape, Use::prefill);
     if (sc != M3_OK) return sc;
     m3::BlockParams bp;
     const m3_status_t sb = resolve_block(block, bp);
     if (sb != M3_OK) return sb;
-    if (bp.on) {
-        // the block kernels also keep this head's weights and biases in LDS
-        const size_t lds = m3::prefill_lds_bytes(shape->io_dtype == M3_DTYPE_BF16, shape->dstate,
-                                                 shape->headdim, shape->rank, true);
-        if (lds == 0 || lds > m3::kMaxLdsBytes) return M3_ERR_UNSUPPORTED;
-    }
+    // the block kernels also keep this head's weights and biases in LDS
+    const int Qpre = chunk_tokens(shape, bp.on, false), Qout = chunk_tokens(shape, bp.on, true);
+    if (Qpre == 0 || Qout == 0) return M3_ERR_UNSUPPORTED;
     const void *ptrs[] = {x, dt, A, lam, theta, B, C, y};
     for (const void *q : ptrs)
         if (!q || !aligned16(q)) return M3_ERR_INVALID_ARGUMENT;
@@ -231,7 +274,8 @@ static m3_status_t prepare_prefill(const m3_shape_t *shape, const void *x, const
     p.G = shape->ngroups ? shape->ngroups : shape->nheads;
     p.hpg = p.H / p.G;
     p.sbf16 = shape->state_dtype == M3_DTYPE_BF16;
-    p.nC = int32_t((p.T + 63) / 64);
+    p.Qpre = Qpre;
+    p.Qout = Qout;
     p.x = x; p.dt = dt; p.lam = lam; p.theta = theta; p.B = B; p.C = C; p.A = A; p.y = y;
     p.has_init = init != nullptr;
     if (init) {
@@ -242,7 +286,10 @@ static m3_status_t prepare_prefill(const m3_shape_t *shape, const void *x, const
         p.hT = final_state->h; p.phiT = final_state->phi; p.prevBT = final_state->prev_B;
         p.prevxT = final_state->prev_x;
     }
-    segments(p.batch * p.H, p.T, p.S, p.cps);
+    // segments of whole pre-pass chunks (which are whole output-pass chunks)
+    int32_t cps;
+    segments(p.batch * p.H, p.T, Qpre, p.S, cps);
+    p.seglen = int64_t(cps) * Qpre;
     unsigned char *ws = static_cast<unsigned char *>(workspace);
     p.segU = reinterpret_cast<float *>(ws + w.segU);
     p.segG = reinterpret_cast<float *>(ws + w.segG);
@@ -253,16 +300,27 @@ static m3_status_t prepare_prefill(const m3_shape_t *shape, const void *x, const
     return M3_OK;
 }
 
-static hipError_t launch_stage(int32_t stage, const PrefillParams &p, bool bf, hipStream_t stream) {
+// The launcher of one (I/O type, N, block variant, chunk kind).
+#define M3_LAUNCHERS(IO, N)                                                                        \
+    { m3::launch_prefill_##IO##_n##N, m3::launch_prefill_##IO##_n##N##_blk,                        \
+      m3::launch_prefill_##IO##_n##N##_qs, m3::launch_prefill_##IO##_n##N##_blk_qs }
+static const m3::prefill_launcher_t kLaunchers[2][4][4] = {
+    {M3_LAUNCHERS(f32, 16), M3_LAUNCHERS(f32, 32), M3_LAUNCHERS(f32, 64), M3_LAUNCHERS(f32, 128)},
+    {M3_LAUNCHERS(bf16, 16), M3_LAUNCHERS(bf16, 32), M3_LAUNCHERS(bf16, 64), M3_LAUNCHERS(bf16, 128)}};
+#undef M3_LAUNCHERS
+
+static hipError_t launch_stage(int32_t stage, const PrefillParams &p0, bool bf, hipStream_t stream) {
     if (stage != M3_STAGE_SEGMENT_STATE && stage != M3_STAGE_OUTPUT) return hipErrorInvalidValue;
     const bool out = stage == M3_STAGE_OUTPUT;
-    switch (p.N) {
-    case 16: return bf ? m3::launch_prefill_bf16_n16(p, out, stream) : m3::launch_prefill_f32_n16(p, out, stream);
-    case 32: return bf ? m3::launch_prefill_bf16_n32(p, out, stream) : m3::launch_prefill_f32_n32(p, out, stream);
-    case 64: return bf ? m3::launch_prefill_bf16_n64(p, out, stream) : m3::launch_prefill_f32_n64(p, out, stream);
-    case 128: return bf ? m3::launch_prefill_bf16_n128(p, out, stream) : m3::launch_prefill_f32_n128(p, out, stream);
-    }
-    return hipErrorInvalidValue;
+    const int ni = p0.N == 16 ? 0 : p0.N == 32 ? 1 : p0.N == 64 ? 2 : p0.N == 128 ? 3 : -1;
+    if (ni < 0) return hipErrorInvalidValue;
+    // this stage's chunk length, chunk count and chunks per segment
+    PrefillParams p = p0;
+    p.Q = out ? p.Qout : p.Qpre;
+    p.nC = int32_t((p.T + p.Q - 1) / p.Q);
+    p.cps = int32_t(p.seglen / p.Q);
+    const int kind = (p.blk.on ? 1 : 0) + (p.Q != 64 ? 2 : 0);
+    return kLaunchers[bf ? 1 : 0][ni][kind](p, out, stream);
 }
 
 m3_status_t m3_ssm_prefill(const m3_shape_t *shape, const void *x, const void *dt, const float *A,
@@ -312,7 +370,7 @@ m3_status_t m3_ssm_decode_step_block(const m3_shape_t *shape, const void *x, con
                                      const float *A, const void *lam, const void *theta,
                                      const void *B, const void *C, const m3_block_t *block,
                                      m3_state_t *state, void *y, hipStream_t stream) {
-    const m3_status_t sc = check_shape(shape, true);
+    const m3_status_t sc = check_shape(shape, Use::decode);
     if (sc != M3_OK) return sc;
     m3::BlockParams bp;
     const m3_status_t sb = resolve_block(block, bp);

@@ -105,14 +105,18 @@ def make_shape(batch, T, H, P, N, R, io_dtype, chunk=64, G=0,
                            int(_IO[io_dtype]), int(G), int(_IO[state_dtype]))
 
 
-def workspace_bytes(batch, T, H, P, N, R, io_dtype=torch.bfloat16) -> int:
-    return capi.m3_ssm_prefill_workspace_bytes(make_shape(batch, T, H, P, N, R, io_dtype))
+def workspace_bytes(batch, T, H, P, N, R, io_dtype=torch.bfloat16, chunk=64) -> int:
+    return capi.m3_ssm_prefill_workspace_bytes(make_shape(batch, T, H, P, N, R, io_dtype, chunk=chunk))
 
 
 def prefill(x, dt, A, lam, theta, B, C, state: State | None = None, final: State | None = None,
             want_final: bool = True, y=None, workspace=None, block: Block | None = None, z=None,
-            state_dtype=None):
+            state_dtype=None, chunk: int = 64):
     """Chunked prefill.  Returns (y, final_state or None).
+
+    ``chunk``: tokens per chunk, 64 (sub-chunks of 64/R tokens where a
+    64-token chunk does not fit on chip) or 64/R (32 for R = 3) to take the
+    small chunk always; the result is the same up to rounding.
 
     The carried state's h~ is float32 or bfloat16: the dtype of the given
     state(s), else ``state_dtype`` (default float32) for a new final state.
@@ -131,7 +135,7 @@ def prefill(x, dt, A, lam, theta, B, C, state: State | None = None, final: State
     sd = given[0] if given else (state_dtype or torch.float32)
     if any(d != sd for d in given) or (state_dtype is not None and state_dtype != sd):
         raise ValueError("initial and final states must share one state dtype")
-    shape = make_shape(b, T, H, P, N, R, io, G=B.shape[2], state_dtype=sd)
+    shape = make_shape(b, T, H, P, N, R, io, chunk=chunk, G=B.shape[2], state_dtype=sd)
     if y is None:
         y = torch.empty_like(x)
     if want_final and final is None:
@@ -165,7 +169,7 @@ def prefill(x, dt, A, lam, theta, B, C, state: State | None = None, final: State
     return y, final
 
 
-def prefill_stage(stage: int, x, dt, A, lam, theta, B, C, state, final, y, workspace):
+def prefill_stage(stage: int, x, dt, A, lam, theta, B, C, state, final, y, workspace, chunk: int = 64):
     """Enqueue one stage of the prefill (include/m3_ssm_stages.h) with the
     arguments of a full prefill; used to time the kernels one at a time."""
     b, T, H, R, P = x.shape
@@ -173,7 +177,7 @@ def prefill_stage(stage: int, x, dt, A, lam, theta, B, C, state, final, y, works
     io = x.dtype
     _check_bc(B, C, (b, T), R, N)
     rc = capi.m3_ssm_prefill_stage(
-        stage, make_shape(b, T, H, P, N, R, io, G=B.shape[2],
+        stage, make_shape(b, T, H, P, N, R, io, chunk=chunk, G=B.shape[2],
                           state_dtype=next((q.h.dtype for q in (state, final) if q is not None), torch.float32)),
         _ptr(x, "x", io), _ptr(dt, "dt", io),
         _ptr(A, "A", torch.float32), _ptr(lam, "lam", io), _ptr(theta, "theta", io),

@@ -160,18 +160,9 @@ def state_to_true(h_rot, phi):
     return rotate_pairs(h_rot, np.asarray(phi)[..., None], axis=2)
 
 
-def state_to_rot(h_true, phi):
-    """h_rot = R(-Phi) h_true."""
-    return rotate_pairs(h_true, -np.asarray(phi)[..., None], axis=2)
-
-
 def prevB_to_true(prevB_rot, phi):
     """B_true = R(Phi) B_rot; prevB [b,H,R,N], phi [b,H,N/2]."""
     return rotate_pairs(prevB_rot, np.asarray(phi)[:, :, None, :], axis=3)
-
-
-def prevB_to_rot(prevB_true, phi):
-    return rotate_pairs(prevB_true, -np.asarray(phi)[:, :, None, :], axis=3)
 
 
 def wrap_angle(phi):

@@ -50,12 +50,12 @@ def gpu_state(state):
                 prev_x=state.prev_x.float().cpu().numpy().astype(np.float64))
 
 
-def run_gpu_prefill(d, io, init=None, want_final=True):
+def run_gpu_prefill(d, io, init=None, want_final=True, chunk=64):
     """d: numpy inputs.  init: mixer.State or None.  Returns (y fp64, State)."""
     from mamba_selective_ssm_ssd_amd import mixer
     t = to_dev(d, io)
     y, st = mixer.prefill(t["x"], t["dt"], t["A"], t["lam"], t["theta"], t["B"], t["C"],
-                          state=init, want_final=want_final)
+                          state=init, want_final=want_final, chunk=chunk)
     return y.double().cpu().numpy(), st
 
 

@@ -48,33 +48,70 @@ def _shape(**kw):
     return capi.m3_shape_t(**d)
 
 
+def _segments(bh, T, Q, slots=256):
+    """Segments per sequence for a chunk length Q: enough (batch, head,
+    segment) workgroups to fill 256 compute units, no empty segment."""
+    nC = -(-T // Q)
+    s = max(1, min(1 if bh >= slots else slots // bh, nC))
+    c = -(-nC // s)
+    return -(-nC // c)
+
+
 def test_workspace_bytes():
     ws = capi.m3_ssm_prefill_workspace_bytes(_shape())
-    # b2 T100 H3: 6 sequences of 2 chunks -> 2 segments of one chunk each
-    bh, S, N, P, K = 6, 2, 64, 64, 32
+    # b2 T100 H3 R4: 6 sequences; the workspace is sized for the smallest
+    # chunk of the rank (16 tokens for R = 4): 7 chunks -> 7 segments
+    bh, N, P, K = 6, 64, 64, 32
+    S = _segments(bh, 100, 16)
+    assert S == 7
     at_least = bh * S * N * P * 4 + bh * S * 4 + bh * S * K * 8 + bh * N * P * 4 + bh * K * 8
     assert at_least <= ws <= at_least + 5 * 256
-    # one segment per sequence once batch * heads fills the chip
-    big = capi.m3_ssm_prefill_workspace_bytes(_shape(batch=4, nheads=64, seqlen=2048))
-    bh = 256
-    assert big <= bh * N * P * 4 * 2 + bh * (4 + K * 8 + K * 8) + 5 * 256
+    # one segment per sequence once batch * heads fills the chip: unused
+    assert capi.m3_ssm_prefill_workspace_bytes(_shape(batch=4, nheads=64, seqlen=2048)) == 256
+    # never more than about 17 MB (batch * heads * segments <= 256)
+    for bh_, T in ((1, 65536), (3, 10000), (255, 5000), (64, 65536)):
+        w = capi.m3_ssm_prefill_workspace_bytes(_shape(batch=1, nheads=bh_, seqlen=T, dstate=128))
+        assert 0 < w <= 256 * 128 * 64 * 4 * 2 + 256 * (4 + 64 * 8 * 2) + 5 * 256
     # invalid or unsupported shapes report 0
     assert capi.m3_ssm_prefill_workspace_bytes(_shape(dstate=63)) == 0
     assert capi.m3_ssm_prefill_workspace_bytes(_shape(dstate=48)) == 0
     assert capi.m3_ssm_prefill_workspace_bytes(_shape(headdim=128)) == 0
     assert capi.m3_ssm_prefill_workspace_bytes(_shape(rank=5)) == 0
-    assert capi.m3_ssm_prefill_workspace_bytes(_shape(chunk=32)) == 0
     assert capi.m3_ssm_prefill_workspace_bytes(_shape(seqlen=0)) == 0
-    # a whole fp32 chunk at N=128, R>=2 or N=64, R=4 does not fit in LDS; every bf16 shape does
-    f32 = capi.M3_DTYPE_F32
-    assert capi.m3_ssm_prefill_workspace_bytes(_shape(dstate=128, rank=2, io_dtype=f32)) == 0
-    assert capi.m3_ssm_prefill_workspace_bytes(_shape(dstate=128, rank=1, io_dtype=f32)) > 0
-    assert capi.m3_ssm_prefill_workspace_bytes(_shape(io_dtype=f32)) == 0
-    assert capi.m3_ssm_prefill_workspace_bytes(_shape(rank=3, io_dtype=f32)) > 0
-    for n in (16, 32, 64, 128):
-        for r in (1, 2, 3, 4):
-            for pd in (16, 32, 64):
-                assert capi.m3_ssm_prefill_workspace_bytes(_shape(dstate=n, rank=r, headdim=pd)) > 0
+    # chunk: 64 or the rank's small chunk (64/R tokens; 32 for R = 3)
+    assert capi.m3_ssm_prefill_workspace_bytes(_shape(chunk=32)) == 0
+    assert capi.m3_ssm_prefill_workspace_bytes(_shape(chunk=16)) > 0
+    assert capi.m3_ssm_prefill_workspace_bytes(_shape(chunk=128)) == 0
+    for r, q in ((1, 64), (2, 32), (3, 32), (4, 16)):
+        assert capi.m3_ssm_prefill_workspace_bytes(_shape(rank=r, chunk=q)) > 0
+        for bad in (8, 16, 32, 48):
+            if bad != q:
+                assert capi.m3_ssm_prefill_workspace_bytes(_shape(rank=r, chunk=bad)) == 0
+    # every (N, P, R) in both I/O types: with fp32 I/O a 64-token chunk at
+    # N = 128 with R >= 2 or N = 64 with R = 4 exceeds the LDS and takes the
+    # small chunk
+    for io in (capi.M3_DTYPE_F32, capi.M3_DTYPE_BF16):
+        for n in (16, 32, 64, 128):
+            for r in (1, 2, 3, 4):
+                for pd in (16, 32, 64):
+                    assert capi.m3_ssm_prefill_workspace_bytes(
+                        _shape(dstate=n, rank=r, headdim=pd, io_dtype=io)) > 0
+
+
+def test_in_chunk_offsets_stay_32_bit():
+    """Offsets within a chunk are 32-bit: 64 * H * R * max(N, P) must stay
+    below 2^31 (a larger shape would wrap them); the boundary is exact."""
+    H = 2 ** 31 // (64 * 4 * 64)                      # 64 * H * 4 * 64 == 2^31
+    assert capi.m3_ssm_prefill_workspace_bytes(_shape(batch=1, nheads=H)) == 0
+    assert capi.m3_ssm_prefill_workspace_bytes(_shape(batch=1, nheads=H - 1)) > 0
+    H2 = 2 ** 31 // (64 * 1 * 128)
+    assert capi.m3_ssm_prefill_workspace_bytes(_shape(batch=1, nheads=H2, rank=1, dstate=128)) == 0
+    assert capi.m3_ssm_prefill_workspace_bytes(_shape(batch=1, nheads=H2 - 1, rank=1, dstate=128)) > 0
+    assert capi.m3_ssm_prefill_backward_workspace_bytes(_shape(batch=1, nheads=H)) == 0
+    # decode: the same limit
+    rc = capi.m3_ssm_decode_step(_shape(batch=1, nheads=H), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                 FAKE, capi.m3_state_t(FAKE, FAKE, FAKE, FAKE), FAKE, None)
+    assert rc == capi.M3_ERR_UNSUPPORTED
 
 
 def _prefill(shape, **over):
@@ -193,10 +230,11 @@ def test_block_errors():
         ptrs = [None] * 5
         ptrs[i] = FAKE_MISALIGNED
         assert _prefill_block(_shape(), capi.m3_block_t(0, 0.0, *ptrs)) == capi.M3_ERR_INVALID_ARGUMENT
-    # bf16, N = 128, P = 64, R = 4: the weight table no longer fits in LDS
+    # bf16, N = 128, P = 64, R = 4: with the weight table the 64-token chunk no
+    # longer fits in LDS, and the block kernels take 16-token chunks
     big = _shape(dstate=128, rank=4)
     assert _prefill_block(big, None) == W
-    assert _prefill_block(big, capi.m3_block_t(1, 1e-6)) == capi.M3_ERR_UNSUPPORTED
+    assert _prefill_block(big, capi.m3_block_t(1, 1e-6)) == W
     st = capi.m3_state_t(FAKE, FAKE, FAKE, FAKE)
 
     def dec(block, **over):

@@ -22,8 +22,8 @@ def _inputs(b, T, H, P, N, R, io, seed=0, cfg=50):
     return synth.prefill_inputs(b, T, H, P, N, R, io=io, seed=seed, cfg=cfg)
 
 
-def _parity(d, io, init=None, init_np=None):
-    y, st = run_gpu_prefill(d, io, init=init)
+def _parity(d, io, init=None, init_np=None, chunk=64):
+    y, st = run_gpu_prefill(d, io, init=init, chunk=chunk)
     yr, hT, phiT = run_oracle(d, init_np)
     tol = TOL[io]
     e_y = slice_err(y, yr, (0, 2))
@@ -45,24 +45,91 @@ def test_cfg0_tiny_siso_fp32():
     (128, 64, 1, "bf16"),   # configuration 1 shape
     (64, 64, 4, "bf16"),    # configurations 2-4 shape
     (128, 64, 1, "f32"),
-    (64, 64, 2, "f32"),
+    (64, 64, 4, "f32"),
+    (128, 64, 4, "f32"),
 ])
 def test_config_shapes_ragged(N, P, R, io):
     d = _inputs(2, 300, 3, P, N, R, io, seed=1)      # 5 chunks, ragged tail of 44
     _parity(d, io)
 
 
-@pytest.mark.parametrize("N,P", [(16, 16), (16, 64), (32, 32), (64, 16), (128, 32), (32, 64)])
+def small_chunk(R):
+    """Tokens per chunk of the small MIMO chunk: 64/R tokens (64 virtual rows),
+    32 for R = 3."""
+    return {1: 64, 2: 32, 3: 32, 4: 16}[R]
+
+
+@pytest.mark.parametrize("N,P", [(16, 16), (16, 64), (32, 32), (64, 16), (128, 32), (32, 64),
+                                 (64, 64), (128, 64)])
 @pytest.mark.parametrize("R", [1, 2, 3, 4])
 def test_tile_set(N, P, R):
+    """Every (N, P, R) of the tile set is compiled for both I/O types (with
+    64-token chunks, or small ones where 64 tokens exceed the LDS)."""
+    from mamba_selective_ssm_ssd_amd import mixer
+    for io in ("f32", "bf16"):
+        assert mixer.workspace_bytes(1, 150, 2, P, N, R, torch.float32 if io == "f32" else torch.bfloat16) > 0
     io = "bf16" if (N + P + R) % 2 == 0 else "f32"
     d = _inputs(1, 150, 2, P, N, R, io, seed=N + P + R)
-    from mamba_selective_ssm_ssd_amd import capi, mixer
-    if mixer.workspace_bytes(1, 150, 2, P, N, R, torch.float32 if io == "f32" else torch.bfloat16) == 0:
-        with pytest.raises(capi.M3Error):
-            run_gpu_prefill(d, io)
-        return
     _parity(d, io)
+
+
+@pytest.mark.parametrize("N,P", [(16, 16), (32, 64), (64, 64), (128, 32), (128, 64)])
+@pytest.mark.parametrize("R", [2, 3, 4])
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_small_chunk(N, P, R, io):
+    """Chunks of 64/R tokens (64 virtual rows; 32 tokens for R = 3) asked for
+    explicitly: several chunks and a ragged tail."""
+    T = 5 * small_chunk(R) + 7
+    d = _inputs(2, T, 2, P, N, R, io, seed=N + 3 * P + 7 * R)
+    d["A"] *= 0.1                                      # the carried state stays visible
+    _parity(d, io, chunk=small_chunk(R))
+
+
+@pytest.mark.parametrize("R", [2, 4])
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_small_chunk_segmented_with_carried_state(R, io):
+    """The small chunk on one long sequence (segments and pre-pass) from a
+    random carried state, then split calls and decode steps after it."""
+    from mamba_selective_ssm_ssd_amd import mixer
+    b, T, H, P, N = 1, 1200, 2, 32, 64
+    d = _inputs(b, T, H, P, N, R, io, seed=40 + R)
+    d["A"] *= 0.02
+    rng = np.random.default_rng(400 + R)
+    init_np = dict(h=rng.standard_normal((b, H, N, P)).astype(np.float32),
+                   phi=rng.uniform(-np.pi, np.pi, size=(b, H, N // 2)).astype(np.float32),
+                   prev_B=rng.standard_normal((b, H, R, N)).astype(np.float32),
+                   prev_x=synth.round_io(rng.standard_normal((b, H, R, P)), io))
+    tio = torch.float32 if io == "f32" else torch.bfloat16
+    init = mixer.State(*(torch.from_numpy(init_np[k]).cuda() for k in ("h", "phi", "prev_B")),
+                       torch.from_numpy(init_np["prev_x"]).to("cuda", tio))
+    init_keep = {k: v.astype(np.float64) for k, v in init_np.items()}
+    yr, hT, phiT = run_oracle(d, init_keep)
+    T1, T2 = 1000, 1190
+    parts = [{k: (v[:, a:c] if v.ndim >= 3 else v) for k, v in d.items()} for a, c in ((0, T1), (T1, T2))]
+    y1, st = run_gpu_prefill(parts[0], io, init=init, chunk=small_chunk(R))
+    y2, st = run_gpu_prefill(parts[1], io, init=st, chunk=small_chunk(R))
+    t = to_dev(d, io)
+    ys = [y1, y2]
+    for s in range(T2, T):
+        y = mixer.decode_step(t["x"][:, s].clone(), t["dt"][:, s].clone(), t["A"],
+                              t["lam"][:, s].clone(), t["theta"][:, s].clone(),
+                              t["B"][:, s].clone(), t["C"][:, s].clone(), st)
+        ys.append(y.double().cpu().numpy()[:, None])
+    yg = np.concatenate(ys, axis=1)
+    assert slice_err(yg, yr, (0, 2)) <= TOL[io]
+    check_final_state(st, d, hT, phiT, io, TOL[io])
+
+
+def test_small_chunk_equals_64_token_chunk():
+    """Both chunk lengths give the same result within fp32 rounding (fp32 I/O
+    at a shape whose 64-token chunk fits on chip)."""
+    d = _inputs(2, 333, 2, 64, 64, 2, "f32", seed=21)
+    d["A"] *= 0.1
+    ya, sa = run_gpu_prefill(d, "f32", chunk=32)
+    yb, sb = run_gpu_prefill(d, "f32", chunk=64)
+    assert slice_err(ya, yb, (0, 2)) < 2e-5
+    ha, hb = gpu_state(sa)["h"], gpu_state(sb)["h"]
+    assert slice_err(ha, hb, (0, 1)) < 2e-5
 
 
 @pytest.mark.parametrize("bh", [(8, 32), (5, 52)])
@@ -134,8 +201,7 @@ def test_s2_split_prefill(io, T1):
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 def test_s2_prefill_then_decode(io):
     from mamba_selective_ssm_ssd_amd import mixer
-    b, T, H, P, N = 2, 150, 3, 64, 64
-    R = 4 if io == "bf16" else 3          # fp32 staging of R = 4 at N = P = 64 exceeds LDS
+    b, T, H, P, N, R = 2, 150, 3, 64, 64, 4
     d = _inputs(b, T, H, P, N, R, io, seed=10)
     d["A"] *= 0.05
     yr, hT, phiT = run_oracle(d)
@@ -197,7 +263,7 @@ def test_s3_extremes(case):
 @pytest.mark.parametrize("T", [1, 2, 63, 64, 65])
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 def test_s4_short_sequences(T, io):
-    d = _inputs(2, T, 3, 64, 64, 4 if io == "bf16" else 3, io, seed=13)
+    d = _inputs(2, T, 3, 64, 64, 4, io, seed=13)
     _parity(d, io)
 
 
