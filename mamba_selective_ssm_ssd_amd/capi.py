@@ -25,7 +25,10 @@ M3_ERR_HIP = 4
 EXPORTED = ("m3_ssm_prefill_workspace_bytes", "m3_ssm_prefill", "m3_ssm_decode_step",
             "m3_status_string", "m3_ssm_prefill_stage", "m3_ssm_prefill_block",
             "m3_ssm_decode_step_block", "m3_ssm_prefill_backward_workspace_bytes",
-            "m3_ssm_prefill_backward")
+            "m3_ssm_prefill_backward", "m3_ssm_prefill_noalloc")
+
+# Size of the static workspace of m3_ssm_prefill_noalloc (include/m3_ssm_noalloc.h).
+M3_NOALLOC_SCRATCH_BYTES = 24 << 20
 
 # Stages of the prefill (include/m3_ssm_stages.h).
 M3_STAGE_SEGMENT_STATE = 0
@@ -102,6 +105,8 @@ def load():
     lib.m3_ssm_prefill_backward.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, stp, vp, gp, vp,
                                             ctypes.c_size_t, vp]
     lib.m3_ssm_prefill_backward.restype = ctypes.c_int
+    lib.m3_ssm_prefill_noalloc.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, stp, stp, vp, vp]
+    lib.m3_ssm_prefill_noalloc.restype = ctypes.c_int
     lib.m3_status_string.argtypes = [ctypes.c_int]
     lib.m3_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -125,6 +130,14 @@ def m3_ssm_prefill(shape, x, dt, A, lam, theta, B, C, init, final_state, y, work
         ctypes.byref(init) if init is not None else None,
         ctypes.byref(final_state) if final_state is not None else None,
         y, workspace, int(workspace_bytes), stream))
+
+
+def m3_ssm_prefill_noalloc(shape, x, dt, A, lam, theta, B, C, init, final_state, y, stream) -> int:
+    """m3_ssm_prefill with the library's static workspace (no workspace argument)."""
+    return int(load().m3_ssm_prefill_noalloc(
+        ctypes.byref(shape), x, dt, A, lam, theta, B, C,
+        ctypes.byref(init) if init is not None else None,
+        ctypes.byref(final_state) if final_state is not None else None, y, stream))
 
 
 def m3_ssm_prefill_stage(stage, shape, x, dt, A, lam, theta, B, C, init, final_state, y,

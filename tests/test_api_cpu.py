@@ -27,6 +27,27 @@ def _declared_functions():
     return sorted(names)
 
 
+def test_library_imports_no_allocation_copy_or_synchronisation():
+    """The library never allocates, frees, copies or synchronises
+    (include/m3_ssm.h; m3_ssm_prefill_noalloc takes a static array): none of
+    its dynamic imports is a HIP allocation, free, memset, memcpy or
+    synchronisation routine."""
+    import shutil
+    import subprocess
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm is not installed")
+    out = subprocess.run([nm, "-D", "--undefined-only", capi.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    names = [line.split()[-1].split("@")[0] for line in out.splitlines() if line.strip()]
+    assert any(n == "hipLaunchKernel" for n in names)       # the listing is the library's
+    banned = re.compile(r"^hip(Malloc|Free|HostMalloc|HostAlloc|HostFree|HostRegister|ExtMalloc|"
+                        r"MemAlloc|MemPool|Memset|Memcpy|DeviceSynchronize|StreamSynchronize|"
+                        r"EventSynchronize|MallocAsync|FreeAsync)")
+    bad = sorted(n for n in names if banned.match(n))
+    assert not bad, f"allocation / copy / synchronisation imports: {bad}"
+
+
 def test_library_exports_every_declared_function():
     lib = capi.load()
     names = _declared_functions()
