@@ -21,7 +21,8 @@
  *                           intra-chunk masked contraction and the incoming-
  *                           state term (MFMA), writing y; the last segment
  *                           writes the final carried state
- * The segmentation depends on the shape only.  Running the stages in order
+ * The segmentation depends on the shape only (m3_ssm_prefill_plan reports
+ * it, with each stage's chunk length).  Running the stages in order
  * with the same arguments is a full prefill; either stage may be enqueued
  * again afterwards with the same arguments and rewrites the same outputs.
  *
@@ -41,6 +42,16 @@ typedef enum {
     M3_STAGE_SEGMENT_STATE = 0,
     M3_STAGE_OUTPUT = 1
 } m3_stage_t;
+
+/* How m3_ssm_prefill runs a shape with the plain kernels (with_block = 0)
+ * or with the block kernels (with_block != 0: a call of m3_ssm_prefill_block
+ * whose block has at least one piece): tokens per chunk of the pre-pass and
+ * of the output pass (64 or m3_ssm.h's qs(R)), segments per sequence (1: no
+ * pre-pass is enqueued) and tokens per segment (the last segment may be
+ * shorter).  Any output pointer may be NULL.  Errors: those of the shape
+ * check of m3_ssm_prefill. */
+m3_status_t m3_ssm_prefill_plan(const m3_shape_t *shape, int32_t with_block, int32_t *chunk_pre,
+                                int32_t *chunk_out, int32_t *segments, int64_t *segment_tokens);
 
 m3_status_t m3_ssm_prefill_stage(int32_t stage, const m3_shape_t *shape, const void *x,
                                  const void *dt, const float *A, const void *lam,

@@ -25,7 +25,8 @@ M3_ERR_HIP = 4
 EXPORTED = ("m3_ssm_prefill_workspace_bytes", "m3_ssm_prefill", "m3_ssm_decode_step",
             "m3_status_string", "m3_ssm_prefill_stage", "m3_ssm_prefill_block",
             "m3_ssm_decode_step_block", "m3_ssm_prefill_backward_workspace_bytes",
-            "m3_ssm_prefill_backward", "m3_ssm_prefill_noalloc")
+            "m3_ssm_prefill_backward", "m3_ssm_prefill_noalloc", "m3_ssm_prefill_plan",
+            "m3_ceiling_mfma", "m3_ceiling_stream")
 
 # Size of the static workspace of m3_ssm_prefill_noalloc (include/m3_ssm_noalloc.h).
 M3_NOALLOC_SCRATCH_BYTES = 24 << 20
@@ -107,6 +108,13 @@ def load():
     lib.m3_ssm_prefill_backward.restype = ctypes.c_int
     lib.m3_ssm_prefill_noalloc.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, stp, stp, vp, vp]
     lib.m3_ssm_prefill_noalloc.restype = ctypes.c_int
+    i32p, i64p = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
+    lib.m3_ssm_prefill_plan.argtypes = [sp, ctypes.c_int32, i32p, i32p, i32p, i64p]
+    lib.m3_ssm_prefill_plan.restype = ctypes.c_int
+    lib.m3_ceiling_mfma.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp, vp]
+    lib.m3_ceiling_mfma.restype = ctypes.c_int
+    lib.m3_ceiling_stream.argtypes = [ctypes.c_int32, vp, vp, ctypes.c_int64, ctypes.c_int32, vp]
+    lib.m3_ceiling_stream.restype = ctypes.c_int
     lib.m3_status_string.argtypes = [ctypes.c_int]
     lib.m3_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -138,6 +146,24 @@ def m3_ssm_prefill_noalloc(shape, x, dt, A, lam, theta, B, C, init, final_state,
         ctypes.byref(shape), x, dt, A, lam, theta, B, C,
         ctypes.byref(init) if init is not None else None,
         ctypes.byref(final_state) if final_state is not None else None, y, stream))
+
+
+def m3_ssm_prefill_plan(shape, block=False):
+    """(status, chunk_pre, chunk_out, segments, segment_tokens) of a shape;
+    block: whether the call carries block pieces."""
+    q1, q2, sg = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int32(0)
+    st = ctypes.c_int64(0)
+    rc = int(load().m3_ssm_prefill_plan(ctypes.byref(shape), 1 if block else 0, ctypes.byref(q1),
+                                        ctypes.byref(q2), ctypes.byref(sg), ctypes.byref(st)))
+    return rc, q1.value, q2.value, sg.value, st.value
+
+
+def m3_ceiling_mfma(kind, nblocks, iters, sink, stream) -> int:
+    return int(load().m3_ceiling_mfma(int(kind), int(nblocks), int(iters), sink, stream))
+
+
+def m3_ceiling_stream(mode, src, dst, n, nblocks, stream) -> int:
+    return int(load().m3_ceiling_stream(int(mode), src, dst, int(n), int(nblocks), stream))
 
 
 def m3_ssm_prefill_stage(stage, shape, x, dt, A, lam, theta, B, C, init, final_state, y,

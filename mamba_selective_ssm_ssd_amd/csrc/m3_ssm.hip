@@ -346,6 +346,22 @@ m3_status_t m3_ssm_prefill_block(const m3_shape_t *shape, const void *x, const v
     return M3_OK;
 }
 
+m3_status_t m3_ssm_prefill_plan(const m3_shape_t *shape, int32_t with_block, int32_t *chunk_pre,
+                                int32_t *chunk_out, int32_t *segments_out, int64_t *segment_tokens) {
+    const m3_status_t sc = check_shape(shape, Use::prefill);
+    if (sc != M3_OK) return sc;
+    const bool blk = with_block != 0;
+    const int Qpre = chunk_tokens(shape, blk, false), Qout = chunk_tokens(shape, blk, true);
+    if (Qpre == 0 || Qout == 0) return M3_ERR_UNSUPPORTED;
+    int32_t S, cps;
+    segments(shape->batch * shape->nheads, shape->seqlen, Qpre, S, cps);
+    if (chunk_pre) *chunk_pre = Qpre;
+    if (chunk_out) *chunk_out = Qout;
+    if (segments_out) *segments_out = S;
+    if (segment_tokens) *segment_tokens = int64_t(cps) * Qpre;
+    return M3_OK;
+}
+
 m3_status_t m3_ssm_prefill_stage(int32_t stage, const m3_shape_t *shape, const void *x,
                                  const void *dt, const float *A, const void *lam,
                                  const void *theta, const void *B, const void *C,
