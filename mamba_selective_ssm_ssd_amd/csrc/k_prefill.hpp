@@ -918,29 +918,46 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
         }
 
         // ---- a3 mask of this chunk: L[t][s] = exp(ell_t - ell_s) wgt_s (s < t),
-        // gam_t (s = t), 0 (s > t); row t, 8 consecutive s per thread (Q / 8
-        // threads per row).  With R = 1 and 64-token chunks the rows t < 32 are
-        // read for s < 32 only (their source pair), so 384 groups are
-        // evaluated, by the first six waves.
+        // gam_t (s = t), 0 (s > t); row t, ME consecutive s per thread: 8 for
+        // 64-token chunks, fewer for small chunks so that more threads share
+        // the table (with 8 per thread a 16-token chunk's table would fall on
+        // 32 threads of one wave).  With R = 1 and 64-token chunks the rows
+        // t < 32 are read for s < 32 only (their source pair), so 384 groups
+        // are evaluated, by the first six waves.
         if constexpr (C::LWT) {
             constexpr bool HALF = R == 1 && Q == 64 && kPT == 512;
-            constexpr int G8 = Q / 8; // threads per mask row
+            constexpr int ME = Q * Q >= 8 * kPT ? 8 : Q * Q >= kPT ? Q * Q / kPT : 1; // entries per thread
+            constexpr int GM = Q / ME;                                                // threads per mask row
             const int gi = HALF && tid >= 128 ? tid + 128 : tid; // skip rows < 32 x s >= 32
-            const int tt = HALF ? (tid < 128 ? tid >> 2 : gi >> 3) : tid / G8;
-            const int s0 = HALF ? (tid < 128 ? (tid & 3) * 8 : (gi & 7) * 8) : (tid % G8) * 8;
-            if (OUT && (HALF ? tid < 384 : tid < Q * G8)) {
-                float w[8];
+            const int tt = HALF ? (tid < 128 ? tid >> 2 : gi >> 3) : tid / GM;
+            const int s0 = HALF ? (tid < 128 ? (tid & 3) * 8 : (gi & 7) * 8) : (tid % GM) * ME;
+            if (OUT && (HALF ? tid < 384 : tid < Q * GM)) {
+                float w[ME];
                 {
                     // branch-free: every entry is evaluated, then selected
                     const float et = ell_s[tt], gt = gam_s[tt];
-                    const float4 e0 = *reinterpret_cast<const float4 *>(ell_s + s0);
-                    const float4 e1 = *reinterpret_cast<const float4 *>(ell_s + s0 + 4);
-                    const float4 w0 = *reinterpret_cast<const float4 *>(wgt_s + s0);
-                    const float4 w1 = *reinterpret_cast<const float4 *>(wgt_s + s0 + 4);
-                    const float el[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
-                    const float wg[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+                    float el[ME], wg[ME];
+                    if constexpr (ME == 8) {
+                        const float4 e0 = *reinterpret_cast<const float4 *>(ell_s + s0);
+                        const float4 e1 = *reinterpret_cast<const float4 *>(ell_s + s0 + 4);
+                        const float4 w0 = *reinterpret_cast<const float4 *>(wgt_s + s0);
+                        const float4 w1 = *reinterpret_cast<const float4 *>(wgt_s + s0 + 4);
+                        const float ev[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
+                        const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) {
+                        for (int j = 0; j < 8; ++j) {
+                            el[j] = ev[j];
+                            wg[j] = wv[j];
+                        }
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < ME; ++j) {
+                            el[j] = ell_s[s0 + j];
+                            wg[j] = wgt_s[s0 + j];
+                        }
+                    }
+#pragma unroll
+                    for (int j = 0; j < ME; ++j) {
                         // exp of a selected argument (0 where masked), then 0/1
                         // weights: no select or branch around the exp
                         const int ts = s0 + j;
@@ -949,9 +966,14 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
                         w[j] = lt * (e * wg[j]) + eq * gt;
                     }
                 }
-                float4 *dst = reinterpret_cast<float4 *>(lw_s + tt * C::LWP + s0);
-                dst[0] = make_float4(w[0], w[1], w[2], w[3]);
-                dst[1] = make_float4(w[4], w[5], w[6], w[7]);
+                float *dst = lw_s + tt * C::LWP + s0;
+                if constexpr (ME == 8) {
+                    reinterpret_cast<float4 *>(dst)[0] = make_float4(w[0], w[1], w[2], w[3]);
+                    reinterpret_cast<float4 *>(dst)[1] = make_float4(w[4], w[5], w[6], w[7]);
+                } else {
+#pragma unroll
+                    for (int j = 0; j < ME; ++j) dst[j] = w[j];
+                }
             }
             if (OUT && tid < Q) lw_s[Q * C::LWP + tid] = __expf(ell_s[tid]);
         }
