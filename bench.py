@@ -69,17 +69,17 @@ def aggregate_bytes(N, P):
 
 def kernel_bytes(kernel, b, T, H, P, N, R, plan, s=2):
     """Bytes each prefill kernel must move.  plan = (chunk_pre, chunk_out,
-    segments S, tokens per segment)."""
-    _, _, S, L = plan
+    segments S, tokens per segment, pre-pass pieces per segment k)."""
+    _, _, S, L, k = plan
     if kernel == "output":
-        # everything once, plus the aggregates of the segments before each one
-        return path_min_bytes(b, T, H, P, N, R, s) + b * H * aggregate_bytes(N, P) * S * (S - 1) // 2
+        # everything once, plus the aggregates of the pieces before each segment
+        return path_min_bytes(b, T, H, P, N, R, s) + b * H * aggregate_bytes(N, P) * k * S * (S - 1) // 2
     if kernel == "segment_state":
         if S == 1:
             return 0
         toks = min(T, (S - 1) * L)
         per = R * P * s + R * N * s + (N // 2) * s + 2 * s  # x, B, theta, dt, lam
-        return b * H * (toks * per + (S - 1) * aggregate_bytes(N, P))
+        return b * H * (toks * per + (S - 1) * k * aggregate_bytes(N, P))
     raise KeyError(kernel)
 
 
@@ -313,7 +313,7 @@ def prefill_entry(pf, ms, pre, out, name, kname, ceil):
     """The JSON entry of one prefill workload."""
     b, T, H, P, N, R = pf.dims
     s = 4 if pf.io == "f32" else 2
-    qpre, qout, S, L = pf.plan
+    qpre, qout, S, L, kp = pf.plan
     ob = kernel_bytes("output", b, T, H, P, N, R, pf.plan, s)
     pb = kernel_bytes("segment_state", b, T, H, P, N, R, pf.plan, s)
     flops = output_useful_flops(b, T, H, P, N, R, qout)
@@ -324,7 +324,8 @@ def prefill_entry(pf, ms, pre, out, name, kname, ceil):
                          "mfma_frac_of_bf16_peak": round(mf / BF16_MFMA_PEAK_TFLOPS, 4)})
     pm = path_min_bytes(b, T, H, P, N, R, s)
     e = {"workload": name, "tokens_per_s": round(b * T / (ms / 1000), 1), "ms_per_step": round(ms, 4),
-         "plan": {"chunk_pre": qpre, "chunk_out": qout, "segments": S, "segment_tokens": L},
+         "plan": {"chunk_pre": qpre, "chunk_out": qout, "segments": S, "segment_tokens": L,
+                  "prepass_pieces": kp},
          "roofline": roof,
          "path": {"min_bytes": pm, "frac_of_hbm_peak_at_min_bytes": round(pm / (ms / 1000) / 1e9 / HBM_PEAK_GBS, 4)},
          "kernels": {"output": {"avg_us": round(out * 1000, 2), "alg_bytes": ob,

@@ -129,9 +129,11 @@ typedef struct {
  * the GPU (below 256), each sequence is cut into S segments of whole chunks;
  * the workspace holds each segment's aggregate (an N x P fp32 state, its
  * summed log decay and rotation angle) and the carried state at the sequence
- * start.  It is sized for the largest S any chunk length of the shape can
- * give, so it serves m3_ssm_prefill_block too; batch * nheads * S <= 256, so
- * it never exceeds about 17 MB.  With S = 1 it is 256 bytes, unused. */
+ * start.  The pre-pass may cut each segment into pieces with an aggregate
+ * each, when that fills the GPU in whole rounds (m3_ssm_stages.h).  It is
+ * sized for both the plain and the block kernels' plans, so it serves
+ * m3_ssm_prefill_block too; the aggregates stay below 16 MiB and the whole
+ * workspace below about 27 MB.  With S = 1 it is 256 bytes, unused. */
 size_t m3_ssm_prefill_workspace_bytes(const m3_shape_t *shape);
 
 /*

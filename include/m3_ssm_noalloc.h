@@ -14,8 +14,9 @@
  * looked up once per device, on the first call with that device current.
  *
  * The workspace a shape needs (m3_ssm_prefill_workspace_bytes) is below about
- * 17 MB for every supported shape (batch * nheads * segments <= 256), so every
- * shape fits; a larger need would return M3_ERR_WORKSPACE.
+ * 27 MB for every supported shape (segment aggregates below 16 MiB, the
+ * carried state of fewer than 256 sequences), so every shape fits; a larger
+ * need would return M3_ERR_WORKSPACE.
  *
  * Every call on one GPU shares that GPU's array: calls that can overlap on
  * one GPU (on different streams, or from different threads) race and must
@@ -33,7 +34,7 @@
 extern "C" {
 #endif
 
-#define M3_NOALLOC_SCRATCH_BYTES (24u << 20) /* 24 MiB per GPU */
+#define M3_NOALLOC_SCRATCH_BYTES (32u << 20) /* 32 MiB per GPU */
 
 m3_status_t m3_ssm_prefill_noalloc(const m3_shape_t *shape, const void *x, const void *dt,
                                    const float *A, const void *lam, const void *theta,

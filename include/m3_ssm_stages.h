@@ -10,7 +10,8 @@
  * passes the state from chunk to chunk on chip.  It enqueues, in order:
  *   M3_STAGE_SEGMENT_STATE  when batch * heads is too small to fill the chip,
  *                           every sequence is cut into segments and this
- *                           pre-pass computes each segment's aggregate (its
+ *                           pre-pass computes each segment's (or each piece
+ *                           of a segment's) aggregate (its
  *                           state from a zero start, summed log decay and
  *                           rotary angle) and the carried state in its own
  *                           frame; it enqueues nothing when there is one
@@ -47,11 +48,14 @@ typedef enum {
  * or with the block kernels (with_block != 0: a call of m3_ssm_prefill_block
  * whose block has at least one piece): tokens per chunk of the pre-pass and
  * of the output pass (64 or m3_ssm.h's qs(R)), segments per sequence (1: no
- * pre-pass is enqueued) and tokens per segment (the last segment may be
- * shorter).  Any output pointer may be NULL.  Errors: those of the shape
- * check of m3_ssm_prefill. */
+ * pre-pass is enqueued), tokens per segment (the last segment may be
+ * shorter) and the pieces the pre-pass cuts each of the first segments - 1
+ * segments into (one workgroup and one aggregate per piece; more pieces than
+ * one when that fills the compute units in whole rounds).  Any output pointer
+ * may be NULL.  Errors: those of the shape check of m3_ssm_prefill. */
 m3_status_t m3_ssm_prefill_plan(const m3_shape_t *shape, int32_t with_block, int32_t *chunk_pre,
-                                int32_t *chunk_out, int32_t *segments, int64_t *segment_tokens);
+                                int32_t *chunk_out, int32_t *segments, int64_t *segment_tokens,
+                                int32_t *prepass_pieces);
 
 m3_status_t m3_ssm_prefill_stage(int32_t stage, const m3_shape_t *shape, const void *x,
                                  const void *dt, const float *A, const void *lam,

@@ -29,7 +29,7 @@ EXPORTED = ("m3_ssm_prefill_workspace_bytes", "m3_ssm_prefill", "m3_ssm_decode_s
             "m3_ceiling_mfma", "m3_ceiling_stream")
 
 # Size of the static workspace of m3_ssm_prefill_noalloc (include/m3_ssm_noalloc.h).
-M3_NOALLOC_SCRATCH_BYTES = 24 << 20
+M3_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 # Stages of the prefill (include/m3_ssm_stages.h).
 M3_STAGE_SEGMENT_STATE = 0
@@ -109,7 +109,7 @@ def load():
     lib.m3_ssm_prefill_noalloc.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, stp, stp, vp, vp]
     lib.m3_ssm_prefill_noalloc.restype = ctypes.c_int
     i32p, i64p = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
-    lib.m3_ssm_prefill_plan.argtypes = [sp, ctypes.c_int32, i32p, i32p, i32p, i64p]
+    lib.m3_ssm_prefill_plan.argtypes = [sp, ctypes.c_int32, i32p, i32p, i32p, i64p, i32p]
     lib.m3_ssm_prefill_plan.restype = ctypes.c_int
     lib.m3_ceiling_mfma.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp, vp]
     lib.m3_ceiling_mfma.restype = ctypes.c_int
@@ -149,13 +149,14 @@ def m3_ssm_prefill_noalloc(shape, x, dt, A, lam, theta, B, C, init, final_state,
 
 
 def m3_ssm_prefill_plan(shape, block=False):
-    """(status, chunk_pre, chunk_out, segments, segment_tokens) of a shape;
-    block: whether the call carries block pieces."""
-    q1, q2, sg = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int32(0)
+    """(status, chunk_pre, chunk_out, segments, segment_tokens, prepass_pieces)
+    of a shape; block: whether the call carries block pieces."""
+    q1, q2, sg, kp = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int32(0)
     st = ctypes.c_int64(0)
     rc = int(load().m3_ssm_prefill_plan(ctypes.byref(shape), 1 if block else 0, ctypes.byref(q1),
-                                        ctypes.byref(q2), ctypes.byref(sg), ctypes.byref(st)))
-    return rc, q1.value, q2.value, sg.value, st.value
+                                        ctypes.byref(q2), ctypes.byref(sg), ctypes.byref(st),
+                                        ctypes.byref(kp)))
+    return rc, q1.value, q2.value, sg.value, st.value, kp.value
 
 
 def m3_ceiling_mfma(kind, nblocks, iters, sink, stream) -> int:

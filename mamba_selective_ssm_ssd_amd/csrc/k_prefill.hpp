@@ -621,7 +621,9 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
     constexpr bool CP2 = C::MFP && C::FREEW > 0;
 
     // workgroup -> (b, h, segment); consecutive heads land on the same XCD
-    const int nseg = OUT ? p.S : p.S - 1;
+    // output pass: S segments per sequence; pre-pass: the first S - 1 of
+    // them, each cut into kpre pieces (aggregates indexed by piece)
+    const int nseg = OUT ? p.S : (p.S - 1) * p.kpre;
     const int64_t total = p.batch * p.H * nseg;
     int64_t li = blockIdx.x;
     if (total % 8 == 0) li = int64_t(blockIdx.x % 8) * (total / 8) + blockIdx.x / 8;
@@ -652,7 +654,7 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
         double a = 0.0;
         if (OUT && p.has_init) a = p.S == 1 ? double(p.phi0[bh * K + k]) : p.phi0ws[bh * K + k];
         if (OUT)
-            for (int s2 = 0; s2 < seg; ++s2) a += p.segTh[(bh * p.S + s2) * K + k];
+            for (int s2 = 0; s2 < seg * p.kpre; ++s2) a += p.segTh[(bh * p.NA + s2) * K + k];
         ths_s[k] = a;
     }
 
@@ -710,8 +712,8 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
 #pragma unroll
                         for (int v = 0; v < 4; ++v) st[j][v] = hi[(16 * nt + 4 * g + v) * P + pc];
                     }
-                    for (int s2 = 0; s2 < seg; ++s2) {
-                        const int64_t so = bh * p.S + s2;
+                    for (int s2 = 0; s2 < seg * p.kpre; ++s2) {
+                        const int64_t so = bh * p.NA + s2;
                         const float eg = __expf(p.segG[so]);
                         const float *U = p.segU + so * int64_t(N) * P;
 #pragma unroll
@@ -1265,7 +1267,7 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
 
     if (!OUT) {
         // segment aggregate: state from zero, summed log decay and angle
-        float *U = p.segU + (bh * p.S + seg) * int64_t(N) * P;
+        float *U = p.segU + (bh * p.NA + seg) * int64_t(N) * P;
 #pragma unroll
         for (int j = 0; j < C::TW; ++j) {
             const int tile = wave + kPW * j;
@@ -1274,8 +1276,8 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
 #pragma unroll
             for (int v = 0; v < 4; ++v) U[(16 * nt + 4 * g + v) * P + 16 * pt + l16] = st[j][v];
         }
-        if (tid == 0) p.segG[bh * p.S + seg] = gsum;
-        for (int k = tid; k < K; k += kPT) p.segTh[(bh * p.S + seg) * K + k] = ths_s[k];
+        if (tid == 0) p.segG[bh * p.NA + seg] = gsum;
+        for (int k = tid; k < K; k += kPT) p.segTh[(bh * p.NA + seg) * K + k] = ths_s[k];
         return;
     }
     if (seg != p.S - 1 || !p.has_final) return;
@@ -1342,7 +1344,7 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
 template <typename IO, int N, int P, int R, int QC, bool OUT, bool BLK>
 hipError_t launch_prefill_inst(const PrefillParams &p, hipStream_t s) {
     typedef Cfg<IO, N, P, R, QC, BLK> C;
-    const int nseg = OUT ? p.S : p.S - 1;
+    const int nseg = OUT ? p.S : (p.S - 1) * p.kpre;
     if (nseg <= 0) return hipSuccess;
     if (C::bytes > 65536) {
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_prefill<IO, N, P, R, QC, OUT, BLK>),

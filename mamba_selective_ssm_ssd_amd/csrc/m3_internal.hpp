@@ -26,7 +26,8 @@ struct PrefillParams {
     int32_t Q, nC;             // tokens per chunk of the launched pass (64 or small_chunk(R)), ceil(T/Q) chunks
     int32_t G, hpg;            // B/C groups, heads per group (head h reads group h / hpg)
     int32_t sbf16;             // carried state h~ stored in bf16
-    int32_t S, cps;            // segments per sequence, chunks of the launched pass per segment
+    int32_t S, cps;            // segments per sequence, chunks of the launched pass per segment (piece)
+    int32_t kpre, NA;          // pre-pass pieces per segment, aggregates per sequence ((S - 1) kpre)
     int32_t Qpre, Qout;        // tokens per chunk of the pre-pass and of the output pass (host)
     int64_t seglen;            // tokens per segment, a multiple of both (host)
     // inputs (I/O dtype unless noted)
@@ -45,9 +46,9 @@ struct PrefillParams {
     float *phiT, *prevBT;
     void *prevxT;
     // workspace (used when S > 1)
-    float *segU;    // [b][H][S][N][P]  segment aggregate: its state from a zero start
-    float *segG;    // [b][H][S]        summed log decay of the segment
-    double *segTh;  // [b][H][S][K]     summed rotary angle of the segment
+    float *segU;    // [b][H][NA][N][P] aggregate of each pre-pass piece: its state from a zero start
+    float *segG;    // [b][H][NA]       summed log decay of the piece
+    double *segTh;  // [b][H][NA][K]    summed rotary angle of the piece
     float *hinit;   // [b][H][N][P]     carried state in its own frame at the sequence start
     double *phi0ws; // [b][H][K]        Phi_{-1}
     BlockParams blk;

@@ -104,21 +104,57 @@ void segments(int64_t bh, int64_t T, int Q, int32_t &S, int32_t &cps) {
     S = int32_t((nC + c - 1) / c);
 }
 
-// Sized for the largest segment count any chunk length of the shape can
-// give (the smallest chunk has the most chunks), so one workspace serves the
-// plain and the block kernels.  Only a sequence cut into S > 1 segments uses
-// it; with S = 1 for every chunk length it is one aligned block, unused.
+// How one prefill call runs: chunk lengths of the two passes, S segments of
+// seglen tokens per sequence (whole pre-pass chunks), and the pre-pass cut
+// into kpre pieces per segment.  With S > 1 the pre-pass has (S - 1) b H
+// workgroups; when that is not a whole number of rounds over the 256
+// compute units, cutting each segment into kpre pieces (a power of two up to
+// 8, at least two chunks each) that make it one fills every round, at
+// NA = (S - 1) kpre aggregates per sequence (kept below 16 MiB in all).
+struct Plan {
+    int32_t Qpre, Qout, S, cps, kpre, NA;
+    int64_t seglen;
+};
+Plan make_plan(const m3_shape_t *s, bool blk) {
+    Plan pl{};
+    pl.Qpre = chunk_tokens(s, blk, false);
+    pl.Qout = chunk_tokens(s, blk, true);
+    if (pl.Qpre == 0 || pl.Qout == 0) return pl;
+    const int64_t bh = s->batch * s->nheads;
+    segments(bh, s->seqlen, pl.Qpre, pl.S, pl.cps);
+    pl.seglen = int64_t(pl.cps) * pl.Qpre;
+    pl.kpre = 1;
+    if (pl.S > 1) {
+        const int64_t w = int64_t(pl.S - 1) * bh;
+        const double agg = double(s->dstate) * double(s->headdim) * 4.0;
+        if (w % kSlots != 0) {
+            for (int k = 2; k <= 8; k *= 2) {
+                if ((w * k) % kSlots == 0 && pl.cps % k == 0 && pl.cps / k >= 2 &&
+                    double(w * k) * agg <= double(16 << 20)) {
+                    pl.kpre = k;
+                    break;
+                }
+            }
+        }
+    }
+    pl.NA = (pl.S - 1) * pl.kpre;
+    return pl;
+}
+
+// Sized for the plain and the block kernels' plans (their chunk lengths may
+// differ), so one workspace serves both.  Only a sequence cut into S > 1
+// segments uses it; otherwise it is one aligned block, unused.
 WorkspaceLayout layout(const m3_shape_t *s) {
     const size_t bh = size_t(s->batch) * size_t(s->nheads);
-    int32_t S, cps;
-    segments(int64_t(bh), s->seqlen, m3::small_chunk(s->rank), S, cps);
+    const Plan a = make_plan(s, false), b = make_plan(s, true);
+    const size_t NA = size_t(a.NA > b.NA ? a.NA : b.NA);
     const size_t N = size_t(s->dstate), P = size_t(s->headdim), K = N / 2;
-    const size_t used = S > 1 ? 1 : 0;
+    const size_t used = NA > 0 ? 1 : 0;
     WorkspaceLayout w;
     size_t off = 0;
-    w.segU = off; off += round_up(used * bh * S * N * P * sizeof(float));
-    w.segG = off; off += round_up(used * bh * S * sizeof(float));
-    w.segTh = off; off += round_up(used * bh * S * K * sizeof(double));
+    w.segU = off; off += round_up(bh * NA * N * P * sizeof(float));
+    w.segG = off; off += round_up(bh * NA * sizeof(float));
+    w.segTh = off; off += round_up(bh * NA * K * sizeof(double));
     w.hinit = off; off += round_up(used * bh * N * P * sizeof(float));
     w.phi0 = off; off += round_up(used * bh * K * sizeof(double));
     w.total = off > kAlign ? off : kAlign;
@@ -253,8 +289,8 @@ static m3_status_t prepare_prefill(const m3_shape_t *shape, const void *x, const
     const m3_status_t sb = resolve_block(block, bp);
     if (sb != M3_OK) return sb;
     // the block kernels also keep this head's weights and biases in LDS
-    const int Qpre = chunk_tokens(shape, bp.on, false), Qout = chunk_tokens(shape, bp.on, true);
-    if (Qpre == 0 || Qout == 0) return M3_ERR_UNSUPPORTED;
+    const Plan pl = make_plan(shape, bp.on);
+    if (pl.Qpre == 0 || pl.Qout == 0) return M3_ERR_UNSUPPORTED;
     const void *ptrs[] = {x, dt, A, lam, theta, B, C, y};
     for (const void *q : ptrs)
         if (!q || !aligned16(q)) return M3_ERR_INVALID_ARGUMENT;
@@ -274,8 +310,8 @@ static m3_status_t prepare_prefill(const m3_shape_t *shape, const void *x, const
     p.G = shape->ngroups ? shape->ngroups : shape->nheads;
     p.hpg = p.H / p.G;
     p.sbf16 = shape->state_dtype == M3_DTYPE_BF16;
-    p.Qpre = Qpre;
-    p.Qout = Qout;
+    p.Qpre = pl.Qpre;
+    p.Qout = pl.Qout;
     p.x = x; p.dt = dt; p.lam = lam; p.theta = theta; p.B = B; p.C = C; p.A = A; p.y = y;
     p.has_init = init != nullptr;
     if (init) {
@@ -287,9 +323,10 @@ static m3_status_t prepare_prefill(const m3_shape_t *shape, const void *x, const
         p.prevxT = final_state->prev_x;
     }
     // segments of whole pre-pass chunks (which are whole output-pass chunks)
-    int32_t cps;
-    segments(p.batch * p.H, p.T, Qpre, p.S, cps);
-    p.seglen = int64_t(cps) * Qpre;
+    p.S = pl.S;
+    p.seglen = pl.seglen;
+    p.kpre = pl.kpre;
+    p.NA = pl.NA;
     unsigned char *ws = static_cast<unsigned char *>(workspace);
     p.segU = reinterpret_cast<float *>(ws + w.segU);
     p.segG = reinterpret_cast<float *>(ws + w.segG);
@@ -318,7 +355,7 @@ static hipError_t launch_stage(int32_t stage, const PrefillParams &p0, bool bf, 
     PrefillParams p = p0;
     p.Q = out ? p.Qout : p.Qpre;
     p.nC = int32_t((p.T + p.Q - 1) / p.Q);
-    p.cps = int32_t(p.seglen / p.Q);
+    p.cps = int32_t(p.seglen / p.Q / (out ? 1 : p.kpre));
     const int kind = (p.blk.on ? 1 : 0) + (p.Q != 64 ? 2 : 0);
     return kLaunchers[bf ? 1 : 0][ni][kind](p, out, stream);
 }
@@ -347,18 +384,17 @@ m3_status_t m3_ssm_prefill_block(const m3_shape_t *shape, const void *x, const v
 }
 
 m3_status_t m3_ssm_prefill_plan(const m3_shape_t *shape, int32_t with_block, int32_t *chunk_pre,
-                                int32_t *chunk_out, int32_t *segments_out, int64_t *segment_tokens) {
+                                int32_t *chunk_out, int32_t *segments_out, int64_t *segment_tokens,
+                                int32_t *prepass_pieces) {
     const m3_status_t sc = check_shape(shape, Use::prefill);
     if (sc != M3_OK) return sc;
-    const bool blk = with_block != 0;
-    const int Qpre = chunk_tokens(shape, blk, false), Qout = chunk_tokens(shape, blk, true);
-    if (Qpre == 0 || Qout == 0) return M3_ERR_UNSUPPORTED;
-    int32_t S, cps;
-    segments(shape->batch * shape->nheads, shape->seqlen, Qpre, S, cps);
-    if (chunk_pre) *chunk_pre = Qpre;
-    if (chunk_out) *chunk_out = Qout;
-    if (segments_out) *segments_out = S;
-    if (segment_tokens) *segment_tokens = int64_t(cps) * Qpre;
+    const Plan pl = make_plan(shape, with_block != 0);
+    if (pl.Qpre == 0 || pl.Qout == 0) return M3_ERR_UNSUPPORTED;
+    if (chunk_pre) *chunk_pre = pl.Qpre;
+    if (chunk_out) *chunk_out = pl.Qout;
+    if (segments_out) *segments_out = pl.S;
+    if (segment_tokens) *segment_tokens = pl.seglen;
+    if (prepass_pieces) *prepass_pieces = pl.kpre;
     return M3_OK;
 }
 

@@ -80,19 +80,29 @@ def _segments(bh, T, Q, slots=256):
 
 def test_workspace_bytes():
     ws = capi.m3_ssm_prefill_workspace_bytes(_shape())
-    # b2 T100 H3 R4: 6 sequences; the workspace is sized for the smallest
-    # chunk of the rank (16 tokens for R = 4): 7 chunks -> 7 segments
-    bh, N, P, K = 6, 64, 64, 32
-    S = _segments(bh, 100, 16)
-    assert S == 7
-    at_least = bh * S * N * P * 4 + bh * S * 4 + bh * S * K * 8 + bh * N * P * 4 + bh * K * 8
+    # b2 T100 H3 R4 bf16: 6 sequences of two 64-token pre-pass chunks -> 2
+    # segments; the pre-pass covers the first, one aggregate per sequence
+    assert capi.m3_ssm_prefill_plan(_shape()) == (0, 64, 16, 2, 64, 1)
+    assert _segments(6, 100, 64) == 2
+    bh, N, P, K, NA = 6, 64, 64, 32, 1
+    at_least = bh * NA * N * P * 4 + bh * NA * 4 + bh * NA * K * 8 + bh * N * P * 4 + bh * K * 8
     assert at_least <= ws <= at_least + 5 * 256
     # one segment per sequence once batch * heads fills the chip: unused
     assert capi.m3_ssm_prefill_workspace_bytes(_shape(batch=4, nheads=64, seqlen=2048)) == 256
-    # never more than about 17 MB (batch * heads * segments <= 256)
-    for bh_, T in ((1, 65536), (3, 10000), (255, 5000), (64, 65536)):
-        w = capi.m3_ssm_prefill_workspace_bytes(_shape(batch=1, nheads=bh_, seqlen=T, dstate=128))
-        assert 0 < w <= 256 * 128 * 64 * 4 * 2 + 256 * (4 + 64 * 8 * 2) + 5 * 256
+    # never more than the allocation-free entry point's static array
+    # (include/m3_ssm_noalloc.h): aggregates below 16 MiB, the carried state
+    # of fewer than 256 sequences
+    worst = 0
+    for n in (16, 64, 128):
+        for pd in (16, 64):
+            for r in (1, 4):
+                for bh_ in (1, 2, 3, 5, 17, 32, 63, 64, 85, 100, 127, 128, 200, 255, 256):
+                    for T in (1, 100, 2048, 5000, 65536):
+                        w = capi.m3_ssm_prefill_workspace_bytes(
+                            _shape(batch=1, nheads=bh_, seqlen=T, dstate=n, headdim=pd, rank=r))
+                        assert 0 < w <= capi.M3_NOALLOC_SCRATCH_BYTES, (n, pd, r, bh_, T, w)
+                        worst = max(worst, w)
+    assert worst <= 27e6
     # invalid or unsupported shapes report 0
     assert capi.m3_ssm_prefill_workspace_bytes(_shape(dstate=63)) == 0
     assert capi.m3_ssm_prefill_workspace_bytes(_shape(dstate=48)) == 0
@@ -117,6 +127,24 @@ def test_workspace_bytes():
                 for pd in (16, 32, 64):
                     assert capi.m3_ssm_prefill_workspace_bytes(
                         _shape(dstate=n, rank=r, headdim=pd, io_dtype=io)) > 0
+
+
+def test_prefill_plan_prepass_pieces():
+    """The long-context MIMO shape (b1 T65536 H64): 4 segments of 16384 tokens;
+    the pre-pass's 3 x 64 = 192 workgroups would leave a quarter of 256 compute
+    units idle, so each segment is cut into 4 pieces (768 workgroups, three
+    full rounds).  The output pass takes 16-token chunks, the pre-pass 64."""
+    sh = _shape(batch=1, nheads=64, seqlen=65536, dstate=64, headdim=64, rank=4)
+    assert capi.m3_ssm_prefill_plan(sh) == (0, 64, 16, 4, 16384, 4)
+    ws = capi.m3_ssm_prefill_workspace_bytes(sh)
+    NA = 12                                           # (4 - 1) x 4 aggregates per sequence
+    at_least = 64 * NA * (64 * 64 * 4 + 4 + 32 * 8) + 64 * (64 * 64 * 4 + 32 * 8)
+    assert at_least <= ws <= at_least + 5 * 256
+    # whole rounds already: no pieces (b1 H128 -> 2 segments, 128 pre-pass workgroups -> 2 pieces)
+    assert capi.m3_ssm_prefill_plan(_shape(batch=1, nheads=128, seqlen=4096))[3:] == (2, 2048, 2)
+    assert capi.m3_ssm_prefill_plan(_shape(batch=1, nheads=256, seqlen=4096))[3:] == (1, 4096, 1)
+    # aggregates would pass 16 MiB: no pieces (N = 128, P = 64: 32 KiB each, 192 x 4 = 768 of them)
+    assert capi.m3_ssm_prefill_plan(_shape(batch=1, nheads=64, seqlen=65536, dstate=128, rank=1))[3:] == (4, 16384, 1)
 
 
 def test_in_chunk_offsets_stay_32_bit():

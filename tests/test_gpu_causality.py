@@ -42,7 +42,7 @@ def _chunk_out(t, chunk):
     from mamba_selective_ssm_ssd_amd import capi, mixer
     x = t["x"]
     b, T, H, R, P = x.shape
-    rc, qpre, qout, S, L = capi.m3_ssm_prefill_plan(mixer.make_shape(b, T, H, P, t["B"].shape[-1], R, x.dtype,
+    rc, qpre, qout, S, L, kp = capi.m3_ssm_prefill_plan(mixer.make_shape(b, T, H, P, t["B"].shape[-1], R, x.dtype,
                                                                       chunk=chunk))
     assert rc == 0
     return qout

@@ -149,6 +149,29 @@ def test_segmented_long_sequence():
     _parity(d, "bf16")
 
 
+@pytest.mark.parametrize("H,T,R,io,kpre", [(128, 1000, 1, "bf16", 2), (64, 2048, 2, "f32", 4),
+                                           (64, 2048, 4, "bf16", 4)])
+def test_prepass_pieces(H, T, R, io, kpre):
+    """One sequence per head on few sequences: segments with a pre-pass cut
+    into kpre pieces per segment (aggregates folded piece by piece), from a
+    random carried state."""
+    from mamba_selective_ssm_ssd_amd import capi, mixer
+    b, P, N = 1, 16, 32
+    tio = torch.float32 if io == "f32" else torch.bfloat16
+    plan = capi.m3_ssm_prefill_plan(mixer.make_shape(b, T, H, P, N, R, tio))
+    assert plan[0] == 0 and plan[3] > 1 and plan[5] == kpre, plan
+    d = _inputs(b, T, H, P, N, R, io, seed=31)
+    d["A"] *= 0.02                                     # earlier pieces stay visible
+    rng = np.random.default_rng(310)
+    init_np = dict(h=rng.standard_normal((b, H, N, P)).astype(np.float32),
+                   phi=rng.uniform(-np.pi, np.pi, size=(b, H, N // 2)).astype(np.float32),
+                   prev_B=rng.standard_normal((b, H, R, N)).astype(np.float32),
+                   prev_x=synth.round_io(rng.standard_normal((b, H, R, P)), io))
+    init = mixer.State(*(torch.from_numpy(init_np[k]).cuda() for k in ("h", "phi", "prev_B")),
+                       torch.from_numpy(init_np["prev_x"]).to("cuda", tio))
+    _parity(d, io, init=init, init_np={k: v.astype(np.float64) for k, v in init_np.items()})
+
+
 # --------------------------------------------------------------------------
 # S1: slow decay -- the carried inter-chunk state dominates the output.
 # --------------------------------------------------------------------------
