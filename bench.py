@@ -757,7 +757,7 @@ def main():
         result["decode"] = {"workload": c["name"], "us_per_step": round(us, 2), "steps": args.decode_steps,
                             "roofline": roofline_hbm("k_decode_step", db, us / 1000,
                                                      load_traffic("decode_step", c["name"]),
-                                                     ceil.get("stream_rmw_gbs"))}
+                                                     ceil.get("stream_rmw_gbs_268MB"))}
         log(f"[mimo decode] {us:.1f} us/step  {result['decode']['roofline']['frac']:.3f} of HBM")
         if chk is not None:
             oracle_jobs.append(("parity_decode", chk))
