@@ -11,8 +11,11 @@
  * prefill, as in the chunked algorithm of the "20.2 Mamba and S6" page,
  * section 2, whose prefill kernels are trained through).
  *
- * The gradients of the final state's outputs are not inputs (L depends on y
- * only).  Supported: the shapes m3_ssm_prefill supports, ngroups = 0 or H,
+ * m3_ssm_prefill_backward_ex also takes the gradient of L with respect to the
+ * final carried state the prefill returns (h~, Phi, prev_B, prev_x), so that
+ * split calls chain in training: the gradients of the carried state the next
+ * call started from are the incoming final-state gradients of this one.
+ * Supported: the shapes m3_ssm_prefill supports, ngroups = 0 or H,
  * state_dtype F32; otherwise M3_ERR_UNSUPPORTED.  Arithmetic is fp32 with
  * fp64 angles; every gradient is written in fp32.
  */
@@ -42,6 +45,18 @@ typedef struct {
     float *prev_x; /* [b][H][R][P]  of its previous x                         */
 } m3_grads_t;
 
+/* Incoming gradients of L with respect to the final carried state of the
+ * prefill (m3_ssm.h's m3_state_t, rotated frame), fp32, 16-byte aligned,
+ * caller-owned; a NULL entry is a zero gradient.  The gradients of the
+ * initial state that m3_grads_t returns for the next call have exactly these
+ * shapes and meaning. */
+typedef struct {
+    const float *h;      /* [b][H][N][P]  of the final h~                          */
+    const float *phi;    /* [b][H][K]     of the final Phi (wrapped; derivative 1) */
+    const float *prev_B; /* [b][H][R][N]  of the final prev_B, the last token's B~  */
+    const float *prev_x; /* [b][H][R][P]  of the final prev_x, the last token's x   */
+} m3_final_grads_t;
+
 /* Bytes of device workspace m3_ssm_prefill_backward needs (0: unsupported).
  * The pass stores the state entering every chunk of 32 / R tokens in fp32
  * and the angle there in fp64, so the size grows with the sequence:
@@ -64,6 +79,21 @@ m3_status_t m3_ssm_prefill_backward(const m3_shape_t *shape, const void *x, cons
                                     const void *B, const void *C, const m3_state_t *init,
                                     const void *gy, const m3_grads_t *grads, void *workspace,
                                     size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Gradients of L = sum(gy * y) + <gfinal.h, h~_T> + <gfinal.phi, Phi_T>
+ *   + <gfinal.prev_B, B~_{T-1}> + <gfinal.prev_x, x_{T-1}> for the prefill
+ * with final state (h~_T, Phi_T, B~_{T-1}, x_{T-1}).  gfinal NULL (or every
+ * entry NULL) is m3_ssm_prefill_backward.  Other arguments, outputs and
+ * errors as m3_ssm_prefill_backward; M3_ERR_INVALID_ARGUMENT for a
+ * misaligned gfinal entry.
+ */
+m3_status_t m3_ssm_prefill_backward_ex(const m3_shape_t *shape, const void *x, const void *dt,
+                                       const float *A, const void *lam, const void *theta,
+                                       const void *B, const void *C, const m3_state_t *init,
+                                       const void *gy, const m3_final_grads_t *gfinal,
+                                       const m3_grads_t *grads, void *workspace,
+                                       size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

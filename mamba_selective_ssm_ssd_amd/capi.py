@@ -25,7 +25,8 @@ M3_ERR_HIP = 4
 EXPORTED = ("m3_ssm_prefill_workspace_bytes", "m3_ssm_prefill", "m3_ssm_decode_step",
             "m3_status_string", "m3_ssm_prefill_stage", "m3_ssm_prefill_block",
             "m3_ssm_decode_step_block", "m3_ssm_prefill_backward_workspace_bytes",
-            "m3_ssm_prefill_backward", "m3_ssm_prefill_noalloc", "m3_ssm_prefill_plan",
+            "m3_ssm_prefill_backward", "m3_ssm_prefill_backward_ex", "m3_ssm_prefill_noalloc",
+            "m3_ssm_prefill_plan",
             "m3_ceiling_mfma", "m3_ceiling_stream")
 
 # Size of the static workspace of m3_ssm_prefill_noalloc (include/m3_ssm_noalloc.h).
@@ -62,6 +63,11 @@ class m3_grads_t(ctypes.Structure):
     """Gradient outputs of the backward pass (include/m3_ssm_backward.h)."""
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("x", "dt", "A", "lam", "theta", "B", "C", "h", "phi", "prev_B", "prev_x")]
+
+
+class m3_final_grads_t(ctypes.Structure):
+    """Incoming gradients of the final carried state (include/m3_ssm_backward.h)."""
+    _fields_ = [(n, ctypes.c_void_p) for n in ("h", "phi", "prev_B", "prev_x")]
 
 
 class M3Error(RuntimeError):
@@ -106,6 +112,10 @@ def load():
     lib.m3_ssm_prefill_backward.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, stp, vp, gp, vp,
                                             ctypes.c_size_t, vp]
     lib.m3_ssm_prefill_backward.restype = ctypes.c_int
+    lib.m3_ssm_prefill_backward_ex.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, stp, vp,
+                                               ctypes.POINTER(m3_final_grads_t), gp, vp,
+                                               ctypes.c_size_t, vp]
+    lib.m3_ssm_prefill_backward_ex.restype = ctypes.c_int
     lib.m3_ssm_prefill_noalloc.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, stp, stp, vp, vp]
     lib.m3_ssm_prefill_noalloc.restype = ctypes.c_int
     i32p, i64p = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
@@ -211,5 +221,16 @@ def m3_ssm_prefill_backward(shape, x, dt, A, lam, theta, B, C, init, gy, grads, 
     return int(load().m3_ssm_prefill_backward(
         ctypes.byref(shape), x, dt, A, lam, theta, B, C,
         ctypes.byref(init) if init is not None else None, gy,
+        ctypes.byref(grads) if grads is not None else None,
+        workspace, int(workspace_bytes), stream))
+
+
+def m3_ssm_prefill_backward_ex(shape, x, dt, A, lam, theta, B, C, init, gy, gfinal, grads, workspace,
+                               workspace_bytes, stream) -> int:
+    """m3_ssm_prefill_backward with gfinal (an m3_final_grads_t or None)."""
+    return int(load().m3_ssm_prefill_backward_ex(
+        ctypes.byref(shape), x, dt, A, lam, theta, B, C,
+        ctypes.byref(init) if init is not None else None, gy,
+        ctypes.byref(gfinal) if gfinal is not None else None,
         ctypes.byref(grads) if grads is not None else None,
         workspace, int(workspace_bytes), stream))

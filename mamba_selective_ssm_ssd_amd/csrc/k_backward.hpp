@@ -470,9 +470,34 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
     for (int i = 0; i < GSN; ++i) GS[i] = zero4();
 #define G2(nb) GS[nb]
 #define G1(q, pb) GS[(q) * PB + (pb)]
+    // after the last chunk G is the incoming gradient of the final h~ (the
+    // last token has no next token, so H after the last chunk is h~_{T-1})
+    if (p.ghT) {
+        const float *gh = p.ghT + bh * int64_t(N) * P;
+        if (w < 4 && w < PB) {
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) G2(nb)[e] = gh[(nb * 16 + 4 * lg + e) * P + w * 16 + li];
+        } else if (w >= 4) {
+#pragma unroll
+            for (int q = 0; q < NBW; ++q) {
+                const int nb = w - 4 + 4 * q;
+                if (nb >= NB) continue;
+#pragma unroll
+                for (int pb = 0; pb < PB; ++pb)
+                    G1(q, pb) = lds4(gh + (nb * 16 + li) * P + pb * 16 + 4 * lg);
+            }
+        }
+    }
     double carry[KP];    // lanes (pair, segment): sum of dPhi over the later chunks
 #pragma unroll
-    for (int kp = 0; kp < KP; ++kp) carry[kp] = 0.0;
+    for (int kp = 0; kp < KP; ++kp) {
+        // the final Phi_T = Phi_{-1} + sum theta: its incoming gradient adds
+        // to every dtheta_t and to dPhi_{-1}
+        const int k = KS * kp + 8 * w + (lane & 7);
+        carry[kp] = p.gphiT && k < K ? double(p.gphiT[bh * K + k]) : 0.0;
+    }
     float gA = 0.f;      // wave 0: this lane's share of dA
     bool pend = false;   // wave 0, lane 0: the later chunk's first token awaits its d(delta)
     float pd_g = 0.f, pd_l = 0.f, pd_dt = 0.f, pd_lam = 0.f;
@@ -675,7 +700,11 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int v = vb * 16 + 4 * lg + e, i = v / R;
-                    if (v < VQ && i < Tc) gxb[(i * HR + v - i * R) * P + pb * 16 + li] = acc[vb][e];
+                    // the last token's x is the final state's x_prev
+                    float gx = acc[vb][e];
+                    if (p.gxpT && t0 + i == T - 1 && v < VQ)
+                        gx += p.gxpT[(bh * R + (v - i * R)) * P + pb * 16 + li];
+                    if (v < VQ && i < Tc) gxb[(i * HR + v - i * R) * P + pb * 16 + li] = gx;
                 }
             // G <- e^{ec_end} G + C~^T diag(E) gy  (this orientation)
 #pragma unroll
@@ -699,6 +728,17 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
             floatx4 (&dc)[VB] = dcq[q], (&db)[VB] = dbq[q];
             mm_lds<V, pV, pV, VB, ZHI, 1>(dc, MN, BT + nb * 16 * pV, li, lg);
             mm_lds<V, pV, pV, VB, ZLO, 0>(db, MT, CT + nb * 16 * pV, li, lg);
+            // the last token's B~ is the final state's prev_B
+            if (p.gBpT && t0 + Tc == T) {
+#pragma unroll
+                for (int vb = 0; vb < VB; ++vb)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int v = vb * 16 + 4 * lg + e, i = v / R;
+                        if (v < VQ && i == Tc - 1)
+                            db[vb][e] += p.gBpT[(bh * R + (v - i * R)) * N + nb * 16 + li];
+                    }
+            }
 #pragma unroll
             for (int vb = 0; vb < VB; ++vb)
 #pragma unroll

@@ -80,6 +80,9 @@ struct BwdParams {
     int32_t has_init;
     const float *h0, *phi0, *prevB0; // rotated frame, fp32
     const void *prevx0;             // I/O dtype
+    // incoming gradients of the final carried state (fp32, rotated frame;
+    // null: zero): h~_T [N][P], Phi_T [K], B~_{T-1} [R][N], x_{T-1} [R][P] per (b, h)
+    const float *ghT, *gphiT, *gBpT, *gxpT;
     // outputs (fp32); the carried-state ones may be null
     float *gx, *gdt, *glam, *gtheta, *gB, *gC, *gA;
     float *gh0, *gphi0, *gprevB0, *gprevx0;

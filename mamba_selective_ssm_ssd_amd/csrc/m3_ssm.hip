@@ -459,6 +459,16 @@ m3_status_t m3_ssm_prefill_backward(const m3_shape_t *shape, const void *x, cons
                                     const void *B, const void *C, const m3_state_t *init,
                                     const void *gy, const m3_grads_t *grads, void *workspace,
                                     size_t workspace_bytes, hipStream_t stream) {
+    return m3_ssm_prefill_backward_ex(shape, x, dt, A, lam, theta, B, C, init, gy, nullptr, grads,
+                                      workspace, workspace_bytes, stream);
+}
+
+m3_status_t m3_ssm_prefill_backward_ex(const m3_shape_t *shape, const void *x, const void *dt,
+                                       const float *A, const void *lam, const void *theta,
+                                       const void *B, const void *C, const m3_state_t *init,
+                                       const void *gy, const m3_final_grads_t *gfinal,
+                                       const m3_grads_t *grads, void *workspace,
+                                       size_t workspace_bytes, hipStream_t stream) {
     const m3_status_t sc = check_backward_shape(shape);
     if (sc != M3_OK) return sc;
     const void *ptrs[] = {x, dt, A, lam, theta, B, C, gy};
@@ -471,6 +481,11 @@ m3_status_t m3_ssm_prefill_backward(const m3_shape_t *shape, const void *x, cons
     const void *opt[] = {grads->h, grads->phi, grads->prev_B, grads->prev_x};
     for (const void *q : opt)
         if (q && !aligned16(q)) return M3_ERR_INVALID_ARGUMENT;
+    if (gfinal) {
+        const void *gf[] = {gfinal->h, gfinal->phi, gfinal->prev_B, gfinal->prev_x};
+        for (const void *q : gf)
+            if (q && !aligned16(q)) return M3_ERR_INVALID_ARGUMENT;
+    }
     if (init && !state_ok(init)) return M3_ERR_INVALID_ARGUMENT;
     const BwdLayout w = bwd_layout(shape);
     if (!workspace || !aligned16(workspace) || workspace_bytes < w.total) return M3_ERR_WORKSPACE;
@@ -492,6 +507,9 @@ m3_status_t m3_ssm_prefill_backward(const m3_shape_t *shape, const void *x, cons
     }
     p.gx = grads->x; p.gdt = grads->dt; p.glam = grads->lam; p.gtheta = grads->theta;
     p.gB = grads->B; p.gC = grads->C; p.gA = grads->A;
+    if (gfinal) {
+        p.ghT = gfinal->h; p.gphiT = gfinal->phi; p.gBpT = gfinal->prev_B; p.gxpT = gfinal->prev_x;
+    }
     unsigned char *ws = static_cast<unsigned char *>(workspace);
     p.ck_h = reinterpret_cast<float *>(ws + w.ck_h);
     p.ck_phi = reinterpret_cast<double *>(ws + w.ck_phi);

@@ -215,8 +215,14 @@ def decode_step(x, dt, A, lam, theta, B, C, state: State, y=None, block: Block |
     return y
 
 
-def backward(x, dt, A, lam, theta, B, C, gy, state: State | None = None, workspace=None):
+def backward(x, dt, A, lam, theta, B, C, gy, state: State | None = None, workspace=None,
+             gfinal: dict | None = None):
     """Gradients of sum(gy * y) for y = prefill(x, ..., state=state).
+
+    ``gfinal``: incoming gradients of the final carried state, a dict with
+    any of h, phi, prev_B, prev_x (fp32 device tensors shaped like the
+    State's fields); they add <gfinal, final state> to the loss, so that the
+    gradients a later call returns for its initial state chain into this one.
 
     Returns a dict of fp32 tensors: x, dt, A, lam, theta, B, C and, when a
     carried state is given, h, phi, prev_B, prev_x (its gradients).
@@ -241,11 +247,24 @@ def backward(x, dt, A, lam, theta, B, C, gy, state: State | None = None, workspa
                  prev_B=torch.empty(state.prev_B.shape, **f), prev_x=torch.empty(state.prev_x.shape, **f))
     gs = capi.m3_grads_t(*(g[k].data_ptr() if k in g else None for k in
                            ("x", "dt", "A", "lam", "theta", "B", "C", "h", "phi", "prev_B", "prev_x")))
-    rc = capi.m3_ssm_prefill_backward(
+    gf = None
+    if gfinal:
+        want = dict(h=(b, H, N, P), phi=(b, H, N // 2), prev_B=(b, H, R, N), prev_x=(b, H, R, P))
+        ptrs = {}
+        for k, t in gfinal.items():
+            if k not in want:
+                raise ValueError(f"gfinal: unknown entry {k}")
+            if t is None:
+                continue
+            if tuple(t.shape) != want[k]:
+                raise ValueError(f"gfinal[{k}] must be {want[k]}, got {tuple(t.shape)}")
+            ptrs[k] = _ptr(t, "gfinal." + k, torch.float32)
+        gf = capi.m3_final_grads_t(*(ptrs.get(k) for k in ("h", "phi", "prev_B", "prev_x")))
+    rc = capi.m3_ssm_prefill_backward_ex(
         shape, _ptr(x, "x", io), _ptr(dt, "dt", io), _ptr(A, "A", torch.float32),
         _ptr(lam, "lam", io), _ptr(theta, "theta", io), _ptr(B, "B", io), _ptr(C, "C", io),
-        state.c() if state is not None else None, _ptr(gy, "gy", io), gs,
+        state.c() if state is not None else None, _ptr(gy, "gy", io), gf, gs,
         workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream())
     if rc != capi.M3_OK:
-        raise capi.M3Error(rc, "m3_ssm_prefill_backward")
+        raise capi.M3Error(rc, "m3_ssm_prefill_backward_ex")
     return g

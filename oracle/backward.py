@@ -19,8 +19,11 @@ at a time, and it is a different formulation from the complex true-frame
 recurrence of ``m3_oracle.c``; the pins check that the two agree.
 
 ``grad`` differentiates it with torch autograd for the loss
-L = sum(gy * y): the gradients of every input and of the carried state.  The
-pins check them against central finite differences of ``m3_oracle.c``.
+L = sum(gy * y), plus, when given, the inner products of incoming gradients
+with the final carried state (h~_T, Phi_T, B~_{T-1}, x_{T-1}): the gradients
+of every input and of the initial carried state.  The pins check them
+against central finite differences of ``m3_oracle.c``, and the final-state
+terms against the chain rule over split calls.
 """
 from __future__ import annotations
 
@@ -40,12 +43,13 @@ def _rot_neg(V, phi):
     return out.flatten(-2)
 
 
-def forward_rot(x, dt, A, lam, theta, B, C, h0=None, phi0=None, prevB0=None, prevx0=None):
+def forward_rot(x, dt, A, lam, theta, B, C, h0=None, phi0=None, prevB0=None, prevx0=None, final=False):
     """The mixer in the rotated frame (fp64 torch tensors).
 
     Shapes: x [b,T,H,R,P], dt/lam [b,T,H], A [H], theta [b,T,H,K], B/C
     [b,T,H,R,N]; h0 [b,H,N,P], phi0 [b,H,K], prevB0 [b,H,R,N] (rotated),
-    prevx0 [b,H,R,P].  Returns y [b,T,H,R,P] and the final h~ [b,H,N,P].
+    prevx0 [b,H,R,P].  Returns y [b,T,H,R,P] and the final h~ [b,H,N,P];
+    with ``final=True`` also Phi_T (unwrapped), B~_{T-1} and x_{T-1}.
     """
     b, T, H, R, P = x.shape
     N = B.shape[-1]
@@ -68,16 +72,20 @@ def forward_rot(x, dt, A, lam, theta, B, C, h0=None, phi0=None, prevB0=None, pre
              + gamma[..., None, None] * torch.einsum("bhrn,bhrp->bhnp", Bt, x[:, t]))
         ys.append(torch.einsum("bhrn,bhnp->bhrp", Ct, h))
         Bprev, xprev = Bt, x[:, t]
+    if final:
+        return torch.stack(ys, dim=1), h, Phi, Bprev, xprev
     return torch.stack(ys, dim=1), h
 
 
-def grad(inputs: dict, gy, init: dict | None = None):
-    """Gradients of L = sum(gy * y) (fp64).
+def grad(inputs: dict, gy, init: dict | None = None, gfinal: dict | None = None):
+    """Gradients of L = sum(gy * y) + <gfinal, final state> (fp64).
 
     ``inputs``: x, dt, A, lam, theta, B, C as numpy arrays; ``init``: any of
-    h0, phi0, prevB0, prevx0 (rotated frame).  Returns (y, dict of gradients
-    keyed like the inputs, with g_h0, g_phi0, g_prevB0, g_prevx0 for the
-    carried state; a missing carried state gets the gradient at zero).
+    h0, phi0, prevB0, prevx0 (rotated frame); ``gfinal``: any of h, phi,
+    prev_B, prev_x, the incoming gradients of the final h~_T, Phi_T, B~_{T-1}
+    and x_{T-1}.  Returns (y, dict of gradients keyed like the inputs, with
+    g_h0, g_phi0, g_prevB0, g_prevx0 for the carried state; a missing carried
+    state gets the gradient at zero).
     """
     t = {k: torch.tensor(np.asarray(inputs[k], dtype=np.float64), requires_grad=True) for k in NAMES}
     b, T, H, R, P = t["x"].shape
@@ -86,8 +94,12 @@ def grad(inputs: dict, gy, init: dict | None = None):
     init = init or {}
     s = {k: torch.tensor(np.asarray(init[k], dtype=np.float64) if k in init else np.zeros(shapes[k]),
                          requires_grad=True) for k in INIT}
-    y, _ = forward_rot(*(t[k] for k in NAMES), **s)
-    (y * torch.tensor(np.asarray(gy, dtype=np.float64))).sum().backward()
+    y, hT, phiT, bT, xT = forward_rot(*(t[k] for k in NAMES), **s, final=True)
+    loss = (y * torch.tensor(np.asarray(gy, dtype=np.float64))).sum()
+    for k, v in zip(("h", "phi", "prev_B", "prev_x"), (hT, phiT, bT, xT)):
+        if gfinal and gfinal.get(k) is not None:
+            loss = loss + (v * torch.tensor(np.asarray(gfinal[k], dtype=np.float64))).sum()
+    loss.backward()
     out = {k: t[k].grad.numpy() for k in NAMES}
     out.update({"g_" + k: s[k].grad.numpy() for k in INIT})
     return y.detach().numpy(), out

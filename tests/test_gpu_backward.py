@@ -25,7 +25,7 @@ AXES = dict(x=(0, 2), dt=(0, 2), lam=(0, 2), theta=(0, 2), B=(0, 2), C=(0, 2),
             h=(0, 1), phi=(0, 1), prev_B=(0, 1), prev_x=(0, 1))
 
 
-def _run(b, T, H, P, N, R, io, seed, with_init):
+def _run(b, T, H, P, N, R, io, seed, with_init, with_gfinal=False):
     from mamba_selective_ssm_ssd_amd import mixer
     d = synth.prefill_inputs(b, T, H, P, N, R, io=io, seed=seed, cfg=90)
     d["A"] *= 0.2                                  # slower decay: long-range terms matter
@@ -39,16 +39,25 @@ def _run(b, T, H, P, N, R, io, seed, with_init):
                        prevx0=synth.round_io(rng.standard_normal((b, H, R, P)), io))
         st = mixer.State(*(torch.from_numpy(init_np[k]).cuda() for k in ("h0", "phi0", "prevB0")),
                          torch.from_numpy(init_np["prevx0"]).to("cuda", torch_io(io)))
+    gf_np, gf = None, None
+    if with_gfinal:
+        gf_np = dict(h=rng.standard_normal((b, H, N, P)), phi=rng.standard_normal((b, H, N // 2)),
+                     prev_B=rng.standard_normal((b, H, R, N)), prev_x=rng.standard_normal((b, H, R, P)))
+        gf_np = {k: v.astype(np.float32) for k, v in gf_np.items()}
+        gf = {k: torch.from_numpy(v).cuda() for k, v in gf_np.items()}
     t = to_dev(d, io)
     gyd = torch.from_numpy(gy).to("cuda", torch_io(io))
-    g = mixer.backward(*(t[k] for k in ("x", "dt", "A", "lam", "theta", "B", "C")), gyd, state=st)
+    g = mixer.backward(*(t[k] for k in ("x", "dt", "A", "lam", "theta", "B", "C")), gyd, state=st,
+                       gfinal=gf)
     torch.cuda.synchronize()
-    _, r = ob.grad(d, gy, {k: v.astype(np.float64) for k, v in init_np.items()} if init_np else None)
+    _, r = ob.grad(d, gy, {k: v.astype(np.float64) for k, v in init_np.items()} if init_np else None,
+                   gf_np)
     errs = {}
     for k in ("x", "dt", "lam", "theta", "B", "C"):
         errs[k] = slice_err(g[k].double().cpu().numpy(), r[k], AXES[k])
     gA, rA = g["A"].double().cpu().numpy(), r["A"]
-    errs["A"] = float(np.max(np.abs(gA - rA)) / np.max(np.abs(rA)))
+    den = np.max(np.abs(rA))          # 0 when no decay reaches a loss term (T = 1, fresh state)
+    errs["A"] = float(np.max(np.abs(gA - rA)) / den) if den > 0 else float(np.max(np.abs(gA)))
     if with_init:
         for k, rk in (("h", "g_h0"), ("phi", "g_phi0"), ("prev_B", "g_prevB0"), ("prev_x", "g_prevx0")):
             errs[k] = slice_err(g[k].double().cpu().numpy(), r[rk], AXES[k])
@@ -96,3 +105,75 @@ def test_backward_random_case(seed):
           + " ".join(f"{k} {v:.1e}" for k, v in errs.items()))
     for k, v in errs.items():
         assert v <= BAR, f"case {seed}: gradient of {k}: error {v:.3e}"
+
+
+@pytest.mark.parametrize("N,P,R,io,T", [
+    (16, 16, 1, "f32", 150), (64, 32, 3, "f32", 64), (128, 32, 2, "f32", 1),
+    (64, 64, 4, "bf16", 200), (32, 64, 2, "bf16", 63),
+])
+@pytest.mark.parametrize("with_init", [False, True])
+def test_backward_final_state_gradient(N, P, R, io, T, with_init):
+    """An incoming gradient of every part of the final state (h, angle,
+    previous B and x) adds <gfinal, final state> to the loss."""
+    errs = _run(2, T, 2, P, N, R, io, seed=7 * N + P + R + T, with_init=with_init, with_gfinal=True)
+    print(f"backward+gfinal N{N} P{P} R{R} {io} T{T} init={with_init}: "
+          + " ".join(f"{k} {v:.1e}" for k, v in errs.items()))
+    for k, v in errs.items():
+        assert v <= BAR, f"gradient of {k}: error {v:.3e} > {BAR}"
+
+
+@pytest.mark.parametrize("N,P,R,io,T1,T2,handoff", [
+    (32, 32, 2, "f32", 100, 90, "prefill"), (64, 64, 4, "f32", 64, 137, "prefill"),
+    (16, 16, 1, "f32", 1, 70, "prefill"), (64, 64, 4, "bf16", 7, 137, "decode"),
+    (128, 32, 3, "bf16", 5, 64, "decode"),
+])
+def test_backward_chains_over_split_calls(N, P, R, io, T1, T2, handoff):
+    """A sequence run as two calls (the second starts from the first's final
+    state): the second call's backward gives the gradient of its initial state,
+    which flows into the first call's backward as the final-state gradient.
+    The gradients of both halves and of the first call's initial state match
+    the oracle's gradients of the whole sequence.
+
+    The state handed over is part of the second call's input, so it must be
+    as exact as the backward's bar: it comes from the prefill at fp32 I/O, and
+    from decode steps (fp32 arithmetic) at bf16 I/O -- the bf16 prefill's
+    products run on bf16 MFMA and its state carries the forward's bf16 error."""
+    from mamba_selective_ssm_ssd_amd import mixer
+    b, H, T = 2, 2, T1 + T2
+    d = synth.prefill_inputs(b, T, H, P, N, R, io=io, seed=T1 * T2, cfg=91)
+    d["A"] *= 0.2
+    rng = np.random.default_rng(T1 + 31 * T2)
+    gy = synth.round_io(rng.standard_normal((b, T, H, R, P)), io)
+    init_np = dict(h0=rng.standard_normal((b, H, N, P)).astype(np.float32) * 0.5,
+                   phi0=rng.uniform(-np.pi, np.pi, size=(b, H, N // 2)).astype(np.float32),
+                   prevB0=rng.standard_normal((b, H, R, N)).astype(np.float32),
+                   prevx0=synth.round_io(rng.standard_normal((b, H, R, P)), io))
+    st0 = mixer.State(*(torch.from_numpy(init_np[k]).cuda() for k in ("h0", "phi0", "prevB0")),
+                      torch.from_numpy(init_np["prevx0"]).to("cuda", torch_io(io)))
+    t = to_dev(d, io)
+    names = ("x", "dt", "A", "lam", "theta", "B", "C")
+    half = [{k: (t[k] if k == "A" else t[k][:, lo:hi].contiguous()) for k in names}
+            for lo, hi in ((0, T1), (T1, T))]
+    gyd = torch.from_numpy(gy).to("cuda", torch_io(io))
+    if handoff == "prefill":
+        _, st1 = mixer.prefill(*(half[0][k] for k in names), state=st0.clone())   # final in place
+    else:
+        st1 = st0.clone()
+        for i in range(T1):
+            mixer.decode_step(*((t[k] if k == "A" else t[k][:, i].contiguous()) for k in names), st1)
+    g2 = mixer.backward(*(half[1][k] for k in names), gyd[:, T1:].contiguous(), state=st1)
+    g1 = mixer.backward(*(half[0][k] for k in names), gyd[:, :T1].contiguous(), state=st0,
+                        gfinal={k: g2[k] for k in ("h", "phi", "prev_B", "prev_x")})
+    torch.cuda.synchronize()
+    _, r = ob.grad(d, gy, {k: v.astype(np.float64) for k, v in init_np.items()})
+    errs = {}
+    for k in ("x", "dt", "lam", "theta", "B", "C"):
+        gk = torch.cat([g1[k], g2[k]], dim=1).double().cpu().numpy()
+        errs[k] = slice_err(gk, r[k], AXES[k])
+    gA, rA = (g1["A"] + g2["A"]).double().cpu().numpy(), r["A"]
+    errs["A"] = float(np.max(np.abs(gA - rA)) / np.max(np.abs(rA)))
+    for k, rk in (("h", "g_h0"), ("phi", "g_phi0"), ("prev_B", "g_prevB0"), ("prev_x", "g_prevx0")):
+        errs[k] = slice_err(g1[k].double().cpu().numpy(), r[rk], AXES[k])
+    print(f"split N{N} P{P} R{R} {io} {T1}+{T2}: " + " ".join(f"{k} {v:.1e}" for k, v in errs.items()))
+    for k, v in errs.items():
+        assert v <= BAR, f"gradient of {k}: error {v:.3e} > {BAR}"

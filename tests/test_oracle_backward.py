@@ -96,3 +96,58 @@ def test_fresh_sequence_has_no_previous_token_gradient_path():
     zero = {k: np.zeros_like(v) for k, v in init.items()}
     _, g = ob.grad(d, gy, zero)
     assert np.max(np.abs(g["g_prevx0"])) == 0.0
+
+
+@pytest.mark.parametrize("R,T1", [(1, 9), (2, 14), (3, 1)])
+def test_final_state_gradients_chain_over_split_calls(R, T1):
+    """The incoming final-state gradients (h~_T, Phi_T, B~_{T-1}, x_{T-1}) by
+    the chain rule over a split: the gradients of a sequence split into two
+    calls -- the second call's gradients of its initial carried state fed to
+    the first call as gradients of its final state -- equal those of the whole
+    sequence in one call (for every input; dA summed over the calls)."""
+    d, init, gy = _case(T=23, R=R, seed=10 + R)
+    _, g_full = ob.grad(d, gy, init)
+    first = {k: (v[:, :T1] if v.ndim >= 3 else v) for k, v in d.items()}
+    second = {k: (v[:, T1:] if v.ndim >= 3 else v) for k, v in d.items()}
+    # the first call's final state, in the rotated frame, starts the second
+    t = {k: torch.tensor(v) for k, v in first.items()}
+    ti = {k: torch.tensor(v) for k, v in init.items()}
+    _, hT, phiT, bT, xT = ob.forward_rot(*(t[k] for k in ob.NAMES), **ti, final=True)
+    init2 = dict(h0=hT.numpy(), phi0=phiT.numpy(), prevB0=bT.numpy(), prevx0=xT.numpy())
+    _, g2 = ob.grad(second, gy[:, T1:], init2)
+    gfinal = dict(h=g2["g_h0"], phi=g2["g_phi0"], prev_B=g2["g_prevB0"], prev_x=g2["g_prevx0"])
+    _, g1 = ob.grad(first, gy[:, :T1], init, gfinal)
+    for k in ("x", "dt", "lam", "theta", "B", "C"):
+        got = np.concatenate([g1[k], g2[k]], axis=1)
+        assert np.max(np.abs(got - g_full[k])) <= 1e-10 * max(1.0, np.max(np.abs(g_full[k]))), k
+    assert np.max(np.abs(g1["A"] + g2["A"] - g_full["A"])) <= 1e-10 * max(1.0, np.max(np.abs(g_full["A"])))
+    for k in ("g_h0", "g_phi0", "g_prevB0", "g_prevx0"):
+        assert np.max(np.abs(g1[k] - g_full[k])) <= 1e-10 * max(1.0, np.max(np.abs(g_full[k]))), k
+
+
+def test_final_state_gradient_of_h_matches_finite_differences():
+    """<g, h~_T> through the complex true-frame oracle (h~_T = R(-Phi_T) h_T):
+    its gradients with respect to x, dt and theta by central differences."""
+    d, init, _ = _case(b=1, T=11, H=1, P=3, N=4, R=2, seed=21)
+    rng = np.random.default_rng(2100)
+    gh = rng.standard_normal((1, 1, 4, 3))
+    gy0 = np.zeros((1, 11, 1, 2, 3))
+
+    def loss(dd):
+        h0 = oracle.state_to_true(init["h0"], init["phi0"])
+        pB = oracle.prevB_to_true(init["prevB0"], init["phi0"])
+        _, hT, _ = oracle.run(dd["x"], dd["dt"], dd["A"], dd["lam"], dd["theta"], dd["B"], dd["C"],
+                              h0=h0, prevB0=pB, prevx0=init["prevx0"])
+        phiT = oracle.cumulative_angle(dd["theta"], init["phi0"])
+        h_rot = oracle.rotate_pairs(hT, -np.asarray(phiT)[..., None], axis=2)
+        return float(np.sum(gh * h_rot))
+
+    _, g = ob.grad(d, gy0, init, dict(h=gh))
+    eps = 1e-6
+    for k, idx in (("x", (0, 4, 0, 1, 2)), ("dt", (0, 7, 0)), ("theta", (0, 3, 0, 1)), ("B", (0, 10, 0, 0, 3))):
+        dp = {kk: vv.copy() for kk, vv in d.items()}
+        dm = {kk: vv.copy() for kk, vv in d.items()}
+        dp[k][idx] += eps
+        dm[k][idx] -= eps
+        fd = (loss(dp) - loss(dm)) / (2 * eps)
+        assert abs(fd - g[k][idx]) <= 1e-6 * max(1.0, abs(fd)), (k, fd, g[k][idx])
