@@ -1021,9 +1021,21 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
                         cf[i][ks] = (N % 32 == 0 || n0 < N) ? M::template lds8<C::BS_PS>(cl + (t0v + l16) * NBP + n0) : M::zero();
                     }
                 }
-                floatx4 acc[PT];
+                // acci: the inter-chunk term C~ H; acc: the intra-chunk term M x.
+                // With rank R > 1 and 64 virtual rows both source pairs are
+                // always taken (the mask is zero above the diagonal) and the
+                // whole products phase is one straight-line block, so the
+                // compiler interleaves the two independent chains (ILP).
+                // Otherwise the inter term is scaled in place and the intra
+                // term accumulates onto it.
+                constexpr bool ILP = R > 1 && V <= 64;
+                floatx4 acc[PT], acci[ILP ? PT : 1];
+                auto inter = [&](int pt) -> floatx4 & {
+                    if constexpr (ILP) return acci[pt];
+                    else return acc[pt];
+                };
 #pragma unroll
-                for (int pt = 0; pt < PT; ++pt) acc[pt] = floatx4{0.f, 0.f, 0.f, 0.f};
+                for (int pt = 0; pt < PT; ++pt) acc[pt] = inter(pt) = floatx4{0.f, 0.f, 0.f, 0.f};
                 {
                     // C~ H, the state fragments read DEPTH products ahead
                     constexpr int NI = PT * NKS, DEPTH = NI < 4 ? NI : 4;
@@ -1033,18 +1045,19 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
                         const int pt = it % PT, n0 = 32 * (it / PT) + 8 * g;
                         return (N % 32 == 0 || n0 < N) ? M::template lds8<C::HT_PS>(ht + (16 * pt + l16) * NBP + n0) : M::zero();
                     };
-                    __builtin_amdgcn_sched_barrier(0);
+                    if constexpr (!ILP) __builtin_amdgcn_sched_barrier(0);
                     frag hq[DEPTH];
 #pragma unroll
                     for (int d = 0; d < DEPTH; ++d) hq[d] = hfrag(d);
 #pragma unroll
                     for (int it = 0; it < NI; ++it) {
-                        acc[it % PT] = M::mma(acc[it % PT], hq[it % DEPTH], cf[i][it / PT]);
+                        inter(it % PT) = M::mma(inter(it % PT), hq[it % DEPTH], cf[i][it / PT]);
                         if (it + DEPTH < NI) hq[it % DEPTH] = hfrag(it + DEPTH);
                     }
-                    if constexpr (N % 32 == 0) sched_pipeline<NI, DEPTH, PL, M::kMfma>();
-                    __builtin_amdgcn_sched_barrier(0);
+                    if constexpr (N % 32 == 0 && !ILP) sched_pipeline<NI, DEPTH, PL, M::kMfma>();
+                    if constexpr (!ILP) __builtin_amdgcn_sched_barrier(0);
                 }
+                float einter; // e^{ell} of this lane's column token (0 past Tc)
                 {
                     // the products are transposed (rows p, column = this lane's
                     // virtual row t0v + l16), so one decay factor per lane
@@ -1053,8 +1066,11 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
                     if constexpr (C::LWT) e = lw_s[Q * C::LWP + tok];
                     else e = __expf(ell_s[tok]);
                     if (tok >= Tc) e = 0.f;
+                    einter = e;
+                    if constexpr (!ILP) {
 #pragma unroll
-                    for (int pt = 0; pt < PT; ++pt) acc[pt] *= e;
+                        for (int pt = 0; pt < PT; ++pt) acc[pt] *= e;
+                    }
                 }
                 const int tt = (t0v + l16) / R; // token of this lane's column t
                 const float ell_t = ell_s[tt], gam_t = gam_s[tt];
@@ -1083,12 +1099,12 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
                         sb[it % 2] = M::mma(sb[it % 2], bq[it % D2], cf[i][it / 2]);
                         if (it + D2 < NI2) bq[it % D2] = bfrag(it + D2);
                     }
-                    if constexpr (N % 32 == 0) sched_pipeline<NI2, D2, PL, M::kMfma>();
+                    if constexpr (N % 32 == 0 && !ILP) sched_pipeline<NI2, D2, PL, M::kMfma>();
                 };
                 // x operand of M x: slots 0-3 are rows s0 + 4g .. +3, slots
                 // 4-7 rows s0 + 16 + 4g .. +3 (the k order of the M fragment)
                 const uint16_t *xq = xr + (4 * g + (l16 >> 2)) * PP + 4 * (l16 & 3);
-                const int npairs = (R * (tok_last + 1) + 31) / 32;
+                const int npairs = ILP ? V / 32 : (R * (tok_last + 1) + 31) / 32;
                 // mask weights of this lane's 4 source rows r0 .. r0+3 of block q
                 // of the pair at s0, for its column token tt
                 auto mask4 = [&](int s0, int q, float *w) {
@@ -1138,7 +1154,7 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
                     mask4(0, 0, wn[0]);
                     mask4(0, 1, wn[1]);
                 }
-                for (int mp = 0; mp < npairs; ++mp) {
+                for (int mp = 0; mp < (ILP ? V / 32 : npairs); ++mp) {
                     const int s0 = 32 * mp;
                     const floatx4 sb[2] = {sn[0], sn[1]};
                     float wb[2][4];
@@ -1177,7 +1193,9 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
                         IO *dst = ybase + ((tok * p.H * R + ch) * P + 4 * g);
 #pragma unroll
                         for (int pt = 0; pt < PT; ++pt) {
-                            float o4[4] = {acc[pt][0], acc[pt][1], acc[pt][2], acc[pt][3]};
+                            float o4[4];
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) o4[q] = ILP ? acc[pt][q] + einter * inter(pt)[q] : acc[pt][q];
                             if constexpr (BLK) {
                                 if (p.blk.z) {
                                     // output gate: y * silu(z)
