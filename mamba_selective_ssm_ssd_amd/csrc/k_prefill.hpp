@@ -620,15 +620,21 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
     // chunk's coefficients in the second phase instead of the first
     constexpr bool CP2 = C::MFP && C::FREEW > 0;
 
-    // workgroup -> (b, h, segment); consecutive heads land on the same XCD
-    // output pass: S segments per sequence; pre-pass: the first S - 1 of
-    // them, each cut into kpre pieces (aggregates indexed by piece)
+    // workgroup -> (b, h, segment); consecutive indices li land on the same
+    // XCD.  Output pass: S segments per sequence, li = bh S + seg (the few
+    // segments of a head, and neighbouring heads, share an XCD).  Pre-pass:
+    // the first S - 1 segments, each cut into kpre pieces (aggregates indexed
+    // by piece), li = piece (b H) + bh, so that the workgroups running at
+    // once on an XCD are neighbouring heads at the same tokens: the per-token
+    // rows of dt, lam and theta (a few bytes per head) then share cache lines
+    // instead of each pulling its own.
     const int nseg = OUT ? p.S : (p.S - 1) * p.kpre;
-    const int64_t total = p.batch * p.H * nseg;
+    const int64_t nbh = p.batch * p.H;
+    const int64_t total = nbh * nseg;
     int64_t li = blockIdx.x;
     if (total % 8 == 0) li = int64_t(blockIdx.x % 8) * (total / 8) + blockIdx.x / 8;
-    const int seg = int(li % nseg);
-    const int64_t bh = li / nseg;
+    const int seg = OUT ? int(li % nseg) : int(li / nbh);
+    const int64_t bh = OUT ? li / nseg : li % nbh;
     const int h = int(bh % p.H);
     const int hg = h / p.hpg; // B/C group of the head
     const int64_t b = bh / p.H;
