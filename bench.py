@@ -371,6 +371,25 @@ def time_backward(torch, mixer, inp, steps, warm_s):
     return time_whole(torch, lambda: mixer.backward(*args, gy), steps, 2, warm_s)
 
 
+def backward_entry(capi, mixer, torch, name, dims, msw, ceil):
+    """The JSON entry of one backward workload timed at msw ms per call."""
+    b, T, H, P, N, R = dims
+    bb, bfl = backward_bytes(b, T, H, P, N, R), backward_flops(b, T, H, P, N, R)
+    tf = bfl / (msw / 1000) / 1e12
+    _, S, L = capi.m3_ssm_prefill_backward_plan(mixer.make_shape(b, T, H, P, N, R, torch.bfloat16))
+    e = {"workload": name, "ms_per_step": round(msw, 3), "tokens_per_s": round(b * T / (msw / 1000), 1),
+         "segments": S, "segment_tokens": L,
+         "roofline": {"kernel": "k_backward", "bound": "mfma", "achieved": round(tf, 2),
+                      "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                      "frac": round(tf / FP32_MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                      "alg_flops": bfl, "avg_us": round(msw * 1000, 1)},
+         "alg_bytes": bb, "frac_of_hbm_peak_at_alg_bytes": round(bb / (msw / 1000) / 1e9 / HBM_PEAK_GBS, 4),
+         "note": "chunked, 32 (token, rank) rows per chunk, products on fp32 MFMA"}
+    if ceil.get("mfma_fp32_tflops"):
+        e["roofline"]["frac_of_measured_mfma_ceiling"] = round(tf / ceil["mfma_fp32_tflops"], 4)
+    return e
+
+
 def time_decode(torch, mixer, synth, b, H, P, N, R, steps, warmup, seed=0, with_block=False,
                 state_dtype=None, warm_s=0.2, sample=None):
     """`steps` decode steps on step-major inputs after `warmup` steps and
@@ -669,6 +688,12 @@ def main():
         result["prewarm_s"] = round(prewarm, 3)
         log(f"[long mimo prefill] {ms:.3f} ms/step (pre-pass {pre:.3f}, output {out:.3f})  "
             f"{e['tokens_per_s']:.3e} tokens/s  output {e['roofline']['frac']:.3f} of HBM")
+        if not args.no_variants:
+            # its backward: 64 sequences, each cut into segments to fill the chip
+            msw = time_backward(torch, mixer, inp, 3, args.warm_s)
+            result["backward_long_mimo_prefill"] = backward_entry(capi, mixer, torch, c["name"], pf.dims, msw, ceil)
+            log(f"[long mimo prefill backward] {msw:.3f} ms/step")
+            torch.cuda.empty_cache()
         if not args.no_cpu:
             oracle_jobs.append(("cpu_baseline", inp, pf))
         else:
@@ -718,18 +743,7 @@ def main():
             log(f"[{key} + block] {msb * 1000:.1f} us/step")
             del blk, z, wsb
             msw = time_backward(torch, mixer, inp, 10, args.warm_s)
-            bb, bfl = backward_bytes(b, T, H, P, N, R), backward_flops(b, T, H, P, N, R)
-            tf = bfl / (msw / 1000) / 1e12
-            result[f"backward_{key}"] = {
-                "workload": c["name"], "ms_per_step": round(msw, 3), "tokens_per_s": round(b * T / (msw / 1000), 1),
-                "roofline": {"kernel": "k_backward", "bound": "mfma", "achieved": round(tf, 2),
-                             "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                             "frac": round(tf / FP32_MFMA_PEAK_TFLOPS, 4), "traffic": None,
-                             "alg_flops": bfl, "avg_us": round(msw * 1000, 1)},
-                "alg_bytes": bb, "frac_of_hbm_peak_at_alg_bytes": round(bb / (msw / 1000) / 1e9 / HBM_PEAK_GBS, 4),
-                "note": "chunked, 32 (token, rank) rows per chunk, products on fp32 MFMA"}
-            if ceil.get("mfma_fp32_tflops"):
-                result[f"backward_{key}"]["roofline"]["frac_of_measured_mfma_ceiling"] = round(tf / ceil["mfma_fp32_tflops"], 4)
+            result[f"backward_{key}"] = backward_entry(capi, mixer, torch, c["name"], pf.dims, msw, ceil)
             log(f"[{key} backward] {msw:.3f} ms/step")
             if cfg == 1:
                 del inp, pf

@@ -57,12 +57,31 @@ typedef struct {
     const float *prev_x; /* [b][H][R][P]  of the final prev_x, the last token's x   */
 } m3_final_grads_t;
 
+/* How the backward pass splits the work (depends on the shape only): each
+ * (batch, head) sequence is cut into `segments` segments of `segment_tokens`
+ * tokens (the last may be shorter), one workgroup per (batch, head, segment),
+ * when batch * H is below 256 and the sequence has at least four chunks of
+ * 32 / R tokens (at most 64 segments, at least two chunks each); 1 segment
+ * otherwise.  A split sequence takes three more launches: the segments'
+ * aggregates (the state at each segment's end from a zero start, and the
+ * gradient of the state at each segment's start from a zero gradient at its
+ * end, with the summed log decay and angle), folded into each segment's
+ * starting state and incoming gradient as in the chunked algorithm's
+ * inter-chunk state passing (the "20.2 Mamba and S6" page, section 2); and a
+ * fix-up that adds the later segments' summed angle gradients to each
+ * segment's dtheta and the gradient of a segment's first delta to its dt and
+ * lam.  Either output pointer may be NULL.  Errors: those of the shape check
+ * of m3_ssm_prefill_backward. */
+m3_status_t m3_ssm_prefill_backward_plan(const m3_shape_t *shape, int32_t *segments,
+                                         int64_t *segment_tokens);
+
 /* Bytes of device workspace m3_ssm_prefill_backward needs (0: unsupported).
  * The pass stores the state entering every chunk of 32 / R tokens in fp32
  * and the angle there in fp64, so the size grows with the sequence:
  * batch * H * ceil(T / (32 / R)) * (N * P * 4 + N / 2 * 8) bytes, plus
- * alignment and 4 bytes per (batch, head).  The workspace is caller-owned
- * and needs no initialisation. */
+ * alignment, 4 bytes per (batch, head, segment) and, for split sequences,
+ * batch * H * segments * (2 N P * 4 + 8 + N * 8) bytes of segment
+ * aggregates.  The workspace is caller-owned and needs no initialisation. */
 size_t m3_ssm_prefill_backward_workspace_bytes(const m3_shape_t *shape);
 
 /*

@@ -25,7 +25,8 @@ M3_ERR_HIP = 4
 EXPORTED = ("m3_ssm_prefill_workspace_bytes", "m3_ssm_prefill", "m3_ssm_decode_step",
             "m3_status_string", "m3_ssm_prefill_stage", "m3_ssm_prefill_block",
             "m3_ssm_decode_step_block", "m3_ssm_prefill_backward_workspace_bytes",
-            "m3_ssm_prefill_backward", "m3_ssm_prefill_backward_ex", "m3_ssm_prefill_noalloc",
+            "m3_ssm_prefill_backward", "m3_ssm_prefill_backward_ex", "m3_ssm_prefill_backward_plan",
+            "m3_ssm_prefill_noalloc",
             "m3_ssm_prefill_plan",
             "m3_ceiling_mfma", "m3_ceiling_stream")
 
@@ -116,6 +117,8 @@ def load():
                                                ctypes.POINTER(m3_final_grads_t), gp, vp,
                                                ctypes.c_size_t, vp]
     lib.m3_ssm_prefill_backward_ex.restype = ctypes.c_int
+    lib.m3_ssm_prefill_backward_plan.argtypes = [sp, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)]
+    lib.m3_ssm_prefill_backward_plan.restype = ctypes.c_int
     lib.m3_ssm_prefill_noalloc.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, stp, stp, vp, vp]
     lib.m3_ssm_prefill_noalloc.restype = ctypes.c_int
     i32p, i64p = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
@@ -234,3 +237,10 @@ def m3_ssm_prefill_backward_ex(shape, x, dt, A, lam, theta, B, C, init, gy, gfin
         ctypes.byref(gfinal) if gfinal is not None else None,
         ctypes.byref(grads) if grads is not None else None,
         workspace, int(workspace_bytes), stream))
+
+
+def m3_ssm_prefill_backward_plan(shape):
+    """(status, segments per sequence, tokens per segment) of the backward pass."""
+    sg, tk = ctypes.c_int32(0), ctypes.c_int64(0)
+    rc = int(load().m3_ssm_prefill_backward_plan(ctypes.byref(shape), ctypes.byref(sg), ctypes.byref(tk)))
+    return rc, sg.value, tk.value

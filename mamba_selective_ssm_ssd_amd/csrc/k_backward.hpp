@@ -180,11 +180,29 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
         lg = lane >> 4;
     };
     lane_ids();
-    const int64_t bh = blockIdx.x;
+    // workgroup -> (b, h, segment) and its role: 0 the gradients of the
+    // segment, 1 its forward-state aggregate, 2 its adjoint aggregate
+    const int S = p.S;
+    int64_t bh;
+    int sg, role;
+    if (p.mode == 0) {
+        bh = blockIdx.x / S;
+        sg = int(blockIdx.x % S);
+        role = 0;
+    } else {
+        const int64_t nf = int64_t(S - 1) * p.batch * p.H;
+        int64_t idx = blockIdx.x;
+        role = idx < nf ? 1 : 2;
+        if (role == 2) idx -= nf;
+        bh = idx / (S - 1);
+        sg = int(idx % (S - 1)) + (role == 2 ? 1 : 0);
+    }
     const int h = int(bh % p.H);
     const int64_t b = bh / p.H;
     const int64_t T = p.T;
     const int nC = p.nC;
+    const int c0 = sg * p.cps, c1 = min(nC, c0 + p.cps); // this segment's chunks
+    const int64_t bs = bh * S + sg;                        // (b, h, segment) index
     const float Ah = p.A[h];
     const IO *xg = static_cast<const IO *>(p.x), *Bg = static_cast<const IO *>(p.B);
     const IO *Cg = static_cast<const IO *>(p.C), *gyg = static_cast<const IO *>(p.gy);
@@ -279,7 +297,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
     // fp64: lane = 8 segments x 8 pairs, a segment's prefix in registers, the
     // segment totals scanned over lanes 8 apart.  Writes CS (cos and sin of
     // Phi_t) and PHE (the wrapped angle of the chunk's last token).
-    auto stage_angles = [&](int Tc, bool fwd, int c) {
+    auto stage_angles = [&](int Tc, bool fwd, int c, bool store) {
 #pragma unroll
         for (int kp = 0; kp < KP; ++kp) {
             const int k = KS * kp + 8 * w + (lane & 7), seg = lane >> 3;
@@ -303,7 +321,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
                 if (lane >= o) x += y;
             }
             const double ex = x - run;
-            if (fwd && kv && seg == 0) ckp[int64_t(c) * K + k] = ph0;
+            if (fwd && store && kv && seg == 0) ckp[int64_t(c) * K + k] = ph0;
 #pragma unroll
             for (int u = 0; u < TPS; ++u) {
                 const int i = seg * TPS + u;
@@ -376,12 +394,101 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
             for (int e = 0; e < 4; ++e) f[kb][e] = sc(s, row_tok(kb * 16 + 4 * lg + e));
     };
 
+    // element (n, pc) of R(-phi) M for a [N][P] matrix M (rows 2k, 2k+1 rotated
+    // by the angle of pair k)
+    auto rot_el = [&](const float *M, int n, int pc, double phi) {
+        float sn, cs;
+        sincos_wrapped(wrap_angle(phi), &sn, &cs);
+        const float u = M[(n & ~1) * P + pc], v = M[(n | 1) * P + pc];
+        return (n & 1) ? cs * v - sn * u : cs * u + sn * v;
+    };
+    // the angle Phi before segment sg's first chunk: Phi_{-1} plus the
+    // summed theta of the segments before it
+    auto phi_start = [&](int k, int upto) {
+        double a = p.has_init ? double(p.phi0[bh * K + k]) : 0.0;
+        for (int s2 = 0; s2 < upto; ++s2) a += p.segTh[(bh * S + s2) * K + k];
+        return a;
+    };
+
+    if (role == 2) {
+        // ===================== adjoint aggregate of segment sg: the gradient
+        // of the state before its first chunk from the segment's own outputs,
+        // with zero gradient after its last chunk, in the frame of its start:
+        //   G = sum_c (prod_{c' < c} e^{ec_end(c')}) C~_c^T diag(E_c) gy_c,
+        // accumulated in chunk order (G1 layout, second wave group)
+        floatx4 Ga[NBW][PB];
+#pragma unroll
+        for (int q = 0; q < NBW; ++q)
+#pragma unroll
+            for (int pb = 0; pb < PB; ++pb) Ga[q][pb] = zero4();
+        float lsum = 0.f;
+        if (tid < K) PHE[tid] = 0.0;
+        issue(int64_t(c0) * Q, int(min<int64_t>(T - int64_t(c0) * Q, Q)), true);
+        __syncthreads();
+        for (int c = c0; c < c1; ++c) {
+            lane_ids();
+            const int64_t t0 = int64_t(c) * Q;
+            const int Tc = int(min<int64_t>(T - t0, Q));
+            stage_scalars(t0, Tc);
+            stage_angles(Tc, true, c, false);
+            stage_xg(Tc, false, nullptr);
+            __syncthreads();
+            rot_store(qc, Tc, CT, nullptr);
+            const float dec = __expf(lsum);
+            lsum += sc(Cf::s_ec, Q - 1);
+            float ev[VB][4];
+            row_factor(Cf::s_E, ev);
+            __syncthreads();
+            if (c + 1 < c1) issue(t0 + Q, int(min<int64_t>(T - t0 - Q, Q)), true);
+            if (w >= 4) {
+                const int wb = w - 4;
+#pragma unroll
+                for (int kb = 0; kb < VB; ++kb) {
+                    floatx4 bc[NBW], ag[PB];
+#pragma unroll
+                    for (int q = 0; q < NBW; ++q)
+                        if (wb + 4 * q < NB) bc[q] = lds4(CT + ((wb + 4 * q) * 16 + li) * pV + 16 * kb + 4 * lg);
+#pragma unroll
+                    for (int pb = 0; pb < PB; ++pb) ag[pb] = lds4(T2 + (pb * 16 + li) * pV + 16 * kb + 4 * lg);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+#pragma unroll
+                        for (int q = 0; q < NBW; ++q) {
+                            if (wb + 4 * q >= NB) continue;
+                            const float bq = bc[q][e] * (ev[kb][e] * dec);
+#pragma unroll
+                            for (int pb = 0; pb < PB; ++pb) Ga[q][pb] = mfma4(ag[pb][e], bq, Ga[q][pb]);
+                        }
+                }
+            }
+            __syncthreads();
+        }
+        if (w >= 4) {
+            const int wb = w - 4;
+            float *out = p.segGa + bs * int64_t(N) * P;
+#pragma unroll
+            for (int q = 0; q < NBW; ++q) {
+                const int nb = wb + 4 * q;
+                if (nb >= NB) continue;
+#pragma unroll
+                for (int pb = 0; pb < PB; ++pb)
+                    *reinterpret_cast<floatx4 *>(out + (nb * 16 + li) * P + pb * 16 + 4 * lg) = Ga[q][pb];
+            }
+        }
+        if (sg == S - 1 && tid == 0) p.segg[bs] = lsum; // the other segments' sums come from role 1
+        return;
+    }
+
     // ===================== forward sweep: H_c and Phi at each chunk start
     // Hf: transposed tiles (pb, nb = w + 8 q) of H_c; element e of lane
     // (li, lg) is H[nb*16 + li][pb*16 + 4 lg + e] (the layout of G in the
     // second wave group below).
     floatx4 Hf[NBH][PB];
     {
+        // the state entering the segment: at the sequence start the carried
+        // state with its pending term; later, the aggregates of the segments
+        // before it folded in, H <- e^{g} H + R(-Phi_start) A (role 1 starts
+        // from zero in the frame of its own start)
         const float d0 = io<IO>::get(dtg + tok(0)), l0 = io<IO>::get(lmg + tok(0));
         const float dl0 = (1.f - l0) * d0;
 #pragma unroll
@@ -390,35 +497,52 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
             for (int pb = 0; pb < PB; ++pb) {
                 Hf[q][pb] = zero4();
                 const int nb = w + kBwdWaves * q;
-                if (nb >= NB || !p.has_init) continue;
+                if (nb >= NB || role != 0) continue;
                 const int n = nb * 16 + li, pc = pb * 16 + 4 * lg;
-                const float4 hv = *reinterpret_cast<const float4 *>(p.h0 + (bh * N + n) * int64_t(P) + pc);
-                float hh[4] = {hv.x, hv.y, hv.z, hv.w};
+                float hh[4] = {0.f, 0.f, 0.f, 0.f};
+                if (p.has_init) {
+                    const float4 hv = *reinterpret_cast<const float4 *>(p.h0 + (bh * N + n) * int64_t(P) + pc);
+                    hh[0] = hv.x; hh[1] = hv.y; hh[2] = hv.z; hh[3] = hv.w;
 #pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    const float bb = dl0 * p.prevB0[(bh * R + r) * N + n];
-                    float xv[4];
-                    io<IO>::load4(static_cast<const IO *>(p.prevx0) + (bh * R + r) * P + pc, xv);
+                    for (int r = 0; r < R; ++r) {
+                        const float bb = dl0 * p.prevB0[(bh * R + r) * N + n];
+                        float xv[4];
+                        io<IO>::load4(static_cast<const IO *>(p.prevx0) + (bh * R + r) * P + pc, xv);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) hh[e] += bb * xv[e];
+                        for (int e = 0; e < 4; ++e) hh[e] += bb * xv[e];
+                    }
+                }
+                if (sg > 0) {
+                    double ph = p.has_init ? double(p.phi0[bh * K + (n >> 1)]) : 0.0;
+                    for (int s2 = 0; s2 < sg; ++s2) {
+                        const int64_t o = bh * S + s2;
+                        const float eg = __expf(p.segg[o]);
+                        const float *A = p.segA + o * int64_t(N) * P;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) hh[e] = eg * hh[e] + rot_el(A, n, pc + e, ph);
+                        ph += p.segTh[o * K + (n >> 1)];
+                    }
                 }
                 Hf[q][pb] = floatx4{hh[0], hh[1], hh[2], hh[3]};
             }
-        if (tid < K) PHE[tid] = p.has_init ? double(p.phi0[bh * K + tid]) : 0.0;
+        if (tid < K) PHE[tid] = role == 0 ? phi_start(tid, sg) : 0.0;
     }
-    issue(0, int(min<int64_t>(T, Q)), false);
+    float gsum = 0.f; // role 1: summed log decay of the segment
+    issue(int64_t(c0) * Q, int(min<int64_t>(T - int64_t(c0) * Q, Q)), false);
     __syncthreads();
-    for (int c = 0; c < nC; ++c) {
+    for (int c = c0; c < c1; ++c) {
         lane_ids();
         const int64_t t0 = int64_t(c) * Q;
         const int Tc = int(min<int64_t>(T - t0, Q));
+        if (role == 0) {
 #pragma unroll
-        for (int q = 0; q < NBH; ++q)
+            for (int q = 0; q < NBH; ++q)
 #pragma unroll
-            for (int pb = 0; pb < PB; ++pb)
-                if (w + kBwdWaves * q < NB) *reinterpret_cast<floatx4 *>(ck_at(c, w + kBwdWaves * q, pb)) = Hf[q][pb];
+                for (int pb = 0; pb < PB; ++pb)
+                    if (w + kBwdWaves * q < NB) *reinterpret_cast<floatx4 *>(ck_at(c, w + kBwdWaves * q, pb)) = Hf[q][pb];
+        }
         stage_scalars(t0, Tc);
-        stage_angles(Tc, true, c);
+        stage_angles(Tc, true, c, role == 0);
         // x^T alternates between two buffers (T2 and the mask area, unused in
         // this sweep), so the next chunk's staging needs no barrier after
         // this chunk's update; the token factors are read before the second
@@ -428,10 +552,11 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
         __syncthreads();
         rot_store(qb, Tc, BT, nullptr);
         const float eE = sc(Cf::s_misc, 0);
+        gsum += sc(Cf::s_ec, Q - 1);
         float uv[VB][4];
         row_factor(Cf::s_U, uv);
         __syncthreads();
-        if (c + 1 < nC) issue(t0 + Q, int(min<int64_t>(T - t0 - Q, Q)), false);
+        if (c + 1 < c1) issue(t0 + Q, int(min<int64_t>(T - t0 - Q, Q)), false);
         // H^T[p][n] <- e^{ec_end} H^T + sum_v x[v][p] U_v B~[v][n]
         {
 #pragma unroll
@@ -459,6 +584,21 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
         }
     }
     __syncthreads(); // the backward sweep's staging reuses the LDS
+    if (role == 1) {
+        // forward aggregate of segment sg: its state at the end from zero (frame
+        // of its start), summed log decay and summed angle
+        float *out = p.segA + bs * int64_t(N) * P;
+#pragma unroll
+        for (int q = 0; q < NBH; ++q)
+#pragma unroll
+            for (int pb = 0; pb < PB; ++pb) {
+                const int nb = w + kBwdWaves * q;
+                if (nb < NB) *reinterpret_cast<floatx4 *>(out + (nb * 16 + li) * P + pb * 16 + 4 * lg) = Hf[q][pb];
+            }
+        if (tid == 0) p.segg[bs] = gsum;
+        if (tid < K) p.segTh[bs * K + tid] = PHE[tid];
+        return;
+    }
 
     // ===================== backward sweep
     // G, the gradient of H_{c+1}, in registers GS: waves 0-3 hold G in tiles
@@ -471,8 +611,38 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
 #define G2(nb) GS[nb]
 #define G1(q, pb) GS[(q) * PB + (pb)]
     // after the last chunk G is the incoming gradient of the final h~ (the
-    // last token has no next token, so H after the last chunk is h~_{T-1})
-    if (p.ghT) {
+    // last token has no next token, so H after the last chunk is h~_{T-1});
+    // after an earlier segment's last chunk it is that gradient carried back
+    // through the later segments, folded from their adjoint aggregates:
+    // G <- e^{g} G + R(-Phi_start) Ga, last segment first
+    if (sg < S - 1) {
+        auto gend = [&](int n, int pc) {
+            float v = p.ghT ? p.ghT[(bh * N + n) * int64_t(P) + pc] : 0.f;
+            double ph = phi_start(n >> 1, S - 1);
+            for (int s2 = S - 1; s2 > sg; --s2) {
+                const int64_t o = bh * S + s2;
+                v = __expf(p.segg[o]) * v + rot_el(p.segGa + o * int64_t(N) * P, n, pc, ph);
+                ph -= p.segTh[(o - 1) * K + (n >> 1)];
+            }
+            return v;
+        };
+        if (w < 4 && w < PB) {
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) G2(nb)[e] = gend(nb * 16 + 4 * lg + e, w * 16 + li);
+        } else if (w >= 4) {
+#pragma unroll
+            for (int q = 0; q < NBW; ++q) {
+                const int nb = w - 4 + 4 * q;
+                if (nb >= NB) continue;
+#pragma unroll
+                for (int pb = 0; pb < PB; ++pb)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) G1(q, pb)[e] = gend(nb * 16 + li, pb * 16 + 4 * lg + e);
+            }
+        }
+    } else if (p.ghT) {
         const float *gh = p.ghT + bh * int64_t(N) * P;
         if (w < 4 && w < PB) {
 #pragma unroll
@@ -491,24 +661,27 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
         }
     }
     double carry[KP];    // lanes (pair, segment): sum of dPhi over the later chunks
+    double carry0[KP];   // its value at the segment's end
 #pragma unroll
     for (int kp = 0; kp < KP; ++kp) {
         // the final Phi_T = Phi_{-1} + sum theta: its incoming gradient adds
-        // to every dtheta_t and to dPhi_{-1}
+        // to every dtheta_t and to dPhi_{-1}.  An earlier segment starts from
+        // zero; the later segments' sums are added to its dtheta afterwards.
         const int k = KS * kp + 8 * w + (lane & 7);
-        carry[kp] = p.gphiT && k < K ? double(p.gphiT[bh * K + k]) : 0.0;
+        carry[kp] = p.gphiT && k < K && sg == S - 1 ? double(p.gphiT[bh * K + k]) : 0.0;
+        carry0[kp] = carry[kp];
     }
     float gA = 0.f;      // wave 0: this lane's share of dA
     bool pend = false;   // wave 0, lane 0: the later chunk's first token awaits its d(delta)
     float pd_g = 0.f, pd_l = 0.f, pd_dt = 0.f, pd_lam = 0.f;
     int64_t pd_tok = 0;
-    issue(int64_t(nC - 1) * Q, int(T - int64_t(nC - 1) * Q), true);
-    for (int c = nC - 1; c >= 0; --c) {
+    issue(int64_t(c1 - 1) * Q, int(min<int64_t>(T - int64_t(c1 - 1) * Q, Q)), true);
+    for (int c = c1 - 1; c >= c0; --c) {
         lane_ids();
         const int64_t t0 = int64_t(c) * Q;
         const int Tc = int(min<int64_t>(T - t0, Q));
         stage_scalars(t0, Tc);
-        stage_angles(Tc, false, c);
+        stage_angles(Tc, false, c, false);
         stage_xg(Tc, false, nullptr);
         // H_c (the second group's tiles), in flight during the staging
         const int wb = w - 4; // wave index in the second group
@@ -618,7 +791,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
         // the previous chunk's inputs, in flight during the products (the first
         // group, whose products are fewer, prefetches now, the second after its
         // products)
-        if (c > 0 && w < 4) issue(t0 - Q, Q, true);
+        if (c > c0 && w < 4) issue(t0 - Q, Q, true);
         // ---- per token j (8 threads each): row sums of dW.W and column sums
         // of dW.e^{ec_i - ec_j} off the diagonal, and dW(j, j); dW(i, j) is
         // the sum of S.D over the R x R block of the token pair
@@ -800,7 +973,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
         pz += __shfl_xor(pz, 16);
         pz += __shfl_xor(pz, 32);
         if (lane == 0) PZ[wb * 4] = pz;
-        if (c > 0) issue(t0 - Q, Q, true);
+        if (c > c0) issue(t0 - Q, Q, true);
         }
         __syncthreads();
         // ---- the scalars (wave 0, lane = token)
@@ -837,6 +1010,9 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
                 p.glam[o] = (dgam - dd) * dtj;
             }
             if (j < Tc) gA += dl * dtj;
+            // the last chunk of an earlier segment: the gradient of the next
+            // segment's first delta, added to that token's dt, lam afterwards
+            if (j == 0 && c == c1 - 1 && sg < S - 1) p.segdd[bs + 1] = ddLast;
             if (j == 0) {
                 if (pend) {
                     p.gdt[pd_tok] = pd_g * pd_lam + ddLast * (1.f - pd_lam) + pd_l * Ah;
@@ -883,10 +1059,18 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
         __syncthreads();
     }
 
-    // ===================== the carried state (G is now the gradient of H_0)
+    // ===================== the segment's summed dPhi (the later segments'
+    // sums are added to an earlier segment's dtheta afterwards)
     lane_ids();
+    if (S > 1 && lane < 8)
+#pragma unroll
+        for (int kp = 0; kp < KP; ++kp) {
+            const int k = KS * kp + 8 * w + lane;
+            if (k < K) p.segDphi[bs * K + k] = carry[kp] - carry0[kp];
+        }
+    // ===================== the carried state (G is now the gradient of H_0)
     float dd0 = 0.f;
-    if (p.has_init) {
+    if (p.has_init && sg == 0) {
         const float d0 = io<IO>::get(dtg + tok(0)), l0 = io<IO>::get(lmg + tok(0));
         const float dl0 = (1.f - l0) * d0;
         // from G2 (columns p = w*16 + li): dx_{-1} and the gradient of d_0
@@ -938,7 +1122,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
                 if (lg == 0 && p.gprevB0) p.gprevB0[(bh * R + r) * N + n] = dl0 * s;
             }
         }
-        if (p.gphi0)
+        if (p.gphi0 && S == 1)
 #pragma unroll
             for (int kp = 0; kp < KP; ++kp) {
                 const int k = KS * kp + 8 * w + lane;
@@ -954,19 +1138,63 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
         }
 #pragma unroll
         for (int o = 1; o < kWave; o <<= 1) gA += __shfl_xor(gA, o);
-        if (lane == 0) p.gA_part[bh] = gA;
+        if (lane == 0) p.gA_part[bs] = gA;
     }
 #undef G1
 #undef G2
 }
 
-// Sum of the per-(batch, head) partials of dA over the batch.
+// Sum of the per-(batch, head, segment) partials of dA over batch and segments.
 static __global__ void k_backward_gA(const BwdParams p) {
     const int h = blockIdx.x * blockDim.x + threadIdx.x;
     if (h >= p.H) return;
     float s = 0.f;
-    for (int64_t b = 0; b < p.batch; ++b) s += p.gA_part[b * p.H + h];
+    for (int64_t b = 0; b < p.batch; ++b)
+        for (int sg = 0; sg < p.S; ++sg) s += p.gA_part[(b * p.H + h) * p.S + sg];
     p.gA[h] = s;
+}
+
+// Split sequences, after the segments' gradients: per (b, h, segment sg)
+//  * dtheta of every token of an earlier segment += dPhi_T's gradient plus
+//    the summed dPhi of the later segments (the suffix sums the segment began
+//    at zero);
+//  * the first token of a later segment: the gradient of its delta from the
+//    segment before (delta = (1 - lam) dt) into its dt and lam;
+//  * dPhi_{-1} = dPhi_T's gradient plus every segment's sum (segment 0).
+template <typename IO>
+__global__ __launch_bounds__(256) void k_backward_fix(const BwdParams p) {
+    const int S = p.S, K = p.K;
+    const int64_t bh = blockIdx.x / S;
+    const int sg = int(blockIdx.x % S);
+    const int h = int(bh % p.H);
+    const int64_t b = bh / p.H;
+    const int Q = kBwdV / p.R;
+    const int64_t t0 = int64_t(sg) * p.cps * Q, t1 = min<int64_t>(p.T, t0 + int64_t(p.cps) * Q);
+    auto carry_from = [&](int k, int first) {
+        double a = p.gphiT ? double(p.gphiT[bh * K + k]) : 0.0;
+        for (int s2 = first; s2 < S; ++s2) a += p.segDphi[(bh * S + s2) * K + k];
+        return a;
+    };
+    if (sg < S - 1) {
+        const int64_t n = (t1 - t0) * K;
+        for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
+            const int64_t t = t0 + i / K;
+            const int k = int(i % K);
+            // the carry is recomputed per element: S is small, and K consecutive
+            // threads share each k's sums (cached)
+            p.gtheta[((b * p.T + t) * p.H + h) * K + k] += float(carry_from(k, sg + 1));
+        }
+    }
+    if (sg > 0 && threadIdx.x == 0) {
+        const int64_t o = (b * p.T + t0) * p.H + h;
+        const float dd = p.segdd[bh * S + sg];
+        const float dtv = io<IO>::get(static_cast<const IO *>(p.dt) + o);
+        const float lmv = io<IO>::get(static_cast<const IO *>(p.lam) + o);
+        p.gdt[o] += dd * (1.f - lmv);
+        p.glam[o] -= dd * dtv;
+    }
+    if (sg == 0 && p.has_init && p.gphi0)
+        for (int k = threadIdx.x; k < K; k += blockDim.x) p.gphi0[bh * K + k] = float(carry_from(k, 0));
 }
 
 template <typename IO, int N, int P, int R>
@@ -977,9 +1205,24 @@ hipError_t launch_backward_inst(const BwdParams &p, hipStream_t s) {
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, int(Cf::bytes));
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((k_backward<IO, N, P, R>), dim3(unsigned(p.batch * p.H)), dim3(kBwdThreads), Cf::bytes, s, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    const int64_t nbh = p.batch * p.H;
+    hipError_t e;
+    if (p.S > 1) {
+        // segment aggregates: forward state of segments 0 .. S-2, adjoint of 1 .. S-1
+        BwdParams pa = p;
+        pa.mode = 1;
+        hipLaunchKernelGGL((k_backward<IO, N, P, R>), dim3(unsigned(2 * (p.S - 1) * nbh)), dim3(kBwdThreads), Cf::bytes,
+                           s, pa);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    BwdParams pm = p;
+    pm.mode = 0;
+    hipLaunchKernelGGL((k_backward<IO, N, P, R>), dim3(unsigned(p.S * nbh)), dim3(kBwdThreads), Cf::bytes, s, pm);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (p.S > 1) {
+        hipLaunchKernelGGL((k_backward_fix<IO>), dim3(unsigned(p.S * nbh)), dim3(256), 0, s, p);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     hipLaunchKernelGGL(k_backward_gA, dim3(unsigned((p.H + 255) / 256)), dim3(256), 0, s, p);
     return hipGetLastError();
 }

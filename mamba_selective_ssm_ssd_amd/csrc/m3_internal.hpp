@@ -89,7 +89,18 @@ struct BwdParams {
     // workspace
     float *ck_h;    // [b][H][nC][N x P] state entering each chunk (tile-major)
     double *ck_phi; // [b][H][nC][K]     angle before each chunk
-    float *gA_part; // [b][H]
+    float *gA_part; // [b][H][S]
+    // sequences split into S segments of cps chunks (S = 1: no split).
+    // mode 0: the gradients of each (b, h, segment); mode 1: the segment
+    // aggregates, (S - 1) b H workgroups of forward state (segments 0 .. S-2)
+    // then as many of adjoint state (segments 1 .. S-1).
+    int32_t S, cps, mode;
+    float *segA;     // [b][H][S][N][P] state at a segment's end from zero, frame of its start
+    float *segGa;    // [b][H][S][N][P] adjoint at a segment's start from zero at its end, same frame
+    float *segg;     // [b][H][S] summed log decay of a segment
+    float *segdd;    // [b][H][S] gradient of delta of a segment's first token from the segment before
+    double *segTh;   // [b][H][S][K] summed theta of a segment (wrapped)
+    double *segDphi; // [b][H][S][K] summed dPhi of a segment
 };
 
 // Workspace layout (byte offsets of each region, 256-byte aligned).

@@ -15,6 +15,7 @@
 #include "k_prefill.hpp"
 #include "m3_internal.hpp"
 
+#include <algorithm>
 #include <limits>
 
 namespace {
@@ -161,21 +162,47 @@ WorkspaceLayout layout(const m3_shape_t *s) {
     return w;
 }
 
+// Backward segments: with fewer than 256 (batch, head) sequences each is cut
+// into S segments of whole chunks (at least two chunks each, at most 64
+// segments), one workgroup per (b, h, segment), so that the grid fills the
+// 256 CUs; S = 1 otherwise.
+struct BwdPlan {
+    int32_t S, cps;
+};
+BwdPlan bwd_plan(const m3_shape_t *s) {
+    const int64_t bh = int64_t(s->batch) * s->nheads;
+    const int64_t Q = m3::kBwdV / s->rank;
+    const int64_t nC = (int64_t(s->seqlen) + Q - 1) / Q;
+    int64_t S = 1;
+    if (bh < 256) S = std::min<int64_t>({(256 + bh - 1) / bh, nC / 2, 64});
+    if (S < 2) return {1, int32_t(nC)};
+    const int64_t cps = (nC + S - 1) / S;
+    return {int32_t((nC + cps - 1) / cps), int32_t(cps)};
+}
+
 // Backward workspace: the state and angle entering each chunk, the
-// per-sequence partials of dA.
+// per-(sequence, segment) partials of dA and, for split sequences, the
+// segment aggregates.
 struct BwdLayout {
-    size_t ck_h, ck_phi, gA, total;
+    size_t ck_h, ck_phi, gA, segA, segGa, segg, segdd, segTh, segDphi, total;
 };
 BwdLayout bwd_layout(const m3_shape_t *s) {
     const size_t bh = size_t(s->batch) * size_t(s->nheads);
     const size_t Q = size_t(m3::kBwdV / s->rank);
     const size_t nC = (size_t(s->seqlen) + Q - 1) / Q;
     const size_t N = size_t(s->dstate), P = size_t(s->headdim), K = N / 2;
+    const size_t S = size_t(bwd_plan(s).S), nseg = S > 1 ? bh * S : 0;
     BwdLayout w;
     size_t off = 0;
     w.ck_h = off; off += round_up(bh * nC * N * P * sizeof(float));
     w.ck_phi = off; off += round_up(bh * nC * K * sizeof(double));
-    w.gA = off; off += round_up(bh * sizeof(float));
+    w.gA = off; off += round_up(bh * S * sizeof(float));
+    w.segA = off; off += round_up(nseg * N * P * sizeof(float));
+    w.segGa = off; off += round_up(nseg * N * P * sizeof(float));
+    w.segg = off; off += round_up(nseg * sizeof(float));
+    w.segdd = off; off += round_up(nseg * sizeof(float));
+    w.segTh = off; off += round_up(nseg * K * sizeof(double));
+    w.segDphi = off; off += round_up(nseg * K * sizeof(double));
     w.total = off;
     return w;
 }
@@ -454,6 +481,15 @@ size_t m3_ssm_prefill_backward_workspace_bytes(const m3_shape_t *shape) {
     return bwd_layout(shape).total;
 }
 
+m3_status_t m3_ssm_prefill_backward_plan(const m3_shape_t *shape, int32_t *segments, int64_t *segment_tokens) {
+    const m3_status_t sc = check_backward_shape(shape);
+    if (sc != M3_OK) return sc;
+    const BwdPlan plan = bwd_plan(shape);
+    if (segments) *segments = plan.S;
+    if (segment_tokens) *segment_tokens = int64_t(plan.cps) * (m3::kBwdV / shape->rank);
+    return M3_OK;
+}
+
 m3_status_t m3_ssm_prefill_backward(const m3_shape_t *shape, const void *x, const void *dt,
                                     const float *A, const void *lam, const void *theta,
                                     const void *B, const void *C, const m3_state_t *init,
@@ -514,6 +550,15 @@ m3_status_t m3_ssm_prefill_backward_ex(const m3_shape_t *shape, const void *x, c
     p.ck_h = reinterpret_cast<float *>(ws + w.ck_h);
     p.ck_phi = reinterpret_cast<double *>(ws + w.ck_phi);
     p.gA_part = reinterpret_cast<float *>(ws + w.gA);
+    const BwdPlan plan = bwd_plan(shape);
+    p.S = plan.S;
+    p.cps = plan.cps;
+    p.segA = reinterpret_cast<float *>(ws + w.segA);
+    p.segGa = reinterpret_cast<float *>(ws + w.segGa);
+    p.segg = reinterpret_cast<float *>(ws + w.segg);
+    p.segdd = reinterpret_cast<float *>(ws + w.segdd);
+    p.segTh = reinterpret_cast<double *>(ws + w.segTh);
+    p.segDphi = reinterpret_cast<double *>(ws + w.segDphi);
     const hipError_t e = shape->io_dtype == M3_DTYPE_BF16 ? m3::launch_backward_bf16(p, stream)
                                                           : m3::launch_backward_f32(p, stream);
     return e == hipSuccess ? M3_OK : M3_ERR_HIP;

@@ -354,13 +354,46 @@ def test_backward_errors():
 
 
 @pytest.mark.parametrize("b,T,H,P,N,R", [(4, 2048, 64, 64, 128, 1), (4, 2048, 64, 64, 64, 4),
-                                        (1, 150, 2, 32, 64, 3), (2, 1, 3, 16, 16, 2)])
+                                        (1, 150, 2, 32, 64, 3), (2, 1, 3, 16, 16, 2),
+                                        (1, 65536, 64, 64, 64, 4), (1, 1000, 1, 16, 32, 2)])
 def test_backward_workspace_size_as_documented(b, T, H, P, N, R):
     """include/m3_ssm_backward.h: per (batch, head), one fp32 state and one
-    fp64 angle vector per chunk of 32 / R tokens, plus alignment and 4 bytes."""
+    fp64 angle vector per chunk of 32 / R tokens, plus alignment, 4 bytes per
+    (batch, head, segment) and the aggregates of split sequences."""
     import math
     torch = pytest.importorskip("torch")
     from mamba_selective_ssm_ssd_amd import capi, mixer
-    got = capi.m3_ssm_prefill_backward_workspace_bytes(mixer.make_shape(b, T, H, P, N, R, torch.bfloat16))
-    est = b * H * math.ceil(T / (32 // R)) * (N * P * 4 + N // 2 * 8) + 4 * b * H
-    assert est <= got <= est + 3 * 256
+    shape = mixer.make_shape(b, T, H, P, N, R, torch.bfloat16)
+    got = capi.m3_ssm_prefill_backward_workspace_bytes(shape)
+    rc, S, _ = capi.m3_ssm_prefill_backward_plan(shape)
+    assert rc == capi.M3_OK
+    est = b * H * math.ceil(T / (32 // R)) * (N * P * 4 + N // 2 * 8) + 4 * b * H * S
+    if S > 1:
+        est += b * H * S * (2 * N * P * 4 + 8 + N * 8)
+    assert est <= got <= est + 9 * 256
+
+
+@pytest.mark.parametrize("b,T,H,R,S,tokens", [
+    (4, 2048, 64, 1, 1, 2048),        # 256 sequences fill the chip
+    (4, 2048, 64, 4, 1, 2048),
+    (1, 65536, 64, 4, 4, 16384),      # long context: 64 sequences, 4 segments
+    (1, 150, 2, 1, 2, 96),            # 5 chunks of 32 tokens: 2 segments of 3, 2 chunks
+    (2, 150, 2, 4, 7, 24),            # 19 chunks of 8 tokens: segments of 3 chunks
+    (1, 64, 1, 1, 1, 64),             # 2 chunks: too short to split
+    (1, 100000, 1, 2, 64, 1568),      # at most 64 segments
+])
+def test_backward_plan(b, T, H, R, S, tokens):
+    """m3_ssm_prefill_backward_plan: fewer than 256 sequences are cut into
+    segments of at least two chunks (at most 64) so that the grid fills the
+    256 CUs; the segments cover the sequence and none is empty."""
+    import math
+    torch = pytest.importorskip("torch")
+    from mamba_selective_ssm_ssd_amd import capi, mixer
+    rc, got_s, got_t = capi.m3_ssm_prefill_backward_plan(mixer.make_shape(b, T, H, 64, 64, R, torch.bfloat16))
+    assert rc == capi.M3_OK
+    assert (got_s, got_t) == (S, tokens)
+    Q = 32 // R
+    assert got_t % Q == 0 and (got_s - 1) * got_t < T <= got_s * got_t
+    assert got_s == 1 or got_t >= 2 * Q
+    rc, _, _ = capi.m3_ssm_prefill_backward_plan(mixer.make_shape(b, T, H, 64, 5, R, torch.bfloat16))
+    assert rc == capi.M3_ERR_INVALID_ARGUMENT

@@ -177,3 +177,24 @@ def test_backward_chains_over_split_calls(N, P, R, io, T1, T2, handoff):
     print(f"split N{N} P{P} R{R} {io} {T1}+{T2}: " + " ".join(f"{k} {v:.1e}" for k, v in errs.items()))
     for k, v in errs.items():
         assert v <= BAR, f"gradient of {k}: error {v:.3e} > {BAR}"
+
+
+@pytest.mark.parametrize("N,P,R,io,T", [
+    (32, 32, 2, "f32", 1000), (64, 64, 4, "bf16", 600), (16, 16, 1, "f32", 2000), (128, 32, 3, "bf16", 500),
+])
+@pytest.mark.parametrize("with_init", [False, True])
+def test_backward_split_sequence(N, P, R, io, T, with_init):
+    """One sequence cut into 20 or more segments (one workgroup each): the
+    state entering each segment comes from the earlier segments' aggregates,
+    the gradient leaving it from the later segments' adjoint aggregates, and
+    the dtheta suffix sums and the boundary tokens' delta gradients are
+    completed afterwards.  With a carried state the incoming final-state
+    gradients are given too, so every cross-segment term is exercised."""
+    from mamba_selective_ssm_ssd_amd import capi, mixer
+    rc, S, L = capi.m3_ssm_prefill_backward_plan(mixer.make_shape(1, T, 1, P, N, R, torch_io(io)))
+    assert rc == capi.M3_OK and S >= 20, (S, L)
+    errs = _run(1, T, 1, P, N, R, io, seed=11 * R + T, with_init=with_init, with_gfinal=with_init)
+    print(f"split backward N{N} P{P} R{R} {io} T{T} ({S} segments of {L} tokens) init={with_init}: "
+          + " ".join(f"{k} {v:.1e}" for k, v in errs.items()))
+    for k, v in errs.items():
+        assert v <= BAR, f"gradient of {k}: error {v:.3e} > {BAR}"
