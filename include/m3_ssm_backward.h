@@ -63,9 +63,9 @@ typedef struct {
  * when batch * H is below 256 and the sequence has at least four chunks of
  * 32 / R tokens (at most 64 segments, at least two chunks each); 1 segment
  * otherwise.  A split sequence takes three more launches: the segments'
- * aggregates (the state at each segment's end from a zero start, and the
- * gradient of the state at each segment's start from a zero gradient at its
- * end, with the summed log decay and angle), folded into each segment's
+ * aggregates, per piece of a segment (the state at the piece's end from a
+ * zero start, and the gradient of the state at its start from a zero
+ * gradient at its end, with the summed log decay and angle), folded into each segment's
  * starting state and incoming gradient as in the chunked algorithm's
  * inter-chunk state passing (the "20.2 Mamba and S6" page, section 2); and a
  * fix-up that adds the later segments' summed angle gradients to each
@@ -80,8 +80,10 @@ m3_status_t m3_ssm_prefill_backward_plan(const m3_shape_t *shape, int32_t *segme
  * and the angle there in fp64, so the size grows with the sequence:
  * batch * H * ceil(T / (32 / R)) * (N * P * 4 + N / 2 * 8) bytes, plus
  * alignment, 4 bytes per (batch, head, segment) and, for split sequences,
- * batch * H * segments * (2 N P * 4 + 8 + N * 8) bytes of segment
- * aggregates.  The workspace is caller-owned and needs no initialisation. */
+ * batch * H * segments * (p * (8 N P + 4 + 4 N) + 4 + 4 N) bytes of segment
+ * aggregates, with p (1 to 8) the pieces each segment's aggregates are cut
+ * into so that their launch fills whole rounds of the compute units.  The
+ * workspace is caller-owned and needs no initialisation. */
 size_t m3_ssm_prefill_backward_workspace_bytes(const m3_shape_t *shape);
 
 /*

@@ -181,28 +181,37 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
     };
     lane_ids();
     // workgroup -> (b, h, segment) and its role: 0 the gradients of the
-    // segment, 1 its forward-state aggregate, 2 its adjoint aggregate
-    const int S = p.S;
+    // segment, 1 the forward-state aggregate of one piece of a segment, 2 the
+    // adjoint aggregate of one piece (a segment's aggregates are cut into KA
+    // pieces of cps / KA chunks, so that the aggregate launch fills whole
+    // rounds of the CUs)
+    const int S = p.S, KA = p.kagg, NPC = S * KA; // pieces per sequence
     int64_t bh;
-    int sg, role;
+    int sg, role, pi = 0;
     if (p.mode == 0) {
         bh = blockIdx.x / S;
         sg = int(blockIdx.x % S);
         role = 0;
     } else {
-        const int64_t nf = int64_t(S - 1) * p.batch * p.H;
+        const int64_t nf = int64_t(S - 1) * KA * p.batch * p.H;
         int64_t idx = blockIdx.x;
         role = idx < nf ? 1 : 2;
         if (role == 2) idx -= nf;
-        bh = idx / (S - 1);
-        sg = int(idx % (S - 1)) + (role == 2 ? 1 : 0);
+        bh = idx / ((S - 1) * KA);
+        pi = int(idx % ((S - 1) * KA)) + (role == 2 ? KA : 0);
+        sg = pi / KA;
     }
     const int h = int(bh % p.H);
     const int64_t b = bh / p.H;
     const int64_t T = p.T;
     const int nC = p.nC;
-    const int c0 = sg * p.cps, c1 = min(nC, c0 + p.cps); // this segment's chunks
-    const int64_t bs = bh * S + sg;                        // (b, h, segment) index
+    // this workgroup's chunks: the segment's, or one piece of it (possibly
+    // empty past the end of a shorter last segment)
+    const int cpp = p.cps / KA;
+    const int c0 = role == 0 ? sg * p.cps : min(nC, sg * p.cps + (pi % KA) * cpp);
+    const int c1 = role == 0 ? min(nC, c0 + p.cps) : min(nC, c0 + cpp);
+    const int64_t bs = bh * S + sg;          // (b, h, segment) index
+    const int64_t bp = int64_t(bh) * NPC + pi; // (b, h, piece) index of the aggregates
     const float Ah = p.A[h];
     const IO *xg = static_cast<const IO *>(p.x), *Bg = static_cast<const IO *>(p.B);
     const IO *Cg = static_cast<const IO *>(p.C), *gyg = static_cast<const IO *>(p.gy);
@@ -404,9 +413,9 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
     };
     // the angle Phi before segment sg's first chunk: Phi_{-1} plus the
     // summed theta of the segments before it
-    auto phi_start = [&](int k, int upto) {
+    auto phi_start = [&](int k, int upto) { // upto: pieces
         double a = p.has_init ? double(p.phi0[bh * K + k]) : 0.0;
-        for (int s2 = 0; s2 < upto; ++s2) a += p.segTh[(bh * S + s2) * K + k];
+        for (int s2 = 0; s2 < upto; ++s2) a += p.segTh[(int64_t(bh) * NPC + s2) * K + k];
         return a;
     };
 
@@ -423,7 +432,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
             for (int pb = 0; pb < PB; ++pb) Ga[q][pb] = zero4();
         float lsum = 0.f;
         if (tid < K) PHE[tid] = 0.0;
-        issue(int64_t(c0) * Q, int(min<int64_t>(T - int64_t(c0) * Q, Q)), true);
+        if (c0 < c1) issue(int64_t(c0) * Q, int(min<int64_t>(T - int64_t(c0) * Q, Q)), true);
         __syncthreads();
         for (int c = c0; c < c1; ++c) {
             lane_ids();
@@ -465,7 +474,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
         }
         if (w >= 4) {
             const int wb = w - 4;
-            float *out = p.segGa + bs * int64_t(N) * P;
+            float *out = p.segGa + bp * int64_t(N) * P;
 #pragma unroll
             for (int q = 0; q < NBW; ++q) {
                 const int nb = wb + 4 * q;
@@ -475,7 +484,12 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
                     *reinterpret_cast<floatx4 *>(out + (nb * 16 + li) * P + pb * 16 + 4 * lg) = Ga[q][pb];
             }
         }
-        if (sg == S - 1 && tid == 0) p.segg[bs] = lsum; // the other segments' sums come from role 1
+        // the last segment's pieces record their sums (the other pieces' come
+        // from role 1)
+        if (sg == S - 1) {
+            if (tid == 0) p.segg[bp] = lsum;
+            if (tid < K) p.segTh[bp * K + tid] = PHE[tid];
+        }
         return;
     }
 
@@ -514,8 +528,8 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
                 }
                 if (sg > 0) {
                     double ph = p.has_init ? double(p.phi0[bh * K + (n >> 1)]) : 0.0;
-                    for (int s2 = 0; s2 < sg; ++s2) {
-                        const int64_t o = bh * S + s2;
+                    for (int s2 = 0; s2 < sg * KA; ++s2) {
+                        const int64_t o = int64_t(bh) * NPC + s2;
                         const float eg = __expf(p.segg[o]);
                         const float *A = p.segA + o * int64_t(N) * P;
 #pragma unroll
@@ -525,10 +539,10 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
                 }
                 Hf[q][pb] = floatx4{hh[0], hh[1], hh[2], hh[3]};
             }
-        if (tid < K) PHE[tid] = role == 0 ? phi_start(tid, sg) : 0.0;
+        if (tid < K) PHE[tid] = role == 0 ? phi_start(tid, sg * KA) : 0.0;
     }
     float gsum = 0.f; // role 1: summed log decay of the segment
-    issue(int64_t(c0) * Q, int(min<int64_t>(T - int64_t(c0) * Q, Q)), false);
+    if (c0 < c1) issue(int64_t(c0) * Q, int(min<int64_t>(T - int64_t(c0) * Q, Q)), false);
     __syncthreads();
     for (int c = c0; c < c1; ++c) {
         lane_ids();
@@ -587,7 +601,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
     if (role == 1) {
         // forward aggregate of segment sg: its state at the end from zero (frame
         // of its start), summed log decay and summed angle
-        float *out = p.segA + bs * int64_t(N) * P;
+        float *out = p.segA + bp * int64_t(N) * P;
 #pragma unroll
         for (int q = 0; q < NBH; ++q)
 #pragma unroll
@@ -595,8 +609,8 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
                 const int nb = w + kBwdWaves * q;
                 if (nb < NB) *reinterpret_cast<floatx4 *>(out + (nb * 16 + li) * P + pb * 16 + 4 * lg) = Hf[q][pb];
             }
-        if (tid == 0) p.segg[bs] = gsum;
-        if (tid < K) p.segTh[bs * K + tid] = PHE[tid];
+        if (tid == 0) p.segg[bp] = gsum;
+        if (tid < K) p.segTh[bp * K + tid] = PHE[tid];
         return;
     }
 
@@ -618,9 +632,9 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
     if (sg < S - 1) {
         auto gend = [&](int n, int pc) {
             float v = p.ghT ? p.ghT[(bh * N + n) * int64_t(P) + pc] : 0.f;
-            double ph = phi_start(n >> 1, S - 1);
-            for (int s2 = S - 1; s2 > sg; --s2) {
-                const int64_t o = bh * S + s2;
+            double ph = phi_start(n >> 1, NPC - 1);
+            for (int s2 = NPC - 1; s2 >= (sg + 1) * KA; --s2) {
+                const int64_t o = int64_t(bh) * NPC + s2;
                 v = __expf(p.segg[o]) * v + rot_el(p.segGa + o * int64_t(N) * P, n, pc, ph);
                 ph -= p.segTh[(o - 1) * K + (n >> 1)];
             }
@@ -1154,18 +1168,23 @@ static __global__ void k_backward_gA(const BwdParams p) {
     p.gA[h] = s;
 }
 
-// Split sequences, after the segments' gradients: per (b, h, segment sg)
+// Split sequences, after the segments' gradients: per (b, h, segment sg),
+// kFixParts workgroups each taking a share of the segment's tokens:
 //  * dtheta of every token of an earlier segment += dPhi_T's gradient plus
 //    the summed dPhi of the later segments (the suffix sums the segment began
-//    at zero);
+//    at zero), the K carries computed once into LDS;
 //  * the first token of a later segment: the gradient of its delta from the
 //    segment before (delta = (1 - lam) dt) into its dt and lam;
 //  * dPhi_{-1} = dPhi_T's gradient plus every segment's sum (segment 0).
+constexpr int kFixParts = 8;
 template <typename IO>
 __global__ __launch_bounds__(256) void k_backward_fix(const BwdParams p) {
+    __shared__ float carry[128]; // K <= 64
     const int S = p.S, K = p.K;
-    const int64_t bh = blockIdx.x / S;
-    const int sg = int(blockIdx.x % S);
+    const int part = int(blockIdx.x % kFixParts);
+    const int64_t bs = blockIdx.x / kFixParts;
+    const int64_t bh = bs / S;
+    const int sg = int(bs % S);
     const int h = int(bh % p.H);
     const int64_t b = bh / p.H;
     const int Q = kBwdV / p.R;
@@ -1176,16 +1195,22 @@ __global__ __launch_bounds__(256) void k_backward_fix(const BwdParams p) {
         return a;
     };
     if (sg < S - 1) {
-        const int64_t n = (t1 - t0) * K;
-        for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
-            const int64_t t = t0 + i / K;
-            const int k = int(i % K);
-            // the carry is recomputed per element: S is small, and K consecutive
-            // threads share each k's sums (cached)
-            p.gtheta[((b * p.T + t) * p.H + h) * K + k] += float(carry_from(k, sg + 1));
+        for (int k = threadIdx.x; k < K; k += blockDim.x) carry[k] = float(carry_from(k, sg + 1));
+        __syncthreads();
+        // this part's tokens; rows of K floats, float4 along k (K % 8 == 0)
+        const int64_t nt = t1 - t0, per = (nt + kFixParts - 1) / kFixParts;
+        const int64_t ta = t0 + part * per, tb = min(t1, ta + per);
+        const int K4 = K / 4;
+        for (int64_t i = threadIdx.x; i < (tb - ta) * K4; i += blockDim.x) {
+            const int64_t t = ta + i / K4;
+            const int k = 4 * int(i % K4);
+            float4 *g = reinterpret_cast<float4 *>(p.gtheta + ((b * p.T + t) * p.H + h) * K + k);
+            float4 v = *g;
+            v.x += carry[k]; v.y += carry[k + 1]; v.z += carry[k + 2]; v.w += carry[k + 3];
+            *g = v;
         }
     }
-    if (sg > 0 && threadIdx.x == 0) {
+    if (part == 0 && sg > 0 && threadIdx.x == 0) {
         const int64_t o = (b * p.T + t0) * p.H + h;
         const float dd = p.segdd[bh * S + sg];
         const float dtv = io<IO>::get(static_cast<const IO *>(p.dt) + o);
@@ -1193,7 +1218,7 @@ __global__ __launch_bounds__(256) void k_backward_fix(const BwdParams p) {
         p.gdt[o] += dd * (1.f - lmv);
         p.glam[o] -= dd * dtv;
     }
-    if (sg == 0 && p.has_init && p.gphi0)
+    if (part == 0 && sg == 0 && p.has_init && p.gphi0)
         for (int k = threadIdx.x; k < K; k += blockDim.x) p.gphi0[bh * K + k] = float(carry_from(k, 0));
 }
 
@@ -1211,7 +1236,7 @@ hipError_t launch_backward_inst(const BwdParams &p, hipStream_t s) {
         // segment aggregates: forward state of segments 0 .. S-2, adjoint of 1 .. S-1
         BwdParams pa = p;
         pa.mode = 1;
-        hipLaunchKernelGGL((k_backward<IO, N, P, R>), dim3(unsigned(2 * (p.S - 1) * nbh)), dim3(kBwdThreads), Cf::bytes,
+        hipLaunchKernelGGL((k_backward<IO, N, P, R>), dim3(unsigned(2 * (p.S - 1) * p.kagg * nbh)), dim3(kBwdThreads), Cf::bytes,
                            s, pa);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
@@ -1220,7 +1245,7 @@ hipError_t launch_backward_inst(const BwdParams &p, hipStream_t s) {
     hipLaunchKernelGGL((k_backward<IO, N, P, R>), dim3(unsigned(p.S * nbh)), dim3(kBwdThreads), Cf::bytes, s, pm);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (p.S > 1) {
-        hipLaunchKernelGGL((k_backward_fix<IO>), dim3(unsigned(p.S * nbh)), dim3(256), 0, s, p);
+        hipLaunchKernelGGL((k_backward_fix<IO>), dim3(unsigned(p.S * nbh * kFixParts)), dim3(256), 0, s, p);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     hipLaunchKernelGGL(k_backward_gA, dim3(unsigned((p.H + 255) / 256)), dim3(256), 0, s, p);

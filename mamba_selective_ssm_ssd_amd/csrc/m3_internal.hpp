@@ -94,12 +94,14 @@ struct BwdParams {
     // mode 0: the gradients of each (b, h, segment); mode 1: the segment
     // aggregates, (S - 1) b H workgroups of forward state (segments 0 .. S-2)
     // then as many of adjoint state (segments 1 .. S-1).
-    int32_t S, cps, mode;
-    float *segA;     // [b][H][S][N][P] state at a segment's end from zero, frame of its start
-    float *segGa;    // [b][H][S][N][P] adjoint at a segment's start from zero at its end, same frame
-    float *segg;     // [b][H][S] summed log decay of a segment
+    // The aggregates are taken per piece: kagg pieces of cps / kagg chunks per
+    // segment, S kagg pieces per sequence.
+    int32_t S, cps, mode, kagg;
+    float *segA;     // [b][H][S kagg][N][P] state at a piece's end from zero, frame of its start
+    float *segGa;    // [b][H][S kagg][N][P] adjoint at a piece's start from zero at its end, same frame
+    float *segg;     // [b][H][S kagg] summed log decay of a piece
     float *segdd;    // [b][H][S] gradient of delta of a segment's first token from the segment before
-    double *segTh;   // [b][H][S][K] summed theta of a segment (wrapped)
+    double *segTh;   // [b][H][S kagg][K] summed theta of a piece (wrapped)
     double *segDphi; // [b][H][S][K] summed dPhi of a segment
 };
 

@@ -167,7 +167,7 @@ WorkspaceLayout layout(const m3_shape_t *s) {
 // segments), one workgroup per (b, h, segment), so that the grid fills the
 // 256 CUs; S = 1 otherwise.
 struct BwdPlan {
-    int32_t S, cps;
+    int32_t S, cps, kagg; // kagg: pieces per segment of the aggregate launch
 };
 BwdPlan bwd_plan(const m3_shape_t *s) {
     const int64_t bh = int64_t(s->batch) * s->nheads;
@@ -175,9 +175,18 @@ BwdPlan bwd_plan(const m3_shape_t *s) {
     const int64_t nC = (int64_t(s->seqlen) + Q - 1) / Q;
     int64_t S = 1;
     if (bh < 256) S = std::min<int64_t>({(256 + bh - 1) / bh, nC / 2, 64});
-    if (S < 2) return {1, int32_t(nC)};
+    if (S < 2) return {1, int32_t(nC), 1};
     const int64_t cps = (nC + S - 1) / S;
-    return {int32_t((nC + cps - 1) / cps), int32_t(cps)};
+    S = (nC + cps - 1) / cps;
+    // the aggregate launch has 2 (S - 1) b H jobs of a segment each; cut them
+    // into pieces so that the launch fills whole rounds of the 256 CUs
+    int32_t kagg = 1;
+    for (int32_t k = 1; k <= 8; k *= 2)
+        if ((2 * (S - 1) * bh * k) % 256 == 0 && cps % k == 0) {
+            kagg = k;
+            break;
+        }
+    return {int32_t(S), int32_t(cps), kagg};
 }
 
 // Backward workspace: the state and angle entering each chunk, the
@@ -191,17 +200,18 @@ BwdLayout bwd_layout(const m3_shape_t *s) {
     const size_t Q = size_t(m3::kBwdV / s->rank);
     const size_t nC = (size_t(s->seqlen) + Q - 1) / Q;
     const size_t N = size_t(s->dstate), P = size_t(s->headdim), K = N / 2;
-    const size_t S = size_t(bwd_plan(s).S), nseg = S > 1 ? bh * S : 0;
+    const BwdPlan plan = bwd_plan(s);
+    const size_t S = size_t(plan.S), nseg = S > 1 ? bh * S : 0, npc = nseg * size_t(plan.kagg);
     BwdLayout w;
     size_t off = 0;
     w.ck_h = off; off += round_up(bh * nC * N * P * sizeof(float));
     w.ck_phi = off; off += round_up(bh * nC * K * sizeof(double));
     w.gA = off; off += round_up(bh * S * sizeof(float));
-    w.segA = off; off += round_up(nseg * N * P * sizeof(float));
-    w.segGa = off; off += round_up(nseg * N * P * sizeof(float));
-    w.segg = off; off += round_up(nseg * sizeof(float));
+    w.segA = off; off += round_up(npc * N * P * sizeof(float));
+    w.segGa = off; off += round_up(npc * N * P * sizeof(float));
+    w.segg = off; off += round_up(npc * sizeof(float));
     w.segdd = off; off += round_up(nseg * sizeof(float));
-    w.segTh = off; off += round_up(nseg * K * sizeof(double));
+    w.segTh = off; off += round_up(npc * K * sizeof(double));
     w.segDphi = off; off += round_up(nseg * K * sizeof(double));
     w.total = off;
     return w;
@@ -553,6 +563,7 @@ m3_status_t m3_ssm_prefill_backward_ex(const m3_shape_t *shape, const void *x, c
     const BwdPlan plan = bwd_plan(shape);
     p.S = plan.S;
     p.cps = plan.cps;
+    p.kagg = plan.kagg;
     p.segA = reinterpret_cast<float *>(ws + w.segA);
     p.segGa = reinterpret_cast<float *>(ws + w.segGa);
     p.segg = reinterpret_cast<float *>(ws + w.segg);

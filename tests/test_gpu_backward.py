@@ -198,3 +198,19 @@ def test_backward_split_sequence(N, P, R, io, T, with_init):
           + " ".join(f"{k} {v:.1e}" for k, v in errs.items()))
     for k, v in errs.items():
         assert v <= BAR, f"gradient of {k}: error {v:.3e} > {BAR}"
+
+
+@pytest.mark.parametrize("T", [512, 480])
+def test_backward_split_with_aggregate_pieces(T):
+    """32 sequences of 64 (T = 512) or 60 (T = 480) chunks of 8 tokens: 8
+    segments each, whose aggregates are cut into 4 pieces so that their launch
+    (2 x 7 x 32 x 4 = 1792 workgroups) fills whole rounds of the compute
+    units; with T = 480 the last segment is half as long and its last pieces
+    are empty.  Carried state and final-state gradients included."""
+    from mamba_selective_ssm_ssd_amd import capi, mixer
+    rc, S, L = capi.m3_ssm_prefill_backward_plan(mixer.make_shape(1, T, 32, 64, 64, 4, torch.bfloat16))
+    assert rc == capi.M3_OK and (S, L) == (8, 64)
+    errs = _run(1, T, 32, 64, 64, 4, "bf16", seed=T, with_init=True, with_gfinal=True)
+    print(f"split backward with pieces T{T}: " + " ".join(f"{k} {v:.1e}" for k, v in errs.items()))
+    for k, v in errs.items():
+        assert v <= BAR, f"gradient of {k}: error {v:.3e} > {BAR}"
