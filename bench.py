@@ -632,7 +632,7 @@ def main():
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the mixer shards over (batch, head) with no communication; see DESIGN.md).",
+              "(the mixer would shard over (batch, head) with no communication between GPUs).",
               file=sys.stderr)
         sys.exit(2)
 
