@@ -619,6 +619,10 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
     // bf16 I/O with a wave free of intra-chunk rows: that wave scans the next
     // chunk's coefficients in the second phase instead of the first
     constexpr bool CP2 = C::MFP && C::FREEW > 0;
+    // the pre-pass has no intra-chunk product, so it stages B~ already scaled
+    // by the chunk-end factors (a multiply per value while the row is in
+    // registers) and takes x as it is, instead of a scaled copy of x
+    constexpr bool BSC = !OUT;
 
     // workgroup -> (b, h, segment); consecutive indices li land on the same
     // XCD.  Output pass: S segments per sequence, li = bh S + seg (the few
@@ -818,6 +822,11 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
                         rot_neg(a.z, a.w, ec[4 * w4 + 2], ec[4 * w4 + 3]);
                     }
                 }
+                if constexpr (BSC) {
+                    const float sc = scl_s[v / R];
+#pragma unroll
+                    for (int i = 0; i < EPU; ++i) e[i] *= sc;
+                }
                 st_planes<PL, C::BS_PS, EPU>(bs + v * NBP + q * EPU, e);
                 if constexpr (OUT && C::CL) st_planes<PL, C::BS_PS, EPU>(cl + v * NBP + q * EPU, ec);
             } else {
@@ -837,7 +846,7 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
                     st_planes<PL, C::X_PS, EPU>(xr + v * PP + q * EPU, e);
                 __builtin_amdgcn_sched_barrier(0);
                 load_chunk<C, IO, OUT, 2, j>(p, b, h, hg, tn0, Tn, raw);
-                if constexpr (C::XS) {
+                if constexpr (C::XS && !BSC) {
                     const float sc = scl_s[v / R];
 #pragma unroll
                     for (int ee = 0; ee < EPU; ++ee) e[ee] *= sc;
@@ -1232,11 +1241,11 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
             floatx4 acc[C::TW];
 #pragma unroll
             for (int j = 0; j < C::TW; ++j) acc[j] = st[j] * eg;
-            const uint16_t *bp = (C::XS ? xs : xr) + ra * PP + 16 * pt + ca;
+            const uint16_t *bp = ((C::XS && !BSC) ? xs : xr) + ra * PP + 16 * pt + ca;
 #pragma unroll 2
             for (int ks = 0; ks < V / 32; ++ks) {
                 frag bf = M::template tr8<C::X_PS>(bp + 32 * ks * PP, bp + (32 * ks + 16) * PP);
-                if constexpr (!C::XS) {
+                if constexpr (!C::XS && !BSC) {
                     float f[8];
                     M::unpack(bf, f);
 #pragma unroll
