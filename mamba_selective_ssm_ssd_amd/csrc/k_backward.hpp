@@ -233,7 +233,8 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
     uint32_t qth[KP][TPS], qdt = 0, qlm = 0;
     // (addresses: the chunk's first token + a 32-bit offset; token i of the
     // chunk is i * H rows further)
-    auto issue = [&](int64_t t0, int Tc, bool bwd) {
+    // (adj: only what the adjoint aggregate reads: C, gy and the scalars)
+    auto issue = [&](int64_t t0, int Tc, bool bwd, bool adj) {
         const int64_t tb = tok(t0);
         const int HR = p.H * R;
         const IO *bb = Bg + tb * (R * N), *cb = Cg + tb * (R * N), *xb = xg + tb * (R * P), *gb = gyg + tb * (R * P);
@@ -243,7 +244,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
             const int v = gi % V, n = 4 * (gi / V), i = v / R;
             const bool ok = gi < V * N / 4 && v < VQ && i < Tc;
             const int off = ok ? (i * HR + v - i * R) * N + n : 0;
-            qb[j] = io4<IO>::load(bb + off);
+            if (!adj) qb[j] = io4<IO>::load(bb + off);
             if (bwd) qc[j] = io4<IO>::load(cb + off);
         }
 #pragma unroll
@@ -252,7 +253,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
             const int v = gi % V, pc = 4 * (gi / V), i = v / R;
             const bool ok = gi < V * P / 4 && v < VQ && i < Tc;
             const int off = ok ? (i * HR + v - i * R) * P + pc : 0;
-            qx[j] = io4<IO>::load(xb + off);
+            if (!adj) qx[j] = io4<IO>::load(xb + off);
             if (bwd) qg[j] = io4<IO>::load(gb + off);
         }
         const IO *tbp = thg + tb * K;
@@ -369,15 +370,15 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
     };
     // x (and gy) of the chunk into LDS: the forward sweep keeps x transposed
     // (T2); the backward sweep keeps x row-major (XN) and gy both ways (GN, T2)
-    auto stage_xg = [&](int Tc, bool fwd, float *xT) {
+    auto stage_xg = [&](int Tc, bool fwd, float *xT, bool adj = false) {
 #pragma unroll
         for (int j = 0; j < NXL; ++j) {
             const int gi = tid + j * kBwdThreads;
             if (gi >= V * P / 4) continue;
             const int v = gi % V, pc = 4 * (gi / V), i = v / R;
             const bool ok = v < VQ && i < Tc;
-            float xv[4], gv[4];
-            io4<IO>::unpack(qx[j], xv);
+            float xv[4] = {0.f, 0.f, 0.f, 0.f}, gv[4];
+            if (!adj) io4<IO>::unpack(qx[j], xv);
             if (!fwd) io4<IO>::unpack(qg[j], gv);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -388,7 +389,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) xT[(pc + q) * pV + v] = xv[q];
             } else {
-                *reinterpret_cast<float4 *>(XN + v * pP + pc) = make_float4(xv[0], xv[1], xv[2], xv[3]);
+                if (!adj) *reinterpret_cast<float4 *>(XN + v * pP + pc) = make_float4(xv[0], xv[1], xv[2], xv[3]);
                 *reinterpret_cast<float4 *>(GN + v * pP + pc) = make_float4(gv[0], gv[1], gv[2], gv[3]);
 #pragma unroll
                 for (int q = 0; q < 4; ++q) T2[(pc + q) * pV + v] = gv[q];
@@ -432,7 +433,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
             for (int pb = 0; pb < PB; ++pb) Ga[q][pb] = zero4();
         float lsum = 0.f;
         if (tid < K) PHE[tid] = 0.0;
-        if (c0 < c1) issue(int64_t(c0) * Q, int(min<int64_t>(T - int64_t(c0) * Q, Q)), true);
+        if (c0 < c1) issue(int64_t(c0) * Q, int(min<int64_t>(T - int64_t(c0) * Q, Q)), true, true);
         __syncthreads();
         for (int c = c0; c < c1; ++c) {
             lane_ids();
@@ -440,7 +441,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
             const int Tc = int(min<int64_t>(T - t0, Q));
             stage_scalars(t0, Tc);
             stage_angles(Tc, true, c, false);
-            stage_xg(Tc, false, nullptr);
+            stage_xg(Tc, false, nullptr, true);
             __syncthreads();
             rot_store(qc, Tc, CT, nullptr);
             const float dec = __expf(lsum);
@@ -448,7 +449,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
             float ev[VB][4];
             row_factor(Cf::s_E, ev);
             __syncthreads();
-            if (c + 1 < c1) issue(t0 + Q, int(min<int64_t>(T - t0 - Q, Q)), true);
+            if (c + 1 < c1) issue(t0 + Q, int(min<int64_t>(T - t0 - Q, Q)), true, true);
             if (w >= 4) {
                 const int wb = w - 4;
 #pragma unroll
@@ -542,7 +543,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
         if (tid < K) PHE[tid] = role == 0 ? phi_start(tid, sg * KA) : 0.0;
     }
     float gsum = 0.f; // role 1: summed log decay of the segment
-    if (c0 < c1) issue(int64_t(c0) * Q, int(min<int64_t>(T - int64_t(c0) * Q, Q)), false);
+    if (c0 < c1) issue(int64_t(c0) * Q, int(min<int64_t>(T - int64_t(c0) * Q, Q)), false, false);
     __syncthreads();
     for (int c = c0; c < c1; ++c) {
         lane_ids();
@@ -570,7 +571,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
         float uv[VB][4];
         row_factor(Cf::s_U, uv);
         __syncthreads();
-        if (c + 1 < c1) issue(t0 + Q, int(min<int64_t>(T - t0 - Q, Q)), false);
+        if (c + 1 < c1) issue(t0 + Q, int(min<int64_t>(T - t0 - Q, Q)), false, false);
         // H^T[p][n] <- e^{ec_end} H^T + sum_v x[v][p] U_v B~[v][n]
         {
 #pragma unroll
@@ -689,7 +690,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
     bool pend = false;   // wave 0, lane 0: the later chunk's first token awaits its d(delta)
     float pd_g = 0.f, pd_l = 0.f, pd_dt = 0.f, pd_lam = 0.f;
     int64_t pd_tok = 0;
-    issue(int64_t(c1 - 1) * Q, int(min<int64_t>(T - int64_t(c1 - 1) * Q, Q)), true);
+    issue(int64_t(c1 - 1) * Q, int(min<int64_t>(T - int64_t(c1 - 1) * Q, Q)), true, false);
     for (int c = c1 - 1; c >= c0; --c) {
         lane_ids();
         const int64_t t0 = int64_t(c) * Q;
@@ -805,7 +806,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
         // the previous chunk's inputs, in flight during the products (the first
         // group, whose products are fewer, prefetches now, the second after its
         // products)
-        if (c > c0 && w < 4) issue(t0 - Q, Q, true);
+        if (c > c0 && w < 4) issue(t0 - Q, Q, true, false);
         // ---- per token j (8 threads each): row sums of dW.W and column sums
         // of dW.e^{ec_i - ec_j} off the diagonal, and dW(j, j); dW(i, j) is
         // the sum of S.D over the R x R block of the token pair
@@ -987,7 +988,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
         pz += __shfl_xor(pz, 16);
         pz += __shfl_xor(pz, 32);
         if (lane == 0) PZ[wb * 4] = pz;
-        if (c > c0) issue(t0 - Q, Q, true);
+        if (c > c0) issue(t0 - Q, Q, true, false);
         }
         __syncthreads();
         // ---- the scalars (wave 0, lane = token)
