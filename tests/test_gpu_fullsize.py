@@ -117,3 +117,32 @@ def test_siso_backward_full_size():
 
 def test_mimo_backward_full_size():
     _check_backward(2, [(1, 9), (2, 50)])
+
+
+@pytest.mark.parametrize("H,N,P,R,T", [
+    (2 ** 31 // (64 * 1 * 128) - 1, 128, 64, 1, 64),   # SISO, 64-token chunks: in-chunk offsets up to 2.11e9
+    (2 ** 31 // (64 * 4 * 64) - 1, 64, 64, 4, 32),     # MIMO, 16-token chunks
+])
+def test_prefill_at_the_largest_accepted_head_count(H, N, P, R, T):
+    """The largest number of heads the shape check accepts (64 H R max(N, P)
+    just below 2^31, the bound of the 32-bit offsets inside a chunk): every
+    head is computed, and the first and last heads (whose offsets are the
+    largest) match the oracle."""
+    from mamba_selective_ssm_ssd_amd import capi, mixer
+    shape = mixer.make_shape(1, T, H, P, N, R, torch.bfloat16)
+    assert capi.m3_ssm_prefill_workspace_bytes(shape) > 0
+    assert capi.m3_ssm_prefill_workspace_bytes(mixer.make_shape(1, T, H + 1, P, N, R, torch.bfloat16)) == 0
+    inp = synth.torch_inputs(1, T, H, P, N, R, io="bf16", seed=3)
+    y, st = mixer.prefill(*(inp[k] for k in ("x", "dt", "A", "lam", "theta", "B", "C")))
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(y).all())
+    for hi in (0, H // 2, H - 1):
+        d = _sample_inputs(inp, 0, hi)
+        yr, hT, _ = oracle.run(d["x"], d["dt"], d["A"], d["lam"], d["theta"], d["B"], d["C"])
+        e = slice_err(y[0:1, :, hi:hi + 1].double().cpu().numpy(), yr, (0, 2))
+        hg = oracle.state_to_true(st.h[0:1, hi:hi + 1].double().cpu().numpy(), oracle.cumulative_angle(d["theta"]))
+        eh = slice_err(hg, hT, (0, 1))
+        print(f"H={H} N{N} P{P} R{R} head {hi}: y err {e:.2e}, state err {eh:.2e}")
+        assert e <= TOL["bf16"] and eh <= TOL["bf16"]
+    del inp, y, st
+    torch.cuda.empty_cache()
