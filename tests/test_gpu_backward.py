@@ -214,3 +214,31 @@ def test_backward_split_with_aggregate_pieces(T):
     print(f"split backward with pieces T{T}: " + " ".join(f"{k} {v:.1e}" for k, v in errs.items()))
     for k, v in errs.items():
         assert v <= BAR, f"gradient of {k}: error {v:.3e} > {BAR}"
+
+
+def test_backward_at_the_largest_accepted_head_count():
+    """SISO N128 P64 with the largest head count the shape check accepts
+    (262143 heads, T = 64): the whole batch runs on the GPU, and the first,
+    middle and last heads (whose 32-bit in-chunk offsets are the largest)
+    match the oracle's gradients."""
+    from mamba_selective_ssm_ssd_amd import capi, mixer
+    H, N, P, R, T = 2 ** 31 // (64 * 1 * 128) - 1, 128, 64, 1, 64
+    assert capi.m3_ssm_prefill_backward_workspace_bytes(mixer.make_shape(1, T, H, P, N, R, torch.bfloat16)) > 0
+    inp = synth.torch_inputs(1, T, H, P, N, R, io="bf16", seed=5)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(55)
+    gy = torch.randn(inp["x"].shape, generator=g, device="cuda").to(torch.bfloat16)
+    names = ("x", "dt", "A", "lam", "theta", "B", "C")
+    grads = mixer.backward(*(inp[k] for k in names), gy)
+    torch.cuda.synchronize()
+    for hi in (0, H // 2, H - 1):
+        d = {k: inp[k][:, :, hi:hi + 1].float().cpu().numpy() for k in names if k != "A"}
+        d["A"] = inp["A"][hi:hi + 1].cpu().numpy()
+        _, r = ob.grad(d, gy[:, :, hi:hi + 1].float().cpu().numpy())
+        errs = {k: slice_err(grads[k][:, :, hi:hi + 1].double().cpu().numpy(), r[k], AXES[k])
+                for k in ("x", "dt", "lam", "theta", "B", "C")}
+        print(f"backward H={H} head {hi}: " + " ".join(f"{k} {v:.1e}" for k, v in errs.items()))
+        for k, v in errs.items():
+            assert v <= BAR, f"head {hi}: gradient of {k}: error {v:.3e}"
+    del inp, gy, grads
+    torch.cuda.empty_cache()
