@@ -11,7 +11,7 @@
 // with alpha = exp(dt A), beta = (1 - lam) dt alpha, gamma = lam dt.
 //
 // Decode is bound by the read-modify-write of the fp32 state (N x P per
-// head).  Workgroups of 256 threads walk the (b, h) items grid-stride; each
+// head).  Workgroups of 128 or 256 threads walk the (b, h) items grid-stride; each
 // thread owns float4 runs along P of the state, so every state access is a
 // coalesced 16-byte access, and the state of the workgroup's next item is
 // loaded while the current one is computed, so state loads are always in
@@ -35,18 +35,34 @@
 namespace m3 {
 
 constexpr int kDecodeCus = 256; // compute units of an MI355X
-// Resident decode workgroups per compute unit: each holds the state of two
-// items (current and prefetched) in registers; a bf16 state takes half the
-// registers, so one more workgroup fits (measured: 75.0 vs 77.4 us per step
-// of the b256 H64 P64 N64 R4 decode).
-constexpr int decode_wg_per_cu(int N, int P, bool SB = false) {
-    return N * P > 4096 || (N > 64 && N * P >= 4096) ? 2 : (SB ? 5 : 4);
+// Threads per decode workgroup.  An item's step is a chain of phases
+// separated by two workgroup barriers, so two-wave workgroups (each thread
+// holding twice the state runs) put more items in flight per CU and wait on
+// fewer waves at each barrier, where their registers allow it: the plain
+// step with N <= 64 and N P <= 4096 (b256 H64 P64 N64 R4: 71.4 vs 74.9 us
+// per step with a bf16 state, 103.4 vs 104.2 with fp32).  The block step
+// and larger states would spill at that occupancy and keep four waves.
+constexpr int decode_threads(int N, int P, bool BLK) { return !BLK && N <= 64 && N * P <= 4096 ? 128 : 256; }
+// Resident waves per SIMD: each workgroup holds the state of two items
+// (current and prefetched) in registers; a bf16 state takes half the
+// registers, so more waves fit (256 threads: 75.0 vs 77.4 us per step of
+// the b256 H64 P64 N64 R4 decode at five waves instead of four).  The block
+// step's weights, biases and gate inputs take one wave fewer, which keeps
+// every instantiation free of register spills.
+constexpr int decode_waves_per_simd(int N, int P, bool BLK, bool SB) {
+    return N * P > 4096 || (N > 64 && N * P >= 4096) ? 2
+         : decode_threads(N, P, BLK) == 128 ? (SB ? 4 : 3)
+         : BLK ? (SB ? 4 : 3) : (SB && N <= 64 ? 5 : 4);
+}
+// Resident workgroups per CU (4 SIMDs).
+constexpr int decode_wg_per_cu(int N, int P, bool BLK, bool SB) {
+    return decode_waves_per_simd(N, P, BLK, SB) * 4 / (decode_threads(N, P, BLK) / kWave);
 }
 
-template <int N, int P>
+template <int N, int P, int DT>
 struct DecodeLds {
     static constexpr int K = N / 2, P4 = P / 4;
-    static constexpr int G = kThreads / P4; // row groups of the state
+    static constexpr int G = DT / P4; // row groups of the state
     // floats: bt, bp, ct [4][N]; x, xp [4][P]; phi' [K]; a 16-byte sink for
     // threads without a unit; red [G][4][P]
     static constexpr int o_bt = 0, o_bp = o_bt + 4 * N, o_ct = o_bp + 4 * N;
@@ -122,19 +138,20 @@ struct StateRun<true> {
 };
 
 template <typename IO, int N, int P, int R, bool BLK, bool SB>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode_wg_per_cu(N, P, SB)))) void k_decode_step(const DecodeParams p) {
+__global__ __launch_bounds__(decode_threads(N, P, BLK)) __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd(N, P, BLK, SB)))) void k_decode_step(const DecodeParams p) {
     typedef StateRun<SB> SR;
     typedef typename SR::raw HV;
-    typedef DecodeLds<N, P> L;
+    constexpr int DT = decode_threads(N, P, BLK);
+    typedef DecodeLds<N, P, DT> L;
     constexpr int K = N / 2, P4 = L::P4, G = L::G;
     constexpr int SZ = int(sizeof(IO)), EPU = 16 / SZ, NPU = EPU / 2;
     constexpr int SLOTS = N * P4;                          // float4 runs in the state
-    constexpr int SPT = (SLOTS + kThreads - 1) / kThreads; // runs per thread
+    constexpr int SPT = (SLOTS + DT - 1) / DT; // runs per thread
     constexpr int URN = N * SZ / 16, URP = P * SZ / 16;    // 16-byte units per row of B/C and of x
     constexpr int UB = R * URN, UX = R * URP, UPB = R * N / 4, UT = 2 * UB + 2 * UX + UPB;
-    constexpr int UPT = (UT + kThreads - 1) / kThreads;    // units per thread
+    constexpr int UPT = (UT + DT - 1) / DT;    // units per thread
     constexpr int64_t sB = int64_t(R) * N * SZ, sX = int64_t(R) * P * SZ, sBp = int64_t(R) * N * 4; // item strides
-    static_assert(!BLK || R * P <= 4 * kThreads, "one gated output quad per thread");
+    static_assert(!BLK || R * P <= 4 * DT, "one gated output quad per thread");
     __shared__ __align__(16) float sm[L::floats];
     float *bt_s = sm + L::o_bt, *bp_s = sm + L::o_bp, *ct_s = sm + L::o_ct;
     float *x_s = sm + L::o_x, *xp_s = sm + L::o_xp, *ph_s = sm + L::o_ph, *red = sm + L::o_red;
@@ -148,7 +165,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode
     const char *ubase[UPT];
 #pragma unroll
     for (int j = 0; j < UPT; ++j) {
-        const int u = tid + j * kThreads;
+        const int u = tid + j * DT;
         int kind, w;
         if (u < UB) kind = kUnitB, w = u;
         else if (u < 2 * UB) kind = kUnitC, w = u - UB;
@@ -175,7 +192,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode
     auto load_state = [&](int64_t item, HV *hv) {
         const HV *hs = static_cast<const HV *>(p.h) + item * SLOTS;
 #pragma unroll
-        for (int j = 0; j < SPT; ++j) hv[j] = hs[j * kThreads + tslot];
+        for (int j = 0; j < SPT; ++j) hv[j] = hs[j * DT + tslot];
     };
 
     // The small vectors of an item, as loaded (raw bits).  They are loaded one
@@ -292,15 +309,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode
         __syncthreads();
 
         // ---- carried small state: B~_prev <- B~, x_prev <- x, Phi <- Phi'
-        for (int w = tid; w < UPB; w += kThreads)
+        for (int w = tid; w < UPB; w += DT)
             *reinterpret_cast<float4 *>(p.prevB + item * R * N + 4 * w) = *reinterpret_cast<const float4 *>(bt_s + 4 * w);
-        for (int w = tid; w < UX; w += kThreads) {
+        for (int w = tid; w < UX; w += DT) {
             const float *s = x_s + w * EPU;
             IO *d = static_cast<IO *>(p.prevx) + item * R * P + w * EPU;
 #pragma unroll
             for (int i = 0; i < EPU; i += 4) io<IO>::store4(d + i, s + i);
         }
-        for (int k = tid; k < K; k += kThreads) p.phi[item * K + k] = ph_s[k];
+        for (int k = tid; k < K; k += DT) p.phi[item * K + k] = ph_s[k];
 
         // ---- state update and partial outputs
         const float dtv = io<IO>::value(dt_raw), lamv = io<IO>::value(lam_raw);
@@ -315,8 +332,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode
             for (int q = 0; q < 4; ++q) yp[i][q] = 0.f;
 #pragma unroll
         for (int j = 0; j < SPT; ++j) {
-            const int slot = tid + j * kThreads;
-            if (SLOTS % kThreads != 0 && slot >= SLOTS) continue;
+            const int slot = tid + j * DT;
+            if (SLOTS % DT != 0 && slot >= SLOTS) continue;
             const int n = slot / P4;
             const float4 hv = SR::unpack(hc[j]);
             float u[4] = {alpha * hv.x, alpha * hv.y, alpha * hv.z, alpha * hv.w};
@@ -347,7 +364,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode
         // y: four consecutive outputs per thread, one 4-element store
         IO *y = static_cast<IO *>(p.y) + item * R * P;
         constexpr int GACT = G < N ? G : N; // row groups that own at least one row
-        for (int o = 4 * tid; o < R * P; o += 4 * kThreads) {
+        for (int o = 4 * tid; o < R * P; o += 4 * DT) {
             const int i = o / P, pc = o - i * P;
             float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
@@ -413,8 +430,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode
 template <typename IO, int N, int P, int R, bool BLK, bool SB>
 hipError_t launch_decode_inst(const DecodeParams &p, hipStream_t s) {
     const int64_t bh = p.batch * p.H;
-    const int64_t cap = int64_t(kDecodeCus) * decode_wg_per_cu(N, P, SB);
-    const dim3 grid{static_cast<unsigned>(bh < cap ? bh : cap)}, block{kThreads};
+    const int64_t cap = int64_t(kDecodeCus) * decode_wg_per_cu(N, P, BLK, SB);
+    const dim3 grid{static_cast<unsigned>(bh < cap ? bh : cap)}, block{unsigned(decode_threads(N, P, BLK))};
     hipLaunchKernelGGL((k_decode_step<IO, N, P, R, BLK, SB>), grid, block, 0, s, p);
     return hipGetLastError();
 }

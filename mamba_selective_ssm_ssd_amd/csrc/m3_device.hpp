@@ -10,7 +10,6 @@ namespace m3 {
 
 constexpr int kQ = 64;        // tokens per chunk
 constexpr int kWave = 64;     // CDNA wavefront width
-constexpr int kThreads = 256; // threads per workgroup of the chunk kernels
 constexpr double kPi = 3.14159265358979323846;
 constexpr double kTwoPi = 6.28318530717958647692;
 
