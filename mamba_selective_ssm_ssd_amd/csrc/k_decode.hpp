@@ -54,6 +54,14 @@ constexpr int decode_waves_per_simd(int N, int P, bool BLK, bool SB) {
          : decode_threads(N, P, BLK) == 128 ? (SB ? 4 : 3)
          : BLK ? (SB ? 4 : 3) : (SB && N <= 64 ? 5 : 4);
 }
+// Streaming cache hints on the state's read-modify-write (non-temporal
+// loads and stores, global_load/store ... nt), chosen per instantiation by
+// measurement on the b256 H64 P64 N64 R4 step (us per step, plain / hint):
+// the fp32 state reads with the hint (104.2 / 101.2; its stores with it are
+// slower, 106.2); the bf16 state and the block step write with it (74.8 /
+// 71.0 and 115.4 / 109.8).
+constexpr bool decode_nt_load(bool BLK, bool SB) { return !SB; }
+constexpr bool decode_nt_store(bool BLK, bool SB) { return SB || BLK; }
 // Resident workgroups per CU (4 SIMDs).
 constexpr int decode_wg_per_cu(int N, int P, bool BLK, bool SB) {
     return decode_waves_per_simd(N, P, BLK, SB) * 4 / (decode_threads(N, P, BLK) / kWave);
@@ -119,6 +127,33 @@ enum : int { kUnitB = 0, kUnitC = 1, kUnitX = 2, kUnitXp = 3, kUnitBp = 4, kUnit
 // even when stored).  Registers hold the stored form until the run is used.
 template <bool SB>
 struct StateRun;
+typedef float f32x4_v __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_v __attribute__((ext_vector_type(2)));
+// One state run moved with or without the non-temporal hint.
+template <bool NT>
+__device__ __forceinline__ float4 run_load(const float4 *p) {
+    if constexpr (!NT) return *p;
+    const f32x4_v v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_v *>(p));
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+template <bool NT>
+__device__ __forceinline__ uint2 run_load(const uint2 *p) {
+    if constexpr (!NT) return *p;
+    const u32x2_v v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_v *>(p));
+    return make_uint2(v.x, v.y);
+}
+template <bool NT>
+__device__ __forceinline__ void run_store(float4 *p, const float4 &a) {
+    if constexpr (!NT) { *p = a; return; }
+    const f32x4_v v = {a.x, a.y, a.z, a.w};
+    __builtin_nontemporal_store(v, reinterpret_cast<f32x4_v *>(p));
+}
+template <bool NT>
+__device__ __forceinline__ void run_store(uint2 *p, const uint2 &a) {
+    if constexpr (!NT) { *p = a; return; }
+    const u32x2_v v = {a.x, a.y};
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x2_v *>(p));
+}
 template <>
 struct StateRun<false> {
     typedef float4 raw;
@@ -192,7 +227,7 @@ __global__ __launch_bounds__(decode_threads(N, P, BLK)) __attribute__((amdgpu_wa
     auto load_state = [&](int64_t item, HV *hv) {
         const HV *hs = static_cast<const HV *>(p.h) + item * SLOTS;
 #pragma unroll
-        for (int j = 0; j < SPT; ++j) hv[j] = hs[j * DT + tslot];
+        for (int j = 0; j < SPT; ++j) hv[j] = run_load<decode_nt_load(BLK, SB)>(hs + j * DT + tslot);
     };
 
     // The small vectors of an item, as loaded (raw bits).  They are loaded one
@@ -347,7 +382,7 @@ __global__ __launch_bounds__(decode_threads(N, P, BLK)) __attribute__((amdgpu_wa
                 u[2] += cb * xp4.z + cg * x4.z;
                 u[3] += cb * xp4.w + cg * x4.w;
             }
-            hs[slot] = SR::pack(u);
+            run_store<decode_nt_store(BLK, SB)>(hs + slot, SR::pack(u));
 #pragma unroll
             for (int i = 0; i < R; ++i) {
                 const float cc = ct_s[i * N + n];
