@@ -61,6 +61,11 @@ constexpr int decode_waves_per_simd(int N, int P, bool BLK, bool SB) {
 // slower, 106.2); the bf16 state and the block step write with it (74.8 /
 // 71.0 and 115.4 / 109.8).
 constexpr bool decode_nt_load(bool BLK, bool SB) { return !SB; }
+// State runs updated together per LDS read of x and x_prev (see the update):
+// 4 takes the LDS operand reads of a step from 75 to 27 per wave.  On the b256
+// H64 P64 N64 R4 step: bf16 state 69.6 -> 67.0 us, fp32 state and block step
+// unchanged (groups of 2: 67.7 us; of 8: register spills, 84 us).
+constexpr int DG = 4;
 constexpr bool decode_nt_store(bool BLK, bool SB) { return SB || BLK; }
 // Resident workgroups per CU (4 SIMDs).
 constexpr int decode_wg_per_cu(int N, int P, bool BLK, bool SB) {
@@ -365,31 +370,46 @@ __global__ __launch_bounds__(decode_threads(N, P, BLK)) __attribute__((amdgpu_wa
         for (int i = 0; i < R; ++i)
 #pragma unroll
             for (int q = 0; q < 4; ++q) yp[i][q] = 0.f;
+        // The runs of a thread share their columns (4 pg .. 4 pg + 3), so
+        // x and x_prev of those columns are read from LDS once per group of
+        // GR runs and rank instead of once per run.
+        constexpr int GR = DG < SPT ? DG : SPT;
 #pragma unroll
-        for (int j = 0; j < SPT; ++j) {
-            const int slot = tid + j * DT;
-            if (SLOTS % DT != 0 && slot >= SLOTS) continue;
-            const int n = slot / P4;
-            const float4 hv = SR::unpack(hc[j]);
-            float u[4] = {alpha * hv.x, alpha * hv.y, alpha * hv.z, alpha * hv.w};
+        for (int j0 = 0; j0 < SPT; j0 += GR) {
+            float u[GR][4];
+#pragma unroll
+            for (int jj = 0; jj < GR; ++jj) {
+                const float4 hv = SR::unpack(hc[j0 + jj]);
+                u[jj][0] = alpha * hv.x; u[jj][1] = alpha * hv.y; u[jj][2] = alpha * hv.z; u[jj][3] = alpha * hv.w;
+            }
 #pragma unroll
             for (int r = 0; r < R; ++r) {
-                const float cb = beta * bp_s[r * N + n], cg = gamma * bt_s[r * N + n];
                 const float4 xp4 = *reinterpret_cast<const float4 *>(xp_s + r * P + 4 * pg);
                 const float4 x4 = *reinterpret_cast<const float4 *>(x_s + r * P + 4 * pg);
-                u[0] += cb * xp4.x + cg * x4.x;
-                u[1] += cb * xp4.y + cg * x4.y;
-                u[2] += cb * xp4.z + cg * x4.z;
-                u[3] += cb * xp4.w + cg * x4.w;
-            }
-            run_store<decode_nt_store(BLK, SB)>(hs + slot, SR::pack(u));
 #pragma unroll
-            for (int i = 0; i < R; ++i) {
-                const float cc = ct_s[i * N + n];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) yp[i][q] += cc * u[q];
+                for (int jj = 0; jj < GR; ++jj) {
+                    const int n = min(tid + (j0 + jj) * DT, SLOTS - 1) / P4;
+                    const float cb = beta * bp_s[r * N + n], cg = gamma * bt_s[r * N + n];
+                    u[jj][0] += cb * xp4.x + cg * x4.x;
+                    u[jj][1] += cb * xp4.y + cg * x4.y;
+                    u[jj][2] += cb * xp4.z + cg * x4.z;
+                    u[jj][3] += cb * xp4.w + cg * x4.w;
+                }
             }
-            __builtin_amdgcn_sched_barrier(0); // one run at a time: bounds register use
+#pragma unroll
+            for (int jj = 0; jj < GR; ++jj) {
+                const int slot = tid + (j0 + jj) * DT;
+                if (SLOTS % DT != 0 && slot >= SLOTS) continue;
+                const int n = slot / P4;
+                run_store<decode_nt_store(BLK, SB)>(hs + slot, SR::pack(u[jj]));
+#pragma unroll
+                for (int i = 0; i < R; ++i) {
+                    const float cc = ct_s[i * N + n];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) yp[i][q] += cc * u[jj][q];
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0); // one group at a time: bounds register use
         }
 #pragma unroll
         for (int i = 0; i < R; ++i)
