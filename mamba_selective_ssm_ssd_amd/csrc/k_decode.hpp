@@ -374,6 +374,7 @@ __global__ __launch_bounds__(decode_threads(N, P, BLK)) __attribute__((amdgpu_wa
         // x and x_prev of those columns are read from LDS once per group of
         // GR runs and rank instead of once per run.
         constexpr int GR = DG < SPT ? DG : SPT;
+        static_assert(SPT % GR == 0, "whole groups of state runs");
 #pragma unroll
         for (int j0 = 0; j0 < SPT; j0 += GR) {
             float u[GR][4];
