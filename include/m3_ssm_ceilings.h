@@ -34,8 +34,10 @@ m3_status_t m3_ceiling_mfma(int32_t kind, int32_t nblocks, int32_t iters, float 
 
 /* Stream of n float4 (16-byte) elements.  mode 0: dst = src (reads and
  * writes 16 n bytes each); mode 1: dst = dst * 1.0001f + 1e-7f in place
- * (reads and writes dst; src unused, may be NULL).  Grid-stride over
- * nblocks workgroups of 256 threads, 8 float4 per thread per trip. */
+ * (reads and writes dst; src unused, may be NULL); modes 2 and 3: the same
+ * as 0 and 1 with non-temporal loads and stores (global_load/store ... nt),
+ * the streaming cache hints some of the mixer's kernels use.  Grid-stride
+ * over nblocks workgroups of 256 threads, 8 float4 per thread per trip. */
 m3_status_t m3_ceiling_stream(int32_t mode, const void *src, void *dst, int64_t n,
                               int32_t nblocks, hipStream_t stream);
 

@@ -51,28 +51,39 @@ __global__ __launch_bounds__(256) void k_ceiling_mfma(int iters, float *sink) {
     sink[blockIdx.x * 256 + threadIdx.x] = t[0] + t[1] + t[2] + t[3];
 }
 
+// One float4 moved with or without the non-temporal hint.
+template <bool NT>
+__device__ __forceinline__ floatx4_t ld4(const floatx4_t *p) {
+    if constexpr (NT) return __builtin_nontemporal_load(p);
+    return *p;
+}
+template <bool NT>
+__device__ __forceinline__ void st4(floatx4_t *p, const floatx4_t &v) {
+    if constexpr (NT) __builtin_nontemporal_store(v, p);
+    else *p = v;
+}
+
 // Each thread moves 8 float4 per trip (all 8 loads issued before the first
-// store), so every wave keeps 8 loads in flight.
+// store), so every wave keeps 8 loads in flight.  MODE & 1: in place
+// read-modify-write (else copy); MODE & 2: non-temporal hints.
 template <int MODE>
-__global__ __launch_bounds__(256) void k_ceiling_stream(const float4 *src, float4 *dst, int64_t n) {
+__global__ __launch_bounds__(256) void k_ceiling_stream(const floatx4_t *src, floatx4_t *dst, int64_t n) {
     constexpr int U = 8;
+    constexpr bool RMW = (MODE & 1) != 0, NT = (MODE & 2) != 0;
     const int64_t stride = int64_t(gridDim.x) * 256 * U;
     for (int64_t i0 = int64_t(blockIdx.x) * 256 * U + threadIdx.x; i0 < n; i0 += stride) {
-        float4 v[U];
+        floatx4_t v[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t i = i0 + int64_t(u) * 256;
-            if (i < n) v[u] = MODE == 0 ? src[i] : dst[i];
+            if (i < n) v[u] = ld4<NT>(RMW ? dst + i : src + i);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t i = i0 + int64_t(u) * 256;
             if (i < n) {
-                if constexpr (MODE == 1) {
-                    v[u].x = v[u].x * 1.0001f + 1e-7f; v[u].y = v[u].y * 1.0001f + 1e-7f;
-                    v[u].z = v[u].z * 1.0001f + 1e-7f; v[u].w = v[u].w * 1.0001f + 1e-7f;
-                }
-                dst[i] = v[u];
+                if constexpr (RMW) v[u] = v[u] * 1.0001f + 1e-7f;
+                st4<NT>(dst + i, v[u]);
             }
         }
     }
@@ -93,14 +104,16 @@ extern "C" m3_status_t m3_ceiling_mfma(int32_t kind, int32_t nblocks, int32_t it
 
 extern "C" m3_status_t m3_ceiling_stream(int32_t mode, const void *src, void *dst, int64_t n,
                                          int32_t nblocks, hipStream_t stream) {
-    if ((mode != 0 && mode != 1) || n < 1 || nblocks < 1 || !dst || !aligned16(dst) ||
-        (mode == 0 && (!src || !aligned16(src))))
+    if (mode < 0 || mode > 3 || n < 1 || nblocks < 1 || !dst || !aligned16(dst) ||
+        ((mode & 1) == 0 && (!src || !aligned16(src))))
         return M3_ERR_INVALID_ARGUMENT;
-    if (mode == 0)
-        hipLaunchKernelGGL(k_ceiling_stream<0>, dim3(nblocks), dim3(256), 0, stream,
-                           static_cast<const float4 *>(src), static_cast<float4 *>(dst), n);
-    else
-        hipLaunchKernelGGL(k_ceiling_stream<1>, dim3(nblocks), dim3(256), 0, stream,
-                           static_cast<const float4 *>(src), static_cast<float4 *>(dst), n);
+    const floatx4_t *s = static_cast<const floatx4_t *>(src);
+    floatx4_t *d = static_cast<floatx4_t *>(dst);
+    switch (mode) {
+    case 0: hipLaunchKernelGGL(k_ceiling_stream<0>, dim3(nblocks), dim3(256), 0, stream, s, d, n); break;
+    case 1: hipLaunchKernelGGL(k_ceiling_stream<1>, dim3(nblocks), dim3(256), 0, stream, s, d, n); break;
+    case 2: hipLaunchKernelGGL(k_ceiling_stream<2>, dim3(nblocks), dim3(256), 0, stream, s, d, n); break;
+    default: hipLaunchKernelGGL(k_ceiling_stream<3>, dim3(nblocks), dim3(256), 0, stream, s, d, n); break;
+    }
     return hipGetLastError() == hipSuccess ? M3_OK : M3_ERR_HIP;
 }

@@ -400,3 +400,20 @@ def test_backward_plan(b, T, H, R, S, tokens):
     assert got_s == 1 or got_t >= 2 * Q
     rc, _, _ = capi.m3_ssm_prefill_backward_plan(mixer.make_shape(b, T, H, 64, 5, R, torch.bfloat16))
     assert rc == capi.M3_ERR_INVALID_ARGUMENT
+
+
+def test_ceiling_errors():
+    """The on-box ceiling kernels reject bad arguments before any launch."""
+    for mode in (-1, 4, 9):
+        assert capi.m3_ceiling_stream(mode, FAKE, FAKE, 64, 8, None) == capi.M3_ERR_INVALID_ARGUMENT
+    for mode in (0, 2):  # copies need a source
+        assert capi.m3_ceiling_stream(mode, None, FAKE, 64, 8, None) == capi.M3_ERR_INVALID_ARGUMENT
+        assert capi.m3_ceiling_stream(mode, FAKE_MISALIGNED, FAKE, 64, 8, None) == capi.M3_ERR_INVALID_ARGUMENT
+    for mode in range(4):
+        assert capi.m3_ceiling_stream(mode, FAKE, None, 64, 8, None) == capi.M3_ERR_INVALID_ARGUMENT
+        assert capi.m3_ceiling_stream(mode, FAKE, FAKE, 0, 8, None) == capi.M3_ERR_INVALID_ARGUMENT
+        assert capi.m3_ceiling_stream(mode, FAKE, FAKE, 64, 0, None) == capi.M3_ERR_INVALID_ARGUMENT
+    for kind in (-1, 2):
+        assert capi.m3_ceiling_mfma(kind, 8, 1, FAKE, None) == capi.M3_ERR_INVALID_ARGUMENT
+    assert capi.m3_ceiling_mfma(0, 0, 1, FAKE, None) == capi.M3_ERR_INVALID_ARGUMENT
+    assert capi.m3_ceiling_mfma(0, 8, 1, None, None) == capi.M3_ERR_INVALID_ARGUMENT
