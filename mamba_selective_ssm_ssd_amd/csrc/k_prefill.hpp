@@ -1006,6 +1006,13 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
                 run_coef<C, IO>(rp, tc_of(c + 1), t0 + Q, p.T, Ah, coef_s + (buf ^ 1) * (4 * kWave), misc_s + (buf ^ 1));
             load_pro<C, IO>(p, b, h, int64_t(cn2) * Q, tc_of(cn2), rp);
         }
+        // a1 angles of the next chunk (bf16 I/O: from the theta table written
+        // before the barrier), on the waves that own no intra-chunk rows, while
+        // the others take the products.  This chunk's staging has read the
+        // cos/sin table, and the chunk rotation is double-buffered.
+        if constexpr (C::MFP) {
+            if (c + 1 < c_end) run_angles<C, IO>(rp, tc_of(c + 1), cs_s, thc_s + (buf ^ 1) * K, ths_s, tht);
+        }
         if (OUT) {
             // ---- a3 + a5: y = M x + exp(ell) Chat H for this wave's row blocks,
             // evaluated transposed (y^T = x^T M^T + H^T Chat^T exp(ell)) so that
@@ -1276,10 +1283,11 @@ __global__ __launch_bounds__(kPT) void k_prefill(const PrefillParams p) {
         }
         gsum += gc;
 
-        // ---- a1 of the next chunk: angles (and, for fp32 I/O, coefficients)
+        // ---- a1 of the next chunk, fp32 I/O: angles and coefficients (from
+        // the registers loaded a chunk ahead)
         if (c + 1 < c_end) {
-            run_angles<C, IO>(rp, tc_of(c + 1), cs_s, thc_s + (buf ^ 1) * K, ths_s, tht);
             if constexpr (!C::MFP) {
+                run_angles<C, IO>(rp, tc_of(c + 1), cs_s, thc_s + (buf ^ 1) * K, ths_s, tht);
                 run_coef<C, IO>(rp, tc_of(c + 1), t0 + Q, p.T, Ah, coef_s + (buf ^ 1) * (4 * kWave), misc_s + (buf ^ 1));
                 load_pro<C, IO>(p, b, h, int64_t(cn2) * Q, tc_of(cn2), rp);
             }
