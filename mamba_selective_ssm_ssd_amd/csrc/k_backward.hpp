@@ -136,7 +136,13 @@ struct BwdCfg {
     static constexpr int o_pe = o_pu + 4 * V;   // dE partials [4][V]
     static constexpr int o_pz = o_pe + 4 * V;   // per-wave scalars [4][4]
     static constexpr int o_phe = (o_pz + 16 + 1) / 2 * 2; // Phi at the chunk end, fp64 [K]
-    static constexpr int floats = o_phe + 2 * K;
+    // When it fits: the adjoint G handed from the first wave group, which
+    // updates it, to the second, which reloads it in its own layout, instead
+    // of both groups updating it [N][pG] (row n, column p)
+    static constexpr int pG = P + 4;
+    static constexpr int o_gx = (o_phe + 2 * K + 3) / 4 * 4;
+    static constexpr bool GX = size_t(o_gx + N * pG) * 4 <= kMaxLdsBytes;
+    static constexpr int floats = GX ? o_gx + N * pG : o_phe + 2 * K;
     static constexpr size_t bytes = size_t(floats) * 4;
     static_assert(bytes <= kMaxLdsBytes, "backward LDS layout exceeds the workgroup's LDS");
     static_assert(Q * 8 <= kBwdThreads, "one group of 8 threads per token");
@@ -166,6 +172,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
     float2 *CS = reinterpret_cast<float2 *>(sm + Cf::o_cs);
     float *SC = sm + Cf::o_sc, *PU = sm + Cf::o_pu, *PE = sm + Cf::o_pe, *PZ = sm + Cf::o_pz;
     double *PHE = reinterpret_cast<double *>(sm + Cf::o_phe);
+    float *GXS = sm + Cf::o_gx; // (GX) the adjoint G, [N][pG]
     auto sc = [&](int s, int i) -> float & { return SC[s * SQ + i]; };
 
     // lane ids, re-derived through an opaque copy at the top of every chunk so
@@ -907,6 +914,13 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
                     for (int e = 0; e < 4; ++e) G2(nb) = mfma4(aq[e], bq[e] * ev[kb][e], G2(nb));
                 }
             }
+            if constexpr (Cf::GX) {
+                // the updated G for the second group (read after the barrier)
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) GXS[(nb * 16 + 4 * lg + e) * Cf::pG + w * 16 + li] = G2(nb)[e];
+            }
         }
         // dC~ and dB~ (tiles (vb, nb = w + 4 q)) completed, rotated back; dPhi terms
 #pragma unroll
@@ -949,8 +963,10 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
                     }
                 }
         }
-        // G <- e^{ec_end} G + C~^T diag(E) gy  (the transposed orientation)
+        // G <- e^{ec_end} G + C~^T diag(E) gy  (the transposed orientation;
+        // with GX reloaded from the first group's after the barrier instead)
         if (w >= 4) {
+        if constexpr (!Cf::GX) {
 #pragma unroll
         for (int q = 0; q < NBW; ++q)
 #pragma unroll
@@ -973,6 +989,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
                     for (int pb = 0; pb < PB; ++pb) G1(q, pb) = mfma4(ag[pb][e], bq, G1(q, pb));
                 }
         }
+        }
         // per-row partial sums of dE and dU over this wave's columns
 #pragma unroll
         for (int vb = 0; vb < VB; ++vb)
@@ -991,6 +1008,20 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
         if (c > c0) issue(t0 - Q, Q, true, false);
         }
         __syncthreads();
+        if constexpr (Cf::GX) {
+            // the second group's G tiles (pb, nb = w - 4 + 4 q) from the first
+            // group's update; the buffer is next written a chunk later, after
+            // further barriers
+            if (w >= 4) {
+#pragma unroll
+                for (int q = 0; q < NBW; ++q) {
+                    const int nb = w - 4 + 4 * q;
+                    if (nb >= NB) continue;
+#pragma unroll
+                    for (int pb = 0; pb < PB; ++pb) G1(q, pb) = lds4(GXS + (nb * 16 + li) * Cf::pG + pb * 16 + 4 * lg);
+                }
+            }
+        }
         // ---- the scalars (wave 0, lane = token)
         if (w == 0) {
             const int j = lane;
