@@ -143,6 +143,11 @@ struct BwdCfg {
     static constexpr int o_gx = (o_phe + 2 * K + 3) / 4 * 4;
     static constexpr bool GX = size_t(o_gx + N * pG) * 4 <= kMaxLdsBytes;
     static constexpr int floats = GX ? o_gx + N * pG : o_phe + 2 * K;
+    // Otherwise (GA) G goes through areas that are dead from the end of the
+    // products to the next chunk's staging: 16-row blocks of G in the run
+    // gy^T, x, gy, (W.S)^T (GAN blocks), the rest in S.D.
+    static constexpr int GAN = (P * pV + 2 * V * pP + V * pV) / (16 * pG);
+    static constexpr bool GA = !GX && GAN + (V * pV) / (16 * pG) >= NB;
     static constexpr size_t bytes = size_t(floats) * 4;
     static_assert(bytes <= kMaxLdsBytes, "backward LDS layout exceeds the workgroup's LDS");
     static_assert(Q * 8 <= kBwdThreads, "one group of 8 threads per token");
@@ -172,7 +177,14 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
     float2 *CS = reinterpret_cast<float2 *>(sm + Cf::o_cs);
     float *SC = sm + Cf::o_sc, *PU = sm + Cf::o_pu, *PE = sm + Cf::o_pe, *PZ = sm + Cf::o_pz;
     double *PHE = reinterpret_cast<double *>(sm + Cf::o_phe);
-    float *GXS = sm + Cf::o_gx; // (GX) the adjoint G, [N][pG]
+    // row n of the adjoint G handed from the first wave group to the second
+    // (GX: its own buffer [N][pG]; GA: 16-row blocks in borrowed areas)
+    auto gx_row = [&](int n) -> float * {
+        if constexpr (Cf::GX) return sm + Cf::o_gx + n * Cf::pG;
+        const int nb = n >> 4;
+        return (nb < Cf::GAN ? sm + Cf::o_t2 + nb * 16 * Cf::pG : sm + Cf::o_sd + (nb - Cf::GAN) * 16 * Cf::pG) +
+               (n & 15) * Cf::pG;
+    };
     auto sc = [&](int s, int i) -> float & { return SC[s * SQ + i]; };
 
     // lane ids, re-derived through an opaque copy at the top of every chunk so
@@ -919,7 +931,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) GXS[(nb * 16 + 4 * lg + e) * Cf::pG + w * 16 + li] = G2(nb)[e];
+                    for (int e = 0; e < 4; ++e) gx_row(nb * 16 + 4 * lg + e)[w * 16 + li] = G2(nb)[e];
             }
         }
         // dC~ and dB~ (tiles (vb, nb = w + 4 q)) completed, rotated back; dPhi terms
@@ -964,9 +976,9 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
                 }
         }
         // G <- e^{ec_end} G + C~^T diag(E) gy  (the transposed orientation;
-        // with GX reloaded from the first group's after the barrier instead)
+        // with GX or GA reloaded from the first group's after the barrier)
         if (w >= 4) {
-        if constexpr (!Cf::GX) {
+        if constexpr (!Cf::GX && !Cf::GA) {
 #pragma unroll
         for (int q = 0; q < NBW; ++q)
 #pragma unroll
@@ -1008,7 +1020,18 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
         if (c > c0) issue(t0 - Q, Q, true, false);
         }
         __syncthreads();
-        if constexpr (Cf::GX) {
+        if constexpr (Cf::GA) {
+            // every read of the areas G borrows is behind this chunk's
+            // products; the next writes are the next chunk's staging
+            if (w < 4 && w < PB) {
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) gx_row(nb * 16 + 4 * lg + e)[w * 16 + li] = G2(nb)[e];
+            }
+            __syncthreads();
+        }
+        if constexpr (Cf::GX || Cf::GA) {
             // the second group's G tiles (pb, nb = w - 4 + 4 q) from the first
             // group's update; the buffer is next written a chunk later, after
             // further barriers
@@ -1018,7 +1041,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(const BwdParams p) {
                     const int nb = w - 4 + 4 * q;
                     if (nb >= NB) continue;
 #pragma unroll
-                    for (int pb = 0; pb < PB; ++pb) G1(q, pb) = lds4(GXS + (nb * 16 + li) * Cf::pG + pb * 16 + 4 * lg);
+                    for (int pb = 0; pb < PB; ++pb) G1(q, pb) = lds4(gx_row(nb * 16 + li) + pb * 16 + 4 * lg);
                 }
             }
         }
