@@ -242,3 +242,25 @@ def test_backward_at_the_largest_accepted_head_count():
             assert v <= BAR, f"head {hi}: gradient of {k}: error {v:.3e}"
     del inp, gy, grads
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("R", [1, 2, 3, 4])
+@pytest.mark.parametrize("split", [False, True])
+def test_backward_adjoint_through_borrowed_lds(R, split):
+    """At N = 128, P = 64 the updated adjoint state reaches the second wave
+    group through LDS areas the chunk no longer reads (no room for a buffer
+    of its own): every rank, a carried state and final-state gradients, in
+    one workgroup per sequence and cut into segments."""
+    from mamba_selective_ssm_ssd_amd import capi, mixer
+    N, P = 128, 64
+    io = "bf16" if R % 2 else "f32"
+    # without a split: three chunks (32 / R tokens each, 10 for R = 3) and a
+    # ragged tail, too few to cut into segments of two chunks or more
+    b, H, T = (1, 1, 700) if split else (2, 2, 3 * (32 // R) - 2)
+    rc, S, L = capi.m3_ssm_prefill_backward_plan(mixer.make_shape(b, T, H, P, N, R, torch_io(io)))
+    assert rc == capi.M3_OK and (S > 1) == split, (S, L)
+    errs = _run(b, T, H, P, N, R, io, seed=13 * R + T, with_init=True, with_gfinal=True)
+    print(f"backward N{N} P{P} R{R} {io} T{T} ({S} segments): "
+          + " ".join(f"{k} {v:.1e}" for k, v in errs.items()))
+    for k, v in errs.items():
+        assert v <= BAR, f"gradient of {k}: error {v:.3e} > {BAR}"
